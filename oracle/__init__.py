@@ -1,0 +1,7 @@
+"""CPU float64 oracle for the selective scan and the decode step.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import or call this
+package: only the tests, the smoke check and the benchmark's CPU-baseline leg use
+it.  It shares no code with the HIP library and does not import it.
+"""
+from .ssm import selective_scan, state_update, softplus, silu  # noqa: F401

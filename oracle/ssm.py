@@ -1,0 +1,110 @@
+"""Plain, sequential float64 definition of the selective scan and its decode step.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): the GPU library never
+imports this module, and this module never imports the GPU library.
+
+What is computed, for batch b, time t, channel d, state n (all in float64, on the
+exact values the device receives):
+
+  delta'[b,t,d] = delta_raw[b,t,d] + bias[d]                     (bias = 0 if absent)
+  Delta[b,t,d]  = softplus(delta') if the flag is set, else delta'
+  abar          = exp(Delta * A[d,n])                            zero-order-hold decay
+  bbar*u        = Delta * B[b,t,n] * u[b,t,d]                    simplified input term
+  h[b,t,d,n]    = abar * h[b,t-1,d,n] + Delta * B[b,t,n] * u[b,t,d],  h[b,-1] = h0 (0)
+  y[b,t,d]      = sum_n C[b,t,n] * h[b,t,d,n] + Dskip[d] * u[b,t,d]
+  y            <- y * silu(z[b,t,d])                              if z is given
+  final[b,d,n]  = h[b,L-1,d,n]
+
+Sources, by page and section:
+  * the recurrence, the readout after the update and the zero initial state follow
+    the interview-prep page's "Selective scan pseudo-code" and the slide deck's
+    "Mamba selective" listing (decay exp(Delta*A), input term Delta*B);
+  * Delta = softplus(W x + b) with the bias added before the softplus is the
+    interview-prep page's "Discretization and initialization details";
+  * the skip term D*u is the output equation y = Cx + Du of the slide deck's S4
+    section; the SiLU(z) gate multiplies the SSM output (lecture notes §6 "The
+    block"; interview-prep page "The Mamba Block").
+  Readings taken where the pages are silent: the gate multiplies (C.h + D.u), the
+  softplus has no threshold, SiLU(z) = z / (1 + exp(-z)).
+
+Memory order of the arguments matches the library: u, delta, z are [batch][D][L];
+B, C are [batch][L][N]; A is [D][N]; Dskip and bias are [D].
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def softplus(x):
+    """log(1 + e^x) in float64, written in the overflow-free form max(x,0) + log1p(e^-|x|)."""
+    x = np.asarray(x, dtype=np.float64)
+    return np.maximum(x, 0.0) + np.log1p(np.exp(-np.abs(x)))
+
+
+def silu(z):
+    """SiLU(z) = z * sigmoid(z) = z / (1 + e^-z), float64."""
+    z = np.asarray(z, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def _step_delta(delta_raw, bias, delta_softplus):
+    d = np.asarray(delta_raw, dtype=np.float64)
+    if bias is not None:
+        d = d + bias
+    return softplus(d) if delta_softplus else d
+
+
+def selective_scan(u, delta, A, B, C, Dskip=None, z=None, delta_bias=None,
+                   delta_softplus=True, h0=None):
+    """Return (y [batch][D][L], final_state [batch][D][N]) in float64.
+
+    A plain loop over time, vectorised over (batch, channel, state).
+    """
+    u = np.asarray(u, dtype=np.float64)
+    Bt, Dc, L = u.shape
+    A = np.asarray(A, dtype=np.float64)
+    N = A.shape[1]
+    Bm = np.asarray(B, dtype=np.float64)
+    Cm = np.asarray(C, dtype=np.float64)
+    assert A.shape == (Dc, N) and Bm.shape == (Bt, L, N) and Cm.shape == (Bt, L, N)
+    delta = np.asarray(delta, dtype=np.float64)
+    bias = None if delta_bias is None else np.asarray(delta_bias, dtype=np.float64)[None, :]
+    Dv = None if Dskip is None else np.asarray(Dskip, dtype=np.float64)[None, :]
+
+    h = np.zeros((Bt, Dc, N)) if h0 is None else np.array(h0, dtype=np.float64)
+    y = np.empty((Bt, Dc, L))
+    for t in range(L):
+        dt = _step_delta(delta[:, :, t], bias, delta_softplus)          # [Bt, Dc]
+        abar = np.exp(dt[:, :, None] * A[None, :, :])                   # [Bt, Dc, N]
+        inp = (dt * u[:, :, t])[:, :, None] * Bm[:, t, None, :]         # Delta*B*u
+        h = abar * h + inp
+        yt = np.einsum("bdn,bn->bd", h, Cm[:, t, :])
+        if Dv is not None:
+            yt = yt + Dv * u[:, :, t]
+        y[:, :, t] = yt
+    if z is not None:
+        y = y * silu(z)
+    return y, h
+
+
+def state_update(state, u_t, delta_t, A, B_t, C_t, Dskip=None, z_t=None,
+                 delta_bias=None, delta_softplus=True):
+    """One recurrent decode step: returns (y_t [S][D], new_state [S][D][N]) in float64.
+
+    The same step as one iteration of ``selective_scan`` started from ``state``.
+    """
+    h = np.asarray(state, dtype=np.float64)
+    u_t = np.asarray(u_t, dtype=np.float64)
+    A = np.asarray(A, dtype=np.float64)
+    bias = None if delta_bias is None else np.asarray(delta_bias, dtype=np.float64)[None, :]
+    dt = _step_delta(delta_t, bias, delta_softplus)                       # [S, D]
+    abar = np.exp(dt[:, :, None] * A[None, :, :])
+    inp = (dt * u_t)[:, :, None] * np.asarray(B_t, dtype=np.float64)[:, None, :]
+    h = abar * h + inp
+    y = np.einsum("sdn,sn->sd", h, np.asarray(C_t, dtype=np.float64))
+    if Dskip is not None:
+        y = y + np.asarray(Dskip, dtype=np.float64)[None, :] * u_t
+    if z_t is not None:
+        y = y * silu(z_t)
+    return y, h

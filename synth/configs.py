@@ -1,0 +1,69 @@
+"""The five synthetic workloads: shapes, activation dtype and input recipe.
+
+Shapes come from Mamba-style layer widths: the decode workload's D = 5120 and
+N = 16 follow the Mamba-2.8B card (d_model 2560, expand 2, d_state 16) on the
+interview-prep page's "Model Card" table; the long-context scan uses that
+card's d_model as its channel count.
+"""
+from dataclasses import dataclass
+
+
+@dataclass(frozen=True)
+class ScanConfig:
+    name: str
+    batch: int
+    L: int
+    D: int
+    N: int
+    dtype: str          # activation dtype: "f32" or "bf16"
+    gate: bool          # SiLU(z) output gate present
+    d_skip: str         # "normal": D ~ N(0,1); "ones": D = 1
+    seed: int = 0
+
+    @property
+    def elements(self) -> int:
+        return self.batch * self.L * self.D * self.N
+
+    def algorithmic_bytes(self) -> int:
+        """Each input read once and each output written once."""
+        e = 4 if self.dtype == "f32" else 2
+        per_tok = self.batch * self.L * self.D * e
+        n_act = 3 + (1 if self.gate else 0)          # u, delta, y (+ z)
+        return (per_tok * n_act
+                + 2 * self.batch * self.L * self.N * e  # B, C
+                + 4 * self.D * self.N                   # A
+                + 4 * self.D * 2                        # D skip + delta bias
+                + 4 * self.batch * self.D * self.N)     # final state
+
+
+@dataclass(frozen=True)
+class DecodeConfig:
+    name: str
+    batch: int          # sequences S
+    D: int
+    N: int
+    steps: int
+    dtype: str = "bf16"
+    gate: bool = True
+    seed: int = 0
+
+    @property
+    def elements_per_step(self) -> int:
+        return self.batch * self.D * self.N
+
+    def algorithmic_bytes_per_step(self) -> int:
+        e = 4 if self.dtype == "f32" else 2
+        sd = self.batch * self.D
+        return (8 * sd * self.N                        # state read + write
+                + sd * e * (4 if self.gate else 3)     # u, delta, (z), y
+                + 2 * self.batch * self.N * e          # B_t, C_t
+                + 4 * self.D * self.N + 8 * self.D)    # A, D skip, bias
+
+
+CONFIGS = {
+    "tiny_f32": ScanConfig("tiny_f32", 1, 64, 16, 4, "f32", gate=False, d_skip="normal"),
+    "mamba130m_f32": ScanConfig("mamba130m_f32", 2, 2048, 1536, 16, "f32", gate=True, d_skip="ones"),
+    "mamba1p4b_bf16": ScanConfig("mamba1p4b_bf16", 8, 2048, 4096, 16, "bf16", gate=True, d_skip="ones"),
+    "long131k_bf16": ScanConfig("long131k_bf16", 1, 131072, 2560, 16, "bf16", gate=True, d_skip="ones"),
+    "decode_bf16": DecodeConfig("decode_bf16", 256, 5120, 16, 512),
+}
