@@ -1,0 +1,259 @@
+"""Benchmark of the selective scan (and the decode step) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one full pass of the hot path over one batch: one selective-scan call
+over the whole [batch, D, L] workload (softplus, discretisation, scan, readout,
+skip, gate, final state), or for the decode workload one state-update call.
+Inputs are synthetic and seeded (synth/), resident in HBM before timing.  Each
+step reads a different copy of the inputs (enough copies to exceed the 256 MB
+Infinity Cache), so every step streams its inputs from HBM.  The K steps are
+captured in one HIP graph and replayed between two synchronisations.
+
+Prints one JSON line: elements/s (B*L*D*N per second), the roofline of the
+dominant kernel (algorithmic bytes / average kernel time, against 8 TB/s), and
+the float64 CPU oracle timed on this host on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+PEAK_HBM_GBS = 8000.0
+MALL_BYTES = 256 << 20
+DEFAULT_WORKLOAD = "mamba130m_f32"
+KERNEL_SRC = {"scan": "selective_state_space_68_amd/csrc/scan_chunked.hip",
+              "decode": "selective_state_space_68_amd/csrc/state_update.hip"}
+KERNEL_NAME = {"scan": "scan_chunked_kernel", "decode": "state_update_vec_kernel"}
+
+
+def src_hash(kind):
+    h = hashlib.sha256()
+    for p in (KERNEL_SRC[kind], "selective_state_space_68_amd/csrc/device_common.hpp"):
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(workload, kind):
+    """HBM bytes per launch from committed rocprofv3 PMC summaries, or None when the
+    kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(workload)
+    if not rec or rec.get("source_hash") != src_hash(kind):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def dev(torch, a):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to("cuda").view(torch.bfloat16)
+    return torch.from_numpy(a.astype(np.float32, copy=False)).to("cuda")
+
+
+def cpu_baseline_scan(cfg, inp, budget_s=20.0):
+    """The float64 oracle, as it is, on a bounded sample of the workload: whole
+    channels (full length L) of the first batch rows, enough for ~budget_s."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:  # pragma: no cover
+        threadpool_limits = None
+    per_b = cfg.L * cfg.D * cfg.N
+    nb = cfg.batch
+    # time one small slice first to size the sample
+    d_probe = min(cfg.D, 64)
+    t0 = time.perf_counter()
+    oracle.selective_scan(inp.u[:1, :d_probe], inp.delta[:1, :d_probe], inp.A[:d_probe], inp.B[:1], inp.C[:1],
+                          None if inp.Dskip is None else inp.Dskip[:d_probe],
+                          None if inp.z is None else inp.z[:1, :d_probe],
+                          None if inp.delta_bias is None else inp.delta_bias[:d_probe], inp.delta_softplus)
+    t_probe = time.perf_counter() - t0
+    # numpy's per-step overhead dominates small slices; widen the slice to fill the budget
+    d_take = cfg.D
+    b_take = max(1, min(nb, int(budget_s / max(t_probe * cfg.D / d_probe, 1e-3))))
+    ctx = threadpool_limits(1) if threadpool_limits else None
+    if ctx:
+        ctx.__enter__()
+    try:
+        t0 = time.perf_counter()
+        oracle.selective_scan(inp.u[:b_take], inp.delta[:b_take], inp.A, inp.B[:b_take], inp.C[:b_take],
+                              inp.Dskip, None if inp.z is None else inp.z[:b_take], inp.delta_bias,
+                              inp.delta_softplus)
+        dt = time.perf_counter() - t0
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+    elems = b_take * per_b
+    return {"value": elems / dt, "unit": "elements/s", "cores": 1, "kind": "oracle",
+            "sample": f"{b_take} of {nb} batch rows x all {d_take} channels x full L={cfg.L}, "
+                      f"N={cfg.N} ({elems:.3e} elements, {dt:.1f} s, float64 numpy, 1 thread)"}
+
+
+def bench_scan(args, torch, lib_ops):
+    cfg = synth.CONFIGS[args.workload]
+    inp = synth.make_config_inputs(cfg)
+    nbytes = cfg.algorithmic_bytes()
+    sets = args.sets or max(2, int(np.ceil(600e6 / nbytes)))
+    A, Dk, bias = dev(torch, inp.A), dev(torch, inp.Dskip), dev(torch, inp.delta_bias)
+    bufs = []
+    for _ in range(sets):
+        t = {k: dev(torch, inp.upload_array(k)) if inp.upload_array(k) is not None else None
+             for k in ("u", "delta", "B", "C", "z")}
+        t["y"] = torch.empty_like(t["u"])
+        t["fs"] = torch.empty((cfg.batch, cfg.D, cfg.N), dtype=torch.float32, device="cuda")
+        bufs.append(t)
+
+    def step(i):
+        t = bufs[i % sets]
+        lib_ops.selective_scan_fwd(t["u"], t["delta"], A, t["B"], t["C"], Dk, t["z"], bias, True,
+                                   y=t["y"], final_state=t["fs"], variant=args.variant,
+                                   tokens_per_lane=args.kpl)
+
+    return cfg, inp, nbytes, cfg.elements, sets, step, bufs
+
+
+def bench_decode(args, torch, lib_ops):
+    cfg = synth.CONFIGS[args.workload]
+    S, D, N = cfg.batch, cfg.D, cfg.N
+    A, Dk, bias = (dev(torch, x) for x in synth.make_decode_params(S, D, N, seed=cfg.seed))
+    nbytes = cfg.algorithmic_bytes_per_step()
+    sets = args.sets or max(2, int(np.ceil(600e6 / nbytes)))
+    st0 = synth.make_decode_state(S, D, N, seed=cfg.seed)
+    bufs = []
+    for i in range(sets):
+        x = synth.make_decode_step(S, D, N, i, cfg.dtype, cfg.gate, seed=cfg.seed)
+        t = {k: dev(torch, x.dev[k]) for k in ("u", "delta", "B", "C", "z")}
+        t["state"] = dev(torch, st0)
+        t["y"] = torch.empty((S, D), dtype=t["u"].dtype, device="cuda")
+        bufs.append(t)
+
+    def step(i):
+        t = bufs[i % sets]
+        lib_ops.state_update(t["state"], t["u"], t["delta"], A, t["B"], t["C"], Dk, t["z"], bias, True,
+                             y=t["y"])
+
+    return cfg, None, nbytes, cfg.elements_per_step, sets, step, bufs
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(synth.CONFIGS))
+    ap.add_argument("--variant", type=int, default=0)
+    ap.add_argument("--kpl", type=int, default=0)
+    ap.add_argument("--sets", type=int, default=0, help="input copies to rotate (0 = enough to exceed 600 MB)")
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the selective scan shards by independent (batch, channel) "
+              "pairs with no communication, and multi-GPU runs are not part of this build; "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import selective_state_space_68_amd as lib_ops
+    lib_ops.load_library()
+    torch.cuda.set_device(0)
+    kind = "decode" if args.workload.startswith("decode") else "scan"
+    maker = bench_decode if kind == "decode" else bench_scan
+    cfg, inp, nbytes, elements, sets, step, bufs = maker(args, torch, lib_ops)
+    print(f"# workload {args.workload}: {elements:.3e} elements/step, {nbytes / 1e6:.2f} MB/step "
+          f"algorithmic, {sets} input copies", file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    graph = None
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(K):
+                step(i)
+        graph.replay()            # untimed replay (warm-up of the graph itself)
+        torch.cuda.synchronize()
+        if kind == "scan":        # the replayed outputs must equal an eager call's, bit for bit
+            ref = {k: bufs[(K - 1) % sets][k].clone() for k in ("y", "fs")}
+            step(K - 1)
+            torch.cuda.synchronize()
+            assert torch.equal(ref["y"], bufs[(K - 1) % sets]["y"]) and \
+                torch.equal(ref["fs"], bufs[(K - 1) % sets]["fs"]), "graph replay differs from eager"
+
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    ev0.record(stream)
+    if graph is not None:
+        graph.replay()
+    else:
+        for i in range(K):
+            step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    gpu_ms = ev0.elapsed_time(ev1)
+    ms_per_step = wall * 1e3 / K
+    kernel_ms = gpu_ms / K            # one kernel launch per step: events bracket the K launches
+    value = elements / (ms_per_step / 1e3)
+    achieved = nbytes / (kernel_ms / 1e3) / 1e9
+
+    cpu = None
+    if kind == "scan" and not args.no_cpu_baseline:
+        cpu = cpu_baseline_scan(cfg, inp, args.cpu_budget)
+
+    traffic = traffic_from_profiles(args.workload, kind)
+    out = {
+        "metric": "selective-scan elements/s (B*L*D*N) + achieved HBM GB/s vs peak, 1 GPU"
+        if kind == "scan" else "decode-step elements/s (S*D*N per step) + achieved HBM GB/s vs peak, 1 GPU",
+        "value": value,
+        "unit": "elements/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; shapes and distributions of the named workload)",
+        "config": ({"workload": args.workload, "batch": cfg.batch, "L": cfg.L, "D": cfg.D, "N": cfg.N,
+                    "act_dtype": cfg.dtype, "gate": cfg.gate, "variant": args.variant,
+                    "tokens_per_lane": args.kpl or 16, "graph": graph is not None, "input_copies": sets}
+                   if kind == "scan" else
+                   {"workload": args.workload, "sequences": cfg.batch, "D": cfg.D, "N": cfg.N,
+                    "act_dtype": cfg.dtype, "graph": graph is not None, "input_copies": sets}),
+        "roofline": {"bound": "hbm", "kernel": KERNEL_NAME[kind], "achieved": achieved,
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
+                     "traffic": traffic, "algorithmic_bytes_per_launch": nbytes,
+                     "avg_kernel_us": kernel_ms * 1e3},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,145 @@
+/*
+ * ssm.h - C ABI of the MI355X (gfx950) selective-scan library (libssm.so).
+ *
+ * The operation is Mamba's selective state-space scan.  For batch b, time t,
+ * channel d and state n:
+ *
+ *   Delta[b,t,d] = softplus(delta[b,t,d] + delta_bias[d])   (or without softplus)
+ *   h[b,t,d,n]   = exp(Delta * A[d,n]) * h[b,t-1,d,n] + Delta * B[b,t,n] * u[b,t,d]
+ *   y[b,t,d]     = (sum_n C[b,t,n] * h[b,t,d,n] + Dskip[d] * u[b,t,d]) * silu(z[b,t,d])
+ *
+ * with h[b,-1] = 0 and silu(z) = z / (1 + exp(-z)).  Sources: the recurrence and
+ * its readout follow the "Selective scan pseudo-code" of the interview-prep
+ * page on Mamba (vanos001.github.io) and the "Mamba selective" listing of the
+ * slide deck (brendanjameslynskey.github.io, Arch_02_Mamba_SSM): decay
+ * exp(Delta*A), input term Delta*B (the simplified zero-order hold).  The
+ * softplus of a biased projection is that page's "Discretization and
+ * initialization details"; the skip term D*u is the deck's S4 output equation;
+ * the SiLU(z) gate is the lecture notes' §6 "The block".
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers (HBM), row-major, densely packed.
+ *  - Activations (u, delta, z, y, B, C) use the activation dtype `dt`:
+ *    SSM_F32 = float32, SSM_BF16 = bfloat16 (raw 16-bit patterns; y is
+ *    rounded to nearest even).  Parameters A, Dskip, delta_bias and every
+ *    state buffer are always float32.  Arithmetic is float32.
+ *  - Calls are asynchronous and stream-ordered on `stream` (a hipStream_t;
+ *    NULL = the null stream).  They never synchronise.  Argument errors are
+ *    returned before anything is enqueued and leave outputs untouched.
+ *    Device faults surface at the caller's next synchronisation.
+ *  - The library never allocates or frees device memory; the caller owns
+ *    every buffer.  NaN/Inf inputs are not checked and propagate.
+ *  - Results are deterministic: same inputs, shapes and device give
+ *    bitwise-identical outputs.
+ *  - Alignment: every pointer must be aligned to its element size.  16-byte
+ *    aligned pointers and L a multiple of 8 select the vectorised kernels;
+ *    other shapes run a slower path with the same results.
+ */
+#ifndef SSM_H
+#define SSM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SSM_OK = 0,
+  SSM_ERR_INVALID_ARG = 1,  /* null required pointer, negative size, misalignment, aliasing */
+  SSM_ERR_UNSUPPORTED = 2,  /* N outside [1, 64], unknown dtype or variant */
+  SSM_ERR_HIP = 3           /* no usable device, launch failure, or missing gfx950 code */
+} ssm_status;
+
+typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
+
+#define SSM_MAX_N 64
+
+/*
+ * Selective scan, forward (prefill / training forward).
+ *
+ *   u, delta, z  : [batch][D][L] act   (each channel's time series is contiguous)
+ *   A            : [D][N] float32      (the diagonal state matrix, one row per channel)
+ *   Bm, Cm       : [batch][L][N] act   (shared by all D channels of a batch row)
+ *   Dskip        : [D] float32 or NULL (NULL means 0)
+ *   z            : NULL means no gate
+ *   delta_bias   : [D] float32 or NULL (NULL means 0); added before the softplus
+ *   delta_softplus: 0 or 1
+ *   y            : out [batch][D][L] act
+ *   final_state  : out [batch][D][N] float32, h[b, L-1, d, :], or NULL
+ *   batch, L, D  : >= 0 (a zero size is a no-op; with L == 0 the final state is 0)
+ *   N            : 1..64
+ *   workspace    : caller scratch of ssm_selective_scan_workspace_size() bytes,
+ *                  may be NULL when that size is 0
+ *
+ * Errors: SSM_ERR_INVALID_ARG for a NULL required pointer, a negative size, a
+ * misaligned pointer, a too-small workspace, or y / final_state overlapping any
+ * input or each other; SSM_ERR_UNSUPPORTED for N outside [1, 64] or a bad dtype;
+ * SSM_ERR_HIP when no device is usable or the launch fails.
+ */
+ssm_status ssm_selective_scan_fwd(
+    const void *u, const void *delta, const float *A, const void *Bm, const void *Cm,
+    const float *Dskip, const void *z, const float *delta_bias, int delta_softplus,
+    void *y, float *final_state,
+    int64_t batch, int64_t L, int64_t D, int64_t N, ssm_dtype dt,
+    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Same operation with an explicit kernel choice, for testing that every
+ * implementation agrees: SSM_SCAN_AUTO picks the fastest valid one;
+ * SSM_SCAN_SEQUENTIAL runs one thread per (b, d) channel stepping through time
+ * (the plain recurrence); SSM_SCAN_CHUNKED runs the chunked wave-scan kernel
+ * (returns SSM_ERR_UNSUPPORTED when the shape does not fit it).
+ * `tokens_per_lane` (0 = default) selects the chunked kernel's tokens per lane
+ * (8 or 16).  Other arguments as in ssm_selective_scan_fwd.
+ */
+typedef enum { SSM_SCAN_AUTO = 0, SSM_SCAN_SEQUENTIAL = 1, SSM_SCAN_CHUNKED = 2 } ssm_scan_variant;
+
+ssm_status ssm_selective_scan_fwd_variant(
+    const void *u, const void *delta, const float *A, const void *Bm, const void *Cm,
+    const float *Dskip, const void *z, const float *delta_bias, int delta_softplus,
+    void *y, float *final_state,
+    int64_t batch, int64_t L, int64_t D, int64_t N, ssm_dtype dt,
+    void *workspace, size_t workspace_bytes, void *stream,
+    int variant, int tokens_per_lane);
+
+/*
+ * One recurrent decode step (the O(1)-state generation mode): advances the
+ * state of `batch` sequences by one token with the same arithmetic as one step
+ * of the scan, started from state_in instead of zero.
+ *
+ *   state_in     : [batch][D][N] float32
+ *   state_out    : [batch][D][N] float32; may equal state_in (in place) but must
+ *                  not partially overlap it
+ *   u_t, delta_t, z_t : [batch][D] act (z_t NULL = no gate)
+ *   A            : [D][N] float32
+ *   B_t, C_t     : [batch][N] act
+ *   Dskip, delta_bias : [D] float32 or NULL
+ *   y_t          : out [batch][D] act
+ *
+ * Errors as for the scan; y_t overlapping any input or the state is invalid.
+ */
+ssm_status ssm_state_update(
+    const float *state_in, float *state_out,
+    const void *u_t, const void *delta_t, const float *A,
+    const void *B_t, const void *C_t,
+    const float *Dskip, const void *z_t, const float *delta_bias, int delta_softplus,
+    void *y_t,
+    int64_t batch, int64_t D, int64_t N, ssm_dtype dt, void *stream);
+
+/* Workspace bytes ssm_selective_scan_fwd needs for this shape (0 = none). */
+size_t ssm_selective_scan_workspace_size(int64_t batch, int64_t L, int64_t D, int64_t N,
+                                         ssm_dtype dt);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char *ssm_status_string(ssm_status s);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int ssm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSM_H */

@@ -1,0 +1,12 @@
+"""MI355X (gfx950) selective scan and recurrent decode step.
+
+The kernels and the C ABI live in libssm.so (include/ssm.h); this package is a
+thin binding over it.  Importing the package does not load the library; the
+first call does, and raises if the library has not been built.
+"""
+from ._lib import SsmError, load_library, LIB_PATH  # noqa: F401
+from ._lib import (SSM_SCAN_AUTO, SSM_SCAN_SEQUENTIAL, SSM_SCAN_CHUNKED)  # noqa: F401
+from .ops import selective_scan_fwd, state_update  # noqa: F401
+
+__all__ = ["selective_scan_fwd", "state_update", "SsmError", "load_library", "LIB_PATH",
+           "SSM_SCAN_AUTO", "SSM_SCAN_SEQUENTIAL", "SSM_SCAN_CHUNKED"]

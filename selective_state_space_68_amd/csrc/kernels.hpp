@@ -1,0 +1,57 @@
+// Internal launch interface between the C-ABI host layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssm {
+
+enum class Dt : int { F32 = 0, BF16 = 1 };
+
+struct ScanArgs {
+  const void* u;         // [batch][D][L] act
+  const void* delta;     // [batch][D][L] act (raw)
+  const float* A;        // [D][N]
+  const void* Bm;        // [batch][L][N] act
+  const void* Cm;        // [batch][L][N] act
+  const float* Dskip;    // [D] or null
+  const void* z;         // [batch][D][L] act or null
+  const float* bias;     // [D] or null
+  void* y;               // [batch][D][L] act
+  float* final_state;    // [batch][D][N] or null
+  int64_t batch, L, D;
+  int N;
+  int softplus;
+};
+
+struct StepArgs {
+  const float* state_in;  // [S][D][N]
+  float* state_out;       // [S][D][N]
+  const void* u;          // [S][D] act
+  const void* delta;      // [S][D] act
+  const float* A;         // [D][N]
+  const void* Bm;         // [S][N] act
+  const void* Cm;         // [S][N] act
+  const float* Dskip;     // [D] or null
+  const void* z;          // [S][D] act or null
+  const float* bias;      // [D] or null
+  void* y;                // [S][D] act
+  int64_t batch, D;
+  int N;
+  int softplus;
+};
+
+// One thread per (b, d) channel, sequential over time.  Any N in [1, 64].
+hipError_t launch_scan_sequential(const ScanArgs& a, Dt dt, hipStream_t s);
+
+// Chunked wave-scan kernel.  Returns hipErrorInvalidValue when the shape does not
+// fit (callers check chunked_supported first).
+bool chunked_supported(const ScanArgs& a, Dt dt, int tokens_per_lane);
+hipError_t launch_scan_chunked(const ScanArgs& a, Dt dt, int tokens_per_lane, hipStream_t s);
+
+// Writes zeros to final_state (the L == 0 scan).
+hipError_t launch_zero_state(float* p, int64_t n, hipStream_t s);
+
+hipError_t launch_state_update(const StepArgs& a, Dt dt, hipStream_t s);
+
+}  // namespace ssm

@@ -1,0 +1,198 @@
+// C-ABI host layer of libssm.so: argument validation, aliasing checks and
+// dispatch to the gfx950 kernels on the caller's stream.  No allocation, no
+// synchronisation, no global mutable state beyond a cached device probe.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+
+#include "../../include/ssm.h"
+#include "kernels.hpp"
+
+namespace {
+
+constexpr int kVersion = 10000;  // 1.0.0
+
+struct Span {
+  uintptr_t lo = 0, hi = 0;  // [lo, hi); empty when lo == hi
+  bool empty() const { return lo == hi; }
+};
+
+Span span(const void* p, uint64_t bytes) {
+  Span s;
+  s.lo = reinterpret_cast<uintptr_t>(p);
+  s.hi = s.lo + (p ? bytes : 0);
+  return s;
+}
+
+bool overlaps(const Span& a, const Span& b) {
+  if (a.empty() || b.empty()) return false;
+  return a.lo < b.hi && b.lo < a.hi;
+}
+
+bool mul_ok(uint64_t a, uint64_t b, uint64_t* out) { return !__builtin_mul_overflow(a, b, out); }
+
+bool aligned(const void* p, uintptr_t a) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// 1 = a device is usable, 0 = none; probed once per process.
+std::atomic<int> g_device_state{-1};
+
+ssm_status probe_device() {
+  int st = g_device_state.load(std::memory_order_relaxed);
+  if (st == 1) return SSM_OK;
+  if (st == 0) return SSM_ERR_HIP;
+  int count = 0;
+  const hipError_t e = hipGetDeviceCount(&count);
+  st = (e == hipSuccess && count > 0) ? 1 : 0;
+  if (e != hipSuccess) (void)hipGetLastError();
+  g_device_state.store(st, std::memory_order_relaxed);
+  return st ? SSM_OK : SSM_ERR_HIP;
+}
+
+ssm_status from_hip(hipError_t e) { return e == hipSuccess ? SSM_OK : SSM_ERR_HIP; }
+
+struct ScanSizes {
+  uint64_t act_bytes = 0, bc_bytes = 0, a_bytes = 0, vec_bytes = 0, state_bytes = 0;
+};
+
+ssm_status check_scan(const void* u, const void* delta, const float* A, const void* Bm, const void* Cm,
+                      const float* Dskip, const void* z, const float* delta_bias, int delta_softplus,
+                      const void* y, const float* final_state, int64_t batch, int64_t L, int64_t D,
+                      int64_t N, ssm_dtype dt, size_t workspace_bytes, ScanSizes* sz) {
+  if (dt != SSM_F32 && dt != SSM_BF16) return SSM_ERR_UNSUPPORTED;
+  if (batch < 0 || L < 0 || D < 0 || N < 0) return SSM_ERR_INVALID_ARG;
+  if (N < 1 || N > SSM_MAX_N) return SSM_ERR_UNSUPPORTED;
+  if (delta_softplus != 0 && delta_softplus != 1) return SSM_ERR_INVALID_ARG;
+  (void)workspace_bytes;  // no workspace is needed; any size (including 0) is accepted
+  const uint64_t e = dt == SSM_BF16 ? 2 : 4;
+  uint64_t bd, bdl, bl, bln, dn, bdn;
+  if (!mul_ok(batch, D, &bd) || !mul_ok(bd, L, &bdl) || !mul_ok(bdl, e, &sz->act_bytes) ||
+      !mul_ok(batch, L, &bl) || !mul_ok(bl, N, &bln) || !mul_ok(bln, e, &sz->bc_bytes) ||
+      !mul_ok(D, N, &dn) || !mul_ok(dn, 4, &sz->a_bytes) || !mul_ok(bd, N, &bdn) ||
+      !mul_ok(bdn, 4, &sz->state_bytes) || sz->act_bytes > (uint64_t(1) << 62))
+    return SSM_ERR_INVALID_ARG;
+  // Required pointers may be NULL only when the buffer they describe is empty.
+  if ((!u && sz->act_bytes) || (!delta && sz->act_bytes) || (!y && sz->act_bytes) ||
+      (!Bm && sz->bc_bytes) || (!Cm && sz->bc_bytes) || (!A && sz->a_bytes))
+    return SSM_ERR_INVALID_ARG;
+  sz->vec_bytes = static_cast<uint64_t>(D) * 4;
+  if (!aligned(u, e) || !aligned(delta, e) || !aligned(z, e) || !aligned(y, e) || !aligned(Bm, e) ||
+      !aligned(Cm, e) || !aligned(A, 4) || !aligned(Dskip, 4) || !aligned(delta_bias, 4) ||
+      !aligned(final_state, 4))
+    return SSM_ERR_INVALID_ARG;
+  const Span in[] = {span(u, sz->act_bytes),        span(delta, sz->act_bytes),
+                     span(z, sz->act_bytes),        span(A, sz->a_bytes),
+                     span(Bm, sz->bc_bytes),        span(Cm, sz->bc_bytes),
+                     span(Dskip, sz->vec_bytes),    span(delta_bias, sz->vec_bytes)};
+  const Span ys = span(y, sz->act_bytes);
+  const Span fs = span(final_state, sz->state_bytes);
+  for (const Span& s : in)
+    if (overlaps(ys, s) || overlaps(fs, s)) return SSM_ERR_INVALID_ARG;
+  if (overlaps(ys, fs)) return SSM_ERR_INVALID_ARG;
+  return SSM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ssm_status_string(ssm_status s) {
+  switch (s) {
+    case SSM_OK: return "SSM_OK: success";
+    case SSM_ERR_INVALID_ARG: return "SSM_ERR_INVALID_ARG: invalid argument (null pointer, negative size, misalignment or aliasing)";
+    case SSM_ERR_UNSUPPORTED: return "SSM_ERR_UNSUPPORTED: unsupported configuration (N outside [1, 64], dtype or variant)";
+    case SSM_ERR_HIP: return "SSM_ERR_HIP: HIP runtime error (no usable device, or launch failed)";
+  }
+  return "SSM: unknown status";
+}
+
+int ssm_version(void) { return kVersion; }
+
+size_t ssm_selective_scan_workspace_size(int64_t, int64_t, int64_t, int64_t, ssm_dtype) { return 0; }
+
+ssm_status ssm_selective_scan_fwd_variant(const void* u, const void* delta, const float* A, const void* Bm,
+                                          const void* Cm, const float* Dskip, const void* z,
+                                          const float* delta_bias, int delta_softplus, void* y,
+                                          float* final_state, int64_t batch, int64_t L, int64_t D,
+                                          int64_t N, ssm_dtype dt, void* workspace, size_t workspace_bytes,
+                                          void* stream, int variant, int tokens_per_lane) {
+  (void)workspace;
+  ScanSizes sz;
+  ssm_status st = check_scan(u, delta, A, Bm, Cm, Dskip, z, delta_bias, delta_softplus, y, final_state,
+                             batch, L, D, N, dt, workspace_bytes, &sz);
+  if (st != SSM_OK) return st;
+  if (variant != SSM_SCAN_AUTO && variant != SSM_SCAN_SEQUENTIAL && variant != SSM_SCAN_CHUNKED)
+    return SSM_ERR_UNSUPPORTED;
+  if (!(tokens_per_lane == 0 || tokens_per_lane == 8 || tokens_per_lane == 16)) return SSM_ERR_UNSUPPORTED;
+  if (batch == 0 || D == 0) return SSM_OK;  // nothing to compute or write
+  st = probe_device();
+  if (st != SSM_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (L == 0) return final_state ? from_hip(ssm::launch_zero_state(final_state, batch * D * N, s)) : SSM_OK;
+
+  ssm::ScanArgs a;
+  a.u = u; a.delta = delta; a.A = A; a.Bm = Bm; a.Cm = Cm; a.Dskip = Dskip; a.z = z;
+  a.bias = delta_bias; a.y = y; a.final_state = final_state;
+  a.batch = batch; a.L = L; a.D = D; a.N = static_cast<int>(N); a.softplus = delta_softplus;
+  const ssm::Dt d = dt == SSM_BF16 ? ssm::Dt::BF16 : ssm::Dt::F32;
+
+  if (variant == SSM_SCAN_SEQUENTIAL) return from_hip(ssm::launch_scan_sequential(a, d, s));
+  if (variant == SSM_SCAN_CHUNKED && !ssm::chunked_supported(a, d, tokens_per_lane)) return SSM_ERR_UNSUPPORTED;
+  if (ssm::chunked_supported(a, d, tokens_per_lane))
+    return from_hip(ssm::launch_scan_chunked(a, d, tokens_per_lane, s));
+  return from_hip(ssm::launch_scan_sequential(a, d, s));
+}
+
+ssm_status ssm_selective_scan_fwd(const void* u, const void* delta, const float* A, const void* Bm,
+                                  const void* Cm, const float* Dskip, const void* z, const float* delta_bias,
+                                  int delta_softplus, void* y, float* final_state, int64_t batch, int64_t L,
+                                  int64_t D, int64_t N, ssm_dtype dt, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  return ssm_selective_scan_fwd_variant(u, delta, A, Bm, Cm, Dskip, z, delta_bias, delta_softplus, y,
+                                        final_state, batch, L, D, N, dt, workspace, workspace_bytes, stream,
+                                        SSM_SCAN_AUTO, 0);
+}
+
+ssm_status ssm_state_update(const float* state_in, float* state_out, const void* u_t, const void* delta_t,
+                            const float* A, const void* B_t, const void* C_t, const float* Dskip,
+                            const void* z_t, const float* delta_bias, int delta_softplus, void* y_t,
+                            int64_t batch, int64_t D, int64_t N, ssm_dtype dt, void* stream) {
+  if (dt != SSM_F32 && dt != SSM_BF16) return SSM_ERR_UNSUPPORTED;
+  if (batch < 0 || D < 0 || N < 0) return SSM_ERR_INVALID_ARG;
+  if (N < 1 || N > SSM_MAX_N) return SSM_ERR_UNSUPPORTED;
+  if (delta_softplus != 0 && delta_softplus != 1) return SSM_ERR_INVALID_ARG;
+  const uint64_t e = dt == SSM_BF16 ? 2 : 4;
+  uint64_t bd, bdn, st_bytes, act_bytes, bn, bc_bytes, dn;
+  if (!mul_ok(batch, D, &bd) || !mul_ok(bd, N, &bdn) || !mul_ok(bdn, 4, &st_bytes) ||
+      !mul_ok(bd, e, &act_bytes) || !mul_ok(batch, N, &bn) || !mul_ok(bn, e, &bc_bytes) ||
+      !mul_ok(D, N, &dn) || st_bytes > (uint64_t(1) << 62))
+    return SSM_ERR_INVALID_ARG;
+  // Required pointers may be NULL only when the buffer they describe is empty.
+  if ((!state_in && st_bytes) || (!state_out && st_bytes) || (!u_t && act_bytes) || (!delta_t && act_bytes) ||
+      (!y_t && act_bytes) || (!B_t && bc_bytes) || (!C_t && bc_bytes) || (!A && dn))
+    return SSM_ERR_INVALID_ARG;
+  if (!aligned(state_in, 4) || !aligned(state_out, 4) || !aligned(A, 4) || !aligned(Dskip, 4) ||
+      !aligned(delta_bias, 4) || !aligned(u_t, e) || !aligned(delta_t, e) || !aligned(z_t, e) ||
+      !aligned(B_t, e) || !aligned(C_t, e) || !aligned(y_t, e))
+    return SSM_ERR_INVALID_ARG;
+  const Span sin = span(state_in, st_bytes), sout = span(state_out, st_bytes), ys = span(y_t, act_bytes);
+  const Span in[] = {span(u_t, act_bytes),         span(delta_t, act_bytes),    span(z_t, act_bytes),
+                     span(A, dn * 4),              span(B_t, bc_bytes),         span(C_t, bc_bytes),
+                     span(Dskip, uint64_t(D) * 4), span(delta_bias, uint64_t(D) * 4)};
+  for (const Span& s : in)
+    if (overlaps(ys, s) || overlaps(sout, s)) return SSM_ERR_INVALID_ARG;
+  if (overlaps(ys, sin) || overlaps(ys, sout)) return SSM_ERR_INVALID_ARG;
+  if (sin.lo != sout.lo && overlaps(sin, sout)) return SSM_ERR_INVALID_ARG;  // exact in-place only
+  if (batch == 0 || D == 0) return SSM_OK;  // nothing to compute or write
+  const ssm_status dst = probe_device();
+  if (dst != SSM_OK) return dst;
+
+  ssm::StepArgs a;
+  a.state_in = state_in; a.state_out = state_out; a.u = u_t; a.delta = delta_t; a.A = A; a.Bm = B_t;
+  a.Cm = C_t; a.Dskip = Dskip; a.z = z_t; a.bias = delta_bias; a.y = y_t;
+  a.batch = batch; a.D = D; a.N = static_cast<int>(N); a.softplus = delta_softplus;
+  return from_hip(ssm::launch_state_update(a, dt == SSM_BF16 ? ssm::Dt::BF16 : ssm::Dt::F32,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

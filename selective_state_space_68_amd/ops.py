@@ -1,0 +1,100 @@
+"""Torch-facing wrappers of the C ABI: allocation, pointer and stream marshalling.
+
+Torch is used for device memory and streams only; the arithmetic happens in
+libssm.so.  Activations (u, delta, z, B, C and the outputs y) are float32 or
+bfloat16 CUDA/HIP tensors of one dtype; A, D, delta_bias and states are float32.
+Layouts: u, delta, z [batch, D, L]; B, C [batch, L, N]; A [D, N]; D, bias [D].
+"""
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return _lib.SSM_F32
+    if t.dtype == torch.bfloat16:
+        return _lib.SSM_BF16
+    raise TypeError(f"activations must be float32 or bfloat16, got {t.dtype}")
+
+
+def _ptr(t: Optional[torch.Tensor], name: str, dtype=None, device=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live on the GPU")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True, *,
+                       y=None, final_state=None, return_final_state=True, variant=0,
+                       tokens_per_lane=0, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Selective scan forward.  Returns (y [batch, D, L], final_state [batch, D, N] or None)."""
+    lib = _lib.load_library()
+    if u.dim() != 3 or B.dim() != 3 or A.dim() != 2:
+        raise ValueError("expected u [batch, D, L], B/C [batch, L, N], A [D, N]")
+    batch, Dc, L = u.shape
+    N = A.shape[1]
+    act = u.dtype
+    dev = u.device
+    if tuple(delta.shape) != (batch, Dc, L) or tuple(A.shape) != (Dc, N):
+        raise ValueError("delta / A shape mismatch")
+    if tuple(B.shape) != (batch, L, N) or tuple(C.shape) != (batch, L, N):
+        raise ValueError("B / C must be [batch, L, N]")
+    if z is not None and tuple(z.shape) != (batch, Dc, L):
+        raise ValueError("z must be [batch, D, L]")
+    for name, v in (("D", D), ("delta_bias", delta_bias)):
+        if v is not None and tuple(v.shape) != (Dc,):
+            raise ValueError(f"{name} must be [D]")
+    if y is None:
+        y = torch.empty((batch, Dc, L), dtype=act, device=dev)
+    if final_state is None and return_final_state:
+        final_state = torch.empty((batch, Dc, N), dtype=torch.float32, device=dev)
+    st = lib.ssm_selective_scan_fwd_variant(
+        _ptr(u, "u", act, dev), _ptr(delta, "delta", act, dev), _ptr(A, "A", torch.float32, dev),
+        _ptr(B, "B", act, dev), _ptr(C, "C", act, dev), _ptr(D, "D", torch.float32, dev),
+        _ptr(z, "z", act, dev), _ptr(delta_bias, "delta_bias", torch.float32, dev),
+        1 if delta_softplus else 0, _ptr(y, "y", act, dev),
+        _ptr(final_state, "final_state", torch.float32, dev),
+        batch, L, Dc, N, _dt(u), None, 0, _stream(stream), int(variant), int(tokens_per_lane))
+    _lib.check(st)
+    return y, final_state
+
+
+def state_update(state, u_t, delta_t, A, B_t, C_t, D=None, z_t=None, delta_bias=None,
+                 delta_softplus=True, *, out_state=None, y=None, stream=None) -> torch.Tensor:
+    """One decode step.  Updates `out_state` (default: `state`, in place); returns y_t [S, D]."""
+    lib = _lib.load_library()
+    S, Dc, N = state.shape
+    act = u_t.dtype
+    dev = state.device
+    if out_state is None:
+        out_state = state
+    if y is None:
+        y = torch.empty((S, Dc), dtype=act, device=dev)
+    st = lib.ssm_state_update(
+        _ptr(state, "state", torch.float32, dev), _ptr(out_state, "out_state", torch.float32, dev),
+        _ptr(u_t, "u_t", act, dev), _ptr(delta_t, "delta_t", act, dev), _ptr(A, "A", torch.float32, dev),
+        _ptr(B_t, "B_t", act, dev), _ptr(C_t, "C_t", act, dev), _ptr(D, "D", torch.float32, dev),
+        _ptr(z_t, "z_t", act, dev), _ptr(delta_bias, "delta_bias", torch.float32, dev),
+        1 if delta_softplus else 0, _ptr(y, "y", act, dev), S, Dc, N, _dt(u_t), _stream(stream))
+    _lib.check(st)
+    return y

@@ -1,0 +1,141 @@
+"""C-ABI tests that need no GPU: the library loads, exports every declared entry
+point, and rejects bad arguments with the documented status before touching a
+device.  Pointers here are fake addresses; no call reaches a kernel launch.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from selective_state_space_68_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssm.h")
+
+F = 0x10000          # fake, 64 KiB-aligned device addresses, never dereferenced
+MB = 1 << 20
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssm_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert {"ssm_selective_scan_fwd", "ssm_state_update", "ssm_status_string"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in _lib.SIGNATURES, f"binding lacks {n}"
+
+
+def test_version_and_status_strings(lib):
+    assert lib.ssm_version() == 10000
+    for s in range(4):
+        assert lib.ssm_status_string(s).decode().startswith(("SSM_OK", "SSM_ERR"))
+    assert b"unknown" in lib.ssm_status_string(99)
+    assert lib.ssm_selective_scan_workspace_size(2, 2048, 1536, 16, 0) == 0
+
+
+def _scan(lib, **kw):
+    a = dict(u=F, delta=F + 1 * 64 * MB, A=F + 2 * 64 * MB, B=F + 3 * 64 * MB, C=F + 4 * 64 * MB,
+             Dskip=None, z=None, bias=None, softplus=1, y=F + 5 * 64 * MB, final=F + 6 * 64 * MB,
+             batch=1, L=64, D=16, N=4, dt=0, variant=0, kpl=0)
+    a.update(kw)
+    return lib.ssm_selective_scan_fwd_variant(a["u"], a["delta"], a["A"], a["B"], a["C"], a["Dskip"], a["z"],
+                                              a["bias"], a["softplus"], a["y"], a["final"], a["batch"], a["L"],
+                                              a["D"], a["N"], a["dt"], None, 0, None, a["variant"], a["kpl"])
+
+
+def _step(lib, **kw):
+    a = dict(sin=F, sout=F + 1 * 64 * MB, u=F + 2 * 64 * MB, delta=F + 3 * 64 * MB, A=F + 4 * 64 * MB,
+             B=F + 5 * 64 * MB, C=F + 6 * 64 * MB, Dskip=None, z=None, bias=None, softplus=1,
+             y=F + 7 * 64 * MB, batch=4, D=8, N=16, dt=1)
+    a.update(kw)
+    return lib.ssm_state_update(a["sin"], a["sout"], a["u"], a["delta"], a["A"], a["B"], a["C"], a["Dskip"],
+                                a["z"], a["bias"], a["softplus"], a["y"], a["batch"], a["D"], a["N"], a["dt"],
+                                None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(u=None), _lib.SSM_ERR_INVALID_ARG),
+    (dict(y=None), _lib.SSM_ERR_INVALID_ARG),
+    (dict(A=None), _lib.SSM_ERR_INVALID_ARG),
+    (dict(batch=-1), _lib.SSM_ERR_INVALID_ARG),
+    (dict(L=-5), _lib.SSM_ERR_INVALID_ARG),
+    (dict(N=0), _lib.SSM_ERR_UNSUPPORTED),
+    (dict(N=65), _lib.SSM_ERR_UNSUPPORTED),
+    (dict(dt=7), _lib.SSM_ERR_UNSUPPORTED),
+    (dict(softplus=2), _lib.SSM_ERR_INVALID_ARG),
+    (dict(variant=9), _lib.SSM_ERR_UNSUPPORTED),
+    (dict(kpl=12), _lib.SSM_ERR_UNSUPPORTED),
+    (dict(u=F + 2), _lib.SSM_ERR_INVALID_ARG),                       # misaligned f32
+    (dict(dt=1, u=F + 1), _lib.SSM_ERR_INVALID_ARG),                 # misaligned bf16
+    (dict(y=F), _lib.SSM_ERR_INVALID_ARG),                           # y aliases u
+    (dict(y=F + 4 * 64 * MB + 128), _lib.SSM_ERR_INVALID_ARG),       # y overlaps C
+    (dict(final=F + 2 * 64 * MB), _lib.SSM_ERR_INVALID_ARG),         # final state aliases A
+    (dict(final=F + 5 * 64 * MB + 64), _lib.SSM_ERR_INVALID_ARG),    # final state overlaps y
+    (dict(batch=1 << 40, L=1 << 40), _lib.SSM_ERR_INVALID_ARG),      # size overflow
+])
+def test_scan_argument_errors(lib, kw, status):
+    assert _scan(lib, **kw) == status
+
+
+def test_scan_empty_inputs_are_noops(lib):
+    assert _scan(lib, batch=0) == _lib.SSM_OK
+    assert _scan(lib, D=0) == _lib.SSM_OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(sin=None), _lib.SSM_ERR_INVALID_ARG),
+    (dict(y=None), _lib.SSM_ERR_INVALID_ARG),
+    (dict(N=0), _lib.SSM_ERR_UNSUPPORTED),
+    (dict(N=100), _lib.SSM_ERR_UNSUPPORTED),
+    (dict(D=-1), _lib.SSM_ERR_INVALID_ARG),
+    (dict(sout=F + 16), _lib.SSM_ERR_INVALID_ARG),                   # partial overlap of state
+    (dict(y=F + 64), _lib.SSM_ERR_INVALID_ARG),                      # y inside the state
+    (dict(sout=F + 2 * 64 * MB), _lib.SSM_ERR_INVALID_ARG),          # state_out aliases u_t
+    (dict(u=F + 2 * 64 * MB + 1), _lib.SSM_ERR_INVALID_ARG),         # misaligned bf16
+    (dict(dt=5), _lib.SSM_ERR_UNSUPPORTED),
+])
+def test_state_update_argument_errors(lib, kw, status):
+    assert _step(lib, **kw) == status
+
+
+def test_state_update_empty_is_noop(lib):
+    assert _step(lib, batch=0) == _lib.SSM_OK
+
+
+def _no_gpu():
+    try:
+        import torch
+        return torch.cuda.device_count() == 0
+    except Exception:
+        return True
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="forces the no-device path; only meaningful without a GPU")
+def test_valid_call_without_device_reports_hip_error(lib):
+    # Valid arguments reach the device probe, which fails cleanly (no launch happens).
+    assert _scan(lib) == _lib.SSM_ERR_HIP
+    assert _step(lib, sout=F) == _lib.SSM_ERR_HIP          # exact in-place is valid
+    with pytest.raises(_lib.SsmError) as ei:
+        _lib.check(_lib.SSM_ERR_HIP)
+    assert ei.value.status == _lib.SSM_ERR_HIP
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    saved = _lib._lib
+    _lib._lib = None
+    try:
+        with pytest.raises(RuntimeError, match="missing"):
+            _lib.load_library(str(tmp_path / "nope.so"))
+    finally:
+        _lib._lib = saved

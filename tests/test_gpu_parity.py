@@ -1,0 +1,272 @@
+"""GPU parity: the HIP library against the float64 oracle, through the C ABI.
+
+Tolerance (max row-relative error, see ssm_metrics): 1e-4 for float32
+activations, 2e-2 for bfloat16 activations with float32 state.  The five named
+workloads run at full size in the launch configuration the benchmark times;
+where the oracle would take minutes, it checks a sample of channels (each one a
+complete time series).  Edge shapes cover single tokens, ragged tails, N outside
+the vector path, missing optional inputs, and every kernel variant.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import TOL, dev, host, oracle_scan, run_scan, sample_channels, upload_scan
+from ssm_metrics import row_rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+def _need_gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    _need_gpu()
+    from selective_state_space_68_amd import load_library
+    load_library()
+
+
+def _check(y, fs, ry, rf, dtype, what=""):
+    ey, ef = row_rel_err(y, ry), row_rel_err(fs, rf)
+    print(f"{what} y_err={ey:.3e} state_err={ef:.3e} tol={TOL[dtype]:.0e}", flush=True)
+    assert ey <= TOL[dtype], (what, ey)
+    assert ef <= TOL[dtype], (what, ef)
+
+
+# ------------------------------------------------------------------ named workloads
+
+def test_tiny_f32_all_variants():
+    cfg = synth.CONFIGS["tiny_f32"]
+    inp = synth.make_config_inputs(cfg)
+    ry, rf = oracle_scan(inp)
+    t = upload_scan(inp)
+    for variant, kpl in ((0, 0), (1, 0), (2, 8), (2, 16)):
+        y, fs = run_scan(inp, t, variant=variant, tokens_per_lane=kpl)
+        _check(host(y), host(fs), ry, rf, cfg.dtype, f"tiny v{variant}/{kpl}")
+
+
+def test_mamba130m_f32_full():
+    cfg = synth.CONFIGS["mamba130m_f32"]
+    inp = synth.make_config_inputs(cfg)
+    y, fs = run_scan(inp)
+    ry, rf = oracle_scan(inp)
+    _check(host(y), host(fs), ry, rf, cfg.dtype, "mamba130m")
+
+
+@pytest.mark.parametrize("name,k", [("mamba1p4b_bf16", 48), ("long131k_bf16", 10)])
+def test_bf16_workloads_sampled(name, k):
+    cfg = synth.CONFIGS[name]
+    inp = synth.make_config_inputs(cfg)
+    y, fs = run_scan(inp)
+    yh, fh = host(y), host(fs)
+    del y, fs
+    chans = sample_channels(cfg.batch, cfg.D, k, seed=1)
+    ry, rf = oracle_scan(inp, chans)
+    ys = np.stack([yh[b, d] for b, d in chans])
+    fss = np.stack([fh[b, d] for b, d in chans])
+    _check(ys, fss, ry, rf, cfg.dtype, name)
+    # the end of a long sequence is where accumulated error would show
+    tail = max(1, cfg.L // 64)
+    assert row_rel_err(ys[:, -tail:], ry[:, -tail:]) <= TOL[cfg.dtype]
+    # every output is finite (no channel left unwritten with garbage/NaN)
+    assert np.isfinite(yh).all() and np.isfinite(fh).all()
+
+
+def test_decode_workload_512_steps():
+    import torch
+    from selective_state_space_68_amd import state_update
+    cfg = synth.CONFIGS["decode_bf16"]
+    S, D, N = cfg.batch, cfg.D, cfg.N
+    A, Dsk, bias = synth.make_decode_params(S, D, N, seed=cfg.seed)
+    st0 = synth.make_decode_state(S, D, N, seed=cfg.seed)
+    state = dev(st0)
+    tA, tD, tb = dev(A), dev(Dsk), dev(bias)
+    chans = sample_channels(S, D, 64, seed=2)
+    sidx = np.array([c[0] for c in chans])
+    didx = np.array([c[1] for c in chans])
+    ys_gpu = []
+    h_ref = st0[sidx, didx].astype(np.float64)[:, None, :]       # [k, 1, N]
+    ys_ref = []
+    for step in range(cfg.steps):
+        x = synth.make_decode_step(S, D, N, step, cfg.dtype, cfg.gate, seed=cfg.seed)
+        y = state_update(state, dev(x.dev["u"]), dev(x.dev["delta"]), tA, dev(x.dev["B"]), dev(x.dev["C"]),
+                         tD, dev(x.dev["z"]), tb, True)
+        ys_gpu.append(host(y)[sidx, didx])
+        # oracle on the sampled channels: each (s, d) is a 1-sequence, 1-channel problem
+        yr, h_ref = _decode_ref(h_ref, x, sidx, didx, A, Dsk, bias)
+        ys_ref.append(yr)
+    torch.cuda.synchronize()
+    fin = host(state)[sidx, didx]
+    _check(np.stack(ys_gpu, 1), fin, np.stack(ys_ref, 1), h_ref[:, 0, :], cfg.dtype, "decode512")
+
+
+def _decode_ref(h, x, sidx, didx, A, Dsk, bias):
+    """Oracle step for k independent (s, d) channels, each as its own 1 x 1 problem."""
+    k = len(sidx)
+    ys = np.empty(k)
+    hn = np.empty_like(h)
+    for i, (s, d) in enumerate(zip(sidx, didx)):
+        y, hh = oracle.state_update(h[i:i + 1], x.u[s:s + 1, d:d + 1], x.delta[s:s + 1, d:d + 1],
+                                    A[d:d + 1], x.B[s:s + 1], x.C[s:s + 1], Dsk[d:d + 1],
+                                    x.z[s:s + 1, d:d + 1], bias[d:d + 1], True)
+        ys[i] = y[0, 0]
+        hn[i] = hh[0]
+    return ys, hn
+
+
+# ------------------------------------------------------------------ edge shapes
+
+EDGE = [
+    # batch, L, D, N, dtype, gate, d_skip, bias, softplus
+    (1, 1, 1, 1, "f32", True, "normal", True, True),
+    (1, 2, 3, 4, "bf16", False, "none", False, True),
+    (2, 63, 5, 16, "f32", True, "ones", True, True),
+    (1, 65, 4, 16, "bf16", True, "normal", True, True),
+    (2, 1000, 6, 16, "f32", False, "normal", True, False),
+    (1, 1024, 4, 16, "bf16", True, "ones", True, True),
+    (1, 1025, 9, 16, "f32", True, "ones", True, True),
+    (1, 2056, 3, 8, "bf16", True, "normal", True, True),
+    (2, 300, 5, 3, "f32", True, "normal", True, True),
+    (1, 129, 2, 17, "f32", True, "normal", False, True),
+    (1, 520, 3, 64, "f32", True, "normal", True, True),
+    (1, 96, 7, 64, "bf16", False, "normal", True, True),
+    (3, 4100, 2, 5, "bf16", True, "normal", True, True),
+]
+
+
+@pytest.mark.parametrize("shape", EDGE, ids=lambda s: "x".join(map(str, s[:4])) + f"-{s[4]}")
+def test_edge_shapes_all_variants(shape):
+    batch, L, D, N, dtype, gate, dsk, bias, sp = shape
+    inp = synth.make_scan_inputs(batch, L, D, N, dtype, gate=gate, d_skip=dsk, seed=L + D + N,
+                                 a_kind="lognormal", with_bias=bias, delta_softplus=sp)
+    ry, rf = oracle_scan(inp)
+    t = upload_scan(inp)
+    for variant, kpl in ((0, 0), (1, 0), (2, 8), (2, 16)):
+        y, fs = run_scan(inp, t, variant=variant, tokens_per_lane=kpl)
+        _check(host(y), host(fs), ry, rf, dtype, f"{shape} v{variant}/{kpl}")
+
+
+def test_no_final_state_and_zero_length():
+    import torch
+    from selective_state_space_68_amd import selective_scan_fwd
+    inp = synth.make_scan_inputs(2, 40, 3, 4, "f32", seed=5)
+    t = upload_scan(inp)
+    y, fs = selective_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["bias"],
+                               return_final_state=False)
+    assert fs is None
+    ry, _ = oracle_scan(inp)
+    assert row_rel_err(host(y), ry) <= TOL["f32"]
+    # L = 0: the final state is the zero initial state
+    e = torch.empty((2, 3, 0), device="cuda")
+    fs0 = torch.full((2, 3, 4), 7.0, device="cuda")
+    selective_scan_fwd(e, e.clone(), t["A"], torch.empty((2, 0, 4), device="cuda"),
+                       torch.empty((2, 0, 4), device="cuda"), final_state=fs0)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(fs0).item() == 0
+
+
+def test_unaligned_views_take_the_scalar_path():
+    """Offset (but element-aligned) pointers must give the same answer."""
+    import torch
+    from selective_state_space_68_amd import selective_scan_fwd
+    inp = synth.make_scan_inputs(1, 200, 3, 16, "bf16", seed=8)
+    t = upload_scan(inp)
+    ref, reff = run_scan(inp, t)
+    sh = {}
+    for k in ("u", "delta", "z"):
+        buf = torch.empty(t[k].numel() + 1, dtype=t[k].dtype, device="cuda")
+        buf[1:] = t[k].reshape(-1)
+        sh[k] = buf[1:].view(t[k].shape)
+    y, fs = selective_scan_fwd(sh["u"], sh["delta"], t["A"], t["B"], t["C"], t["D"], sh["z"], t["bias"])
+    torch.cuda.synchronize()
+    assert row_rel_err(host(y), host(ref)) <= 1e-6 and row_rel_err(host(fs), host(reff)) <= 1e-6
+
+
+# ------------------------------------------------------------------ limits and invariants
+
+def test_forget_limit_softplus_overflow_path():
+    inp = synth.make_scan_inputs(1, 300, 4, 16, "f32", gate=False, d_skip="normal", seed=3, with_bias=False)
+    inp.delta = np.full_like(inp.delta, 200.0)
+    inp.refresh()
+    y, fs = run_scan(inp)
+    ry, rf = oracle_scan(inp)
+    _check(host(y), host(fs), ry, rf, "f32", "forget")
+
+
+def test_hold_limit_decode_is_bitwise_identity():
+    import torch
+    from selective_state_space_68_amd import state_update
+    S, D, N = 8, 40, 16
+    st = dev(np.random.default_rng(0).standard_normal((S, D, N)).astype(np.float32))
+    before = st.clone()
+    A, Dsk, _ = synth.make_decode_params(S, D, N)
+    x = synth.make_decode_step(S, D, N, 0, "f32", True)
+    zero = torch.zeros((S, D), device="cuda")
+    state_update(st, dev(x.u), zero, dev(A), dev(x.B), dev(x.C), dev(Dsk), dev(x.z), None, False)
+    torch.cuda.synchronize()
+    assert torch.equal(st, before)
+
+
+def test_deterministic_bitwise():
+    import torch
+    inp = synth.make_scan_inputs(2, 2048, 64, 16, "bf16", seed=13)
+    t = upload_scan(inp)
+    y1, f1 = run_scan(inp, t)
+    y2, f2 = run_scan(inp, t)
+    assert torch.equal(y1, y2) and torch.equal(f1, f2)
+
+
+def test_scan_then_decode_matches_longer_scan():
+    import torch
+    from selective_state_space_68_amd import state_update
+    k = 6
+    inp = synth.make_scan_inputs(2, 700, 5, 16, "f32", seed=17, a_kind="lognormal")
+    y_full, f_full = run_scan(inp)
+    head = synth.make_scan_inputs(2, 700, 5, 16, "f32", seed=17, a_kind="lognormal")
+    for name in ("u", "delta", "z"):
+        setattr(head, name, np.ascontiguousarray(getattr(inp, name)[:, :, :-k]))
+    for name in ("B", "C"):
+        setattr(head, name, np.ascontiguousarray(getattr(inp, name)[:, :-k]))
+    head.L = inp.L - k
+    head.refresh()
+    _, state = run_scan(head)
+    ys = []
+    for j in range(inp.L - k, inp.L):
+        ys.append(host(state_update(state, dev(inp.u[:, :, j].copy()), dev(inp.delta[:, :, j].copy()),
+                                    dev(inp.A), dev(inp.B[:, j].copy()), dev(inp.C[:, j].copy()),
+                                    dev(inp.Dskip), dev(inp.z[:, :, j].copy()), dev(inp.delta_bias))))
+    torch.cuda.synchronize()
+    yf = host(y_full)[:, :, -k:]
+    assert row_rel_err(np.stack(ys, -1), yf) <= TOL["f32"]
+    assert row_rel_err(host(state), host(f_full)) <= TOL["f32"]
+
+
+def test_causality_bitwise():
+    import torch
+    inp = synth.make_scan_inputs(1, 3000, 4, 16, "f32", seed=19)
+    y1, _ = run_scan(inp)
+    t0 = 1500
+    inp.u[:, :, t0] += 1.0
+    inp.refresh()
+    y2, _ = run_scan(inp)
+    assert torch.equal(y1[:, :, :t0], y2[:, :, :t0])
+    assert not torch.equal(y1[:, :, t0], y2[:, :, t0])
+
+
+def test_channel_permutation_and_batch_independence():
+    import torch
+    inp = synth.make_scan_inputs(2, 1500, 8, 16, "bf16", seed=23)
+    y, fs = run_scan(inp)
+    perm = np.array([3, 7, 0, 5, 1, 2, 6, 4])
+    p = synth.make_scan_inputs(2, 1500, 8, 16, "bf16", seed=23)
+    for name in ("u", "delta", "z"):
+        setattr(p, name, np.ascontiguousarray(getattr(inp, name)[:, perm]))
+    p.A, p.Dskip, p.delta_bias = inp.A[perm].copy(), inp.Dskip[perm].copy(), inp.delta_bias[perm].copy()
+    p.refresh()
+    yp, fp = run_scan(p)
+    assert torch.equal(yp, y[:, perm]) and torch.equal(fp, fs[:, perm])
