@@ -32,6 +32,7 @@ import synth  # noqa: E402
 
 PEAK_HBM_GBS = 8000.0
 MALL_BYTES = 256 << 20
+CALIB_BYTES = 256 << 20
 DEFAULT_WORKLOAD = "mamba130m_f32"
 KERNEL_SRC = {"scan": "selective_state_space_68_amd/csrc/scan_chunked.hip",
               "decode": "selective_state_space_68_amd/csrc/state_update.hip"}
@@ -111,6 +112,10 @@ def bench_scan(args, torch, lib_ops):
     nbytes = cfg.algorithmic_bytes()
     sets = args.sets or max(2, int(np.ceil(600e6 / nbytes)))
     A, Dk, bias = dev(torch, inp.A), dev(torch, inp.Dskip), dev(torch, inp.delta_bias)
+    # one scratch buffer (packed B/C tiles) shared by all steps: they run in stream order
+    ws = torch.empty(max(1, lib_ops.workspace_bytes(cfg.batch, cfg.L, cfg.D, cfg.N,
+                                                    torch.bfloat16 if cfg.dtype == "bf16" else torch.float32)),
+                     dtype=torch.uint8, device="cuda")
     bufs = []
     for _ in range(sets):
         t = {k: dev(torch, inp.upload_array(k)) if inp.upload_array(k) is not None else None
@@ -122,7 +127,7 @@ def bench_scan(args, torch, lib_ops):
     def step(i):
         t = bufs[i % sets]
         lib_ops.selective_scan_fwd(t["u"], t["delta"], A, t["B"], t["C"], Dk, t["z"], bias, True,
-                                   y=t["y"], final_state=t["fs"], variant=args.variant,
+                                   y=t["y"], final_state=t["fs"], workspace=ws, variant=args.variant,
                                    tokens_per_lane=args.kpl)
 
     return cfg, inp, nbytes, cfg.elements, sets, step, bufs
@@ -180,6 +185,14 @@ def main():
     cfg, inp, nbytes, elements, sets, step, bufs = maker(args, torch, lib_ops)
     print(f"# workload {args.workload}: {elements:.3e} elements/step, {nbytes / 1e6:.2f} MB/step "
           f"algorithmic, {sets} input copies", file=sys.stderr, flush=True)
+
+    # A plain device-to-device copy of known size (256 MiB read + 256 MiB written):
+    # the calibration that HBM-byte counters (FETCH_SIZE / WRITE_SIZE) are scaled by.
+    calib_src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
+    calib_dst = torch.empty_like(calib_src)
+    calib_dst.copy_(calib_src)
+    torch.cuda.synchronize()
+    del calib_src, calib_dst
 
     stream = torch.cuda.current_stream()
     for i in range(args.warmup):

@@ -70,13 +70,18 @@ typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
  *   final_state  : out [batch][D][N] float32, h[b, L-1, d, :], or NULL
  *   batch, L, D  : >= 0 (a zero size is a no-op; with L == 0 the final state is 0)
  *   N            : 1..64
- *   workspace    : caller scratch of ssm_selective_scan_workspace_size() bytes,
- *                  may be NULL when that size is 0
+ *   workspace    : device scratch owned by the caller, 16-byte aligned, at least
+ *                  ssm_selective_scan_workspace_size() bytes (the chunked kernel
+ *                  packs B and C there as float32 tiles); may be NULL when that
+ *                  size is 0 or the sequential kernel is selected.  Its contents
+ *                  are overwritten; it must not overlap any other argument, and
+ *                  calls that share one workspace must not run concurrently.
  *
  * Errors: SSM_ERR_INVALID_ARG for a NULL required pointer, a negative size, a
- * misaligned pointer, a too-small workspace, or y / final_state overlapping any
- * input or each other; SSM_ERR_UNSUPPORTED for N outside [1, 64] or a bad dtype;
- * SSM_ERR_HIP when no device is usable or the launch fails.
+ * misaligned pointer, a missing or too-small workspace, or y / final_state /
+ * workspace overlapping any input or each other; SSM_ERR_UNSUPPORTED for N
+ * outside [1, 64] or a bad dtype; SSM_ERR_HIP when no device is usable or the
+ * launch fails.
  */
 ssm_status ssm_selective_scan_fwd(
     const void *u, const void *delta, const float *A, const void *Bm, const void *Cm,
@@ -128,7 +133,9 @@ ssm_status ssm_state_update(
     void *y_t,
     int64_t batch, int64_t D, int64_t N, ssm_dtype dt, void *stream);
 
-/* Workspace bytes ssm_selective_scan_fwd needs for this shape (0 = none). */
+/* Workspace bytes ssm_selective_scan_fwd needs for this shape: the packed B/C
+ * tiles of the chunked kernel, batch * ceil(L / 1024) * 1024 * N * 8 bytes (0 for
+ * an empty or invalid shape).  Enough for every variant and tokens_per_lane. */
 size_t ssm_selective_scan_workspace_size(int64_t batch, int64_t L, int64_t D, int64_t N,
                                          ssm_dtype dt);
 

@@ -64,12 +64,20 @@ __device__ __forceinline__ void store_act<ActBF16>(void* p, int64_t i, float v) 
 // 2^x on the transcendental unit (v_exp_f32).
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// log(1 + e^x) = max(x, 0) + log1p(e^-|x|): no overflow for large x and, through
-// an accurate log1p, full relative accuracy for the small steps the scan sees
-// (a plain log(1 + e^x) loses ~3e-4 relative at e^x ~ 2e-4).
+constexpr float kLn2 = 0.69314718055994531f;
+
+// softplus(x) = log(1 + e^x) = max(x, 0) + log1p(e) with e = e^-|x| in (0, 1]: no
+// overflow for large x.  log1p(e) is evaluated as ln(w) + (e - (w - 1)) with
+// w = fl(1 + e): the second term is the exact rounding error of 1 + e (w - 1 is
+// exact by Sterbenz), which restores the low bits of e that w lost, and the
+// first-order remainder is below |rounding error| * e.  With the hardware log2
+// this keeps ~1e-6 relative accuracy even where e ~ 1e-4, where a plain
+// log(1 + e^x) in float32 is off by ~3e-4.
 __device__ __forceinline__ float softplus_f(float x) {
   const float e = exp2_hw(-fabsf(x) * kLog2e);
-  return fmaxf(x, 0.0f) + log1pf(e);
+  const float w = 1.0f + e;
+  const float err = e - (w - 1.0f);
+  return fmaxf(x, 0.0f) + __builtin_fmaf(__builtin_amdgcn_logf(w), kLn2, err);
 }
 
 // SiLU(z) = z / (1 + e^-z); e^-z = inf for very negative z gives -0.
@@ -87,31 +95,43 @@ __device__ __forceinline__ float dpp_mov(float old, float v) {
                                          CTRL, ROW_MASK, 0xf, BOUND_ZERO));
 }
 
-// One Kogge-Stone step of the inclusive scan of (a, b) pairs under the operator
-// (a1, b1) then (a2, b2) = (a2 a1, a2 b1 + b2).  Lanes whose source lane is out
-// of range (or whose row is masked off) combine with the identity (1, 0).
-template <int CTRL, int ROW_MASK, bool UPDATE_A>
-__device__ __forceinline__ void scan_step(float& a, float& b) {
-  const float bs = dpp_mov<CTRL, ROW_MASK, false>(0.0f, b);
-  if (UPDATE_A) {
-    const float as = dpp_mov<CTRL, ROW_MASK, false>(1.0f, a);
-    b = __builtin_fmaf(a, bs, b);
-    a = a * as;
-  } else {
-    b = __builtin_fmaf(a, bs, b);
-  }
-}
-
-// Inclusive scan across the 64 lanes of a wave.  On return b holds, in lane i,
-// the composition of lanes 0..i applied to zero; `a` is left partially combined
-// (its final value is not needed by the callers).
+// Inclusive scan across the 64 lanes of a wave of (a, b) pairs under the operator
+// (a1, b1) then (a2, b2) = (a2 a1, a2 b1 + b2): Kogge-Stone with the row shifts
+// 1, 2, 4, 8 and the two row broadcasts (15 -> rows 1, 3; 31 -> rows 2, 3).
+// On return lane i's b is the composition of lanes 0..i applied to zero (its a is
+// a scratch value: the final decay product is not needed by the callers).
+//
+// Each step is one in-place DPP instruction per component:
+//   v_fmac_f32_dpp b, b(src lane), a   ->  b = a * b_src + b
+//   v_mul_f32_dpp  a, a(src lane), a   ->  a = a_src * a
+// with bound_ctrl off, so a lane whose source is outside its row (or whose row
+// is masked off in the broadcasts) is not written: it keeps (a, b), which is
+// exactly combining with the identity (1, 0).  The compiler does not form these
+// in-place DPP operations itself, hence the asm.  gfx9 needs two wait states
+// between a VALU write and a DPP read of the same VGPR: one s_nop 0 between steps
+// (plus the other component's instruction), s_nop 1 on entry and exit because
+// the surrounding code is compiler-scheduled.  Pure VALU, no memory access.
 __device__ __forceinline__ void wave_scan_pairs(float& a, float& b) {
-  scan_step<0x111, 0xf, true>(a, b);   // row_shr:1
-  scan_step<0x112, 0xf, true>(a, b);   // row_shr:2
-  scan_step<0x114, 0xf, true>(a, b);   // row_shr:4
-  scan_step<0x118, 0xf, true>(a, b);   // row_shr:8
-  scan_step<0x142, 0xa, true>(a, b);   // row_bcast:15 into rows 1, 3
-  scan_step<0x143, 0xc, false>(a, b);  // row_bcast:31 into rows 2, 3
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %0, %0, %1 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %1, %1, %1 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 0\n\t"
+      "v_fmac_f32_dpp %0, %0, %1 row_shr:2 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %1, %1, %1 row_shr:2 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 0\n\t"
+      "v_fmac_f32_dpp %0, %0, %1 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %1, %1, %1 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 0\n\t"
+      "v_fmac_f32_dpp %0, %0, %1 row_shr:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %1, %1, %1 row_shr:8 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 0\n\t"
+      "v_fmac_f32_dpp %0, %0, %1 row_bcast:15 row_mask:0xa bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %1, %1, %1 row_bcast:15 row_mask:0xa bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %0, %0, %1 row_bcast:31 row_mask:0xc bank_mask:0xf\n\t"
+      "s_nop 1"
+      : "+v"(b), "+v"(a));
 }
 
 // Value of lane i-1 in lane i; lane 0 receives `lane0`.

@@ -19,6 +19,7 @@ struct ScanArgs {
   const float* bias;     // [D] or null
   void* y;               // [batch][D][L] act
   float* final_state;    // [batch][D][N] or null
+  void* workspace;       // chunked kernel: packed B/C, chunked_workspace_bytes() bytes
   int64_t batch, L, D;
   int N;
   int softplus;
@@ -45,8 +46,9 @@ struct StepArgs {
 hipError_t launch_scan_sequential(const ScanArgs& a, Dt dt, hipStream_t s);
 
 // Chunked wave-scan kernel.  Returns hipErrorInvalidValue when the shape does not
-// fit (callers check chunked_supported first).
+// fit (callers check chunked_supported first) or the workspace is missing.
 bool chunked_supported(const ScanArgs& a, Dt dt, int tokens_per_lane);
+size_t chunked_workspace_bytes(int64_t batch, int64_t L, int64_t N, int tokens_per_lane);
 hipError_t launch_scan_chunked(const ScanArgs& a, Dt dt, int tokens_per_lane, hipStream_t s);
 
 // Writes zeros to final_state (the L == 0 scan).

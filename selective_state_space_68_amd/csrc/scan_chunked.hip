@@ -4,79 +4,110 @@
 // recurrence, so it can be evaluated as a prefix scan over (decay, input) pairs
 // under the associative operator (a1, b1) then (a2, b2) = (a2 a1, a2 b1 + b2)
 // (the slide deck's "Parallel scan" section; the lecture notes' §4.1).  The
-// kernel is fused end to end, as the pages' hardware-aware scan is: inputs are
-// read from HBM once, the (L, D, N) states never leave registers, and only y and
-// the final state are written.
+// kernel is fused end to end, as the pages' hardware-aware scan is: every input
+// is read from HBM once, the (L, D, N) states never leave registers, and only y
+// and the final state are written.
 //
 // Work decomposition (one wave = one (batch b, channel d) pair):
 //   * a chunk is 64 * KPL consecutive tokens; lane i owns tokens [i*KPL, (i+1)*KPL)
 //     of it, so u / delta / z / y move as coalesced 16-byte vectors along L;
 //   * per token, once for all N states: Delta = softplus(delta + bias), Delta*u,
 //     the skip term D*u and, at the end, the SiLU(z) gate;
-//   * per state n (a runtime loop; A[d, n] is wave-uniform and sits in an SGPR):
+//   * per state n (A[d, n] is wave-uniform and comes from lane n of a register):
 //       pass 1  each lane folds its KPL tokens sequentially into a local end state
 //               (lane 0 starts from the carry of the previous chunk) and keeps the
-//               per-token decay a_j and input b_j in registers;
-//               the lane's aggregate decay is one exp2 of A * (sum of its Deltas);
-//       scan    a 64-lane inclusive DPP scan of the (aggregate decay, end state)
-//               pairs turns each lane's end state into the true state;
+//               per-token decay a_j and input b_j in registers; the lane's
+//               aggregate decay is one exp2 of A * (sum of its Deltas);
+//       scan    a 64-lane inclusive DPP scan of (aggregate decay, end state) pairs
+//               turns each lane's end state into the true state;
 //       pass 2  each lane replays its KPL tokens from the true state of the lane
 //               before it and accumulates y_t += C_t,n h_t,n;
-//     the carry for the next chunk is lane 63's end state;
-//   * a workgroup holds W waves = W channels of the same batch row.  B and C are
-//     shared by all channels of a row, so each (chunk, block of NB states) tile of
-//     B and C is staged once per workgroup in LDS, transposed so that a lane reads
-//     its KPL values of one state with 128-bit, conflict-free LDS reads.
+//     the carry for the next chunk is lane 63's end state.
+//
+// Data movement (kW waves = kW channels of one batch row per workgroup):
+//   * B and C are shared by all channels of a row.  A small pre-pass packs them
+//     (as float32) into a workspace laid out exactly like the LDS tiles: per
+//     (b, chunk, state, B|C) a 4*CH-byte block in the order the lanes read it.
+//     Each step of the kernel covers kNB states of one chunk; the workgroup copies
+//     the next step's tile into the other of two LDS buffers with direct
+//     global->LDS loads (no registers) while it computes on the current one, and
+//     one barrier per step publishes it;
+//   * a wave loads its next chunk's u and delta into registers at the first step
+//     of the current chunk and its z into LDS, so the chunk-to-chunk HBM traffic
+//     overlaps compute instead of arriving as one burst per chunk;
+//   * y of chunk c is gated and stored at the first step of chunk c+1, after the
+//     barrier, so barrier waits never cover store latency.
 // No MFMA: the readout is a per-token dot product over n, not a shared-operand
-// contraction.  The kernel is bound by HBM bandwidth and the VALU/transcendental
-// rate (one exp per element).
+// contraction.  The kernel is bound by HBM bandwidth and by the VALU and
+// transcendental rate (one exp per element).
+#include <algorithm>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 
 namespace ssm {
 namespace {
 
-constexpr int kNB = 4;   // states per staged B/C tile
-constexpr int kW = 4;    // waves (channels) per workgroup
+constexpr int kNB = 4;               // states per step (per staged B/C tile)
+constexpr int kW = 12;               // waves (channels) per workgroup
+constexpr int kThreads = 64 * kW;
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Direct global->LDS copy: lane l moves 16 bytes from gsrc (per lane) to
+// lds_base + 16*l (lds_base must be wave-uniform).
+__device__ __forceinline__ void dma16(const void* gsrc, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, (lds_void*)(lds_base), 16, 0, 0);
+}
 
 template <typename ACT, int KPL>
 struct TokenIO;
 
 template <int KPL>
 struct TokenIO<ActF32, KPL> {
-  static __device__ __forceinline__ void load(const void* base, int64_t off, float (&v)[KPL]) {
+  static constexpr int kVec = KPL / 4;                 // 16-byte vectors per lane
+  using raw_t = float4;
+  static __device__ __forceinline__ void load_raw(const void* base, int64_t off, raw_t (&r)[kVec]) {
     const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
 #pragma unroll
-    for (int q = 0; q < KPL / 4; ++q) {
-      const float4 x = p[q];
-      v[4 * q + 0] = x.x; v[4 * q + 1] = x.y; v[4 * q + 2] = x.z; v[4 * q + 3] = x.w;
+    for (int q = 0; q < kVec; ++q) r[q] = p[q];
+  }
+  static __device__ __forceinline__ void unpack(const raw_t (&r)[kVec], float (&v)[KPL]) {
+#pragma unroll
+    for (int q = 0; q < kVec; ++q) {
+      v[4 * q + 0] = r[q].x; v[4 * q + 1] = r[q].y; v[4 * q + 2] = r[q].z; v[4 * q + 3] = r[q].w;
     }
   }
   static __device__ __forceinline__ void store(void* base, int64_t off, const float (&v)[KPL]) {
     float4* p = reinterpret_cast<float4*>(static_cast<float*>(base) + off);
 #pragma unroll
-    for (int q = 0; q < KPL / 4; ++q)
+    for (int q = 0; q < kVec; ++q)
       p[q] = make_float4(v[4 * q + 0], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
   }
 };
 
 template <int KPL>
 struct TokenIO<ActBF16, KPL> {
-  static __device__ __forceinline__ void load(const void* base, int64_t off, float (&v)[KPL]) {
+  static constexpr int kVec = KPL / 8;
+  using raw_t = uint4;
+  static __device__ __forceinline__ void load_raw(const void* base, int64_t off, raw_t (&r)[kVec]) {
     const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off);
 #pragma unroll
-    for (int q = 0; q < KPL / 8; ++q) {
-      const uint4 x = p[q];
-      v[8 * q + 0] = bf16_lo(x.x); v[8 * q + 1] = bf16_hi(x.x);
-      v[8 * q + 2] = bf16_lo(x.y); v[8 * q + 3] = bf16_hi(x.y);
-      v[8 * q + 4] = bf16_lo(x.z); v[8 * q + 5] = bf16_hi(x.z);
-      v[8 * q + 6] = bf16_lo(x.w); v[8 * q + 7] = bf16_hi(x.w);
+    for (int q = 0; q < kVec; ++q) r[q] = p[q];
+  }
+  static __device__ __forceinline__ void unpack(const raw_t (&r)[kVec], float (&v)[KPL]) {
+#pragma unroll
+    for (int q = 0; q < kVec; ++q) {
+      v[8 * q + 0] = bf16_lo(r[q].x); v[8 * q + 1] = bf16_hi(r[q].x);
+      v[8 * q + 2] = bf16_lo(r[q].y); v[8 * q + 3] = bf16_hi(r[q].y);
+      v[8 * q + 4] = bf16_lo(r[q].z); v[8 * q + 5] = bf16_hi(r[q].z);
+      v[8 * q + 6] = bf16_lo(r[q].w); v[8 * q + 7] = bf16_hi(r[q].w);
     }
   }
   static __device__ __forceinline__ void store(void* base, int64_t off, const float (&v)[KPL]) {
     uint4* p = reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + off);
 #pragma unroll
-    for (int q = 0; q < KPL / 8; ++q) {
+    for (int q = 0; q < kVec; ++q) {
       uint4 x;
       x.x = pack_bf16x2(v[8 * q + 0], v[8 * q + 1]);
       x.y = pack_bf16x2(v[8 * q + 2], v[8 * q + 3]);
@@ -87,192 +118,263 @@ struct TokenIO<ActBF16, KPL> {
   }
 };
 
-// Loads the lane's KPL tokens starting at token index `t` of the channel whose
-// series starts at element `row`; tokens at or past L read as zero.
-template <typename ACT, int KPL, bool VEC>
-__device__ __forceinline__ void load_lane(const void* base, int64_t row, int64_t t, int64_t L,
-                                          float (&v)[KPL]) {
-  if (VEC && t + KPL <= L) {
-    TokenIO<ACT, KPL>::load(base, row + t, v);
-  } else {
-#pragma unroll
-    for (int j = 0; j < KPL; ++j) v[j] = (t + j < L) ? load_act<ACT>(base, row + t + j) : 0.0f;
-  }
-}
-
-template <typename ACT, int KPL, bool VEC>
-__device__ __forceinline__ void store_lane(void* base, int64_t row, int64_t t, int64_t L,
-                                           const float (&v)[KPL]) {
-  if (VEC && t + KPL <= L) {
-    TokenIO<ACT, KPL>::store(base, row + t, v);
-  } else {
-#pragma unroll
-    for (int j = 0; j < KPL; ++j)
-      if (t + j < L) store_act<ACT>(base, row + t + j, v[j]);
-  }
-}
-
-// Four consecutive states [n, n+4) of one token row of B or C; past N or L reads 0.
-template <typename ACT, bool VEC>
-__device__ __forceinline__ float4 load_bc4(const void* base, int64_t rowoff, int n, int N, bool tok_ok) {
-  if (!tok_ok) return make_float4(0.f, 0.f, 0.f, 0.f);
-  if (VEC && n + 4 <= N) {
-    if constexpr (ACT::kBytes == 4) {
-      return *reinterpret_cast<const float4*>(static_cast<const float*>(base) + rowoff + n);
-    } else {
-      const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + rowoff + n);
-      return make_float4(bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y));
-    }
-  }
-  float4 r;
-  r.x = (n + 0 < N) ? load_act<ACT>(base, rowoff + n + 0) : 0.f;
-  r.y = (n + 1 < N) ? load_act<ACT>(base, rowoff + n + 1) : 0.f;
-  r.z = (n + 2 < N) ? load_act<ACT>(base, rowoff + n + 2) : 0.f;
-  r.w = (n + 3 < N) ? load_act<ACT>(base, rowoff + n + 3) : 0.f;
-  return r;
-}
-
-// Stage one matrix (B or C) tile: tokens [t0, t0 + 64*KPL), states [n0, n0 + kNB).
-// LDS element (state nl, token 64-block lane i, token j within the lane) lives at
-//   nl * CH + (j / 4) * 256 + i * 4 + (j % 4)
-// so that lane i reads tokens 4q..4q+3 of state nl as one float4 at float4 index
-//   nl * CH/4 + q * 64 + i           (64 consecutive float4 per read: conflict-free).
-template <typename ACT, int KPL, bool VEC>
-__device__ __forceinline__ void stage_tile(float4* __restrict__ dst, const void* src, int64_t b,
-                                           int64_t t0, int n0, int64_t L, int N) {
+// ---- B/C packing pre-pass --------------------------------------------------
+// Workspace layout, float32: [b][chunk][n][m = B, C][q][i][r] with token
+// t = chunk*CH + i*KPL + 4q + r (zero past L).  One block [q][i][r] is 4*CH
+// bytes; a step tile (kNB states x {B, C}) is kNB*2 consecutive blocks.
+template <typename ACT, int KPL>
+__global__ __launch_bounds__(256) void pack_bc_kernel(const void* __restrict__ Bm, const void* __restrict__ Cm,
+                                                      float4* __restrict__ ws, int64_t batch, int64_t L, int N,
+                                                      int64_t nchunks) {
   constexpr int CH = 64 * KPL;
-  constexpr int QUADS = 64 * (KPL / 4);            // (lane block, token quad) pairs
-  constexpr int THREADS = 64 * kW;
-  for (int qd = threadIdx.x; qd < QUADS; qd += THREADS) {
-    const int i = qd & 63;
-    const int jq = qd >> 6;
-    const int64_t tt = t0 + static_cast<int64_t>(i) * KPL + jq * 4;
-    float4 r[4];
+  constexpr int Q = KPL / 4;
+  const int64_t total = batch * nchunks * N * 2 * (CH / 4);
+  for (int64_t g = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; g < total;
+       g += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    int64_t rest = g;
+    const int i = static_cast<int>(rest % 64); rest /= 64;
+    const int q = static_cast<int>(rest % Q); rest /= Q;
+    const int m = static_cast<int>(rest % 2); rest /= 2;
+    const int n = static_cast<int>(rest % N); rest /= N;
+    const int64_t c = rest % nchunks;
+    const int64_t b = rest / nchunks;
+    const void* src = m == 0 ? Bm : Cm;
+    const int64_t t0 = c * CH + static_cast<int64_t>(i) * KPL + 4 * q;
+    float v[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int64_t t = tt + k;
-      r[k] = load_bc4<ACT, VEC>(src, (b * L + (t < L ? t : 0)) * N, n0, N, t < L);
+    for (int r = 0; r < 4; ++r) {
+      const int64_t t = t0 + r;
+      v[r] = t < L ? load_act<ACT>(src, (b * L + t) * N + n) : 0.0f;
     }
-    // transpose 4 tokens x 4 states -> one float4 of 4 tokens per state
-    dst[0 * (CH / 4) + jq * 64 + i] = make_float4(r[0].x, r[1].x, r[2].x, r[3].x);
-    dst[1 * (CH / 4) + jq * 64 + i] = make_float4(r[0].y, r[1].y, r[2].y, r[3].y);
-    dst[2 * (CH / 4) + jq * 64 + i] = make_float4(r[0].z, r[1].z, r[2].z, r[3].z);
-    dst[3 * (CH / 4) + jq * 64 + i] = make_float4(r[0].w, r[1].w, r[2].w, r[3].w);
+    ws[g] = make_float4(v[0], v[1], v[2], v[3]);
   }
 }
 
+// ---- the scan ----------------------------------------------------------------
 template <typename ACT, bool GATE, int KPL, bool VEC>
-__global__ __launch_bounds__(64 * kW) void scan_chunked_kernel(ScanArgs p, int n_dblk) {
+__global__ __launch_bounds__(kThreads) void scan_chunked_kernel(ScanArgs p, int n_dblk) {
+  using IO = TokenIO<ACT, KPL>;
+  using raw_t = typename IO::raw_t;
   constexpr int CH = 64 * KPL;
-  static_assert(kNB == 4, "tile transpose assumes 4 states per tile");
-  __shared__ float4 sB[kNB * CH / 4];
-  __shared__ float4 sC[kNB * CH / 4];
+  constexpr int BLK4 = CH / 4;                       // float4 per (state, matrix) block
+  constexpr int TILE4 = kNB * 2 * BLK4;              // float4 per step tile
+  constexpr int ZBYTES = KPL * ACT::kBytes * 64;     // z of one chunk for one wave
+  // Two distinct objects, so the compiler can tell the buffer being read from the
+  // one being filled (a DMA into one never forces a wait before reading the other).
+  __shared__ float4 s_tile0[TILE4];
+  __shared__ float4 s_tile1[TILE4];
+  __shared__ float4 s_z[(GATE && VEC) ? kW * ZBYTES / 16 : 1];
 
   const int lane = threadIdx.x & 63;
+  const bool lane0 = lane == 0;
   const int w = uniform_int(threadIdx.x >> 6);
   const int blk = blockIdx.x;
   const int64_t b = blk / n_dblk;
   const int64_t d = static_cast<int64_t>(blk % n_dblk) * kW + w;
-  const bool valid = d < p.D;                       // wave-uniform
+  const bool valid = d < p.D;                        // wave-uniform
   const int N = p.N;
   const int64_t L = p.L;
   const int64_t row = (b * p.D + (valid ? d : 0)) * L;
   const float bias = (valid && p.bias) ? p.bias[d] : 0.0f;
   const float dsk = (valid && p.Dskip) ? p.Dskip[d] : 0.0f;
+  // A[d, n] * log2(e) in lane n (read once, before any store, so the state loop
+  // never issues a vector load of A).
+  const float a2_v = (valid && lane < N) ? p.A[d * N + lane] * kLog2e : 0.0f;
+  float carry_v = 0.0f;                              // carry of state n lives in lane n
 
-  // carry[n] lives in lane n of this register (N <= 64).
-  float carry_v = 0.0f;
-
+  const int nblk = (N + kNB - 1) / kNB;
   const int64_t nchunks = (L + CH - 1) / CH;
-  for (int64_t c = 0; c < nchunks; ++c) {
-    const int64_t tl = c * CH + static_cast<int64_t>(lane) * KPL;   // first token of this lane
-    float dl[KPL], du[KPL], yv[KPL], zv[KPL];
-    float sdl = 0.0f;
-    if (valid) {
-      float uv[KPL];
-      load_lane<ACT, KPL, VEC>(p.u, row, tl, L, uv);
-      load_lane<ACT, KPL, VEC>(p.delta, row, tl, L, dl);
-      if (GATE) load_lane<ACT, KPL, VEC>(p.z, row, tl, L, zv);
+  const int64_t nsteps = nchunks * nblk;
+  const float4* ws = reinterpret_cast<const float4*>(p.workspace) + b * nchunks * N * 2 * BLK4;
+
+  float dl[KPL], du[KPL], yv[KPL];
+  float sdl = 0.0f;
+  int nv = KPL;                                      // valid tokens of this lane in its chunk
+  raw_t u_raw[IO::kVec], d_raw[IO::kVec];            // next chunk's u and delta
+
+  // Issue the loads of chunk c's u and delta (full lanes of the vector path).
+  auto prefetch_ud = [&](int64_t c) {
+    const int64_t tl = c * CH + static_cast<int64_t>(lane) * KPL;
+    if (VEC && tl + KPL <= L) {
+      IO::load_raw(p.u, row + tl, u_raw);
+      IO::load_raw(p.delta, row + tl, d_raw);
+    }
+  };
+  // Copy chunk c's z for this wave into LDS: DMA q moves this lane's 16-byte
+  // vector q to s_z + w*ZBYTES + q*1024 + 16*lane.  Vectors at or past L read a
+  // valid address (their values are never used).
+  auto prefetch_z = [&](int64_t c) {
+    if constexpr (GATE && VEC) {
+      const int64_t tl = c * CH + static_cast<int64_t>(lane) * KPL;
+#pragma unroll
+      for (int q = 0; q < IO::kVec; ++q) {
+        const int64_t t = tl + q * (16 / ACT::kBytes);
+        const int64_t off = (t < L ? row + t : 0) * ACT::kBytes;
+        dma16(static_cast<const char*>(p.z) + off, reinterpret_cast<char*>(s_z) + w * ZBYTES + q * 1024);
+      }
+    }
+  };
+
+  // Per-token work of chunk c, once for all N states.
+  auto prologue = [&](int64_t c) {
+    const int64_t tl = c * CH + static_cast<int64_t>(lane) * KPL;
+    const int64_t rem = L - tl;
+    nv = rem >= KPL ? KPL : (rem > 0 ? static_cast<int>(rem) : 0);
+    float uv[KPL];
+    if (VEC && nv == KPL) {
+      IO::unpack(u_raw, uv);
+      IO::unpack(d_raw, dl);
+    } else {
 #pragma unroll
       for (int j = 0; j < KPL; ++j) {
-        float x = dl[j] + bias;
-        if (p.softplus) x = softplus_f(x);
-        dl[j] = (tl + j < L) ? x : 0.0f;            // padding tokens: identity step
-        du[j] = dl[j] * uv[j];
-        yv[j] = dsk * uv[j];
-        sdl += dl[j];
+        const bool ok = j < nv;
+        uv[j] = ok ? load_act<ACT>(p.u, row + tl + j) : 0.0f;
+        dl[j] = ok ? load_act<ACT>(p.delta, row + tl + j) : 0.0f;
       }
     }
+    if (p.softplus) {
+#pragma unroll
+      for (int j = 0; j < KPL; ++j) dl[j] = softplus_f(dl[j] + bias);
+    } else {
+#pragma unroll
+      for (int j = 0; j < KPL; ++j) dl[j] = dl[j] + bias;
+    }
+    if (nv < KPL) {                                  // padding tokens: identity step
+#pragma unroll
+      for (int j = 0; j < KPL; ++j) dl[j] = j < nv ? dl[j] : 0.0f;
+    }
+    sdl = 0.0f;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+      du[j] = dl[j] * uv[j];
+      yv[j] = dsk * uv[j];
+      sdl += dl[j];
+    }
+  };
 
-    for (int n0 = 0; n0 < N; n0 += kNB) {
-      __syncthreads();                                // previous tile fully consumed
-      stage_tile<ACT, KPL, VEC>(sB, p.Bm, b, c * CH, n0, L, N);
-      stage_tile<ACT, KPL, VEC>(sC, p.Cm, b, c * CH, n0, L, N);
-      __syncthreads();
-      if (!valid) continue;
-      const int nn = (N - n0 < kNB) ? (N - n0) : kNB;
-      for (int nl = 0; nl < nn; ++nl) {
-        const int n = n0 + nl;
-        const float a2 = p.A[d * N + n] * kLog2e;     // wave-uniform
-        const float carry = __builtin_bit_cast(
-            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, carry_v), n));
-        float av[KPL], bv[KPL];
-        float h = (lane == 0) ? carry : 0.0f;
-        const float4* bq = sB + nl * (CH / 4) + lane;
+  auto epilogue = [&](int64_t c) {
+    const int64_t tl = c * CH + static_cast<int64_t>(lane) * KPL;
+    if (GATE) {
+      float zv[KPL];
+      if (VEC) {
+        raw_t zr[IO::kVec];
+        const raw_t* zs = reinterpret_cast<const raw_t*>(reinterpret_cast<const char*>(s_z) + w * ZBYTES);
 #pragma unroll
-        for (int q = 0; q < KPL / 4; ++q) {
-          const float4 bb = bq[q * 64];
-          const float bs[4] = {bb.x, bb.y, bb.z, bb.w};
+        for (int q = 0; q < IO::kVec; ++q) zr[q] = zs[q * 64 + lane];
+        IO::unpack(zr, zv);
+      } else {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int j = 4 * q + r;
-            av[j] = exp2_hw(dl[j] * a2);
-            bv[j] = du[j] * bs[r];
-            h = __builtin_fmaf(av[j], h, bv[j]);
-          }
-        }
-        float P = exp2_hw(a2 * sdl);                  // this lane's aggregate decay
-        wave_scan_pairs(P, h);                        // h: true state after this lane
-        const float hin = wave_shift_up(h, carry);    // true state before this lane
-        const float cnew = wave_lane63(h);
-        carry_v = (lane == n) ? cnew : carry_v;
-        float hh = hin;
-        const float4* cq = sC + nl * (CH / 4) + lane;
+        for (int j = 0; j < KPL; ++j) zv[j] = j < nv ? load_act<ACT>(p.z, row + tl + j) : 0.0f;
+      }
 #pragma unroll
-        for (int q = 0; q < KPL / 4; ++q) {
-          const float4 cc = cq[q * 64];
-          const float cs[4] = {cc.x, cc.y, cc.z, cc.w};
+      for (int j = 0; j < KPL; ++j) yv[j] *= silu_f(zv[j]);
+    }
+    if (VEC && nv == KPL) {
+      IO::store(p.y, row + tl, yv);
+    } else {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int j = 4 * q + r;
-            hh = __builtin_fmaf(av[j], hh, bv[j]);
-            yv[j] = __builtin_fmaf(cs[r], hh, yv[j]);
-          }
-        }
+      for (int j = 0; j < KPL; ++j)
+        if (j < nv) store_act<ACT>(p.y, row + tl + j, yv[j]);
+    }
+  };
+
+  // One state n over the current chunk; its B and C blocks are sB, sC in LDS.
+  auto scan_state = [&](const float4* __restrict__ sB, const float4* __restrict__ sC, int n) {
+    const float a2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, a2_v), n));
+    const float carry = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, carry_v), n));
+    float av[KPL], bv[KPL];
+    float h = lane0 ? carry : 0.0f;
+#pragma unroll
+    for (int q = 0; q < KPL / 4; ++q) {
+      const float4 bb = sB[q * 64 + lane];
+      const float bs[4] = {bb.x, bb.y, bb.z, bb.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = 4 * q + r;
+        av[j] = exp2_hw(dl[j] * a2);
+        bv[j] = du[j] * bs[r];
+        h = __builtin_fmaf(av[j], h, bv[j]);
       }
     }
+    float P = exp2_hw(a2 * sdl);                     // this lane's decay over its tokens
+    float4 cq[KPL / 4];                              // C reads issued before the scan
+#pragma unroll
+    for (int q = 0; q < KPL / 4; ++q) cq[q] = sC[q * 64 + lane];
+    wave_scan_pairs(P, h);                           // h: true state after this lane
+    const float hin = wave_shift_up(h, carry);       // true state before this lane
+    const float cnew = wave_lane63(h);
+    carry_v = (lane == n) ? cnew : carry_v;
+    float hh = hin;
+#pragma unroll
+    for (int q = 0; q < KPL / 4; ++q) {
+      const float cs[4] = {cq[q].x, cq[q].y, cq[q].z, cq[q].w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = 4 * q + r;
+        hh = __builtin_fmaf(av[j], hh, bv[j]);
+        yv[j] = __builtin_fmaf(cs[r], hh, yv[j]);
+      }
+    }
+  };
 
+  // Tile of step k = (chunk k / nblk, states n0 = (k % nblk) * kNB ...) is the
+  // contiguous run of float4 at ws + (c * N + n0) * 2 * BLK4 covering min(kNB,
+  // N - n0) states.  Wave w copies its 1 KB pieces w, w + kW, ... into dst.
+  auto issue_tile = [&](int64_t k, float4* dst) {
+    const int64_t c = k / nblk;
+    const int n0 = static_cast<int>(k % nblk) * kNB;
+    const int pieces = ((N - n0 < kNB) ? (N - n0) : kNB) * 2 * BLK4 / 64;
+    const float4* src = ws + (c * N + n0) * 2 * BLK4;
+    for (int piece = w; piece < pieces; piece += kW) dma16(src + piece * 64 + lane, dst + piece * 64);
+  };
+
+  // Step k computes on `cur` while the next step's tile lands in `nxt`.
+  auto step = [&](int64_t k, const float4* cur, float4* nxt) {
+    const int64_t c = k / nblk;
+    const int nb = static_cast<int>(k % nblk);
+    if (nb == 0 && valid) {
+      if (c > 0) epilogue(c - 1);                    // z of c-1 landed during chunk c-1
+      prologue(c);                                   // u, delta of c prefetched during c-1
+      if (c + 1 < nchunks) prefetch_ud(c + 1);
+      prefetch_z(c);
+    }
+    if (k + 1 < nsteps) issue_tile(k + 1, nxt);
     if (valid) {
-      if (GATE) {
-#pragma unroll
-        for (int j = 0; j < KPL; ++j) yv[j] *= silu_f(zv[j]);
-      }
-      store_lane<ACT, KPL, VEC>(p.y, row, tl, L, yv);
+      const int n0 = nb * kNB;
+      const int nn = (N - n0 < kNB) ? (N - n0) : kNB;
+      for (int nl = 0; nl < nn; ++nl) scan_state(cur + nl * 2 * BLK4, cur + (nl * 2 + 1) * BLK4, n0 + nl);
     }
+    __syncthreads();                                 // waits for this wave's copies, then publishes
+  };
+
+  if (valid) prefetch_ud(0);
+  issue_tile(0, s_tile0);
+  __syncthreads();
+  for (int64_t k = 0; k < nsteps; k += 2) {
+    step(k, s_tile0, s_tile1);
+    if (k + 1 < nsteps) step(k + 1, s_tile1, s_tile0);
   }
-  if (valid && p.final_state && lane < N) p.final_state[(b * p.D + d) * N + lane] = carry_v;
+  if (valid) {
+    epilogue(nchunks - 1);
+    if (p.final_state && lane < N) p.final_state[(b * p.D + d) * N + lane] = carry_v;
+  }
 }
 
 bool aligned16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; }
 
 template <typename ACT, bool GATE, int KPL>
 hipError_t launch_kpl(const ScanArgs& a, hipStream_t s) {
+  constexpr int CH = 64 * KPL;
+  const int64_t nchunks = (a.L + CH - 1) / CH;
+  const int64_t packed4 = a.batch * nchunks * a.N * 2 * (CH / 4);
+  const int pack_blocks = static_cast<int>(std::min<int64_t>((packed4 + 255) / 256, 65536));
+  hipLaunchKernelGGL((pack_bc_kernel<ACT, KPL>), dim3(pack_blocks), dim3(256), 0, s, a.Bm, a.Cm,
+                     reinterpret_cast<float4*>(a.workspace), a.batch, a.L, a.N, nchunks);
   const int n_dblk = static_cast<int>((a.D + kW - 1) / kW);
   const int64_t blocks = a.batch * n_dblk;
-  const bool vec = (a.L % 8 == 0) && (a.N % 4 == 0) && aligned16(a.u) && aligned16(a.delta) &&
-                   aligned16(a.y) && aligned16(a.Bm) && aligned16(a.Cm) &&
+  const bool vec = (a.L % 8 == 0) && aligned16(a.u) && aligned16(a.delta) && aligned16(a.y) &&
                    (a.z == nullptr || aligned16(a.z));
-  const dim3 grid(static_cast<unsigned>(blocks)), block(64 * kW);
+  const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
   if (vec)
     hipLaunchKernelGGL((scan_chunked_kernel<ACT, GATE, KPL, true>), grid, block, 0, s, a, n_dblk);
   else
@@ -286,18 +388,26 @@ hipError_t launch_gate(const ScanArgs& a, int kpl, hipStream_t s) {
   return launch_kpl<ACT, GATE, 16>(a, s);
 }
 
+int resolve_kpl(int tokens_per_lane) { return tokens_per_lane == 0 ? 16 : tokens_per_lane; }
+
 }  // namespace
+
+size_t chunked_workspace_bytes(int64_t batch, int64_t L, int64_t N, int tokens_per_lane) {
+  const int64_t ch = 64 * resolve_kpl(tokens_per_lane);
+  const int64_t nchunks = (L + ch - 1) / ch;
+  return static_cast<size_t>(batch) * nchunks * N * 2 * ch * sizeof(float);
+}
 
 bool chunked_supported(const ScanArgs& a, Dt, int tokens_per_lane) {
   if (!(tokens_per_lane == 0 || tokens_per_lane == 8 || tokens_per_lane == 16)) return false;
   if (a.N < 1 || a.N > 64) return false;
   const int64_t n_dblk = (a.D + kW - 1) / kW;
-  return a.batch * n_dblk <= 0x7fffffff && n_dblk <= 0x7fffffff;
+  return a.batch * n_dblk <= 0x7fffffff;
 }
 
 hipError_t launch_scan_chunked(const ScanArgs& a, Dt dt, int tokens_per_lane, hipStream_t s) {
-  if (!chunked_supported(a, dt, tokens_per_lane)) return hipErrorInvalidValue;
-  const int kpl = tokens_per_lane == 0 ? 16 : tokens_per_lane;
+  if (!chunked_supported(a, dt, tokens_per_lane) || a.workspace == nullptr) return hipErrorInvalidValue;
+  const int kpl = resolve_kpl(tokens_per_lane);
   const bool gate = a.z != nullptr;
   if (dt == Dt::F32)
     return gate ? launch_gate<ActF32, true>(a, kpl, s) : launch_gate<ActF32, false>(a, kpl, s);

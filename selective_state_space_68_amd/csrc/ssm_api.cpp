@@ -58,12 +58,11 @@ struct ScanSizes {
 ssm_status check_scan(const void* u, const void* delta, const float* A, const void* Bm, const void* Cm,
                       const float* Dskip, const void* z, const float* delta_bias, int delta_softplus,
                       const void* y, const float* final_state, int64_t batch, int64_t L, int64_t D,
-                      int64_t N, ssm_dtype dt, size_t workspace_bytes, ScanSizes* sz) {
+                      int64_t N, ssm_dtype dt, ScanSizes* sz) {
   if (dt != SSM_F32 && dt != SSM_BF16) return SSM_ERR_UNSUPPORTED;
   if (batch < 0 || L < 0 || D < 0 || N < 0) return SSM_ERR_INVALID_ARG;
   if (N < 1 || N > SSM_MAX_N) return SSM_ERR_UNSUPPORTED;
   if (delta_softplus != 0 && delta_softplus != 1) return SSM_ERR_INVALID_ARG;
-  (void)workspace_bytes;  // no workspace is needed; any size (including 0) is accepted
   const uint64_t e = dt == SSM_BF16 ? 2 : 4;
   uint64_t bd, bdl, bl, bln, dn, bdn;
   if (!mul_ok(batch, D, &bd) || !mul_ok(bd, L, &bdl) || !mul_ok(bdl, e, &sz->act_bytes) ||
@@ -108,7 +107,10 @@ const char* ssm_status_string(ssm_status s) {
 
 int ssm_version(void) { return kVersion; }
 
-size_t ssm_selective_scan_workspace_size(int64_t, int64_t, int64_t, int64_t, ssm_dtype) { return 0; }
+size_t ssm_selective_scan_workspace_size(int64_t batch, int64_t L, int64_t D, int64_t N, ssm_dtype dt) {
+  if (batch <= 0 || L <= 0 || D <= 0 || N < 1 || N > SSM_MAX_N || (dt != SSM_F32 && dt != SSM_BF16)) return 0;
+  return ssm::chunked_workspace_bytes(batch, L, N, 0);
+}
 
 ssm_status ssm_selective_scan_fwd_variant(const void* u, const void* delta, const float* A, const void* Bm,
                                           const void* Cm, const float* Dskip, const void* z,
@@ -116,30 +118,39 @@ ssm_status ssm_selective_scan_fwd_variant(const void* u, const void* delta, cons
                                           float* final_state, int64_t batch, int64_t L, int64_t D,
                                           int64_t N, ssm_dtype dt, void* workspace, size_t workspace_bytes,
                                           void* stream, int variant, int tokens_per_lane) {
-  (void)workspace;
   ScanSizes sz;
   ssm_status st = check_scan(u, delta, A, Bm, Cm, Dskip, z, delta_bias, delta_softplus, y, final_state,
-                             batch, L, D, N, dt, workspace_bytes, &sz);
+                             batch, L, D, N, dt, &sz);
   if (st != SSM_OK) return st;
   if (variant != SSM_SCAN_AUTO && variant != SSM_SCAN_SEQUENTIAL && variant != SSM_SCAN_CHUNKED)
     return SSM_ERR_UNSUPPORTED;
   if (!(tokens_per_lane == 0 || tokens_per_lane == 8 || tokens_per_lane == 16)) return SSM_ERR_UNSUPPORTED;
   if (batch == 0 || D == 0) return SSM_OK;  // nothing to compute or write
+  ssm::ScanArgs a;
+  a.u = u; a.delta = delta; a.A = A; a.Bm = Bm; a.Cm = Cm; a.Dskip = Dskip; a.z = z;
+  a.bias = delta_bias; a.y = y; a.final_state = final_state; a.workspace = workspace;
+  a.batch = batch; a.L = L; a.D = D; a.N = static_cast<int>(N); a.softplus = delta_softplus;
+  const ssm::Dt d = dt == SSM_BF16 ? ssm::Dt::BF16 : ssm::Dt::F32;
+  const bool chunked = L > 0 && variant != SSM_SCAN_SEQUENTIAL && ssm::chunked_supported(a, d, tokens_per_lane);
+  if (variant == SSM_SCAN_CHUNKED && L > 0 && !chunked) return SSM_ERR_UNSUPPORTED;
+  if (chunked) {
+    // the chunked kernel packs B and C into the caller's workspace
+    const size_t need = ssm::chunked_workspace_bytes(batch, L, N, tokens_per_lane);
+    if (workspace == nullptr || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 15u))
+      return SSM_ERR_INVALID_ARG;
+    const Span ws = span(workspace, need);
+    const Span all[] = {span(u, sz.act_bytes),     span(delta, sz.act_bytes),        span(z, sz.act_bytes),
+                        span(A, sz.a_bytes),       span(Bm, sz.bc_bytes),            span(Cm, sz.bc_bytes),
+                        span(Dskip, sz.vec_bytes), span(delta_bias, sz.vec_bytes),   span(y, sz.act_bytes),
+                        span(final_state, sz.state_bytes)};
+    for (const Span& o : all)
+      if (overlaps(ws, o)) return SSM_ERR_INVALID_ARG;
+  }
   st = probe_device();
   if (st != SSM_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (L == 0) return final_state ? from_hip(ssm::launch_zero_state(final_state, batch * D * N, s)) : SSM_OK;
-
-  ssm::ScanArgs a;
-  a.u = u; a.delta = delta; a.A = A; a.Bm = Bm; a.Cm = Cm; a.Dskip = Dskip; a.z = z;
-  a.bias = delta_bias; a.y = y; a.final_state = final_state;
-  a.batch = batch; a.L = L; a.D = D; a.N = static_cast<int>(N); a.softplus = delta_softplus;
-  const ssm::Dt d = dt == SSM_BF16 ? ssm::Dt::BF16 : ssm::Dt::F32;
-
-  if (variant == SSM_SCAN_SEQUENTIAL) return from_hip(ssm::launch_scan_sequential(a, d, s));
-  if (variant == SSM_SCAN_CHUNKED && !ssm::chunked_supported(a, d, tokens_per_lane)) return SSM_ERR_UNSUPPORTED;
-  if (ssm::chunked_supported(a, d, tokens_per_lane))
-    return from_hip(ssm::launch_scan_chunked(a, d, tokens_per_lane, s));
+  if (chunked) return from_hip(ssm::launch_scan_chunked(a, d, tokens_per_lane, s));
   return from_hip(ssm::launch_scan_sequential(a, d, s));
 }
 
