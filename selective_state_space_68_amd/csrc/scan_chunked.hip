@@ -32,11 +32,11 @@
 //     the next step's tile into the other of two LDS buffers with direct
 //     global->LDS loads (no registers) while it computes on the current one, and
 //     one barrier per step publishes it;
-//   * a wave loads its next chunk's u and delta into registers at the first step
-//     of the current chunk and its z into LDS, so the chunk-to-chunk HBM traffic
-//     overlaps compute instead of arriving as one burst per chunk;
-//   * y of chunk c is gated and stored at the first step of chunk c+1, after the
-//     barrier, so barrier waits never cover store latency.
+//   * a wave loads its next chunk's u and delta into registers and this chunk's z
+//     into LDS during the current chunk, and stores the previous chunk's y at its
+//     first step, one kind of traffic per step: every barrier waits for the wave's
+//     outstanding memory operations, so a chunk's HBM traffic is spread over its
+//     steps instead of arriving as one burst per chunk.
 // No MFMA: the readout is a per-token dot product over n, not a shared-operand
 // contraction.  The kernel is bound by HBM bandwidth and by the VALU and
 // transcendental rate (one exp per element).
@@ -122,36 +122,71 @@ struct TokenIO<ActBF16, KPL> {
 // Workspace layout, float32: [b][chunk][n][m = B, C][q][i][r] with token
 // t = chunk*CH + i*KPL + 4q + r (zero past L).  One block [q][i][r] is 4*CH
 // bytes; a step tile (kNB states x {B, C}) is kNB*2 consecutive blocks.
+// One thread per (b, token quad, matrix): it reads the quad's 4 token rows
+// (contiguous, so a wave reads one contiguous span) and writes one float4 per
+// state.
 template <typename ACT, int KPL>
 __global__ __launch_bounds__(256) void pack_bc_kernel(const void* __restrict__ Bm, const void* __restrict__ Cm,
                                                       float4* __restrict__ ws, int64_t batch, int64_t L, int N,
-                                                      int64_t nchunks) {
+                                                      int64_t nchunks, int vec4) {
   constexpr int CH = 64 * KPL;
-  constexpr int Q = KPL / 4;
-  const int64_t total = batch * nchunks * N * 2 * (CH / 4);
+  const int64_t quads = nchunks * (CH / 4);              // token quads per batch row (padded)
+  const int64_t total = batch * quads * 2;
   for (int64_t g = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; g < total;
        g += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    int64_t rest = g;
-    const int i = static_cast<int>(rest % 64); rest /= 64;
-    const int q = static_cast<int>(rest % Q); rest /= Q;
-    const int m = static_cast<int>(rest % 2); rest /= 2;
-    const int n = static_cast<int>(rest % N); rest /= N;
-    const int64_t c = rest % nchunks;
-    const int64_t b = rest / nchunks;
+    const int m = static_cast<int>(g % 2);
+    const int64_t gq = (g / 2) % quads;                   // token quad within the batch row
+    const int64_t b = g / (2 * quads);
+    const int64_t t0 = gq * 4;
+    const int64_t c = t0 / CH;
+    const int tc = static_cast<int>(t0 - c * CH);         // token within the chunk
+    const int i = tc / KPL;
+    const int q = (tc % KPL) / 4;
     const void* src = m == 0 ? Bm : Cm;
-    const int64_t t0 = c * CH + static_cast<int64_t>(i) * KPL + 4 * q;
-    float v[4];
+    float4* dst = ws + ((b * nchunks + c) * N * 2 + m) * (CH / 4) + q * 64 + i;
+    const int64_t stride = 2 * (CH / 4);                  // float4 between consecutive states
+    if (vec4) {                                           // N % 4 == 0, rows 4-state aligned
+#pragma unroll 4
+      for (int n = 0; n < N; n += 4) {
+        float4 r4[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t t = t0 + r;
-      v[r] = t < L ? load_act<ACT>(src, (b * L + t) * N + n) : 0.0f;
+        for (int r = 0; r < 4; ++r) {
+          const int64_t t = t0 + r;
+          const int64_t o = (b * L + (t < L ? t : 0)) * N + n;
+          float4 x;
+          if constexpr (ACT::kBytes == 4) {
+            x = *reinterpret_cast<const float4*>(static_cast<const float*>(src) + o);
+          } else {
+            const uint2 w2 = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(src) + o);
+            x = make_float4(bf16_lo(w2.x), bf16_hi(w2.x), bf16_lo(w2.y), bf16_hi(w2.y));
+          }
+          r4[r] = t < L ? x : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        dst[(n + 0) * stride] = make_float4(r4[0].x, r4[1].x, r4[2].x, r4[3].x);
+        dst[(n + 1) * stride] = make_float4(r4[0].y, r4[1].y, r4[2].y, r4[3].y);
+        dst[(n + 2) * stride] = make_float4(r4[0].z, r4[1].z, r4[2].z, r4[3].z);
+        dst[(n + 3) * stride] = make_float4(r4[0].w, r4[1].w, r4[2].w, r4[3].w);
+      }
+    } else {
+      for (int n = 0; n < N; ++n) {
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int64_t t = t0 + r;
+          v[r] = t < L ? load_act<ACT>(src, (b * L + t) * N + n) : 0.0f;
+        }
+        dst[n * stride] = make_float4(v[0], v[1], v[2], v[3]);
+      }
     }
-    ws[g] = make_float4(v[0], v[1], v[2], v[3]);
   }
 }
 
 // ---- the scan ----------------------------------------------------------------
-template <typename ACT, bool GATE, int KPL, bool VEC>
+// NBLK > 0: the state count is fixed at compile time to (4*(NBLK-1), 4*NBLK]
+// steps per chunk, and the steps of a chunk are unrolled (so every prefetch
+// register is consumed before it is refilled within one loop iteration, and the
+// compiler's wait tracking stays exact).  NBLK = 0: any N, steps in a runtime loop.
+template <typename ACT, bool GATE, int KPL, bool VEC, int NBLK>
 __global__ __launch_bounds__(kThreads) void scan_chunked_kernel(ScanArgs p, int n_dblk) {
   using IO = TokenIO<ACT, KPL>;
   using raw_t = typename IO::raw_t;
@@ -168,9 +203,12 @@ __global__ __launch_bounds__(kThreads) void scan_chunked_kernel(ScanArgs p, int 
   const int lane = threadIdx.x & 63;
   const bool lane0 = lane == 0;
   const int w = uniform_int(threadIdx.x >> 6);
+  // Consecutive workgroups go to different XCDs (round robin over 8); taking the
+  // batch row as blk % batch keeps one row per XCD when batch divides 8, so each
+  // XCD's L2 holds only that row's packed B/C tiles.
   const int blk = blockIdx.x;
-  const int64_t b = blk / n_dblk;
-  const int64_t d = static_cast<int64_t>(blk % n_dblk) * kW + w;
+  const int64_t b = blk % p.batch;
+  const int64_t d = static_cast<int64_t>(blk / p.batch) * kW + w;
   const bool valid = d < p.D;                        // wave-uniform
   const int N = p.N;
   const int64_t L = p.L;
@@ -182,7 +220,7 @@ __global__ __launch_bounds__(kThreads) void scan_chunked_kernel(ScanArgs p, int 
   const float a2_v = (valid && lane < N) ? p.A[d * N + lane] * kLog2e : 0.0f;
   float carry_v = 0.0f;                              // carry of state n lives in lane n
 
-  const int nblk = (N + kNB - 1) / kNB;
+  const int nblk = NBLK > 0 ? NBLK : (N + kNB - 1) / kNB;
   const int64_t nchunks = (L + CH - 1) / CH;
   const int64_t nsteps = nchunks * nblk;
   const float4* ws = reinterpret_cast<const float4*>(p.workspace) + b * nchunks * N * 2 * BLK4;
@@ -192,13 +230,10 @@ __global__ __launch_bounds__(kThreads) void scan_chunked_kernel(ScanArgs p, int 
   int nv = KPL;                                      // valid tokens of this lane in its chunk
   raw_t u_raw[IO::kVec], d_raw[IO::kVec];            // next chunk's u and delta
 
-  // Issue the loads of chunk c's u and delta (full lanes of the vector path).
-  auto prefetch_ud = [&](int64_t c) {
+  // Issue the loads of chunk c's u (or delta) for full lanes of the vector path.
+  auto prefetch_act = [&](const void* src, int64_t c, raw_t (&dst)[IO::kVec]) {
     const int64_t tl = c * CH + static_cast<int64_t>(lane) * KPL;
-    if (VEC && tl + KPL <= L) {
-      IO::load_raw(p.u, row + tl, u_raw);
-      IO::load_raw(p.delta, row + tl, d_raw);
-    }
+    if (VEC && tl + KPL <= L) IO::load_raw(src, row + tl, dst);
   };
   // Copy chunk c's z for this wave into LDS: DMA q moves this lane's 16-byte
   // vector q to s_z + w*ZBYTES + q*1024 + 16*lane.  Vectors at or past L read a
@@ -328,31 +363,67 @@ __global__ __launch_bounds__(kThreads) void scan_chunked_kernel(ScanArgs p, int 
     for (int piece = w; piece < pieces; piece += kW) dma16(src + piece * 64 + lane, dst + piece * 64);
   };
 
+  // Every barrier first waits for all of this wave's outstanding memory
+  // operations (the copies into LDS must have landed before any wave reads the
+  // tile, and they are tracked by the same counter as the HBM loads, with no
+  // ordering between the two kinds).  So a load issued in a step lands within that
+  // step, and a chunk's HBM traffic is spread over its steps, one kind per step:
+  // y of the previous chunk is stored at step 0, the next chunk's u is loaded at
+  // step 1, its delta at step 2 and this chunk's z at step 3.
+  const int st_u = nblk > 1 ? 1 : 0;
+  const int st_d = nblk > 2 ? 2 : st_u;
+  const int st_z = nblk > 3 ? 3 : st_d;
+
   // Step k computes on `cur` while the next step's tile lands in `nxt`.
   auto step = [&](int64_t k, const float4* cur, float4* nxt) {
     const int64_t c = k / nblk;
     const int nb = static_cast<int>(k % nblk);
-    if (nb == 0 && valid) {
+    if (valid && nb == 0) {
       if (c > 0) epilogue(c - 1);                    // z of c-1 landed during chunk c-1
       prologue(c);                                   // u, delta of c prefetched during c-1
-      if (c + 1 < nchunks) prefetch_ud(c + 1);
-      prefetch_z(c);
     }
     if (k + 1 < nsteps) issue_tile(k + 1, nxt);
+    __builtin_amdgcn_sched_barrier(0);               // keep the issue order of memory operations
+    if (valid) {
+      if (c + 1 < nchunks && nb == st_u) prefetch_act(p.u, c + 1, u_raw);
+      if (c + 1 < nchunks && nb == st_d) prefetch_act(p.delta, c + 1, d_raw);
+      if (nb == st_z) prefetch_z(c);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     if (valid) {
       const int n0 = nb * kNB;
       const int nn = (N - n0 < kNB) ? (N - n0) : kNB;
       for (int nl = 0; nl < nn; ++nl) scan_state(cur + nl * 2 * BLK4, cur + (nl * 2 + 1) * BLK4, n0 + nl);
     }
-    __syncthreads();                                 // waits for this wave's copies, then publishes
+    // s_waitcnt vmcnt(0): vmcnt in bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8].
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
   };
 
-  if (valid) prefetch_ud(0);
+  if (valid) {
+    prefetch_act(p.u, 0, u_raw);
+    prefetch_act(p.delta, 0, d_raw);
+  }
   issue_tile(0, s_tile0);
-  __syncthreads();
-  for (int64_t k = 0; k < nsteps; k += 2) {
-    step(k, s_tile0, s_tile1);
-    if (k + 1 < nsteps) step(k + 1, s_tile1, s_tile0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (NBLK > 0 && NBLK % 2 == 0) {
+    for (int64_t c = 0; c < nchunks; ++c) {
+#pragma unroll
+      for (int nb = 0; nb < NBLK; nb += 2) {
+        step(c * NBLK + nb, s_tile0, s_tile1);
+        step(c * NBLK + nb + 1, s_tile1, s_tile0);
+      }
+    }
+  } else {
+    for (int64_t k = 0; k < nsteps; k += 2) {
+      step(k, s_tile0, s_tile1);
+      if (k + 1 < nsteps) step(k + 1, s_tile1, s_tile0);
+    }
   }
   if (valid) {
     epilogue(nchunks - 1);
@@ -366,19 +437,26 @@ template <typename ACT, bool GATE, int KPL>
 hipError_t launch_kpl(const ScanArgs& a, hipStream_t s) {
   constexpr int CH = 64 * KPL;
   const int64_t nchunks = (a.L + CH - 1) / CH;
-  const int64_t packed4 = a.batch * nchunks * a.N * 2 * (CH / 4);
-  const int pack_blocks = static_cast<int>(std::min<int64_t>((packed4 + 255) / 256, 65536));
+  const int64_t pack_threads = a.batch * nchunks * (CH / 4) * 2;
+  const int pack_blocks = static_cast<int>(std::min<int64_t>((pack_threads + 255) / 256, 65536));
+  const int vec4 = (a.N % 4 == 0) && (reinterpret_cast<uintptr_t>(a.Bm) % (4 * ACT::kBytes) == 0) &&
+                   (reinterpret_cast<uintptr_t>(a.Cm) % (4 * ACT::kBytes) == 0);
   hipLaunchKernelGGL((pack_bc_kernel<ACT, KPL>), dim3(pack_blocks), dim3(256), 0, s, a.Bm, a.Cm,
-                     reinterpret_cast<float4*>(a.workspace), a.batch, a.L, a.N, nchunks);
+                     reinterpret_cast<float4*>(a.workspace), a.batch, a.L, a.N, nchunks, vec4);
   const int n_dblk = static_cast<int>((a.D + kW - 1) / kW);
   const int64_t blocks = a.batch * n_dblk;
   const bool vec = (a.L % 8 == 0) && aligned16(a.u) && aligned16(a.delta) && aligned16(a.y) &&
                    (a.z == nullptr || aligned16(a.z));
   const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
-  if (vec)
-    hipLaunchKernelGGL((scan_chunked_kernel<ACT, GATE, KPL, true>), grid, block, 0, s, a, n_dblk);
+  const bool n16 = a.N > 12 && a.N <= 16;
+  if (vec && n16)
+    hipLaunchKernelGGL((scan_chunked_kernel<ACT, GATE, KPL, true, 4>), grid, block, 0, s, a, n_dblk);
+  else if (vec)
+    hipLaunchKernelGGL((scan_chunked_kernel<ACT, GATE, KPL, true, 0>), grid, block, 0, s, a, n_dblk);
+  else if (n16)
+    hipLaunchKernelGGL((scan_chunked_kernel<ACT, GATE, KPL, false, 4>), grid, block, 0, s, a, n_dblk);
   else
-    hipLaunchKernelGGL((scan_chunked_kernel<ACT, GATE, KPL, false>), grid, block, 0, s, a, n_dblk);
+    hipLaunchKernelGGL((scan_chunked_kernel<ACT, GATE, KPL, false, 0>), grid, block, 0, s, a, n_dblk);
   return hipGetLastError();
 }
 
