@@ -28,10 +28,10 @@
 //   * B and C are shared by all channels of a row.  A small pre-pass packs them
 //     (as float32) into a workspace laid out exactly like the LDS tiles: per
 //     (b, chunk, state, B|C) a 4*CH-byte block in the order the lanes read it.
-//     Each step of the kernel covers kNB states of one chunk; the workgroup copies
-//     the next step's tile into the other of two LDS buffers with direct
-//     global->LDS loads (no registers) while it computes on the current one, and
-//     one barrier per step publishes it;
+//     Each step of the kernel covers kNB states of one chunk; the workgroup loads
+//     the next step's tile into registers while it computes on the current one
+//     and writes it to the other of two LDS buffers, and one barrier per step
+//     publishes it;
 //   * a wave loads its next chunk's u and delta into registers and this chunk's z
 //     into LDS during the current chunk, and stores the previous chunk's y at its
 //     first step, one kind of traffic per step: every barrier waits for the wave's
@@ -122,62 +122,57 @@ struct TokenIO<ActBF16, KPL> {
 // Workspace layout, float32: [b][chunk][n][m = B, C][q][i][r] with token
 // t = chunk*CH + i*KPL + 4q + r (zero past L).  One block [q][i][r] is 4*CH
 // bytes; a step tile (kNB states x {B, C}) is kNB*2 consecutive blocks.
-// One thread per (b, token quad, matrix): it reads the quad's 4 token rows
-// (contiguous, so a wave reads one contiguous span) and writes one float4 per
-// state.
+// One thread per (b, token quad, matrix, group of 4 states): it reads 4 states of
+// 4 consecutive token rows (four threads cover a quad's rows, so a wave reads one
+// contiguous span when N == 16) and writes one float4 of 4 tokens per state.
 template <typename ACT, int KPL>
-__global__ __launch_bounds__(256) void pack_bc_kernel(const void* __restrict__ Bm, const void* __restrict__ Cm,
-                                                      float4* __restrict__ ws, int64_t batch, int64_t L, int N,
-                                                      int64_t nchunks, int vec4) {
+__global__ __launch_bounds__(64) void pack_bc_kernel(const void* __restrict__ Bm, const void* __restrict__ Cm,
+                                                     float4* __restrict__ ws, int64_t batch, int64_t L, int N,
+                                                     int64_t nchunks, int vec4) {
   constexpr int CH = 64 * KPL;
+  const int nsq = (N + 3) / 4;                           // state groups
   const int64_t quads = nchunks * (CH / 4);              // token quads per batch row (padded)
-  const int64_t total = batch * quads * 2;
+  const int64_t total = batch * quads * 2 * nsq;
   for (int64_t g = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; g < total;
        g += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const int m = static_cast<int>(g % 2);
-    const int64_t gq = (g / 2) % quads;                   // token quad within the batch row
-    const int64_t b = g / (2 * quads);
+    const int sq = static_cast<int>(g % nsq);
+    const int m = static_cast<int>((g / nsq) % 2);
+    const int64_t gq = (g / (2 * nsq)) % quads;          // token quad within the batch row
+    const int64_t b = g / (2 * nsq * quads);
     const int64_t t0 = gq * 4;
     const int64_t c = t0 / CH;
-    const int tc = static_cast<int>(t0 - c * CH);         // token within the chunk
+    const int tc = static_cast<int>(t0 - c * CH);        // token within the chunk
     const int i = tc / KPL;
     const int q = (tc % KPL) / 4;
+    const int n0 = sq * 4;
     const void* src = m == 0 ? Bm : Cm;
-    float4* dst = ws + ((b * nchunks + c) * N * 2 + m) * (CH / 4) + q * 64 + i;
-    const int64_t stride = 2 * (CH / 4);                  // float4 between consecutive states
-    if (vec4) {                                           // N % 4 == 0, rows 4-state aligned
-#pragma unroll 4
-      for (int n = 0; n < N; n += 4) {
-        float4 r4[4];
+    const int64_t stride = 2 * (CH / 4);                 // float4 between consecutive states
+    float4* dst = ws + ((b * nchunks + c) * N * 2 + m) * (CH / 4) + q * 64 + i + n0 * stride;
+    float4 r4[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int64_t t = t0 + r;
-          const int64_t o = (b * L + (t < L ? t : 0)) * N + n;
-          float4 x;
-          if constexpr (ACT::kBytes == 4) {
-            x = *reinterpret_cast<const float4*>(static_cast<const float*>(src) + o);
-          } else {
-            const uint2 w2 = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(src) + o);
-            x = make_float4(bf16_lo(w2.x), bf16_hi(w2.x), bf16_lo(w2.y), bf16_hi(w2.y));
-          }
-          r4[r] = t < L ? x : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int r = 0; r < 4; ++r) {
+      const int64_t t = t0 + r;
+      const int64_t o = (b * L + (t < L ? t : 0)) * N + n0;
+      float4 x;
+      if (vec4) {                                        // N % 4 == 0 and 4-state aligned rows
+        if constexpr (ACT::kBytes == 4) {
+          x = *reinterpret_cast<const float4*>(static_cast<const float*>(src) + o);
+        } else {
+          const uint2 w2 = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(src) + o);
+          x = make_float4(bf16_lo(w2.x), bf16_hi(w2.x), bf16_lo(w2.y), bf16_hi(w2.y));
         }
-        dst[(n + 0) * stride] = make_float4(r4[0].x, r4[1].x, r4[2].x, r4[3].x);
-        dst[(n + 1) * stride] = make_float4(r4[0].y, r4[1].y, r4[2].y, r4[3].y);
-        dst[(n + 2) * stride] = make_float4(r4[0].z, r4[1].z, r4[2].z, r4[3].z);
-        dst[(n + 3) * stride] = make_float4(r4[0].w, r4[1].w, r4[2].w, r4[3].w);
+      } else {
+        x.x = n0 + 0 < N ? load_act<ACT>(src, o + 0) : 0.f;
+        x.y = n0 + 1 < N ? load_act<ACT>(src, o + 1) : 0.f;
+        x.z = n0 + 2 < N ? load_act<ACT>(src, o + 2) : 0.f;
+        x.w = n0 + 3 < N ? load_act<ACT>(src, o + 3) : 0.f;
       }
-    } else {
-      for (int n = 0; n < N; ++n) {
-        float v[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int64_t t = t0 + r;
-          v[r] = t < L ? load_act<ACT>(src, (b * L + t) * N + n) : 0.0f;
-        }
-        dst[n * stride] = make_float4(v[0], v[1], v[2], v[3]);
-      }
+      r4[r] = t < L ? x : make_float4(0.f, 0.f, 0.f, 0.f);
     }
+    dst[0] = make_float4(r4[0].x, r4[1].x, r4[2].x, r4[3].x);
+    if (n0 + 1 < N) dst[stride] = make_float4(r4[0].y, r4[1].y, r4[2].y, r4[3].y);
+    if (n0 + 2 < N) dst[2 * stride] = make_float4(r4[0].z, r4[1].z, r4[2].z, r4[3].z);
+    if (n0 + 3 < N) dst[3 * stride] = make_float4(r4[0].w, r4[1].w, r4[2].w, r4[3].w);
   }
 }
 
@@ -332,9 +327,6 @@ __global__ __launch_bounds__(kThreads) void scan_chunked_kernel(ScanArgs p, int 
       }
     }
     float P = exp2_hw(a2 * sdl);                     // this lane's decay over its tokens
-    float4 cq[KPL / 4];                              // C reads issued before the scan
-#pragma unroll
-    for (int q = 0; q < KPL / 4; ++q) cq[q] = sC[q * 64 + lane];
     wave_scan_pairs(P, h);                           // h: true state after this lane
     const float hin = wave_shift_up(h, carry);       // true state before this lane
     const float cnew = wave_lane63(h);
@@ -342,7 +334,8 @@ __global__ __launch_bounds__(kThreads) void scan_chunked_kernel(ScanArgs p, int 
     float hh = hin;
 #pragma unroll
     for (int q = 0; q < KPL / 4; ++q) {
-      const float cs[4] = {cq[q].x, cq[q].y, cq[q].z, cq[q].w};
+      const float4 cc = sC[q * 64 + lane];
+      const float cs[4] = {cc.x, cc.y, cc.z, cc.w};
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int j = 4 * q + r;
@@ -354,13 +347,31 @@ __global__ __launch_bounds__(kThreads) void scan_chunked_kernel(ScanArgs p, int 
 
   // Tile of step k = (chunk k / nblk, states n0 = (k % nblk) * kNB ...) is the
   // contiguous run of float4 at ws + (c * N + n0) * 2 * BLK4 covering min(kNB,
-  // N - n0) states.  Wave w copies its 1 KB pieces w, w + kW, ... into dst.
-  auto issue_tile = [&](int64_t k, float4* dst) {
+  // N - n0) states.  Thread t moves float4 t, t + kThreads, ...: loaded into
+  // registers at the start of a step, written to LDS at its end (a plain vector
+  // load plus an LDS store is far cheaper to issue than a direct global->LDS copy).
+  constexpr int TPT = (TILE4 + kThreads - 1) / kThreads;    // tile float4 per thread
+  static_assert(TPT <= 3, "tile share per thread held in three registers");
+  float4 tr0 = make_float4(0.f, 0.f, 0.f, 0.f), tr1 = tr0, tr2 = tr0;
+  int tile_n4 = 0;                                           // float4 in the prefetched tile
+  const int e0 = threadIdx.x, e1 = threadIdx.x + kThreads, e2 = threadIdx.x + 2 * kThreads;
+  auto load_tile = [&](int64_t k) {
     const int64_t c = k / nblk;
     const int n0 = static_cast<int>(k % nblk) * kNB;
-    const int pieces = ((N - n0 < kNB) ? (N - n0) : kNB) * 2 * BLK4 / 64;
+    tile_n4 = ((N - n0 < kNB) ? (N - n0) : kNB) * 2 * BLK4;
     const float4* src = ws + (c * N + n0) * 2 * BLK4;
-    for (int piece = w; piece < pieces; piece += kW) dma16(src + piece * 64 + lane, dst + piece * 64);
+    // Unconditional loads (indices clamped into the tile; the surplus values are
+    // never stored) so the compiler cannot sink them to their use after the
+    // state loop, which would expose their latency at the end of every step.
+    tr0 = src[e0 < tile_n4 ? e0 : tile_n4 - 1];
+    if (TPT > 1) tr1 = src[e1 < tile_n4 ? e1 : tile_n4 - 1];
+    if (TPT > 2) tr2 = src[e2 < tile_n4 ? e2 : tile_n4 - 1];
+    asm volatile("" ::: "memory");                 // compiler-only fence: keep the loads here
+  };
+  auto store_tile = [&](float4* dst) {
+    if (e0 < tile_n4) dst[e0] = tr0;
+    if (TPT > 1 && e1 < tile_n4) dst[e1] = tr1;
+    if (TPT > 2 && e2 < tile_n4) dst[e2] = tr2;
   };
 
   // Every barrier first waits for all of this wave's outstanding memory
@@ -382,8 +393,8 @@ __global__ __launch_bounds__(kThreads) void scan_chunked_kernel(ScanArgs p, int 
       if (c > 0) epilogue(c - 1);                    // z of c-1 landed during chunk c-1
       prologue(c);                                   // u, delta of c prefetched during c-1
     }
-    if (k + 1 < nsteps) issue_tile(k + 1, nxt);
-    __builtin_amdgcn_sched_barrier(0);               // keep the issue order of memory operations
+    if (k + 1 < nsteps) load_tile(k + 1);
+    __builtin_amdgcn_sched_barrier(0);               // issue the tile loads now, not at their use
     if (valid) {
       if (c + 1 < nchunks && nb == st_u) prefetch_act(p.u, c + 1, u_raw);
       if (c + 1 < nchunks && nb == st_d) prefetch_act(p.delta, c + 1, d_raw);
@@ -395,22 +406,17 @@ __global__ __launch_bounds__(kThreads) void scan_chunked_kernel(ScanArgs p, int 
       const int nn = (N - n0 < kNB) ? (N - n0) : kNB;
       for (int nl = 0; nl < nn; ++nl) scan_state(cur + nl * 2 * BLK4, cur + (nl * 2 + 1) * BLK4, n0 + nl);
     }
-    // s_waitcnt vmcnt(0): vmcnt in bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8].
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
+    if (k + 1 < nsteps) store_tile(nxt);
+    __syncthreads();                                 // publishes the tile; waits for all loads
   };
 
   if (valid) {
     prefetch_act(p.u, 0, u_raw);
     prefetch_act(p.delta, 0, d_raw);
   }
-  issue_tile(0, s_tile0);
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_sched_barrier(0);
+  load_tile(0);
+  store_tile(s_tile0);
+  __syncthreads();
   if constexpr (NBLK > 0 && NBLK % 2 == 0) {
     for (int64_t c = 0; c < nchunks; ++c) {
 #pragma unroll
@@ -437,11 +443,11 @@ template <typename ACT, bool GATE, int KPL>
 hipError_t launch_kpl(const ScanArgs& a, hipStream_t s) {
   constexpr int CH = 64 * KPL;
   const int64_t nchunks = (a.L + CH - 1) / CH;
-  const int64_t pack_threads = a.batch * nchunks * (CH / 4) * 2;
-  const int pack_blocks = static_cast<int>(std::min<int64_t>((pack_threads + 255) / 256, 65536));
+  const int64_t pack_threads = a.batch * nchunks * (CH / 4) * 2 * ((a.N + 3) / 4);
+  const int pack_blocks = static_cast<int>(std::min<int64_t>((pack_threads + 63) / 64, 1 << 20));
   const int vec4 = (a.N % 4 == 0) && (reinterpret_cast<uintptr_t>(a.Bm) % (4 * ACT::kBytes) == 0) &&
                    (reinterpret_cast<uintptr_t>(a.Cm) % (4 * ACT::kBytes) == 0);
-  hipLaunchKernelGGL((pack_bc_kernel<ACT, KPL>), dim3(pack_blocks), dim3(256), 0, s, a.Bm, a.Cm,
+  hipLaunchKernelGGL((pack_bc_kernel<ACT, KPL>), dim3(pack_blocks), dim3(64), 0, s, a.Bm, a.Cm,
                      reinterpret_cast<float4*>(a.workspace), a.batch, a.L, a.N, nchunks, vec4);
   const int n_dblk = static_cast<int>((a.D + kW - 1) / kW);
   const int64_t blocks = a.batch * n_dblk;
