@@ -10,9 +10,11 @@ step reads a different copy of the inputs (enough copies to exceed the 256 MB
 Infinity Cache), so every step streams its inputs from HBM.  The K steps are
 captured in one HIP graph and replayed between two synchronisations.
 
-Prints one JSON line: elements/s (B*L*D*N per second), the roofline of the
-dominant kernel (algorithmic bytes / average kernel time, against 8 TB/s), and
-the float64 CPU oracle timed on this host on a bounded sample.
+Prints one JSON line: elements/s (B*L*D*N per second); the roofline of the
+call (the scan is bound by the vector ALUs: algorithmic VALU slots / average call
+time against the single-issue fp32 peak; the decode step by HBM bandwidth); the
+achieved HBM GB/s against 8 TB/s; and the float64 CPU oracle timed on this
+host's cores on a bounded sample.
 """
 from __future__ import annotations
 
@@ -31,6 +33,8 @@ sys.path.insert(0, ROOT)
 import synth  # noqa: E402
 
 PEAK_HBM_GBS = 8000.0
+PEAK_VALU_TSLOTS = 256 * 4 * 16 * 2.4e9 / 1e12    # 39.32 T single-issue fp32 lane slots/s
+ALU_SLOTS_PER_ELEMENT = 6                           # 4 fp32 ops + one exp2 at half rate
 MALL_BYTES = 256 << 20
 CALIB_BYTES = 256 << 20
 DEFAULT_WORKLOAD = "mamba130m_f32"
@@ -67,43 +71,62 @@ def dev(torch, a):
     return torch.from_numpy(a.astype(np.float32, copy=False)).to("cuda")
 
 
-def cpu_baseline_scan(cfg, inp, budget_s=20.0):
-    """The float64 oracle, as it is, on a bounded sample of the workload: whole
-    channels (full length L) of the first batch rows, enough for ~budget_s."""
+def _oracle_shard(args):
+    """Worker: the oracle on one (batch row, channel block) shard; returns seconds."""
+    os.environ.setdefault("OMP_NUM_THREADS", "1")
     import oracle
-    try:
-        from threadpoolctl import threadpool_limits
-    except Exception:  # pragma: no cover
-        threadpool_limits = None
-    per_b = cfg.L * cfg.D * cfg.N
-    nb = cfg.batch
-    # time one small slice first to size the sample
+    (u, delta, A, B, C, Dk, z, bias, sp) = args
+    t0 = time.perf_counter()
+    oracle.selective_scan(u, delta, A, B, C, Dk, z, bias, sp)
+    return time.perf_counter() - t0
+
+
+def _oracle_warm(_):
+    import oracle  # noqa: F401
+    return 0
+
+
+def cpu_baseline_scan(cfg, inp, budget_s=20.0, workers=0):
+    """The float64 oracle, as it is, timed on this host's cores: the workload is split
+    into (batch row, channel block) shards run by a pool of worker processes, on as
+    many whole batch rows as fit in about budget_s of CPU time."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+    import oracle
+    ncpu = len(os.sched_getaffinity(0))
+    workers = workers or max(1, min(16, ncpu))
+    # size the sample from a single-process probe on one channel block
     d_probe = min(cfg.D, 64)
+    sl = lambda x, b0, b1, d0, d1: None if x is None else x[b0:b1, d0:d1]
+    vec = lambda x, d0, d1: None if x is None else x[d0:d1]
     t0 = time.perf_counter()
     oracle.selective_scan(inp.u[:1, :d_probe], inp.delta[:1, :d_probe], inp.A[:d_probe], inp.B[:1], inp.C[:1],
-                          None if inp.Dskip is None else inp.Dskip[:d_probe],
-                          None if inp.z is None else inp.z[:1, :d_probe],
-                          None if inp.delta_bias is None else inp.delta_bias[:d_probe], inp.delta_softplus)
-    t_probe = time.perf_counter() - t0
-    # numpy's per-step overhead dominates small slices; widen the slice to fill the budget
-    d_take = cfg.D
-    b_take = max(1, min(nb, int(budget_s / max(t_probe * cfg.D / d_probe, 1e-3))))
-    ctx = threadpool_limits(1) if threadpool_limits else None
-    if ctx:
-        ctx.__enter__()
-    try:
+                          vec(inp.Dskip, 0, d_probe), sl(inp.z, 0, 1, 0, d_probe),
+                          vec(inp.delta_bias, 0, d_probe), inp.delta_softplus)
+    per_row_cpu = (time.perf_counter() - t0) * cfg.D / d_probe
+    b_take = max(1, min(cfg.batch, int(budget_s / max(per_row_cpu, 1e-3))))
+    # a sample far below the budget (the whole workload) is repeated, for a stable time
+    reps = max(1, min(20, int(budget_s / max(per_row_cpu * b_take, 1e-3))))
+    dblk = max(1, -(-cfg.D // max(1, (workers + b_take - 1) // b_take)))
+    shards = []
+    for b in range(b_take):
+        for d0 in range(0, cfg.D, dblk):
+            d1 = min(cfg.D, d0 + dblk)
+            shards.append((sl(inp.u, b, b + 1, d0, d1), sl(inp.delta, b, b + 1, d0, d1), inp.A[d0:d1],
+                           inp.B[b:b + 1], inp.C[b:b + 1], vec(inp.Dskip, d0, d1), sl(inp.z, b, b + 1, d0, d1),
+                           vec(inp.delta_bias, d0, d1), inp.delta_softplus))
+    with cf.ProcessPoolExecutor(max_workers=workers, mp_context=mp.get_context("spawn")) as ex:
+        list(ex.map(_oracle_warm, range(workers)))   # start the workers and import the oracle
         t0 = time.perf_counter()
-        oracle.selective_scan(inp.u[:b_take], inp.delta[:b_take], inp.A, inp.B[:b_take], inp.C[:b_take],
-                              inp.Dskip, None if inp.z is None else inp.z[:b_take], inp.delta_bias,
-                              inp.delta_softplus)
-        dt = time.perf_counter() - t0
-    finally:
-        if ctx:
-            ctx.__exit__(None, None, None)
-    elems = b_take * per_b
-    return {"value": elems / dt, "unit": "elements/s", "cores": 1, "kind": "oracle",
-            "sample": f"{b_take} of {nb} batch rows x all {d_take} channels x full L={cfg.L}, "
-                      f"N={cfg.N} ({elems:.3e} elements, {dt:.1f} s, float64 numpy, 1 thread)"}
+        secs = list(ex.map(_oracle_shard, shards * reps))
+        wall = time.perf_counter() - t0
+    elems = b_take * cfg.L * cfg.D * cfg.N
+    return {"value": reps * elems / wall, "unit": "elements/s", "cores": workers, "kind": "oracle",
+            "sample": f"{b_take} of {cfg.batch} batch rows x all {cfg.D} channels x full L={cfg.L}, N={cfg.N} "
+                      f"({elems:.3e} elements), {reps}x, in {len(shards)} shards per pass over {workers} "
+                      f"worker processes "
+                      f"(float64 numpy, 1 thread each; {wall:.1f} s wall, {sum(secs):.1f} s CPU); "
+                      f"host has {ncpu} usable cores"}
 
 
 def bench_scan(args, torch, lib_ops):
@@ -230,15 +253,31 @@ def main():
     wall = time.perf_counter() - w0
     gpu_ms = ev0.elapsed_time(ev1)
     ms_per_step = wall * 1e3 / K
-    kernel_ms = gpu_ms / K            # one kernel launch per step: events bracket the K launches
+    launch_s = gpu_ms / K / 1e3       # events bracket the K calls; a call is one step
     value = elements / (ms_per_step / 1e3)
-    achieved = nbytes / (kernel_ms / 1e3) / 1e9
+    hbm_gbs = nbytes / launch_s / 1e9
 
     cpu = None
     if kind == "scan" and not args.no_cpu_baseline:
         cpu = cpu_baseline_scan(cfg, inp, args.cpu_budget)
 
     traffic = traffic_from_profiles(args.workload, kind)
+    hbm = {"achieved": hbm_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": hbm_gbs / PEAK_HBM_GBS,
+           "algorithmic_bytes_per_launch": nbytes}
+    if kind == "scan":
+        # Bound by the vector ALUs: per element 4 fp32 VALU ops plus one exp2, which
+        # issues at half the VALU rate (2 slots), against 256 CUs x 4 SIMDs x 16 lanes
+        # x 2.4 GHz single-issue fp32 slots.
+        slots = ALU_SLOTS_PER_ELEMENT * elements
+        alu = slots / launch_s / 1e12
+        roofline = {"bound": "alu", "kernel": "pack_bc_kernel + scan_chunked_kernel (one scan call)",
+                    "achieved": alu, "peak": PEAK_VALU_TSLOTS, "unit": "T VALU slots/s",
+                    "frac": alu / PEAK_VALU_TSLOTS, "traffic": traffic,
+                    "algorithmic_slots_per_launch": slots, "slots_per_element": ALU_SLOTS_PER_ELEMENT,
+                    "avg_launch_us": launch_s * 1e6}
+    else:
+        roofline = dict(hbm, bound="hbm", kernel=KERNEL_NAME[kind], traffic=traffic,
+                        avg_launch_us=launch_s * 1e6)
     out = {
         "metric": "selective-scan elements/s (B*L*D*N) + achieved HBM GB/s vs peak, 1 GPU"
         if kind == "scan" else "decode-step elements/s (S*D*N per step) + achieved HBM GB/s vs peak, 1 GPU",
@@ -255,14 +294,12 @@ def main():
         "data": "synthetic (seeded; shapes and distributions of the named workload)",
         "config": ({"workload": args.workload, "batch": cfg.batch, "L": cfg.L, "D": cfg.D, "N": cfg.N,
                     "act_dtype": cfg.dtype, "gate": cfg.gate, "variant": args.variant,
-                    "tokens_per_lane": args.kpl or 16, "graph": graph is not None, "input_copies": sets}
+                    "tokens_per_lane": args.kpl or "auto", "graph": graph is not None, "input_copies": sets}
                    if kind == "scan" else
                    {"workload": args.workload, "sequences": cfg.batch, "D": cfg.D, "N": cfg.N,
                     "act_dtype": cfg.dtype, "graph": graph is not None, "input_copies": sets}),
-        "roofline": {"bound": "hbm", "kernel": KERNEL_NAME[kind], "achieved": achieved,
-                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
-                     "traffic": traffic, "algorithmic_bytes_per_launch": nbytes,
-                     "avg_kernel_us": kernel_ms * 1e3},
+        "roofline": roofline,
+        "hbm": hbm,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
