@@ -177,12 +177,15 @@ __global__ __launch_bounds__(64) void pack_bc_kernel(const void* __restrict__ Bm
 }
 
 // ---- the scan ----------------------------------------------------------------
-// NBLK > 0: the state count is fixed at compile time to (4*(NBLK-1), 4*NBLK]
-// steps per chunk, and the steps of a chunk are unrolled (so every prefetch
-// register is consumed before it is refilled within one loop iteration, and the
-// compiler's wait tracking stays exact).  NBLK = 0: any N, steps in a runtime loop.
+// NBLK > 0: N == 4 * NBLK, fixed at compile time; the steps of a chunk are
+// unrolled (so every prefetch register is consumed before it is refilled within
+// one loop iteration, and the compiler's wait tracking stays exact) and the
+// per-state values sit in scalar registers.  NBLK = 0: any N, steps in a runtime
+// loop.
 template <typename ACT, bool GATE, int KPL, bool VEC, int NBLK>
 __global__ __launch_bounds__(kThreads) void scan_chunked_kernel(ScanArgs p, int n_dblk) {
+  // states processed two at a time where the registers allow it (8 tokens per lane)
+  constexpr bool PAIR = KPL <= 8;
   using IO = TokenIO<ACT, KPL>;
   using raw_t = typename IO::raw_t;
   constexpr int CH = 64 * KPL;
@@ -308,10 +311,11 @@ __global__ __launch_bounds__(kThreads) void scan_chunked_kernel(ScanArgs p, int 
     }
   };
 
-  // One state n over the current chunk; its B and C blocks are sB, sC in LDS.
-  auto scan_state = [&](const float4* __restrict__ sB, const float4* __restrict__ sC, int n) {
-    const float a2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, a2_v), n));
-    const float carry = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, carry_v), n));
+  // One state over the current chunk: its B and C blocks are sB, sC in LDS,
+  // a2 = A[d, n] * log2(e) and `carry` (the state before the chunk) are
+  // wave-uniform.  Returns the state after the chunk (lane 63's).
+  auto scan_one = [&](const float4* __restrict__ sB, const float4* __restrict__ sC, float a2,
+                      float carry) -> float {
     float av[KPL], bv[KPL];
     float h = lane0 ? carry : 0.0f;
 #pragma unroll
@@ -330,7 +334,6 @@ __global__ __launch_bounds__(kThreads) void scan_chunked_kernel(ScanArgs p, int 
     wave_scan_pairs(P, h);                           // h: true state after this lane
     const float hin = wave_shift_up(h, carry);       // true state before this lane
     const float cnew = wave_lane63(h);
-    carry_v = (lane == n) ? cnew : carry_v;
     float hh = hin;
 #pragma unroll
     for (int q = 0; q < KPL / 4; ++q) {
@@ -343,6 +346,65 @@ __global__ __launch_bounds__(kThreads) void scan_chunked_kernel(ScanArgs p, int 
         yv[j] = __builtin_fmaf(cs[r], hh, yv[j]);
       }
     }
+    return cnew;
+  };
+
+  // Two states at once, interleaved instruction by instruction: two independent
+  // dependency chains in every phase, and one DPP scan sequence with no wait states.
+  auto scan_two = [&](const float4* __restrict__ sB0, const float4* __restrict__ sC0, float a20, float carry0,
+                      const float4* __restrict__ sB1, const float4* __restrict__ sC1, float a21, float carry1,
+                      float& out0, float& out1) {
+    float av0[KPL], bv0[KPL], av1[KPL], bv1[KPL];
+    float h0 = lane0 ? carry0 : 0.0f;
+    float h1 = lane0 ? carry1 : 0.0f;
+#pragma unroll
+    for (int q = 0; q < KPL / 4; ++q) {
+      const float4 b0 = sB0[q * 64 + lane];
+      const float4 b1 = sB1[q * 64 + lane];
+      const float bs0[4] = {b0.x, b0.y, b0.z, b0.w};
+      const float bs1[4] = {b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = 4 * q + r;
+        av0[j] = exp2_hw(dl[j] * a20);
+        av1[j] = exp2_hw(dl[j] * a21);
+        bv0[j] = du[j] * bs0[r];
+        bv1[j] = du[j] * bs1[r];
+        h0 = __builtin_fmaf(av0[j], h0, bv0[j]);
+        h1 = __builtin_fmaf(av1[j], h1, bv1[j]);
+      }
+    }
+    float P0 = exp2_hw(a20 * sdl);
+    float P1 = exp2_hw(a21 * sdl);
+    wave_scan_pairs2(P0, h0, P1, h1);
+    float hh0 = wave_shift_up(h0, carry0);
+    float hh1 = wave_shift_up(h1, carry1);
+    out0 = wave_lane63(h0);
+    out1 = wave_lane63(h1);
+#pragma unroll
+    for (int q = 0; q < KPL / 4; ++q) {
+      const float4 c0 = sC0[q * 64 + lane];
+      const float4 c1 = sC1[q * 64 + lane];
+      const float cs0[4] = {c0.x, c0.y, c0.z, c0.w};
+      const float cs1[4] = {c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = 4 * q + r;
+        hh0 = __builtin_fmaf(av0[j], hh0, bv0[j]);
+        hh1 = __builtin_fmaf(av1[j], hh1, bv1[j]);
+        yv[j] = __builtin_fmaf(cs0[r], hh0, yv[j]);
+        yv[j] = __builtin_fmaf(cs1[r], hh1, yv[j]);
+      }
+    }
+  };
+
+  // Generic state loop: A*log2(e) and the carry of state n live in lane n of a
+  // register and are read with readlane.
+  auto scan_state = [&](const float4* sB, const float4* sC, int n) {
+    const float a2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, a2_v), n));
+    const float carry = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, carry_v), n));
+    const float cnew = scan_one(sB, sC, a2, carry);
+    carry_v = (lane == n) ? cnew : carry_v;
   };
 
   // Tile of step k = (chunk k / nblk, states n0 = (k % nblk) * kNB ...) is the
@@ -385,10 +447,52 @@ __global__ __launch_bounds__(kThreads) void scan_chunked_kernel(ScanArgs p, int 
   const int st_d = nblk > 2 ? 2 : st_u;
   const int st_z = nblk > 3 ? 3 : st_d;
 
-  // Step k computes on `cur` while the next step's tile lands in `nxt`.
-  auto step = [&](int64_t k, const float4* cur, float4* nxt) {
-    const int64_t c = k / nblk;
-    const int nb = static_cast<int>(k % nblk);
+  // Per-state wave-uniform values when the state count is fixed at compile time
+  // (NBLK > 0): A*log2(e) and the carry of state n in scalar registers, indexed
+  // by compile-time n once the steps are unrolled.
+  constexpr int NS = NBLK > 0 ? 4 * NBLK : 1;
+  float a2s[NS], cs[NS];
+  if constexpr (NBLK > 0) {
+#pragma unroll
+    for (int n = 0; n < NS; ++n) {
+      a2s[n] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, a2_v), n));
+      cs[n] = 0.0f;
+    }
+  }
+
+  // The states of step nb of the current chunk, from the tile `cur`.
+  auto states = [&](const float4* cur, int nb) {
+    const int n0 = nb * kNB;
+    if constexpr (NBLK > 0) {
+      constexpr int nn = kNB;                          // N == 4 * NBLK: every step is full
+      const float4* t = cur;
+      if constexpr (PAIR) {
+#pragma unroll
+        for (int nl = 0; nl < kNB; nl += 2) {
+          const int n = n0 + nl;
+          if (nl + 1 < nn) {
+            scan_two(t + nl * 2 * BLK4, t + (nl * 2 + 1) * BLK4, a2s[n], cs[n],
+                     t + (nl * 2 + 2) * BLK4, t + (nl * 2 + 3) * BLK4, a2s[n + 1], cs[n + 1], cs[n], cs[n + 1]);
+          } else if (nl < nn) {
+            cs[n] = scan_one(t + nl * 2 * BLK4, t + (nl * 2 + 1) * BLK4, a2s[n], cs[n]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int nl = 0; nl < kNB; ++nl) {
+          const int n = n0 + nl;
+          if (nl < nn) cs[n] = scan_one(t + nl * 2 * BLK4, t + (nl * 2 + 1) * BLK4, a2s[n], cs[n]);
+        }
+      }
+    } else {
+      const int nn = (N - n0 < kNB) ? (N - n0) : kNB;
+      for (int nl = 0; nl < nn; ++nl) scan_state(cur + nl * 2 * BLK4, cur + (nl * 2 + 1) * BLK4, n0 + nl);
+    }
+  };
+
+  // Step k (state block nb of chunk c) computes on `cur` while the next step's
+  // tile lands in `nxt`.
+  auto step = [&](int64_t k, int64_t c, int nb, const float4* cur, float4* nxt) {
     if (valid && nb == 0) {
       if (c > 0) epilogue(c - 1);                    // z of c-1 landed during chunk c-1
       prologue(c);                                   // u, delta of c prefetched during c-1
@@ -401,11 +505,7 @@ __global__ __launch_bounds__(kThreads) void scan_chunked_kernel(ScanArgs p, int 
       if (nb == st_z) prefetch_z(c);
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (valid) {
-      const int n0 = nb * kNB;
-      const int nn = (N - n0 < kNB) ? (N - n0) : kNB;
-      for (int nl = 0; nl < nn; ++nl) scan_state(cur + nl * 2 * BLK4, cur + (nl * 2 + 1) * BLK4, n0 + nl);
-    }
+    if (valid) states(cur, nb);
     if (k + 1 < nsteps) store_tile(nxt);
     __syncthreads();                                 // publishes the tile; waits for all loads
   };
@@ -421,15 +521,20 @@ __global__ __launch_bounds__(kThreads) void scan_chunked_kernel(ScanArgs p, int 
     for (int64_t c = 0; c < nchunks; ++c) {
 #pragma unroll
       for (int nb = 0; nb < NBLK; nb += 2) {
-        step(c * NBLK + nb, s_tile0, s_tile1);
-        step(c * NBLK + nb + 1, s_tile1, s_tile0);
+        step(c * NBLK + nb, c, nb, s_tile0, s_tile1);
+        step(c * NBLK + nb + 1, c, nb + 1, s_tile1, s_tile0);
       }
     }
   } else {
     for (int64_t k = 0; k < nsteps; k += 2) {
-      step(k, s_tile0, s_tile1);
-      if (k + 1 < nsteps) step(k + 1, s_tile1, s_tile0);
+      step(k, k / nblk, static_cast<int>(k % nblk), s_tile0, s_tile1);
+      if (k + 1 < nsteps) step(k + 1, (k + 1) / nblk, static_cast<int>((k + 1) % nblk), s_tile1, s_tile0);
     }
+  }
+  if constexpr (NBLK > 0) {
+    // carries back into lane n for the final-state store
+#pragma unroll
+    for (int n = 0; n < NS; ++n) carry_v = lane == n ? cs[n] : carry_v;
   }
   if (valid) {
     epilogue(nchunks - 1);
@@ -454,7 +559,7 @@ hipError_t launch_kpl(const ScanArgs& a, hipStream_t s) {
   const bool vec = (a.L % 8 == 0) && aligned16(a.u) && aligned16(a.delta) && aligned16(a.y) &&
                    (a.z == nullptr || aligned16(a.z));
   const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
-  const bool n16 = a.N > 12 && a.N <= 16;
+  const bool n16 = a.N == 16;
   if (vec && n16)
     hipLaunchKernelGGL((scan_chunked_kernel<ACT, GATE, KPL, true, 4>), grid, block, 0, s, a, n_dblk);
   else if (vec)
