@@ -135,10 +135,6 @@ def bench_scan(args, torch, lib_ops):
     nbytes = cfg.algorithmic_bytes()
     sets = args.sets or max(2, int(np.ceil(600e6 / nbytes)))
     A, Dk, bias = dev(torch, inp.A), dev(torch, inp.Dskip), dev(torch, inp.delta_bias)
-    # one scratch buffer (packed B/C tiles) shared by all steps: they run in stream order
-    ws = torch.empty(max(1, lib_ops.workspace_bytes(cfg.batch, cfg.L, cfg.D, cfg.N,
-                                                    torch.bfloat16 if cfg.dtype == "bf16" else torch.float32)),
-                     dtype=torch.uint8, device="cuda")
     bufs = []
     for _ in range(sets):
         t = {k: dev(torch, inp.upload_array(k)) if inp.upload_array(k) is not None else None
@@ -150,7 +146,7 @@ def bench_scan(args, torch, lib_ops):
     def step(i):
         t = bufs[i % sets]
         lib_ops.selective_scan_fwd(t["u"], t["delta"], A, t["B"], t["C"], Dk, t["z"], bias, True,
-                                   y=t["y"], final_state=t["fs"], workspace=ws, variant=args.variant,
+                                   y=t["y"], final_state=t["fs"], variant=args.variant,
                                    tokens_per_lane=args.kpl)
 
     return cfg, inp, nbytes, cfg.elements, sets, step, bufs
@@ -253,7 +249,7 @@ def main():
     wall = time.perf_counter() - w0
     gpu_ms = ev0.elapsed_time(ev1)
     ms_per_step = wall * 1e3 / K
-    launch_s = gpu_ms / K / 1e3       # events bracket the K calls; a call is one step
+    launch_s = gpu_ms / K / 1e3       # events bracket the K calls; a call is one kernel launch
     value = elements / (ms_per_step / 1e3)
     hbm_gbs = nbytes / launch_s / 1e9
 
@@ -270,7 +266,7 @@ def main():
         # x 2.4 GHz single-issue fp32 slots.
         slots = ALU_SLOTS_PER_ELEMENT * elements
         alu = slots / launch_s / 1e12
-        roofline = {"bound": "alu", "kernel": "pack_bc_kernel + scan_chunked_kernel (one scan call)",
+        roofline = {"bound": "alu", "kernel": KERNEL_NAME[kind],
                     "achieved": alu, "peak": PEAK_VALU_TSLOTS, "unit": "T VALU slots/s",
                     "frac": alu / PEAK_VALU_TSLOTS, "traffic": traffic,
                     "algorithmic_slots_per_launch": slots, "slots_per_element": ALU_SLOTS_PER_ELEMENT,

@@ -32,8 +32,8 @@
  *  - Results are deterministic: same inputs, shapes and device give
  *    bitwise-identical outputs.
  *  - Alignment: every pointer must be aligned to its element size.  16-byte
- *    aligned pointers and L a multiple of 8 select the vectorised kernels;
- *    other shapes run a slower path with the same results.
+ *    aligned pointers and L a multiple of 8 select the vectorised scan; other
+ *    shapes run a slower path with the same results.
  */
 #ifndef SSM_H
 #define SSM_H
@@ -61,7 +61,8 @@ typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
  *
  *   u, delta, z  : [batch][D][L] act   (each channel's time series is contiguous)
  *   A            : [D][N] float32      (the diagonal state matrix, one row per channel)
- *   Bm, Cm       : [batch][L][N] act   (shared by all D channels of a batch row)
+ *   Bm, Cm       : [batch][N][L] act   (each state's time series is contiguous;
+ *                                       shared by all D channels of a batch row)
  *   Dskip        : [D] float32 or NULL (NULL means 0)
  *   z            : NULL means no gate
  *   delta_bias   : [D] float32 or NULL (NULL means 0); added before the softplus
@@ -70,25 +71,21 @@ typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
  *   final_state  : out [batch][D][N] float32, h[b, L-1, d, :], or NULL
  *   batch, L, D  : >= 0 (a zero size is a no-op; with L == 0 the final state is 0)
  *   N            : 1..64
- *   workspace    : device scratch owned by the caller, 16-byte aligned, at least
- *                  ssm_selective_scan_workspace_size() bytes (the chunked kernel
- *                  packs B and C there as float32 tiles); may be NULL when that
- *                  size is 0 or the sequential kernel is selected.  Its contents
- *                  are overwritten; it must not overlap any other argument, and
- *                  calls that share one workspace must not run concurrently.
+ *
+ * The pages write B and C as (batch, L, N); the library stores every time series
+ * contiguous along L (u, delta, z, y per channel; B, C per state), so that each
+ * is read as coalesced vectors along L.  The values are the same.
  *
  * Errors: SSM_ERR_INVALID_ARG for a NULL required pointer, a negative size, a
- * misaligned pointer, a missing or too-small workspace, or y / final_state /
- * workspace overlapping any input or each other; SSM_ERR_UNSUPPORTED for N
- * outside [1, 64] or a bad dtype; SSM_ERR_HIP when no device is usable or the
- * launch fails.
+ * misaligned pointer, or y / final_state overlapping any input or each other;
+ * SSM_ERR_UNSUPPORTED for N outside [1, 64] or a bad dtype; SSM_ERR_HIP when no
+ * device is usable or the launch fails.
  */
 ssm_status ssm_selective_scan_fwd(
     const void *u, const void *delta, const float *A, const void *Bm, const void *Cm,
     const float *Dskip, const void *z, const float *delta_bias, int delta_softplus,
     void *y, float *final_state,
-    int64_t batch, int64_t L, int64_t D, int64_t N, ssm_dtype dt,
-    void *workspace, size_t workspace_bytes, void *stream);
+    int64_t batch, int64_t L, int64_t D, int64_t N, ssm_dtype dt, void *stream);
 
 /*
  * Same operation with an explicit kernel choice, for testing that every
@@ -105,8 +102,7 @@ ssm_status ssm_selective_scan_fwd_variant(
     const void *u, const void *delta, const float *A, const void *Bm, const void *Cm,
     const float *Dskip, const void *z, const float *delta_bias, int delta_softplus,
     void *y, float *final_state,
-    int64_t batch, int64_t L, int64_t D, int64_t N, ssm_dtype dt,
-    void *workspace, size_t workspace_bytes, void *stream,
+    int64_t batch, int64_t L, int64_t D, int64_t N, ssm_dtype dt, void *stream,
     int variant, int tokens_per_lane);
 
 /*
@@ -132,12 +128,6 @@ ssm_status ssm_state_update(
     const float *Dskip, const void *z_t, const float *delta_bias, int delta_softplus,
     void *y_t,
     int64_t batch, int64_t D, int64_t N, ssm_dtype dt, void *stream);
-
-/* Workspace bytes ssm_selective_scan_fwd needs for this shape: the packed B/C
- * tiles of the chunked kernel, batch * ceil(L / 1024) * 1024 * N * 8 bytes (0 for
- * an empty or invalid shape).  Enough for every variant and tokens_per_lane. */
-size_t ssm_selective_scan_workspace_size(int64_t batch, int64_t L, int64_t D, int64_t N,
-                                         ssm_dtype dt);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char *ssm_status_string(ssm_status s);

@@ -31,13 +31,11 @@ _int = ctypes.c_int
 # name -> (restype, argtypes); mirrors include/ssm.h
 SIGNATURES = {
     "ssm_selective_scan_fwd": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _vp, _vp,
-                                      _i64, _i64, _i64, _i64, _int, _vp, ctypes.c_size_t, _vp]),
+                                      _i64, _i64, _i64, _i64, _int, _vp]),
     "ssm_selective_scan_fwd_variant": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _vp, _vp,
-                                              _i64, _i64, _i64, _i64, _int, _vp, ctypes.c_size_t, _vp,
-                                              _int, _int]),
+                                              _i64, _i64, _i64, _i64, _int, _vp, _int, _int]),
     "ssm_state_update": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _vp,
                                 _i64, _i64, _i64, _int, _vp]),
-    "ssm_selective_scan_workspace_size": (ctypes.c_size_t, [_i64, _i64, _i64, _i64, _int]),
     "ssm_status_string": (ctypes.c_char_p, [_int]),
     "ssm_version": (_int, []),
 }

@@ -12,14 +12,13 @@ struct ScanArgs {
   const void* u;         // [batch][D][L] act
   const void* delta;     // [batch][D][L] act (raw)
   const float* A;        // [D][N]
-  const void* Bm;        // [batch][L][N] act
-  const void* Cm;        // [batch][L][N] act
+  const void* Bm;        // [batch][N][L] act
+  const void* Cm;        // [batch][N][L] act
   const float* Dskip;    // [D] or null
   const void* z;         // [batch][D][L] act or null
   const float* bias;     // [D] or null
   void* y;               // [batch][D][L] act
   float* final_state;    // [batch][D][N] or null
-  void* workspace;       // chunked kernel: packed B/C, chunked_workspace_bytes() bytes
   int64_t batch, L, D;
   int N;
   int softplus;
@@ -46,9 +45,8 @@ struct StepArgs {
 hipError_t launch_scan_sequential(const ScanArgs& a, Dt dt, hipStream_t s);
 
 // Chunked wave-scan kernel.  Returns hipErrorInvalidValue when the shape does not
-// fit (callers check chunked_supported first) or the workspace is missing.
+// fit (callers check chunked_supported first).
 bool chunked_supported(const ScanArgs& a, Dt dt, int tokens_per_lane);
-size_t chunked_workspace_bytes(int64_t batch, int64_t L, int64_t N, int tokens_per_lane);
 hipError_t launch_scan_chunked(const ScanArgs& a, Dt dt, int tokens_per_lane, hipStream_t s);
 
 // Writes zeros to final_state (the L == 0 scan).

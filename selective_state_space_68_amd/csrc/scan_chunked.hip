@@ -25,13 +25,13 @@
 //     the carry for the next chunk is lane 63's end state.
 //
 // Data movement (kW waves = kW channels of one batch row per workgroup):
-//   * B and C are shared by all channels of a row.  A small pre-pass packs them
-//     (as float32) into a workspace laid out exactly like the LDS tiles: per
-//     (b, chunk, state, B|C) a 4*CH-byte block in the order the lanes read it.
-//     Each step of the kernel covers kNB states of one chunk; the workgroup loads
-//     the next step's tile into registers while it computes on the current one
-//     and writes it to the other of two LDS buffers, and one barrier per step
-//     publishes it;
+//   * B and C are shared by all channels of a row and stored [batch][N][L], so a
+//     state's values over a chunk are one contiguous run.  Each step of the
+//     kernel covers kNB states of one chunk: the workgroup loads the next step's
+//     B/C tile into registers (coalesced 16- or 8-byte vectors along L) while it
+//     computes on the current one, and at the end of the step writes it, as
+//     float32 and permuted into the order the lanes read it, to the other of two
+//     LDS buffers; one barrier per step publishes it;
 //   * a wave loads its next chunk's u and delta into registers and this chunk's z
 //     into LDS during the current chunk, and stores the previous chunk's y at its
 //     first step, one kind of traffic per step: every barrier waits for the wave's
@@ -40,7 +40,7 @@
 // No MFMA: the readout is a per-token dot product over n, not a shared-operand
 // contraction.  The kernel is bound by HBM bandwidth and by the VALU and
 // transcendental rate (one exp per element).
-#include <algorithm>
+#include <utility>
 
 #include "device_common.hpp"
 #include "kernels.hpp"
@@ -118,70 +118,61 @@ struct TokenIO<ActBF16, KPL> {
   }
 };
 
-// ---- B/C packing pre-pass --------------------------------------------------
-// Workspace layout, float32: [b][chunk][n][m = B, C][q][i][r] with token
-// t = chunk*CH + i*KPL + 4q + r (zero past L).  One block [q][i][r] is 4*CH
-// bytes; a step tile (kNB states x {B, C}) is kNB*2 consecutive blocks.
-// One thread per (b, token quad, matrix, group of 4 states): it reads 4 states of
-// 4 consecutive token rows (four threads cover a quad's rows, so a wave reads one
-// contiguous span when N == 16) and writes one float4 of 4 tokens per state.
-template <typename ACT, int KPL>
-__global__ __launch_bounds__(64) void pack_bc_kernel(const void* __restrict__ Bm, const void* __restrict__ Cm,
-                                                     float4* __restrict__ ws, int64_t batch, int64_t L, int N,
-                                                     int64_t nchunks, int vec4) {
-  constexpr int CH = 64 * KPL;
-  const int nsq = (N + 3) / 4;                           // state groups
-  const int64_t quads = nchunks * (CH / 4);              // token quads per batch row (padded)
-  const int64_t total = batch * quads * 2 * nsq;
-  for (int64_t g = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; g < total;
-       g += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const int sq = static_cast<int>(g % nsq);
-    const int m = static_cast<int>((g / nsq) % 2);
-    const int64_t gq = (g / (2 * nsq)) % quads;          // token quad within the batch row
-    const int64_t b = g / (2 * nsq * quads);
-    const int64_t t0 = gq * 4;
-    const int64_t c = t0 / CH;
-    const int tc = static_cast<int>(t0 - c * CH);        // token within the chunk
-    const int i = tc / KPL;
-    const int q = (tc % KPL) / 4;
-    const int n0 = sq * 4;
-    const void* src = m == 0 ? Bm : Cm;
-    const int64_t stride = 2 * (CH / 4);                 // float4 between consecutive states
-    float4* dst = ws + ((b * nchunks + c) * N * 2 + m) * (CH / 4) + q * 64 + i + n0 * stride;
-    float4 r4[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t t = t0 + r;
-      const int64_t o = (b * L + (t < L ? t : 0)) * N + n0;
-      float4 x;
-      if (vec4) {                                        // N % 4 == 0 and 4-state aligned rows
-        if constexpr (ACT::kBytes == 4) {
-          x = *reinterpret_cast<const float4*>(static_cast<const float*>(src) + o);
-        } else {
-          const uint2 w2 = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(src) + o);
-          x = make_float4(bf16_lo(w2.x), bf16_hi(w2.x), bf16_lo(w2.y), bf16_hi(w2.y));
-        }
-      } else {
-        x.x = n0 + 0 < N ? load_act<ACT>(src, o + 0) : 0.f;
-        x.y = n0 + 1 < N ? load_act<ACT>(src, o + 1) : 0.f;
-        x.z = n0 + 2 < N ? load_act<ACT>(src, o + 2) : 0.f;
-        x.w = n0 + 3 < N ? load_act<ACT>(src, o + 3) : 0.f;
-      }
-      r4[r] = t < L ? x : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    dst[0] = make_float4(r4[0].x, r4[1].x, r4[2].x, r4[3].x);
-    if (n0 + 1 < N) dst[stride] = make_float4(r4[0].y, r4[1].y, r4[2].y, r4[3].y);
-    if (n0 + 2 < N) dst[2 * stride] = make_float4(r4[0].z, r4[1].z, r4[2].z, r4[3].z);
-    if (n0 + 3 < N) dst[3 * stride] = make_float4(r4[0].w, r4[1].w, r4[2].w, r4[3].w);
+// One B/C tile element: the largest vector load of consecutive tokens of one
+// state (16 bytes): 4 float32 or 8 bfloat16 tokens, converted to kOut float4.
+template <typename ACT>
+struct TileIO;
+
+template <>
+struct TileIO<ActF32> {
+  static constexpr int kTok = 4;
+  static constexpr int kOut = 1;
+  using raw_t = float4;
+  static __device__ __forceinline__ raw_t load(const void* base, int64_t off) {
+    return *reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
   }
+  static __device__ __forceinline__ float4 out(const raw_t& r, int) { return r; }
+};
+
+template <>
+struct TileIO<ActBF16> {
+  static constexpr int kTok = 8;
+  static constexpr int kOut = 2;
+  using raw_t = uint4;
+  static __device__ __forceinline__ raw_t load(const void* base, int64_t off) {
+    return *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off);
+  }
+  static __device__ __forceinline__ float4 out(const raw_t& r, int j) {
+    const unsigned a = j == 0 ? r.x : r.z, b = j == 0 ? r.y : r.w;
+    return make_float4(bf16_lo(a), bf16_hi(a), bf16_lo(b), bf16_hi(b));
+  }
+};
+
+// Calls f(std::integral_constant<int, I>) for I = 0 .. N-1, as straight-line code
+// (a compile-time loop the compiler cannot leave rolled).
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Workgroup barrier that orders LDS only: outstanding global loads stay in
+// flight across it (the compiler waits for each where its value is used).
+__device__ __forceinline__ void barrier_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // ---- the scan ----------------------------------------------------------------
 // NBLK > 0: N == 4 * NBLK, fixed at compile time; the steps of a chunk are
-// unrolled (so every prefetch register is consumed before it is refilled within
-// one loop iteration, and the compiler's wait tracking stays exact) and the
-// per-state values sit in scalar registers.  NBLK = 0: any N, steps in a runtime
-// loop.
+// unrolled, the last chunk is peeled, and the per-state values sit in scalar
+// registers.  The steady state then has no branch around any load, so the
+// compiler's tracking of outstanding loads stays exact and it never waits for a
+// load before its value is needed.  NBLK = 0: any N, steps in a runtime loop.
 template <typename ACT, bool GATE, int KPL, bool VEC, int NBLK>
 __global__ __launch_bounds__(kThreads) void scan_chunked_kernel(ScanArgs p, int n_dblk) {
   // states processed two at a time where the registers allow it (8 tokens per lane)
@@ -191,65 +182,54 @@ __global__ __launch_bounds__(kThreads) void scan_chunked_kernel(ScanArgs p, int 
   constexpr int CH = 64 * KPL;
   constexpr int BLK4 = CH / 4;                       // float4 per (state, matrix) block
   constexpr int TILE4 = kNB * 2 * BLK4;              // float4 per step tile
-  constexpr int ZBYTES = KPL * ACT::kBytes * 64;     // z of one chunk for one wave
-  // Two distinct objects, so the compiler can tell the buffer being read from the
-  // one being filled (a DMA into one never forces a wait before reading the other).
-  __shared__ float4 s_tile0[TILE4];
-  __shared__ float4 s_tile1[TILE4];
-  __shared__ float4 s_z[(GATE && VEC) ? kW * ZBYTES / 16 : 1];
+  __shared__ float4 s_tile[2][TILE4];
 
   const int lane = threadIdx.x & 63;
   const bool lane0 = lane == 0;
   const int w = uniform_int(threadIdx.x >> 6);
   // Consecutive workgroups go to different XCDs (round robin over 8); taking the
   // batch row as blk % batch keeps one row per XCD when batch divides 8, so each
-  // XCD's L2 holds only that row's packed B/C tiles.
+  // XCD's L2 holds only that row's B and C.
   const int blk = blockIdx.x;
   const int64_t b = blk % p.batch;
-  const int64_t d = static_cast<int64_t>(blk / p.batch) * kW + w;
-  const bool valid = d < p.D;                        // wave-uniform
+  const int64_t d_own = static_cast<int64_t>(blk / p.batch) * kW + w;
+  const bool valid = d_own < p.D;                    // wave-uniform
+  // A wave past the last channel runs the same code on the last channel (so no
+  // branch depends on it) and stores nothing.
+  const int64_t d = valid ? d_own : p.D - 1;
   const int N = p.N;
   const int64_t L = p.L;
-  const int64_t row = (b * p.D + (valid ? d : 0)) * L;
-  const float bias = (valid && p.bias) ? p.bias[d] : 0.0f;
-  const float dsk = (valid && p.Dskip) ? p.Dskip[d] : 0.0f;
-  // A[d, n] * log2(e) in lane n (read once, before any store, so the state loop
-  // never issues a vector load of A).
-  const float a2_v = (valid && lane < N) ? p.A[d * N + lane] * kLog2e : 0.0f;
+  const int64_t row = (b * p.D + d) * L;
+  const float bias = p.bias ? p.bias[d] : 0.0f;
+  const float dsk = p.Dskip ? p.Dskip[d] : 0.0f;
+  // A[d, n] * log2(e) in lane n (read once, so the state loop never issues a
+  // vector load of A).
+  const float a2_v = lane < N ? p.A[d * N + lane] * kLog2e : 0.0f;
   float carry_v = 0.0f;                              // carry of state n lives in lane n
 
   const int nblk = NBLK > 0 ? NBLK : (N + kNB - 1) / kNB;
   const int64_t nchunks = (L + CH - 1) / CH;
   const int64_t nsteps = nchunks * nblk;
-  const float4* ws = reinterpret_cast<const float4*>(p.workspace) + b * nchunks * N * 2 * BLK4;
 
   float dl[KPL], du[KPL], yv[KPL];
   float sdl = 0.0f;
   int nv = KPL;                                      // valid tokens of this lane in its chunk
   raw_t u_raw[IO::kVec], d_raw[IO::kVec];            // next chunk's u and delta
+  raw_t z_raw[IO::kVec];                             // this chunk's z
 
-  // Issue the loads of chunk c's u (or delta) for full lanes of the vector path.
-  auto prefetch_act = [&](const void* src, int64_t c, raw_t (&dst)[IO::kVec]) {
-    const int64_t tl = c * CH + static_cast<int64_t>(lane) * KPL;
-    if (VEC && tl + KPL <= L) IO::load_raw(src, row + tl, dst);
-  };
-  // Copy chunk c's z for this wave into LDS: DMA q moves this lane's 16-byte
-  // vector q to s_z + w*ZBYTES + q*1024 + 16*lane.  Vectors at or past L read a
-  // valid address (their values are never used).
-  auto prefetch_z = [&](int64_t c) {
-    if constexpr (GATE && VEC) {
-      const int64_t tl = c * CH + static_cast<int64_t>(lane) * KPL;
-#pragma unroll
-      for (int q = 0; q < IO::kVec; ++q) {
-        const int64_t t = tl + q * (16 / ACT::kBytes);
-        const int64_t off = (t < L ? row + t : 0) * ACT::kBytes;
-        dma16(static_cast<const char*>(p.z) + off, reinterpret_cast<char*>(s_z) + w * ZBYTES + q * 1024);
-      }
+  // Vector path: load this lane's KPL values of chunk c.  The start is clamped
+  // into the row (the vector path needs L >= KPL), so a lane past the end loads
+  // real data that it never uses and the load needs no branch.
+  auto prefetch_act = [&](const void* src, int64_t c, raw_t (&dst)[IO::kVec]) __attribute__((always_inline)) {
+    if constexpr (VEC) {
+      int64_t tl = c * CH + static_cast<int64_t>(lane) * KPL;
+      tl = tl + KPL <= L ? tl : L - KPL;
+      IO::load_raw(src, row + tl, dst);
     }
   };
 
   // Per-token work of chunk c, once for all N states.
-  auto prologue = [&](int64_t c) {
+  auto prologue = [&](int64_t c) __attribute__((always_inline)) {
     const int64_t tl = c * CH + static_cast<int64_t>(lane) * KPL;
     const int64_t rem = L - tl;
     nv = rem >= KPL ? KPL : (rem > 0 ? static_cast<int>(rem) : 0);
@@ -285,16 +265,12 @@ __global__ __launch_bounds__(kThreads) void scan_chunked_kernel(ScanArgs p, int 
     }
   };
 
-  auto epilogue = [&](int64_t c) {
+  auto epilogue = [&](int64_t c) __attribute__((always_inline)) {
     const int64_t tl = c * CH + static_cast<int64_t>(lane) * KPL;
     if (GATE) {
       float zv[KPL];
-      if (VEC) {
-        raw_t zr[IO::kVec];
-        const raw_t* zs = reinterpret_cast<const raw_t*>(reinterpret_cast<const char*>(s_z) + w * ZBYTES);
-#pragma unroll
-        for (int q = 0; q < IO::kVec; ++q) zr[q] = zs[q * 64 + lane];
-        IO::unpack(zr, zv);
+      if (VEC && nv == KPL) {
+        IO::unpack(z_raw, zv);
       } else {
 #pragma unroll
         for (int j = 0; j < KPL; ++j) zv[j] = j < nv ? load_act<ACT>(p.z, row + tl + j) : 0.0f;
@@ -302,12 +278,14 @@ __global__ __launch_bounds__(kThreads) void scan_chunked_kernel(ScanArgs p, int 
 #pragma unroll
       for (int j = 0; j < KPL; ++j) yv[j] *= silu_f(zv[j]);
     }
-    if (VEC && nv == KPL) {
-      IO::store(p.y, row + tl, yv);
-    } else {
+    if (valid) {
+      if (VEC && nv == KPL) {
+        IO::store(p.y, row + tl, yv);
+      } else {
 #pragma unroll
-      for (int j = 0; j < KPL; ++j)
-        if (j < nv) store_act<ACT>(p.y, row + tl + j, yv[j]);
+        for (int j = 0; j < KPL; ++j)
+          if (j < nv) store_act<ACT>(p.y, row + tl + j, yv[j]);
+      }
     }
   };
 
@@ -315,7 +293,7 @@ __global__ __launch_bounds__(kThreads) void scan_chunked_kernel(ScanArgs p, int 
   // a2 = A[d, n] * log2(e) and `carry` (the state before the chunk) are
   // wave-uniform.  Returns the state after the chunk (lane 63's).
   auto scan_one = [&](const float4* __restrict__ sB, const float4* __restrict__ sC, float a2,
-                      float carry) -> float {
+                      float carry) __attribute__((always_inline)) -> float {
     float av[KPL], bv[KPL];
     float h = lane0 ? carry : 0.0f;
 #pragma unroll
@@ -353,7 +331,7 @@ __global__ __launch_bounds__(kThreads) void scan_chunked_kernel(ScanArgs p, int 
   // dependency chains in every phase, and one DPP scan sequence with no wait states.
   auto scan_two = [&](const float4* __restrict__ sB0, const float4* __restrict__ sC0, float a20, float carry0,
                       const float4* __restrict__ sB1, const float4* __restrict__ sC1, float a21, float carry1,
-                      float& out0, float& out1) {
+                      float& out0, float& out1) __attribute__((always_inline)) {
     float av0[KPL], bv0[KPL], av1[KPL], bv1[KPL];
     float h0 = lane0 ? carry0 : 0.0f;
     float h1 = lane0 ? carry1 : 0.0f;
@@ -400,49 +378,89 @@ __global__ __launch_bounds__(kThreads) void scan_chunked_kernel(ScanArgs p, int 
 
   // Generic state loop: A*log2(e) and the carry of state n live in lane n of a
   // register and are read with readlane.
-  auto scan_state = [&](const float4* sB, const float4* sC, int n) {
+  auto scan_state = [&](const float4* sB, const float4* sC, int n) __attribute__((always_inline)) {
     const float a2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, a2_v), n));
     const float carry = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, carry_v), n));
     const float cnew = scan_one(sB, sC, a2, carry);
     carry_v = (lane == n) ? cnew : carry_v;
   };
 
-  // Tile of step k = (chunk k / nblk, states n0 = (k % nblk) * kNB ...) is the
-  // contiguous run of float4 at ws + (c * N + n0) * 2 * BLK4 covering min(kNB,
-  // N - n0) states.  Thread t moves float4 t, t + kThreads, ...: loaded into
-  // registers at the start of a step, written to LDS at its end (a plain vector
-  // load plus an LDS store is far cheaper to issue than a direct global->LDS copy).
-  constexpr int TPT = (TILE4 + kThreads - 1) / kThreads;    // tile float4 per thread
+  // Tile of step k = (chunk c = k / nblk, states n0 = (k % nblk) * kNB ...): for
+  // each of its nn = min(kNB, N - n0) states, B's then C's CH values of the
+  // chunk, which are contiguous in memory.  Float4 f of a block (2 * state +
+  // matrix) holds tokens 4f .. 4f+3; in LDS it goes to the slot lane f / (KPL/4)
+  // reads as its vector f % (KPL/4), so the state loop's LDS reads are
+  // contiguous.  Threads move one 16-byte vector (kTok tokens) each per element:
+  // element e of the tile covers float4 (e % BLKR) * kOut ... of block e / BLKR.
+  // A block is a multiple of 64 elements, so a wave's block (state, matrix) is
+  // wave-uniform and only the token offset is per lane.
+  //
+  // Pipeline: tile j is loaded into register set j % 2 during step j - 2 and
+  // written (as float32, permuted) to LDS buffer j % 2 at the end of step j - 1,
+  // so each load has a whole step to arrive before its value is needed.
+  using TIO = TileIO<ACT>;
+  using traw_t = typename TIO::raw_t;
+  constexpr int BLKR = BLK4 / TIO::kOut;                     // 16-byte elements per block
+  constexpr int TILER = kNB * 2 * BLKR;                      // elements per tile
+  constexpr int TPT = (TILER + kThreads - 1) / kThreads;     // elements per thread
   static_assert(TPT <= 3, "tile share per thread held in three registers");
-  float4 tr0 = make_float4(0.f, 0.f, 0.f, 0.f), tr1 = tr0, tr2 = tr0;
-  int tile_n4 = 0;                                           // float4 in the prefetched tile
-  const int e0 = threadIdx.x, e1 = threadIdx.x + kThreads, e2 = threadIdx.x + 2 * kThreads;
-  auto load_tile = [&](int64_t k) {
+  static_assert(BLKR % 64 == 0, "a tile block spans whole waves");
+  traw_t tr[2][TPT];
+  int tile_nr[2] = {0, 0};                                   // elements in each staged tile
+  const int64_t bc_row = b * N * L;                          // this batch row of B and C
+  auto load_tile = [&](int64_t k, int set) __attribute__((always_inline)) {
     const int64_t c = k / nblk;
     const int n0 = static_cast<int>(k % nblk) * kNB;
-    tile_n4 = ((N - n0 < kNB) ? (N - n0) : kNB) * 2 * BLK4;
-    const float4* src = ws + (c * N + n0) * 2 * BLK4;
-    // Unconditional loads (indices clamped into the tile; the surplus values are
-    // never stored) so the compiler cannot sink them to their use after the
-    // state loop, which would expose their latency at the end of every step.
-    tr0 = src[e0 < tile_n4 ? e0 : tile_n4 - 1];
-    if (TPT > 1) tr1 = src[e1 < tile_n4 ? e1 : tile_n4 - 1];
-    if (TPT > 2) tr2 = src[e2 < tile_n4 ? e2 : tile_n4 - 1];
-    asm volatile("" ::: "memory");                 // compiler-only fence: keep the loads here
+    const int nr = ((N - n0 < kNB) ? (N - n0) : kNB) * 2 * BLKR;
+    tile_nr[set] = nr;
+    const int64_t tok0 = c * CH;
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) {
+      // this wave's first element, clamped into the tile (the surplus is never stored)
+      int eb = w * 64 + i * kThreads;
+      eb = eb < nr ? eb : nr - 64;
+      const int blkk = eb / BLKR;
+      const void* src = (blkk & 1) ? p.Cm : p.Bm;
+      const int64_t srow = bc_row + static_cast<int64_t>(n0 + (blkk >> 1)) * L;
+      const int64_t t = tok0 + TIO::kTok * (eb % BLKR + lane);
+      if constexpr (VEC) {
+        // Unconditional load, clamped into the row: a lane past L reloads the
+        // row's last tokens.  Those padding tokens have Delta = 0, so they are
+        // identity steps whatever finite B and C they see, and their y is never
+        // stored.
+        tr[set][i] = TIO::load(src, srow + (t < L ? t : L - TIO::kTok));
+      } else {
+        float x[TIO::kTok];
+#pragma unroll
+        for (int r = 0; r < TIO::kTok; ++r) x[r] = t + r < L ? load_act<ACT>(src, srow + t + r) : 0.0f;
+        if constexpr (ACT::kBytes == 4) {
+          tr[set][i] = make_float4(x[0], x[1], x[2], x[3]);
+        } else {
+          tr[set][i] = make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
+                                  pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7]));
+        }
+      }
+    }
   };
-  auto store_tile = [&](float4* dst) {
-    if (e0 < tile_n4) dst[e0] = tr0;
-    if (TPT > 1 && e1 < tile_n4) dst[e1] = tr1;
-    if (TPT > 2 && e2 < tile_n4) dst[e2] = tr2;
+  auto store_tile = [&](int set) __attribute__((always_inline)) {
+    float4* dst = s_tile[set];
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) {
+      const int eb = w * 64 + i * kThreads;
+      if (eb < tile_nr[set]) {
+        const int blkk = eb / BLKR;
+#pragma unroll
+        for (int j = 0; j < TIO::kOut; ++j) {
+          const int f = (eb % BLKR + lane) * TIO::kOut + j;
+          dst[blkk * BLK4 + (f % (KPL / 4)) * 64 + f / (KPL / 4)] = TIO::out(tr[set][i], j);
+        }
+      }
+    }
   };
 
-  // Every barrier first waits for all of this wave's outstanding memory
-  // operations (the copies into LDS must have landed before any wave reads the
-  // tile, and they are tracked by the same counter as the HBM loads, with no
-  // ordering between the two kinds).  So a load issued in a step lands within that
-  // step, and a chunk's HBM traffic is spread over its steps, one kind per step:
-  // y of the previous chunk is stored at step 0, the next chunk's u is loaded at
-  // step 1, its delta at step 2 and this chunk's z at step 3.
+  // HBM traffic is spread over a chunk's steps, one kind per step: y of the
+  // previous chunk is stored at step 0, the next chunk's u is loaded at step 1,
+  // its delta at step 2 and this chunk's z at step 3.
   const int st_u = nblk > 1 ? 1 : 0;
   const int st_d = nblk > 2 ? 2 : st_u;
   const int st_z = nblk > 3 ? 3 : st_d;
@@ -461,27 +479,23 @@ __global__ __launch_bounds__(kThreads) void scan_chunked_kernel(ScanArgs p, int 
   }
 
   // The states of step nb of the current chunk, from the tile `cur`.
-  auto states = [&](const float4* cur, int nb) {
+  auto states = [&](const float4* cur, int nb) __attribute__((always_inline)) {
     const int n0 = nb * kNB;
     if constexpr (NBLK > 0) {
       constexpr int nn = kNB;                          // N == 4 * NBLK: every step is full
       const float4* t = cur;
       if constexpr (PAIR) {
 #pragma unroll
-        for (int nl = 0; nl < kNB; nl += 2) {
+        for (int nl = 0; nl < nn; nl += 2) {
           const int n = n0 + nl;
-          if (nl + 1 < nn) {
-            scan_two(t + nl * 2 * BLK4, t + (nl * 2 + 1) * BLK4, a2s[n], cs[n],
-                     t + (nl * 2 + 2) * BLK4, t + (nl * 2 + 3) * BLK4, a2s[n + 1], cs[n + 1], cs[n], cs[n + 1]);
-          } else if (nl < nn) {
-            cs[n] = scan_one(t + nl * 2 * BLK4, t + (nl * 2 + 1) * BLK4, a2s[n], cs[n]);
-          }
+          scan_two(t + nl * 2 * BLK4, t + (nl * 2 + 1) * BLK4, a2s[n], cs[n],
+                   t + (nl * 2 + 2) * BLK4, t + (nl * 2 + 3) * BLK4, a2s[n + 1], cs[n + 1], cs[n], cs[n + 1]);
         }
       } else {
 #pragma unroll
-        for (int nl = 0; nl < kNB; ++nl) {
+        for (int nl = 0; nl < nn; ++nl) {
           const int n = n0 + nl;
-          if (nl < nn) cs[n] = scan_one(t + nl * 2 * BLK4, t + (nl * 2 + 1) * BLK4, a2s[n], cs[n]);
+          cs[n] = scan_one(t + nl * 2 * BLK4, t + (nl * 2 + 1) * BLK4, a2s[n], cs[n]);
         }
       }
     } else {
@@ -490,45 +504,53 @@ __global__ __launch_bounds__(kThreads) void scan_chunked_kernel(ScanArgs p, int 
     }
   };
 
-  // Step k (state block nb of chunk c) computes on `cur` while the next step's
-  // tile lands in `nxt`.
-  auto step = [&](int64_t k, int64_t c, int nb, const float4* cur, float4* nxt) {
-    if (valid && nb == 0) {
-      if (c > 0) epilogue(c - 1);                    // z of c-1 landed during chunk c-1
+  // Step k (state block nb of chunk c) computes on LDS buffer k % 2.  It loads
+  // tile k + 2 into register set k % 2 (unless `tail`), prefetches the next
+  // chunk's u and delta (unless `last_chunk`) and this chunk's z, and at its end
+  // writes tile k + 1 (register set (k + 1) % 2) to LDS buffer (k + 1) % 2.
+  auto step = [&](int64_t k, int64_t c, int nb, int par, bool last_chunk, bool tail2, bool tail1) __attribute__((always_inline)) {
+    if (nb == 0) {
+      if (c > 0) epilogue(c - 1);                    // z of c-1 loaded during chunk c-1
       prologue(c);                                   // u, delta of c prefetched during c-1
     }
-    if (k + 1 < nsteps) load_tile(k + 1);
-    __builtin_amdgcn_sched_barrier(0);               // issue the tile loads now, not at their use
-    if (valid) {
-      if (c + 1 < nchunks && nb == st_u) prefetch_act(p.u, c + 1, u_raw);
-      if (c + 1 < nchunks && nb == st_d) prefetch_act(p.delta, c + 1, d_raw);
-      if (nb == st_z) prefetch_z(c);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    if (valid) states(cur, nb);
-    if (k + 1 < nsteps) store_tile(nxt);
-    __syncthreads();                                 // publishes the tile; waits for all loads
+    if (!tail2) load_tile(k + 2, par);
+    if (!last_chunk && nb == st_u) prefetch_act(p.u, c + 1, u_raw);
+    if (!last_chunk && nb == st_d) prefetch_act(p.delta, c + 1, d_raw);
+    if (GATE && nb == st_z) prefetch_act(p.z, c, z_raw);
+    // (a wave past the last channel skips the state loop; keeping the loop in
+    // its own block also keeps the compiler from scheduling it into the
+    // surrounding per-token code, which costs registers)
+    if (valid) states(s_tile[par], nb);
+    if (!tail1) store_tile(par ^ 1);
+    barrier_lds();
   };
 
-  if (valid) {
-    prefetch_act(p.u, 0, u_raw);
-    prefetch_act(p.delta, 0, d_raw);
-  }
-  load_tile(0);
-  store_tile(s_tile0);
-  __syncthreads();
-  if constexpr (NBLK > 0 && NBLK % 2 == 0) {
-    for (int64_t c = 0; c < nchunks; ++c) {
-#pragma unroll
-      for (int nb = 0; nb < NBLK; nb += 2) {
-        step(c * NBLK + nb, c, nb, s_tile0, s_tile1);
-        step(c * NBLK + nb + 1, c, nb + 1, s_tile1, s_tile0);
-      }
+  prefetch_act(p.u, 0, u_raw);
+  prefetch_act(p.delta, 0, d_raw);
+  load_tile(0, 0);
+  if (nsteps > 1) load_tile(1, 1);
+  store_tile(0);
+  barrier_lds();
+  if constexpr (NBLK > 0) {
+    static_assert(NBLK % 2 == 0, "steps are unrolled in pairs");
+    for (int64_t c = 0; c + 1 < nchunks; ++c) {
+      static_for<NBLK>([&](auto nbc) __attribute__((always_inline)) {
+        constexpr int nb = decltype(nbc)::value;
+        step(c * NBLK + nb, c, nb, nb & 1, false, false, false);
+      });
     }
+    const int64_t c = nchunks - 1;
+    static_for<NBLK>([&](auto nbc) __attribute__((always_inline)) {
+      constexpr int nb = decltype(nbc)::value;
+      const int64_t k = c * NBLK + nb;
+      step(k, c, nb, nb & 1, true, k + 2 >= nsteps, k + 1 >= nsteps);
+    });
   } else {
     for (int64_t k = 0; k < nsteps; k += 2) {
-      step(k, k / nblk, static_cast<int>(k % nblk), s_tile0, s_tile1);
-      if (k + 1 < nsteps) step(k + 1, (k + 1) / nblk, static_cast<int>((k + 1) % nblk), s_tile1, s_tile0);
+      const int64_t c0 = k / nblk, c1 = (k + 1) / nblk;
+      step(k, c0, static_cast<int>(k % nblk), 0, c0 + 1 >= nchunks, k + 2 >= nsteps, k + 1 >= nsteps);
+      if (k + 1 < nsteps)
+        step(k + 1, c1, static_cast<int>((k + 1) % nblk), 1, c1 + 1 >= nchunks, k + 3 >= nsteps, k + 2 >= nsteps);
     }
   }
   if constexpr (NBLK > 0) {
@@ -536,28 +558,20 @@ __global__ __launch_bounds__(kThreads) void scan_chunked_kernel(ScanArgs p, int 
 #pragma unroll
     for (int n = 0; n < NS; ++n) carry_v = lane == n ? cs[n] : carry_v;
   }
-  if (valid) {
-    epilogue(nchunks - 1);
-    if (p.final_state && lane < N) p.final_state[(b * p.D + d) * N + lane] = carry_v;
-  }
+  epilogue(nchunks - 1);
+  if (valid && p.final_state && lane < N) p.final_state[(b * p.D + d) * N + lane] = carry_v;
 }
 
 bool aligned16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; }
 
 template <typename ACT, bool GATE, int KPL>
 hipError_t launch_kpl(const ScanArgs& a, hipStream_t s) {
-  constexpr int CH = 64 * KPL;
-  const int64_t nchunks = (a.L + CH - 1) / CH;
-  const int64_t pack_threads = a.batch * nchunks * (CH / 4) * 2 * ((a.N + 3) / 4);
-  const int pack_blocks = static_cast<int>(std::min<int64_t>((pack_threads + 63) / 64, 1 << 20));
-  const int vec4 = (a.N % 4 == 0) && (reinterpret_cast<uintptr_t>(a.Bm) % (4 * ACT::kBytes) == 0) &&
-                   (reinterpret_cast<uintptr_t>(a.Cm) % (4 * ACT::kBytes) == 0);
-  hipLaunchKernelGGL((pack_bc_kernel<ACT, KPL>), dim3(pack_blocks), dim3(64), 0, s, a.Bm, a.Cm,
-                     reinterpret_cast<float4*>(a.workspace), a.batch, a.L, a.N, nchunks, vec4);
   const int n_dblk = static_cast<int>((a.D + kW - 1) / kW);
   const int64_t blocks = a.batch * n_dblk;
+  // vector path: 16-byte vectors of u, delta, z, y along L, and 4-token vectors of
+  // B and C (L % 8 == 0 keeps every row start 16-byte aligned in both dtypes)
   const bool vec = (a.L % 8 == 0) && aligned16(a.u) && aligned16(a.delta) && aligned16(a.y) &&
-                   (a.z == nullptr || aligned16(a.z));
+                   (a.z == nullptr || aligned16(a.z)) && aligned16(a.Bm) && aligned16(a.Cm);
   const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
   const bool n16 = a.N == 16;
   if (vec && n16)
@@ -587,13 +601,6 @@ int resolve_kpl(int tokens_per_lane, Dt dt) {
 
 }  // namespace
 
-size_t chunked_workspace_bytes(int64_t batch, int64_t L, int64_t N, int tokens_per_lane) {
-  // 0 = whichever default the launch picks: size for the larger chunk (16 tokens per lane)
-  const int64_t ch = 64 * (tokens_per_lane == 0 ? 16 : tokens_per_lane);
-  const int64_t nchunks = (L + ch - 1) / ch;
-  return static_cast<size_t>(batch) * nchunks * N * 2 * ch * sizeof(float);
-}
-
 bool chunked_supported(const ScanArgs& a, Dt, int tokens_per_lane) {
   if (!(tokens_per_lane == 0 || tokens_per_lane == 8 || tokens_per_lane == 16)) return false;
   if (a.N < 1 || a.N > 64) return false;
@@ -602,7 +609,7 @@ bool chunked_supported(const ScanArgs& a, Dt, int tokens_per_lane) {
 }
 
 hipError_t launch_scan_chunked(const ScanArgs& a, Dt dt, int tokens_per_lane, hipStream_t s) {
-  if (!chunked_supported(a, dt, tokens_per_lane) || a.workspace == nullptr) return hipErrorInvalidValue;
+  if (!chunked_supported(a, dt, tokens_per_lane)) return hipErrorInvalidValue;
   const int kpl = resolve_kpl(tokens_per_lane, dt);
   const bool gate = a.z != nullptr;
   if (dt == Dt::F32)

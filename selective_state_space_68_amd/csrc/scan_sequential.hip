@@ -29,7 +29,7 @@ __global__ __launch_bounds__(64) void scan_sequential_kernel(ScanArgs p) {
   const float bias = p.bias ? p.bias[d] : 0.0f;
   const float dsk = p.Dskip ? p.Dskip[d] : 0.0f;
   const int64_t row = ch * p.L;                // u / delta / z / y offset of this channel
-  const int64_t bc_row = b * p.L * N;          // B / C offset of this batch row
+  const int64_t bc_row = b * N * p.L;          // B / C offset of this batch row ([N][L] within it)
 
   for (int64_t t = 0; t < p.L; ++t) {
     const float u = load_act<ACT>(p.u, row + t);
@@ -37,13 +37,13 @@ __global__ __launch_bounds__(64) void scan_sequential_kernel(ScanArgs p) {
     if (p.softplus) dl = softplus_f(dl);
     const float du = dl * u;
     float y = 0.0f;
-    const int64_t bo = bc_row + t * N;
+    const int64_t bo = bc_row + t;
 #pragma unroll
     for (int n = 0; n < NB; ++n) {
       if (n < N) {
         const float a = exp2_hw(dl * a2[n]);
-        h[n] = __builtin_fmaf(a, h[n], du * load_act<ACT>(p.Bm, bo + n));
-        y = __builtin_fmaf(load_act<ACT>(p.Cm, bo + n), h[n], y);
+        h[n] = __builtin_fmaf(a, h[n], du * load_act<ACT>(p.Bm, bo + n * p.L));
+        y = __builtin_fmaf(load_act<ACT>(p.Cm, bo + n * p.L), h[n], y);
       }
     }
     y = __builtin_fmaf(dsk, u, y);

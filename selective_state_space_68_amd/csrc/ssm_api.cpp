@@ -11,7 +11,7 @@
 
 namespace {
 
-constexpr int kVersion = 10000;  // 1.0.0
+constexpr int kVersion = 20000;  // 2.0.0: B and C stored [batch][N][L], no workspace
 
 struct Span {
   uintptr_t lo = 0, hi = 0;  // [lo, hi); empty when lo == hi
@@ -107,17 +107,12 @@ const char* ssm_status_string(ssm_status s) {
 
 int ssm_version(void) { return kVersion; }
 
-size_t ssm_selective_scan_workspace_size(int64_t batch, int64_t L, int64_t D, int64_t N, ssm_dtype dt) {
-  if (batch <= 0 || L <= 0 || D <= 0 || N < 1 || N > SSM_MAX_N || (dt != SSM_F32 && dt != SSM_BF16)) return 0;
-  return ssm::chunked_workspace_bytes(batch, L, N, 0);
-}
-
 ssm_status ssm_selective_scan_fwd_variant(const void* u, const void* delta, const float* A, const void* Bm,
                                           const void* Cm, const float* Dskip, const void* z,
                                           const float* delta_bias, int delta_softplus, void* y,
                                           float* final_state, int64_t batch, int64_t L, int64_t D,
-                                          int64_t N, ssm_dtype dt, void* workspace, size_t workspace_bytes,
-                                          void* stream, int variant, int tokens_per_lane) {
+                                          int64_t N, ssm_dtype dt, void* stream, int variant,
+                                          int tokens_per_lane) {
   ScanSizes sz;
   ssm_status st = check_scan(u, delta, A, Bm, Cm, Dskip, z, delta_bias, delta_softplus, y, final_state,
                              batch, L, D, N, dt, &sz);
@@ -128,24 +123,11 @@ ssm_status ssm_selective_scan_fwd_variant(const void* u, const void* delta, cons
   if (batch == 0 || D == 0) return SSM_OK;  // nothing to compute or write
   ssm::ScanArgs a;
   a.u = u; a.delta = delta; a.A = A; a.Bm = Bm; a.Cm = Cm; a.Dskip = Dskip; a.z = z;
-  a.bias = delta_bias; a.y = y; a.final_state = final_state; a.workspace = workspace;
+  a.bias = delta_bias; a.y = y; a.final_state = final_state;
   a.batch = batch; a.L = L; a.D = D; a.N = static_cast<int>(N); a.softplus = delta_softplus;
   const ssm::Dt d = dt == SSM_BF16 ? ssm::Dt::BF16 : ssm::Dt::F32;
   const bool chunked = L > 0 && variant != SSM_SCAN_SEQUENTIAL && ssm::chunked_supported(a, d, tokens_per_lane);
   if (variant == SSM_SCAN_CHUNKED && L > 0 && !chunked) return SSM_ERR_UNSUPPORTED;
-  if (chunked) {
-    // the chunked kernel packs B and C into the caller's workspace
-    const size_t need = ssm::chunked_workspace_bytes(batch, L, N, tokens_per_lane);
-    if (workspace == nullptr || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 15u))
-      return SSM_ERR_INVALID_ARG;
-    const Span ws = span(workspace, need);
-    const Span all[] = {span(u, sz.act_bytes),     span(delta, sz.act_bytes),        span(z, sz.act_bytes),
-                        span(A, sz.a_bytes),       span(Bm, sz.bc_bytes),            span(Cm, sz.bc_bytes),
-                        span(Dskip, sz.vec_bytes), span(delta_bias, sz.vec_bytes),   span(y, sz.act_bytes),
-                        span(final_state, sz.state_bytes)};
-    for (const Span& o : all)
-      if (overlaps(ws, o)) return SSM_ERR_INVALID_ARG;
-  }
   st = probe_device();
   if (st != SSM_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -157,11 +139,9 @@ ssm_status ssm_selective_scan_fwd_variant(const void* u, const void* delta, cons
 ssm_status ssm_selective_scan_fwd(const void* u, const void* delta, const float* A, const void* Bm,
                                   const void* Cm, const float* Dskip, const void* z, const float* delta_bias,
                                   int delta_softplus, void* y, float* final_state, int64_t batch, int64_t L,
-                                  int64_t D, int64_t N, ssm_dtype dt, void* workspace, size_t workspace_bytes,
-                                  void* stream) {
+                                  int64_t D, int64_t N, ssm_dtype dt, void* stream) {
   return ssm_selective_scan_fwd_variant(u, delta, A, Bm, Cm, Dskip, z, delta_bias, delta_softplus, y,
-                                        final_state, batch, L, D, N, dt, workspace, workspace_bytes, stream,
-                                        SSM_SCAN_AUTO, 0);
+                                        final_state, batch, L, D, N, dt, stream, SSM_SCAN_AUTO, 0);
 }
 
 ssm_status ssm_state_update(const float* state_in, float* state_out, const void* u_t, const void* delta_t,

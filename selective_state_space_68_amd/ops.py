@@ -3,7 +3,7 @@
 Torch is used for device memory and streams only; the arithmetic happens in
 libssm.so.  Activations (u, delta, z, B, C and the outputs y) are float32 or
 bfloat16 CUDA/HIP tensors of one dtype; A, D, delta_bias and states are float32.
-Layouts: u, delta, z [batch, D, L]; B, C [batch, L, N]; A [D, N]; D, bias [D].
+Layouts: u, delta, z [batch, D, L]; B, C [batch, N, L]; A [D, N]; D, bias [D].
 """
 from __future__ import annotations
 
@@ -44,32 +44,21 @@ def _stream(stream) -> int:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def workspace_bytes(batch: int, L: int, D: int, N: int, dtype=torch.float32) -> int:
-    """Scratch bytes selective_scan_fwd needs (the packed B/C tiles of the chunked kernel)."""
-    lib = _lib.load_library()
-    dt = _lib.SSM_BF16 if dtype == torch.bfloat16 else _lib.SSM_F32
-    return int(lib.ssm_selective_scan_workspace_size(batch, L, D, N, dt))
-
-
 def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True, *,
-                       y=None, final_state=None, return_final_state=True, workspace=None, variant=0,
+                       y=None, final_state=None, return_final_state=True, variant=0,
                        tokens_per_lane=0, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """Selective scan forward.  Returns (y [batch, D, L], final_state [batch, D, N] or None).
-
-    `workspace` (a device tensor of at least workspace_bytes(...) bytes) is allocated
-    here when not given.
-    """
+    """Selective scan forward.  Returns (y [batch, D, L], final_state [batch, D, N] or None)."""
     lib = _lib.load_library()
     if u.dim() != 3 or B.dim() != 3 or A.dim() != 2:
-        raise ValueError("expected u [batch, D, L], B/C [batch, L, N], A [D, N]")
+        raise ValueError("expected u [batch, D, L], B/C [batch, N, L], A [D, N]")
     batch, Dc, L = u.shape
     N = A.shape[1]
     act = u.dtype
     dev = u.device
     if tuple(delta.shape) != (batch, Dc, L) or tuple(A.shape) != (Dc, N):
         raise ValueError("delta / A shape mismatch")
-    if tuple(B.shape) != (batch, L, N) or tuple(C.shape) != (batch, L, N):
-        raise ValueError("B / C must be [batch, L, N]")
+    if tuple(B.shape) != (batch, N, L) or tuple(C.shape) != (batch, N, L):
+        raise ValueError("B / C must be [batch, N, L]")
     if z is not None and tuple(z.shape) != (batch, Dc, L):
         raise ValueError("z must be [batch, D, L]")
     for name, v in (("D", D), ("delta_bias", delta_bias)):
@@ -79,18 +68,13 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta
         y = torch.empty((batch, Dc, L), dtype=act, device=dev)
     if final_state is None and return_final_state:
         final_state = torch.empty((batch, Dc, N), dtype=torch.float32, device=dev)
-    need = int(lib.ssm_selective_scan_workspace_size(batch, L, Dc, N, _dt(u)))
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.ssm_selective_scan_fwd_variant(
         _ptr(u, "u", act, dev), _ptr(delta, "delta", act, dev), _ptr(A, "A", torch.float32, dev),
         _ptr(B, "B", act, dev), _ptr(C, "C", act, dev), _ptr(D, "D", torch.float32, dev),
         _ptr(z, "z", act, dev), _ptr(delta_bias, "delta_bias", torch.float32, dev),
         1 if delta_softplus else 0, _ptr(y, "y", act, dev),
         _ptr(final_state, "final_state", torch.float32, dev),
-        batch, L, Dc, N, _dt(u), _ptr(workspace, "workspace", None, dev), ws_bytes, _stream(stream),
-        int(variant), int(tokens_per_lane))
+        batch, L, Dc, N, _dt(u), _stream(stream), int(variant), int(tokens_per_lane))
     _lib.check(st)
     return y, final_state
 

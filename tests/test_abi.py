@@ -37,25 +37,20 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.ssm_version() == 10000
+    assert lib.ssm_version() == 20000
     for s in range(4):
         assert lib.ssm_status_string(s).decode().startswith(("SSM_OK", "SSM_ERR"))
     assert b"unknown" in lib.ssm_status_string(99)
-    # packed B/C tiles: batch * ceil(L / 1024) * 1024 tokens * N states * 2 matrices * 4 bytes
-    assert lib.ssm_selective_scan_workspace_size(2, 2048, 1536, 16, 0) == 2 * 2048 * 16 * 8
-    assert lib.ssm_selective_scan_workspace_size(1, 1025, 3, 5, 1) == 2048 * 5 * 8
-    assert lib.ssm_selective_scan_workspace_size(0, 2048, 3, 5, 1) == 0
 
 
 def _scan(lib, **kw):
     a = dict(u=F, delta=F + 1 * 64 * MB, A=F + 2 * 64 * MB, B=F + 3 * 64 * MB, C=F + 4 * 64 * MB,
              Dskip=None, z=None, bias=None, softplus=1, y=F + 5 * 64 * MB, final=F + 6 * 64 * MB,
-             batch=1, L=64, D=16, N=4, dt=0, variant=0, kpl=0, ws=F + 7 * 64 * MB, ws_bytes=1 * MB)
+             batch=1, L=64, D=16, N=4, dt=0, variant=0, kpl=0)
     a.update(kw)
     return lib.ssm_selective_scan_fwd_variant(a["u"], a["delta"], a["A"], a["B"], a["C"], a["Dskip"], a["z"],
                                               a["bias"], a["softplus"], a["y"], a["final"], a["batch"], a["L"],
-                                              a["D"], a["N"], a["dt"], a["ws"], a["ws_bytes"], None,
-                                              a["variant"], a["kpl"])
+                                              a["D"], a["N"], a["dt"], None, a["variant"], a["kpl"])
 
 
 def _step(lib, **kw):
@@ -87,10 +82,8 @@ def _step(lib, **kw):
     (dict(final=F + 2 * 64 * MB), _lib.SSM_ERR_INVALID_ARG),         # final state aliases A
     (dict(final=F + 5 * 64 * MB + 64), _lib.SSM_ERR_INVALID_ARG),    # final state overlaps y
     (dict(batch=1 << 40, L=1 << 40), _lib.SSM_ERR_INVALID_ARG),      # size overflow
-    (dict(ws=None), _lib.SSM_ERR_INVALID_ARG),                       # chunked path needs a workspace
-    (dict(ws_bytes=1024), _lib.SSM_ERR_INVALID_ARG),                 # workspace too small
-    (dict(ws=F + 7 * 64 * MB + 8), _lib.SSM_ERR_INVALID_ARG),        # workspace misaligned
-    (dict(ws=F + 4 * 64 * MB), _lib.SSM_ERR_INVALID_ARG),            # workspace overlaps C
+    (dict(B=F + 3 * 64 * MB + 2), _lib.SSM_ERR_INVALID_ARG),         # misaligned B
+    (dict(final=F + 3 * 64 * MB), _lib.SSM_ERR_INVALID_ARG),         # final state aliases B
 ])
 def test_scan_argument_errors(lib, kw, status):
     assert _scan(lib, **kw) == status
@@ -99,7 +92,7 @@ def test_scan_argument_errors(lib, kw, status):
 def test_scan_empty_inputs_are_noops(lib):
     assert _scan(lib, batch=0) == _lib.SSM_OK
     assert _scan(lib, D=0) == _lib.SSM_OK
-    assert _scan(lib, batch=0, ws=None, ws_bytes=0) == _lib.SSM_OK
+    assert _scan(lib, batch=0, u=None, delta=None, y=None, B=None, C=None) == _lib.SSM_OK
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -134,7 +127,7 @@ def _no_gpu():
 def test_valid_call_without_device_reports_hip_error(lib):
     # Valid arguments reach the device probe, which fails cleanly (no launch happens).
     assert _scan(lib) == _lib.SSM_ERR_HIP
-    assert _scan(lib, variant=1, ws=None, ws_bytes=0) == _lib.SSM_ERR_HIP   # sequential: no workspace
+    assert _scan(lib, variant=1) == _lib.SSM_ERR_HIP                      # sequential kernel
     assert _step(lib, sout=F) == _lib.SSM_ERR_HIP          # exact in-place is valid
     with pytest.raises(_lib.SsmError) as ei:
         _lib.check(_lib.SSM_ERR_HIP)

@@ -170,8 +170,8 @@ def test_no_final_state_and_zero_length():
     # L = 0: the final state is the zero initial state
     e = torch.empty((2, 3, 0), device="cuda")
     fs0 = torch.full((2, 3, 4), 7.0, device="cuda")
-    selective_scan_fwd(e, e.clone(), t["A"], torch.empty((2, 0, 4), device="cuda"),
-                       torch.empty((2, 0, 4), device="cuda"), final_state=fs0)
+    selective_scan_fwd(e, e.clone(), t["A"], torch.empty((2, 4, 0), device="cuda"),
+                       torch.empty((2, 4, 0), device="cuda"), final_state=fs0)
     torch.cuda.synchronize()
     assert torch.count_nonzero(fs0).item() == 0
 
