@@ -105,8 +105,6 @@ def cpu_baseline_scan(cfg, inp, budget_s=20.0, workers=0):
                           vec(inp.delta_bias, 0, d_probe), inp.delta_softplus)
     per_row_cpu = (time.perf_counter() - t0) * cfg.D / d_probe
     b_take = max(1, min(cfg.batch, int(budget_s / max(per_row_cpu, 1e-3))))
-    # a sample far below the budget (the whole workload) is repeated, for a stable time
-    reps = max(1, min(20, int(budget_s / max(per_row_cpu * b_take, 1e-3))))
     dblk = max(1, -(-cfg.D // max(1, (workers + b_take - 1) // b_take)))
     shards = []
     for b in range(b_take):
@@ -117,6 +115,10 @@ def cpu_baseline_scan(cfg, inp, budget_s=20.0, workers=0):
                            vec(inp.delta_bias, d0, d1), inp.delta_softplus))
     with cf.ProcessPoolExecutor(max_workers=workers, mp_context=mp.get_context("spawn")) as ex:
         list(ex.map(_oracle_warm, range(workers)))   # start the workers and import the oracle
+        t0 = time.perf_counter()
+        one = sum(ex.map(_oracle_shard, shards))       # one pass: sizes the repetition count
+        # a pass far below the CPU budget (the whole workload) is repeated, for a stable time
+        reps = max(1, min(50, int(budget_s / max(one, 1e-3))))
         t0 = time.perf_counter()
         secs = list(ex.map(_oracle_shard, shards * reps))
         wall = time.perf_counter() - t0
