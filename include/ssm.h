@@ -88,20 +88,41 @@ ssm_status ssm_selective_scan_fwd(
     int64_t batch, int64_t L, int64_t D, int64_t N, ssm_dtype dt, void *stream);
 
 /*
+ * The same scan started from a given state instead of zero: h[b, -1, d, :] =
+ * initial_state[b, d, :] (the lecture notes' §2.1 solves the system from a zero
+ * initial state; this takes any).  Scanning a sequence in pieces, each piece
+ * from the previous piece's final state, gives the result of one scan over the
+ * whole sequence: chunked prefill, the carry step of a sequence split across
+ * devices, and the state-level prefix reuse of the interview-prep page's
+ * "Common Pitfalls" (the state after a shared prefix is resumed).
+ *
+ *   initial_state : [batch][D][N] float32, or NULL (= zero, as ssm_selective_scan_fwd)
+ *   final_state   : may be the same pointer as initial_state (updated in place)
+ *                   but must not otherwise overlap it
+ * Other arguments and errors as for ssm_selective_scan_fwd; with L == 0 the
+ * final state is the initial state.
+ */
+ssm_status ssm_selective_scan_fwd_from_state(
+    const void *u, const void *delta, const float *A, const void *Bm, const void *Cm,
+    const float *Dskip, const void *z, const float *delta_bias, int delta_softplus,
+    const float *initial_state, void *y, float *final_state,
+    int64_t batch, int64_t L, int64_t D, int64_t N, ssm_dtype dt, void *stream);
+
+/*
  * Same operation with an explicit kernel choice, for testing that every
  * implementation agrees: SSM_SCAN_AUTO picks the fastest valid one;
  * SSM_SCAN_SEQUENTIAL runs one thread per (b, d) channel stepping through time
  * (the plain recurrence); SSM_SCAN_CHUNKED runs the chunked wave-scan kernel
  * (returns SSM_ERR_UNSUPPORTED when the shape does not fit it).
  * `tokens_per_lane` (0 = default) selects the chunked kernel's tokens per lane
- * (8 or 16).  Other arguments as in ssm_selective_scan_fwd.
+ * (8 or 16).  Other arguments as in ssm_selective_scan_fwd_from_state.
  */
 typedef enum { SSM_SCAN_AUTO = 0, SSM_SCAN_SEQUENTIAL = 1, SSM_SCAN_CHUNKED = 2 } ssm_scan_variant;
 
 ssm_status ssm_selective_scan_fwd_variant(
     const void *u, const void *delta, const float *A, const void *Bm, const void *Cm,
     const float *Dskip, const void *z, const float *delta_bias, int delta_softplus,
-    void *y, float *final_state,
+    const float *initial_state, void *y, float *final_state,
     int64_t batch, int64_t L, int64_t D, int64_t N, ssm_dtype dt, void *stream,
     int variant, int tokens_per_lane);
 

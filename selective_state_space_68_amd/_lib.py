@@ -32,7 +32,9 @@ _int = ctypes.c_int
 SIGNATURES = {
     "ssm_selective_scan_fwd": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _vp, _vp,
                                       _i64, _i64, _i64, _i64, _int, _vp]),
-    "ssm_selective_scan_fwd_variant": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _vp, _vp,
+    "ssm_selective_scan_fwd_from_state": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _vp, _vp, _vp,
+                                                 _i64, _i64, _i64, _i64, _int, _vp]),
+    "ssm_selective_scan_fwd_variant": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _vp, _vp, _vp,
                                               _i64, _i64, _i64, _i64, _int, _vp, _int, _int]),
     "ssm_state_update": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _vp,
                                 _i64, _i64, _i64, _int, _vp]),

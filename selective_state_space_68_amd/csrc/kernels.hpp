@@ -17,6 +17,7 @@ struct ScanArgs {
   const float* Dskip;    // [D] or null
   const void* z;         // [batch][D][L] act or null
   const float* bias;     // [D] or null
+  const float* h0;       // [batch][D][N] initial state or null (zero); may equal final_state
   void* y;               // [batch][D][L] act
   float* final_state;    // [batch][D][N] or null
   int64_t batch, L, D;
@@ -49,8 +50,8 @@ hipError_t launch_scan_sequential(const ScanArgs& a, Dt dt, hipStream_t s);
 bool chunked_supported(const ScanArgs& a, Dt dt, int tokens_per_lane);
 hipError_t launch_scan_chunked(const ScanArgs& a, Dt dt, int tokens_per_lane, hipStream_t s);
 
-// Writes zeros to final_state (the L == 0 scan).
-hipError_t launch_zero_state(float* p, int64_t n, hipStream_t s);
+// final_state = initial state, or zeros when src is null (the L == 0 scan).
+hipError_t launch_copy_state(float* dst, const float* src, int64_t n, hipStream_t s);
 
 hipError_t launch_state_update(const StepArgs& a, Dt dt, hipStream_t s);
 

@@ -205,7 +205,8 @@ __global__ __launch_bounds__(kThreads) void scan_chunked_kernel(ScanArgs p, int 
   // A[d, n] * log2(e) in lane n (read once, so the state loop never issues a
   // vector load of A).
   const float a2_v = lane < N ? p.A[d * N + lane] * kLog2e : 0.0f;
-  float carry_v = 0.0f;                              // carry of state n lives in lane n
+  // carry of state n lives in lane n; it starts as the initial state (zero if none)
+  float carry_v = (lane < N && p.h0) ? p.h0[(b * p.D + d) * N + lane] : 0.0f;
 
   const int nblk = NBLK > 0 ? NBLK : (N + kNB - 1) / kNB;
   const int64_t nchunks = (L + CH - 1) / CH;
@@ -474,7 +475,7 @@ __global__ __launch_bounds__(kThreads) void scan_chunked_kernel(ScanArgs p, int 
 #pragma unroll
     for (int n = 0; n < NS; ++n) {
       a2s[n] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, a2_v), n));
-      cs[n] = 0.0f;
+      cs[n] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, carry_v), n));
     }
   }
 

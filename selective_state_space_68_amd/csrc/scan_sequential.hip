@@ -24,7 +24,7 @@ __global__ __launch_bounds__(64) void scan_sequential_kernel(ScanArgs p) {
 #pragma unroll
   for (int n = 0; n < NB; ++n) {
     a2[n] = (n < N) ? p.A[d * N + n] * kLog2e : 0.0f;
-    h[n] = 0.0f;
+    h[n] = (n < N && p.h0) ? p.h0[ch * N + n] : 0.0f;
   }
   const float bias = p.bias ? p.bias[d] : 0.0f;
   const float dsk = p.Dskip ? p.Dskip[d] : 0.0f;
@@ -75,9 +75,9 @@ hipError_t launch_nb(const ScanArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-__global__ void zero_kernel(float* p, int64_t n) {
+__global__ void copy_state_kernel(float* dst, const float* src, int64_t n) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0.0f;
+  if (i < n) dst[i] = src ? src[i] : 0.0f;
 }
 
 }  // namespace
@@ -88,9 +88,10 @@ hipError_t launch_scan_sequential(const ScanArgs& a, Dt dt, hipStream_t s) {
   return gate ? launch_nb<ActBF16, true>(a, s) : launch_nb<ActBF16, false>(a, s);
 }
 
-hipError_t launch_zero_state(float* p, int64_t n, hipStream_t s) {
-  if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(zero_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, p, n);
+hipError_t launch_copy_state(float* dst, const float* src, int64_t n, hipStream_t s) {
+  if (n <= 0 || dst == src) return hipSuccess;
+  hipLaunchKernelGGL(copy_state_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, dst, src,
+                     n);
   return hipGetLastError();
 }
 

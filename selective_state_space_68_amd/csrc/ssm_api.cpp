@@ -11,7 +11,7 @@
 
 namespace {
 
-constexpr int kVersion = 20000;  // 2.0.0: B and C stored [batch][N][L], no workspace
+constexpr int kVersion = 20100;  // 2.1.0: B and C stored [batch][N][L], no workspace; initial state
 
 struct Span {
   uintptr_t lo = 0, hi = 0;  // [lo, hi); empty when lo == hi
@@ -57,8 +57,8 @@ struct ScanSizes {
 
 ssm_status check_scan(const void* u, const void* delta, const float* A, const void* Bm, const void* Cm,
                       const float* Dskip, const void* z, const float* delta_bias, int delta_softplus,
-                      const void* y, const float* final_state, int64_t batch, int64_t L, int64_t D,
-                      int64_t N, ssm_dtype dt, ScanSizes* sz) {
+                      const float* initial_state, const void* y, const float* final_state, int64_t batch,
+                      int64_t L, int64_t D, int64_t N, ssm_dtype dt, ScanSizes* sz) {
   if (dt != SSM_F32 && dt != SSM_BF16) return SSM_ERR_UNSUPPORTED;
   if (batch < 0 || L < 0 || D < 0 || N < 0) return SSM_ERR_INVALID_ARG;
   if (N < 1 || N > SSM_MAX_N) return SSM_ERR_UNSUPPORTED;
@@ -77,7 +77,7 @@ ssm_status check_scan(const void* u, const void* delta, const float* A, const vo
   sz->vec_bytes = static_cast<uint64_t>(D) * 4;
   if (!aligned(u, e) || !aligned(delta, e) || !aligned(z, e) || !aligned(y, e) || !aligned(Bm, e) ||
       !aligned(Cm, e) || !aligned(A, 4) || !aligned(Dskip, 4) || !aligned(delta_bias, 4) ||
-      !aligned(final_state, 4))
+      !aligned(final_state, 4) || !aligned(initial_state, 4))
     return SSM_ERR_INVALID_ARG;
   const Span in[] = {span(u, sz->act_bytes),        span(delta, sz->act_bytes),
                      span(z, sz->act_bytes),        span(A, sz->a_bytes),
@@ -85,9 +85,12 @@ ssm_status check_scan(const void* u, const void* delta, const float* A, const vo
                      span(Dskip, sz->vec_bytes),    span(delta_bias, sz->vec_bytes)};
   const Span ys = span(y, sz->act_bytes);
   const Span fs = span(final_state, sz->state_bytes);
+  const Span hs = span(initial_state, sz->state_bytes);
   for (const Span& s : in)
-    if (overlaps(ys, s) || overlaps(fs, s)) return SSM_ERR_INVALID_ARG;
-  if (overlaps(ys, fs)) return SSM_ERR_INVALID_ARG;
+    if (overlaps(ys, s) || overlaps(fs, s) || overlaps(hs, s)) return SSM_ERR_INVALID_ARG;
+  if (overlaps(ys, fs) || overlaps(ys, hs)) return SSM_ERR_INVALID_ARG;
+  // the final state may replace the initial state in place, but not partly overlap it
+  if (overlaps(hs, fs) && initial_state != final_state) return SSM_ERR_INVALID_ARG;
   return SSM_OK;
 }
 
@@ -109,13 +112,13 @@ int ssm_version(void) { return kVersion; }
 
 ssm_status ssm_selective_scan_fwd_variant(const void* u, const void* delta, const float* A, const void* Bm,
                                           const void* Cm, const float* Dskip, const void* z,
-                                          const float* delta_bias, int delta_softplus, void* y,
-                                          float* final_state, int64_t batch, int64_t L, int64_t D,
-                                          int64_t N, ssm_dtype dt, void* stream, int variant,
-                                          int tokens_per_lane) {
+                                          const float* delta_bias, int delta_softplus,
+                                          const float* initial_state, void* y, float* final_state,
+                                          int64_t batch, int64_t L, int64_t D, int64_t N, ssm_dtype dt,
+                                          void* stream, int variant, int tokens_per_lane) {
   ScanSizes sz;
-  ssm_status st = check_scan(u, delta, A, Bm, Cm, Dskip, z, delta_bias, delta_softplus, y, final_state,
-                             batch, L, D, N, dt, &sz);
+  ssm_status st = check_scan(u, delta, A, Bm, Cm, Dskip, z, delta_bias, delta_softplus, initial_state, y,
+                             final_state, batch, L, D, N, dt, &sz);
   if (st != SSM_OK) return st;
   if (variant != SSM_SCAN_AUTO && variant != SSM_SCAN_SEQUENTIAL && variant != SSM_SCAN_CHUNKED)
     return SSM_ERR_UNSUPPORTED;
@@ -123,7 +126,7 @@ ssm_status ssm_selective_scan_fwd_variant(const void* u, const void* delta, cons
   if (batch == 0 || D == 0) return SSM_OK;  // nothing to compute or write
   ssm::ScanArgs a;
   a.u = u; a.delta = delta; a.A = A; a.Bm = Bm; a.Cm = Cm; a.Dskip = Dskip; a.z = z;
-  a.bias = delta_bias; a.y = y; a.final_state = final_state;
+  a.bias = delta_bias; a.h0 = initial_state; a.y = y; a.final_state = final_state;
   a.batch = batch; a.L = L; a.D = D; a.N = static_cast<int>(N); a.softplus = delta_softplus;
   const ssm::Dt d = dt == SSM_BF16 ? ssm::Dt::BF16 : ssm::Dt::F32;
   const bool chunked = L > 0 && variant != SSM_SCAN_SEQUENTIAL && ssm::chunked_supported(a, d, tokens_per_lane);
@@ -131,7 +134,8 @@ ssm_status ssm_selective_scan_fwd_variant(const void* u, const void* delta, cons
   st = probe_device();
   if (st != SSM_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (L == 0) return final_state ? from_hip(ssm::launch_zero_state(final_state, batch * D * N, s)) : SSM_OK;
+  if (L == 0)  // the final state is the initial state
+    return final_state ? from_hip(ssm::launch_copy_state(final_state, initial_state, batch * D * N, s)) : SSM_OK;
   if (chunked) return from_hip(ssm::launch_scan_chunked(a, d, tokens_per_lane, s));
   return from_hip(ssm::launch_scan_sequential(a, d, s));
 }
@@ -140,8 +144,19 @@ ssm_status ssm_selective_scan_fwd(const void* u, const void* delta, const float*
                                   const void* Cm, const float* Dskip, const void* z, const float* delta_bias,
                                   int delta_softplus, void* y, float* final_state, int64_t batch, int64_t L,
                                   int64_t D, int64_t N, ssm_dtype dt, void* stream) {
-  return ssm_selective_scan_fwd_variant(u, delta, A, Bm, Cm, Dskip, z, delta_bias, delta_softplus, y,
+  return ssm_selective_scan_fwd_variant(u, delta, A, Bm, Cm, Dskip, z, delta_bias, delta_softplus, nullptr, y,
                                         final_state, batch, L, D, N, dt, stream, SSM_SCAN_AUTO, 0);
+}
+
+ssm_status ssm_selective_scan_fwd_from_state(const void* u, const void* delta, const float* A, const void* Bm,
+                                             const void* Cm, const float* Dskip, const void* z,
+                                             const float* delta_bias, int delta_softplus,
+                                             const float* initial_state, void* y, float* final_state,
+                                             int64_t batch, int64_t L, int64_t D, int64_t N, ssm_dtype dt,
+                                             void* stream) {
+  return ssm_selective_scan_fwd_variant(u, delta, A, Bm, Cm, Dskip, z, delta_bias, delta_softplus,
+                                        initial_state, y, final_state, batch, L, D, N, dt, stream,
+                                        SSM_SCAN_AUTO, 0);
 }
 
 ssm_status ssm_state_update(const float* state_in, float* state_out, const void* u_t, const void* delta_t,

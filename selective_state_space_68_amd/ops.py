@@ -45,9 +45,13 @@ def _stream(stream) -> int:
 
 
 def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True, *,
-                       y=None, final_state=None, return_final_state=True, variant=0,
+                       initial_state=None, y=None, final_state=None, return_final_state=True, variant=0,
                        tokens_per_lane=0, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """Selective scan forward.  Returns (y [batch, D, L], final_state [batch, D, N] or None)."""
+    """Selective scan forward.  Returns (y [batch, D, L], final_state [batch, D, N] or None).
+
+    `initial_state` [batch, D, N] float32 starts the scan from a given state (zero
+    when None); `final_state` may be the same tensor (updated in place).
+    """
     lib = _lib.load_library()
     if u.dim() != 3 or B.dim() != 3 or A.dim() != 2:
         raise ValueError("expected u [batch, D, L], B/C [batch, N, L], A [D, N]")
@@ -64,6 +68,8 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta
     for name, v in (("D", D), ("delta_bias", delta_bias)):
         if v is not None and tuple(v.shape) != (Dc,):
             raise ValueError(f"{name} must be [D]")
+    if initial_state is not None and tuple(initial_state.shape) != (batch, Dc, N):
+        raise ValueError("initial_state must be [batch, D, N]")
     if y is None:
         y = torch.empty((batch, Dc, L), dtype=act, device=dev)
     if final_state is None and return_final_state:
@@ -72,7 +78,8 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta
         _ptr(u, "u", act, dev), _ptr(delta, "delta", act, dev), _ptr(A, "A", torch.float32, dev),
         _ptr(B, "B", act, dev), _ptr(C, "C", act, dev), _ptr(D, "D", torch.float32, dev),
         _ptr(z, "z", act, dev), _ptr(delta_bias, "delta_bias", torch.float32, dev),
-        1 if delta_softplus else 0, _ptr(y, "y", act, dev),
+        1 if delta_softplus else 0, _ptr(initial_state, "initial_state", torch.float32, dev),
+        _ptr(y, "y", act, dev),
         _ptr(final_state, "final_state", torch.float32, dev),
         batch, L, Dc, N, _dt(u), _stream(stream), int(variant), int(tokens_per_lane))
     _lib.check(st)

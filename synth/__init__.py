@@ -11,6 +11,7 @@ from .gen import (  # noqa: F401
     f32_from_bf16_bits,
     make_scan_inputs,
     make_config_inputs,
+    make_scan_initial_state,
     make_decode_state,
     make_decode_step,
     make_decode_params,

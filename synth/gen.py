@@ -165,6 +165,13 @@ def make_scan_inputs(batch: int, L: int, D: int, N: int, dtype: str = "f32",
     return inp
 
 
+def make_scan_initial_state(batch: int, D: int, N: int, seed: int = 0) -> np.ndarray:
+    """Initial state [batch][D][N] ~ N(0, 1), float32, from the seed's "h0" stream."""
+    ss = np.random.SeedSequence(seed)
+    kid = ss.spawn(len(_SCAN_STREAMS))[_SCAN_STREAMS.index("h0")]
+    return np.random.Generator(np.random.PCG64(kid)).standard_normal((batch, D, N), dtype=np.float32)
+
+
 def make_config_inputs(cfg, seed: Optional[int] = None, **kw) -> ScanInputs:
     """Inputs of a named scan workload (see synth.configs)."""
     return make_scan_inputs(cfg.batch, cfg.L, cfg.D, cfg.N, cfg.dtype, gate=cfg.gate,

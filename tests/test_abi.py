@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.ssm_version() == 20000
+    assert lib.ssm_version() == 20100
     for s in range(4):
         assert lib.ssm_status_string(s).decode().startswith(("SSM_OK", "SSM_ERR"))
     assert b"unknown" in lib.ssm_status_string(99)
@@ -45,11 +45,12 @@ def test_version_and_status_strings(lib):
 
 def _scan(lib, **kw):
     a = dict(u=F, delta=F + 1 * 64 * MB, A=F + 2 * 64 * MB, B=F + 3 * 64 * MB, C=F + 4 * 64 * MB,
-             Dskip=None, z=None, bias=None, softplus=1, y=F + 5 * 64 * MB, final=F + 6 * 64 * MB,
+             Dskip=None, z=None, bias=None, softplus=1, h0=None, y=F + 5 * 64 * MB, final=F + 6 * 64 * MB,
              batch=1, L=64, D=16, N=4, dt=0, variant=0, kpl=0)
     a.update(kw)
     return lib.ssm_selective_scan_fwd_variant(a["u"], a["delta"], a["A"], a["B"], a["C"], a["Dskip"], a["z"],
-                                              a["bias"], a["softplus"], a["y"], a["final"], a["batch"], a["L"],
+                                              a["bias"], a["softplus"], a["h0"], a["y"], a["final"], a["batch"],
+                                              a["L"],
                                               a["D"], a["N"], a["dt"], None, a["variant"], a["kpl"])
 
 
@@ -84,6 +85,10 @@ def _step(lib, **kw):
     (dict(batch=1 << 40, L=1 << 40), _lib.SSM_ERR_INVALID_ARG),      # size overflow
     (dict(B=F + 3 * 64 * MB + 2), _lib.SSM_ERR_INVALID_ARG),         # misaligned B
     (dict(final=F + 3 * 64 * MB), _lib.SSM_ERR_INVALID_ARG),         # final state aliases B
+    (dict(h0=F + 7 * 64 * MB + 2), _lib.SSM_ERR_INVALID_ARG),        # misaligned initial state
+    (dict(h0=F + 5 * 64 * MB), _lib.SSM_ERR_INVALID_ARG),            # initial state aliases y
+    (dict(h0=F + 1 * 64 * MB + 64), _lib.SSM_ERR_INVALID_ARG),       # initial state overlaps delta
+    (dict(h0=F + 6 * 64 * MB + 16), _lib.SSM_ERR_INVALID_ARG),       # partly overlaps the final state
 ])
 def test_scan_argument_errors(lib, kw, status):
     assert _scan(lib, **kw) == status
@@ -128,6 +133,8 @@ def test_valid_call_without_device_reports_hip_error(lib):
     # Valid arguments reach the device probe, which fails cleanly (no launch happens).
     assert _scan(lib) == _lib.SSM_ERR_HIP
     assert _scan(lib, variant=1) == _lib.SSM_ERR_HIP                      # sequential kernel
+    assert _scan(lib, h0=F + 7 * 64 * MB) == _lib.SSM_ERR_HIP             # from a given state
+    assert _scan(lib, h0=F + 6 * 64 * MB) == _lib.SSM_ERR_HIP             # ... updated in place
     assert _step(lib, sout=F) == _lib.SSM_ERR_HIP          # exact in-place is valid
     with pytest.raises(_lib.SsmError) as ei:
         _lib.check(_lib.SSM_ERR_HIP)

@@ -1,0 +1,104 @@
+"""GPU parity of the scan started from a given state (ssm_selective_scan_fwd_from_state).
+
+The oracle runs the same float64 recurrence from the same initial state.  The
+piecewise test checks the property the entry point exists for: scanning a
+sequence in pieces, each from the previous piece's final state (passed in place),
+reproduces one scan over the whole sequence.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import TOL, dev, host, upload_scan
+from ssm_metrics import row_rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from selective_state_space_68_amd import load_library
+    load_library()
+
+
+def _oracle(inp, h0):
+    return oracle.selective_scan(inp.u, inp.delta, inp.A, inp.B, inp.C, inp.Dskip, inp.z, inp.delta_bias,
+                                 inp.delta_softplus, h0=h0)
+
+
+SHAPES = [
+    # batch, L, D, N, dtype, gate
+    (1, 64, 16, 4, "f32", False),
+    (2, 1100, 13, 16, "bf16", True),
+    (1, 700, 5, 16, "f32", True),
+    (2, 333, 3, 7, "f32", True),
+    (1, 2048, 12, 16, "bf16", True),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s[:4])) + f"-{s[4]}")
+def test_initial_state_all_variants(shape):
+    from selective_state_space_68_amd import selective_scan_fwd
+    batch, L, D, N, dtype, gate = shape
+    inp = synth.make_scan_inputs(batch, L, D, N, dtype, gate=gate, d_skip="normal", seed=100 + L,
+                                 a_kind="lognormal")
+    h0 = synth.make_scan_initial_state(batch, D, N, seed=100 + L)
+    ry, rf = _oracle(inp, h0.astype(np.float64))
+    t = upload_scan(inp)
+    th0 = dev(h0)
+    for variant, kpl in ((0, 0), (1, 0), (2, 8), (2, 16)):
+        y, fs = selective_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["bias"],
+                                   inp.delta_softplus, initial_state=th0, variant=variant, tokens_per_lane=kpl)
+        ey, ef = row_rel_err(host(y), ry), row_rel_err(host(fs), rf)
+        print(f"{shape} v{variant}/{kpl} y_err={ey:.3e} state_err={ef:.3e}", flush=True)
+        assert ey <= TOL[dtype] and ef <= TOL[dtype], (variant, kpl, ey, ef)
+    # the initial state is an input: it is left unchanged
+    assert np.array_equal(host(th0), h0.astype(np.float64))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_scan_in_pieces_matches_one_scan(dtype):
+    """Chunked prefill: pieces chained through an in-place state equal one scan."""
+    import torch
+    from selective_state_space_68_amd import selective_scan_fwd
+    batch, L, D, N = 2, 3000, 24, 16
+    inp = synth.make_scan_inputs(batch, L, D, N, dtype, seed=21, a_kind="lognormal")
+    t = upload_scan(inp)
+    y_full, f_full = selective_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["bias"])
+    state = torch.zeros((batch, D, N), dtype=torch.float32, device="cuda")
+    ys = []
+    for a, b in ((0, 1000), (1000, 1001), (1001, 2200), (2200, 3000)):
+        piece = {k: t[k][:, :, a:b].contiguous() for k in ("u", "delta", "z", "B", "C")}
+        y, _ = selective_scan_fwd(piece["u"], piece["delta"], t["A"], piece["B"], piece["C"], t["D"],
+                                  piece["z"], t["bias"], initial_state=state, final_state=state)
+        ys.append(host(y))
+    torch.cuda.synchronize()
+    ey = row_rel_err(np.concatenate(ys, axis=-1), host(y_full))
+    ef = row_rel_err(host(state), host(f_full))
+    print(f"{dtype} pieces y_err={ey:.3e} state_err={ef:.3e}", flush=True)
+    assert ey <= TOL[dtype] and ef <= TOL[dtype]
+    # and both against the oracle
+    ry, rf = _oracle(inp, None)
+    assert row_rel_err(np.concatenate(ys, axis=-1), ry) <= TOL[dtype]
+    assert row_rel_err(host(state), rf) <= TOL[dtype]
+
+
+def test_zero_length_returns_the_initial_state():
+    import torch
+    from selective_state_space_68_amd import selective_scan_fwd
+    h0 = synth.make_scan_initial_state(2, 3, 4, seed=9)
+    th0 = dev(h0)
+    A = dev(np.full((3, 4), -1.0, dtype=np.float32))
+    e = torch.empty((2, 3, 0), device="cuda")
+    ebc = torch.empty((2, 4, 0), device="cuda")
+    _, fs = selective_scan_fwd(e, e.clone(), A, ebc, ebc.clone(), initial_state=th0)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(fs), h0.astype(np.float64))
+    fs2 = th0.clone()
+    selective_scan_fwd(e, e.clone(), A, ebc, ebc.clone(), initial_state=fs2, final_state=fs2)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(fs2), h0.astype(np.float64))
