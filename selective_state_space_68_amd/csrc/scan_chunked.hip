@@ -48,7 +48,7 @@
 namespace ssm {
 namespace {
 
-constexpr int kNB = 4;               // states per step (per staged B/C tile)
+constexpr int kNBGeneric = 4;        // states per step (per staged B/C tile), any N
 constexpr int kW = 12;               // waves (channels) per workgroup
 constexpr int kThreads = 64 * kW;
 
@@ -168,12 +168,12 @@ __device__ __forceinline__ void barrier_lds() {
 }
 
 // ---- the scan ----------------------------------------------------------------
-// NBLK > 0: N == 4 * NBLK, fixed at compile time; the steps of a chunk are
+// kNB states per step.  NBLK > 0: N == kNB * NBLK, fixed at compile time; the steps of a chunk are
 // unrolled, the last chunk is peeled, and the per-state values sit in scalar
 // registers.  The steady state then has no branch around any load, so the
 // compiler's tracking of outstanding loads stays exact and it never waits for a
 // load before its value is needed.  NBLK = 0: any N, steps in a runtime loop.
-template <typename ACT, bool GATE, int KPL, bool VEC, int NBLK>
+template <typename ACT, bool GATE, int KPL, bool VEC, int NBLK, int kNB>
 __global__ __launch_bounds__(kThreads) void scan_chunked_kernel(ScanArgs p, int n_dblk) {
   // states processed two at a time where the registers allow it (8 tokens per lane)
   constexpr bool PAIR = KPL <= 8;
@@ -469,7 +469,7 @@ __global__ __launch_bounds__(kThreads) void scan_chunked_kernel(ScanArgs p, int 
   // Per-state wave-uniform values when the state count is fixed at compile time
   // (NBLK > 0): A*log2(e) and the carry of state n in scalar registers, indexed
   // by compile-time n once the steps are unrolled.
-  constexpr int NS = NBLK > 0 ? 4 * NBLK : 1;
+  constexpr int NS = NBLK > 0 ? kNB * NBLK : 1;
   float a2s[NS], cs[NS];
   if constexpr (NBLK > 0) {
 #pragma unroll
@@ -483,7 +483,7 @@ __global__ __launch_bounds__(kThreads) void scan_chunked_kernel(ScanArgs p, int 
   auto states = [&](const float4* cur, int nb) __attribute__((always_inline)) {
     const int n0 = nb * kNB;
     if constexpr (NBLK > 0) {
-      constexpr int nn = kNB;                          // N == 4 * NBLK: every step is full
+      constexpr int nn = kNB;                          // N == kNB * NBLK: every step is full
       const float4* t = cur;
       if constexpr (PAIR) {
 #pragma unroll
@@ -575,14 +575,20 @@ hipError_t launch_kpl(const ScanArgs& a, hipStream_t s) {
                    (a.z == nullptr || aligned16(a.z)) && aligned16(a.Bm) && aligned16(a.Cm);
   const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
   const bool n16 = a.N == 16;
+  // N == 16, bfloat16, 8 tokens per lane: 8 states per step (two steps per
+  // chunk, half the barriers; measured 2 % faster).  float32 measured no faster
+  // that way, and at 16 tokens per lane the larger tile's registers would spill.
+  constexpr int N16_STEPS = (ACT::kBytes == 2 && KPL <= 8) ? 2 : 4;
   if (vec && n16)
-    hipLaunchKernelGGL((scan_chunked_kernel<ACT, GATE, KPL, true, 4>), grid, block, 0, s, a, n_dblk);
+    hipLaunchKernelGGL((scan_chunked_kernel<ACT, GATE, KPL, true, N16_STEPS, 16 / N16_STEPS>), grid, block, 0, s,
+                       a, n_dblk);
   else if (vec)
-    hipLaunchKernelGGL((scan_chunked_kernel<ACT, GATE, KPL, true, 0>), grid, block, 0, s, a, n_dblk);
+    hipLaunchKernelGGL((scan_chunked_kernel<ACT, GATE, KPL, true, 0, kNBGeneric>), grid, block, 0, s, a, n_dblk);
   else if (n16)
-    hipLaunchKernelGGL((scan_chunked_kernel<ACT, GATE, KPL, false, 4>), grid, block, 0, s, a, n_dblk);
+    hipLaunchKernelGGL((scan_chunked_kernel<ACT, GATE, KPL, false, N16_STEPS, 16 / N16_STEPS>), grid, block, 0, s,
+                       a, n_dblk);
   else
-    hipLaunchKernelGGL((scan_chunked_kernel<ACT, GATE, KPL, false, 0>), grid, block, 0, s, a, n_dblk);
+    hipLaunchKernelGGL((scan_chunked_kernel<ACT, GATE, KPL, false, 0, kNBGeneric>), grid, block, 0, s, a, n_dblk);
   return hipGetLastError();
 }
 
@@ -592,12 +598,11 @@ hipError_t launch_gate(const ScanArgs& a, int kpl, hipStream_t s) {
   return launch_kpl<ACT, GATE, 16>(a, s);
 }
 
-// Default tokens per lane, from measurement on gfx950: with float32 activations
-// 8 tokens per lane (no register spills) beats 16; with bfloat16, 16 (half the
-// wave-scan overhead per element) wins.
-int resolve_kpl(int tokens_per_lane, Dt dt) {
-  if (tokens_per_lane != 0) return tokens_per_lane;
-  return dt == Dt::F32 ? 8 : 16;
+// Default tokens per lane, from measurement on gfx950: 8, where the registers
+// leave room to run two states at once, beats 16 (half the wave-scan overhead
+// per element, one state at a time) for both activation types.
+int resolve_kpl(int tokens_per_lane, Dt) {
+  return tokens_per_lane != 0 ? tokens_per_lane : 8;
 }
 
 }  // namespace
