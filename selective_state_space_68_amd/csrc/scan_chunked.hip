@@ -60,6 +60,27 @@ __device__ __forceinline__ void dma16(const void* gsrc, void* lds_base) {
   __builtin_amdgcn_global_load_lds(gsrc, (lds_void*)(lds_base), 16, 0, 0);
 }
 
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+// u, delta and z are read once and y is written once: non-temporal accesses
+// (measured 3.5 % faster on the float32 workload, neutral on bfloat16).
+__device__ __forceinline__ float4 ld_stream(const float4* p) {
+  const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint4 ld_stream(const uint4* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st_stream(float4* p, float4 v) {
+  const f32x4_t t = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(t, reinterpret_cast<f32x4_t*>(p));
+}
+__device__ __forceinline__ void st_stream(uint4* p, uint4 v) {
+  const u32x4_t t = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(t, reinterpret_cast<u32x4_t*>(p));
+}
+
 template <typename ACT, int KPL>
 struct TokenIO;
 
@@ -70,7 +91,7 @@ struct TokenIO<ActF32, KPL> {
   static __device__ __forceinline__ void load_raw(const void* base, int64_t off, raw_t (&r)[kVec]) {
     const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
 #pragma unroll
-    for (int q = 0; q < kVec; ++q) r[q] = p[q];
+    for (int q = 0; q < kVec; ++q) r[q] = ld_stream(p + q);
   }
   static __device__ __forceinline__ void unpack(const raw_t (&r)[kVec], float (&v)[KPL]) {
 #pragma unroll
@@ -82,7 +103,7 @@ struct TokenIO<ActF32, KPL> {
     float4* p = reinterpret_cast<float4*>(static_cast<float*>(base) + off);
 #pragma unroll
     for (int q = 0; q < kVec; ++q)
-      p[q] = make_float4(v[4 * q + 0], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+      st_stream(p + q, make_float4(v[4 * q + 0], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]));
   }
 };
 
@@ -93,7 +114,7 @@ struct TokenIO<ActBF16, KPL> {
   static __device__ __forceinline__ void load_raw(const void* base, int64_t off, raw_t (&r)[kVec]) {
     const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off);
 #pragma unroll
-    for (int q = 0; q < kVec; ++q) r[q] = p[q];
+    for (int q = 0; q < kVec; ++q) r[q] = ld_stream(p + q);
   }
   static __device__ __forceinline__ void unpack(const raw_t (&r)[kVec], float (&v)[KPL]) {
 #pragma unroll
@@ -113,7 +134,7 @@ struct TokenIO<ActBF16, KPL> {
       x.y = pack_bf16x2(v[8 * q + 2], v[8 * q + 3]);
       x.z = pack_bf16x2(v[8 * q + 4], v[8 * q + 5]);
       x.w = pack_bf16x2(v[8 * q + 6], v[8 * q + 7]);
-      p[q] = x;
+      st_stream(p + q, x);
     }
   }
 };
