@@ -77,6 +77,23 @@ def test_bf16_workloads_sampled(name, k):
     assert np.isfinite(yh).all() and np.isfinite(fh).all()
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_many_channels_sampled(dtype):
+    """Enough channels (batch * D >= 16384) for the 16-wave workgroups, with D not a
+    multiple of 16 so that the last workgroup of each row has idle waves."""
+    batch, L, D, N = 4, 1032, 4100, 16
+    inp = synth.make_scan_inputs(batch, L, D, N, dtype, seed=77, a_kind="lognormal", d_skip="normal")
+    y, fs = run_scan(inp)
+    yh, fh = host(y), host(fs)
+    del y, fs
+    chans = sorted(set(sample_channels(batch, D, 24, seed=2)) | {(b, D - 1 - j) for b in range(batch) for j in range(2)})
+    ry, rf = oracle_scan(inp, chans)
+    ys = np.stack([yh[b, d] for b, d in chans])
+    fss = np.stack([fh[b, d] for b, d in chans])
+    _check(ys, fss, ry, rf, dtype, f"many channels {dtype}")
+    assert np.isfinite(yh).all() and np.isfinite(fh).all()
+
+
 def test_decode_workload_512_steps():
     import torch
     from selective_state_space_68_amd import state_update
