@@ -27,8 +27,9 @@ Sources, by page and section:
   Readings taken where the pages are silent: the gate multiplies (C.h + D.u), the
   softplus has no threshold, SiLU(z) = z / (1 + exp(-z)).
 
-Memory order of the arguments matches the library: u, delta, z are [batch][D][L];
-B, C are [batch][L][N]; A is [D][N]; Dskip and bias are [D].
+Memory order: u, delta, z are [batch][D][L] (as in the library); B, C are
+[batch][L][N] (the pages' order; the library stores them [batch][N][L]); A is
+[D][N]; Dskip and bias are [D].
 """
 from __future__ import annotations
 
@@ -108,3 +109,30 @@ def state_update(state, u_t, delta_t, A, B_t, C_t, Dskip=None, z_t=None,
     if z_t is not None:
         y = y * silu(z_t)
     return y, h
+
+
+def causal_conv1d(x, w, b=None, apply_silu=True):
+    """Depthwise causal convolution along L, then SiLU: returns [batch][D][L] float64.
+
+    out[b,d,t] = sum_{k<K} w[d,k] * x[b,d,t-K+1+k] + b[d]   (x = 0 before t = 0)
+
+    The branch of the Mamba block in front of the selective SSM: a depthwise
+    (per-channel) 1-D convolution of width K (4 in the models) followed by SiLU
+    (dileepadev "Mamba Architecture", SSM block internals; vanos001 "The Mamba
+    Block" diagram and its model card's d_conv).  Causal: output t sees inputs up
+    to t only, as the recurrence that consumes it does.  w[d, K-1] weighs the
+    current token.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    Bt, Dc, L = x.shape
+    K = w.shape[1]
+    assert w.shape == (Dc, K)
+    xp = np.concatenate([np.zeros((Bt, Dc, K - 1)), x], axis=2)     # left zero padding
+    out = np.zeros((Bt, Dc, L))
+    for k in range(K):
+        out += w[None, :, k, None] * xp[:, :, k:k + L]
+    if b is not None:
+        out += np.asarray(b, dtype=np.float64)[None, :, None]
+    return silu(out) if apply_silu else out
+
