@@ -55,6 +55,7 @@ typedef enum {
 typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
 
 #define SSM_MAX_N 64
+#define SSM_MAX_CONV_WIDTH 4
 
 /*
  * Selective scan, forward (prefill / training forward).
@@ -149,6 +150,46 @@ ssm_status ssm_state_update(
     const float *Dskip, const void *z_t, const float *delta_bias, int delta_softplus,
     void *y_t,
     int64_t batch, int64_t D, int64_t N, ssm_dtype dt, void *stream);
+
+/*
+ * Causal depthwise convolution along L, optionally followed by SiLU: the branch of
+ * the Mamba block in front of the selective scan (dileepadev "Mamba
+ * Architecture", SSM block internals: depthwise conv, then SiLU, then the SSM;
+ * vanos001 "The Mamba Block" and its model card's d_conv = 4).
+ *
+ *   out[b,d,t] = act( sum_{k<K} conv_w[d,k] * x[b,d,t-K+1+k] + conv_b[d] ),  x = 0 before t = 0
+ *
+ *   x, out       : [batch][D][L] act (distinct buffers)
+ *   conv_w       : [D][K] float32; conv_w[d, K-1] weighs the current token
+ *   conv_b       : [D] float32 or NULL (= 0)
+ *   conv_width K : 1..SSM_MAX_CONV_WIDTH
+ *   apply_silu   : 1 = SiLU(z) = z / (1 + e^-z) on the result, 0 = none
+ * Errors: SSM_ERR_INVALID_ARG for NULL required pointers, negative sizes,
+ * misalignment or out overlapping an input; SSM_ERR_UNSUPPORTED for K outside
+ * 1..4 or a bad dtype; SSM_ERR_HIP when no device is usable or the launch fails.
+ */
+ssm_status ssm_causal_conv1d_fwd(
+    const void *x, const float *conv_w, const float *conv_b, int64_t conv_width, int apply_silu,
+    void *out, int64_t batch, int64_t D, int64_t L, ssm_dtype dt, void *stream);
+
+/*
+ * The scan with the causal conv1d + SiLU of ssm_causal_conv1d_fwd applied to its
+ * input on the fly: u = SiLU(conv(x)) is computed inside the scan kernel, so the
+ * block's input branch reads x once instead of writing and re-reading u.
+ *
+ *   x            : [batch][D][L] act, the conv input (in place of u)
+ *   conv_w, conv_b, conv_width : as in ssm_causal_conv1d_fwd
+ *   u_out        : [batch][D][L] act, receives u (what a backward pass needs), or NULL
+ *   tokens_per_lane : 0 (default), 8 or 16
+ * Other arguments, outputs and errors as in ssm_selective_scan_fwd_from_state
+ * (initial_state may be NULL).  The convolution starts from zeros at t = 0.
+ */
+ssm_status ssm_selective_scan_fwd_conv(
+    const void *x, const float *conv_w, const float *conv_b, int64_t conv_width,
+    const void *delta, const float *A, const void *Bm, const void *Cm,
+    const float *Dskip, const void *z, const float *delta_bias, int delta_softplus,
+    const float *initial_state, void *u_out, void *y, float *final_state,
+    int64_t batch, int64_t L, int64_t D, int64_t N, ssm_dtype dt, void *stream, int tokens_per_lane);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char *ssm_status_string(ssm_status s);

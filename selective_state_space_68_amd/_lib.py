@@ -36,6 +36,9 @@ SIGNATURES = {
                                                  _i64, _i64, _i64, _i64, _int, _vp]),
     "ssm_selective_scan_fwd_variant": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _vp, _vp, _vp,
                                               _i64, _i64, _i64, _i64, _int, _vp, _int, _int]),
+    "ssm_causal_conv1d_fwd": (_int, [_vp, _vp, _vp, _i64, _int, _vp, _i64, _i64, _i64, _int, _vp]),
+    "ssm_selective_scan_fwd_conv": (_int, [_vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _vp,
+                                           _vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _vp, _int]),
     "ssm_state_update": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _vp,
                                 _i64, _i64, _i64, _int, _vp]),
     "ssm_status_string": (ctypes.c_char_p, [_int]),

@@ -61,6 +61,36 @@ __device__ __forceinline__ void store_act<ActBF16>(void* p, int64_t i, float v) 
   static_cast<uint16_t*>(p)[i] = to_bf16(v);
 }
 
+// Eight consecutive activations as one 32-byte (float32) or 16-byte (bfloat16)
+// access; the element offset must keep the address 16-byte aligned.
+template <typename ACT>
+__device__ __forceinline__ void load_act8(const void* p, int64_t i, float (&v)[8]);
+template <>
+__device__ __forceinline__ void load_act8<ActF32>(const void* p, int64_t i, float (&v)[8]) {
+  const float4* q = reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
+  const float4 a = q[0], b = q[1];
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+template <>
+__device__ __forceinline__ void load_act8<ActBF16>(const void* p, int64_t i, float (&v)[8]) {
+  const uint4 a = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p) + i);
+  v[0] = bf16_lo(a.x); v[1] = bf16_hi(a.x); v[2] = bf16_lo(a.y); v[3] = bf16_hi(a.y);
+  v[4] = bf16_lo(a.z); v[5] = bf16_hi(a.z); v[6] = bf16_lo(a.w); v[7] = bf16_hi(a.w);
+}
+template <typename ACT>
+__device__ __forceinline__ void store_act8(void* p, int64_t i, const float (&v)[8]);
+template <>
+__device__ __forceinline__ void store_act8<ActF32>(void* p, int64_t i, const float (&v)[8]) {
+  float4* q = reinterpret_cast<float4*>(static_cast<float*>(p) + i);
+  q[0] = make_float4(v[0], v[1], v[2], v[3]);
+  q[1] = make_float4(v[4], v[5], v[6], v[7]);
+}
+template <>
+__device__ __forceinline__ void store_act8<ActBF16>(void* p, int64_t i, const float (&v)[8]) {
+  *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p) + i) =
+      make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+}
+
 // 2^x on the transcendental unit (v_exp_f32).
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 

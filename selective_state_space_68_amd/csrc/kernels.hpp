@@ -18,11 +18,26 @@ struct ScanArgs {
   const void* z;         // [batch][D][L] act or null
   const float* bias;     // [D] or null
   const float* h0;       // [batch][D][N] initial state or null (zero); may equal final_state
+  // fused causal conv1d + SiLU on the input (conv_w null: u is the scan input)
+  const float* conv_w = nullptr;  // [D][conv_k]; when set, `u` holds the conv input x
+  const float* conv_b = nullptr;  // [D] or null
+  int conv_k = 0;                 // 1..4
+  void* u_out = nullptr;          // [batch][D][L] act: the conv output (the scan input), or null
   void* y;               // [batch][D][L] act
   float* final_state;    // [batch][D][N] or null
   int64_t batch, L, D;
   int N;
   int softplus;
+};
+
+struct ConvArgs {
+  const void* x;       // [batch][D][L] act
+  const float* w;      // [D][K]
+  const float* bias;   // [D] or null
+  void* out;           // [batch][D][L] act
+  int64_t batch, D, L;
+  int K;               // 1..4
+  int silu;            // 0 or 1
 };
 
 struct StepArgs {
@@ -54,5 +69,7 @@ hipError_t launch_scan_chunked(const ScanArgs& a, Dt dt, int tokens_per_lane, hi
 hipError_t launch_copy_state(float* dst, const float* src, int64_t n, hipStream_t s);
 
 hipError_t launch_state_update(const StepArgs& a, Dt dt, hipStream_t s);
+
+hipError_t launch_causal_conv1d(const ConvArgs& a, Dt dt, hipStream_t s);
 
 }  // namespace ssm

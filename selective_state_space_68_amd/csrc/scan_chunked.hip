@@ -192,9 +192,10 @@ __device__ __forceinline__ void barrier_lds() {
 // registers.  The steady state then has no branch around any load, so the
 // compiler's tracking of outstanding loads stays exact and it never waits for a
 // load before its value is needed.  NBLK = 0: any N, steps in a runtime loop.
-template <typename ACT, bool GATE, int KPL, bool VEC, int NBLK, int kNB, int kW>
+template <typename ACT, bool GATE, int KPL, bool VEC, int NBLK, int kNB, int kW, bool CONV>
 __global__ __launch_bounds__(64 * kW) void scan_chunked_kernel(ScanArgs p, int n_dblk) {
   constexpr int kThreads = 64 * kW;
+  static_assert(KPL >= 3, "the fused conv takes its 3 earlier tokens from the previous lane");
   // states processed two at a time where the registers allow it (8 tokens per lane)
   constexpr bool PAIR = KPL <= 8;
   using IO = TokenIO<ACT, KPL>;
@@ -234,6 +235,15 @@ __global__ __launch_bounds__(64 * kW) void scan_chunked_kernel(ScanArgs p, int n
 
   float dl[KPL], du[KPL], yv[KPL];
   float sdl = 0.0f;
+  // Fused causal conv1d + SiLU on the input (CONV): per-channel taps aligned to
+  // the window x[t-3 .. t] (cw4[4-K+k] = w[d,k], the rest zero) and the last
+  // three inputs of the previous chunk (zero before the sequence starts).
+  float cw4[4] = {0.f, 0.f, 0.f, 0.f}, cbias = 0.0f, cvc[3] = {0.f, 0.f, 0.f};
+  if constexpr (CONV) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) cw4[k] = (k >= 4 - p.conv_k) ? p.conv_w[d * p.conv_k + k - (4 - p.conv_k)] : 0.0f;
+    cbias = p.conv_b ? p.conv_b[d] : 0.0f;
+  }
   int nv = KPL;                                      // valid tokens of this lane in its chunk
   raw_t u_raw[IO::kVec], d_raw[IO::kVec];            // next chunk's u and delta
   raw_t z_raw[IO::kVec];                             // this chunk's z
@@ -264,6 +274,33 @@ __global__ __launch_bounds__(64 * kW) void scan_chunked_kernel(ScanArgs p, int n
         const bool ok = j < nv;
         uv[j] = ok ? load_act<ACT>(p.u, row + tl + j) : 0.0f;
         dl[j] = ok ? load_act<ACT>(p.delta, row + tl + j) : 0.0f;
+      }
+    }
+    if constexpr (CONV) {
+      // uv holds x: u = SiLU(conv(x)).  The 3 inputs before this lane's first
+      // token are the previous lane's last three (lane 0: the previous chunk's).
+      float xx[KPL + 3];
+#pragma unroll
+      for (int k = 0; k < 3; ++k) xx[k] = wave_shift_up(uv[KPL - 3 + k], cvc[k]);
+#pragma unroll
+      for (int j = 0; j < KPL; ++j) xx[3 + j] = uv[j];
+#pragma unroll
+      for (int k = 0; k < 3; ++k) cvc[k] = wave_lane63(uv[KPL - 3 + k]);
+#pragma unroll
+      for (int j = 0; j < KPL; ++j) {
+        float sc = cbias;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) sc = __builtin_fmaf(cw4[k], xx[j + k], sc);
+        uv[j] = sc * __builtin_amdgcn_rcpf(1.0f + exp2_hw(-sc * kLog2e));
+      }
+      if (p.u_out && valid) {
+        if (VEC && nv == KPL) {
+          IO::store(p.u_out, row + tl, uv);
+        } else {
+#pragma unroll
+          for (int j = 0; j < KPL; ++j)
+            if (j < nv) store_act<ACT>(p.u_out, row + tl + j, uv[j]);
+        }
       }
     }
     if (p.softplus) {
@@ -585,7 +622,7 @@ __global__ __launch_bounds__(64 * kW) void scan_chunked_kernel(ScanArgs p, int n
 
 bool aligned16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; }
 
-template <typename ACT, bool GATE, int KPL, int W>
+template <typename ACT, bool GATE, int KPL, int W, bool CONV>
 hipError_t launch_w(const ScanArgs& a, hipStream_t s) {
   const int n_dblk = static_cast<int>((a.D + W - 1) / W);
   const int64_t blocks = a.batch * n_dblk;
@@ -600,21 +637,21 @@ hipError_t launch_w(const ScanArgs& a, hipStream_t s) {
   // that way, and at 16 tokens per lane the larger tile's registers would spill.
   constexpr int N16_STEPS = (ACT::kBytes == 2 && KPL <= 8) ? 2 : 4;
   if (vec && n16)
-    hipLaunchKernelGGL((scan_chunked_kernel<ACT, GATE, KPL, true, N16_STEPS, 16 / N16_STEPS, W>), grid, block, 0,
+    hipLaunchKernelGGL((scan_chunked_kernel<ACT, GATE, KPL, true, N16_STEPS, 16 / N16_STEPS, W, CONV>), grid, block, 0,
                        s, a, n_dblk);
   else if (vec)
-    hipLaunchKernelGGL((scan_chunked_kernel<ACT, GATE, KPL, true, 0, kNBGeneric, W>), grid, block, 0, s, a,
+    hipLaunchKernelGGL((scan_chunked_kernel<ACT, GATE, KPL, true, 0, kNBGeneric, W, CONV>), grid, block, 0, s, a,
                        n_dblk);
   else if (n16)
-    hipLaunchKernelGGL((scan_chunked_kernel<ACT, GATE, KPL, false, N16_STEPS, 16 / N16_STEPS, W>), grid, block,
+    hipLaunchKernelGGL((scan_chunked_kernel<ACT, GATE, KPL, false, N16_STEPS, 16 / N16_STEPS, W, CONV>), grid, block,
                        0, s, a, n_dblk);
   else
-    hipLaunchKernelGGL((scan_chunked_kernel<ACT, GATE, KPL, false, 0, kNBGeneric, W>), grid, block, 0, s, a,
+    hipLaunchKernelGGL((scan_chunked_kernel<ACT, GATE, KPL, false, 0, kNBGeneric, W, CONV>), grid, block, 0, s, a,
                        n_dblk);
   return hipGetLastError();
 }
 
-template <typename ACT, bool GATE, int KPL>
+template <typename ACT, bool GATE, int KPL, bool CONV>
 hipError_t launch_kpl(const ScanArgs& a, hipStream_t s) {
   // 12 waves per workgroup (3 per SIMD, one workgroup per CU) leaves the most
   // registers per wave.  With enough channels for four rounds of 16-wave
@@ -622,15 +659,16 @@ hipError_t launch_kpl(const ScanArgs& a, hipStream_t s) {
   // waves, 4 per SIMD, for more latency hiding: 9 % faster on the 1.4B-shaped
   // bfloat16 workload.  Fewer channels keep 12 so that every CU gets a workgroup.
   if constexpr (KPL == 8) {
-    if (a.batch * a.D >= 16 * 256 * 4) return launch_w<ACT, GATE, KPL, 16>(a, s);
+    if (a.batch * a.D >= 16 * 256 * 4) return launch_w<ACT, GATE, KPL, 16, CONV>(a, s);
   }
-  return launch_w<ACT, GATE, KPL, 12>(a, s);
+  return launch_w<ACT, GATE, KPL, 12, CONV>(a, s);
 }
 
 template <typename ACT, bool GATE>
 hipError_t launch_gate(const ScanArgs& a, int kpl, hipStream_t s) {
-  if (kpl == 8) return launch_kpl<ACT, GATE, 8>(a, s);
-  return launch_kpl<ACT, GATE, 16>(a, s);
+  const bool conv = a.conv_w != nullptr;
+  if (kpl == 8) return conv ? launch_kpl<ACT, GATE, 8, true>(a, s) : launch_kpl<ACT, GATE, 8, false>(a, s);
+  return conv ? launch_kpl<ACT, GATE, 16, true>(a, s) : launch_kpl<ACT, GATE, 16, false>(a, s);
 }
 
 // Default tokens per lane, from measurement on gfx950: 8, where the registers

@@ -11,7 +11,7 @@
 
 namespace {
 
-constexpr int kVersion = 20100;  // 2.1.0: B and C stored [batch][N][L], no workspace; initial state
+constexpr int kVersion = 20200;  // 2.2.0: + causal conv1d, standalone and fused into the scan
 
 struct Span {
   uintptr_t lo = 0, hi = 0;  // [lo, hi); empty when lo == hi
@@ -157,6 +157,79 @@ ssm_status ssm_selective_scan_fwd_from_state(const void* u, const void* delta, c
   return ssm_selective_scan_fwd_variant(u, delta, A, Bm, Cm, Dskip, z, delta_bias, delta_softplus,
                                         initial_state, y, final_state, batch, L, D, N, dt, stream,
                                         SSM_SCAN_AUTO, 0);
+}
+
+ssm_status ssm_selective_scan_fwd_conv(const void* x, const float* conv_w, const float* conv_b, int64_t conv_width,
+                                       const void* delta, const float* A, const void* Bm, const void* Cm,
+                                       const float* Dskip, const void* z, const float* delta_bias,
+                                       int delta_softplus, const float* initial_state, void* u_out, void* y,
+                                       float* final_state, int64_t batch, int64_t L, int64_t D, int64_t N,
+                                       ssm_dtype dt, void* stream, int tokens_per_lane) {
+  ScanSizes sz;
+  ssm_status st = check_scan(x, delta, A, Bm, Cm, Dskip, z, delta_bias, delta_softplus, initial_state, y,
+                             final_state, batch, L, D, N, dt, &sz);
+  if (st != SSM_OK) return st;
+  if (conv_width < 1 || conv_width > SSM_MAX_CONV_WIDTH) return SSM_ERR_UNSUPPORTED;
+  if (!(tokens_per_lane == 0 || tokens_per_lane == 8 || tokens_per_lane == 16)) return SSM_ERR_UNSUPPORTED;
+  uint64_t wbytes = 0;
+  if (!mul_ok(D, conv_width, &wbytes) || !mul_ok(wbytes, 4, &wbytes)) return SSM_ERR_INVALID_ARG;
+  if ((!conv_w && wbytes) || !aligned(conv_w, 4) || !aligned(conv_b, 4) || !aligned(u_out, dt == SSM_BF16 ? 2 : 4))
+    return SSM_ERR_INVALID_ARG;
+  // u_out is an output: it must not overlap any input or the other outputs
+  const Span uo = span(u_out, sz.act_bytes);
+  const Span others[] = {span(x, sz.act_bytes),          span(delta, sz.act_bytes),   span(z, sz.act_bytes),
+                         span(A, sz.a_bytes),            span(Bm, sz.bc_bytes),       span(Cm, sz.bc_bytes),
+                         span(Dskip, sz.vec_bytes),      span(delta_bias, sz.vec_bytes),
+                         span(initial_state, sz.state_bytes), span(y, sz.act_bytes),
+                         span(final_state, sz.state_bytes), span(conv_w, wbytes),     span(conv_b, sz.vec_bytes)};
+  for (const Span& o : others)
+    if (overlaps(uo, o)) return SSM_ERR_INVALID_ARG;
+  const Span ws = span(conv_w, wbytes), bs = span(conv_b, sz.vec_bytes);
+  if (overlaps(ws, span(y, sz.act_bytes)) || overlaps(ws, span(final_state, sz.state_bytes)) ||
+      overlaps(bs, span(y, sz.act_bytes)) || overlaps(bs, span(final_state, sz.state_bytes)))
+    return SSM_ERR_INVALID_ARG;
+  if (batch == 0 || D == 0) return SSM_OK;
+  st = probe_device();
+  if (st != SSM_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (L == 0)
+    return final_state ? from_hip(ssm::launch_copy_state(final_state, initial_state, batch * D * N, s)) : SSM_OK;
+  ssm::ScanArgs a;
+  a.u = x; a.delta = delta; a.A = A; a.Bm = Bm; a.Cm = Cm; a.Dskip = Dskip; a.z = z;
+  a.bias = delta_bias; a.h0 = initial_state; a.y = y; a.final_state = final_state;
+  a.batch = batch; a.L = L; a.D = D; a.N = static_cast<int>(N); a.softplus = delta_softplus;
+  a.conv_w = conv_w; a.conv_b = conv_b; a.conv_k = static_cast<int>(conv_width); a.u_out = u_out;
+  const ssm::Dt d = dt == SSM_BF16 ? ssm::Dt::BF16 : ssm::Dt::F32;
+  if (!ssm::chunked_supported(a, d, tokens_per_lane)) return SSM_ERR_UNSUPPORTED;
+  return from_hip(ssm::launch_scan_chunked(a, d, tokens_per_lane, s));
+}
+
+ssm_status ssm_causal_conv1d_fwd(const void* x, const float* conv_w, const float* conv_b, int64_t conv_width,
+                                 int apply_silu, void* out, int64_t batch, int64_t D, int64_t L, ssm_dtype dt,
+                                 void* stream) {
+  if (dt != SSM_F32 && dt != SSM_BF16) return SSM_ERR_UNSUPPORTED;
+  if (batch < 0 || D < 0 || L < 0) return SSM_ERR_INVALID_ARG;
+  if (conv_width < 1 || conv_width > SSM_MAX_CONV_WIDTH) return SSM_ERR_UNSUPPORTED;
+  if (apply_silu != 0 && apply_silu != 1) return SSM_ERR_INVALID_ARG;
+  const uint64_t e = dt == SSM_BF16 ? 2 : 4;
+  uint64_t bd, bdl, xbytes, wbytes;
+  if (!mul_ok(batch, D, &bd) || !mul_ok(bd, L, &bdl) || !mul_ok(bdl, e, &xbytes) ||
+      !mul_ok(D, conv_width, &wbytes) || !mul_ok(wbytes, 4, &wbytes) || xbytes > (uint64_t(1) << 62))
+    return SSM_ERR_INVALID_ARG;
+  if ((!x && xbytes) || (!out && xbytes) || (!conv_w && wbytes)) return SSM_ERR_INVALID_ARG;
+  if (!aligned(x, e) || !aligned(out, e) || !aligned(conv_w, 4) || !aligned(conv_b, 4)) return SSM_ERR_INVALID_ARG;
+  const Span os = span(out, xbytes);
+  if (overlaps(os, span(x, xbytes)) || overlaps(os, span(conv_w, wbytes)) ||
+      overlaps(os, span(conv_b, static_cast<uint64_t>(D) * 4)))
+    return SSM_ERR_INVALID_ARG;
+  if (xbytes == 0) return SSM_OK;
+  const ssm_status st = probe_device();
+  if (st != SSM_OK) return st;
+  ssm::ConvArgs a;
+  a.x = x; a.w = conv_w; a.bias = conv_b; a.out = out;
+  a.batch = batch; a.D = D; a.L = L; a.K = static_cast<int>(conv_width); a.silu = apply_silu;
+  return from_hip(ssm::launch_causal_conv1d(a, dt == SSM_BF16 ? ssm::Dt::BF16 : ssm::Dt::F32,
+                                            static_cast<hipStream_t>(stream)));
 }
 
 ssm_status ssm_state_update(const float* state_in, float* state_out, const void* u_t, const void* delta_t,

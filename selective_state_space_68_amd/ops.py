@@ -86,6 +86,70 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta
     return y, final_state
 
 
+def causal_conv1d(x, weight, bias=None, silu=True, *, out=None, stream=None) -> torch.Tensor:
+    """Causal depthwise conv1d along L (+ SiLU).  x [batch, D, L]; weight [D, K] float32
+    (K <= 4, weight[:, K-1] weighs the current token); bias [D] or None."""
+    lib = _lib.load_library()
+    if x.dim() != 3 or weight.dim() != 2 or weight.shape[0] != x.shape[1]:
+        raise ValueError("expected x [batch, D, L] and weight [D, K]")
+    batch, Dc, L = x.shape
+    if bias is not None and tuple(bias.shape) != (Dc,):
+        raise ValueError("bias must be [D]")
+    dev = x.device
+    if out is None:
+        out = torch.empty_like(x)
+    st = lib.ssm_causal_conv1d_fwd(
+        _ptr(x, "x", x.dtype, dev), _ptr(weight, "weight", torch.float32, dev),
+        _ptr(bias, "bias", torch.float32, dev), int(weight.shape[1]), 1 if silu else 0,
+        _ptr(out, "out", x.dtype, dev), batch, Dc, L, _dt(x), _stream(stream))
+    _lib.check(st)
+    return out
+
+
+def selective_scan_fwd_conv(x, conv_weight, conv_bias, delta, A, B, C, D=None, z=None, delta_bias=None,
+                            delta_softplus=True, *, initial_state=None, u_out=None, return_u=False, y=None,
+                            final_state=None, return_final_state=True, tokens_per_lane=0,
+                            stream=None):
+    """Scan of u = SiLU(causal_conv1d(x)) with the convolution fused into the scan kernel.
+
+    Returns (y, final_state, u) where u is the convolution output when `return_u`
+    (or `u_out` is given), else None."""
+    lib = _lib.load_library()
+    if x.dim() != 3 or B.dim() != 3 or A.dim() != 2 or conv_weight.dim() != 2:
+        raise ValueError("expected x [batch, D, L], B/C [batch, N, L], A [D, N], conv_weight [D, K]")
+    batch, Dc, L = x.shape
+    N = A.shape[1]
+    act = x.dtype
+    dev = x.device
+    if tuple(delta.shape) != (batch, Dc, L) or tuple(A.shape) != (Dc, N) or conv_weight.shape[0] != Dc:
+        raise ValueError("delta / A / conv_weight shape mismatch")
+    if tuple(B.shape) != (batch, N, L) or tuple(C.shape) != (batch, N, L):
+        raise ValueError("B / C must be [batch, N, L]")
+    if z is not None and tuple(z.shape) != (batch, Dc, L):
+        raise ValueError("z must be [batch, D, L]")
+    for name, v in (("D", D), ("delta_bias", delta_bias), ("conv_bias", conv_bias)):
+        if v is not None and tuple(v.shape) != (Dc,):
+            raise ValueError(f"{name} must be [D]")
+    if y is None:
+        y = torch.empty((batch, Dc, L), dtype=act, device=dev)
+    if final_state is None and return_final_state:
+        final_state = torch.empty((batch, Dc, N), dtype=torch.float32, device=dev)
+    if u_out is None and return_u:
+        u_out = torch.empty((batch, Dc, L), dtype=act, device=dev)
+    st = lib.ssm_selective_scan_fwd_conv(
+        _ptr(x, "x", act, dev), _ptr(conv_weight, "conv_weight", torch.float32, dev),
+        _ptr(conv_bias, "conv_bias", torch.float32, dev), int(conv_weight.shape[1]),
+        _ptr(delta, "delta", act, dev), _ptr(A, "A", torch.float32, dev),
+        _ptr(B, "B", act, dev), _ptr(C, "C", act, dev), _ptr(D, "D", torch.float32, dev),
+        _ptr(z, "z", act, dev), _ptr(delta_bias, "delta_bias", torch.float32, dev),
+        1 if delta_softplus else 0, _ptr(initial_state, "initial_state", torch.float32, dev),
+        _ptr(u_out, "u_out", act, dev), _ptr(y, "y", act, dev),
+        _ptr(final_state, "final_state", torch.float32, dev),
+        batch, L, Dc, N, _dt(x), _stream(stream), int(tokens_per_lane))
+    _lib.check(st)
+    return y, final_state, u_out
+
+
 def state_update(state, u_t, delta_t, A, B_t, C_t, D=None, z_t=None, delta_bias=None,
                  delta_softplus=True, *, out_state=None, y=None, stream=None) -> torch.Tensor:
     """One decode step.  Updates `out_state` (default: `state`, in place); returns y_t [S, D]."""

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.ssm_version() == 20100
+    assert lib.ssm_version() == 20200
     for s in range(4):
         assert lib.ssm_status_string(s).decode().startswith(("SSM_OK", "SSM_ERR"))
     assert b"unknown" in lib.ssm_status_string(99)
@@ -116,6 +116,52 @@ def test_state_update_argument_errors(lib, kw, status):
     assert _step(lib, **kw) == status
 
 
+def _conv(lib, **kw):
+    a = dict(x=F, w=F + 1 * 64 * MB, b=None, K=4, silu=1, out=F + 2 * 64 * MB, batch=2, D=8, L=64, dt=0)
+    a.update(kw)
+    return lib.ssm_causal_conv1d_fwd(a["x"], a["w"], a["b"], a["K"], a["silu"], a["out"], a["batch"], a["D"],
+                                     a["L"], a["dt"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), _lib.SSM_ERR_INVALID_ARG),
+    (dict(w=None), _lib.SSM_ERR_INVALID_ARG),
+    (dict(K=0), _lib.SSM_ERR_UNSUPPORTED),
+    (dict(K=5), _lib.SSM_ERR_UNSUPPORTED),
+    (dict(silu=3), _lib.SSM_ERR_INVALID_ARG),
+    (dict(out=F), _lib.SSM_ERR_INVALID_ARG),                         # in place is not allowed
+    (dict(out=F + 2 * 64 * MB + 2), _lib.SSM_ERR_INVALID_ARG),       # misaligned
+    (dict(L=-1), _lib.SSM_ERR_INVALID_ARG),
+])
+def test_conv_argument_errors(lib, kw, status):
+    assert _conv(lib, **kw) == status
+
+
+def _scan_conv(lib, **kw):
+    a = dict(x=F, w=F + 7 * 64 * MB, cb=None, K=4, delta=F + 1 * 64 * MB, A=F + 2 * 64 * MB, B=F + 3 * 64 * MB,
+             C=F + 4 * 64 * MB, Dskip=None, z=None, bias=None, softplus=1, h0=None, u_out=None,
+             y=F + 5 * 64 * MB, final=F + 6 * 64 * MB, batch=1, L=64, D=16, N=4, dt=0, kpl=0)
+    a.update(kw)
+    return lib.ssm_selective_scan_fwd_conv(a["x"], a["w"], a["cb"], a["K"], a["delta"], a["A"], a["B"], a["C"],
+                                           a["Dskip"], a["z"], a["bias"], a["softplus"], a["h0"], a["u_out"],
+                                           a["y"], a["final"], a["batch"], a["L"], a["D"], a["N"], a["dt"], None,
+                                           a["kpl"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(w=None), _lib.SSM_ERR_INVALID_ARG),
+    (dict(K=7), _lib.SSM_ERR_UNSUPPORTED),
+    (dict(kpl=12), _lib.SSM_ERR_UNSUPPORTED),
+    (dict(u_out=F + 5 * 64 * MB), _lib.SSM_ERR_INVALID_ARG),         # u_out aliases y
+    (dict(u_out=F), _lib.SSM_ERR_INVALID_ARG),                       # u_out aliases x
+    (dict(u_out=F + 7 * 64 * MB), _lib.SSM_ERR_INVALID_ARG),         # u_out aliases the taps
+    (dict(y=F + 7 * 64 * MB), _lib.SSM_ERR_INVALID_ARG),             # y overlaps the taps
+    (dict(x=None), _lib.SSM_ERR_INVALID_ARG),
+])
+def test_scan_conv_argument_errors(lib, kw, status):
+    assert _scan_conv(lib, **kw) == status
+
+
 def test_state_update_empty_is_noop(lib):
     assert _step(lib, batch=0) == _lib.SSM_OK
 
@@ -135,6 +181,9 @@ def test_valid_call_without_device_reports_hip_error(lib):
     assert _scan(lib, variant=1) == _lib.SSM_ERR_HIP                      # sequential kernel
     assert _scan(lib, h0=F + 7 * 64 * MB) == _lib.SSM_ERR_HIP             # from a given state
     assert _scan(lib, h0=F + 6 * 64 * MB) == _lib.SSM_ERR_HIP             # ... updated in place
+    assert _conv(lib) == _lib.SSM_ERR_HIP
+    assert _scan_conv(lib) == _lib.SSM_ERR_HIP
+    assert _scan_conv(lib, u_out=F + 8 * 64 * MB, cb=F + 9 * 64 * MB) == _lib.SSM_ERR_HIP
     assert _step(lib, sout=F) == _lib.SSM_ERR_HIP          # exact in-place is valid
     with pytest.raises(_lib.SsmError) as ei:
         _lib.check(_lib.SSM_ERR_HIP)
