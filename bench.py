@@ -147,6 +147,15 @@ def bench_scan(args, torch, lib_ops):
         t["fs"] = torch.empty((cfg.batch, cfg.D, cfg.N), dtype=torch.float32, device="cuda")
         bufs.append(t)
 
+    if cfg.conv_k:
+        cw, cb = (dev(torch, x) for x in synth.make_conv_params(cfg.D, cfg.conv_k, seed=cfg.seed))
+
+        def step(i):              # u = SiLU(conv1d(x)) fused into the scan; t["u"] holds x
+            t = bufs[i % sets]
+            lib_ops.selective_scan_fwd_conv(t["u"], cw, cb, t["delta"], A, t["B"], t["C"], Dk, t["z"], bias, True,
+                                            y=t["y"], final_state=t["fs"], tokens_per_lane=args.kpl)
+        return cfg, inp, nbytes, cfg.elements, sets, step, bufs
+
     def step(i):
         t = bufs[i % sets]
         lib_ops.selective_scan_fwd(t["u"], t["delta"], A, t["B"], t["C"], Dk, t["z"], bias, True,
@@ -275,7 +284,7 @@ def main():
     hbm_gbs = nbytes / launch_s / 1e9
 
     cpu = None
-    if kind == "scan" and not args.no_cpu_baseline:
+    if kind == "scan" and not args.no_cpu_baseline and not cfg.conv_k:
         cpu = cpu_baseline_scan(cfg, inp, args.cpu_budget)
 
     traffic = traffic_from_profiles(args.workload, kind)
@@ -310,7 +319,7 @@ def main():
         "dtype": "f32",
         "data": "synthetic (seeded; shapes and distributions of the named workload)",
         "config": ({"workload": args.workload, "batch": cfg.batch, "L": cfg.L, "D": cfg.D, "N": cfg.N,
-                    "act_dtype": cfg.dtype, "gate": cfg.gate, "variant": args.variant,
+                    "act_dtype": cfg.dtype, "gate": cfg.gate, "conv_width": cfg.conv_k, "variant": args.variant,
                     "tokens_per_lane": args.kpl or "auto", "graph": graph is not None, "input_copies": sets}
                    if kind == "scan" else
                    {"workload": args.workload, "sequences": cfg.batch, "D": cfg.D, "N": cfg.N,

@@ -19,6 +19,7 @@ class ScanConfig:
     gate: bool          # SiLU(z) output gate present
     d_skip: str         # "normal": D ~ N(0,1); "ones": D = 1
     seed: int = 0
+    conv_k: int = 0     # > 0: the input is x and u = SiLU(causal conv1d of width conv_k) is fused in
 
     @property
     def elements(self) -> int:
@@ -33,7 +34,8 @@ class ScanConfig:
                 + 2 * self.batch * self.L * self.N * e  # B, C
                 + 4 * self.D * self.N                   # A
                 + 4 * self.D * 2                        # D skip + delta bias
-                + 4 * self.batch * self.D * self.N)     # final state
+                + 4 * self.batch * self.D * self.N     # final state
+                + 4 * self.D * (self.conv_k + 1 if self.conv_k else 0))   # conv taps + bias
 
 
 @dataclass(frozen=True)
@@ -66,4 +68,9 @@ CONFIGS = {
     "mamba1p4b_bf16": ScanConfig("mamba1p4b_bf16", 8, 2048, 4096, 16, "bf16", gate=True, d_skip="ones"),
     "long131k_bf16": ScanConfig("long131k_bf16", 1, 131072, 2560, 16, "bf16", gate=True, d_skip="ones"),
     "decode_bf16": DecodeConfig("decode_bf16", 256, 5120, 16, 512),
+    # the block's conv1d (d_conv = 4 on the interview-prep page's model card) fused into the scan
+    "mamba130m_conv_f32": ScanConfig("mamba130m_conv_f32", 2, 2048, 1536, 16, "f32", gate=True, d_skip="ones",
+                                     conv_k=4),
+    "mamba1p4b_conv_bf16": ScanConfig("mamba1p4b_conv_bf16", 8, 2048, 4096, 16, "bf16", gate=True,
+                                      d_skip="ones", conv_k=4),
 }

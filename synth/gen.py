@@ -31,7 +31,7 @@ from typing import Optional
 import numpy as np
 
 # Fixed order of SeedSequence children; adding a tensor at the end keeps old streams.
-_SCAN_STREAMS = ("u", "delta", "dt", "B", "C", "Dskip", "z", "h0", "A")
+_SCAN_STREAMS = ("u", "delta", "dt", "B", "C", "Dskip", "z", "h0", "A", "conv")
 _STEP_STREAMS = ("u", "delta", "B", "C", "z")
 _DECODE_STEP_KEY = 4
 
@@ -170,6 +170,17 @@ def make_scan_initial_state(batch: int, D: int, N: int, seed: int = 0) -> np.nda
     ss = np.random.SeedSequence(seed)
     kid = ss.spawn(len(_SCAN_STREAMS))[_SCAN_STREAMS.index("h0")]
     return np.random.Generator(np.random.PCG64(kid)).standard_normal((batch, D, N), dtype=np.float32)
+
+
+def make_conv_params(D: int, K: int, seed: int = 0):
+    """Causal conv1d taps [D][K] ~ N(0, 1/K) and bias [D] ~ N(0, 0.1^2), float32,
+    from the seed's "conv" stream (the scale keeps the conv output near unit variance)."""
+    ss = np.random.SeedSequence(seed)
+    kid = ss.spawn(len(_SCAN_STREAMS))[_SCAN_STREAMS.index("conv")]
+    r = np.random.Generator(np.random.PCG64(kid))
+    w = (r.standard_normal((D, K)) / np.sqrt(K)).astype(np.float32)
+    b = (r.standard_normal(D) * 0.1).astype(np.float32)
+    return w, b
 
 
 def make_config_inputs(cfg, seed: Optional[int] = None, **kw) -> ScanInputs:
