@@ -4,4 +4,4 @@ TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import or call this
 package: only the tests, the smoke check and the benchmark's CPU-baseline leg use
 it.  It shares no code with the HIP library and does not import it.
 """
-from .ssm import selective_scan, state_update, softplus, silu, causal_conv1d  # noqa: F401
+from .ssm import selective_scan, selective_scan_bwd, state_update, softplus, silu, causal_conv1d  # noqa: F401

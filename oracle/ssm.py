@@ -136,3 +136,75 @@ def causal_conv1d(x, w, b=None, apply_silu=True):
         out += np.asarray(b, dtype=np.float64)[None, :, None]
     return silu(out) if apply_silu else out
 
+
+
+def selective_scan_bwd(u, delta, A, B, C, dy, Dskip=None, z=None, delta_bias=None,
+                       delta_softplus=True, h0=None):
+    """Gradients of sum(dy * y) for y = selective_scan(...), float64.
+
+    Returns a dict with du, ddelta (w.r.t. the raw delta), dA, dB, dC, dD, dz,
+    ddelta_bias and dh0, each shaped like its input (None where the input is None).
+
+    The reverse-time (adjoint) recurrence of the same linear system: with
+    g_t = dy_t * SiLU(z_t) the gradient of the pre-gate output,
+    lam_t = g_t C_t + abar_{t+1} lam_{t+1} is the gradient of the state h_t, and
+    every parameter's gradient is a sum over t of lam_t (or g_t) times the partial
+    derivative of one step.  This is the backward pass that recomputes the states
+    instead of storing them (slide deck "Mamba selective"; blog "Hardware-Aware
+    Parallel Scan"), written plainly: the forward states are kept here.
+    """
+    u = np.asarray(u, dtype=np.float64)
+    Bt, Dc, L = u.shape
+    A = np.asarray(A, dtype=np.float64)
+    N = A.shape[1]
+    Bm = np.asarray(B, dtype=np.float64)
+    Cm = np.asarray(C, dtype=np.float64)
+    dy = np.asarray(dy, dtype=np.float64)
+    raw = np.asarray(delta, dtype=np.float64)
+    if delta_bias is not None:
+        raw = raw + np.asarray(delta_bias, dtype=np.float64)[None, :, None]
+    dlt = softplus(raw) if delta_softplus else raw                     # [Bt, Dc, L]
+    Dv = np.zeros(Dc) if Dskip is None else np.asarray(Dskip, dtype=np.float64)
+
+    # forward, keeping every state and the pre-gate output
+    hs = np.empty((L + 1, Bt, Dc, N))
+    hs[0] = 0.0 if h0 is None else np.asarray(h0, dtype=np.float64)
+    abar = np.exp(dlt[..., None] * A[None, :, None, :])                # [Bt, Dc, L, N]
+    for t in range(L):
+        hs[t + 1] = abar[:, :, t] * hs[t] + (dlt[:, :, t] * u[:, :, t])[..., None] * Bm[:, t, None, :]
+    ytil = np.einsum("tbdn,btn->bdt", hs[1:], Cm) + Dv[None, :, None] * u
+
+    if z is not None:
+        zz = np.asarray(z, dtype=np.float64)
+        sig = 1.0 / (1.0 + np.exp(-zz))
+        g = dy * zz * sig                                              # dy * SiLU(z)
+        dz = dy * ytil * sig * (1.0 + zz * (1.0 - sig))                # dy * ytil * SiLU'(z)
+    else:
+        g = dy
+        dz = None
+
+    du = Dv[None, :, None] * g
+    ddl = np.zeros((Bt, Dc, L))
+    dA = np.zeros((Dc, N))
+    dB = np.zeros((Bt, L, N))
+    dC = np.zeros((Bt, L, N))
+    lam_next = np.zeros((Bt, Dc, N))          # abar_{t+1} * lam_{t+1}
+    for t in range(L - 1, -1, -1):
+        lam = g[:, :, t, None] * Cm[:, t, None, :] + lam_next          # dL/dh_t
+        dC[:, t] = np.einsum("bd,bdn->bn", g[:, :, t], hs[t + 1])
+        dB[:, t] = np.einsum("bdn,bd->bn", lam, dlt[:, :, t] * u[:, :, t])
+        du[:, :, t] += dlt[:, :, t] * np.einsum("bdn,bn->bd", lam, Bm[:, t])
+        da = lam * hs[t]                                               # dL/dabar_t
+        ddl[:, :, t] = (np.einsum("bdn,bn->bd", lam, Bm[:, t]) * u[:, :, t]
+                        + np.einsum("bdn,bdn->bd", da * abar[:, :, t], np.broadcast_to(A, da.shape)))
+        dA += np.einsum("bdn,bd->dn", da * abar[:, :, t], dlt[:, :, t])
+        lam_next = abar[:, :, t] * lam
+    dh0 = lam_next if h0 is not None else None
+    ddraw = ddl * (1.0 / (1.0 + np.exp(-raw))) if delta_softplus else ddl
+    return {
+        "du": du, "ddelta": ddraw, "dA": dA, "dB": dB, "dC": dC,
+        "dD": None if Dskip is None else np.einsum("bdt,bdt->d", g, u),
+        "dz": dz,
+        "ddelta_bias": None if delta_bias is None else ddraw.sum(axis=(0, 2)),
+        "dh0": dh0,
+    }
