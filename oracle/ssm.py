@@ -139,8 +139,9 @@ def causal_conv1d(x, w, b=None, apply_silu=True):
 
 
 def selective_scan_bwd(u, delta, A, B, C, dy, Dskip=None, z=None, delta_bias=None,
-                       delta_softplus=True, h0=None):
-    """Gradients of sum(dy * y) for y = selective_scan(...), float64.
+                       delta_softplus=True, h0=None, dfinal=None):
+    """Gradients of sum(dy * y) + sum(dfinal * final) for (y, final) =
+    selective_scan(...), float64 (dfinal None: the final state is not used).
 
     Returns a dict with du, ddelta (w.r.t. the raw delta), dA, dB, dC, dD, dz,
     ddelta_bias and dh0, each shaped like its input (None where the input is None).
@@ -188,7 +189,8 @@ def selective_scan_bwd(u, delta, A, B, C, dy, Dskip=None, z=None, delta_bias=Non
     dA = np.zeros((Dc, N))
     dB = np.zeros((Bt, L, N))
     dC = np.zeros((Bt, L, N))
-    lam_next = np.zeros((Bt, Dc, N))          # abar_{t+1} * lam_{t+1}
+    # abar_{t+1} * lam_{t+1}; past the last token it is the final state's cotangent
+    lam_next = np.zeros((Bt, Dc, N)) if dfinal is None else np.array(dfinal, dtype=np.float64)
     for t in range(L - 1, -1, -1):
         lam = g[:, :, t, None] * Cm[:, t, None, :] + lam_next          # dL/dh_t
         dC[:, t] = np.einsum("bd,bdn->bn", g[:, :, t], hs[t + 1])

@@ -12,6 +12,7 @@ from .gen import (  # noqa: F401
     make_scan_inputs,
     make_config_inputs,
     make_scan_initial_state,
+    make_scan_cotangents,
     make_conv_params,
     make_decode_state,
     make_decode_step,

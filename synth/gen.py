@@ -31,7 +31,7 @@ from typing import Optional
 import numpy as np
 
 # Fixed order of SeedSequence children; adding a tensor at the end keeps old streams.
-_SCAN_STREAMS = ("u", "delta", "dt", "B", "C", "Dskip", "z", "h0", "A", "conv")
+_SCAN_STREAMS = ("u", "delta", "dt", "B", "C", "Dskip", "z", "h0", "A", "conv", "dy", "dfinal")
 _STEP_STREAMS = ("u", "delta", "B", "C", "z")
 _DECODE_STEP_KEY = 4
 
@@ -181,6 +181,22 @@ def make_conv_params(D: int, K: int, seed: int = 0):
     w = (r.standard_normal((D, K)) / np.sqrt(K)).astype(np.float32)
     b = (r.standard_normal(D) * 0.1).astype(np.float32)
     return w, b
+
+
+def make_scan_cotangents(batch: int, L: int, D: int, N: int, dtype: str = "f32", seed: int = 0,
+                         with_dfinal: bool = False):
+    """Output cotangents for a backward pass: dy [batch][D][L] ~ N(0, 1) in the
+    activation dtype (returned as (float32 values, upload array)) and, if asked,
+    dfinal [batch][D][N] ~ N(0, 1) float32 for the final state; from the seed's
+    "dy" and "dfinal" streams."""
+    ss = np.random.SeedSequence(seed)
+    kids = dict(zip(_SCAN_STREAMS, ss.spawn(len(_SCAN_STREAMS))))
+    dy32 = np.random.Generator(np.random.PCG64(kids["dy"])).standard_normal((batch, D, L), dtype=np.float32)
+    vals, up = _act(dy32, dtype)
+    dfin = None
+    if with_dfinal:
+        dfin = np.random.Generator(np.random.PCG64(kids["dfinal"])).standard_normal((batch, D, N), dtype=np.float32)
+    return vals, up, dfin
 
 
 def make_config_inputs(cfg, seed: Optional[int] = None, **kw) -> ScanInputs:

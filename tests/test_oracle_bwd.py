@@ -29,9 +29,9 @@ NAMES = {"u": "du", "delta": "ddelta", "A": "dA", "B": "dB", "C": "dC", "Dskip":
          "delta_bias": "ddelta_bias", "h0": "dh0"}
 
 
-def _loss(inp, dy):
-    y, _ = oracle.selective_scan(**inp)
-    return float(np.sum(y * dy))
+def _loss(inp, dy, dfinal=None):
+    y, fin = oracle.selective_scan(**inp)
+    return float(np.sum(y * dy)) + (0.0 if dfinal is None else float(np.sum(fin * dfinal)))
 
 
 @pytest.mark.parametrize("cfg", [
@@ -39,14 +39,20 @@ def _loss(inp, dy):
     dict(gate=False, bias=False, h0=False),
     dict(softplus=False),
     dict(L=1, N=1, Dc=1, Bt=1),
+    dict(dfinal=True),
+    dict(dfinal=True, h0=False, gate=False),
 ])
 def test_gradients_match_finite_differences(cfg):
+    cfg = dict(cfg)
+    with_dfinal = cfg.pop("dfinal", False)
     inp = _inputs(3, **cfg)
     r = np.random.default_rng(11)
-    y, _ = oracle.selective_scan(**inp)
+    y, fin = oracle.selective_scan(**inp)
     dy = r.standard_normal(y.shape)
+    dfinal = r.standard_normal(fin.shape) if with_dfinal else None
     grads = oracle.selective_scan_bwd(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"], dy,
-                                      inp["Dskip"], inp["z"], inp["delta_bias"], inp["delta_softplus"], inp["h0"])
+                                      inp["Dskip"], inp["z"], inp["delta_bias"], inp["delta_softplus"], inp["h0"],
+                                      dfinal)
     eps = 1e-6
     for name, gname in NAMES.items():
         if inp[name] is None:
@@ -57,9 +63,9 @@ def test_gradients_match_finite_differences(cfg):
         for idx in np.ndindex(x.shape):
             old = x[idx]
             x[idx] = old + eps
-            lp = _loss(inp, dy)
+            lp = _loss(inp, dy, dfinal)
             x[idx] = old - eps
-            lm = _loss(inp, dy)
+            lm = _loss(inp, dy, dfinal)
             x[idx] = old
             fd[idx] = (lp - lm) / (2 * eps)
         err = np.max(np.abs(fd - grads[gname])) / max(1.0, np.max(np.abs(fd)))
