@@ -30,7 +30,8 @@
  *  - The library never allocates or frees device memory; the caller owns
  *    every buffer.  NaN/Inf inputs are not checked and propagate.
  *  - Results are deterministic: same inputs, shapes and device give
- *    bitwise-identical outputs.
+ *    bitwise-identical outputs (the backward pass's dB and dC excepted, see
+ *    ssm_selective_scan_bwd).
  *  - Alignment: every pointer must be aligned to its element size.  16-byte
  *    aligned pointers and L a multiple of 8 select the vectorised scan; other
  *    shapes run a slower path with the same results.
@@ -190,6 +191,57 @@ ssm_status ssm_selective_scan_fwd_conv(
     const float *Dskip, const void *z, const float *delta_bias, int delta_softplus,
     const float *initial_state, void *u_out, void *y, float *final_state,
     int64_t batch, int64_t L, int64_t D, int64_t N, ssm_dtype dt, void *stream, int tokens_per_lane);
+
+/*
+ * Selective scan, backward pass: the gradients of
+ *     loss = sum(dy * y) + sum(dfinal_state * final_state)
+ * for (y, final_state) = ssm_selective_scan_fwd_from_state(...) with the same
+ * inputs.  The forward states are recomputed from the inputs, not stored (the
+ * recomputation of the slide deck on Mamba's fused kernel and of the "Hardware-
+ * Aware Parallel Scan" sections of the dileepadev and vanos001 pages); the state
+ * gradient is the same recurrence run backwards in time,
+ *     lam_t = dy_t silu(z_t) C_t + exp(Delta_{t+1} A) lam_{t+1},
+ * scanned with the forward pass's associative operator (the slide deck's
+ * "Parallel scan" section).
+ *
+ * Inputs (as in ssm_selective_scan_fwd_from_state): u, delta, A, Bm, Cm, Dskip,
+ * z, delta_bias, delta_softplus, initial_state (NULL = zero), and
+ *   dy            : [batch][D][L] act, the gradient of y
+ *   dfinal_state  : [batch][D][N] float32, the gradient of the final state, or NULL (= 0)
+ * Outputs (each overwritten, never accumulated into):
+ *   du, ddelta    : [batch][D][L] act; ddelta is w.r.t. the raw delta (before bias and softplus)
+ *   dA            : [D][N] float32
+ *   dB, dC        : [batch][N][L] act (the library's B/C layout)
+ *   dD            : [D] float32 or NULL (not computed); the gradient at Dskip (0 if Dskip is NULL)
+ *   dz            : [batch][D][L] act or NULL; must be NULL when z is NULL
+ *   ddelta_bias   : [D] float32 or NULL; the gradient at delta_bias (0 if NULL)
+ *   dinitial_state: [batch][D][N] float32 or NULL; the gradient at the initial state
+ * Workspace: `workspace_bytes` >= ssm_selective_scan_bwd_workspace_size(...)
+ * bytes of device memory, 16-byte aligned, owned by the caller; its contents on
+ * entry do not matter and on return are unspecified.  Calls that share a
+ * workspace must not overlap in time.
+ *
+ * Determinism: dB and dC are sums over the D channels formed with floating-point
+ * atomic additions, so their last bits can differ between runs; every other
+ * output is bitwise reproducible.
+ * Errors: SSM_ERR_INVALID_ARG for a NULL required pointer (u, delta, A, Bm, Cm,
+ * dy, du, ddelta, dA, dB, dC, workspace where the size is nonzero), a negative
+ * size, misalignment, a too-small workspace, dz without z, or any output
+ * overlapping an input, another output or the workspace; SSM_ERR_UNSUPPORTED for
+ * N outside [1, 64] or a bad dtype; SSM_ERR_HIP when no device is usable or a
+ * launch fails.  With L == 0 the sums (dA, dD, ddelta_bias) are zero and
+ * dinitial_state = dfinal_state.
+ */
+size_t ssm_selective_scan_bwd_workspace_size(int64_t batch, int64_t L, int64_t D, int64_t N, ssm_dtype dt);
+
+ssm_status ssm_selective_scan_bwd(
+    const void *u, const void *delta, const float *A, const void *Bm, const void *Cm,
+    const float *Dskip, const void *z, const float *delta_bias, int delta_softplus,
+    const float *initial_state, const void *dy, const float *dfinal_state,
+    void *du, void *ddelta, float *dA, void *dB, void *dC, float *dD, void *dz,
+    float *ddelta_bias, float *dinitial_state,
+    int64_t batch, int64_t L, int64_t D, int64_t N, ssm_dtype dt,
+    void *workspace, size_t workspace_bytes, void *stream);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char *ssm_status_string(ssm_status s);

@@ -6,7 +6,9 @@ first call does, and raises if the library has not been built.
 """
 from ._lib import SsmError, load_library, LIB_PATH  # noqa: F401
 from ._lib import (SSM_SCAN_AUTO, SSM_SCAN_SEQUENTIAL, SSM_SCAN_CHUNKED)  # noqa: F401
-from .ops import selective_scan_fwd, selective_scan_fwd_conv, causal_conv1d, state_update  # noqa: F401
+from .ops import (selective_scan_fwd, selective_scan_fwd_conv, selective_scan_bwd,  # noqa: F401
+                  selective_scan_bwd_workspace_size, causal_conv1d, state_update)
 
-__all__ = ["selective_scan_fwd", "selective_scan_fwd_conv", "causal_conv1d", "state_update", "SsmError", "load_library", "LIB_PATH",
+__all__ = ["selective_scan_fwd", "selective_scan_fwd_conv", "selective_scan_bwd",
+           "selective_scan_bwd_workspace_size", "causal_conv1d", "state_update", "SsmError", "load_library", "LIB_PATH",
            "SSM_SCAN_AUTO", "SSM_SCAN_SEQUENTIAL", "SSM_SCAN_CHUNKED"]

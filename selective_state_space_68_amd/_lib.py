@@ -41,6 +41,10 @@ SIGNATURES = {
                                            _vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _vp, _int]),
     "ssm_state_update": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _vp,
                                 _i64, _i64, _i64, _int, _vp]),
+    "ssm_selective_scan_bwd_workspace_size": (ctypes.c_size_t, [_i64, _i64, _i64, _i64, _int]),
+    "ssm_selective_scan_bwd": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _vp, _vp, _vp,
+                                      _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                      _i64, _i64, _i64, _i64, _int, _vp, ctypes.c_size_t, _vp]),
     "ssm_status_string": (ctypes.c_char_p, [_int]),
     "ssm_version": (_int, []),
 }

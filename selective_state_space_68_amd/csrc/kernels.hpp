@@ -57,6 +57,32 @@ struct StepArgs {
   int softplus;
 };
 
+struct BwdArgs {
+  const void* u;          // [batch][D][L] act
+  const void* delta;      // [batch][D][L] act (raw)
+  const float* A;         // [D][N]
+  const void* Bm;         // [batch][N][L] act
+  const void* Cm;         // [batch][N][L] act
+  const float* Dskip;     // [D] or null
+  const void* z;          // [batch][D][L] act or null
+  const float* bias;      // [D] or null
+  const float* h0;        // [batch][D][N] or null
+  const void* dy;         // [batch][D][L] act: gradient of y
+  const float* dfinal;    // [batch][D][N] or null: gradient of the final state
+  void* du;               // [batch][D][L] act
+  void* ddelta;           // [batch][D][L] act (w.r.t. the raw delta)
+  float* dA;              // [D][N]
+  void* dB;               // [batch][N][L] act
+  void* dC;               // [batch][N][L] act
+  float* dD;              // [D] or null
+  void* dz;               // [batch][D][L] act or null (null whenever z is null)
+  float* dbias;           // [D] or null
+  float* dh0;             // [batch][D][N] or null
+  int64_t batch, L, D;
+  int N;
+  int softplus;
+};
+
 // One thread per (b, d) channel, sequential over time.  Any N in [1, 64].
 hipError_t launch_scan_sequential(const ScanArgs& a, Dt dt, hipStream_t s);
 
@@ -67,6 +93,11 @@ hipError_t launch_scan_chunked(const ScanArgs& a, Dt dt, int tokens_per_lane, hi
 
 // final_state = initial state, or zeros when src is null (the L == 0 scan).
 hipError_t launch_copy_state(float* dst, const float* src, int64_t n, hipStream_t s);
+
+// Backward pass (batch, L, D > 0): float32 workspace of scan_bwd_workspace_bytes.
+size_t scan_bwd_workspace_bytes(int64_t batch, int64_t L, int64_t D, int N);
+bool scan_bwd_grid_ok(int64_t batch, int64_t L, int64_t D, int N);
+hipError_t launch_scan_bwd(const BwdArgs& a, Dt dt, void* workspace, hipStream_t s);
 
 hipError_t launch_state_update(const StepArgs& a, Dt dt, hipStream_t s);
 

@@ -11,7 +11,7 @@
 
 namespace {
 
-constexpr int kVersion = 20200;  // 2.2.0: + causal conv1d, standalone and fused into the scan
+constexpr int kVersion = 20300;  // 2.3.0: + backward pass of the selective scan
 
 struct Span {
   uintptr_t lo = 0, hi = 0;  // [lo, hi); empty when lo == hi
@@ -230,6 +230,74 @@ ssm_status ssm_causal_conv1d_fwd(const void* x, const float* conv_w, const float
   a.batch = batch; a.D = D; a.L = L; a.K = static_cast<int>(conv_width); a.silu = apply_silu;
   return from_hip(ssm::launch_causal_conv1d(a, dt == SSM_BF16 ? ssm::Dt::BF16 : ssm::Dt::F32,
                                             static_cast<hipStream_t>(stream)));
+}
+
+size_t ssm_selective_scan_bwd_workspace_size(int64_t batch, int64_t L, int64_t D, int64_t N, ssm_dtype dt) {
+  if (dt != SSM_F32 && dt != SSM_BF16) return 0;
+  if (batch <= 0 || L <= 0 || D <= 0 || N < 1 || N > SSM_MAX_N) return 0;
+  uint64_t t;
+  if (!mul_ok(batch, D, &t) || !mul_ok(t, L, &t) || t > (uint64_t(1) << 58)) return 0;
+  return ssm::scan_bwd_workspace_bytes(batch, L, D, static_cast<int>(N));
+}
+
+ssm_status ssm_selective_scan_bwd(const void* u, const void* delta, const float* A, const void* Bm, const void* Cm,
+                                  const float* Dskip, const void* z, const float* delta_bias, int delta_softplus,
+                                  const float* initial_state, const void* dy, const float* dfinal_state, void* du,
+                                  void* ddelta, float* dA, void* dB, void* dC, float* dD, void* dz,
+                                  float* ddelta_bias, float* dinitial_state, int64_t batch, int64_t L, int64_t D,
+                                  int64_t N, ssm_dtype dt, void* workspace, size_t workspace_bytes, void* stream) {
+  ScanSizes sz;
+  // the forward checks cover the inputs (du stands in for y: required, act-sized)
+  ssm_status st = check_scan(u, delta, A, Bm, Cm, Dskip, z, delta_bias, delta_softplus, initial_state, du,
+                             nullptr, batch, L, D, N, dt, &sz);
+  if (st != SSM_OK) return st;
+  const uint64_t e = dt == SSM_BF16 ? 2 : 4;
+  if ((!dy && sz.act_bytes) || (!ddelta && sz.act_bytes) || (!dB && sz.bc_bytes) || (!dC && sz.bc_bytes) ||
+      (!dA && sz.a_bytes))
+    return SSM_ERR_INVALID_ARG;
+  if (dz && !z) return SSM_ERR_INVALID_ARG;  // no gate: there is no z to differentiate
+  if (!aligned(dy, e) || !aligned(ddelta, e) || !aligned(dB, e) || !aligned(dC, e) || !aligned(dz, e) ||
+      !aligned(dA, 4) || !aligned(dD, 4) || !aligned(ddelta_bias, 4) || !aligned(dinitial_state, 4) ||
+      !aligned(dfinal_state, 4) || !aligned(workspace, 16))
+    return SSM_ERR_INVALID_ARG;
+  const Span ins[] = {span(u, sz.act_bytes),         span(delta, sz.act_bytes),      span(z, sz.act_bytes),
+                      span(A, sz.a_bytes),           span(Bm, sz.bc_bytes),          span(Cm, sz.bc_bytes),
+                      span(Dskip, sz.vec_bytes),     span(delta_bias, sz.vec_bytes), span(initial_state, sz.state_bytes),
+                      span(dy, sz.act_bytes),        span(dfinal_state, sz.state_bytes)};
+  const size_t need = ssm_selective_scan_bwd_workspace_size(batch, L, D, N, dt);
+  const Span outs[] = {span(du, sz.act_bytes),          span(ddelta, sz.act_bytes),   span(dA, sz.a_bytes),
+                       span(dB, sz.bc_bytes),           span(dC, sz.bc_bytes),        span(dD, sz.vec_bytes),
+                       span(dz, sz.act_bytes),          span(ddelta_bias, sz.vec_bytes),
+                       span(dinitial_state, sz.state_bytes), span(workspace, need)};
+  for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i) {
+    for (const Span& s : ins)
+      if (overlaps(outs[i], s)) return SSM_ERR_INVALID_ARG;
+    for (size_t j = i + 1; j < sizeof(outs) / sizeof(outs[0]); ++j)
+      if (overlaps(outs[i], outs[j])) return SSM_ERR_INVALID_ARG;
+  }
+  if (workspace_bytes < need || (need && !workspace)) return SSM_ERR_INVALID_ARG;
+  if (!ssm::scan_bwd_grid_ok(batch, L, D, static_cast<int>(N))) return SSM_ERR_UNSUPPORTED;
+  if (D == 0) return SSM_OK;  // every output is empty
+  st = probe_device();
+  if (st != SSM_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (batch == 0 || L == 0) {
+    // sums over no tokens are zero; with no tokens the final state is the initial
+    // state, so its cotangent passes straight to the initial state
+    hipError_t he = ssm::launch_copy_state(dA, nullptr, D * N, s);
+    if (he == hipSuccess && dD) he = ssm::launch_copy_state(dD, nullptr, D, s);
+    if (he == hipSuccess && ddelta_bias) he = ssm::launch_copy_state(ddelta_bias, nullptr, D, s);
+    if (he == hipSuccess && dinitial_state)
+      he = ssm::launch_copy_state(dinitial_state, dfinal_state, batch * D * N, s);
+    return from_hip(he);
+  }
+  ssm::BwdArgs a;
+  a.u = u; a.delta = delta; a.A = A; a.Bm = Bm; a.Cm = Cm; a.Dskip = Dskip; a.z = z; a.bias = delta_bias;
+  a.h0 = initial_state; a.dy = dy; a.dfinal = dfinal_state;
+  a.du = du; a.ddelta = ddelta; a.dA = dA; a.dB = dB; a.dC = dC; a.dD = dD; a.dz = dz; a.dbias = ddelta_bias;
+  a.dh0 = dinitial_state;
+  a.batch = batch; a.L = L; a.D = D; a.N = static_cast<int>(N); a.softplus = delta_softplus;
+  return from_hip(ssm::launch_scan_bwd(a, dt == SSM_BF16 ? ssm::Dt::BF16 : ssm::Dt::F32, workspace, s));
 }
 
 ssm_status ssm_state_update(const float* state_in, float* state_out, const void* u_t, const void* delta_t,

@@ -86,6 +86,83 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta
     return y, final_state
 
 
+def selective_scan_bwd_workspace_size(batch, L, D, N, dtype=torch.float32) -> int:
+    """Bytes of device workspace selective_scan_bwd needs for this shape."""
+    lib = _lib.load_library()
+    dt = _lib.SSM_BF16 if dtype == torch.bfloat16 else _lib.SSM_F32
+    return int(lib.ssm_selective_scan_bwd_workspace_size(int(batch), int(L), int(D), int(N), dt))
+
+
+def selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, delta_softplus=True, *,
+                       initial_state=None, dfinal_state=None, want_dD=None, want_ddelta_bias=None,
+                       want_dinitial_state=None, workspace=None, stream=None) -> dict:
+    """Backward pass of selective_scan_fwd (same inputs) for the output gradient dy
+    [batch, D, L] and optionally the final-state gradient dfinal_state [batch, D, N].
+
+    Returns a dict with du, ddelta (w.r.t. the raw delta), dA, dB, dC and, where
+    computed, dD, dz, ddelta_bias and dinitial_state (None otherwise).  dD,
+    ddelta_bias and dinitial_state are computed when the matching input is given,
+    unless the want_* flag says otherwise; dz whenever z is given.  `workspace` is a
+    device tensor of at least selective_scan_bwd_workspace_size(...) bytes, or None
+    to allocate one.
+    """
+    lib = _lib.load_library()
+    if u.dim() != 3 or B.dim() != 3 or A.dim() != 2:
+        raise ValueError("expected u [batch, D, L], B/C [batch, N, L], A [D, N]")
+    batch, Dc, L = u.shape
+    N = A.shape[1]
+    act = u.dtype
+    dev = u.device
+    for name, v in (("delta", delta), ("dy", dy)):
+        if tuple(v.shape) != (batch, Dc, L):
+            raise ValueError(f"{name} must be [batch, D, L]")
+    if tuple(A.shape) != (Dc, N):
+        raise ValueError("A must be [D, N]")
+    if tuple(B.shape) != (batch, N, L) or tuple(C.shape) != (batch, N, L):
+        raise ValueError("B / C must be [batch, N, L]")
+    if z is not None and tuple(z.shape) != (batch, Dc, L):
+        raise ValueError("z must be [batch, D, L]")
+    for name, v in (("D", D), ("delta_bias", delta_bias)):
+        if v is not None and tuple(v.shape) != (Dc,):
+            raise ValueError(f"{name} must be [D]")
+    for name, v in (("initial_state", initial_state), ("dfinal_state", dfinal_state)):
+        if v is not None and tuple(v.shape) != (batch, Dc, N):
+            raise ValueError(f"{name} must be [batch, D, N]")
+    want_dD = D is not None if want_dD is None else want_dD
+    want_db = delta_bias is not None if want_ddelta_bias is None else want_ddelta_bias
+    want_dh0 = initial_state is not None if want_dinitial_state is None else want_dinitial_state
+    f32 = torch.float32
+    out = {
+        "du": torch.empty((batch, Dc, L), dtype=act, device=dev),
+        "ddelta": torch.empty((batch, Dc, L), dtype=act, device=dev),
+        "dA": torch.empty((Dc, N), dtype=f32, device=dev),
+        "dB": torch.empty((batch, N, L), dtype=act, device=dev),
+        "dC": torch.empty((batch, N, L), dtype=act, device=dev),
+        "dD": torch.empty((Dc,), dtype=f32, device=dev) if want_dD else None,
+        "dz": torch.empty((batch, Dc, L), dtype=act, device=dev) if z is not None else None,
+        "ddelta_bias": torch.empty((Dc,), dtype=f32, device=dev) if want_db else None,
+        "dinitial_state": torch.empty((batch, Dc, N), dtype=f32, device=dev) if want_dh0 else None,
+    }
+    need = int(lib.ssm_selective_scan_bwd_workspace_size(batch, L, Dc, N, _dt(u)))
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib.ssm_selective_scan_bwd(
+        _ptr(u, "u", act, dev), _ptr(delta, "delta", act, dev), _ptr(A, "A", f32, dev),
+        _ptr(B, "B", act, dev), _ptr(C, "C", act, dev), _ptr(D, "D", f32, dev),
+        _ptr(z, "z", act, dev), _ptr(delta_bias, "delta_bias", f32, dev), 1 if delta_softplus else 0,
+        _ptr(initial_state, "initial_state", f32, dev), _ptr(dy, "dy", act, dev),
+        _ptr(dfinal_state, "dfinal_state", f32, dev),
+        _ptr(out["du"], "du"), _ptr(out["ddelta"], "ddelta"), _ptr(out["dA"], "dA"), _ptr(out["dB"], "dB"),
+        _ptr(out["dC"], "dC"), _ptr(out["dD"], "dD"), _ptr(out["dz"], "dz"),
+        _ptr(out["ddelta_bias"], "ddelta_bias"), _ptr(out["dinitial_state"], "dinitial_state"),
+        batch, L, Dc, N, _dt(u), workspace.data_ptr(), ws_bytes, _stream(stream))
+    _lib.check(st)
+    return out
+
+
 def causal_conv1d(x, weight, bias=None, silu=True, *, out=None, stream=None) -> torch.Tensor:
     """Causal depthwise conv1d along L (+ SiLU).  x [batch, D, L]; weight [D, K] float32
     (K <= 4, weight[:, K-1] weighs the current token); bias [D] or None."""

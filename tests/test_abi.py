@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.ssm_version() == 20200
+    assert lib.ssm_version() == 20300
     for s in range(4):
         assert lib.ssm_status_string(s).decode().startswith(("SSM_OK", "SSM_ERR"))
     assert b"unknown" in lib.ssm_status_string(99)
@@ -162,6 +162,67 @@ def test_scan_conv_argument_errors(lib, kw, status):
     assert _scan_conv(lib, **kw) == status
 
 
+def _bwd(lib, **kw):
+    slots = ["u", "delta", "A", "B", "C", "Dskip", "z", "bias", "h0", "dy", "dfinal",
+             "du", "ddelta", "dA", "dB", "dC", "dD", "dz", "dbias", "dh0", "ws"]
+    a = {k: F + i * 64 * MB for i, k in enumerate(slots)}
+    a.update(Dskip=None, z=None, bias=None, h0=None, dfinal=None, dD=None, dz=None, dbias=None, dh0=None,
+             softplus=1, batch=1, L=64, D=16, N=4, dt=0, ws_bytes=None)
+    a.update(kw)
+    if a["ws_bytes"] is None:
+        a["ws_bytes"] = lib.ssm_selective_scan_bwd_workspace_size(a["batch"], a["L"], a["D"], a["N"], a["dt"])
+    return lib.ssm_selective_scan_bwd(a["u"], a["delta"], a["A"], a["B"], a["C"], a["Dskip"], a["z"], a["bias"],
+                                      a["softplus"], a["h0"], a["dy"], a["dfinal"], a["du"], a["ddelta"], a["dA"],
+                                      a["dB"], a["dC"], a["dD"], a["dz"], a["dbias"], a["dh0"], a["batch"], a["L"],
+                                      a["D"], a["N"], a["dt"], a["ws"], a["ws_bytes"], None)
+
+
+def test_bwd_workspace_size(lib):
+    ws = lib.ssm_selective_scan_bwd_workspace_size
+    assert ws(0, 64, 16, 4, 0) == 0 and ws(1, 0, 16, 4, 0) == 0 and ws(1, 64, 0, 4, 0) == 0
+    assert ws(1, 64, 16, 0, 0) == 0 and ws(1, 64, 16, 65, 0) == 0 and ws(1, 64, 16, 4, 5) == 0
+    # chunk states (3 x batch*chunks*D*N), float32 dB/dC (batch*2*N*L) and two
+    # per-chunk channel partials, each rounded up to 64 floats
+    r64 = lambda n: (n + 63) // 64 * 64
+    for batch, L, D, N in ((2, 2048, 1536, 16), (1, 1000, 7, 5), (3, 100, 40, 20)):
+        ch = 512 if N <= 16 else 256
+        nc = -(-L // ch)
+        floats = 3 * r64(batch * nc * D * N) + r64(batch * 2 * N * L) + 2 * r64(batch * nc * D)
+        assert ws(batch, L, D, N, 0) == 4 * floats == ws(batch, L, D, N, 1)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(u=None), _lib.SSM_ERR_INVALID_ARG),
+    (dict(dy=None), _lib.SSM_ERR_INVALID_ARG),
+    (dict(du=None), _lib.SSM_ERR_INVALID_ARG),
+    (dict(ddelta=None), _lib.SSM_ERR_INVALID_ARG),
+    (dict(dA=None), _lib.SSM_ERR_INVALID_ARG),
+    (dict(dB=None), _lib.SSM_ERR_INVALID_ARG),
+    (dict(dC=None), _lib.SSM_ERR_INVALID_ARG),
+    (dict(ws=None), _lib.SSM_ERR_INVALID_ARG),
+    (dict(ws_bytes=64), _lib.SSM_ERR_INVALID_ARG),                 # workspace too small
+    (dict(ws=F + 21 * 64 * MB + 8), _lib.SSM_ERR_INVALID_ARG),      # workspace not 16-byte aligned
+    (dict(dz=F + 30 * 64 * MB), _lib.SSM_ERR_INVALID_ARG),          # dz without z
+    (dict(du=F), _lib.SSM_ERR_INVALID_ARG),                         # output aliases u
+    (dict(dB=F + 11 * 64 * MB), _lib.SSM_ERR_INVALID_ARG),          # output aliases another output
+    (dict(ws=F + 9 * 64 * MB), _lib.SSM_ERR_INVALID_ARG),           # workspace aliases dy
+    (dict(dh0=F + 8 * 64 * MB, h0=F + 8 * 64 * MB), _lib.SSM_ERR_INVALID_ARG),  # dh0 aliases h0
+    (dict(dA=F + 13 * 64 * MB + 2), _lib.SSM_ERR_INVALID_ARG),      # misaligned float32 output
+    (dict(dt=1, dB=F + 14 * 64 * MB + 1), _lib.SSM_ERR_INVALID_ARG),  # misaligned bf16 output
+    (dict(N=0), _lib.SSM_ERR_UNSUPPORTED),
+    (dict(N=65), _lib.SSM_ERR_UNSUPPORTED),
+    (dict(dt=3), _lib.SSM_ERR_UNSUPPORTED),
+    (dict(softplus=5), _lib.SSM_ERR_INVALID_ARG),
+    (dict(L=-1), _lib.SSM_ERR_INVALID_ARG),
+])
+def test_bwd_argument_errors(lib, kw, status):
+    assert _bwd(lib, **kw) == status
+
+
+def test_bwd_empty_channels_is_noop(lib):
+    assert _bwd(lib, D=0, u=None, delta=None, dy=None, du=None, ddelta=None, dA=None, ws=None) == _lib.SSM_OK
+
+
 def test_state_update_empty_is_noop(lib):
     assert _step(lib, batch=0) == _lib.SSM_OK
 
@@ -185,6 +246,10 @@ def test_valid_call_without_device_reports_hip_error(lib):
     assert _scan_conv(lib) == _lib.SSM_ERR_HIP
     assert _scan_conv(lib, u_out=F + 8 * 64 * MB, cb=F + 9 * 64 * MB) == _lib.SSM_ERR_HIP
     assert _step(lib, sout=F) == _lib.SSM_ERR_HIP          # exact in-place is valid
+    assert _bwd(lib) == _lib.SSM_ERR_HIP
+    assert _bwd(lib, z=F + 6 * 64 * MB, dz=F + 17 * 64 * MB, h0=F + 8 * 64 * MB, dh0=F + 19 * 64 * MB,
+                dfinal=F + 10 * 64 * MB, Dskip=F + 5 * 64 * MB, dD=F + 16 * 64 * MB) == _lib.SSM_ERR_HIP
+    assert _bwd(lib, L=0) == _lib.SSM_ERR_HIP               # sums over no tokens still write zeros
     with pytest.raises(_lib.SsmError) as ei:
         _lib.check(_lib.SSM_ERR_HIP)
     assert ei.value.status == _lib.SSM_ERR_HIP

@@ -1,0 +1,158 @@
+"""GPU parity of the backward pass (ssm_selective_scan_bwd) against the float64
+oracle's adjoint recurrence (oracle.selective_scan_bwd, itself pinned to finite
+differences of the forward pass).
+
+Every gradient is compared with the row-wise metric of the forward tests: rows
+are a channel's time series (du, ddelta, dz), a state's time series in one batch
+row (dB, dC), a channel's N entries (dA, dinitial_state) and the whole vector
+(dD, ddelta_bias).  Tolerances are the forward pass's: 1e-4 for float32
+activations, 2e-2 for bfloat16 (whose outputs are rounded to bfloat16).  Shapes
+cover several chunks with a ragged tail, the non-vector path, one token, every
+state-count tier (N <= 16, N <= 32 and N <= 64 hold different kernels), missing
+optional inputs, a given initial state and final-state gradient, and more
+channels than one workgroup covers.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import TOL, dev, host
+from ssm_metrics import row_rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from selective_state_space_68_amd import load_library
+    load_library()
+
+
+def _case(batch, L, D, N, dtype="f32", gate=True, d_skip="ones", bias=True, softplus=True, h0=False,
+          dfinal=False, seed=0, a_kind="s4d"):
+    inp = synth.make_scan_inputs(batch, L, D, N, dtype, gate=gate, d_skip=d_skip, seed=seed, a_kind=a_kind,
+                                 with_bias=bias, delta_softplus=softplus)
+    if not softplus:
+        # without the softplus the step must still be positive, or exp(Delta*A) > 1 and
+        # the state grows without bound in any precision
+        inp.delta = np.abs(inp.delta)
+        inp.delta_bias = None
+        inp.refresh()
+    dyv, dyup, dfin = synth.make_scan_cotangents(batch, L, D, N, dtype, seed=seed, with_dfinal=dfinal)
+    hz = synth.make_scan_initial_state(batch, D, N, seed=seed) if h0 else None
+    return inp, dyv, dyup, hz, dfin
+
+
+def _run_gpu(inp, dyup, hz, dfin, want_dh0=None):
+    import torch
+    from selective_state_space_68_amd import selective_scan_bwd
+    t = {k: dev(inp.upload_array(k)) for k in ("u", "delta", "B", "C", "z")}
+    g = selective_scan_bwd(t["u"], t["delta"], dev(inp.A), t["B"], t["C"], dev(dyup), dev(inp.Dskip), t["z"],
+                           dev(inp.delta_bias), inp.delta_softplus, initial_state=dev(hz),
+                           dfinal_state=dev(dfin), want_dinitial_state=want_dh0)
+    torch.cuda.synchronize()
+    return {k: host(v) for k, v in g.items()}
+
+
+def _run_oracle(inp, dyv, hz, dfin):
+    return oracle.selective_scan_bwd(inp.u, inp.delta, inp.A, inp.B, inp.C, dyv, inp.Dskip, inp.z,
+                                     inp.delta_bias, inp.delta_softplus, hz, dfin)
+
+
+def _compare(got, ref, dtype, what, dh0_ref=None):
+    tol = TOL[dtype]
+    errs = {
+        "du": row_rel_err(got["du"], ref["du"]),
+        "ddelta": row_rel_err(got["ddelta"], ref["ddelta"]),
+        "dA": row_rel_err(got["dA"], ref["dA"]),
+        # the library's dB/dC are [batch][N][L]; the oracle's [batch][L][N]
+        "dB": row_rel_err(got["dB"], ref["dB"].transpose(0, 2, 1)),
+        "dC": row_rel_err(got["dC"], ref["dC"].transpose(0, 2, 1)),
+    }
+    if ref["dz"] is not None:
+        errs["dz"] = row_rel_err(got["dz"], ref["dz"])
+    else:
+        assert got["dz"] is None
+    if ref["dD"] is not None:
+        errs["dD"] = row_rel_err(got["dD"], ref["dD"])
+    if ref["ddelta_bias"] is not None:
+        errs["ddelta_bias"] = row_rel_err(got["ddelta_bias"], ref["ddelta_bias"])
+    dh0 = ref["dh0"] if dh0_ref is None else dh0_ref
+    if dh0 is not None:
+        errs["dh0"] = row_rel_err(got["dinitial_state"], dh0)
+    print(what, " ".join(f"{k}={v:.2e}" for k, v in errs.items()), f"tol={tol:.0e}", flush=True)
+    bad = {k: v for k, v in errs.items() if not v <= tol}
+    assert not bad, (what, bad)
+
+
+CASES = [
+    # batch, L, D, N, kwargs
+    (1, 64, 16, 4, dict()),
+    (2, 1100, 13, 16, dict()),                                   # 3 chunks, ragged tail, vector path off (L % 8)
+    (2, 1536, 24, 16, dict(h0=True, dfinal=True)),
+    (1, 1, 3, 16, dict()),                                       # one token
+    (1, 513, 9, 16, dict(gate=False, bias=False, d_skip="none")),
+    (1, 700, 5, 16, dict(softplus=False, a_kind="lognormal")),
+    (2, 600, 6, 5, dict(h0=True)),                               # N not a multiple of 4
+    (1, 520, 7, 24, dict(dfinal=True)),                          # 17..32 states: 4 tokens per lane
+    (1, 300, 4, 40, dict(h0=True)),                              # 33..64 states: global accumulation
+    (1, 256, 3, 64, dict()),
+    (2, 2048, 200, 16, dict()),                                  # several channel slices and rounds
+]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("batch,L,D,N,kw", CASES)
+def test_bwd_matches_oracle(batch, L, D, N, kw, dtype):
+    inp, dyv, dyup, hz, dfin = _case(batch, L, D, N, dtype, **kw)
+    got = _run_gpu(inp, dyup, hz, dfin)
+    ref = _run_oracle(inp, dyv, hz, dfin)
+    _compare(got, ref, dtype, f"bwd {dtype} b={batch} L={L} D={D} N={N} {kw}")
+
+
+def test_bwd_dinitial_state_without_initial_state():
+    # the gradient at a zero initial state is the same adjoint; the oracle reports
+    # it when given an explicit zero state
+    inp, dyv, dyup, _, dfin = _case(1, 700, 6, 16, "f32", dfinal=True)
+    got = _run_gpu(inp, dyup, None, dfin, want_dh0=True)
+    ref = _run_oracle(inp, dyv, np.zeros((1, 6, 16)), dfin)
+    _compare(got, ref, "f32", "bwd dh0 at zero state")
+
+
+def test_bwd_zero_length():
+    import torch
+    from selective_state_space_68_amd import selective_scan_bwd
+    inp, _, _, hz, dfin = _case(2, 8, 4, 16, "f32", h0=True, dfinal=True)
+    e = torch.empty((2, 4, 0), device="cuda")
+    B0 = torch.empty((2, 16, 0), device="cuda")
+    g = selective_scan_bwd(e, e, dev(inp.A), B0, B0, e, dev(inp.Dskip), None, dev(inp.delta_bias), True,
+                           initial_state=dev(hz), dfinal_state=dev(dfin))
+    torch.cuda.synchronize()
+    assert np.all(host(g["dA"]) == 0) and np.all(host(g["dD"]) == 0) and np.all(host(g["ddelta_bias"]) == 0)
+    assert np.array_equal(host(g["dinitial_state"]), dfin.astype(np.float64))
+
+
+def test_bwd_repeatable_and_workspace_reuse():
+    # everything but dB/dC is bitwise reproducible; a dirty, reused workspace
+    # changes nothing
+    import torch
+    from selective_state_space_68_amd import selective_scan_bwd, selective_scan_bwd_workspace_size
+    inp, dyv, dyup, hz, dfin = _case(2, 1024, 40, 16, "bf16", h0=True, dfinal=True)
+    t = {k: dev(inp.upload_array(k)) for k in ("u", "delta", "B", "C", "z")}
+    n = selective_scan_bwd_workspace_size(2, 1024, 40, 16, torch.bfloat16)
+    ws = torch.full((n,), 0x7f, dtype=torch.uint8, device="cuda")
+    outs = []
+    for _ in range(2):
+        g = selective_scan_bwd(t["u"], t["delta"], dev(inp.A), t["B"], t["C"], dev(dyup), dev(inp.Dskip), t["z"],
+                               dev(inp.delta_bias), True, initial_state=dev(hz), dfinal_state=dev(dfin),
+                               workspace=ws)
+        torch.cuda.synchronize()
+        outs.append({k: host(v) for k, v in g.items()})
+    for k in ("du", "ddelta", "dz", "dA", "dD", "ddelta_bias", "dinitial_state"):
+        assert np.array_equal(outs[0][k], outs[1][k]), k
+    ref = _run_oracle(inp, dyv, hz, dfin)
+    _compare(outs[1], ref, "bf16", "bwd reused workspace")
