@@ -37,12 +37,20 @@ import synth  # noqa: E402
 PEAK_HBM_GBS = 8000.0
 PEAK_VALU_TSLOTS = 256 * 4 * 16 * 2.4e9 / 1e12    # 39.32 T single-issue fp32 lane slots/s
 ALU_SLOTS_PER_ELEMENT = 6                           # 4 fp32 ops + one exp2 at half rate
+# Backward, per element (b, t, d, n): the forward recomputation (exp2 at half rate = 2,
+# Delta*u*B, the state FMA, the readout FMA for the pre-gate output: 5 slots) and the
+# adjoint (lam = g*C + abar*lam': 2; sum_n lam*B: 1; dB term lam*Delta*u and its sum
+# over d: 2; dC term g*h and its sum: 2; abar*lam*h_{t-1}: 2, times A into dDelta: 1,
+# times Delta into dA: 1; 11 slots).
+BWD_ALU_SLOTS_PER_ELEMENT = 16
 MALL_BYTES = 256 << 20
 CALIB_BYTES = 256 << 20
 DEFAULT_WORKLOAD = "mamba130m_f32"
 KERNEL_SRC = {"scan": "selective_state_space_68_amd/csrc/scan_chunked.hip",
-              "decode": "selective_state_space_68_amd/csrc/state_update.hip"}
-KERNEL_NAME = {"scan": "scan_chunked_kernel", "decode": "state_update_vec_kernel"}
+              "decode": "selective_state_space_68_amd/csrc/state_update.hip",
+              "bwd": "selective_state_space_68_amd/csrc/scan_bwd.hip"}
+KERNEL_NAME = {"scan": "scan_chunked_kernel", "decode": "state_update_vec_kernel",
+               "bwd": "scan backward call (bwd_summary, bwd_combine, bwd_main, bwd_param_sums, bwd_bc_out kernels)"}
 
 
 def src_hash(kind):
@@ -74,12 +82,16 @@ def dev(torch, a):
 
 
 def _oracle_shard(args):
-    """Worker: the oracle on one (batch row, channel block) shard; returns seconds."""
+    """Worker: the oracle (forward, or backward when an output gradient is given) on one
+    (batch row, channel block) shard; returns seconds."""
     os.environ.setdefault("OMP_NUM_THREADS", "1")
     import oracle
-    (u, delta, A, B, C, Dk, z, bias, sp) = args
+    (u, delta, A, B, C, Dk, z, bias, sp, dy) = args
     t0 = time.perf_counter()
-    oracle.selective_scan(u, delta, A, B, C, Dk, z, bias, sp)
+    if dy is None:
+        oracle.selective_scan(u, delta, A, B, C, Dk, z, bias, sp)
+    else:
+        oracle.selective_scan_bwd(u, delta, A, B, C, dy, Dk, z, bias, sp)
     return time.perf_counter() - t0
 
 
@@ -88,13 +100,14 @@ def _oracle_warm(_):
     return 0
 
 
-def cpu_baseline_scan(cfg, inp, budget_s=20.0, workers=0):
+def cpu_baseline_scan(cfg, inp, budget_s=20.0, workers=0, dy=None):
     """The float64 oracle, as it is, timed on this host's cores: the workload is split
     into (batch row, channel block) shards run by a pool of worker processes, on as
-    many whole batch rows as fit in about budget_s of CPU time."""
+    many whole batch rows as fit in about budget_s of CPU time.  With `dy` the oracle's
+    backward pass is timed (each shard's dB and dC are its channels' partial sums;
+    adding the partials is not timed)."""
     import concurrent.futures as cf
     import multiprocessing as mp
-    import oracle
     ncpu = len(os.sched_getaffinity(0))
     workers = workers or max(1, min(16, ncpu))
     # size the sample from a single-process probe on one channel block
@@ -102,9 +115,9 @@ def cpu_baseline_scan(cfg, inp, budget_s=20.0, workers=0):
     sl = lambda x, b0, b1, d0, d1: None if x is None else x[b0:b1, d0:d1]
     vec = lambda x, d0, d1: None if x is None else x[d0:d1]
     t0 = time.perf_counter()
-    oracle.selective_scan(inp.u[:1, :d_probe], inp.delta[:1, :d_probe], inp.A[:d_probe], inp.B[:1], inp.C[:1],
-                          vec(inp.Dskip, 0, d_probe), sl(inp.z, 0, 1, 0, d_probe),
-                          vec(inp.delta_bias, 0, d_probe), inp.delta_softplus)
+    _oracle_shard((inp.u[:1, :d_probe], inp.delta[:1, :d_probe], inp.A[:d_probe], inp.B[:1], inp.C[:1],
+                   vec(inp.Dskip, 0, d_probe), sl(inp.z, 0, 1, 0, d_probe),
+                   vec(inp.delta_bias, 0, d_probe), inp.delta_softplus, sl(dy, 0, 1, 0, d_probe)))
     per_row_cpu = (time.perf_counter() - t0) * cfg.D / d_probe
     b_take = max(1, min(cfg.batch, int(budget_s / max(per_row_cpu, 1e-3))))
     dblk = max(1, -(-cfg.D // max(1, (workers + b_take - 1) // b_take)))
@@ -114,7 +127,7 @@ def cpu_baseline_scan(cfg, inp, budget_s=20.0, workers=0):
             d1 = min(cfg.D, d0 + dblk)
             shards.append((sl(inp.u, b, b + 1, d0, d1), sl(inp.delta, b, b + 1, d0, d1), inp.A[d0:d1],
                            inp.B[b:b + 1], inp.C[b:b + 1], vec(inp.Dskip, d0, d1), sl(inp.z, b, b + 1, d0, d1),
-                           vec(inp.delta_bias, d0, d1), inp.delta_softplus))
+                           vec(inp.delta_bias, d0, d1), inp.delta_softplus, sl(dy, b, b + 1, d0, d1)))
     with cf.ProcessPoolExecutor(max_workers=workers, mp_context=mp.get_context("spawn")) as ex:
         list(ex.map(_oracle_warm, range(workers)))   # start the workers and import the oracle
         t0 = time.perf_counter()
@@ -126,7 +139,7 @@ def cpu_baseline_scan(cfg, inp, budget_s=20.0, workers=0):
         wall = time.perf_counter() - t0
     elems = b_take * cfg.L * cfg.D * cfg.N
     return {"value": reps * elems / wall, "unit": "elements/s", "cores": workers, "kind": "oracle",
-            "sample": f"{b_take} of {cfg.batch} batch rows x all {cfg.D} channels x full L={cfg.L}, N={cfg.N} "
+            "sample": f"{'backward, ' if dy is not None else ''}{b_take} of {cfg.batch} batch rows x all {cfg.D} channels x full L={cfg.L}, N={cfg.N} "
                       f"({elems:.3e} elements), {reps}x, in {len(shards)} shards per pass over {workers} "
                       f"worker processes "
                       f"(float64 numpy, 1 thread each; {wall:.1f} s wall, {sum(secs):.1f} s CPU); "
@@ -146,6 +159,28 @@ def bench_scan(args, torch, lib_ops):
         t["y"] = torch.empty_like(t["u"])
         t["fs"] = torch.empty((cfg.batch, cfg.D, cfg.N), dtype=torch.float32, device="cuda")
         bufs.append(t)
+
+    if cfg.backward:
+        # gradients of the scan for an output gradient dy; outputs and workspace are
+        # allocated once, outside the timed graph
+        dyv, dyup, _ = synth.make_scan_cotangents(cfg.batch, cfg.L, cfg.D, cfg.N, cfg.dtype, seed=cfg.seed)
+        inp.dy = dyv
+        act = bufs[0]["u"].dtype
+        ws = torch.empty((lib_ops.selective_scan_bwd_workspace_size(cfg.batch, cfg.L, cfg.D, cfg.N, act),),
+                         dtype=torch.uint8, device="cuda")
+        grads = None
+        for t in bufs:
+            t["dy"] = dev(torch, dyup)
+            del t["y"], t["fs"]
+        dyv = dyup = None
+
+        def step(i):
+            nonlocal grads
+            t = bufs[i % sets]
+            grads = lib_ops.selective_scan_bwd(t["u"], t["delta"], A, t["B"], t["C"], t["dy"], Dk, t["z"], bias,
+                                               True, workspace=ws, out=grads)
+            t["g"] = grads
+        return cfg, inp, nbytes, cfg.elements, sets, step, bufs
 
     if cfg.conv_k:
         cw, cb = (dev(torch, x) for x in synth.make_conv_params(cfg.D, cfg.conv_k, seed=cfg.seed))
@@ -214,6 +249,8 @@ def main():
     torch.cuda.set_device(0)
     kind = "decode" if args.workload.startswith("decode") else "scan"
     maker = bench_decode if kind == "decode" else bench_scan
+    if kind == "scan" and synth.CONFIGS[args.workload].backward:
+        kind = "bwd"
     cfg, inp, nbytes, elements, sets, step, bufs = maker(args, torch, lib_ops)
     print(f"# workload {args.workload}: {elements:.3e} elements/step, {nbytes / 1e6:.2f} MB/step "
           f"algorithmic, {sets} input copies", file=sys.stderr, flush=True)
@@ -250,16 +287,20 @@ def main():
             step(warm)
             warm += 1
     torch.cuda.synchronize()
-    if graph is not None and kind == "scan":
-        # the replayed outputs must equal an eager call's, bit for bit
+    if graph is not None and kind in ("scan", "bwd"):
+        # the replayed outputs must equal an eager call's, bit for bit (for the backward,
+        # the outputs that are formed in a fixed order)
         if warm == 0:
             graph.replay()
             torch.cuda.synchronize()
-        ref = {k: bufs[(K - 1) % sets][k].clone() for k in ("y", "fs")}
+        if kind == "scan":
+            get = lambda: {k: bufs[(K - 1) % sets][k] for k in ("y", "fs")}
+        else:
+            get = lambda: {k: bufs[(K - 1) % sets]["g"][k] for k in ("du", "ddelta", "dz", "dA", "dD")}
+        ref = {k: v.clone() for k, v in get().items()}
         step(K - 1)
         torch.cuda.synchronize()
-        assert torch.equal(ref["y"], bufs[(K - 1) % sets]["y"]) and \
-            torch.equal(ref["fs"], bufs[(K - 1) % sets]["fs"]), "graph replay differs from eager"
+        assert all(torch.equal(ref[k], v) for k, v in get().items()), "graph replay differs from eager"
         if warm:                  # back to the sustained state before timing
             graph.replay()
             torch.cuda.synchronize()
@@ -284,29 +325,32 @@ def main():
     hbm_gbs = nbytes / launch_s / 1e9
 
     cpu = None
-    if kind == "scan" and not args.no_cpu_baseline and not cfg.conv_k:
-        cpu = cpu_baseline_scan(cfg, inp, args.cpu_budget)
+    if kind in ("scan", "bwd") and not args.no_cpu_baseline and not cfg.conv_k:
+        cpu = cpu_baseline_scan(cfg, inp, args.cpu_budget, dy=getattr(inp, "dy", None))
 
     traffic = traffic_from_profiles(args.workload, kind)
     hbm = {"achieved": hbm_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": hbm_gbs / PEAK_HBM_GBS,
            "algorithmic_bytes_per_launch": nbytes}
-    if kind == "scan":
+    if kind in ("scan", "bwd"):
         # Bound by the vector ALUs: per element 4 fp32 VALU ops plus one exp2, which
         # issues at half the VALU rate (2 slots), against 256 CUs x 4 SIMDs x 16 lanes
-        # x 2.4 GHz single-issue fp32 slots.
-        slots = ALU_SLOTS_PER_ELEMENT * elements
+        # x 2.4 GHz single-issue fp32 slots (the backward: BWD_ALU_SLOTS_PER_ELEMENT,
+        # over the whole call of its five kernels).
+        spe = BWD_ALU_SLOTS_PER_ELEMENT if kind == "bwd" else ALU_SLOTS_PER_ELEMENT
+        slots = spe * elements
         alu = slots / launch_s / 1e12
         roofline = {"bound": "alu", "kernel": KERNEL_NAME[kind],
                     "achieved": alu, "peak": PEAK_VALU_TSLOTS, "unit": "T VALU slots/s",
                     "frac": alu / PEAK_VALU_TSLOTS, "traffic": traffic,
-                    "algorithmic_slots_per_launch": slots, "slots_per_element": ALU_SLOTS_PER_ELEMENT,
+                    "algorithmic_slots_per_launch": slots, "slots_per_element": spe,
                     "avg_launch_us": launch_s * 1e6}
     else:
         roofline = dict(hbm, bound="hbm", kernel=KERNEL_NAME[kind], traffic=traffic,
                         avg_launch_us=launch_s * 1e6)
     out = {
-        "metric": "selective-scan elements/s (B*L*D*N) + achieved HBM GB/s vs peak, 1 GPU"
-        if kind == "scan" else "decode-step elements/s (S*D*N per step) + achieved HBM GB/s vs peak, 1 GPU",
+        "metric": {"scan": "selective-scan elements/s (B*L*D*N) + achieved HBM GB/s vs peak, 1 GPU",
+                   "bwd": "selective-scan backward elements/s (B*L*D*N) + achieved HBM GB/s vs peak, 1 GPU",
+                   "decode": "decode-step elements/s (S*D*N per step) + achieved HBM GB/s vs peak, 1 GPU"}[kind],
         "value": value,
         "unit": "elements/s",
         "n_gpus": 1,
@@ -321,7 +365,7 @@ def main():
         "config": ({"workload": args.workload, "batch": cfg.batch, "L": cfg.L, "D": cfg.D, "N": cfg.N,
                     "act_dtype": cfg.dtype, "gate": cfg.gate, "conv_width": cfg.conv_k, "variant": args.variant,
                     "tokens_per_lane": args.kpl or "auto", "graph": graph is not None, "input_copies": sets}
-                   if kind == "scan" else
+                   if kind != "decode" else
                    {"workload": args.workload, "sequences": cfg.batch, "D": cfg.D, "N": cfg.N,
                     "act_dtype": cfg.dtype, "graph": graph is not None, "input_copies": sets}),
         "roofline": roofline,

@@ -33,15 +33,18 @@
 //   4. finalize: fixed-order sums of the per-(b, chunk) partials of dA, dD and the
 //      delta bias; dB and dC from float32 to the activation dtype.
 //
-// A workgroup of kBW waves owns one (batch row, chunk) pair and a slice of
-// kBW * rounds channels: it stages the chunk's B and C once in LDS (float32,
+// A workgroup of kW waves owns one (batch row, chunk) pair and a slice of
+// kW * rounds channels: it stages the chunk's B and C once in LDS (float32,
 // permuted so that each lane's tokens are contiguous), and each wave runs one
-// channel per round.  dB and dC are sums over channels: the waves add their
-// terms into a float32 LDS accumulator with LDS atomics, and the workgroup adds
-// the accumulator to a float32 copy in memory with one global atomic per element
-// at its end, so the reduction over D happens on chip.  The LDS and global
-// atomics make dB and dC the only outputs whose last bits depend on the order of
-// the additions; every other output is a fixed-order computation.
+// channel per round.  dB and dC are sums over channels.  The main kernel's waves
+// step through the states in pairs together: each wave writes its channel's dB
+// and dC terms for the pair to its own LDS slot, and after a barrier every thread
+// adds the kW slots' values of the entries it owns, in wave order, into its
+// registers (N = 16) or into the workgroup's region of the workspace (other N).
+// Each workgroup writes its slice's partial sums once; the finalize kernel adds
+// the slices in slice order.  Every output is formed in a fixed order, so the
+// results are bitwise reproducible.  (LDS float atomics, the obvious alternative,
+// measured 7x slower on gfx950 than this whole kernel.)
 #include <utility>
 
 #include "device_common.hpp"
@@ -51,55 +54,54 @@
 namespace ssm {
 namespace {
 
-constexpr int kBW = 8;                // waves per workgroup (channels per round)
-
 struct BwdLayout {
-  int64_t nchunks;                    // chunks of 64 * KPL tokens
-  int64_t nslices;                    // channel slices of kBW * rounds
-  int rounds;
-  int kpl;
+  int kpl;                            // tokens per lane: chunks of 64 * kpl tokens
+  int waves;                          // waves per workgroup
+  int rounds;                         // channels per wave
+  int64_t nchunks;
+  int64_t nslices;                    // channel slices of waves * rounds
   float* F;                           // [batch][nchunks][D][N]: F, then the entering state
   float* X;                           // [batch][nchunks][D][N]: X, then the entering adjoint
   float* P;                           // [batch][nchunks][D][N]: chunk decay, then dA partials
-  float* dBC;                         // [batch][2][N][L] float32 dB (0) and dC (1)
+  float* part;                        // [nslices][batch][2][N][L] per-slice dB (0) and dC (1) sums
   float* dDp;                         // [batch][nchunks][D] dD partials
   float* dbp;                         // [batch][nchunks][D] delta-bias partials
 };
 
-// KPL tokens per lane for a state count: the main kernel holds a chunk's B and C
-// and the dB/dC accumulator for all N states in LDS, 2 * N * 64 * KPL floats each.
-int bwd_kpl(int N) { return N <= 16 ? 8 : 4; }
-// States a main-kernel instantiation holds in LDS (LDSACC) or in the tile alone.
-template <int KPL, bool LDSACC>
-struct BwdCap {
-  static constexpr int CH = 64 * KPL;
-  static constexpr int NMAX = (LDSACC ? 16384 : 32768) / (2 * CH);
-};
+// Up to 16 states (the models' state size is 16): 8 tokens per lane and 8 waves
+// per workgroup.  More states: 4 tokens per lane and 4 waves, so that a chunk's B
+// and C for up to 64 states (2 * 64 * 256 floats, 128 KB) and the waves' slots
+// still fit in LDS.
+constexpr int kWFast = 8, kWGen = 4;
+constexpr int kNMaxFast = 16, kNMaxGen = 64;
+bool bwd_fast(int N) { return N <= kNMaxFast; }
 
 int64_t align64(int64_t n) { return (n + 63) / 64 * 64; }
 
 BwdLayout bwd_layout(int64_t batch, int64_t L, int64_t D, int N, float* ws) {
   BwdLayout g{};
-  g.kpl = bwd_kpl(N);
-  const int64_t CH = 64 * g.kpl;
+  g.kpl = bwd_fast(N) ? 8 : 4;
+  g.waves = bwd_fast(N) ? kWFast : kWGen;
+  const int64_t CH = 64 * g.kpl, W = g.waves;
   g.nchunks = (L + CH - 1) / CH;
   const int64_t tasks = batch * g.nchunks * D;
-  // About 512 workgroups (two per CU) where the shape allows, at most 16 rounds.
-  int64_t r = (tasks + kBW * 512 - 1) / (kBW * 512);
-  const int64_t rmax = (D + kBW - 1) / kBW;
+  // About 512 workgroups where the shape allows, at most 16 rounds: more rounds
+  // amortise the tile load and the partial-sum write over more channels.
+  int64_t r = (tasks + W * 512 - 1) / (W * 512);
+  const int64_t rmax = (D + W - 1) / W;
   r = r < 1 ? 1 : (r > 16 ? 16 : r);
   r = r > rmax ? rmax : r;
   g.rounds = static_cast<int>(r);
-  g.nslices = (D + kBW * r - 1) / (kBW * r);
+  g.nslices = (D + W * r - 1) / (W * r);
   const int64_t st = align64(batch * g.nchunks * D * N);
-  const int64_t bc = align64(batch * 2 * N * L);
+  const int64_t pt = align64(g.nslices * batch * 2 * N * L);
   const int64_t pp = align64(batch * g.nchunks * D);
   if (ws) {
     g.F = ws;
     g.X = g.F + st;
     g.P = g.X + st;
-    g.dBC = g.P + st;
-    g.dDp = g.dBC + bc;
+    g.part = g.P + st;
+    g.dDp = g.part + pt;
     g.dbp = g.dDp + pp;
   }
   return g;
@@ -107,7 +109,7 @@ BwdLayout bwd_layout(int64_t batch, int64_t L, int64_t D, int N, float* ws) {
 
 size_t bwd_ws_floats(int64_t batch, int64_t L, int64_t D, int N) {
   const BwdLayout g = bwd_layout(batch, L, D, N, nullptr);
-  return static_cast<size_t>(3 * align64(batch * g.nchunks * D * N) + align64(batch * 2 * N * L) +
+  return static_cast<size_t>(3 * align64(batch * g.nchunks * D * N) + align64(g.nslices * batch * 2 * N * L) +
                              2 * align64(batch * g.nchunks * D));
 }
 
@@ -144,6 +146,43 @@ __device__ __forceinline__ void wave_rscan_pairs(float& a, float& b, float carry
   const int row = (threadIdx.x & 63) >> 4;
   const float m = row == 3 ? carry : (row == 2 ? m2 : (row == 1 ? m1 : m0));
   b = __builtin_fmaf(a, m, b);
+}
+
+// Two independent reverse scans, interleaved (no wait states between the DPP steps).
+__device__ __forceinline__ void wave_rscan_pairs2(float& a0, float& b0, float carry0, float& a1, float& b1,
+                                                  float carry1) {
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %0, %0, %1 row_shl:1 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %2, %2, %3 row_shl:1 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %1, %1, %1 row_shl:1 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %3, %3, %3 row_shl:1 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %0, %0, %1 row_shl:2 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %2, %2, %3 row_shl:2 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %1, %1, %1 row_shl:2 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %3, %3, %3 row_shl:2 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %0, %0, %1 row_shl:4 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %2, %2, %3 row_shl:4 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %1, %1, %1 row_shl:4 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %3, %3, %3 row_shl:4 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %0, %0, %1 row_shl:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %2, %2, %3 row_shl:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %1, %1, %1 row_shl:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_mul_f32_dpp %3, %3, %3 row_shl:8 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1"
+      : "+v"(b0), "+v"(a0), "+v"(b1), "+v"(a1));
+  auto rl = [](float v, int l) { return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l)); };
+  const float m2a = __builtin_fmaf(rl(a0, 48), carry0, rl(b0, 48));
+  const float m2b = __builtin_fmaf(rl(a1, 48), carry1, rl(b1, 48));
+  const float m1a = __builtin_fmaf(rl(a0, 32), m2a, rl(b0, 32));
+  const float m1b = __builtin_fmaf(rl(a1, 32), m2b, rl(b1, 32));
+  const float m0a = __builtin_fmaf(rl(a0, 16), m1a, rl(b0, 16));
+  const float m0b = __builtin_fmaf(rl(a1, 16), m1b, rl(b1, 16));
+  const int row = (threadIdx.x & 63) >> 4;
+  const float ma = row == 3 ? carry0 : (row == 2 ? m2a : (row == 1 ? m1a : m0a));
+  const float mb = row == 3 ? carry1 : (row == 2 ? m2b : (row == 1 ? m1b : m0b));
+  b0 = __builtin_fmaf(a0, ma, b0);
+  b1 = __builtin_fmaf(a1, mb, b1);
 }
 
 // Value of lane i+1 in lane i; lane 63 receives `last`.
@@ -185,19 +224,9 @@ __device__ __forceinline__ void load4<ActBF16>(const void* p, int64_t i, float (
 }
 
 // KPL consecutive tokens of one channel starting at token t of the row at element
-// offset `row`; tokens at or past L read as 0.
+// offset `row`; tokens at or past L read as 0 (element by element).
 template <typename ACT, int KPL>
-__device__ __forceinline__ void load_tokens(const void* src, int64_t row, int64_t t, int64_t L, bool vec,
-                                            float (&v)[KPL]) {
-  if constexpr (KPL == 8) {
-    if (vec && t + KPL <= L) {
-      using IO = TokenIO<ACT, KPL>;
-      typename IO::raw_t r[IO::kVec];
-      IO::load_raw(src, row + t, r);
-      IO::unpack(r, v);
-      return;
-    }
-  }
+__device__ __forceinline__ void load_tokens(const void* src, int64_t row, int64_t t, int64_t L, float (&v)[KPL]) {
 #pragma unroll
   for (int j = 0; j < KPL; ++j) v[j] = t + j < L ? load_act<ACT>(src, row + t + j) : 0.0f;
 }
@@ -216,54 +245,89 @@ __device__ __forceinline__ void store_tokens(void* dst, int64_t row, int64_t t, 
     if (t + j < L) store_act<ACT>(dst, row + t + j, v[j]);
 }
 
-// Stages chunk [t0, t0 + CH) of B (states 0..N-1) then C into LDS as float32:
-// float4 f of block m*N + n (tokens 4f .. 4f+3 of the chunk) goes to slot
+// Stages chunk [t0, t0 + 64*KPL) of B (states 0..NP-1) then C into LDS as float32,
+// block m*NP + n for matrix m and state n (states N..NP-1, and tokens past L, are
+// zero).  Float4 f of a block (tokens 4f .. 4f+3 of the chunk) goes to slot
 // (f % (KPL/4)) * 64 + f / (KPL/4), so lane i finds its KPL tokens as KPL/4
-// float4 at q * 64 + i.  Tokens past L are zero.
+// float4 at q * 64 + i.
 template <typename ACT, int KPL>
-__device__ __forceinline__ void load_tile(float4* tile, const BwdArgs& p, int64_t b, int64_t t0, bool vec) {
+__device__ __forceinline__ void load_tile(float4* tile, const BwdArgs& p, int64_t b, int64_t t0, int NP, bool vec) {
   constexpr int CH = 64 * KPL, F4 = CH / 4, Q = KPL / 4;
   const int N = p.N;
   const int64_t L = p.L;
-  const int total = 2 * N * F4;
+  const int total = 2 * NP * F4;
   for (int e = threadIdx.x; e < total; e += blockDim.x) {
     const int mn = e / F4, f = e % F4;
-    const int m = mn / N, n = mn % N;
+    const int m = mn / NP, n = mn % NP;
     const void* src = m ? p.Cm : p.Bm;
     const int64_t off = (b * N + n) * L;
     const int64_t t = t0 + 4 * f;
-    float x[4];
-    if (vec && t + 4 <= L) {
-      load4<ACT>(src, off + t, x);
-    } else {
+    float x[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (n < N) {
+      if (vec && t + 4 <= L) {
+        load4<ACT>(src, off + t, x);
+      } else {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) x[r] = t + r < L ? load_act<ACT>(src, off + t + r) : 0.0f;
+        for (int r = 0; r < 4; ++r) x[r] = t + r < L ? load_act<ACT>(src, off + t + r) : 0.0f;
+      }
     }
     tile[mn * F4 + (f % Q) * 64 + f / Q] = make_float4(x[0], x[1], x[2], x[3]);
   }
 }
 
-// Per-token values of one channel's chunk shared by the summary and main kernels:
-// Delta (zero on tokens past L, which makes them identity steps), Delta*u and the
-// gate-scaled output gradient g (zero past L).
+// One channel's per-token inputs for its KPL tokens of the chunk.  The vector path
+// (8 tokens per lane, L % 8 == 0, 16-byte aligned rows) loads them as raw 16-byte
+// vectors ahead of use: fetch() issues the loads, get() unpacks them.  A lane whose
+// tokens start at or past L loads the row's last tokens instead (the start is
+// clamped) and its values are masked by the caller.
 template <typename ACT, int KPL>
+struct TokenLoader {
+  static constexpr bool kVecOk = KPL == 8;
+  using IO = TokenIO<ACT, 8>;
+  typename IO::raw_t ru[IO::kVec], rd[IO::kVec], ry[IO::kVec], rz[IO::kVec];
+
+  __device__ __forceinline__ void fetch(const BwdArgs& p, int64_t row, int64_t t) {
+    if constexpr (kVecOk) {
+      const int64_t tc = t + KPL <= p.L ? t : p.L - KPL;
+      IO::load_raw(p.u, row + tc, ru);
+      IO::load_raw(p.delta, row + tc, rd);
+      IO::load_raw(p.dy, row + tc, ry);
+      if (p.z) IO::load_raw(p.z, row + tc, rz);
+    }
+  }
+  // u, raw delta, dy, z (z only with a gate)
+  __device__ __forceinline__ void get(const BwdArgs& p, int64_t row, int64_t t, bool vec, float (&u)[KPL],
+                                      float (&dl)[KPL], float (&dy)[KPL], float (&z)[KPL]) {
+    if constexpr (kVecOk) {
+      if (vec) {
+        IO::unpack(ru, u);
+        IO::unpack(rd, dl);
+        IO::unpack(ry, dy);
+        if (p.z) IO::unpack(rz, z);
+        return;
+      }
+    }
+    load_tokens<ACT, KPL>(p.u, row, t, p.L, u);
+    load_tokens<ACT, KPL>(p.delta, row, t, p.L, dl);
+    load_tokens<ACT, KPL>(p.dy, row, t, p.L, dy);
+    if (p.z) load_tokens<ACT, KPL>(p.z, row, t, p.L, z);
+  }
+};
+
+// Per-token values of one channel's chunk: Delta (zero on tokens past L or for a
+// wave past the last channel, which makes them identity steps), Delta*u, the
+// gate-scaled output gradient g (zero likewise), and for the main kernel the
+// softplus derivative sigmoid(raw) and the gate factor dy * SiLU'(z).
+template <int KPL, bool FULL>
 struct TokenState {
   float u[KPL], dl[KPL], du[KPL], g[KPL];
+  float sg[FULL ? KPL : 1], dzf[FULL ? KPL : 1];
   float sdl;
 
-  // Returns the raw delta + bias in `raw` (for the softplus derivative) and, with
-  // a gate, the factor dy * SiLU'(z) in `dzf`.
-  template <bool FULL>
-  __device__ __forceinline__ void load(const BwdArgs& p, int64_t row, int64_t t, bool vec, float bias,
-                                       float (&sg)[KPL], float (&dzf)[KPL]) {
+  __device__ __forceinline__ void set(const BwdArgs& p, int64_t t, bool live, float bias, const float (&dy)[KPL],
+                                      const float (&z)[KPL]) {
     const int64_t L = p.L;
-    float dy[KPL];
-    load_tokens<ACT, KPL>(p.u, row, t, L, vec, u);
-    load_tokens<ACT, KPL>(p.delta, row, t, L, vec, dl);
-    load_tokens<ACT, KPL>(p.dy, row, t, L, vec, dy);
     if (p.z) {
-      float z[KPL];
-      load_tokens<ACT, KPL>(p.z, row, t, L, vec, z);
 #pragma unroll
       for (int j = 0; j < KPL; ++j) {
         const float s = __builtin_amdgcn_rcpf(1.0f + exp2_hw(-z[j] * kLog2e));
@@ -283,7 +347,9 @@ struct TokenState {
         d = softplus_f(raw);
         if constexpr (FULL) sg[j] = __builtin_amdgcn_rcpf(1.0f + exp2_hw(-raw * kLog2e));
       }
-      d = t + j < L ? d : 0.0f;
+      const bool ok = live && t + j < L;
+      d = ok ? d : 0.0f;
+      g[j] = ok ? g[j] : 0.0f;
       dl[j] = d;
       du[j] = d * u[j];
       sdl += d;
@@ -292,11 +358,12 @@ struct TokenState {
 };
 
 // ---- 1. chunk summaries -----------------------------------------------------------
-template <typename ACT, int KPL>
-__global__ __launch_bounds__(64 * kBW) void bwd_summary_kernel(BwdArgs p, BwdLayout g, int vec_flag) {
+// One wave per channel per round; the states one at a time.  NT: the most states
+// the instantiation holds in LDS.
+template <typename ACT, int KPL, int kW, int NT>
+__global__ __launch_bounds__(64 * kW) void bwd_summary_kernel(BwdArgs p, BwdLayout g, int vec_flag) {
   constexpr int CH = 64 * KPL, F4 = CH / 4, Q = KPL / 4;
-  constexpr int NMAX = KPL == 8 ? 16 : 64;
-  __shared__ float4 s_tile[2 * NMAX * F4];
+  __shared__ float4 s_tile[2 * NT * F4];
   const bool vec = vec_flag != 0;
   const int lane = threadIdx.x & 63;
   const int w = uniform_int(threadIdx.x >> 6);
@@ -306,34 +373,31 @@ __global__ __launch_bounds__(64 * kBW) void bwd_summary_kernel(BwdArgs p, BwdLay
   const int64_t bc = blockIdx.x % nbc, slice = blockIdx.x / nbc;
   const int64_t b = bc % p.batch, c = bc / p.batch;
   const int N = p.N;
+  const int NP = (N + 1) & ~1;
   const int64_t L = p.L, D = p.D;
   const int64_t t0 = c * CH;
-  load_tile<ACT, KPL>(s_tile, p, b, t0, vec);
-  if (slice == 0) {
-    // this chunk's part of the float32 dB/dC sums starts at zero
-    for (int e = threadIdx.x; e < 2 * N * CH; e += blockDim.x) {
-      const int64_t t = t0 + e % CH;
-      if (t < L) g.dBC[(b * 2 * N + e / CH) * L + t] = 0.0f;
-    }
-  }
+  load_tile<ACT, KPL>(s_tile, p, b, t0, NP, vec);
   __syncthreads();
 
   const int64_t tl = t0 + static_cast<int64_t>(lane) * KPL;
-  const int64_t dg = static_cast<int64_t>(kBW) * g.rounds;
+  const int64_t dg = static_cast<int64_t>(kW) * g.rounds;
   for (int r = 0; r < g.rounds; ++r) {
-    const int64_t d = slice * dg + r * kBW + w;
+    const int64_t d = slice * dg + r * kW + w;
     if (d >= D) break;
     const int64_t row = (b * D + d) * L;
-    TokenState<ACT, KPL> ts;
-    float unused0[KPL], unused1[KPL];
-    ts.template load<false>(p, row, tl, vec, p.bias ? p.bias[d] : 0.0f, unused0, unused1);
+    TokenLoader<ACT, KPL> ld;
+    TokenState<KPL, false> ts;
+    float dy[KPL], z[KPL];
+    if (vec) ld.fetch(p, row, tl);
+    ld.get(p, row, tl, vec, ts.u, ts.dl, dy, z);
+    ts.set(p, tl, true, p.bias ? p.bias[d] : 0.0f, dy, z);
     const float stot = wave_sum(ts.sdl);
     const float a2_v = lane < N ? p.A[d * N + lane] * kLog2e : 0.0f;
     float Fv = 0.0f, Xv = 0.0f;
     for (int n = 0; n < N; ++n) {
       const float a2 = lane_value(a2_v, n);
       const float4* sB = s_tile + n * F4;
-      const float4* sC = s_tile + (N + n) * F4;
+      const float4* sC = s_tile + (NP + n) * F4;
       float av[KPL], cv[KPL];
       float h = 0.0f;
 #pragma unroll
@@ -395,12 +459,22 @@ __global__ void bwd_combine_kernel(BwdArgs p, BwdLayout g) {
 }
 
 // ---- 3. the gradients -----------------------------------------------------------------
-template <typename ACT, int KPL, bool LDSACC>
-__global__ __launch_bounds__(64 * kBW) void bwd_main_kernel(BwdArgs p, BwdLayout g, int vec_flag) {
+// NT: the most states the instantiation holds in LDS (even).  The workgroup's dB/dC
+// sums over its channels accumulate in its own region of the workspace (its
+// slice's partial for this batch row and chunk): each thread owns the same
+// entries in every round, loads a pair's entries before computing the pair and
+// writes them back after adding the waves' terms, so no two threads touch one
+// entry and the loads have a pair's compute time to arrive from L2.
+template <typename ACT, int KPL, int kW, int NT>
+__global__ __launch_bounds__(64 * kW) void bwd_main_kernel(BwdArgs p, BwdLayout g, int vec_flag) {
   constexpr int CH = 64 * KPL, F4 = CH / 4, Q = KPL / 4;
-  constexpr int NMAX = BwdCap<KPL, LDSACC>::NMAX;
-  __shared__ float4 s_tile[2 * NMAX * F4];
-  __shared__ float s_acc[LDSACC ? 2 * NMAX * CH : 1];
+  constexpr int kThreads = 64 * kW;
+  constexpr int RED4 = 4 * F4;                      // float4 per pair: 2 states x (dB, dC) x chunk
+  static_assert(NT % 2 == 0, "states are processed in pairs");
+  static_assert(RED4 % kThreads == 0, "every thread owns whole float4 entries");
+  constexpr int RPT = RED4 / kThreads;               // entries per thread per pair
+  __shared__ float4 s_tile[2 * NT * F4];
+  __shared__ float4 s_red[kW * RED4];               // per wave: its channel's terms for the current pair
   const bool vec = vec_flag != 0;
   const int lane = threadIdx.x & 63;
   const bool lane0 = lane == 0;
@@ -409,36 +483,46 @@ __global__ __launch_bounds__(64 * kBW) void bwd_main_kernel(BwdArgs p, BwdLayout
   const int64_t bc = blockIdx.x % nbc, slice = blockIdx.x / nbc;
   const int64_t b = bc % p.batch, c = bc / p.batch;
   const int N = p.N;
+  const int NP = (N + 1) & ~1;
   const int64_t L = p.L, D = p.D;
   const int64_t t0 = c * CH;
-  load_tile<ACT, KPL>(s_tile, p, b, t0, vec);
-  if constexpr (LDSACC) {
-    for (int e = threadIdx.x; e < 2 * N * CH; e += blockDim.x) s_acc[e] = 0.0f;
-  }
+  load_tile<ACT, KPL>(s_tile, p, b, t0, NP, vec);
+
+  // Entry x (< RED4) of a pair: block x / F4 = 2 * (state within the pair) +
+  // matrix, slot x % F4 (lane slot % 64 and vector slot / 64 of the permuted
+  // layout).  Thread threadIdx.x owns entries threadIdx.x + k * kThreads.
+  float* part = g.part + (slice * p.batch + b) * 2 * N * L;
+  auto entry = [&](int pp, int x, int& n, int& m, int64_t& t) __attribute__((always_inline)) {
+    const int blk = x / F4, slot = x % F4;
+    n = 2 * pp + (blk >> 1);
+    m = blk & 1;
+    t = t0 + static_cast<int64_t>(slot % 64) * KPL + 4 * (slot / 64);
+  };
   __syncthreads();
 
-  // dB (m = 0) or dC (m = 1) term of state n, token j of this lane
-  auto acc_add = [&](int m, int n, int j, float v) __attribute__((always_inline)) {
-    if constexpr (LDSACC) {
-      __hip_atomic_fetch_add(&s_acc[((m * N + n) * KPL + j) * 64 + lane], v, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_WORKGROUP);
-    } else {
-      const int64_t t = t0 + static_cast<int64_t>(lane) * KPL + j;
-      if (t < L) unsafeAtomicAdd(&g.dBC[(b * 2 * N + m * N + n) * L + t], v);
-    }
-  };
-
   const int64_t tl = t0 + static_cast<int64_t>(lane) * KPL;
-  const int64_t dg = static_cast<int64_t>(kBW) * g.rounds;
+  const int64_t dg = static_cast<int64_t>(kW) * g.rounds;
+  auto chan = [&](int r) __attribute__((always_inline)) -> int64_t {
+    const int64_t d = slice * dg + r * kW + w;
+    return d < D ? d : D - 1;
+  };
+  TokenLoader<ACT, KPL> ld;
+  if (vec) ld.fetch(p, (b * D + chan(0)) * L, tl);
   for (int r = 0; r < g.rounds; ++r) {
-    const int64_t d = slice * dg + r * kBW + w;
-    if (d >= D) break;
+    // A wave past the last channel runs the last channel with zero g and Delta*u:
+    // it takes part in the barriers and adds only zeros.
+    const bool valid = slice * dg + r * kW + w < D;
+    const int64_t d = chan(r);
     const int64_t row = (b * D + d) * L;
     const int64_t soff = ((b * g.nchunks + c) * D + d) * N;
     const float dsk = p.Dskip ? p.Dskip[d] : 0.0f;
-    TokenState<ACT, KPL> ts;
-    float sg[KPL], dzf[KPL];
-    ts.template load<true>(p, row, tl, vec, p.bias ? p.bias[d] : 0.0f, sg, dzf);
+    TokenState<KPL, true> ts;
+    {
+      float dy[KPL], z[KPL];
+      ld.get(p, row, tl, vec, ts.u, ts.dl, dy, z);
+      ts.set(p, tl, valid, p.bias ? p.bias[d] : 0.0f, dy, z);
+    }
+    if (vec && r + 1 < g.rounds) ld.fetch(p, (b * D + chan(r + 1)) * L, tl);   // next round's inputs
     const float A_v = lane < N ? p.A[d * N + lane] : 0.0f;
     const float a2_v = A_v * kLog2e;
     const float hs_v = lane < N ? g.F[soff + lane] : 0.0f;
@@ -451,58 +535,160 @@ __global__ __launch_bounds__(64 * kBW) void bwd_main_kernel(BwdArgs p, BwdLayout
       yt[j] = dsk * ts.u[j];
     }
     float dA_v = 0.0f;
-    for (int n = 0; n < N; ++n) {
-      const float a2 = lane_value(a2_v, n), An = lane_value(A_v, n);
-      const float hst = lane_value(hs_v, n), mue = lane_value(mu_v, n);
-      const float4* sB = s_tile + n * F4;
-      const float4* sC = s_tile + (N + n) * F4;
-      float av[KPL], bv[KPL], hv[KPL], bs[KPL], cs[KPL];
+
+    // States n0 = 2 pp and n1 = n0 + 1 (n1 may be the zero padding state N when N
+    // is odd: zero B, C, A and carries, so it contributes nothing).
+    auto pair = [&](int pp) __attribute__((always_inline)) {
+      const int n0 = 2 * pp, n1 = n0 + 1;
+      const float a20 = lane_value(a2_v, n0), a21 = lane_value(a2_v, n1);
+      const float A0 = lane_value(A_v, n0), A1 = lane_value(A_v, n1);
+      const float hs0 = lane_value(hs_v, n0), hs1 = lane_value(hs_v, n1);
+      const float me0 = lane_value(mu_v, n0), me1 = lane_value(mu_v, n1);
+      const float4* sB0 = s_tile + n0 * F4;
+      const float4* sB1 = s_tile + n1 * F4;
+      const float4* sC0 = s_tile + (NP + n0) * F4;
+      const float4* sC1 = s_tile + (NP + n1) * F4;
+      float4* slot = s_red + w * RED4;                 // this wave's dB/dC terms for the pair
+      // B and C are read from LDS again in each phase instead of being held in
+      // registers across the pair (the compiler barrier keeps it from reusing them).
+      auto reload = []() __attribute__((always_inline)) { asm volatile("" ::: "memory"); };
+      barrier_lds();                                 // the previous pair's sums have read the slots
+      // this thread's accumulated entries of the pair (none yet in the first round)
+      float4 prev[RPT];
+      float* dst[RPT];
+      bool whole[RPT];
+#pragma unroll
+      for (int k = 0; k < RPT; ++k) {
+        int n, m;
+        int64_t t;
+        entry(pp, threadIdx.x + k * kThreads, n, m, t);
+        dst[k] = n < N ? part + (m * N + n) * L + t : nullptr;
+        whole[k] = n < N && t + 4 <= L && L % 4 == 0;
+        prev[k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if (r > 0 && whole[k]) prev[k] = *reinterpret_cast<const float4*>(dst[k]);
+      }
+
       // forward recomputation: fold, scan, replay (h_j kept per token)
-      float h = lane0 ? hst : 0.0f;
+      float av0[KPL], av1[KPL], hv0[KPL], hv1[KPL];
+      float h0 = lane0 ? hs0 : 0.0f, h1 = lane0 ? hs1 : 0.0f;
 #pragma unroll
       for (int q = 0; q < Q; ++q) {
-        const float4 bb = sB[q * 64 + lane], cc = sC[q * 64 + lane];
-        bs[4 * q + 0] = bb.x; bs[4 * q + 1] = bb.y; bs[4 * q + 2] = bb.z; bs[4 * q + 3] = bb.w;
-        cs[4 * q + 0] = cc.x; cs[4 * q + 1] = cc.y; cs[4 * q + 2] = cc.z; cs[4 * q + 3] = cc.w;
-      }
+        const float4 x0 = sB0[q * 64 + lane], x1 = sB1[q * 64 + lane];
+        const float b0[4] = {x0.x, x0.y, x0.z, x0.w}, b1[4] = {x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
-      for (int j = 0; j < KPL; ++j) {
-        av[j] = exp2_hw(ts.dl[j] * a2);
-        bv[j] = ts.du[j] * bs[j];
-        h = __builtin_fmaf(av[j], h, bv[j]);
+        for (int k = 0; k < 4; ++k) {
+          const int j = 4 * q + k;
+          av0[j] = exp2_hw(ts.dl[j] * a20);
+          av1[j] = exp2_hw(ts.dl[j] * a21);
+          h0 = __builtin_fmaf(av0[j], h0, ts.du[j] * b0[k]);
+          h1 = __builtin_fmaf(av1[j], h1, ts.du[j] * b1[k]);
+        }
       }
-      float P1 = exp2_hw(a2 * ts.sdl);
-      float P2 = P1;
-      wave_scan_pairs(P1, h);
-      const float hin = wave_shift_up(h, hst);
-      float hh = hin;
+      float P0 = exp2_hw(a20 * ts.sdl), P1 = exp2_hw(a21 * ts.sdl);
+      float R0 = P0, R1 = P1;
+      wave_scan_pairs2(P0, h0, P1, h1);
+      const float hin0 = wave_shift_up(h0, hs0), hin1 = wave_shift_up(h1, hs1);
+      reload();
+      {
+        float hh0 = hin0, hh1 = hin1;
 #pragma unroll
-      for (int j = 0; j < KPL; ++j) {
-        hh = __builtin_fmaf(av[j], hh, bv[j]);
-        hv[j] = hh;
-        yt[j] = __builtin_fmaf(cs[j], hh, yt[j]);
-        acc_add(1, n, j, ts.g[j] * hh);
+        for (int q = 0; q < Q; ++q) {
+          const float4 x0 = sB0[q * 64 + lane], x1 = sB1[q * 64 + lane];
+          const float4 y0 = sC0[q * 64 + lane], y1 = sC1[q * 64 + lane];
+          const float b0[4] = {x0.x, x0.y, x0.z, x0.w}, b1[4] = {x1.x, x1.y, x1.z, x1.w};
+          const float c0[4] = {y0.x, y0.y, y0.z, y0.w}, c1[4] = {y1.x, y1.y, y1.z, y1.w};
+          float t0[4], t1[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int j = 4 * q + k;
+            hh0 = __builtin_fmaf(av0[j], hh0, ts.du[j] * b0[k]);
+            hh1 = __builtin_fmaf(av1[j], hh1, ts.du[j] * b1[k]);
+            hv0[j] = hh0;
+            hv1[j] = hh1;
+            yt[j] = __builtin_fmaf(c0[k], hh0, yt[j]);
+            yt[j] = __builtin_fmaf(c1[k], hh1, yt[j]);
+            t0[k] = ts.g[j] * hh0;                     // dC terms
+            t1[k] = ts.g[j] * hh1;
+          }
+          slot[1 * F4 + q * 64 + lane] = make_float4(t0[0], t0[1], t0[2], t0[3]);
+          slot[3 * F4 + q * 64 + lane] = make_float4(t1[0], t1[1], t1[2], t1[3]);
+        }
       }
       // adjoint: reverse fold, reverse scan, reverse replay
-      float x = 0.0f;
+      reload();
+      float x0 = 0.0f, x1 = 0.0f;
 #pragma unroll
-      for (int j = KPL - 1; j >= 0; --j) x = av[j] * __builtin_fmaf(ts.g[j], cs[j], x);
-      wave_rscan_pairs(P2, x, mue);
-      float mu = wave_shift_down(x, mue);            // adjoint entering this lane's last token
-      float dal = 0.0f;
+      for (int q = Q - 1; q >= 0; --q) {
+        const float4 y0 = sC0[q * 64 + lane], y1 = sC1[q * 64 + lane];
+        const float c0[4] = {y0.x, y0.y, y0.z, y0.w}, c1[4] = {y1.x, y1.y, y1.z, y1.w};
 #pragma unroll
-      for (int j = KPL - 1; j >= 0; --j) {
-        const float lam = __builtin_fmaf(ts.g[j], cs[j], mu);
-        s1[j] = __builtin_fmaf(lam, bs[j], s1[j]);
-        acc_add(0, n, j, lam * ts.du[j]);
-        mu = av[j] * lam;
-        const float t = mu * (j > 0 ? hv[j - 1] : hin);
-        s2[j] = __builtin_fmaf(t, An, s2[j]);
-        dal = __builtin_fmaf(t, ts.dl[j], dal);
+        for (int k = 3; k >= 0; --k) {
+          const int j = 4 * q + k;
+          x0 = av0[j] * __builtin_fmaf(ts.g[j], c0[k], x0);
+          x1 = av1[j] * __builtin_fmaf(ts.g[j], c1[k], x1);
+        }
       }
-      const float dan = wave_sum(dal);
-      dA_v = lane == n ? dan : dA_v;
-    }
+      wave_rscan_pairs2(R0, x0, me0, R1, x1, me1);
+      float mu0 = wave_shift_down(x0, me0), mu1 = wave_shift_down(x1, me1);
+      float dal0 = 0.0f, dal1 = 0.0f;
+      reload();
+#pragma unroll
+      for (int q = Q - 1; q >= 0; --q) {
+        const float4 x0v = sB0[q * 64 + lane], x1v = sB1[q * 64 + lane];
+        const float4 y0 = sC0[q * 64 + lane], y1 = sC1[q * 64 + lane];
+        const float b0[4] = {x0v.x, x0v.y, x0v.z, x0v.w}, b1[4] = {x1v.x, x1v.y, x1v.z, x1v.w};
+        const float c0[4] = {y0.x, y0.y, y0.z, y0.w}, c1[4] = {y1.x, y1.y, y1.z, y1.w};
+        float t0[4], t1[4];
+#pragma unroll
+        for (int k = 3; k >= 0; --k) {
+          const int j = 4 * q + k;
+          const float lam0 = __builtin_fmaf(ts.g[j], c0[k], mu0);
+          const float lam1 = __builtin_fmaf(ts.g[j], c1[k], mu1);
+          s1[j] = __builtin_fmaf(lam0, b0[k], s1[j]);
+          s1[j] = __builtin_fmaf(lam1, b1[k], s1[j]);
+          t0[k] = lam0 * ts.du[j];                     // dB terms
+          t1[k] = lam1 * ts.du[j];
+          mu0 = av0[j] * lam0;
+          mu1 = av1[j] * lam1;
+          const float e0 = mu0 * (j > 0 ? hv0[j - 1] : hin0);
+          const float e1 = mu1 * (j > 0 ? hv1[j - 1] : hin1);
+          s2[j] = __builtin_fmaf(e0, A0, s2[j]);
+          s2[j] = __builtin_fmaf(e1, A1, s2[j]);
+          dal0 = __builtin_fmaf(e0, ts.dl[j], dal0);
+          dal1 = __builtin_fmaf(e1, ts.dl[j], dal1);
+        }
+        slot[0 * F4 + q * 64 + lane] = make_float4(t0[0], t0[1], t0[2], t0[3]);
+        slot[2 * F4 + q * 64 + lane] = make_float4(t1[0], t1[1], t1[2], t1[3]);
+      }
+      const float dan0 = wave_sum(dal0), dan1 = wave_sum(dal1);
+      dA_v = lane == n0 ? dan0 : (lane == n1 ? dan1 : dA_v);
+
+      barrier_lds();                                 // every wave's terms are in its slot
+      // the fixed-order sum over the waves' slots of the entries this thread owns
+#pragma unroll
+      for (int k = 0; k < RPT; ++k) {
+        const int x = threadIdx.x + k * kThreads;
+        float4 sum = s_red[x];
+#pragma unroll
+        for (int ww = 1; ww < kW; ++ww) {
+          const float4 v = s_red[ww * RED4 + x];
+          sum.x += v.x; sum.y += v.y; sum.z += v.z; sum.w += v.w;
+        }
+        if (whole[k]) {
+          sum.x += prev[k].x; sum.y += prev[k].y; sum.z += prev[k].z; sum.w += prev[k].w;
+          *reinterpret_cast<float4*>(dst[k]) = sum;
+        } else if (dst[k]) {
+          int n, m;
+          int64_t t;
+          entry(pp, x, n, m, t);
+          const float sv[4] = {sum.x, sum.y, sum.z, sum.w};
+          for (int rr = 0; rr < 4; ++rr)
+            if (t + rr < L) dst[k][rr] = (r > 0 ? dst[k][rr] : 0.0f) + sv[rr];
+        }
+      }
+    };
+    for (int pp = 0; pp < NP / 2; ++pp) pair(pp);
+
     // per-token gradients
     float o_du[KPL], o_dd[KPL];
     float dDl = 0.0f, dbl = 0.0f;
@@ -510,31 +696,25 @@ __global__ __launch_bounds__(64 * kBW) void bwd_main_kernel(BwdArgs p, BwdLayout
     for (int j = 0; j < KPL; ++j) {
       o_du[j] = __builtin_fmaf(dsk, ts.g[j], ts.dl[j] * s1[j]);
       float dd = __builtin_fmaf(ts.u[j], s1[j], s2[j]);
-      if (p.softplus) dd *= sg[j];
+      if (p.softplus) dd *= ts.sg[j];
       o_dd[j] = dd;
       dDl = __builtin_fmaf(ts.g[j], ts.u[j], dDl);
       dbl += tl + j < L ? dd : 0.0f;
     }
-    store_tokens<ACT, KPL>(p.du, row, tl, L, vec, o_du);
-    store_tokens<ACT, KPL>(p.ddelta, row, tl, L, vec, o_dd);
-    if (p.dz) {
-#pragma unroll
-      for (int j = 0; j < KPL; ++j) o_du[j] = yt[j] * dzf[j];
-      store_tokens<ACT, KPL>(p.dz, row, tl, L, vec, o_du);
-    }
     const float dDs = wave_sum(dDl), dbs = wave_sum(dbl);
-    if (lane < N) g.P[soff + lane] = dA_v;
-    if (lane0) {
-      g.dDp[(b * g.nchunks + c) * D + d] = dDs;
-      g.dbp[(b * g.nchunks + c) * D + d] = dbs;
-    }
-  }
-  if constexpr (LDSACC) {
-    __syncthreads();
-    for (int e = threadIdx.x; e < 2 * N * CH; e += blockDim.x) {
-      const int mn = e / CH, tt = e % CH;
-      const int64_t t = t0 + tt;
-      if (t < L) unsafeAtomicAdd(&g.dBC[(b * 2 * N + mn) * L + t], s_acc[(mn * KPL + tt % KPL) * 64 + tt / KPL]);
+    if (valid) {
+      store_tokens<ACT, KPL>(p.du, row, tl, L, vec, o_du);
+      store_tokens<ACT, KPL>(p.ddelta, row, tl, L, vec, o_dd);
+      if (p.dz) {
+#pragma unroll
+        for (int j = 0; j < KPL; ++j) o_du[j] = yt[j] * ts.dzf[j];
+        store_tokens<ACT, KPL>(p.dz, row, tl, L, vec, o_du);
+      }
+      if (lane < N) g.P[soff + lane] = dA_v;
+      if (lane0) {
+        g.dDp[(b * g.nchunks + c) * D + d] = dDs;
+        g.dbp[(b * g.nchunks + c) * D + d] = dbs;
+      }
     }
   }
 }
@@ -560,29 +740,32 @@ __global__ void bwd_param_sums_kernel(BwdArgs p, BwdLayout g) {
   }
 }
 
+// dB, dC = the sum over channel slices (in slice order) of the per-slice partials.
 template <typename ACT>
 __global__ void bwd_bc_out_kernel(BwdArgs p, BwdLayout g) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int64_t L = p.L, NL = p.N * L;
-  if (i >= p.batch * 2 * NL) return;
+  const int64_t L = p.L, NL = p.N * L, per = p.batch * 2 * NL;
+  if (i >= per) return;
+  float s = 0.0f;
+  for (int64_t k = 0; k < g.nslices; ++k) s += g.part[k * per + i];
   const int64_t b = i / (2 * NL), rem = i % (2 * NL);
   const int m = static_cast<int>(rem / NL);
-  store_act<ACT>(m ? p.dC : p.dB, b * NL + rem % NL, g.dBC[i]);
+  store_act<ACT>(m ? p.dC : p.dB, b * NL + rem % NL, s);
 }
 
 bool aligned16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; }
 
-template <typename ACT, int KPL, bool LDSACC>
+template <typename ACT, int KPL, int kW, int NT>
 hipError_t launch_bwd_typed(const BwdArgs& a, const BwdLayout& g, hipStream_t s) {
   const bool vec = (a.L % 8 == 0) && aligned16(a.u) && aligned16(a.delta) && aligned16(a.dy) &&
                    (a.z == nullptr || aligned16(a.z)) && aligned16(a.du) && aligned16(a.ddelta) &&
                    (a.dz == nullptr || aligned16(a.dz)) && aligned16(a.Bm) && aligned16(a.Cm);
   const int64_t blocks = a.batch * g.nchunks * g.nslices;
-  hipLaunchKernelGGL((bwd_summary_kernel<ACT, KPL>), dim3(static_cast<unsigned>(blocks)), dim3(64 * kBW), 0, s,
+  hipLaunchKernelGGL((bwd_summary_kernel<ACT, KPL, kW, NT>), dim3(static_cast<unsigned>(blocks)), dim3(64 * kW), 0, s,
                      a, g, vec ? 1 : 0);
   const int64_t nc = a.batch * a.D * a.N;
   hipLaunchKernelGGL(bwd_combine_kernel, dim3(static_cast<unsigned>((nc + 255) / 256)), dim3(256), 0, s, a, g);
-  hipLaunchKernelGGL((bwd_main_kernel<ACT, KPL, LDSACC>), dim3(static_cast<unsigned>(blocks)), dim3(64 * kBW), 0,
+  hipLaunchKernelGGL((bwd_main_kernel<ACT, KPL, kW, NT>), dim3(static_cast<unsigned>(blocks)), dim3(64 * kW), 0,
                      s, a, g, vec ? 1 : 0);
   const int64_t np = a.D * a.N + 2 * a.D;
   hipLaunchKernelGGL(bwd_param_sums_kernel, dim3(static_cast<unsigned>((np + 255) / 256)), dim3(256), 0, s, a, g);
@@ -594,9 +777,8 @@ hipError_t launch_bwd_typed(const BwdArgs& a, const BwdLayout& g, hipStream_t s)
 
 template <typename ACT>
 hipError_t launch_bwd_act(const BwdArgs& a, const BwdLayout& g, hipStream_t s) {
-  if (g.kpl == 8) return launch_bwd_typed<ACT, 8, true>(a, g, s);
-  if (a.N <= BwdCap<4, true>::NMAX) return launch_bwd_typed<ACT, 4, true>(a, g, s);
-  return launch_bwd_typed<ACT, 4, false>(a, g, s);
+  if (bwd_fast(a.N)) return launch_bwd_typed<ACT, 8, kWFast, kNMaxFast>(a, g, s);
+  return launch_bwd_typed<ACT, 4, kWGen, kNMaxGen>(a, g, s);
 }
 
 }  // namespace

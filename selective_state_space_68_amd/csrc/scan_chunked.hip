@@ -59,25 +59,6 @@ __device__ __forceinline__ void dma16(const void* gsrc, void* lds_base) {
   __builtin_amdgcn_global_load_lds(gsrc, (lds_void*)(lds_base), 16, 0, 0);
 }
 
-// Calls f(std::integral_constant<int, I>) for I = 0 .. N-1, as straight-line code
-// (a compile-time loop the compiler cannot leave rolled).
-template <typename F, int... I>
-__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
-
-// Workgroup barrier that orders LDS only: outstanding global loads stay in
-// flight across it (the compiler waits for each where its value is used).
-__device__ __forceinline__ void barrier_lds() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 // ---- the scan ----------------------------------------------------------------
 // kNB states per step.  NBLK > 0: N == kNB * NBLK, fixed at compile time; the steps of a chunk are
 // unrolled, the last chunk is peeled, and the per-state values sit in scalar

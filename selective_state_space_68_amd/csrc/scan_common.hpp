@@ -1,7 +1,10 @@
-// Vector I/O shared by the scan kernels (forward and backward): per-lane runs of
-// KPL consecutive tokens of one channel (TokenIO) and the 16-byte B/C tile
-// elements (TileIO), with non-temporal accesses for data read or written once.
+// Pieces shared by the scan kernels (forward and backward): vector I/O of per-lane
+// runs of KPL consecutive tokens of one channel (TokenIO) and of the 16-byte B/C
+// tile elements (TileIO), with non-temporal accesses for data read or written
+// once; a compile-time loop; an LDS-only workgroup barrier.
 #pragma once
+
+#include <utility>
 
 #include "device_common.hpp"
 
@@ -116,6 +119,25 @@ struct TileIO<ActBF16> {
     return make_float4(bf16_lo(a), bf16_hi(a), bf16_lo(b), bf16_hi(b));
   }
 };
+
+// Calls f(std::integral_constant<int, I>) for I = 0 .. N-1, as straight-line code
+// (a compile-time loop the compiler cannot leave rolled).
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Workgroup barrier that orders LDS only: outstanding global loads stay in
+// flight across it (the compiler waits for each where its value is used).
+__device__ __forceinline__ void barrier_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 }  // namespace
 }  // namespace ssm

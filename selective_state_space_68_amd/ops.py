@@ -95,7 +95,7 @@ def selective_scan_bwd_workspace_size(batch, L, D, N, dtype=torch.float32) -> in
 
 def selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, delta_softplus=True, *,
                        initial_state=None, dfinal_state=None, want_dD=None, want_ddelta_bias=None,
-                       want_dinitial_state=None, workspace=None, stream=None) -> dict:
+                       want_dinitial_state=None, workspace=None, out=None, stream=None) -> dict:
     """Backward pass of selective_scan_fwd (same inputs) for the output gradient dy
     [batch, D, L] and optionally the final-state gradient dfinal_state [batch, D, N].
 
@@ -104,7 +104,8 @@ def selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, d
     ddelta_bias and dinitial_state are computed when the matching input is given,
     unless the want_* flag says otherwise; dz whenever z is given.  `workspace` is a
     device tensor of at least selective_scan_bwd_workspace_size(...) bytes, or None
-    to allocate one.
+    to allocate one.  `out` may hold preallocated output tensors under the same keys
+    (missing keys are allocated).
     """
     lib = _lib.load_library()
     if u.dim() != 3 or B.dim() != 3 or A.dim() != 2:
@@ -132,17 +133,27 @@ def selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, d
     want_db = delta_bias is not None if want_ddelta_bias is None else want_ddelta_bias
     want_dh0 = initial_state is not None if want_dinitial_state is None else want_dinitial_state
     f32 = torch.float32
-    out = {
-        "du": torch.empty((batch, Dc, L), dtype=act, device=dev),
-        "ddelta": torch.empty((batch, Dc, L), dtype=act, device=dev),
-        "dA": torch.empty((Dc, N), dtype=f32, device=dev),
-        "dB": torch.empty((batch, N, L), dtype=act, device=dev),
-        "dC": torch.empty((batch, N, L), dtype=act, device=dev),
-        "dD": torch.empty((Dc,), dtype=f32, device=dev) if want_dD else None,
-        "dz": torch.empty((batch, Dc, L), dtype=act, device=dev) if z is not None else None,
-        "ddelta_bias": torch.empty((Dc,), dtype=f32, device=dev) if want_db else None,
-        "dinitial_state": torch.empty((batch, Dc, N), dtype=f32, device=dev) if want_dh0 else None,
+    spec = {  # name: (shape, dtype, computed)
+        "du": ((batch, Dc, L), act, True),
+        "ddelta": ((batch, Dc, L), act, True),
+        "dA": ((Dc, N), f32, True),
+        "dB": ((batch, N, L), act, True),
+        "dC": ((batch, N, L), act, True),
+        "dD": ((Dc,), f32, want_dD),
+        "dz": ((batch, Dc, L), act, z is not None),
+        "ddelta_bias": ((Dc,), f32, want_db),
+        "dinitial_state": ((batch, Dc, N), f32, want_dh0),
     }
+    given = out or {}
+    out = {}
+    for k, (shape, dt_, computed) in spec.items():
+        t = given.get(k)
+        if t is not None and computed:
+            if tuple(t.shape) != shape or t.dtype != dt_:
+                raise ValueError(f"out[{k!r}] must be {dt_} of shape {shape}")
+            out[k] = t
+        else:
+            out[k] = torch.empty(shape, dtype=dt_, device=dev) if computed else None
     need = int(lib.ssm_selective_scan_bwd_workspace_size(batch, L, Dc, N, _dt(u)))
     if workspace is None:
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)

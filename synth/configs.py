@@ -20,6 +20,7 @@ class ScanConfig:
     d_skip: str         # "normal": D ~ N(0,1); "ones": D = 1
     seed: int = 0
     conv_k: int = 0     # > 0: the input is x and u = SiLU(causal conv1d of width conv_k) is fused in
+    backward: bool = False  # the workload is the backward pass (gradients for dy) instead of the forward
 
     @property
     def elements(self) -> int:
@@ -29,6 +30,13 @@ class ScanConfig:
         """Each input read once and each output written once."""
         e = 4 if self.dtype == "f32" else 2
         per_tok = self.batch * self.L * self.D * e
+        if self.backward:
+            # reads u, delta, dy (+ z), B, C, A, D, bias; writes du, ddelta (+ dz), dB, dC, dA, dD, dbias
+            n_act = 5 + (2 if self.gate else 0)
+            return (per_tok * n_act
+                    + 4 * self.batch * self.L * self.N * e    # B, C read; dB, dC written
+                    + 8 * self.D * self.N                     # A read, dA written
+                    + 16 * self.D)                            # D skip, bias read; their gradients written
         n_act = 3 + (1 if self.gate else 0)          # u, delta, y (+ z)
         return (per_tok * n_act
                 + 2 * self.batch * self.L * self.N * e  # B, C
@@ -73,4 +81,11 @@ CONFIGS = {
                                      conv_k=4),
     "mamba1p4b_conv_bf16": ScanConfig("mamba1p4b_conv_bf16", 8, 2048, 4096, 16, "bf16", gate=True,
                                       d_skip="ones", conv_k=4),
+    # the backward pass (training) at the forward workloads' shapes, for an output gradient dy
+    "bwd_mamba130m_f32": ScanConfig("bwd_mamba130m_f32", 2, 2048, 1536, 16, "f32", gate=True, d_skip="ones",
+                                    backward=True),
+    "bwd_mamba1p4b_bf16": ScanConfig("bwd_mamba1p4b_bf16", 8, 2048, 4096, 16, "bf16", gate=True, d_skip="ones",
+                                     backward=True),
+    "bwd_long131k_bf16": ScanConfig("bwd_long131k_bf16", 1, 131072, 2560, 16, "bf16", gate=True, d_skip="ones",
+                                    backward=True),
 }
