@@ -288,15 +288,14 @@ def main():
             warm += 1
     torch.cuda.synchronize()
     if graph is not None and kind in ("scan", "bwd"):
-        # the replayed outputs must equal an eager call's, bit for bit (for the backward,
-        # the outputs that are formed in a fixed order)
+        # the replayed outputs must equal an eager call's, bit for bit
         if warm == 0:
             graph.replay()
             torch.cuda.synchronize()
         if kind == "scan":
             get = lambda: {k: bufs[(K - 1) % sets][k] for k in ("y", "fs")}
         else:
-            get = lambda: {k: bufs[(K - 1) % sets]["g"][k] for k in ("du", "ddelta", "dz", "dA", "dD")}
+            get = lambda: {k: bufs[(K - 1) % sets]["g"][k] for k in ("du", "ddelta", "dz", "dA", "dB", "dC", "dD")}
         ref = {k: v.clone() for k, v in get().items()}
         step(K - 1)
         torch.cuda.synchronize()

@@ -30,8 +30,7 @@
  *  - The library never allocates or frees device memory; the caller owns
  *    every buffer.  NaN/Inf inputs are not checked and propagate.
  *  - Results are deterministic: same inputs, shapes and device give
- *    bitwise-identical outputs (the backward pass's dB and dC excepted, see
- *    ssm_selective_scan_bwd).
+ *    bitwise-identical outputs.
  *  - Alignment: every pointer must be aligned to its element size.  16-byte
  *    aligned pointers and L a multiple of 8 select the vectorised scan; other
  *    shapes run a slower path with the same results.
@@ -221,9 +220,8 @@ ssm_status ssm_selective_scan_fwd_conv(
  * entry do not matter and on return are unspecified.  Calls that share a
  * workspace must not overlap in time.
  *
- * Determinism: dB and dC are sums over the D channels formed with floating-point
- * atomic additions, so their last bits can differ between runs; every other
- * output is bitwise reproducible.
+ * Determinism: every output, including the sums over channels (dB, dC, dA, dD,
+ * ddelta_bias), is formed in a fixed order and is bitwise reproducible.
  * Errors: SSM_ERR_INVALID_ARG for a NULL required pointer (u, delta, A, Bm, Cm,
  * dy, du, ddelta, dA, dB, dC, workspace where the size is nonzero), a negative
  * size, misalignment, a too-small workspace, dz without z, or any output

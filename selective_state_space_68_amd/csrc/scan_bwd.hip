@@ -142,9 +142,12 @@ __device__ __forceinline__ void wave_rscan_pairs(float& a, float& b, float carry
   auto rl = [](float v, int l) { return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l)); };
   const float m2 = __builtin_fmaf(rl(a, 48), carry, rl(b, 48));
   const float m1 = __builtin_fmaf(rl(a, 32), m2, rl(b, 32));
-  const float m0 = __builtin_fmaf(rl(a, 16), m1, rl(b, 16));
+  float m0 = __builtin_fmaf(rl(a, 16), m1, rl(b, 16));
+  float mm1 = m1, mm2 = m2;
+  // (computed for all lanes before the selection, which then stays branch-free)
+  asm volatile("" : "+v"(m0), "+v"(mm1), "+v"(mm2));
   const int row = (threadIdx.x & 63) >> 4;
-  const float m = row == 3 ? carry : (row == 2 ? m2 : (row == 1 ? m1 : m0));
+  const float m = row == 3 ? carry : (row == 2 ? mm2 : (row == 1 ? mm1 : m0));
   b = __builtin_fmaf(a, m, b);
 }
 
@@ -176,11 +179,13 @@ __device__ __forceinline__ void wave_rscan_pairs2(float& a0, float& b0, float ca
   const float m2b = __builtin_fmaf(rl(a1, 48), carry1, rl(b1, 48));
   const float m1a = __builtin_fmaf(rl(a0, 32), m2a, rl(b0, 32));
   const float m1b = __builtin_fmaf(rl(a1, 32), m2b, rl(b1, 32));
-  const float m0a = __builtin_fmaf(rl(a0, 16), m1a, rl(b0, 16));
-  const float m0b = __builtin_fmaf(rl(a1, 16), m1b, rl(b1, 16));
+  float m0a = __builtin_fmaf(rl(a0, 16), m1a, rl(b0, 16));
+  float m0b = __builtin_fmaf(rl(a1, 16), m1b, rl(b1, 16));
+  float xa1 = m1a, xa2 = m2a, xb1 = m1b, xb2 = m2b;
+  asm volatile("" : "+v"(m0a), "+v"(xa1), "+v"(xa2), "+v"(m0b), "+v"(xb1), "+v"(xb2));
   const int row = (threadIdx.x & 63) >> 4;
-  const float ma = row == 3 ? carry0 : (row == 2 ? m2a : (row == 1 ? m1a : m0a));
-  const float mb = row == 3 ? carry1 : (row == 2 ? m2b : (row == 1 ? m1b : m0b));
+  const float ma = row == 3 ? carry0 : (row == 2 ? xa2 : (row == 1 ? xa1 : m0a));
+  const float mb = row == 3 ? carry1 : (row == 2 ? xb2 : (row == 1 ? xb1 : m0b));
   b0 = __builtin_fmaf(a0, ma, b0);
   b1 = __builtin_fmaf(a1, mb, b1);
 }
@@ -358,7 +363,7 @@ struct TokenState {
 };
 
 // ---- 1. chunk summaries -----------------------------------------------------------
-// One wave per channel per round; the states one at a time.  NT: the most states
+// One wave per channel per round; the states two at a time.  NT: the most states
 // the instantiation holds in LDS.
 template <typename ACT, int KPL, int kW, int NT>
 __global__ __launch_bounds__(64 * kW) void bwd_summary_kernel(BwdArgs p, BwdLayout g, int vec_flag) {
@@ -394,34 +399,48 @@ __global__ __launch_bounds__(64 * kW) void bwd_summary_kernel(BwdArgs p, BwdLayo
     const float stot = wave_sum(ts.sdl);
     const float a2_v = lane < N ? p.A[d * N + lane] * kLog2e : 0.0f;
     float Fv = 0.0f, Xv = 0.0f;
-    for (int n = 0; n < N; ++n) {
-      const float a2 = lane_value(a2_v, n);
-      const float4* sB = s_tile + n * F4;
-      const float4* sC = s_tile + (NP + n) * F4;
-      float av[KPL], cv[KPL];
-      float h = 0.0f;
+    // two states at a time (the second may be the zero padding state N when N is
+    // odd: zero A, B and C, nothing stored)
+    for (int n0 = 0; n0 < NP; n0 += 2) {
+      const int n1 = n0 + 1;
+      const float a20 = lane_value(a2_v, n0), a21 = lane_value(a2_v, n1);
+      const float4* sB0 = s_tile + n0 * F4;
+      const float4* sB1 = s_tile + n1 * F4;
+      const float4* sC0 = s_tile + (NP + n0) * F4;
+      const float4* sC1 = s_tile + (NP + n1) * F4;
+      float av0[KPL], av1[KPL], cv0[KPL], cv1[KPL];
+      float h0 = 0.0f, h1 = 0.0f;
 #pragma unroll
       for (int q = 0; q < Q; ++q) {
-        const float4 bb = sB[q * 64 + lane], cc = sC[q * 64 + lane];
-        const float bs[4] = {bb.x, bb.y, bb.z, bb.w}, cs[4] = {cc.x, cc.y, cc.z, cc.w};
+        const float4 x0 = sB0[q * 64 + lane], x1 = sB1[q * 64 + lane];
+        const float4 y0 = sC0[q * 64 + lane], y1 = sC1[q * 64 + lane];
+        const float b0[4] = {x0.x, x0.y, x0.z, x0.w}, b1[4] = {x1.x, x1.y, x1.z, x1.w};
+        const float c0[4] = {y0.x, y0.y, y0.z, y0.w}, c1[4] = {y1.x, y1.y, y1.z, y1.w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const int j = 4 * q + k;
-          av[j] = exp2_hw(ts.dl[j] * a2);
-          cv[j] = cs[k];
-          h = __builtin_fmaf(av[j], h, ts.du[j] * bs[k]);
+          av0[j] = exp2_hw(ts.dl[j] * a20);
+          av1[j] = exp2_hw(ts.dl[j] * a21);
+          cv0[j] = c0[k];
+          cv1[j] = c1[k];
+          h0 = __builtin_fmaf(av0[j], h0, ts.du[j] * b0[k]);
+          h1 = __builtin_fmaf(av1[j], h1, ts.du[j] * b1[k]);
         }
       }
-      float x = 0.0f;
+      float x0 = 0.0f, x1 = 0.0f;
 #pragma unroll
-      for (int j = KPL - 1; j >= 0; --j) x = av[j] * __builtin_fmaf(ts.g[j], cv[j], x);
-      float P1 = exp2_hw(a2 * ts.sdl);
-      float P2 = P1;
-      wave_scan_pairs(P1, h);
-      wave_rscan_pairs(P2, x, 0.0f);
-      const float fn = wave_lane63(h), xn = lane_value(x, 0);
-      Fv = lane == n ? fn : Fv;
-      Xv = lane == n ? xn : Xv;
+      for (int j = KPL - 1; j >= 0; --j) {
+        x0 = av0[j] * __builtin_fmaf(ts.g[j], cv0[j], x0);
+        x1 = av1[j] * __builtin_fmaf(ts.g[j], cv1[j], x1);
+      }
+      float P0 = exp2_hw(a20 * ts.sdl), P1 = exp2_hw(a21 * ts.sdl);
+      float R0 = P0, R1 = P1;
+      wave_scan_pairs2(P0, h0, P1, h1);
+      wave_rscan_pairs2(R0, x0, 0.0f, R1, x1, 0.0f);
+      const float f0 = wave_lane63(h0), f1 = wave_lane63(h1);
+      const float y0 = lane_value(x0, 0), y1 = lane_value(x1, 0);
+      Fv = lane == n0 ? f0 : (lane == n1 ? f1 : Fv);
+      Xv = lane == n0 ? y0 : (lane == n1 ? y1 : Xv);
     }
     if (lane < N) {
       const int64_t off = ((b * g.nchunks + c) * D + d) * N + lane;

@@ -137,8 +137,7 @@ def test_bwd_zero_length():
 
 
 def test_bwd_repeatable_and_workspace_reuse():
-    # everything but dB/dC is bitwise reproducible; a dirty, reused workspace
-    # changes nothing
+    # every output is bitwise reproducible; a dirty, reused workspace changes nothing
     import torch
     from selective_state_space_68_amd import selective_scan_bwd, selective_scan_bwd_workspace_size
     inp, dyv, dyup, hz, dfin = _case(2, 1024, 40, 16, "bf16", h0=True, dfinal=True)
@@ -152,7 +151,7 @@ def test_bwd_repeatable_and_workspace_reuse():
                                workspace=ws)
         torch.cuda.synchronize()
         outs.append({k: host(v) for k, v in g.items()})
-    for k in ("du", "ddelta", "dz", "dA", "dD", "ddelta_bias", "dinitial_state"):
+    for k in ("du", "ddelta", "dz", "dA", "dB", "dC", "dD", "ddelta_bias", "dinitial_state"):
         assert np.array_equal(outs[0][k], outs[1][k]), k
     ref = _run_oracle(inp, dyv, hz, dfin)
     _compare(outs[1], ref, "bf16", "bwd reused workspace")
