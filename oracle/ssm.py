@@ -27,6 +27,12 @@ Sources, by page and section:
   Readings taken where the pages are silent: the gate multiplies (C.h + D.u), the
   softplus has no threshold, SiLU(z) = z / (1 + exp(-z)).
 
+Full zero-order hold (``discretization="zoh"``): the input term becomes
+  bbar*u        = (exp(Delta*A) - 1) / A * B[b,t,n] * u[b,t,d]   (Delta*B*u where A = 0)
+which is the exact solution over one step of h' = A h + B u with u, B held
+constant, the (Delta A)^-1 (exp(Delta A) - I) Delta B of the slide deck's S4
+section and the lecture notes' §3 "Discretisation" for a diagonal A.
+
 Memory order: u, delta, z are [batch][D][L] (as in the library); B, C are
 [batch][L][N] (the pages' order; the library stores them [batch][N][L]); A is
 [D][N]; Dskip and bias are [D].
@@ -49,6 +55,19 @@ def silu(z):
         return z / (1.0 + np.exp(-z))
 
 
+def _input_scale(dt, A, discretization):
+    """Factor multiplying B*u in the input term, [.., D, N] from Delta [.., D] and A [D, N].
+
+    "simplified": Delta.  "zoh": expm1(Delta*A)/A, whose limit at A = 0 is Delta."""
+    dA = dt[..., None] * A
+    if discretization == "simplified":
+        return np.broadcast_to(dt[..., None], dA.shape)
+    if discretization == "zoh":
+        safe = np.where(A == 0.0, 1.0, A)
+        return np.where(A == 0.0, dt[..., None], np.expm1(dA) / safe)
+    raise ValueError(f"unknown discretization {discretization!r}")
+
+
 def _step_delta(delta_raw, bias, delta_softplus):
     d = np.asarray(delta_raw, dtype=np.float64)
     if bias is not None:
@@ -57,7 +76,7 @@ def _step_delta(delta_raw, bias, delta_softplus):
 
 
 def selective_scan(u, delta, A, B, C, Dskip=None, z=None, delta_bias=None,
-                   delta_softplus=True, h0=None):
+                   delta_softplus=True, h0=None, discretization="simplified"):
     """Return (y [batch][D][L], final_state [batch][D][N]) in float64.
 
     A plain loop over time, vectorised over (batch, channel, state).
@@ -78,7 +97,8 @@ def selective_scan(u, delta, A, B, C, Dskip=None, z=None, delta_bias=None,
     for t in range(L):
         dt = _step_delta(delta[:, :, t], bias, delta_softplus)          # [Bt, Dc]
         abar = np.exp(dt[:, :, None] * A[None, :, :])                   # [Bt, Dc, N]
-        inp = (dt * u[:, :, t])[:, :, None] * Bm[:, t, None, :]         # Delta*B*u
+        scale = _input_scale(dt, A[None, :, :], discretization)          # Delta, or expm1(Delta A)/A
+        inp = scale * u[:, :, t, None] * Bm[:, t, None, :]              # Bbar*u
         h = abar * h + inp
         yt = np.einsum("bdn,bn->bd", h, Cm[:, t, :])
         if Dv is not None:
@@ -90,7 +110,7 @@ def selective_scan(u, delta, A, B, C, Dskip=None, z=None, delta_bias=None,
 
 
 def state_update(state, u_t, delta_t, A, B_t, C_t, Dskip=None, z_t=None,
-                 delta_bias=None, delta_softplus=True):
+                 delta_bias=None, delta_softplus=True, discretization="simplified"):
     """One recurrent decode step: returns (y_t [S][D], new_state [S][D][N]) in float64.
 
     The same step as one iteration of ``selective_scan`` started from ``state``.
@@ -101,7 +121,8 @@ def state_update(state, u_t, delta_t, A, B_t, C_t, Dskip=None, z_t=None,
     bias = None if delta_bias is None else np.asarray(delta_bias, dtype=np.float64)[None, :]
     dt = _step_delta(delta_t, bias, delta_softplus)                       # [S, D]
     abar = np.exp(dt[:, :, None] * A[None, :, :])
-    inp = (dt * u_t)[:, :, None] * np.asarray(B_t, dtype=np.float64)[:, None, :]
+    scale = _input_scale(dt, A[None, :, :], discretization)
+    inp = scale * u_t[:, :, None] * np.asarray(B_t, dtype=np.float64)[:, None, :]
     h = abar * h + inp
     y = np.einsum("sdn,sn->sd", h, np.asarray(C_t, dtype=np.float64))
     if Dskip is not None:
