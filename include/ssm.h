@@ -152,6 +152,33 @@ ssm_status ssm_state_update(
     int64_t batch, int64_t D, int64_t N, ssm_dtype dt, void *stream);
 
 /*
+ * The scan and the decode step with the full zero-order-hold discretization: the
+ * input term is (exp(Delta*A) - 1)/A * B * u instead of Delta * B * u, the
+ * (Delta A)^-1 (exp(Delta A) - I) Delta B of the slide deck's S4 section and the
+ * lecture notes' §3 "Discretisation" for a diagonal A (the exact step of
+ * x' = A x + B u with u and B held for a time Delta).  The decay exp(Delta*A), the
+ * readout, the skip term and the gate are unchanged.
+ *
+ * Arguments, layouts, outputs and errors as in ssm_selective_scan_fwd_from_state
+ * and ssm_state_update.  Every A[d, n] must be nonzero (the models use A < 0): the
+ * term is formed as (exp(Delta A) - 1) * (1/A), and an A of zero gives a NaN for
+ * that state instead of the limit Delta * B * u.  The scan runs the chunked kernel
+ * at its default 8 tokens per lane.
+ */
+ssm_status ssm_selective_scan_fwd_zoh(
+    const void *u, const void *delta, const float *A, const void *Bm, const void *Cm,
+    const float *Dskip, const void *z, const float *delta_bias, int delta_softplus,
+    const float *initial_state, void *y, float *final_state,
+    int64_t batch, int64_t L, int64_t D, int64_t N, ssm_dtype dt, void *stream);
+
+ssm_status ssm_state_update_zoh(
+    const float *state_in, float *state_out, const void *u_t, const void *delta_t,
+    const float *A, const void *B_t, const void *C_t,
+    const float *Dskip, const void *z_t, const float *delta_bias, int delta_softplus,
+    void *y_t,
+    int64_t batch, int64_t D, int64_t N, ssm_dtype dt, void *stream);
+
+/*
  * Causal depthwise convolution along L, optionally followed by SiLU: the branch of
  * the Mamba block in front of the selective scan (dileepadev "Mamba
  * Architecture", SSM block internals: depthwise conv, then SiLU, then the SSM;

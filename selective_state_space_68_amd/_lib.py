@@ -36,6 +36,10 @@ SIGNATURES = {
                                                  _i64, _i64, _i64, _i64, _int, _vp]),
     "ssm_selective_scan_fwd_variant": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _vp, _vp, _vp,
                                               _i64, _i64, _i64, _i64, _int, _vp, _int, _int]),
+    "ssm_selective_scan_fwd_zoh": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _vp, _vp, _vp,
+                                          _i64, _i64, _i64, _i64, _int, _vp]),
+    "ssm_state_update_zoh": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _vp,
+                                    _i64, _i64, _i64, _int, _vp]),
     "ssm_causal_conv1d_fwd": (_int, [_vp, _vp, _vp, _i64, _int, _vp, _i64, _i64, _i64, _int, _vp]),
     "ssm_selective_scan_fwd_conv": (_int, [_vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _vp,
                                            _vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _vp, _int]),

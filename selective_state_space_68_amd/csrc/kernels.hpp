@@ -28,6 +28,8 @@ struct ScanArgs {
   int64_t batch, L, D;
   int N;
   int softplus;
+  int zoh = 0;           // 1: full zero-order hold, input term (exp(Delta A) - 1)/A * B * u
+                         //    (chunked kernel only)
 };
 
 struct ConvArgs {
@@ -55,6 +57,7 @@ struct StepArgs {
   int64_t batch, D;
   int N;
   int softplus;
+  int zoh = 0;            // 1: full zero-order hold (as ScanArgs::zoh)
 };
 
 struct BwdArgs {

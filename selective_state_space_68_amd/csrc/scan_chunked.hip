@@ -65,7 +65,11 @@ __device__ __forceinline__ void dma16(const void* gsrc, void* lds_base) {
 // registers.  The steady state then has no branch around any load, so the
 // compiler's tracking of outstanding loads stays exact and it never waits for a
 // load before its value is needed.  NBLK = 0: any N, steps in a runtime loop.
-template <typename ACT, bool GATE, int KPL, bool VEC, int NBLK, int kNB, int kW, bool CONV>
+//
+// ZOH: the full zero-order-hold input term (e^{Delta A} - 1)/A * B * u instead of
+// Delta * B * u: with w = u * B / A it is a*w - w, one FMA and one multiply more per
+// element than the simplified term (1/A is per state, computed once per channel).
+template <typename ACT, bool GATE, int KPL, bool VEC, int NBLK, int kNB, int kW, bool CONV, bool ZOH>
 __global__ __launch_bounds__(64 * kW) void scan_chunked_kernel(ScanArgs p, int n_dblk) {
   constexpr int kThreads = 64 * kW;
   static_assert(KPL >= 3, "the fused conv takes its 3 earlier tokens from the previous lane");
@@ -99,6 +103,8 @@ __global__ __launch_bounds__(64 * kW) void scan_chunked_kernel(ScanArgs p, int n
   // A[d, n] * log2(e) in lane n (read once, so the state loop never issues a
   // vector load of A).
   const float a2_v = lane < N ? p.A[d * N + lane] * kLog2e : 0.0f;
+  // 1/A[d, n] in lane n (full zero-order hold only)
+  const float ra_v = (ZOH && lane < N) ? 1.0f / p.A[d * N + lane] : 0.0f;
   // carry of state n lives in lane n; it starts as the initial state (zero if none)
   float carry_v = (lane < N && p.h0) ? p.h0[(b * p.D + d) * N + lane] : 0.0f;
 
@@ -190,7 +196,7 @@ __global__ __launch_bounds__(64 * kW) void scan_chunked_kernel(ScanArgs p, int n
     sdl = 0.0f;
 #pragma unroll
     for (int j = 0; j < KPL; ++j) {
-      du[j] = dl[j] * uv[j];
+      du[j] = ZOH ? uv[j] : dl[j] * uv[j];              // (ZOH: u itself; the term needs e^{Delta A} first)
       yv[j] = dsk * uv[j];
       sdl += dl[j];
     }
@@ -220,10 +226,20 @@ __global__ __launch_bounds__(64 * kW) void scan_chunked_kernel(ScanArgs p, int n
     }
   };
 
+  // Input term of token j for a state with B value bj and 1/A = ra.
+  auto input_term = [&](float avj, float duj, float bj, float ra) __attribute__((always_inline)) -> float {
+    if constexpr (ZOH) {
+      const float w = (duj * ra) * bj;
+      return __builtin_fmaf(avj, w, -w);
+    } else {
+      return duj * bj;
+    }
+  };
+
   // One state over the current chunk: its B and C blocks are sB, sC in LDS,
   // a2 = A[d, n] * log2(e) and `carry` (the state before the chunk) are
   // wave-uniform.  Returns the state after the chunk (lane 63's).
-  auto scan_one = [&](const float4* __restrict__ sB, const float4* __restrict__ sC, float a2,
+  auto scan_one = [&](const float4* __restrict__ sB, const float4* __restrict__ sC, float a2, float ra,
                       float carry) __attribute__((always_inline)) -> float {
     float av[KPL], bv[KPL];
     float h = lane0 ? carry : 0.0f;
@@ -235,7 +251,7 @@ __global__ __launch_bounds__(64 * kW) void scan_chunked_kernel(ScanArgs p, int n
       for (int r = 0; r < 4; ++r) {
         const int j = 4 * q + r;
         av[j] = exp2_hw(dl[j] * a2);
-        bv[j] = du[j] * bs[r];
+        bv[j] = input_term(av[j], du[j], bs[r], ra);
         h = __builtin_fmaf(av[j], h, bv[j]);
       }
     }
@@ -260,9 +276,9 @@ __global__ __launch_bounds__(64 * kW) void scan_chunked_kernel(ScanArgs p, int n
 
   // Two states at once, interleaved instruction by instruction: two independent
   // dependency chains in every phase, and one DPP scan sequence with no wait states.
-  auto scan_two = [&](const float4* __restrict__ sB0, const float4* __restrict__ sC0, float a20, float carry0,
-                      const float4* __restrict__ sB1, const float4* __restrict__ sC1, float a21, float carry1,
-                      float& out0, float& out1) __attribute__((always_inline)) {
+  auto scan_two = [&](const float4* __restrict__ sB0, const float4* __restrict__ sC0, float a20, float ra0,
+                      float carry0, const float4* __restrict__ sB1, const float4* __restrict__ sC1, float a21,
+                      float ra1, float carry1, float& out0, float& out1) __attribute__((always_inline)) {
     float av0[KPL], bv0[KPL], av1[KPL], bv1[KPL];
     float h0 = lane0 ? carry0 : 0.0f;
     float h1 = lane0 ? carry1 : 0.0f;
@@ -277,8 +293,8 @@ __global__ __launch_bounds__(64 * kW) void scan_chunked_kernel(ScanArgs p, int n
         const int j = 4 * q + r;
         av0[j] = exp2_hw(dl[j] * a20);
         av1[j] = exp2_hw(dl[j] * a21);
-        bv0[j] = du[j] * bs0[r];
-        bv1[j] = du[j] * bs1[r];
+        bv0[j] = input_term(av0[j], du[j], bs0[r], ra0);
+        bv1[j] = input_term(av1[j], du[j], bs1[r], ra1);
         h0 = __builtin_fmaf(av0[j], h0, bv0[j]);
         h1 = __builtin_fmaf(av1[j], h1, bv1[j]);
       }
@@ -312,7 +328,8 @@ __global__ __launch_bounds__(64 * kW) void scan_chunked_kernel(ScanArgs p, int n
   auto scan_state = [&](const float4* sB, const float4* sC, int n) __attribute__((always_inline)) {
     const float a2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, a2_v), n));
     const float carry = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, carry_v), n));
-    const float cnew = scan_one(sB, sC, a2, carry);
+    const float ra = ZOH ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ra_v), n)) : 0.0f;
+    const float cnew = scan_one(sB, sC, a2, ra, carry);
     carry_v = (lane == n) ? cnew : carry_v;
   };
 
@@ -400,11 +417,12 @@ __global__ __launch_bounds__(64 * kW) void scan_chunked_kernel(ScanArgs p, int n
   // (NBLK > 0): A*log2(e) and the carry of state n in scalar registers, indexed
   // by compile-time n once the steps are unrolled.
   constexpr int NS = NBLK > 0 ? kNB * NBLK : 1;
-  float a2s[NS], cs[NS];
+  float a2s[NS], cs[NS], ras[NS];
   if constexpr (NBLK > 0) {
 #pragma unroll
     for (int n = 0; n < NS; ++n) {
       a2s[n] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, a2_v), n));
+      ras[n] = ZOH ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ra_v), n)) : 0.0f;
       cs[n] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, carry_v), n));
     }
   }
@@ -419,14 +437,15 @@ __global__ __launch_bounds__(64 * kW) void scan_chunked_kernel(ScanArgs p, int n
 #pragma unroll
         for (int nl = 0; nl < nn; nl += 2) {
           const int n = n0 + nl;
-          scan_two(t + nl * 2 * BLK4, t + (nl * 2 + 1) * BLK4, a2s[n], cs[n],
-                   t + (nl * 2 + 2) * BLK4, t + (nl * 2 + 3) * BLK4, a2s[n + 1], cs[n + 1], cs[n], cs[n + 1]);
+          scan_two(t + nl * 2 * BLK4, t + (nl * 2 + 1) * BLK4, a2s[n], ras[n], cs[n],
+                   t + (nl * 2 + 2) * BLK4, t + (nl * 2 + 3) * BLK4, a2s[n + 1], ras[n + 1], cs[n + 1], cs[n],
+                   cs[n + 1]);
         }
       } else {
 #pragma unroll
         for (int nl = 0; nl < nn; ++nl) {
           const int n = n0 + nl;
-          cs[n] = scan_one(t + nl * 2 * BLK4, t + (nl * 2 + 1) * BLK4, a2s[n], cs[n]);
+          cs[n] = scan_one(t + nl * 2 * BLK4, t + (nl * 2 + 1) * BLK4, a2s[n], ras[n], cs[n]);
         }
       }
     } else {
@@ -495,7 +514,7 @@ __global__ __launch_bounds__(64 * kW) void scan_chunked_kernel(ScanArgs p, int n
 
 bool aligned16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; }
 
-template <typename ACT, bool GATE, int KPL, int W, bool CONV>
+template <typename ACT, bool GATE, int KPL, int W, bool CONV, bool ZOH>
 hipError_t launch_w(const ScanArgs& a, hipStream_t s) {
   const int n_dblk = static_cast<int>((a.D + W - 1) / W);
   const int64_t blocks = a.batch * n_dblk;
@@ -510,21 +529,21 @@ hipError_t launch_w(const ScanArgs& a, hipStream_t s) {
   // that way, and at 16 tokens per lane the larger tile's registers would spill.
   constexpr int N16_STEPS = (ACT::kBytes == 2 && KPL <= 8) ? 2 : 4;
   if (vec && n16)
-    hipLaunchKernelGGL((scan_chunked_kernel<ACT, GATE, KPL, true, N16_STEPS, 16 / N16_STEPS, W, CONV>), grid, block, 0,
-                       s, a, n_dblk);
+    hipLaunchKernelGGL((scan_chunked_kernel<ACT, GATE, KPL, true, N16_STEPS, 16 / N16_STEPS, W, CONV, ZOH>), grid, block,
+                       0, s, a, n_dblk);
   else if (vec)
-    hipLaunchKernelGGL((scan_chunked_kernel<ACT, GATE, KPL, true, 0, kNBGeneric, W, CONV>), grid, block, 0, s, a,
+    hipLaunchKernelGGL((scan_chunked_kernel<ACT, GATE, KPL, true, 0, kNBGeneric, W, CONV, ZOH>), grid, block, 0, s, a,
                        n_dblk);
   else if (n16)
-    hipLaunchKernelGGL((scan_chunked_kernel<ACT, GATE, KPL, false, N16_STEPS, 16 / N16_STEPS, W, CONV>), grid, block,
+    hipLaunchKernelGGL((scan_chunked_kernel<ACT, GATE, KPL, false, N16_STEPS, 16 / N16_STEPS, W, CONV, ZOH>), grid, block,
                        0, s, a, n_dblk);
   else
-    hipLaunchKernelGGL((scan_chunked_kernel<ACT, GATE, KPL, false, 0, kNBGeneric, W, CONV>), grid, block, 0, s, a,
+    hipLaunchKernelGGL((scan_chunked_kernel<ACT, GATE, KPL, false, 0, kNBGeneric, W, CONV, ZOH>), grid, block, 0, s, a,
                        n_dblk);
   return hipGetLastError();
 }
 
-template <typename ACT, bool GATE, int KPL, bool CONV>
+template <typename ACT, bool GATE, int KPL, bool CONV, bool ZOH>
 hipError_t launch_kpl(const ScanArgs& a, hipStream_t s) {
   // 12 waves per workgroup (3 per SIMD, one workgroup per CU) leaves the most
   // registers per wave.  With enough channels for four rounds of 16-wave
@@ -532,16 +551,17 @@ hipError_t launch_kpl(const ScanArgs& a, hipStream_t s) {
   // waves, 4 per SIMD, for more latency hiding: 9 % faster on the 1.4B-shaped
   // bfloat16 workload.  Fewer channels keep 12 so that every CU gets a workgroup.
   if constexpr (KPL == 8) {
-    if (a.batch * a.D >= 16 * 256 * 4) return launch_w<ACT, GATE, KPL, 16, CONV>(a, s);
+    if (a.batch * a.D >= 16 * 256 * 4) return launch_w<ACT, GATE, KPL, 16, CONV, ZOH>(a, s);
   }
-  return launch_w<ACT, GATE, KPL, 12, CONV>(a, s);
+  return launch_w<ACT, GATE, KPL, 12, CONV, ZOH>(a, s);
 }
 
 template <typename ACT, bool GATE>
 hipError_t launch_gate(const ScanArgs& a, int kpl, hipStream_t s) {
   const bool conv = a.conv_w != nullptr;
-  if (kpl == 8) return conv ? launch_kpl<ACT, GATE, 8, true>(a, s) : launch_kpl<ACT, GATE, 8, false>(a, s);
-  return conv ? launch_kpl<ACT, GATE, 16, true>(a, s) : launch_kpl<ACT, GATE, 16, false>(a, s);
+  if (a.zoh) return launch_kpl<ACT, GATE, 8, false, true>(a, s);   // (8 tokens per lane, no conv: see chunked_supported)
+  if (kpl == 8) return conv ? launch_kpl<ACT, GATE, 8, true, false>(a, s) : launch_kpl<ACT, GATE, 8, false, false>(a, s);
+  return conv ? launch_kpl<ACT, GATE, 16, true, false>(a, s) : launch_kpl<ACT, GATE, 16, false, false>(a, s);
 }
 
 // Default tokens per lane, from measurement on gfx950: 8, where the registers
@@ -556,6 +576,8 @@ int resolve_kpl(int tokens_per_lane, Dt) {
 bool chunked_supported(const ScanArgs& a, Dt, int tokens_per_lane) {
   if (!(tokens_per_lane == 0 || tokens_per_lane == 8 || tokens_per_lane == 16)) return false;
   if (a.N < 1 || a.N > 64) return false;
+  // the full zero-order hold is built for the default 8 tokens per lane without the fused conv
+  if (a.zoh && (a.conv_w != nullptr || tokens_per_lane == 16)) return false;
   const int64_t n_dblk = (a.D + 12 - 1) / 12;                // the most workgroups any launch uses
   return a.batch * n_dblk <= 0x7fffffff;
 }

@@ -11,7 +11,7 @@
 
 namespace {
 
-constexpr int kVersion = 20300;  // 2.3.0: + backward pass of the selective scan
+constexpr int kVersion = 20400;  // 2.4.0: + full zero-order-hold discretization
 
 struct Span {
   uintptr_t lo = 0, hi = 0;  // [lo, hi); empty when lo == hi
@@ -110,12 +110,14 @@ const char* ssm_status_string(ssm_status s) {
 
 int ssm_version(void) { return kVersion; }
 
-ssm_status ssm_selective_scan_fwd_variant(const void* u, const void* delta, const float* A, const void* Bm,
-                                          const void* Cm, const float* Dskip, const void* z,
-                                          const float* delta_bias, int delta_softplus,
-                                          const float* initial_state, void* y, float* final_state,
-                                          int64_t batch, int64_t L, int64_t D, int64_t N, ssm_dtype dt,
-                                          void* stream, int variant, int tokens_per_lane) {
+}  // extern "C"
+
+namespace {
+
+ssm_status scan_fwd(const void* u, const void* delta, const float* A, const void* Bm, const void* Cm,
+                    const float* Dskip, const void* z, const float* delta_bias, int delta_softplus,
+                    const float* initial_state, void* y, float* final_state, int64_t batch, int64_t L, int64_t D,
+                    int64_t N, ssm_dtype dt, void* stream, int variant, int tokens_per_lane, int zoh) {
   ScanSizes sz;
   ssm_status st = check_scan(u, delta, A, Bm, Cm, Dskip, z, delta_bias, delta_softplus, initial_state, y,
                              final_state, batch, L, D, N, dt, &sz);
@@ -127,10 +129,11 @@ ssm_status ssm_selective_scan_fwd_variant(const void* u, const void* delta, cons
   ssm::ScanArgs a;
   a.u = u; a.delta = delta; a.A = A; a.Bm = Bm; a.Cm = Cm; a.Dskip = Dskip; a.z = z;
   a.bias = delta_bias; a.h0 = initial_state; a.y = y; a.final_state = final_state;
-  a.batch = batch; a.L = L; a.D = D; a.N = static_cast<int>(N); a.softplus = delta_softplus;
+  a.batch = batch; a.L = L; a.D = D; a.N = static_cast<int>(N); a.softplus = delta_softplus; a.zoh = zoh;
   const ssm::Dt d = dt == SSM_BF16 ? ssm::Dt::BF16 : ssm::Dt::F32;
   const bool chunked = L > 0 && variant != SSM_SCAN_SEQUENTIAL && ssm::chunked_supported(a, d, tokens_per_lane);
   if (variant == SSM_SCAN_CHUNKED && L > 0 && !chunked) return SSM_ERR_UNSUPPORTED;
+  if (zoh && L > 0 && !chunked) return SSM_ERR_UNSUPPORTED;   // only the chunked kernel has the full hold
   st = probe_device();
   if (st != SSM_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -138,6 +141,28 @@ ssm_status ssm_selective_scan_fwd_variant(const void* u, const void* delta, cons
     return final_state ? from_hip(ssm::launch_copy_state(final_state, initial_state, batch * D * N, s)) : SSM_OK;
   if (chunked) return from_hip(ssm::launch_scan_chunked(a, d, tokens_per_lane, s));
   return from_hip(ssm::launch_scan_sequential(a, d, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+ssm_status ssm_selective_scan_fwd_variant(const void* u, const void* delta, const float* A, const void* Bm,
+                                          const void* Cm, const float* Dskip, const void* z,
+                                          const float* delta_bias, int delta_softplus,
+                                          const float* initial_state, void* y, float* final_state,
+                                          int64_t batch, int64_t L, int64_t D, int64_t N, ssm_dtype dt,
+                                          void* stream, int variant, int tokens_per_lane) {
+  return scan_fwd(u, delta, A, Bm, Cm, Dskip, z, delta_bias, delta_softplus, initial_state, y, final_state, batch, L,
+                  D, N, dt, stream, variant, tokens_per_lane, 0);
+}
+
+ssm_status ssm_selective_scan_fwd_zoh(const void* u, const void* delta, const float* A, const void* Bm,
+                                      const void* Cm, const float* Dskip, const void* z, const float* delta_bias,
+                                      int delta_softplus, const float* initial_state, void* y, float* final_state,
+                                      int64_t batch, int64_t L, int64_t D, int64_t N, ssm_dtype dt, void* stream) {
+  return scan_fwd(u, delta, A, Bm, Cm, Dskip, z, delta_bias, delta_softplus, initial_state, y, final_state, batch, L,
+                  D, N, dt, stream, SSM_SCAN_AUTO, 0, 1);
 }
 
 ssm_status ssm_selective_scan_fwd(const void* u, const void* delta, const float* A, const void* Bm,
@@ -300,10 +325,14 @@ ssm_status ssm_selective_scan_bwd(const void* u, const void* delta, const float*
   return from_hip(ssm::launch_scan_bwd(a, dt == SSM_BF16 ? ssm::Dt::BF16 : ssm::Dt::F32, workspace, s));
 }
 
-ssm_status ssm_state_update(const float* state_in, float* state_out, const void* u_t, const void* delta_t,
-                            const float* A, const void* B_t, const void* C_t, const float* Dskip,
-                            const void* z_t, const float* delta_bias, int delta_softplus, void* y_t,
-                            int64_t batch, int64_t D, int64_t N, ssm_dtype dt, void* stream) {
+}  // extern "C"
+
+namespace {
+
+ssm_status state_update(const float* state_in, float* state_out, const void* u_t, const void* delta_t,
+                        const float* A, const void* B_t, const void* C_t, const float* Dskip, const void* z_t,
+                        const float* delta_bias, int delta_softplus, void* y_t, int64_t batch, int64_t D, int64_t N,
+                        ssm_dtype dt, void* stream, int zoh) {
   if (dt != SSM_F32 && dt != SSM_BF16) return SSM_ERR_UNSUPPORTED;
   if (batch < 0 || D < 0 || N < 0) return SSM_ERR_INVALID_ARG;
   if (N < 1 || N > SSM_MAX_N) return SSM_ERR_UNSUPPORTED;
@@ -337,9 +366,29 @@ ssm_status ssm_state_update(const float* state_in, float* state_out, const void*
   ssm::StepArgs a;
   a.state_in = state_in; a.state_out = state_out; a.u = u_t; a.delta = delta_t; a.A = A; a.Bm = B_t;
   a.Cm = C_t; a.Dskip = Dskip; a.z = z_t; a.bias = delta_bias; a.y = y_t;
-  a.batch = batch; a.D = D; a.N = static_cast<int>(N); a.softplus = delta_softplus;
+  a.batch = batch; a.D = D; a.N = static_cast<int>(N); a.softplus = delta_softplus; a.zoh = zoh;
   return from_hip(ssm::launch_state_update(a, dt == SSM_BF16 ? ssm::Dt::BF16 : ssm::Dt::F32,
                                            static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+ssm_status ssm_state_update(const float* state_in, float* state_out, const void* u_t, const void* delta_t,
+                            const float* A, const void* B_t, const void* C_t, const float* Dskip,
+                            const void* z_t, const float* delta_bias, int delta_softplus, void* y_t,
+                            int64_t batch, int64_t D, int64_t N, ssm_dtype dt, void* stream) {
+  return state_update(state_in, state_out, u_t, delta_t, A, B_t, C_t, Dskip, z_t, delta_bias, delta_softplus, y_t,
+                      batch, D, N, dt, stream, 0);
+}
+
+ssm_status ssm_state_update_zoh(const float* state_in, float* state_out, const void* u_t, const void* delta_t,
+                                const float* A, const void* B_t, const void* C_t, const float* Dskip,
+                                const void* z_t, const float* delta_bias, int delta_softplus, void* y_t,
+                                int64_t batch, int64_t D, int64_t N, ssm_dtype dt, void* stream) {
+  return state_update(state_in, state_out, u_t, delta_t, A, B_t, C_t, Dskip, z_t, delta_bias, delta_softplus, y_t,
+                      batch, D, N, dt, stream, 1);
 }
 
 }  // extern "C"

@@ -46,12 +46,17 @@ def _stream(stream) -> int:
 
 def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True, *,
                        initial_state=None, y=None, final_state=None, return_final_state=True, variant=0,
-                       tokens_per_lane=0, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                       tokens_per_lane=0, discretization="simplified",
+                       stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Selective scan forward.  Returns (y [batch, D, L], final_state [batch, D, N] or None).
 
     `initial_state` [batch, D, N] float32 starts the scan from a given state (zero
     when None); `final_state` may be the same tensor (updated in place).
+    `discretization`: "simplified" (input term Delta*B*u) or "zoh" (the full
+    zero-order hold, (exp(Delta*A) - 1)/A * B * u; every A must be nonzero).
     """
+    if discretization not in ("simplified", "zoh"):
+        raise ValueError(f"unknown discretization {discretization!r}")
     lib = _lib.load_library()
     if u.dim() != 3 or B.dim() != 3 or A.dim() != 2:
         raise ValueError("expected u [batch, D, L], B/C [batch, N, L], A [D, N]")
@@ -74,14 +79,18 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta
         y = torch.empty((batch, Dc, L), dtype=act, device=dev)
     if final_state is None and return_final_state:
         final_state = torch.empty((batch, Dc, N), dtype=torch.float32, device=dev)
-    st = lib.ssm_selective_scan_fwd_variant(
-        _ptr(u, "u", act, dev), _ptr(delta, "delta", act, dev), _ptr(A, "A", torch.float32, dev),
-        _ptr(B, "B", act, dev), _ptr(C, "C", act, dev), _ptr(D, "D", torch.float32, dev),
-        _ptr(z, "z", act, dev), _ptr(delta_bias, "delta_bias", torch.float32, dev),
-        1 if delta_softplus else 0, _ptr(initial_state, "initial_state", torch.float32, dev),
-        _ptr(y, "y", act, dev),
-        _ptr(final_state, "final_state", torch.float32, dev),
-        batch, L, Dc, N, _dt(u), _stream(stream), int(variant), int(tokens_per_lane))
+    args = (_ptr(u, "u", act, dev), _ptr(delta, "delta", act, dev), _ptr(A, "A", torch.float32, dev),
+            _ptr(B, "B", act, dev), _ptr(C, "C", act, dev), _ptr(D, "D", torch.float32, dev),
+            _ptr(z, "z", act, dev), _ptr(delta_bias, "delta_bias", torch.float32, dev),
+            1 if delta_softplus else 0, _ptr(initial_state, "initial_state", torch.float32, dev),
+            _ptr(y, "y", act, dev), _ptr(final_state, "final_state", torch.float32, dev),
+            batch, L, Dc, N, _dt(u), _stream(stream))
+    if discretization == "zoh":
+        if variant or tokens_per_lane:
+            raise ValueError("the zoh scan runs the default kernel (variant=0, tokens_per_lane=0)")
+        st = lib.ssm_selective_scan_fwd_zoh(*args)
+    else:
+        st = lib.ssm_selective_scan_fwd_variant(*args, int(variant), int(tokens_per_lane))
     _lib.check(st)
     return y, final_state
 
@@ -239,8 +248,12 @@ def selective_scan_fwd_conv(x, conv_weight, conv_bias, delta, A, B, C, D=None, z
 
 
 def state_update(state, u_t, delta_t, A, B_t, C_t, D=None, z_t=None, delta_bias=None,
-                 delta_softplus=True, *, out_state=None, y=None, stream=None) -> torch.Tensor:
-    """One decode step.  Updates `out_state` (default: `state`, in place); returns y_t [S, D]."""
+                 delta_softplus=True, *, out_state=None, y=None, discretization="simplified",
+                 stream=None) -> torch.Tensor:
+    """One decode step.  Updates `out_state` (default: `state`, in place); returns y_t [S, D].
+    `discretization` as in selective_scan_fwd."""
+    if discretization not in ("simplified", "zoh"):
+        raise ValueError(f"unknown discretization {discretization!r}")
     lib = _lib.load_library()
     S, Dc, N = state.shape
     act = u_t.dtype
@@ -249,7 +262,8 @@ def state_update(state, u_t, delta_t, A, B_t, C_t, D=None, z_t=None, delta_bias=
         out_state = state
     if y is None:
         y = torch.empty((S, Dc), dtype=act, device=dev)
-    st = lib.ssm_state_update(
+    fn = lib.ssm_state_update_zoh if discretization == "zoh" else lib.ssm_state_update
+    st = fn(
         _ptr(state, "state", torch.float32, dev), _ptr(out_state, "out_state", torch.float32, dev),
         _ptr(u_t, "u_t", act, dev), _ptr(delta_t, "delta_t", act, dev), _ptr(A, "A", torch.float32, dev),
         _ptr(B_t, "B_t", act, dev), _ptr(C_t, "C_t", act, dev), _ptr(D, "D", torch.float32, dev),

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.ssm_version() == 20300
+    assert lib.ssm_version() == 20400
     for s in range(4):
         assert lib.ssm_status_string(s).decode().startswith(("SSM_OK", "SSM_ERR"))
     assert b"unknown" in lib.ssm_status_string(99)
@@ -248,6 +248,15 @@ def test_valid_call_without_device_reports_hip_error(lib):
     assert _scan_conv(lib, u_out=F + 8 * 64 * MB, cb=F + 9 * 64 * MB) == _lib.SSM_ERR_HIP
     assert _step(lib, sout=F) == _lib.SSM_ERR_HIP          # exact in-place is valid
     assert _bwd(lib) == _lib.SSM_ERR_HIP
+    zoh = (F, F + 64 * MB, F + 2 * 64 * MB, F + 3 * 64 * MB, F + 4 * 64 * MB, None, None, None, 1, None,
+           F + 5 * 64 * MB, F + 6 * 64 * MB, 1, 64, 16, 4, 0, None)
+    assert lib.ssm_selective_scan_fwd_zoh(*zoh) == _lib.SSM_ERR_HIP
+    assert lib.ssm_selective_scan_fwd_zoh(None, *zoh[1:]) == _lib.SSM_ERR_INVALID_ARG
+    assert lib.ssm_selective_scan_fwd_zoh(*zoh[:15], 0, *zoh[16:]) == _lib.SSM_ERR_UNSUPPORTED   # N = 0
+    step = (F, F + 64 * MB, F + 2 * 64 * MB, F + 3 * 64 * MB, F + 4 * 64 * MB, F + 5 * 64 * MB, F + 6 * 64 * MB,
+            None, None, None, 1, F + 7 * 64 * MB, 4, 8, 16, 1, None)
+    assert lib.ssm_state_update_zoh(*step) == _lib.SSM_ERR_HIP
+    assert lib.ssm_state_update_zoh(*step[:11], None, *step[12:]) == _lib.SSM_ERR_INVALID_ARG   # y_t NULL
     assert _bwd(lib, z=F + 6 * 64 * MB, dz=F + 17 * 64 * MB, h0=F + 8 * 64 * MB, dh0=F + 19 * 64 * MB,
                 dfinal=F + 10 * 64 * MB, Dskip=F + 5 * 64 * MB, dD=F + 16 * 64 * MB) == _lib.SSM_ERR_HIP
     assert _bwd(lib, L=0) == _lib.SSM_ERR_HIP               # sums over no tokens still write zeros
