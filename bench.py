@@ -43,6 +43,9 @@ ALU_SLOTS_PER_ELEMENT = 6                           # 4 fp32 ops + one exp2 at h
 # over d: 2; dC term g*h and its sum: 2; abar*lam*h_{t-1}: 2, times A into dDelta: 1,
 # times Delta into dA: 1; 11 slots).
 BWD_ALU_SLOTS_PER_ELEMENT = 16
+# Full zero-order hold: the input term (e^{Delta A} - 1)/A * B * u costs u/A*B (2 ops)
+# and one FMA against the one multiply of Delta*u*B.
+ZOH_ALU_SLOTS_PER_ELEMENT = 8
 MALL_BYTES = 256 << 20
 CALIB_BYTES = 256 << 20
 DEFAULT_WORKLOAD = "mamba130m_f32"
@@ -86,10 +89,10 @@ def _oracle_shard(args):
     (batch row, channel block) shard; returns seconds."""
     os.environ.setdefault("OMP_NUM_THREADS", "1")
     import oracle
-    (u, delta, A, B, C, Dk, z, bias, sp, dy) = args
+    (u, delta, A, B, C, Dk, z, bias, sp, dy, disc) = args
     t0 = time.perf_counter()
     if dy is None:
-        oracle.selective_scan(u, delta, A, B, C, Dk, z, bias, sp)
+        oracle.selective_scan(u, delta, A, B, C, Dk, z, bias, sp, discretization=disc)
     else:
         oracle.selective_scan_bwd(u, delta, A, B, C, dy, Dk, z, bias, sp)
     return time.perf_counter() - t0
@@ -117,7 +120,8 @@ def cpu_baseline_scan(cfg, inp, budget_s=20.0, workers=0, dy=None):
     t0 = time.perf_counter()
     _oracle_shard((inp.u[:1, :d_probe], inp.delta[:1, :d_probe], inp.A[:d_probe], inp.B[:1], inp.C[:1],
                    vec(inp.Dskip, 0, d_probe), sl(inp.z, 0, 1, 0, d_probe),
-                   vec(inp.delta_bias, 0, d_probe), inp.delta_softplus, sl(dy, 0, 1, 0, d_probe)))
+                   vec(inp.delta_bias, 0, d_probe), inp.delta_softplus, sl(dy, 0, 1, 0, d_probe),
+                   cfg.discretization))
     per_row_cpu = (time.perf_counter() - t0) * cfg.D / d_probe
     b_take = max(1, min(cfg.batch, int(budget_s / max(per_row_cpu, 1e-3))))
     dblk = max(1, -(-cfg.D // max(1, (workers + b_take - 1) // b_take)))
@@ -127,7 +131,8 @@ def cpu_baseline_scan(cfg, inp, budget_s=20.0, workers=0, dy=None):
             d1 = min(cfg.D, d0 + dblk)
             shards.append((sl(inp.u, b, b + 1, d0, d1), sl(inp.delta, b, b + 1, d0, d1), inp.A[d0:d1],
                            inp.B[b:b + 1], inp.C[b:b + 1], vec(inp.Dskip, d0, d1), sl(inp.z, b, b + 1, d0, d1),
-                           vec(inp.delta_bias, d0, d1), inp.delta_softplus, sl(dy, b, b + 1, d0, d1)))
+                           vec(inp.delta_bias, d0, d1), inp.delta_softplus, sl(dy, b, b + 1, d0, d1),
+                           cfg.discretization))
     with cf.ProcessPoolExecutor(max_workers=workers, mp_context=mp.get_context("spawn")) as ex:
         list(ex.map(_oracle_warm, range(workers)))   # start the workers and import the oracle
         t0 = time.perf_counter()
@@ -139,7 +144,7 @@ def cpu_baseline_scan(cfg, inp, budget_s=20.0, workers=0, dy=None):
         wall = time.perf_counter() - t0
     elems = b_take * cfg.L * cfg.D * cfg.N
     return {"value": reps * elems / wall, "unit": "elements/s", "cores": workers, "kind": "oracle",
-            "sample": f"{'backward, ' if dy is not None else ''}{b_take} of {cfg.batch} batch rows x all {cfg.D} channels x full L={cfg.L}, N={cfg.N} "
+            "sample": f"{'backward, ' if dy is not None else ''}{cfg.discretization} discretization, {b_take} of {cfg.batch} batch rows x all {cfg.D} channels x full L={cfg.L}, N={cfg.N} "
                       f"({elems:.3e} elements), {reps}x, in {len(shards)} shards per pass over {workers} "
                       f"worker processes "
                       f"(float64 numpy, 1 thread each; {wall:.1f} s wall, {sum(secs):.1f} s CPU); "
@@ -195,7 +200,7 @@ def bench_scan(args, torch, lib_ops):
         t = bufs[i % sets]
         lib_ops.selective_scan_fwd(t["u"], t["delta"], A, t["B"], t["C"], Dk, t["z"], bias, True,
                                    y=t["y"], final_state=t["fs"], variant=args.variant,
-                                   tokens_per_lane=args.kpl)
+                                   tokens_per_lane=args.kpl, discretization=cfg.discretization)
 
     return cfg, inp, nbytes, cfg.elements, sets, step, bufs
 
@@ -335,7 +340,8 @@ def main():
         # issues at half the VALU rate (2 slots), against 256 CUs x 4 SIMDs x 16 lanes
         # x 2.4 GHz single-issue fp32 slots (the backward: BWD_ALU_SLOTS_PER_ELEMENT,
         # over the whole call of its five kernels).
-        spe = BWD_ALU_SLOTS_PER_ELEMENT if kind == "bwd" else ALU_SLOTS_PER_ELEMENT
+        spe = (BWD_ALU_SLOTS_PER_ELEMENT if kind == "bwd" else
+               ZOH_ALU_SLOTS_PER_ELEMENT if cfg.discretization == "zoh" else ALU_SLOTS_PER_ELEMENT)
         slots = spe * elements
         alu = slots / launch_s / 1e12
         roofline = {"bound": "alu", "kernel": KERNEL_NAME[kind],
@@ -362,7 +368,8 @@ def main():
         "dtype": "f32",
         "data": "synthetic (seeded; shapes and distributions of the named workload)",
         "config": ({"workload": args.workload, "batch": cfg.batch, "L": cfg.L, "D": cfg.D, "N": cfg.N,
-                    "act_dtype": cfg.dtype, "gate": cfg.gate, "conv_width": cfg.conv_k, "variant": args.variant,
+                    "act_dtype": cfg.dtype, "gate": cfg.gate, "conv_width": cfg.conv_k,
+                    "discretization": cfg.discretization, "variant": args.variant,
                     "tokens_per_lane": args.kpl or "auto", "graph": graph is not None, "input_copies": sets}
                    if kind != "decode" else
                    {"workload": args.workload, "sequences": cfg.batch, "D": cfg.D, "N": cfg.N,

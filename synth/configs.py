@@ -21,6 +21,7 @@ class ScanConfig:
     seed: int = 0
     conv_k: int = 0     # > 0: the input is x and u = SiLU(causal conv1d of width conv_k) is fused in
     backward: bool = False  # the workload is the backward pass (gradients for dy) instead of the forward
+    discretization: str = "simplified"   # or "zoh": the full zero-order-hold input term
 
     @property
     def elements(self) -> int:
@@ -81,6 +82,11 @@ CONFIGS = {
                                      conv_k=4),
     "mamba1p4b_conv_bf16": ScanConfig("mamba1p4b_conv_bf16", 8, 2048, 4096, 16, "bf16", gate=True,
                                       d_skip="ones", conv_k=4),
+    # the full zero-order-hold discretization at the forward workloads' shapes
+    "zoh_mamba130m_f32": ScanConfig("zoh_mamba130m_f32", 2, 2048, 1536, 16, "f32", gate=True, d_skip="ones",
+                                    discretization="zoh"),
+    "zoh_mamba1p4b_bf16": ScanConfig("zoh_mamba1p4b_bf16", 8, 2048, 4096, 16, "bf16", gate=True, d_skip="ones",
+                                     discretization="zoh"),
     # the backward pass (training) at the forward workloads' shapes, for an output gradient dy
     "bwd_mamba130m_f32": ScanConfig("bwd_mamba130m_f32", 2, 2048, 1536, 16, "f32", gate=True, d_skip="ones",
                                     backward=True),
