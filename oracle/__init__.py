@@ -5,3 +5,4 @@ package: only the tests, the smoke check and the benchmark's CPU-baseline leg us
 it.  It shares no code with the HIP library and does not import it.
 """
 from .ssm import selective_scan, selective_scan_bwd, state_update, softplus, silu, causal_conv1d  # noqa: F401
+from .ssd import ssd_scan, ssd_step  # noqa: F401

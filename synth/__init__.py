@@ -13,6 +13,8 @@ from .gen import (  # noqa: F401
     make_config_inputs,
     make_scan_initial_state,
     make_scan_cotangents,
+    SSDInputs,
+    make_ssd_inputs,
     make_conv_params,
     make_decode_state,
     make_decode_step,

@@ -199,6 +199,58 @@ def make_scan_cotangents(batch: int, L: int, D: int, N: int, dtype: str = "f32",
     return vals, up, dfin
 
 
+_SSD_STREAMS = ("x", "dt", "dt0", "A", "B", "C", "D", "h0")
+_SSD_KEY = 7
+
+
+@dataclass
+class SSDInputs:
+    """Inputs of the Mamba-2 SSD scan (float32 values as the device receives them, and
+    upload arrays).  Layouts: x [batch][L][H][P]; dt [batch][L][H]; B, C [batch][L][N];
+    A, D, dt_bias [H]; h0 [batch][H][P][N]."""
+    batch: int
+    L: int
+    H: int
+    P: int
+    N: int
+    dtype: str
+    x: np.ndarray
+    dt: np.ndarray
+    A: np.ndarray
+    B: np.ndarray
+    C: np.ndarray
+    D: Optional[np.ndarray]
+    dt_bias: Optional[np.ndarray]
+    h0: Optional[np.ndarray] = None
+    dev: dict = field(default_factory=dict)
+
+
+def make_ssd_inputs(batch: int, L: int, H: int, P: int, N: int, dtype: str = "bf16", seed: int = 0,
+                    with_h0: bool = False, with_D: bool = True, with_bias: bool = True) -> SSDInputs:
+    """Seeded SSD inputs: x, B, C ~ N(0, 1); raw dt ~ N(0, 0.5^2) plus the per-head bias
+    log(expm1(dt0)) with dt0 log-uniform in [1e-3, 1e-1] (the Mamba-1 recipe); the
+    per-head decay A = -U[1, 16]; D = 1; h0 ~ N(0, 1) when asked.  Child streams of
+    SeedSequence([seed, 7]) in the order x, dt, dt0, A, B, C, D, h0."""
+    ss = np.random.SeedSequence([seed, _SSD_KEY])
+    kids = dict(zip(_SSD_STREAMS, ss.spawn(len(_SSD_STREAMS))))
+    rng = {k: np.random.Generator(np.random.PCG64(v)) for k, v in kids.items()}
+    x32 = rng["x"].standard_normal((batch, L, H, P), dtype=np.float32)
+    dt32 = rng["dt"].standard_normal((batch, L, H), dtype=np.float32) * np.float32(0.5)
+    dt0 = np.exp(rng["dt0"].uniform(np.log(1e-3), np.log(1e-1), size=H))
+    bias = np.log(np.expm1(dt0)).astype(np.float32) if with_bias else None
+    A = (-rng["A"].uniform(1.0, 16.0, size=H)).astype(np.float32)
+    B32 = rng["B"].standard_normal((batch, L, N), dtype=np.float32)
+    C32 = rng["C"].standard_normal((batch, L, N), dtype=np.float32)
+    Dv = np.ones(H, dtype=np.float32) if with_D else None
+    h0 = rng["h0"].standard_normal((batch, H, P, N), dtype=np.float32) if with_h0 else None
+    out = SSDInputs(batch, L, H, P, N, dtype, None, None, A, None, None, Dv, bias, h0)
+    for name, v in (("x", x32), ("dt", dt32), ("B", B32), ("C", C32)):
+        vals, up = _act(v, dtype)
+        setattr(out, name, vals)
+        out.dev[name] = up
+    return out
+
+
 def make_config_inputs(cfg, seed: Optional[int] = None, **kw) -> ScanInputs:
     """Inputs of a named scan workload (see synth.configs)."""
     return make_scan_inputs(cfg.batch, cfg.L, cfg.D, cfg.N, cfg.dtype, gate=cfg.gate,
