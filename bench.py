@@ -51,9 +51,12 @@ CALIB_BYTES = 256 << 20
 DEFAULT_WORKLOAD = "mamba130m_f32"
 KERNEL_SRC = {"scan": "selective_state_space_68_amd/csrc/scan_chunked.hip",
               "decode": "selective_state_space_68_amd/csrc/state_update.hip",
-              "bwd": "selective_state_space_68_amd/csrc/scan_bwd.hip"}
+              "bwd": "selective_state_space_68_amd/csrc/scan_bwd.hip",
+              "ssd": "selective_state_space_68_amd/csrc/ssd.hip"}
 KERNEL_NAME = {"scan": "scan_chunked_kernel", "decode": "state_update_vec_kernel",
-               "bwd": "scan backward call (bwd_summary, bwd_combine, bwd_main, bwd_param_sums, bwd_bc_out kernels)"}
+               "bwd": "scan backward call (bwd_summary, bwd_combine, bwd_main, bwd_param_sums, bwd_bc_out kernels)",
+               "ssd": "ssd_scan_kernel"}
+PEAK_MFMA_BF16_TFLOPS = 2500.0
 
 
 def src_hash(kind):
@@ -228,6 +231,46 @@ def bench_decode(args, torch, lib_ops):
     return cfg, None, nbytes, cfg.elements_per_step, sets, step, bufs
 
 
+def bench_ssd(args, torch, lib_ops):
+    cfg = synth.CONFIGS[args.workload]
+    inp = synth.make_ssd_inputs(cfg.batch, cfg.L, cfg.H, cfg.P, cfg.N, cfg.dtype, seed=cfg.seed)
+    nbytes = cfg.algorithmic_bytes()
+    sets = args.sets or max(2, int(np.ceil(600e6 / nbytes)))
+    A, Dk, bias = dev(torch, inp.A), dev(torch, inp.D), dev(torch, inp.dt_bias)
+    bufs = []
+    for _ in range(sets):
+        t = {k: dev(torch, inp.dev[k]) for k in ("x", "dt", "B", "C")}
+        t["y"] = torch.empty_like(t["x"])
+        t["fs"] = torch.empty((cfg.batch, cfg.H, cfg.P, cfg.N), dtype=torch.float32, device="cuda")
+        bufs.append(t)
+
+    def step(i):
+        t = bufs[i % sets]
+        lib_ops.ssd_scan_fwd(t["x"], t["dt"], A, t["B"], t["C"], Dk, bias, True, y=t["y"], final_state=t["fs"])
+
+    return cfg, inp, nbytes, cfg.elements, sets, step, bufs
+
+
+def cpu_baseline_ssd(cfg, inp, budget_s=20.0):
+    """The float64 SSD oracle, as it is, on one process: whole heads of one batch row,
+    as many as fit in about budget_s."""
+    import oracle
+    t0 = time.perf_counter()
+    oracle.ssd_scan(inp.x[:1, :, :1], inp.dt[:1, :, :1], inp.A[:1], inp.B[:1], inp.C[:1], inp.D[:1],
+                    inp.dt_bias[:1])
+    per_head = time.perf_counter() - t0
+    heads = max(1, min(cfg.H, int(budget_s / max(per_head, 1e-3))))
+    t0 = time.perf_counter()
+    oracle.ssd_scan(inp.x[:1, :, :heads], inp.dt[:1, :, :heads], inp.A[:heads], inp.B[:1], inp.C[:1],
+                    inp.D[:heads], inp.dt_bias[:heads])
+    wall = time.perf_counter() - t0
+    elems = cfg.L * heads * cfg.P * cfg.N
+    return {"value": elems / wall, "unit": "elements/s", "cores": 1, "kind": "oracle",
+            "sample": f"SSD, 1 of {cfg.batch} batch rows x {heads} of {cfg.H} heads x full L={cfg.L}, "
+                      f"P={cfg.P}, N={cfg.N} ({elems:.3e} elements), float64 numpy, one process, "
+                      f"{wall:.1f} s"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -254,7 +297,9 @@ def main():
     torch.cuda.set_device(0)
     kind = "decode" if args.workload.startswith("decode") else "scan"
     maker = bench_decode if kind == "decode" else bench_scan
-    if kind == "scan" and synth.CONFIGS[args.workload].backward:
+    if isinstance(synth.CONFIGS[args.workload], synth.SSDConfig):
+        kind, maker = "ssd", bench_ssd
+    elif kind == "scan" and synth.CONFIGS[args.workload].backward:
         kind = "bwd"
     cfg, inp, nbytes, elements, sets, step, bufs = maker(args, torch, lib_ops)
     print(f"# workload {args.workload}: {elements:.3e} elements/step, {nbytes / 1e6:.2f} MB/step "
@@ -292,12 +337,12 @@ def main():
             step(warm)
             warm += 1
     torch.cuda.synchronize()
-    if graph is not None and kind in ("scan", "bwd"):
+    if graph is not None and kind in ("scan", "bwd", "ssd"):
         # the replayed outputs must equal an eager call's, bit for bit
         if warm == 0:
             graph.replay()
             torch.cuda.synchronize()
-        if kind == "scan":
+        if kind in ("scan", "ssd"):
             get = lambda: {k: bufs[(K - 1) % sets][k] for k in ("y", "fs")}
         else:
             get = lambda: {k: bufs[(K - 1) % sets]["g"][k] for k in ("du", "ddelta", "dz", "dA", "dB", "dC", "dD")}
@@ -329,7 +374,9 @@ def main():
     hbm_gbs = nbytes / launch_s / 1e9
 
     cpu = None
-    if kind in ("scan", "bwd") and not args.no_cpu_baseline and not cfg.conv_k:
+    if kind == "ssd" and not args.no_cpu_baseline:
+        cpu = cpu_baseline_ssd(cfg, inp, args.cpu_budget)
+    elif kind in ("scan", "bwd") and not args.no_cpu_baseline and not cfg.conv_k:
         cpu = cpu_baseline_scan(cfg, inp, args.cpu_budget, dy=getattr(inp, "dy", None))
 
     traffic = traffic_from_profiles(args.workload, kind)
@@ -352,8 +399,14 @@ def main():
     else:
         roofline = dict(hbm, bound="hbm", kernel=KERNEL_NAME[kind], traffic=traffic,
                         avg_launch_us=launch_s * 1e6)
+        if kind == "ssd":
+            # the matrix-core side, for reference: the chunked form's products
+            fl = cfg.flops()
+            roofline["mfma"] = {"achieved": fl / launch_s / 1e12, "peak": PEAK_MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
+                                "frac": fl / launch_s / 1e12 / PEAK_MFMA_BF16_TFLOPS, "flops_per_launch": fl}
     out = {
         "metric": {"scan": "selective-scan elements/s (B*L*D*N) + achieved HBM GB/s vs peak, 1 GPU",
+                   "ssd": "SSD-scan elements/s (B*L*H*P*N) + achieved HBM GB/s vs peak, 1 GPU",
                    "bwd": "selective-scan backward elements/s (B*L*D*N) + achieved HBM GB/s vs peak, 1 GPU",
                    "decode": "decode-step elements/s (S*D*N per step) + achieved HBM GB/s vs peak, 1 GPU"}[kind],
         "value": value,
@@ -365,13 +418,16 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16" if kind == "ssd" else "f32",
         "data": "synthetic (seeded; shapes and distributions of the named workload)",
         "config": ({"workload": args.workload, "batch": cfg.batch, "L": cfg.L, "D": cfg.D, "N": cfg.N,
                     "act_dtype": cfg.dtype, "gate": cfg.gate, "conv_width": cfg.conv_k,
                     "discretization": cfg.discretization, "variant": args.variant,
                     "tokens_per_lane": args.kpl or "auto", "graph": graph is not None, "input_copies": sets}
-                   if kind != "decode" else
+                   if kind in ("scan", "bwd") else
+                   {"workload": args.workload, "batch": cfg.batch, "L": cfg.L, "H": cfg.H, "P": cfg.P, "N": cfg.N,
+                    "act_dtype": cfg.dtype, "chunk": 64, "graph": graph is not None, "input_copies": sets}
+                   if kind == "ssd" else
                    {"workload": args.workload, "sequences": cfg.batch, "D": cfg.D, "N": cfg.N,
                     "act_dtype": cfg.dtype, "graph": graph is not None, "input_copies": sets}),
         "roofline": roofline,

@@ -268,6 +268,48 @@ ssm_status ssm_selective_scan_bwd(
     int64_t batch, int64_t L, int64_t D, int64_t N, ssm_dtype dt,
     void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Mamba-2 SSD scan: a scalar decay per head (the slide deck's "Mamba-2" table; the
+ * interview-prep page's "Mamba-2 and State Space Duality").  For batch b, time t,
+ * head h, head channel p and state n:
+ *
+ *   Delta[b,t,h] = softplus(dt[b,t,h] + dt_bias[h])    (or without softplus)
+ *   H[b,t,h,p,n] = exp(Delta*A[h]) * H[b,t-1,h,p,n] + Delta * x[b,t,h,p] * B[b,t,n]
+ *   y[b,t,h,p]   = sum_n C[b,t,n] * H[b,t,h,p,n] + Dskip[h] * x[b,t,h,p]
+ *
+ * computed in its chunk-parallel form on the matrix cores (chunks of 64 tokens: the
+ * masked quadratic form inside a chunk, the P x N state carried between chunks).
+ *
+ *   x, y          : [batch][L][H][P] bf16 (the pages' (batch, L, D) order, D = H*P)
+ *   dt            : [batch][L][H] bf16 (raw; bias and softplus applied inside)
+ *   A             : [H] float32 (nonpositive in the models)
+ *   Bm, Cm        : [batch][L][N] bf16, shared by all heads
+ *   Dskip, dt_bias: [H] float32 or NULL (= 0)
+ *   initial_state : [batch][H][P][N] float32 or NULL (= 0)
+ *   final_state   : out [batch][H][P][N] float32 or NULL; may be the initial_state
+ *                   pointer (updated in place) but must not otherwise overlap it
+ * Supported: dtype SSM_BF16, P == 64, N in {64, 128} (SSM_ERR_UNSUPPORTED otherwise).
+ * x, y, Bm, Cm, the states and the workspace must be 16-byte aligned.  The products
+ * run in bfloat16 with float32 accumulation and a float32 state (the carried-state
+ * product uses the state as two bfloat16 terms); y is rounded to bfloat16.
+ *
+ * Workspace: with workspace_bytes >= ssm_ssd_scan_workspace_size(...) (owned by the
+ * caller, contents irrelevant) the sequences are cut into segments that run in
+ * parallel (a pre-pass computes each segment's end state); with NULL / 0 each
+ * sequence runs as one segment (slower at few heads x batch rows, same results up to
+ * rounding).  A size query of 0 means no workspace helps for that shape.
+ * Errors as for ssm_selective_scan_fwd; also SSM_ERR_INVALID_ARG for a workspace
+ * overlapping any other argument.  Deterministic for a given workspace size.
+ */
+size_t ssm_ssd_scan_workspace_size(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, ssm_dtype dtype);
+
+ssm_status ssm_ssd_scan_fwd(
+    const void *x, const void *dt, const float *A, const void *Bm, const void *Cm,
+    const float *Dskip, const float *dt_bias, int dt_softplus,
+    const float *initial_state, void *y, float *final_state,
+    int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, ssm_dtype dtype,
+    void *workspace, size_t workspace_bytes, void *stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char *ssm_status_string(ssm_status s);
 

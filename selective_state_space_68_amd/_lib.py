@@ -49,6 +49,9 @@ SIGNATURES = {
     "ssm_selective_scan_bwd": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _vp, _vp, _vp,
                                       _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                       _i64, _i64, _i64, _i64, _int, _vp, ctypes.c_size_t, _vp]),
+    "ssm_ssd_scan_workspace_size": (ctypes.c_size_t, [_i64, _i64, _i64, _i64, _i64, _int]),
+    "ssm_ssd_scan_fwd": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _vp, _vp, _vp,
+                                _i64, _i64, _i64, _i64, _i64, _int, _vp, ctypes.c_size_t, _vp]),
     "ssm_status_string": (ctypes.c_char_p, [_int]),
     "ssm_version": (_int, []),
 }

@@ -86,6 +86,34 @@ struct BwdArgs {
   int softplus;
 };
 
+struct SsdArgs {
+  const void* x;          // [batch][L][H][P] bf16
+  const void* dt;         // [batch][L][H] bf16 (raw)
+  const float* A;         // [H]
+  const void* Bm;         // [batch][L][N] bf16
+  const void* Cm;         // [batch][L][N] bf16
+  const float* Dskip;     // [H] or null
+  const float* dt_bias;   // [H] or null
+  const float* h0;        // [batch][H][P][N] or null
+  void* y;                // [batch][L][H][P] bf16
+  float* final_state;     // [batch][H][P][N] or null
+  int64_t batch, L, H;
+  int P, N;
+  int softplus;
+  // set by the launcher: segments per sequence, chunks per segment, the workspace
+  int nseg = 1;
+  int64_t seg_chunks = 0;
+  float* seg_state = nullptr;   // [batch][H][nseg][P][N]
+  float* seg_decay = nullptr;   // [batch][H][nseg]
+};
+
+// Mamba-2 SSD scan on the matrix cores (P == 64, N in {64, 128}, bfloat16).  A
+// workspace of ssd_workspace_bytes lets the sequence run as parallel segments;
+// without it (NULL or too small) one segment per sequence.
+bool ssd_supported(int64_t P, int64_t N);
+size_t ssd_workspace_bytes(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N);
+hipError_t launch_ssd_scan(const SsdArgs& a, void* ws, size_t ws_bytes, hipStream_t s);
+
 // One thread per (b, d) channel, sequential over time.  Any N in [1, 64].
 hipError_t launch_scan_sequential(const ScanArgs& a, Dt dt, hipStream_t s);
 

@@ -11,7 +11,7 @@
 
 namespace {
 
-constexpr int kVersion = 20400;  // 2.4.0: + full zero-order-hold discretization
+constexpr int kVersion = 20500;  // 2.5.0: + Mamba-2 SSD scan
 
 struct Span {
   uintptr_t lo = 0, hi = 0;  // [lo, hi); empty when lo == hi
@@ -97,6 +97,62 @@ ssm_status check_scan(const void* u, const void* delta, const float* A, const vo
 }  // namespace
 
 extern "C" {
+
+size_t ssm_ssd_scan_workspace_size(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, ssm_dtype dtype) {
+  if (dtype != SSM_BF16 || !ssm::ssd_supported(P, N) || batch <= 0 || L <= 0 || H <= 0) return 0;
+  uint64_t t;
+  if (!mul_ok(batch, H, &t) || !mul_ok(t, L, &t) || t > (uint64_t(1) << 50)) return 0;
+  return ssm::ssd_workspace_bytes(batch, L, H, P, N);
+}
+
+ssm_status ssm_ssd_scan_fwd(const void* x, const void* dt, const float* A, const void* Bm, const void* Cm,
+                            const float* Dskip, const float* dt_bias, int dt_softplus, const float* initial_state,
+                            void* y, float* final_state, int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N,
+                            ssm_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (dtype != SSM_F32 && dtype != SSM_BF16) return SSM_ERR_UNSUPPORTED;
+  if (batch < 0 || L < 0 || H < 0 || P < 0 || N < 0) return SSM_ERR_INVALID_ARG;
+  if (dt_softplus != 0 && dt_softplus != 1) return SSM_ERR_INVALID_ARG;
+  if (dtype != SSM_BF16 || !ssm::ssd_supported(P, N)) return SSM_ERR_UNSUPPORTED;
+  uint64_t blh, xe, xbytes, dtbytes, bl, bcbytes, bh, st, stbytes;
+  if (!mul_ok(batch, L, &blh) || !mul_ok(blh, H, &blh) || !mul_ok(blh, P, &xe) || !mul_ok(xe, 2, &xbytes) ||
+      !mul_ok(batch, L, &bl) || !mul_ok(bl, H, &dtbytes) || !mul_ok(dtbytes, 2, &dtbytes) ||
+      !mul_ok(bl, N, &bcbytes) || !mul_ok(bcbytes, 2, &bcbytes) || !mul_ok(batch, H, &bh) ||
+      !mul_ok(bh, P * N, &st) || !mul_ok(st, 4, &stbytes) || xbytes > (uint64_t(1) << 62))
+    return SSM_ERR_INVALID_ARG;
+  const uint64_t hbytes = static_cast<uint64_t>(H) * 4;
+  if ((!x && xbytes) || (!y && xbytes) || (!dt && dtbytes) || (!Bm && bcbytes) || (!Cm && bcbytes) ||
+      (!A && hbytes))
+    return SSM_ERR_INVALID_ARG;
+  // the kernel moves 16-byte vectors of x, y, B, C and the states
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(Bm, 16) || !aligned(Cm, 16) || !aligned(dt, 2) ||
+      !aligned(A, 4) || !aligned(Dskip, 4) || !aligned(dt_bias, 4) || !aligned(initial_state, 16) ||
+      !aligned(final_state, 16) || !aligned(workspace, 16))
+    return SSM_ERR_INVALID_ARG;
+  if (workspace_bytes && !workspace) return SSM_ERR_INVALID_ARG;
+  const Span ys = span(y, xbytes), fs = span(final_state, stbytes), hs = span(initial_state, stbytes);
+  const Span in[] = {span(x, xbytes),       span(dt, dtbytes),     span(A, hbytes),    span(Bm, bcbytes),
+                     span(Cm, bcbytes),     span(Dskip, hbytes),   span(dt_bias, hbytes)};
+  for (const Span& s : in)
+    if (overlaps(ys, s) || overlaps(fs, s) || overlaps(hs, s)) return SSM_ERR_INVALID_ARG;
+  if (overlaps(ys, fs) || overlaps(ys, hs)) return SSM_ERR_INVALID_ARG;
+  // the final state may replace the initial state in place, but not partly overlap it
+  if (overlaps(hs, fs) && initial_state != final_state) return SSM_ERR_INVALID_ARG;
+  const Span wsp = span(workspace, workspace_bytes);
+  for (const Span& s : in)
+    if (overlaps(wsp, s)) return SSM_ERR_INVALID_ARG;
+  if (overlaps(wsp, ys) || overlaps(wsp, fs) || overlaps(wsp, hs)) return SSM_ERR_INVALID_ARG;
+  if (batch == 0 || H == 0) return SSM_OK;
+  const ssm_status ds = probe_device();
+  if (ds != SSM_OK) return ds;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (L == 0)
+    return final_state ? from_hip(ssm::launch_copy_state(final_state, initial_state, batch * H * P * N, s)) : SSM_OK;
+  ssm::SsdArgs a;
+  a.x = x; a.dt = dt; a.A = A; a.Bm = Bm; a.Cm = Cm; a.Dskip = Dskip; a.dt_bias = dt_bias; a.h0 = initial_state;
+  a.y = y; a.final_state = final_state;
+  a.batch = batch; a.L = L; a.H = H; a.P = static_cast<int>(P); a.N = static_cast<int>(N); a.softplus = dt_softplus;
+  return from_hip(ssm::launch_ssd_scan(a, workspace, workspace_bytes, s));
+}
 
 const char* ssm_status_string(ssm_status s) {
   switch (s) {

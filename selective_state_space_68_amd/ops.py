@@ -183,6 +183,54 @@ def selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, d
     return out
 
 
+def ssd_scan_workspace_size(batch, L, H, P, N) -> int:
+    """Bytes of workspace that let ssd_scan_fwd run sequences as parallel segments."""
+    lib = _lib.load_library()
+    return int(lib.ssm_ssd_scan_workspace_size(int(batch), int(L), int(H), int(P), int(N), _lib.SSM_BF16))
+
+
+def ssd_scan_fwd(x, dt, A, B, C, D=None, dt_bias=None, dt_softplus=True, *, initial_state=None, y=None,
+                 final_state=None, return_final_state=True, workspace="auto", stream=None):
+    """Mamba-2 SSD scan.  x [batch, L, H, P] bf16; dt [batch, L, H] bf16; A [H] float32;
+    B, C [batch, L, N] bf16; D, dt_bias [H] float32.  Returns (y [batch, L, H, P],
+    final_state [batch, H, P, N] float32 or None).  `workspace`: a device tensor of at
+    least ssd_scan_workspace_size(...) bytes, None (one segment per sequence), or
+    "auto" (allocated here)."""
+    lib = _lib.load_library()
+    if x.dim() != 4 or B.dim() != 3:
+        raise ValueError("expected x [batch, L, H, P] and B/C [batch, L, N]")
+    batch, L, H, P = x.shape
+    N = B.shape[2]
+    act, dev = x.dtype, x.device
+    if tuple(dt.shape) != (batch, L, H) or tuple(A.shape) != (H,):
+        raise ValueError("dt must be [batch, L, H] and A [H]")
+    if tuple(B.shape) != (batch, L, N) or tuple(C.shape) != (batch, L, N):
+        raise ValueError("B / C must be [batch, L, N]")
+    for name, v in (("D", D), ("dt_bias", dt_bias)):
+        if v is not None and tuple(v.shape) != (H,):
+            raise ValueError(f"{name} must be [H]")
+    if initial_state is not None and tuple(initial_state.shape) != (batch, H, P, N):
+        raise ValueError("initial_state must be [batch, H, P, N]")
+    if y is None:
+        y = torch.empty((batch, L, H, P), dtype=act, device=dev)
+    if final_state is None and return_final_state:
+        final_state = torch.empty((batch, H, P, N), dtype=torch.float32, device=dev)
+    f32 = torch.float32
+    if isinstance(workspace, str):
+        need = ssd_scan_workspace_size(batch, L, H, P, N)
+        workspace = torch.empty((need,), dtype=torch.uint8, device=dev) if need else None
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.ssm_ssd_scan_fwd(
+        _ptr(x, "x", act, dev), _ptr(dt, "dt", act, dev), _ptr(A, "A", f32, dev), _ptr(B, "B", act, dev),
+        _ptr(C, "C", act, dev), _ptr(D, "D", f32, dev), _ptr(dt_bias, "dt_bias", f32, dev),
+        1 if dt_softplus else 0, _ptr(initial_state, "initial_state", f32, dev), _ptr(y, "y", act, dev),
+        _ptr(final_state, "final_state", f32, dev), batch, L, H, P, N, _dt(x), ws_ptr, ws_bytes,
+        _stream(stream))
+    _lib.check(st)
+    return y, final_state
+
+
 def causal_conv1d(x, weight, bias=None, silu=True, *, out=None, stream=None) -> torch.Tensor:
     """Causal depthwise conv1d along L (+ SiLU).  x [batch, D, L]; weight [D, K] float32
     (K <= 4, weight[:, K-1] weighs the current token); bias [D] or None."""

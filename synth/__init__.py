@@ -20,4 +20,4 @@ from .gen import (  # noqa: F401
     make_decode_step,
     make_decode_params,
 )
-from .configs import CONFIGS, ScanConfig, DecodeConfig  # noqa: F401
+from .configs import CONFIGS, ScanConfig, DecodeConfig, SSDConfig  # noqa: F401

@@ -71,6 +71,41 @@ class DecodeConfig:
                 + 4 * self.D * self.N + 8 * self.D)    # A, D skip, bias
 
 
+@dataclass(frozen=True)
+class SSDConfig:
+    """A Mamba-2 SSD scan workload (scalar decay per head, P x N state per head)."""
+    name: str
+    batch: int
+    L: int
+    H: int
+    P: int
+    N: int
+    dtype: str = "bf16"
+    seed: int = 0
+
+    @property
+    def elements(self) -> int:
+        """Recurrence elements B*L*H*P*N (one state-entry update each)."""
+        return self.batch * self.L * self.H * self.P * self.N
+
+    def algorithmic_bytes(self) -> int:
+        """x read and y written, dt, B, C read, A, D, bias read, the final state written."""
+        e = 2
+        return (2 * self.batch * self.L * self.H * self.P * e + self.batch * self.L * self.H * e
+                + 2 * self.batch * self.L * self.N * e + 12 * self.H
+                + 4 * self.batch * self.H * self.P * self.N)
+
+    def flops(self, chunk: int = 64) -> int:
+        """Matrix-core work of the chunked form per call: per (batch, head, chunk) the
+        products C B^T (Q x Q x N), its masked product with x (Q x P x Q), the chunk's
+        state contribution (N x P x Q) and the carried-state output (Q x P x N), 2 flops
+        per multiply-add."""
+        nch = -(-self.L // chunk)
+        Q = chunk
+        per = Q * Q * self.N + Q * self.P * Q + self.N * self.P * Q + Q * self.P * self.N
+        return 2 * per * self.batch * self.H * nch
+
+
 CONFIGS = {
     "tiny_f32": ScanConfig("tiny_f32", 1, 64, 16, 4, "f32", gate=False, d_skip="normal"),
     "mamba130m_f32": ScanConfig("mamba130m_f32", 2, 2048, 1536, 16, "f32", gate=True, d_skip="ones"),
@@ -87,6 +122,9 @@ CONFIGS = {
                                     discretization="zoh"),
     "zoh_mamba1p4b_bf16": ScanConfig("zoh_mamba1p4b_bf16", 8, 2048, 4096, 16, "bf16", gate=True, d_skip="ones",
                                      discretization="zoh"),
+    # Mamba-2 SSD at a 2.7B-shaped layer: d_model 2560 (the prep page's model card),
+    # expanded 2x to 5120 channels = 80 heads of 64, state 64 per head channel
+    "ssd_2p7b_bf16": SSDConfig("ssd_2p7b_bf16", 4, 2048, 80, 64, 64),
     # the backward pass (training) at the forward workloads' shapes, for an output gradient dy
     "bwd_mamba130m_f32": ScanConfig("bwd_mamba130m_f32", 2, 2048, 1536, 16, "f32", gate=True, d_skip="ones",
                                     backward=True),

@@ -1,0 +1,141 @@
+"""GPU parity of the Mamba-2 SSD scan (ssm_ssd_scan_fwd, MFMA chunked form) against
+the float64 oracle (oracle.ssd_scan: the plain recurrence, pinned to the selective
+scan, the quadratic dual form and a chunked evaluation in test_oracle_ssd.py).
+
+Rows of the metric: one (b, h, p) output time series; one (b, h, p) state row.
+Tolerance 2e-2 (bfloat16 inputs and output; the products run in bfloat16 with
+float32 accumulation).  Shapes cover one chunk, ragged tails, L = 1, both state
+sizes, a given initial state updated in place, missing skip and bias, softplus
+off, and the full-size workload on sampled heads.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import TOL, dev, host
+from ssm_metrics import row_rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from selective_state_space_68_amd import load_library
+    load_library()
+
+
+def _run(inp, h0=None, in_place=False, softplus=True):
+    import torch
+    from selective_state_space_68_amd import ssd_scan_fwd
+    h = dev(h0)
+    y, fs = ssd_scan_fwd(dev(inp.dev["x"]), dev(inp.dev["dt"]), dev(inp.A), dev(inp.dev["B"]), dev(inp.dev["C"]),
+                         dev(inp.D), dev(inp.dt_bias), softplus, initial_state=h,
+                         final_state=h if in_place else None)
+    torch.cuda.synchronize()
+    return host(y), host(fs)
+
+
+def _check(y, fs, ry, rf, what):
+    B, L, H, P = ry.shape
+    ey = row_rel_err(y.transpose(0, 2, 3, 1), ry.transpose(0, 2, 3, 1))
+    ef = row_rel_err(fs, rf)
+    print(f"ssd {what}: y_err={ey:.2e} state_err={ef:.2e}", flush=True)
+    assert ey <= TOL["bf16"] and ef <= TOL["bf16"], (what, ey, ef)
+
+
+@pytest.mark.parametrize("batch,L,H,N,kw", [
+    (1, 64, 2, 64, dict()),
+    (2, 200, 3, 64, dict(h0=True)),
+    (1, 1, 2, 128, dict()),
+    (2, 517, 4, 128, dict(h0=True, in_place=True)),
+    (1, 300, 2, 64, dict(no_skip=True)),
+    (1, 256, 3, 64, dict(softplus=False)),
+])
+def test_ssd_matches_oracle(batch, L, H, N, kw):
+    inp = synth.make_ssd_inputs(batch, L, H, 64, N, "bf16", seed=L + H, with_h0=kw.get("h0", False),
+                                with_D=not kw.get("no_skip"), with_bias=not kw.get("no_skip"))
+    sp = kw.get("softplus", True)
+    if not sp:
+        # without the softplus the step must be positive (A < 0 then decays)
+        inp.dt = np.abs(inp.dt)
+        inp.dev["dt"] = synth.bf16_bits_from_f32(inp.dt)
+        inp.dt_bias = None
+    y, fs = _run(inp, inp.h0, kw.get("in_place", False), sp)
+    ry, rf = oracle.ssd_scan(inp.x, inp.dt, inp.A, inp.B, inp.C, inp.D, inp.dt_bias, sp, h0=inp.h0)
+    _check(y, fs, ry, rf, f"b={batch} L={L} H={H} N={N} {kw}")
+
+
+def test_ssd_chained_pieces_equal_one_scan():
+    # scanning in two pieces through the in-place state equals one scan
+    import torch
+    from selective_state_space_68_amd import ssd_scan_fwd
+    inp = synth.make_ssd_inputs(1, 384, 2, 64, 64, "bf16", seed=5)
+    t = {k: dev(inp.dev[k]) for k in ("x", "dt", "B", "C")}
+    A, Dk, bias = dev(inp.A), dev(inp.D), dev(inp.dt_bias)
+    y_all, f_all = ssd_scan_fwd(t["x"], t["dt"], A, t["B"], t["C"], Dk, bias, True)
+    st = torch.zeros((1, 2, 64, 64), dtype=torch.float32, device="cuda")
+    ys = []
+    for a, b in ((0, 200), (200, 384)):
+        y, _ = ssd_scan_fwd(t["x"][:, a:b].contiguous(), t["dt"][:, a:b].contiguous(), A,
+                            t["B"][:, a:b].contiguous(), t["C"][:, a:b].contiguous(), Dk, bias, True,
+                            initial_state=st, final_state=st)
+        ys.append(y)
+    torch.cuda.synchronize()
+    y2 = torch.cat(ys, dim=1)
+    ry, rf = oracle.ssd_scan(inp.x, inp.dt, inp.A, inp.B, inp.C, inp.D, inp.dt_bias)
+    _check(host(y2), host(st), ry, rf, "two pieces")
+    _check(host(y_all), host(f_all), ry, rf, "one scan")
+
+
+def test_ssd_full_workload_sampled_heads():
+    import torch
+    from selective_state_space_68_amd import ssd_scan_fwd
+    cfg = synth.CONFIGS["ssd_2p7b_bf16"]
+    inp = synth.make_ssd_inputs(cfg.batch, cfg.L, cfg.H, cfg.P, cfg.N, "bf16", seed=cfg.seed)
+    y, fs = ssd_scan_fwd(dev(inp.dev["x"]), dev(inp.dev["dt"]), dev(inp.A), dev(inp.dev["B"]), dev(inp.dev["C"]),
+                         dev(inp.D), dev(inp.dt_bias), True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(y.float()).all() and torch.isfinite(fs).all()
+    heads = [0, 37, cfg.H - 1]
+    for b in (0, cfg.batch - 1):
+        sl = slice(b, b + 1)
+        ry, rf = oracle.ssd_scan(inp.x[sl][:, :, heads], inp.dt[sl][:, :, heads], inp.A[heads], inp.B[sl], inp.C[sl],
+                                 inp.D[heads], inp.dt_bias[heads])
+        _check(host(y[sl][:, :, heads]), host(fs[sl][:, heads]), ry, rf, f"full workload b={b} heads={heads}")
+
+
+def test_ssd_deterministic_and_unsupported():
+    import torch
+    from selective_state_space_68_amd import SsmError, ssd_scan_fwd
+    inp = synth.make_ssd_inputs(2, 300, 3, 64, 64, "bf16", seed=9)
+    a = _run(inp)
+    b = _run(inp)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    x32 = torch.zeros((1, 64, 2, 64), device="cuda")
+    with pytest.raises(SsmError):
+        ssd_scan_fwd(x32, torch.zeros((1, 64, 2), device="cuda"), torch.zeros(2, device="cuda"),
+                     torch.zeros((1, 64, 64), device="cuda"), torch.zeros((1, 64, 64), device="cuda"))
+
+
+def test_ssd_segments_match_single_pass_and_oracle():
+    # a long sequence with few heads runs as parallel segments (pre-pass + combine);
+    # without a workspace it runs as one segment; both match the oracle, and the
+    # final state may replace the initial state in place with segments
+    import torch
+    from selective_state_space_68_amd import ssd_scan_fwd, ssd_scan_workspace_size
+    inp = synth.make_ssd_inputs(1, 2048 + 37, 2, 64, 64, "bf16", seed=21, with_h0=True)
+    assert ssd_scan_workspace_size(1, 2048 + 37, 2, 64, 64) > 0
+    t = {k: dev(inp.dev[k]) for k in ("x", "dt", "B", "C")}
+    A, Dk, bias = dev(inp.A), dev(inp.D), dev(inp.dt_bias)
+    ry, rf = oracle.ssd_scan(inp.x, inp.dt, inp.A, inp.B, inp.C, inp.D, inp.dt_bias, h0=inp.h0)
+    st = dev(inp.h0)
+    y_seg, _ = ssd_scan_fwd(t["x"], t["dt"], A, t["B"], t["C"], Dk, bias, True, initial_state=st, final_state=st)
+    y_one, f_one = ssd_scan_fwd(t["x"], t["dt"], A, t["B"], t["C"], Dk, bias, True, initial_state=dev(inp.h0),
+                                workspace=None)
+    torch.cuda.synchronize()
+    _check(host(y_seg), host(st), ry, rf, "segments, in place")
+    _check(host(y_one), host(f_one), ry, rf, "one segment")
