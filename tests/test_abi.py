@@ -224,6 +224,50 @@ def test_bwd_empty_channels_is_noop(lib):
     assert _bwd(lib, D=0, u=None, delta=None, dy=None, du=None, ddelta=None, dA=None, ws=None) == _lib.SSM_OK
 
 
+def _ssd(lib, **kw):
+    slots = ["x", "dt", "A", "B", "C", "D", "bias", "h0", "y", "fs", "ws"]
+    a = {k: F + i * 64 * MB for i, k in enumerate(slots)}
+    a.update(D=None, bias=None, h0=None, fs=None, softplus=1, batch=1, L=128, H=2, P=64, N=64, dt_=1,
+             ws_bytes=0, ws=None)
+    a.update(kw)
+    return lib.ssm_ssd_scan_fwd(a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["bias"], a["softplus"], a["h0"],
+                                a["y"], a["fs"], a["batch"], a["L"], a["H"], a["P"], a["N"], a["dt_"], a["ws"],
+                                a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), _lib.SSM_ERR_INVALID_ARG),
+    (dict(y=None), _lib.SSM_ERR_INVALID_ARG),
+    (dict(A=None), _lib.SSM_ERR_INVALID_ARG),
+    (dict(x=F + 8), _lib.SSM_ERR_INVALID_ARG),                     # x not 16-byte aligned
+    (dict(y=F), _lib.SSM_ERR_INVALID_ARG),                         # y aliases x
+    (dict(fs=F + 8 * 64 * MB), _lib.SSM_ERR_INVALID_ARG),           # final state aliases y
+    (dict(ws=F + 10 * 64 * MB, ws_bytes=64 * MB + 1), _lib.SSM_ERR_INVALID_ARG),   # workspace runs into... nothing
+    (dict(ws=None, ws_bytes=256), _lib.SSM_ERR_INVALID_ARG),        # size without a pointer
+    (dict(ws=F + 1 * 64 * MB, ws_bytes=1024), _lib.SSM_ERR_INVALID_ARG),  # workspace aliases dt
+    (dict(P=32), _lib.SSM_ERR_UNSUPPORTED),
+    (dict(N=16), _lib.SSM_ERR_UNSUPPORTED),
+    (dict(dt_=0), _lib.SSM_ERR_UNSUPPORTED),                       # float32 activations
+    (dict(L=-1), _lib.SSM_ERR_INVALID_ARG),
+    (dict(softplus=3), _lib.SSM_ERR_INVALID_ARG),
+])
+def test_ssd_argument_errors(lib, kw, status):
+    st = _ssd(lib, **kw)
+    if kw.get("ws_bytes") == 64 * MB + 1:
+        assert st == _lib.SSM_ERR_HIP                               # a large, separate workspace is fine
+    else:
+        assert st == status
+
+
+def test_ssd_workspace_size(lib):
+    ws = lib.ssm_ssd_scan_workspace_size
+    assert ws(4, 2048, 80, 64, 64, 1) > 0                          # 320 (batch, head) pairs: segments help
+    assert ws(1, 64, 2, 64, 64, 1) == 0                            # a single chunk: nothing to split
+    assert ws(4, 2048, 80, 64, 64, 0) == 0 and ws(4, 2048, 80, 32, 64, 1) == 0
+    assert _ssd(lib) == _lib.SSM_ERR_HIP                            # valid arguments reach the device probe
+    assert _ssd(lib, batch=0) == _lib.SSM_OK
+
+
 def test_state_update_empty_is_noop(lib):
     assert _step(lib, batch=0) == _lib.SSM_OK
 
