@@ -514,14 +514,18 @@ __global__ __launch_bounds__(64 * kW) void scan_chunked_kernel(ScanArgs p, int n
 
 bool aligned16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; }
 
+// Vector path: 16-byte vectors of u, delta, z, y along L, and of B and C (L % 8
+// == 0 keeps every row start 16-byte aligned in both dtypes).
+bool vec_path(const ScanArgs& a, int kpl) {
+  return (a.L % 8 == 0) && a.L >= kpl && aligned16(a.u) && aligned16(a.delta) && aligned16(a.y) &&
+         (a.z == nullptr || aligned16(a.z)) && aligned16(a.Bm) && aligned16(a.Cm);
+}
+
 template <typename ACT, bool GATE, int KPL, int W, bool CONV, bool ZOH>
 hipError_t launch_w(const ScanArgs& a, hipStream_t s) {
   const int n_dblk = static_cast<int>((a.D + W - 1) / W);
   const int64_t blocks = a.batch * n_dblk;
-  // vector path: 16-byte vectors of u, delta, z, y along L, and of B and C (L % 8
-  // == 0 keeps every row start 16-byte aligned in both dtypes)
-  const bool vec = (a.L % 8 == 0) && a.L >= KPL && aligned16(a.u) && aligned16(a.delta) && aligned16(a.y) &&
-                   (a.z == nullptr || aligned16(a.z)) && aligned16(a.Bm) && aligned16(a.Cm);
+  const bool vec = vec_path(a, KPL);
   const dim3 grid(static_cast<unsigned>(blocks)), block(64 * W);
   const bool n16 = a.N == 16;
   // N == 16, bfloat16, 8 tokens per lane: 8 states per step (two steps per
@@ -545,13 +549,28 @@ hipError_t launch_w(const ScanArgs& a, hipStream_t s) {
 
 template <typename ACT, bool GATE, int KPL, bool CONV, bool ZOH>
 hipError_t launch_kpl(const ScanArgs& a, hipStream_t s) {
-  // 12 waves per workgroup (3 per SIMD, one workgroup per CU) leaves the most
-  // registers per wave.  With enough channels for four rounds of 16-wave
-  // workgroups on 256 CUs, 8 tokens per lane (which fits 128 registers) runs 16
-  // waves, 4 per SIMD, for more latency hiding: 9 % faster on the 1.4B-shaped
-  // bfloat16 workload.  Fewer channels keep 12 so that every CU gets a workgroup.
+  // Waves per workgroup, from measurement on gfx950 (256 CUs).  Workgroup sizes
+  // are multiples of 4 waves: a 6-wave group puts two waves on two of the four
+  // SIMDs, and ran 50 % slower.
+  //  * 12 waves (3 per SIMD, one workgroup per CU) leaves the most registers per
+  //    wave.  It is the choice when one round of 12-wave groups covers every
+  //    channel (at most 12 * 256), as on the 130M- and 131k-shaped workloads.
+  //  * bfloat16, 8 tokens per lane, fits 128 registers, so two 8-wave groups share
+  //    a CU: 4 waves per SIMD, and each barrier waits for 8 waves, not 16.  Above
+  //    12 * 256 channels that is 7 % faster than one 16-wave group and 6-20 %
+  //    faster than 12 waves (1.4B-shaped workload: 307 against 329 us).  The
+  //    scalar-load kernel for N = 16 needs more registers and keeps 12 waves.
+  //  * float32 needs more than 128 registers unless the launch bound of a 16-wave
+  //    group forces it under; 16 waves (4 per SIMD) win once there are channels
+  //    for three rounds of them (8 % faster at 12288 channels, 14 % slower at 6144).
+  constexpr int64_t kCUs = 256;
   if constexpr (KPL == 8) {
-    if (a.batch * a.D >= 16 * 256 * 4) return launch_w<ACT, GATE, KPL, 16, CONV, ZOH>(a, s);
+    const int64_t ch = a.batch * a.D;
+    if constexpr (ACT::kBytes == 2) {
+      if (ch > 12 * kCUs && (a.N != 16 || vec_path(a, KPL))) return launch_w<ACT, GATE, KPL, 8, CONV, ZOH>(a, s);
+    } else {
+      if (ch >= 16 * kCUs * 3) return launch_w<ACT, GATE, KPL, 16, CONV, ZOH>(a, s);
+    }
   }
   return launch_w<ACT, GATE, KPL, 12, CONV, ZOH>(a, s);
 }
@@ -578,7 +597,7 @@ bool chunked_supported(const ScanArgs& a, Dt, int tokens_per_lane) {
   if (a.N < 1 || a.N > 64) return false;
   // the full zero-order hold is built for the default 8 tokens per lane without the fused conv
   if (a.zoh && (a.conv_w != nullptr || tokens_per_lane == 16)) return false;
-  const int64_t n_dblk = (a.D + 12 - 1) / 12;                // the most workgroups any launch uses
+  const int64_t n_dblk = (a.D + 8 - 1) / 8;                  // the most workgroups any launch uses (8 waves each)
   return a.batch * n_dblk <= 0x7fffffff;
 }
 

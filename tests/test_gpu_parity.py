@@ -79,8 +79,9 @@ def test_bf16_workloads_sampled(name, k):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_many_channels_sampled(dtype):
-    """Enough channels (batch * D >= 16384) for the 16-wave workgroups, with D not a
-    multiple of 16 so that the last workgroup of each row has idle waves."""
+    """Many channels (batch * D = 16400: 8-wave workgroups for bfloat16, 16-wave for
+    float32), with D not a multiple of 16 so that the last workgroup of each row has
+    idle waves."""
     batch, L, D, N = 4, 1032, 4100, 16
     inp = synth.make_scan_inputs(batch, L, D, N, dtype, seed=77, a_kind="lognormal", d_skip="normal")
     y, fs = run_scan(inp)
@@ -91,6 +92,28 @@ def test_many_channels_sampled(dtype):
     ys = np.stack([yh[b, d] for b, d in chans])
     fss = np.stack([fh[b, d] for b, d in chans])
     _check(ys, fss, ry, rf, dtype, f"many channels {dtype}")
+    assert np.isfinite(yh).all() and np.isfinite(fh).all()
+
+
+@pytest.mark.parametrize("shape", [
+    (1, 1104, 3080, 16, "bf16"),   # just past 12 * 256 channels: 8-wave groups, the last one ragged
+    (1, 1100, 3080, 16, "bf16"),   # L % 8 != 0: the scalar-load kernel keeps 12-wave groups
+    (2, 520, 1700, 32, "bf16"),    # the any-N kernel in 8-wave groups
+    (3, 600, 4100, 16, "f32"),     # 12300 channels: 16-wave groups, the last one ragged
+], ids=lambda s: "x".join(map(str, s)))
+def test_workgroup_size_boundaries(shape):
+    """Channel counts on both sides of the launch's workgroup-size rule, with a
+    ragged last workgroup; every channel's last outputs are checked."""
+    batch, L, D, N, dtype = shape
+    inp = synth.make_scan_inputs(batch, L, D, N, dtype, seed=D + L, a_kind="lognormal", d_skip="normal")
+    y, fs = run_scan(inp)
+    yh, fh = host(y), host(fs)
+    del y, fs
+    chans = sorted(set(sample_channels(batch, D, 12, seed=3)) | {(b, D - 1 - j) for b in range(batch) for j in range(5)})
+    ry, rf = oracle_scan(inp, chans)
+    ys = np.stack([yh[b, d] for b, d in chans])
+    fss = np.stack([fh[b, d] for b, d in chans])
+    _check(ys, fss, ry, rf, dtype, f"workgroup boundary {shape}")
     assert np.isfinite(yh).all() and np.isfinite(fh).all()
 
 
