@@ -288,7 +288,8 @@ ssm_status ssm_selective_scan_bwd(
  *   initial_state : [batch][H][P][N] float32 or NULL (= 0)
  *   final_state   : out [batch][H][P][N] float32 or NULL; may be the initial_state
  *                   pointer (updated in place) but must not otherwise overlap it
- * Supported: dtype SSM_BF16, P == 64, N in {64, 128} (SSM_ERR_UNSUPPORTED otherwise).
+ * Supported: dtype SSM_BF16, P == 64, N in {64, 128}, H <= 65536 (SSM_ERR_UNSUPPORTED
+ * otherwise).
  * x, y, Bm, Cm, the states and the workspace must be 16-byte aligned.  The products
  * run in bfloat16 with float32 accumulation and a float32 state (the carried-state
  * product uses the state as two bfloat16 terms); y is rounded to bfloat16.

@@ -110,7 +110,7 @@ struct SsdArgs {
 // Mamba-2 SSD scan on the matrix cores (P == 64, N in {64, 128}, bfloat16).  A
 // workspace of ssd_workspace_bytes lets the sequence run as parallel segments;
 // without it (NULL or too small) one segment per sequence.
-bool ssd_supported(int64_t P, int64_t N);
+bool ssd_supported(int64_t H, int64_t P, int64_t N);
 size_t ssd_workspace_bytes(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N);
 hipError_t launch_ssd_scan(const SsdArgs& a, void* ws, size_t ws_bytes, hipStream_t s);
 

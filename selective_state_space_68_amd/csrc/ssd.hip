@@ -71,38 +71,58 @@ __device__ __forceinline__ float wave_prefix_sum(float v) {
 __device__ __forceinline__ uint32_t bf16x2(float lo, float hi) { return pack_bf16x2(lo, hi); }
 __device__ __forceinline__ float bf16_at(const uint16_t* p) { return __uint_as_float(static_cast<uint32_t>(*p) << 16); }
 
-// One chunk's inputs in registers (prefetch): thread t moves the 16-byte pieces
-// v = t + 256 k of the 64-token tiles of x (8 channels per piece: token v / 8, piece
-// v % 8) and of B and C (8 states per piece), so 8 consecutive lanes read one token's
-// contiguous row.
+// One chunk's inputs in registers (prefetch), moved as token pairs: thread t takes
+// the 16-byte piece q of tokens 2m and 2m + 1 of the 64-token tiles of x (8 channels
+// per piece) and of B and C (8 states per piece), (m, q) = (v / R, v % R) for
+// v = t + 256 k and R pieces per token row.  R consecutive lanes read one token's
+// contiguous row, and a thread holds both tokens of every pair it writes into the
+// transposed LDS copies, so those writes are 4-byte token pairs.
 template <int NS>
 struct ChunkRegs {
-  static constexpr int kXV = kQ * kP / 8 / 256;     // x pieces per thread (2)
-  static constexpr int kBV = kQ * NS / 8 / 256;     // B (and C) pieces per thread
-  uint4 x[kXV], b[kBV], c[kBV];
-  float dt;                                          // raw Delta of token `lane` (each wave loads it)
+  static constexpr int kXR = kP / 8;                // 16-byte pieces per token row of x
+  static constexpr int kBR = NS / 8;                // ... of B and C
+  static constexpr int kXV = kQ / 2 * kXR / 256;    // x token pairs per thread (1)
+  static constexpr int kBV = kQ / 2 * kBR / 256;    // B (and C) token pairs per thread (1 or 2)
+  uint4 x[kXV][2], b[kBV][2], c[kBV][2];
+  float dt;                                         // raw Delta of token `lane` (each wave loads it)
 };
+
+// Two bfloat16 words -> the pair of their low (HI = false) or high halves, the first
+// word's in the low half of the result.
+template <bool HI>
+__device__ __forceinline__ uint32_t pair16(uint32_t a, uint32_t b) {
+  return HI ? (a >> 16) | (b & 0xffff0000u) : (a & 0xffffu) | (b << 16);
+}
 
 // STATE_ONLY: the pre-pass of the segmented form: the segment's end state from a
 // zero start (x, B and Delta only; no C, no output), written to the workspace.
 // Otherwise the full scan of the segment's chunks from its entering state: the
 // initial state for segment 0, else the combined state in the workspace.
+//
+// Operand order: every product is arranged so that the four values a lane holds of
+// its output tile (four consecutive rows m of one column n) are contiguous in the
+// array the next step reads: S is computed transposed (rows i of B against rows j of
+// C), so a lane's four entries of a row j of S' are one 8-byte LDS write, and the
+// output is computed as y^T (x^T against S'^T and H against C^T), so a lane's four
+// entries of a token's row of y are one 8-byte write.
 template <int NS, bool STATE_ONLY>
 __global__ __launch_bounds__(256) void ssd_scan_kernel(SsdArgs p) {
-  constexpr int RX = kQ + kPad;                     // row stride of [.][Q] arrays
+  constexpr int RX = kQ + kPad;                     // row stride of [.][Q] and [.][P] arrays
   constexpr int RN = NS + kPad;                     // row stride of [.][N] arrays
   constexpr int NT = NS / 16;                       // 16-row tiles of the state
+  using CR = ChunkRegs<NS>;
   __shared__ __attribute__((aligned(16))) uint16_t sXT[kP * RX];    // x^T [p][i]
+  __shared__ __attribute__((aligned(16))) uint16_t sX[kQ * RX];     // x [i][p]
   __shared__ __attribute__((aligned(16))) uint16_t sB[kQ * RN];     // B [i][n]
   __shared__ __attribute__((aligned(16))) uint16_t sBwT[NS * RX];   // (B diag(w))^T [n][i]
   __shared__ __attribute__((aligned(16))) uint16_t sC[kQ * RN];     // C [j][n]
   __shared__ __attribute__((aligned(16))) uint16_t sS[kQ * RX];     // (C B^T o M) Delta [j][i]
   __shared__ __attribute__((aligned(16))) uint16_t sY[kQ * RX];     // y [j][p] staging
-  __shared__ float sCum[kQ], sDl[kQ], sEc[kQ];
+  __shared__ __attribute__((aligned(16))) float sCum[kQ], sDl[kQ], sEc[kQ];
   // [row][token] arrays written transposed (x^T, B^T) place the 8-token block b of
   // row r at block b ^ ((r / 8) % 8): the 8 rows one instruction writes for one
-  // token then fall in 8 different banks, and every 8-token block stays a contiguous,
-  // aligned 16-byte MFMA operand.
+  // token pair then fall in 8 different banks, and every 8-token block stays a
+  // contiguous, aligned 16-byte MFMA operand.
   auto swz = [](int r, int i) __attribute__((always_inline)) { return r * RX + (i ^ (((r >> 3) & 7) << 3)); };
 
   const int tid = threadIdx.x;
@@ -126,12 +146,16 @@ __global__ __launch_bounds__(256) void ssd_scan_kernel(SsdArgs p) {
   // the initial state, which the final state may overwrite in place)
   float* seg_state = p.seg_state ? p.seg_state + (bh * nseg) * kP * NS : nullptr;
   if (STATE_ONLY && seg == nseg - 1) return;         // the last segment's own state is not needed
-  const int64_t xrow = H * kP;                      // elements between consecutive tokens of x / y
-  const uint16_t* xg = static_cast<const uint16_t*>(p.x) + (b * L * H + h) * kP;
-  const uint16_t* bg = static_cast<const uint16_t*>(p.Bm) + b * L * NS;
-  const uint16_t* cg = static_cast<const uint16_t*>(p.Cm) + b * L * NS;
-  const uint16_t* dtg = static_cast<const uint16_t*>(p.dt) + b * L * H + h;
-  uint16_t* yg = static_cast<uint16_t*>(p.y) + (b * L * H + h) * kP;
+  // Byte strides between consecutive tokens (x / y rows, B / C rows, dt) and the
+  // sequence bases; a chunk's loads are 32-bit offsets from its first token.
+  const uint32_t xrow_b = static_cast<uint32_t>(H) * kP * 2;
+  constexpr uint32_t brow_b = NS * 2;
+  const uint32_t dtrow_b = static_cast<uint32_t>(H) * 2;
+  const char* xg = static_cast<const char*>(p.x) + (b * L * H + h) * kP * 2;
+  const char* bg = static_cast<const char*>(p.Bm) + b * L * NS * 2;
+  const char* cg = static_cast<const char*>(p.Cm) + b * L * NS * 2;
+  const char* dtg = static_cast<const char*>(p.dt) + (b * L * H + h) * 2;
+  char* yg = static_cast<char*>(p.y) + (b * L * H + h) * kP * 2;
 
   // State H[p][n] for p = 16w + c16, n = 16 mt + 4g + e: tile mt, element e.
   f32x4_t Hs[NT];
@@ -152,35 +176,57 @@ __global__ __launch_bounds__(256) void ssd_scan_kernel(SsdArgs p) {
   }
   float log_decay = 0.0f;                           // the segment's total decay exponent (base 2)
 
-  using CR = ChunkRegs<NS>;
+  // Per-thread byte offsets of its pieces within a chunk, and of piece q of the
+  // chunk's row `lim` (the clamp: min(offset, row lim) for a piece in row i is the
+  // piece in row min(i, lim)).
+  uint32_t xo_off[CR::kXV][2], xq_b[CR::kXV], bo_off[CR::kBV][2], bq_b[CR::kBV];
+#pragma unroll
+  for (int k = 0; k < CR::kXV; ++k) {
+    const int v = tid + 256 * k, m = v / CR::kXR, q = v % CR::kXR;
+    xq_b[k] = 16u * q;
+    xo_off[k][0] = (2 * m) * xrow_b + xq_b[k];
+    xo_off[k][1] = (2 * m + 1) * xrow_b + xq_b[k];
+  }
+#pragma unroll
+  for (int k = 0; k < CR::kBV; ++k) {
+    const int v = tid + 256 * k, m = v / CR::kBR, q = v % CR::kBR;
+    bq_b[k] = 16u * q;
+    bo_off[k][0] = (2 * m) * brow_b + bq_b[k];
+    bo_off[k][1] = (2 * m + 1) * brow_b + bq_b[k];
+  }
+  const uint32_t dt_off = static_cast<uint32_t>(lane) * dtrow_b;
+
   CR cr;
-  // Loads of chunk c into registers; tokens past L read as zero.  No load sits
-  // behind a branch (rows past L reload the last row and are then replaced by zero),
-  // so the loads issued for the next chunk stay in flight during this one.
+  // Loads of chunk c into registers.  Rows past L reload row L - 1 (finite values);
+  // those padding tokens get Delta = 0, which zeroes their weight in every product
+  // that reaches a stored output, and their own output rows are not stored.  No load
+  // sits behind a branch, so the loads issued for the next chunk stay in flight
+  // during this one.
   auto fetch = [&](int64_t c) __attribute__((always_inline)) {
     const int64_t t0 = c * kQ;
-    const uint4 zero = make_uint4(0, 0, 0, 0);
+    const uint32_t lim = static_cast<uint32_t>(L - 1 - t0 < kQ - 1 ? L - 1 - t0 : kQ - 1);
+    const char* xc = xg + t0 * xrow_b;
+    const char* bc = bg + t0 * brow_b;
+    const char* cc = cg + t0 * brow_b;
 #pragma unroll
     for (int k = 0; k < CR::kXV; ++k) {
-      const int v = tid + 256 * k, i = v >> 3, q = v & 7;
-      const int64_t t = t0 + i < L ? t0 + i : L - 1;
-      const uint4 r = *reinterpret_cast<const uint4*>(xg + t * xrow + 8 * q);
-      cr.x[k] = t0 + i < L ? r : zero;
+      const uint32_t cap = lim * xrow_b + xq_b[k];
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        cr.x[k][s] = *reinterpret_cast<const uint4*>(xc + (xo_off[k][s] < cap ? xo_off[k][s] : cap));
     }
 #pragma unroll
     for (int k = 0; k < CR::kBV; ++k) {
-      const int v = tid + 256 * k, i = v / (NS / 8), q = v % (NS / 8);
-      const int64_t t = t0 + i < L ? t0 + i : L - 1;
-      const uint4 rb = *reinterpret_cast<const uint4*>(bg + t * NS + 8 * q);
-      cr.b[k] = t0 + i < L ? rb : zero;
-      if constexpr (!STATE_ONLY) {
-        const uint4 rc = *reinterpret_cast<const uint4*>(cg + t * NS + 8 * q);
-        cr.c[k] = t0 + i < L ? rc : zero;
+      const uint32_t cap = lim * brow_b + bq_b[k];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const uint32_t o = bo_off[k][s] < cap ? bo_off[k][s] : cap;
+        cr.b[k][s] = *reinterpret_cast<const uint4*>(bc + o);
+        if constexpr (!STATE_ONLY) cr.c[k][s] = *reinterpret_cast<const uint4*>(cc + o);
       }
     }
-    const int64_t tl = t0 + lane < L ? t0 + lane : L - 1;
-    const float dv = bf16_at(dtg + tl * H);
-    cr.dt = t0 + lane < L ? dv : 0.0f;
+    const uint32_t dcap = lim * dtrow_b;
+    cr.dt = bf16_at(reinterpret_cast<const uint16_t*>(dtg + t0 * dtrow_b + (dt_off < dcap ? dt_off : dcap)));
   };
 
   fetch(c_begin);
@@ -200,67 +246,85 @@ __global__ __launch_bounds__(256) void ssd_scan_kernel(SsdArgs p) {
       sDl[lane] = dl;
       sEc[lane] = exp2_hw(cum);                     // decay of the carried state up to token `lane`
     }
-    {
-      const uint16_t* e;
 #pragma unroll
-      for (int k = 0; k < CR::kXV; ++k) {
-        const int v = tid + 256 * k, i = v >> 3, q = v & 7;
-        e = reinterpret_cast<const uint16_t*>(&cr.x[k]);
-#pragma unroll
-        for (int r = 0; r < 8; ++r) sXT[swz(8 * q + r, i)] = e[r];
+    for (int k = 0; k < CR::kXV; ++k) {
+      const int v = tid + 256 * k, i0 = 2 * (v / CR::kXR), q = v % CR::kXR;
+      if constexpr (!STATE_ONLY) {
+        *reinterpret_cast<uint4*>(&sX[i0 * RX + 8 * q]) = cr.x[k][0];
+        *reinterpret_cast<uint4*>(&sX[(i0 + 1) * RX + 8 * q]) = cr.x[k][1];
       }
+      const uint32_t a0[4] = {cr.x[k][0].x, cr.x[k][0].y, cr.x[k][0].z, cr.x[k][0].w};
+      const uint32_t a1[4] = {cr.x[k][1].x, cr.x[k][1].y, cr.x[k][1].z, cr.x[k][1].w};
 #pragma unroll
-      for (int k = 0; k < CR::kBV; ++k) {
-        const int v = tid + 256 * k, i = v / (NS / 8), q = v % (NS / 8);
-        if constexpr (!STATE_ONLY) {
-          *reinterpret_cast<uint4*>(&sB[i * RN + 8 * q]) = cr.b[k];
-          *reinterpret_cast<uint4*>(&sC[i * RN + 8 * q]) = cr.c[k];
-        }
-        // B^T scaled by the token weights, for the state contribution
-        const float wi = __shfl(wgt, i);
-        const uint32_t rw[4] = {cr.b[k].x, cr.b[k].y, cr.b[k].z, cr.b[k].w};
+      for (int r = 0; r < 4; ++r) {
+        *reinterpret_cast<uint32_t*>(&sXT[swz(8 * q + 2 * r, i0)]) = pair16<false>(a0[r], a1[r]);
+        *reinterpret_cast<uint32_t*>(&sXT[swz(8 * q + 2 * r + 1, i0)]) = pair16<true>(a0[r], a1[r]);
+      }
+    }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          sBwT[swz(8 * q + 2 * r, i)] = to_bf16(bf16_lo(rw[r]) * wi);
-          sBwT[swz(8 * q + 2 * r + 1, i)] = to_bf16(bf16_hi(rw[r]) * wi);
-        }
+    for (int k = 0; k < CR::kBV; ++k) {
+      const int v = tid + 256 * k, i0 = 2 * (v / CR::kBR), q = v % CR::kBR;
+      if constexpr (!STATE_ONLY) {
+        *reinterpret_cast<uint4*>(&sB[i0 * RN + 8 * q]) = cr.b[k][0];
+        *reinterpret_cast<uint4*>(&sB[(i0 + 1) * RN + 8 * q]) = cr.b[k][1];
+        *reinterpret_cast<uint4*>(&sC[i0 * RN + 8 * q]) = cr.c[k][0];
+        *reinterpret_cast<uint4*>(&sC[(i0 + 1) * RN + 8 * q]) = cr.c[k][1];
+      }
+      // B^T scaled by the token weights, for the state contribution
+      const float w0 = __shfl(wgt, i0), w1 = __shfl(wgt, i0 + 1);
+      const uint32_t b0[4] = {cr.b[k][0].x, cr.b[k][0].y, cr.b[k][0].z, cr.b[k][0].w};
+      const uint32_t b1[4] = {cr.b[k][1].x, cr.b[k][1].y, cr.b[k][1].z, cr.b[k][1].w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        *reinterpret_cast<uint32_t*>(&sBwT[swz(8 * q + 2 * r, i0)]) =
+            bf16x2(bf16_lo(b0[r]) * w0, bf16_lo(b1[r]) * w1);
+        *reinterpret_cast<uint32_t*>(&sBwT[swz(8 * q + 2 * r + 1, i0)]) =
+            bf16x2(bf16_hi(b0[r]) * w0, bf16_hi(b1[r]) * w1);
       }
     }
     fetch(c + 1 < c_end ? c + 1 : c);                // (the last chunk reloads itself, unused)
     log_decay += cum_last;
     barrier_lds();
 
-    // ---- 2. S' = (C B^T o M) Delta for rows j of this wave; the chunk's state
-    // contribution; the output from the carried state
+    // this wave's channels p = 16w + c16 of x^T, as MFMA operands (state and output)
+    uint4 xo[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) xo[kb] = *reinterpret_cast<const uint4*>(&sXT[swz(16 * w + c16, 32 * kb + 8 * g)]);
+
+    // ---- 2. S' = (C B^T o M) Delta for rows j = 16w + c16 of this wave (computed as
+    // tiles of S^T: rows i of B against row j of C); the chunk's state contribution;
+    // the output from the carried state
     if constexpr (!STATE_ONLY) {
-      f32x4_t S[4];
+      const int j = 16 * w + c16;
+      const float cj = sCum[j];
+      uint4 cb[NS / 32];
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) S[nt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int kb = 0; kb < NS / 32; ++kb) cb[kb] = *reinterpret_cast<const uint4*>(&sC[j * RN + 32 * kb + 8 * g]);
 #pragma unroll
-      for (int kb = 0; kb < NS / 32; ++kb) {
-        const uint4 a = *reinterpret_cast<const uint4*>(&sC[(16 * w + c16) * RN + 32 * kb + 8 * g]);
+      for (int it = 0; it < 4; ++it) {
+        const int i0 = 16 * it + 4 * g;             // this lane's 4 consecutive i
+        uint2 packed = make_uint2(0u, 0u);
+        if (it <= w) {                              // tiles right of the diagonal are all zero
+          f32x4_t S = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          const uint4 bo = *reinterpret_cast<const uint4*>(&sB[(16 * nt + c16) * RN + 32 * kb + 8 * g]);
-          S[nt] = mfma32(a, bo, S[nt]);
+          for (int kb = 0; kb < NS / 32; ++kb) {
+            const uint4 a = *reinterpret_cast<const uint4*>(&sB[(16 * it + c16) * RN + 32 * kb + 8 * g]);
+            S = mfma32(a, cb[kb], S);
+          }
+          const float4 ci = *reinterpret_cast<const float4*>(&sCum[i0]);
+          const float4 di = *reinterpret_cast<const float4*>(&sDl[i0]);
+          const float cis[4] = {ci.x, ci.y, ci.z, ci.w}, dis[4] = {di.x, di.y, di.z, di.w};
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            // (computed for every element, then selected: no branch per element)
+            v[e] = S[e] * exp2_hw(fminf(cj - cis[e], 0.0f)) * dis[e];
+            asm volatile("" : "+v"(v[e]));
+            v[e] = j >= i0 + e ? v[e] : 0.0f;
+          }
+          packed = make_uint2(bf16x2(v[0], v[1]), bf16x2(v[2], v[3]));
         }
-      }
-      // mask and scale: element (j = 16w + 4g + e, i = 16nt + c16)
-      float cj[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) cj[e] = sCum[16 * w + 4 * g + e];
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const int i = 16 * nt + c16;
-        const float ci = sCum[i], di = sDl[i];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int j = 16 * w + 4 * g + e;
-          // (computed for every element, then selected: no branch per element)
-          float v = S[nt][e] * exp2_hw(fminf(cj[e] - ci, 0.0f)) * di;
-          asm volatile("" : "+v"(v));
-          sS[j * RX + i] = to_bf16(j >= i ? v : 0.0f);
-        }
+        *reinterpret_cast<uint2*>(&sS[j * RX + i0]) = packed;
       }
     }
     // the chunk's state contribution st[n][p] = sum_i B[i][n] w_i x[i][p],
@@ -270,11 +334,10 @@ __global__ __launch_bounds__(256) void ssd_scan_kernel(SsdArgs p) {
     for (int mt = 0; mt < NT; ++mt) st[mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const uint4 xo = *reinterpret_cast<const uint4*>(&sXT[swz(16 * w + c16, 32 * kb + 8 * g)]);
 #pragma unroll
       for (int mt = 0; mt < NT; ++mt) {
         const uint4 a = *reinterpret_cast<const uint4*>(&sBwT[swz(16 * mt + c16, 32 * kb + 8 * g)]);
-        st[mt] = mfma32(a, xo, st[mt]);
+        st[mt] = mfma32(a, xo[kb], st[mt]);
       }
     }
     if constexpr (STATE_ONLY) {
@@ -286,9 +349,9 @@ __global__ __launch_bounds__(256) void ssd_scan_kernel(SsdArgs p) {
       barrier_lds();                                // every wave is done with this chunk's LDS
       continue;
     }
-    // output from the carried state: Yc[j][p] = sum_n C[j][n] H[p][n] (16x16x16: the
-    // state tiles are the B operands as they are).  The float32 state is split into
-    // two bfloat16 terms, hi + lo, so the product keeps ~16 bits of the state.
+    // output from the carried state, transposed: Yc[p][j] = sum_n H[p][n] C[j][n]
+    // (16x16x16: the state tiles are the A operands as they are).  The float32 state
+    // is split into two bfloat16 terms, hi + lo, so the product keeps ~16 bits of it.
     f32x4_t Yc[4];
 #pragma unroll
     for (int jt = 0; jt < 4; ++jt) Yc[jt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -304,37 +367,37 @@ __global__ __launch_bounds__(256) void ssd_scan_kernel(SsdArgs p) {
       const uint2 lb = make_uint2(bf16x2(lo[0], lo[1]), bf16x2(lo[2], lo[3]));
 #pragma unroll
       for (int jt = 0; jt < 4; ++jt) {
-        const uint2 a = *reinterpret_cast<const uint2*>(&sC[(16 * jt + c16) * RN + 16 * mt + 4 * g]);
-        Yc[jt] = mfma16(a, hb, Yc[jt]);
-        Yc[jt] = mfma16(a, lb, Yc[jt]);
+        const uint2 cbv = *reinterpret_cast<const uint2*>(&sC[(16 * jt + c16) * RN + 16 * mt + 4 * g]);
+        Yc[jt] = mfma16(hb, cbv, Yc[jt]);
+        Yc[jt] = mfma16(lb, cbv, Yc[jt]);
       }
     }
     barrier_lds();                                  // S' complete
 
-    // ---- 3. Y = S' x + exp(cum_j) Yc + D x; the state update
+    // ---- 3. y^T = x^T S'^T + H C^T diag(exp(cum_j)) + D x^T; the state update.  Lane
+    // (g, c16) holds y[j = 16 jt + c16][p = 16w + 4g + e].
     f32x4_t Yo[4];
 #pragma unroll
     for (int jt = 0; jt < 4; ++jt) Yo[jt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const uint4 xo = *reinterpret_cast<const uint4*>(&sXT[swz(16 * w + c16, 32 * kb + 8 * g)]);
 #pragma unroll
       for (int jt = 0; jt < 4; ++jt) {
-        const uint4 a = *reinterpret_cast<const uint4*>(&sS[(16 * jt + c16) * RX + 32 * kb + 8 * g]);
-        Yo[jt] = mfma32(a, xo, Yo[jt]);
+        const uint4 sb = *reinterpret_cast<const uint4*>(&sS[(16 * jt + c16) * RX + 32 * kb + 8 * g]);
+        Yo[jt] = mfma32(xo[kb], sb, Yo[jt]);
       }
     }
-    const int pcol = 16 * w + c16;
+    const int p0 = 16 * w + 4 * g;
 #pragma unroll
     for (int jt = 0; jt < 4; ++jt) {
-      const uint2 xr = *reinterpret_cast<const uint2*>(&sXT[swz(pcol, 16 * jt + 4 * g)]);
+      const int j = 16 * jt + c16;
+      const uint2 xr = *reinterpret_cast<const uint2*>(&sX[j * RX + p0]);
       const float xv[4] = {bf16_lo(xr.x), bf16_hi(xr.x), bf16_lo(xr.y), bf16_hi(xr.y)};
+      const float ec = sEc[j];
+      float v[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = 16 * jt + 4 * g + e;
-        const float v = Yo[jt][e] + sEc[j] * Yc[jt][e] + dsk * xv[e];
-        sY[j * RX + pcol] = to_bf16(v);
-      }
+      for (int e = 0; e < 4; ++e) v[e] = __builtin_fmaf(dsk, xv[e], __builtin_fmaf(ec, Yc[jt][e], Yo[jt][e]));
+      *reinterpret_cast<uint2*>(&sY[j * RX + p0]) = make_uint2(bf16x2(v[0], v[1]), bf16x2(v[2], v[3]));
     }
     const float decay = exp2_hw(cum_last);
 #pragma unroll
@@ -344,11 +407,12 @@ __global__ __launch_bounds__(256) void ssd_scan_kernel(SsdArgs p) {
     barrier_lds();                                  // y tile complete
 
     // ---- 4. y rows to memory (128 contiguous bytes per token)
+    char* yc = yg + t0 * xrow_b;
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int v = tid + 256 * k, j = v >> 3, q = v & 7;
       if (t0 + j < L)
-        *reinterpret_cast<uint4*>(yg + (t0 + j) * xrow + 8 * q) = *reinterpret_cast<const uint4*>(&sY[j * RX + 8 * q]);
+        *reinterpret_cast<uint4*>(yc + j * xrow_b + 16 * q) = *reinterpret_cast<const uint4*>(&sY[j * RX + 8 * q]);
     }
   }
   float* dst = nullptr;
@@ -382,7 +446,9 @@ __global__ void ssd_combine_kernel(SsdArgs p, int64_t PN) {
 
 }  // namespace
 
-bool ssd_supported(int64_t P, int64_t N) { return P == kP && (N == 64 || N == 128); }
+// (H is bounded so that a chunk's 64 token rows of x span less than 4 GB: the loads
+// use 32-bit offsets from the chunk's first token)
+bool ssd_supported(int64_t H, int64_t P, int64_t N) { return H <= 65536 && P == kP && (N == 64 || N == 128); }
 
 // Segments per sequence: enough workgroups for about three per CU (the kernel is
 // latency-bound at one wave per SIMD), at least 4 chunks per segment.

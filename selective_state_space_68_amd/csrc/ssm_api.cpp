@@ -99,7 +99,7 @@ ssm_status check_scan(const void* u, const void* delta, const float* A, const vo
 extern "C" {
 
 size_t ssm_ssd_scan_workspace_size(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, ssm_dtype dtype) {
-  if (dtype != SSM_BF16 || !ssm::ssd_supported(P, N) || batch <= 0 || L <= 0 || H <= 0) return 0;
+  if (dtype != SSM_BF16 || !ssm::ssd_supported(H, P, N) || batch <= 0 || L <= 0 || H <= 0) return 0;
   uint64_t t;
   if (!mul_ok(batch, H, &t) || !mul_ok(t, L, &t) || t > (uint64_t(1) << 50)) return 0;
   return ssm::ssd_workspace_bytes(batch, L, H, P, N);
@@ -112,7 +112,7 @@ ssm_status ssm_ssd_scan_fwd(const void* x, const void* dt, const float* A, const
   if (dtype != SSM_F32 && dtype != SSM_BF16) return SSM_ERR_UNSUPPORTED;
   if (batch < 0 || L < 0 || H < 0 || P < 0 || N < 0) return SSM_ERR_INVALID_ARG;
   if (dt_softplus != 0 && dt_softplus != 1) return SSM_ERR_INVALID_ARG;
-  if (dtype != SSM_BF16 || !ssm::ssd_supported(P, N)) return SSM_ERR_UNSUPPORTED;
+  if (dtype != SSM_BF16 || !ssm::ssd_supported(H, P, N)) return SSM_ERR_UNSUPPORTED;
   uint64_t blh, xe, xbytes, dtbytes, bl, bcbytes, bh, st, stbytes;
   if (!mul_ok(batch, L, &blh) || !mul_ok(blh, H, &blh) || !mul_ok(blh, P, &xe) || !mul_ok(xe, 2, &xbytes) ||
       !mul_ok(batch, L, &bl) || !mul_ok(bl, H, &dtbytes) || !mul_ok(dtbytes, 2, &dtbytes) ||
