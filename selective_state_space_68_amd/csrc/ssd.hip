@@ -27,11 +27,11 @@
 // accumulate in float32 and the state stays float32 (it is rounded to bfloat16
 // only as the operand of the carried-state product).
 //
-// MFMA lane layouts (gfx950, checked on the device): for v_mfma_f32_16x16x32_bf16,
+// MFMA lane layout (gfx950, checked on the device): for v_mfma_f32_16x16x32_bf16,
 // lane l holds A[m = l%16][k = 8(l/16) .. +7], B[k = 8(l/16) .. +7][n = l%16] and
-// D[m = 4(l/16) + e][n = l%16]; v_mfma_f32_16x16x16_bf16 the same with 4 k per lane.
-// The D layout of a 16 x 16 tile equals the 16x16x16 B-operand layout, so the state
-// produced by one product feeds the next without a shuffle.
+// D[m = 4(l/16) + e][n = l%16].  Only the pairing of A's and B's K slots matters, so
+// the state, which a product leaves in the D layout, is used as an A operand without
+// a shuffle by giving the K slots of each lane the state entries it already holds.
 #include "device_common.hpp"
 #include "kernels.hpp"
 #include "scan_common.hpp"
@@ -44,16 +44,11 @@ constexpr int kP = 64;            // head channels (4 waves x 16)
 constexpr int kPad = 8;           // bfloat16 elements of row padding in LDS
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x4_t mfma32(const uint4& a, const uint4& b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
                                                  0, 0, 0);
-}
-__device__ __forceinline__ f32x4_t mfma16(const uint2& a, const uint2& b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4_t, a), __builtin_bit_cast(i16x4_t, b), c,
-                                                   0, 0, 0);
 }
 
 // Inclusive prefix sum over the 64 lanes (Kogge-Stone with row shifts and the row
@@ -349,27 +344,36 @@ __global__ __launch_bounds__(256) void ssd_scan_kernel(SsdArgs p) {
       barrier_lds();                                // every wave is done with this chunk's LDS
       continue;
     }
-    // output from the carried state, transposed: Yc[p][j] = sum_n H[p][n] C[j][n]
-    // (16x16x16: the state tiles are the A operands as they are).  The float32 state
-    // is split into two bfloat16 terms, hi + lo, so the product keeps ~16 bits of it.
+    // output from the carried state, transposed: Yc[p][j] = sum_n H[p][n] C[j][n].
+    // The float32 state is split into two bfloat16 terms, hi + lo, so the product
+    // keeps ~16 bits of it.  A product's K order is free: the 8 K slots of a lane
+    // hold the entries it already has of two state tiles, n = 32t + 4g + e and
+    // 32t + 16 + 4g + e, against the same entries of C (two 8-byte reads); hi and lo
+    // are two products sharing that C operand.
     f32x4_t Yc[4];
 #pragma unroll
     for (int jt = 0; jt < 4; ++jt) Yc[jt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int mt = 0; mt < NT; ++mt) {
-      float hi[4], lo[4];
+    for (int t = 0; t < NT / 2; ++t) {
+      uint32_t hw[4], lw[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        hi[e] = __uint_as_float(static_cast<uint32_t>(to_bf16(Hs[mt][e])) << 16);
-        lo[e] = Hs[mt][e] - hi[e];
+      for (int u = 0; u < 2; ++u) {
+        const f32x4_t hv = Hs[2 * t + u];
+        const uint32_t h01 = bf16x2(hv[0], hv[1]), h23 = bf16x2(hv[2], hv[3]);
+        hw[2 * u] = h01;
+        hw[2 * u + 1] = h23;
+        lw[2 * u] = bf16x2(hv[0] - bf16_lo(h01), hv[1] - bf16_hi(h01));
+        lw[2 * u + 1] = bf16x2(hv[2] - bf16_lo(h23), hv[3] - bf16_hi(h23));
       }
-      const uint2 hb = make_uint2(bf16x2(hi[0], hi[1]), bf16x2(hi[2], hi[3]));
-      const uint2 lb = make_uint2(bf16x2(lo[0], lo[1]), bf16x2(lo[2], lo[3]));
+      const uint4 hq = make_uint4(hw[0], hw[1], hw[2], hw[3]), lq = make_uint4(lw[0], lw[1], lw[2], lw[3]);
 #pragma unroll
       for (int jt = 0; jt < 4; ++jt) {
-        const uint2 cbv = *reinterpret_cast<const uint2*>(&sC[(16 * jt + c16) * RN + 16 * mt + 4 * g]);
-        Yc[jt] = mfma16(hb, cbv, Yc[jt]);
-        Yc[jt] = mfma16(lb, cbv, Yc[jt]);
+        const uint16_t* crow = &sC[(16 * jt + c16) * RN + 32 * t + 4 * g];
+        const uint2 c0 = *reinterpret_cast<const uint2*>(crow);
+        const uint2 c1 = *reinterpret_cast<const uint2*>(crow + 16);
+        const uint4 cq = make_uint4(c0.x, c0.y, c1.x, c1.y);
+        Yc[jt] = mfma32(hq, cq, Yc[jt]);
+        Yc[jt] = mfma32(lq, cq, Yc[jt]);
       }
     }
     barrier_lds();                                  // S' complete
