@@ -49,25 +49,40 @@ ZOH_ALU_SLOTS_PER_ELEMENT = 8
 MALL_BYTES = 256 << 20
 CALIB_BYTES = 256 << 20
 DEFAULT_WORKLOAD = "mamba130m_f32"
-KERNEL_SRC = {"scan": "selective_state_space_68_amd/csrc/scan_chunked.hip",
-              "decode": "selective_state_space_68_amd/csrc/state_update.hip",
-              "bwd": "selective_state_space_68_amd/csrc/scan_bwd.hip",
-              "ssd": "selective_state_space_68_amd/csrc/ssd.hip"}
-KERNEL_NAME = {"scan": "scan_chunked_kernel", "decode": "state_update_vec_kernel",
+_CSRC = "selective_state_space_68_amd/csrc/"
+KERNEL_SRC = {"scan_chunked_kernel": _CSRC + "scan_chunked.hip", "scan_tokseq_kernel": _CSRC + "scan_tokseq.hip",
+              "scan_sequential_kernel": _CSRC + "scan_sequential.hip",
+              "state_update_vec_kernel": _CSRC + "state_update.hip", "ssd_scan_kernel": _CSRC + "ssd.hip"}
+KERNEL_NAME = {"decode": "state_update_vec_kernel",
                "bwd": "scan backward call (bwd_summary, bwd_combine, bwd_main, bwd_param_sums, bwd_bc_out kernels)",
                "ssd": "ssd_scan_kernel"}
+KERNEL_SRC[KERNEL_NAME["bwd"]] = _CSRC + "scan_bwd.hip"
 PEAK_MFMA_BF16_TFLOPS = 2500.0
 
 
-def src_hash(kind):
+def kernel_of(cfg, kind, variant=0, tokens_per_lane=0):
+    """The kernel (or, for the backward, the call) a workload's timed region runs.
+    The forward scan asks the library which kernel it picks for the shape; the full
+    zero-order hold and the fused conv always run the chunked kernel."""
+    if kind != "scan":
+        return KERNEL_NAME[kind]
+    if cfg.discretization == "zoh" or cfg.conv_k:
+        return "scan_chunked_kernel"
+    import torch
+    from selective_state_space_68_amd import selective_scan_fwd_kernel
+    dtype = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    return selective_scan_fwd_kernel(cfg.batch, cfg.L, cfg.D, cfg.N, dtype, cfg.gate, variant, tokens_per_lane)
+
+
+def src_hash(kernel):
     h = hashlib.sha256()
-    for p in (KERNEL_SRC[kind], "selective_state_space_68_amd/csrc/device_common.hpp"):
+    for p in (KERNEL_SRC[kernel], "selective_state_space_68_amd/csrc/device_common.hpp"):
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(workload, kind):
+def traffic_from_profiles(workload, kernel):
     """HBM bytes per launch from committed rocprofv3 PMC summaries, or None when the
     kernel source changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
@@ -75,7 +90,7 @@ def traffic_from_profiles(workload, kind):
         return None
     with open(path) as f:
         rec = json.load(f).get(workload)
-    if not rec or rec.get("source_hash") != src_hash(kind):
+    if not rec or rec.get("source_hash") != src_hash(kernel):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -379,7 +394,8 @@ def main():
     elif kind in ("scan", "bwd") and not args.no_cpu_baseline and not cfg.conv_k:
         cpu = cpu_baseline_scan(cfg, inp, args.cpu_budget, dy=getattr(inp, "dy", None))
 
-    traffic = traffic_from_profiles(args.workload, kind)
+    kernel = kernel_of(cfg, kind, args.variant, args.kpl)
+    traffic = traffic_from_profiles(args.workload, kernel)
     hbm = {"achieved": hbm_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": hbm_gbs / PEAK_HBM_GBS,
            "algorithmic_bytes_per_launch": nbytes}
     if kind in ("scan", "bwd"):
@@ -391,13 +407,13 @@ def main():
                ZOH_ALU_SLOTS_PER_ELEMENT if cfg.discretization == "zoh" else ALU_SLOTS_PER_ELEMENT)
         slots = spe * elements
         alu = slots / launch_s / 1e12
-        roofline = {"bound": "alu", "kernel": KERNEL_NAME[kind],
+        roofline = {"bound": "alu", "kernel": kernel,
                     "achieved": alu, "peak": PEAK_VALU_TSLOTS, "unit": "T VALU slots/s",
                     "frac": alu / PEAK_VALU_TSLOTS, "traffic": traffic,
                     "algorithmic_slots_per_launch": slots, "slots_per_element": spe,
                     "avg_launch_us": launch_s * 1e6}
     else:
-        roofline = dict(hbm, bound="hbm", kernel=KERNEL_NAME[kind], traffic=traffic,
+        roofline = dict(hbm, bound="hbm", kernel=kernel, traffic=traffic,
                         avg_launch_us=launch_s * 1e6)
         if kind == "ssd":
             # the matrix-core side, for reference: the chunked form's products

@@ -111,14 +111,24 @@ ssm_status ssm_selective_scan_fwd_from_state(
 
 /*
  * Same operation with an explicit kernel choice, for testing that every
- * implementation agrees: SSM_SCAN_AUTO picks the fastest valid one;
+ * implementation agrees: SSM_SCAN_AUTO picks the fastest valid one (measured: the
+ * token-sequential kernel for N == 16 from 32768 channels batch * D, in bfloat16
+ * only below 65536; else the chunked kernel; else the sequential one);
  * SSM_SCAN_SEQUENTIAL runs one thread per (b, d) channel stepping through time
  * (the plain recurrence); SSM_SCAN_CHUNKED runs the chunked wave-scan kernel
- * (returns SSM_ERR_UNSUPPORTED when the shape does not fit it).
- * `tokens_per_lane` (0 = default) selects the chunked kernel's tokens per lane
- * (8 or 16).  Other arguments as in ssm_selective_scan_fwd_from_state.
+ * (returns SSM_ERR_UNSUPPORTED when the shape does not fit it); SSM_SCAN_TOKSEQ
+ * runs the token-sequential kernel, whose lanes own states and walk the tokens in
+ * order (N == 16, L % 8 == 0, 16-byte aligned activations, B and C; else
+ * SSM_ERR_UNSUPPORTED).  `tokens_per_lane` (0 = default) selects the chunked
+ * kernel's tokens per lane (8 or 16), and for SSM_SCAN_TOKSEQ the states per lane
+ * (4 or 2).  Other arguments as in ssm_selective_scan_fwd_from_state.
  */
-typedef enum { SSM_SCAN_AUTO = 0, SSM_SCAN_SEQUENTIAL = 1, SSM_SCAN_CHUNKED = 2 } ssm_scan_variant;
+typedef enum {
+  SSM_SCAN_AUTO = 0,
+  SSM_SCAN_SEQUENTIAL = 1,
+  SSM_SCAN_CHUNKED = 2,
+  SSM_SCAN_TOKSEQ = 3
+} ssm_scan_variant;
 
 ssm_status ssm_selective_scan_fwd_variant(
     const void *u, const void *delta, const float *A, const void *Bm, const void *Cm,
@@ -126,6 +136,15 @@ ssm_status ssm_selective_scan_fwd_variant(
     const float *initial_state, void *y, float *final_state,
     int64_t batch, int64_t L, int64_t D, int64_t N, ssm_dtype dt, void *stream,
     int variant, int tokens_per_lane);
+
+/*
+ * The kernel ssm_selective_scan_fwd_variant runs for a scan of this shape (L > 0)
+ * with 16-byte-aligned buffers, `gate` nonzero when z is given:
+ * SSM_SCAN_SEQUENTIAL, SSM_SCAN_CHUNKED or SSM_SCAN_TOKSEQ; or a negative
+ * ssm_status when such a call would be rejected.  Host-only: touches no device.
+ */
+int ssm_selective_scan_fwd_kernel(int64_t batch, int64_t L, int64_t D, int64_t N, ssm_dtype dt, int gate,
+                                  int variant, int tokens_per_lane);
 
 /*
  * One recurrent decode step (the O(1)-state generation mode): advances the

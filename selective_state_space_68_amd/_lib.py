@@ -23,6 +23,7 @@ SSM_BF16 = 1
 SSM_SCAN_AUTO = 0
 SSM_SCAN_SEQUENTIAL = 1
 SSM_SCAN_CHUNKED = 2
+SSM_SCAN_TOKSEQ = 3
 
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -36,6 +37,7 @@ SIGNATURES = {
                                                  _i64, _i64, _i64, _i64, _int, _vp]),
     "ssm_selective_scan_fwd_variant": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _vp, _vp, _vp,
                                               _i64, _i64, _i64, _i64, _int, _vp, _int, _int]),
+    "ssm_selective_scan_fwd_kernel": (_int, [_i64, _i64, _i64, _i64, _int, _int, _int, _int]),
     "ssm_selective_scan_fwd_zoh": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _vp, _vp, _vp,
                                           _i64, _i64, _i64, _i64, _int, _vp]),
     "ssm_state_update_zoh": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _vp,

@@ -23,7 +23,7 @@ ARCH = "gfx950"
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-command-line-argument",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-DEVICE_SOURCES = ["scan_sequential.hip", "scan_chunked.hip", "state_update.hip", "conv1d.hip", "scan_bwd.hip", "ssd.hip"]
+DEVICE_SOURCES = ["scan_sequential.hip", "scan_chunked.hip", "state_update.hip", "conv1d.hip", "scan_bwd.hip", "ssd.hip", "scan_tokseq.hip"]
 HOST_SOURCES = ["ssm_api.cpp"]
 
 

@@ -122,6 +122,14 @@ hipError_t launch_scan_sequential(const ScanArgs& a, Dt dt, hipStream_t s);
 bool chunked_supported(const ScanArgs& a, Dt dt, int tokens_per_lane);
 hipError_t launch_scan_chunked(const ScanArgs& a, Dt dt, int tokens_per_lane, hipStream_t s);
 
+// Token-sequential kernel for many channels: N == 16, L % 8 == 0, 16-byte aligned
+// activations, B and C; no fused conv, simplified discretization.  states_per_lane
+// 4 (default) or 2.
+bool tokseq_supported(const ScanArgs& a);
+// Whether the automatic choice runs the token-sequential kernel (measured crossovers).
+bool tokseq_preferred(const ScanArgs& a, Dt dt);
+hipError_t launch_scan_tokseq(const ScanArgs& a, Dt dt, int states_per_lane, hipStream_t s);
+
 // final_state = initial state, or zeros when src is null (the L == 0 scan).
 hipError_t launch_copy_state(float* dst, const float* src, int64_t n, hipStream_t s);
 

@@ -1,0 +1,289 @@
+// Token-sequential selective scan for gfx950, for workloads with many channels.
+//
+// The chunked kernel owns tokens per lane and pays for that with a wave scan, a
+// replay of every token and a per-lane aggregate decay, about 2.75 of its ~11.6
+// VALU issue slots per element.  When batch * D is large there are enough
+// (channel, state) pairs to give every lane its own states and walk the sequence
+// in order, as the recurrence is written (the slide deck's selective-SSM listing;
+// the prep page's sequential pseudo-code):
+//
+//   * a lane owns SPL consecutive states of one channel, 16 / SPL lanes (an aligned
+//     group) own a channel, and a wave owns 64 * SPL / 16 channels of one batch row;
+//   * per token a lane computes exp(Delta A), the state update and its part of the
+//     readout for its SPL states, and the group adds the parts with DPP (two
+//     quad_perm steps, plus a half-row mirror for 8-lane groups);
+//   * the per-token work (softplus, Delta * u, D * u, the SiLU gate) runs once per
+//     (token, channel): each lane does it for one 8-token piece of its channel in
+//     a block of 8 * 16 / SPL tokens and leaves (Delta, Delta * u) in LDS, and the
+//     readout of its piece's tokens ends up in the same lane for the output;
+//   * B and C of the block are staged in LDS as float32 [token][state], so a lane
+//     reads its SPL states of one token as one vector.
+//
+// Every wave uses its own LDS slice and never waits for another: a workgroup is
+// kTsWaves independent waves.  Loads of the next block are issued when the current
+// block's inputs have been written to LDS, so they have the whole block to arrive.
+// VALU issue per element: SPL x (multiply, exp, multiply, FMA) and the readout
+// FMA, plus the group reduction and the per-token work spread over 16 states.
+#include "device_common.hpp"
+#include "kernels.hpp"
+#include "scan_common.hpp"
+
+namespace ssm {
+namespace {
+
+constexpr int kTsWaves = 4;          // independent waves per workgroup
+constexpr int kTsN = 16;             // states per channel the kernel is built for
+
+// Eight consecutive B or C values of one state (a 16- or 32-byte load, cached:
+// every channel group of the batch row reads the same tile).
+template <typename ACT>
+struct Piece8;
+template <>
+struct Piece8<ActF32> {
+  float4 r[2];
+  __device__ __forceinline__ void load(const void* base, int64_t off) {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
+    r[0] = p[0];
+    r[1] = p[1];
+  }
+  __device__ __forceinline__ float get(int k) const {
+    const float4& v = r[k >> 2];
+    const int e = k & 3;
+    return e == 0 ? v.x : (e == 1 ? v.y : (e == 2 ? v.z : v.w));
+  }
+};
+template <>
+struct Piece8<ActBF16> {
+  uint4 r;
+  __device__ __forceinline__ void load(const void* base, int64_t off) {
+    r = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off);
+  }
+  __device__ __forceinline__ float get(int k) const {
+    const uint32_t w = (k >> 1) == 0 ? r.x : ((k >> 1) == 1 ? r.y : ((k >> 1) == 2 ? r.z : r.w));
+    return (k & 1) ? bf16_hi(w) : bf16_lo(w);
+  }
+};
+
+template <typename ACT, bool GATE, int SPL>
+__global__ __launch_bounds__(64 * kTsWaves) void scan_tokseq_kernel(ScanArgs p) {
+  constexpr int QL = kTsN / SPL;           // lanes per channel (an aligned group)
+  constexpr int CPW = 64 / QL;             // channels per wave
+  constexpr int T = 8 * QL;                // tokens per block: one 8-token piece per lane of a group
+  constexpr int DUS = 2 * T + 4;           // row stride (floats) of a channel's (Delta, Delta*u) pairs
+  constexpr int BCP = QL / 4;              // B (and C) pieces per lane per block
+  static_assert(SPL == 2 || SPL == 4, "4 or 8 lanes per channel");
+  using IO = TokenIO<ACT, 8>;
+  using raw_t = typename IO::raw_t;
+  // [wave][matrix][token][16 states]; the float4 group of states g of token t sits
+  // at group g ^ ((t / 8) % 4), so the lanes writing one token row of different
+  // pieces fall in different banks
+  __shared__ float4 s_bc[kTsWaves][2][T][kTsN / 4];
+  __shared__ __attribute__((aligned(16))) float s_du[kTsWaves][CPW * DUS];
+
+  const int lane = threadIdx.x & 63;
+  const int w = uniform_int(threadIdx.x >> 6);
+  const int64_t L = p.L, D = p.D;
+  const int64_t ngrp = (D + CPW - 1) / CPW;
+  // Consecutive workgroups go to different XCDs; the batch row is blockIdx % batch
+  // so that one row's B and C stay in one XCD's L2 when the batch size divides 8.
+  const int64_t b = blockIdx.x % p.batch;
+  const int64_t grp = static_cast<int64_t>(blockIdx.x / p.batch) * kTsWaves + w;
+  // A wave past the last channel group runs the last group and stores nothing; a
+  // lane past the last channel runs the last channel and stores nothing.
+  const int64_t gcl = grp < ngrp ? grp : ngrp - 1;
+  const int ch = lane / QL, q = lane % QL;           // channel in the wave; state group and token piece
+  const int64_t d_own = gcl * CPW + ch;
+  const bool store_ok = grp < ngrp && d_own < D;
+  const int64_t d = d_own < D ? d_own : D - 1;
+  const int64_t row = (b * D + d) * L;
+  const float bias = p.bias ? p.bias[d] : 0.0f;
+  const float dsk = p.Dskip ? p.Dskip[d] : 0.0f;
+  float a2[SPL], h[SPL];
+#pragma unroll
+  for (int j = 0; j < SPL; ++j) {
+    const int64_t sidx = d * kTsN + SPL * q + j;
+    a2[j] = p.A[sidx] * kLog2e;
+    h[j] = p.h0 ? p.h0[(b * D + d) * kTsN + SPL * q + j] : 0.0f;
+  }
+  const int64_t bc_row = b * kTsN * L;               // B, C rows of this batch row ([N][L])
+  float* du_w = s_du[w];
+  float* bc_w = reinterpret_cast<float*>(s_bc[w]);
+
+  // Block inputs in registers: this lane's piece (tokens 8q .. 8q+7 of the block) of
+  // u, delta and z, and its BCP pieces of B and C (piece v = lane + 64k: state
+  // v / QL, tokens 8 (v % QL) ..).  Pieces past L (L % 8 == 0: a piece is all in or
+  // all out) reload the row's last piece; their Delta is set to 0.
+  raw_t u_raw[IO::kVec], d_raw[IO::kVec], z_raw[IO::kVec];
+  Piece8<ACT> bp[BCP], cp[BCP];
+  auto fetch = [&](int64_t t0) __attribute__((always_inline)) {
+    int64_t tp = t0 + 8 * q;
+    tp = tp + 8 <= L ? tp : L - 8;
+    IO::load_raw(p.u, row + tp, u_raw);
+    IO::load_raw(p.delta, row + tp, d_raw);
+    if constexpr (GATE) IO::load_raw(p.z, row + tp, z_raw);
+#pragma unroll
+    for (int k = 0; k < BCP; ++k) {
+      const int v = lane + 64 * k, n = v / QL, pc = v % QL;
+      int64_t t = t0 + 8 * pc;
+      t = t + 8 <= L ? t : L - 8;
+      bp[k].load(p.Bm, bc_row + n * L + t);
+      cp[k].load(p.Cm, bc_row + n * L + t);
+    }
+  };
+
+  const int64_t nblk = (L + T - 1) / T;
+  fetch(0);
+  for (int64_t blk = 0; blk < nblk; ++blk) {
+    const int64_t t0 = blk * T;
+    const bool pvalid = t0 + 8 * q < L;
+    // ---- per-token work of this lane's piece; (Delta, Delta*u) and the B/C tile to LDS
+    float uv[8], dl[8], ysk[8], gt[8] = {};
+    IO::unpack(u_raw, uv);
+    IO::unpack(d_raw, dl);
+    if constexpr (GATE) {
+      float zv[8];
+      IO::unpack(z_raw, zv);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) gt[k] = silu_f(zv[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float x = dl[k] + bias;
+      dl[k] = p.softplus ? softplus_f(x) : x;
+      dl[k] = pvalid ? dl[k] : 0.0f;                 // padding tokens: identity steps
+      ysk[k] = dsk * uv[k];
+    }
+    float4* dst = reinterpret_cast<float4*>(du_w + ch * DUS + 16 * q);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      dst[k] = make_float4(dl[2 * k], dl[2 * k] * uv[2 * k], dl[2 * k + 1], dl[2 * k + 1] * uv[2 * k + 1]);
+#pragma unroll
+    for (int k = 0; k < BCP; ++k) {
+      const int v = lane + 64 * k, n = v / QL, pc = v % QL;
+      const int col = 4 * ((n >> 2) ^ (pc & 3)) + (n & 3);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int t = 8 * pc + e;
+        bc_w[(0 * T + t) * kTsN + col] = bp[k].get(e);
+        bc_w[(1 * T + t) * kTsN + col] = cp[k].get(e);
+      }
+    }
+    // the wave's own LDS writes before its reads (one wave's LDS operations are
+    // performed in order; this keeps the compiler from moving reads above writes)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    fetch(t0 + T < L ? t0 + T : t0);                 // next block (the last one reloads itself, unused)
+
+    // ---- the recurrence, token by token; lane q keeps the readout of tokens 8q .. 8q+7
+    float rsel[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) rsel[k] = 0.0f;
+    const float* du_c = du_w + ch * DUS;
+    const int qg = SPL == 4 ? q : q >> 1;           // this lane's float4 group of states
+    // (fully unrolled: the compiler then pipelines the LDS reads across pieces, 2-5 %
+    // faster at the 2-3 waves per SIMD this kernel runs with)
+#pragma unroll
+    for (int tb = 0; tb < T / 8; ++tb) {             // 8-token piece tb (its per-token work was lane tb's)
+      const int gsw = qg ^ (tb & 3);
+      const float* brow = bc_w + (0 * T + 8 * tb) * kTsN;
+      const float* crow = bc_w + (1 * T + 8 * tb) * kTsN;
+      const bool mine = q == tb;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float2 dd = *reinterpret_cast<const float2*>(du_c + 2 * (8 * tb + k));
+        float bs[SPL], cs[SPL];
+        if constexpr (SPL == 4) {
+          const float4 bb = reinterpret_cast<const float4*>(brow + k * kTsN)[gsw];
+          const float4 cc = reinterpret_cast<const float4*>(crow + k * kTsN)[gsw];
+          bs[0] = bb.x; bs[1] = bb.y; bs[2] = bb.z; bs[3] = bb.w;
+          cs[0] = cc.x; cs[1] = cc.y; cs[2] = cc.z; cs[3] = cc.w;
+        } else {
+          const float2 bb = reinterpret_cast<const float2*>(brow + k * kTsN)[2 * gsw + (q & 1)];
+          const float2 cc = reinterpret_cast<const float2*>(crow + k * kTsN)[2 * gsw + (q & 1)];
+          bs[0] = bb.x; bs[1] = bb.y;
+          cs[0] = cc.x; cs[1] = cc.y;
+        }
+        float r = 0.0f;
+#pragma unroll
+        for (int j = 0; j < SPL; ++j) {
+          const float a = exp2_hw(dd.x * a2[j]);
+          h[j] = __builtin_fmaf(a, h[j], dd.y * bs[j]);
+          r = __builtin_fmaf(cs[j], h[j], r);
+        }
+        r += dpp_mov<0xB1, 0xf, false>(0.0f, r);     // quad_perm [1, 0, 3, 2]
+        r += dpp_mov<0x4E, 0xf, false>(0.0f, r);     // quad_perm [2, 3, 0, 1]
+        if constexpr (SPL == 2) r += dpp_mov<0x141, 0xf, false>(0.0f, r);   // row_half_mirror
+        rsel[k] = mine ? r : rsel[k];
+      }
+    }
+    // ---- the outputs of this lane's piece
+    if (store_ok && pvalid) {
+      float yv[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        yv[k] = rsel[k] + ysk[k];
+        if constexpr (GATE) yv[k] *= gt[k];
+      }
+      IO::store(p.y, row + t0 + 8 * q, yv);
+    }
+    // reads of this block's LDS before the next block's writes
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+  if (store_ok && p.final_state) {
+#pragma unroll
+    for (int j = 0; j < SPL; ++j) p.final_state[(b * D + d) * kTsN + SPL * q + j] = h[j];
+  }
+}
+
+bool aligned16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; }
+
+template <typename ACT, bool GATE, int SPL>
+hipError_t launch_spl(const ScanArgs& a, hipStream_t s) {
+  constexpr int CPW = 64 * SPL / kTsN;
+  const int64_t ngrp = (a.D + CPW - 1) / CPW;
+  const int64_t blocks = a.batch * ((ngrp + kTsWaves - 1) / kTsWaves);
+  hipLaunchKernelGGL((scan_tokseq_kernel<ACT, GATE, SPL>), dim3(static_cast<unsigned>(blocks)), dim3(64 * kTsWaves), 0,
+                     s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool tokseq_supported(const ScanArgs& a) {
+  if (a.N != kTsN || a.conv_w != nullptr || a.zoh) return false;
+  if (a.L < 8 || a.L % 8 != 0) return false;
+  if (!aligned16(a.u) || !aligned16(a.delta) || !aligned16(a.y) || !aligned16(a.Bm) || !aligned16(a.Cm)) return false;
+  if (a.z != nullptr && !aligned16(a.z)) return false;
+  const int64_t ngrp = (a.D + 8 - 1) / 8;            // the smallest channel group (SPL = 2)
+  return a.batch * ((ngrp + kTsWaves - 1) / kTsWaves) <= 0x7fffffff;
+}
+
+// Measured on gfx950 (256 CUs), N = 16, 2048 tokens, against the chunked kernel:
+//  * float32: 18 % faster from 32768 channels (2 waves per SIMD at 4 states per
+//    lane; 305 against 372 us at 4 x 8192 channels), even at 16384;
+//  * bfloat16: 3-5 % faster at 32768 channels (289 against 303 us on the 1.4B-shaped
+//    workload), 1 % slower at 65536 where the chunked kernel's two 8-wave groups per
+//    CU have enough waves, 25 % slower at 16384;
+//  * slower everywhere below 16384 channels (too few waves: it has no split of the
+//    sequence).  Two states per lane (twice the waves) measured slower throughout.
+bool tokseq_preferred(const ScanArgs& a, Dt dt) {
+  if (!tokseq_supported(a)) return false;
+  const int64_t ch = a.batch * a.D;
+  if (dt == Dt::F32) return ch >= 32768;
+  return ch >= 32768 && ch < 65536;
+}
+
+hipError_t launch_scan_tokseq(const ScanArgs& a, Dt dt, int states_per_lane, hipStream_t s) {
+  if (!tokseq_supported(a)) return hipErrorInvalidValue;
+  const bool gate = a.z != nullptr;
+  const int spl = states_per_lane == 2 ? 2 : 4;
+  if (dt == Dt::F32) {
+    if (spl == 4) return gate ? launch_spl<ActF32, true, 4>(a, s) : launch_spl<ActF32, false, 4>(a, s);
+    return gate ? launch_spl<ActF32, true, 2>(a, s) : launch_spl<ActF32, false, 2>(a, s);
+  }
+  if (spl == 4) return gate ? launch_spl<ActBF16, true, 4>(a, s) : launch_spl<ActBF16, false, 4>(a, s);
+  return gate ? launch_spl<ActBF16, true, 2>(a, s) : launch_spl<ActBF16, false, 2>(a, s);
+}
+
+}  // namespace ssm

@@ -11,7 +11,7 @@
 
 namespace {
 
-constexpr int kVersion = 20500;  // 2.5.0: + Mamba-2 SSD scan
+constexpr int kVersion = 20600;  // 2.6.0: + token-sequential scan kernel (SSM_SCAN_TOKSEQ)
 
 struct Span {
   uintptr_t lo = 0, hi = 0;  // [lo, hi); empty when lo == hi
@@ -170,6 +170,27 @@ int ssm_version(void) { return kVersion; }
 
 namespace {
 
+// The per-kernel option: tokens per lane of the chunked kernel (8 or 16), states
+// per lane of the token-sequential kernel (2 or 4); 0 = default.
+bool kernel_option_ok(int variant, int tokens_per_lane) {
+  if (variant == SSM_SCAN_TOKSEQ) return tokens_per_lane == 0 || tokens_per_lane == 2 || tokens_per_lane == 4;
+  return tokens_per_lane == 0 || tokens_per_lane == 8 || tokens_per_lane == 16;
+}
+
+// The kernel a scan with these arguments runs (L > 0): SSM_SCAN_SEQUENTIAL,
+// SSM_SCAN_CHUNKED or SSM_SCAN_TOKSEQ, or minus SSM_ERR_UNSUPPORTED.
+int choose_scan_kernel(const ssm::ScanArgs& a, ssm::Dt d, int variant, int tokens_per_lane) {
+  const bool tokseq = (variant == SSM_SCAN_TOKSEQ && ssm::tokseq_supported(a)) ||
+                      (variant == SSM_SCAN_AUTO && tokens_per_lane == 0 && ssm::tokseq_preferred(a, d));
+  if (variant == SSM_SCAN_TOKSEQ && !tokseq) return -SSM_ERR_UNSUPPORTED;
+  if (tokseq) return SSM_SCAN_TOKSEQ;
+  const bool chunked = (variant == SSM_SCAN_AUTO || variant == SSM_SCAN_CHUNKED) &&
+                       ssm::chunked_supported(a, d, tokens_per_lane);
+  if (variant == SSM_SCAN_CHUNKED && !chunked) return -SSM_ERR_UNSUPPORTED;
+  if (a.zoh && !chunked) return -SSM_ERR_UNSUPPORTED;   // only the chunked kernel has the full hold
+  return chunked ? SSM_SCAN_CHUNKED : SSM_SCAN_SEQUENTIAL;
+}
+
 ssm_status scan_fwd(const void* u, const void* delta, const float* A, const void* Bm, const void* Cm,
                     const float* Dskip, const void* z, const float* delta_bias, int delta_softplus,
                     const float* initial_state, void* y, float* final_state, int64_t batch, int64_t L, int64_t D,
@@ -178,23 +199,25 @@ ssm_status scan_fwd(const void* u, const void* delta, const float* A, const void
   ssm_status st = check_scan(u, delta, A, Bm, Cm, Dskip, z, delta_bias, delta_softplus, initial_state, y,
                              final_state, batch, L, D, N, dt, &sz);
   if (st != SSM_OK) return st;
-  if (variant != SSM_SCAN_AUTO && variant != SSM_SCAN_SEQUENTIAL && variant != SSM_SCAN_CHUNKED)
+  if (variant != SSM_SCAN_AUTO && variant != SSM_SCAN_SEQUENTIAL && variant != SSM_SCAN_CHUNKED &&
+      variant != SSM_SCAN_TOKSEQ)
     return SSM_ERR_UNSUPPORTED;
-  if (!(tokens_per_lane == 0 || tokens_per_lane == 8 || tokens_per_lane == 16)) return SSM_ERR_UNSUPPORTED;
+  if (!kernel_option_ok(variant, tokens_per_lane)) return SSM_ERR_UNSUPPORTED;
   if (batch == 0 || D == 0) return SSM_OK;  // nothing to compute or write
   ssm::ScanArgs a;
   a.u = u; a.delta = delta; a.A = A; a.Bm = Bm; a.Cm = Cm; a.Dskip = Dskip; a.z = z;
   a.bias = delta_bias; a.h0 = initial_state; a.y = y; a.final_state = final_state;
   a.batch = batch; a.L = L; a.D = D; a.N = static_cast<int>(N); a.softplus = delta_softplus; a.zoh = zoh;
   const ssm::Dt d = dt == SSM_BF16 ? ssm::Dt::BF16 : ssm::Dt::F32;
-  const bool chunked = L > 0 && variant != SSM_SCAN_SEQUENTIAL && ssm::chunked_supported(a, d, tokens_per_lane);
-  if (variant == SSM_SCAN_CHUNKED && L > 0 && !chunked) return SSM_ERR_UNSUPPORTED;
-  if (zoh && L > 0 && !chunked) return SSM_ERR_UNSUPPORTED;   // only the chunked kernel has the full hold
+  const int kernel = L > 0 ? choose_scan_kernel(a, d, variant, tokens_per_lane) : SSM_SCAN_SEQUENTIAL;
+  if (kernel < 0) return static_cast<ssm_status>(-kernel);
+  const bool tokseq = L > 0 && kernel == SSM_SCAN_TOKSEQ, chunked = L > 0 && kernel == SSM_SCAN_CHUNKED;
   st = probe_device();
   if (st != SSM_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (L == 0)  // the final state is the initial state
     return final_state ? from_hip(ssm::launch_copy_state(final_state, initial_state, batch * D * N, s)) : SSM_OK;
+  if (tokseq) return from_hip(ssm::launch_scan_tokseq(a, d, tokens_per_lane, s));
   if (chunked) return from_hip(ssm::launch_scan_chunked(a, d, tokens_per_lane, s));
   return from_hip(ssm::launch_scan_sequential(a, d, s));
 }
@@ -211,6 +234,24 @@ ssm_status ssm_selective_scan_fwd_variant(const void* u, const void* delta, cons
                                           void* stream, int variant, int tokens_per_lane) {
   return scan_fwd(u, delta, A, Bm, Cm, Dskip, z, delta_bias, delta_softplus, initial_state, y, final_state, batch, L,
                   D, N, dt, stream, variant, tokens_per_lane, 0);
+}
+
+int ssm_selective_scan_fwd_kernel(int64_t batch, int64_t L, int64_t D, int64_t N, ssm_dtype dt, int gate,
+                                  int variant, int tokens_per_lane) {
+  if (dt != SSM_F32 && dt != SSM_BF16) return -SSM_ERR_UNSUPPORTED;
+  if (batch <= 0 || L <= 0 || D <= 0 || N < 1) return -SSM_ERR_INVALID_ARG;
+  if (N > SSM_MAX_N) return -SSM_ERR_UNSUPPORTED;
+  if (variant != SSM_SCAN_AUTO && variant != SSM_SCAN_SEQUENTIAL && variant != SSM_SCAN_CHUNKED &&
+      variant != SSM_SCAN_TOKSEQ)
+    return -SSM_ERR_UNSUPPORTED;
+  if (!kernel_option_ok(variant, tokens_per_lane)) return -SSM_ERR_UNSUPPORTED;
+  // stand-in pointers: 256-byte aligned, never dereferenced
+  void* const any = reinterpret_cast<void*>(uintptr_t(256));
+  ssm::ScanArgs a;
+  a.u = any; a.delta = any; a.A = static_cast<const float*>(any); a.Bm = any; a.Cm = any; a.Dskip = nullptr;
+  a.z = gate ? any : nullptr; a.bias = nullptr; a.h0 = nullptr; a.y = any; a.final_state = nullptr;
+  a.batch = batch; a.L = L; a.D = D; a.N = static_cast<int>(N); a.softplus = 1; a.zoh = 0;
+  return choose_scan_kernel(a, dt == SSM_BF16 ? ssm::Dt::BF16 : ssm::Dt::F32, variant, tokens_per_lane);
 }
 
 ssm_status ssm_selective_scan_fwd_zoh(const void* u, const void* delta, const float* A, const void* Bm,

@@ -95,6 +95,22 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta
     return y, final_state
 
 
+SCAN_KERNELS = {_lib.SSM_SCAN_SEQUENTIAL: "scan_sequential_kernel", _lib.SSM_SCAN_CHUNKED: "scan_chunked_kernel",
+                _lib.SSM_SCAN_TOKSEQ: "scan_tokseq_kernel"}
+
+
+def selective_scan_fwd_kernel(batch, L, D, N, dtype=torch.float32, gate=True, variant=0, tokens_per_lane=0) -> str:
+    """Name of the kernel selective_scan_fwd runs for this shape (16-byte-aligned
+    tensors, L > 0).  Raises SsmError when such a call would be rejected."""
+    lib = _lib.load_library()
+    dt = _lib.SSM_BF16 if dtype == torch.bfloat16 else _lib.SSM_F32
+    k = lib.ssm_selective_scan_fwd_kernel(int(batch), int(L), int(D), int(N), dt, 1 if gate else 0, int(variant),
+                                          int(tokens_per_lane))
+    if k < 0:
+        _lib.check(-k)
+    return SCAN_KERNELS[k]
+
+
 def selective_scan_bwd_workspace_size(batch, L, D, N, dtype=torch.float32) -> int:
     """Bytes of device workspace selective_scan_bwd needs for this shape."""
     lib = _lib.load_library()

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.ssm_version() == 20500
+    assert lib.ssm_version() == 20600
     for s in range(4):
         assert lib.ssm_status_string(s).decode().startswith(("SSM_OK", "SSM_ERR"))
     assert b"unknown" in lib.ssm_status_string(99)
@@ -266,6 +266,31 @@ def test_ssd_workspace_size(lib):
     assert ws(4, 2048, 80, 64, 64, 0) == 0 and ws(4, 2048, 80, 32, 64, 1) == 0
     assert _ssd(lib) == _lib.SSM_ERR_HIP                            # valid arguments reach the device probe
     assert _ssd(lib, batch=0) == _lib.SSM_OK
+
+
+def test_scan_kernel_choice(lib):
+    """The kernel query (host-only) follows the documented choice: the token-sequential
+    kernel for N = 16 from 32768 channels (bfloat16 only below 65536), the chunked
+    kernel otherwise, and the explicit variants as asked."""
+    k = lib.ssm_selective_scan_fwd_kernel
+    F32, BF16 = _lib.SSM_F32, _lib.SSM_BF16
+    SEQ, CHK, TOK = _lib.SSM_SCAN_SEQUENTIAL, _lib.SSM_SCAN_CHUNKED, _lib.SSM_SCAN_TOKSEQ
+    assert k(2, 2048, 1536, 16, F32, 1, 0, 0) == CHK                # 130M-shaped
+    assert k(8, 2048, 4096, 16, BF16, 1, 0, 0) == TOK               # 1.4B-shaped: 32768 channels
+    assert k(8, 2048, 4096, 16, F32, 1, 0, 0) == TOK
+    assert k(16, 2048, 4096, 16, BF16, 1, 0, 0) == CHK              # 65536 bfloat16 channels
+    assert k(16, 2048, 4096, 16, F32, 0, 0, 0) == TOK
+    assert k(4, 2048, 4095, 16, BF16, 1, 0, 0) == CHK               # 16380 channels
+    assert k(8, 2048, 4096, 8, BF16, 1, 0, 0) == CHK                # N != 16
+    assert k(8, 2044, 4096, 16, BF16, 1, 0, 0) == CHK               # L % 8 != 0
+    assert k(8, 2048, 4096, 16, BF16, 1, 0, 16) == CHK              # a chunked option pins the chunked kernel
+    assert k(1, 64, 16, 4, F32, 0, SEQ, 0) == SEQ
+    assert k(1, 64, 16, 16, F32, 0, TOK, 2) == TOK                  # asked for: any supported size
+    assert k(1, 100, 16, 16, F32, 0, TOK, 0) == -_lib.SSM_ERR_UNSUPPORTED
+    assert k(1, 64, 16, 16, F32, 0, TOK, 8) == -_lib.SSM_ERR_UNSUPPORTED   # states per lane: 2 or 4
+    assert k(1, 64, 16, 65, F32, 0, 0, 0) == -_lib.SSM_ERR_UNSUPPORTED
+    assert k(1, 64, 16, 16, F32, 0, 7, 0) == -_lib.SSM_ERR_UNSUPPORTED
+    assert k(0, 64, 16, 16, F32, 0, 0, 0) == -_lib.SSM_ERR_INVALID_ARG
 
 
 def test_state_update_empty_is_noop(lib):

@@ -100,10 +100,14 @@ def test_many_channels_sampled(dtype):
     (1, 1100, 3080, 16, "bf16"),   # L % 8 != 0: the scalar-load kernel keeps 12-wave groups
     (2, 520, 1700, 32, "bf16"),    # the any-N kernel in 8-wave groups
     (3, 600, 4100, 16, "f32"),     # 12300 channels: 16-wave groups, the last one ragged
+    (2, 264, 16401, 16, "bf16"),   # 32802 channels: the token-sequential kernel, last lane group ragged
+    (1, 264, 32771, 16, "f32"),    # 32771 channels: the token-sequential kernel in float32
+    (4, 264, 16400, 16, "bf16"),   # 65600 channels: back to the chunked kernel for bfloat16
 ], ids=lambda s: "x".join(map(str, s)))
 def test_workgroup_size_boundaries(shape):
-    """Channel counts on both sides of the launch's workgroup-size rule, with a
-    ragged last workgroup; every channel's last outputs are checked."""
+    """Channel counts on both sides of the launch's workgroup-size rules and of the
+    automatic choice of the token-sequential kernel, with a ragged last workgroup;
+    every batch row's last channels are checked."""
     batch, L, D, N, dtype = shape
     inp = synth.make_scan_inputs(batch, L, D, N, dtype, seed=D + L, a_kind="lognormal", d_skip="normal")
     y, fs = run_scan(inp)
