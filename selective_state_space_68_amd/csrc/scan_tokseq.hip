@@ -64,6 +64,40 @@ struct Piece8<ActBF16> {
   }
 };
 
+// Eight consecutive activations of one channel, cached (temporal) loads and stores.
+// In bfloat16 a channel's block is 64 bytes, half a cache line, and the other half
+// is the next block's: non-temporal accesses lost the line in between and fetched
+// every line twice (1.69x the algorithmic HBM reads, 3 % slower).
+template <typename ACT>
+struct ActIO8;
+template <>
+struct ActIO8<ActF32> {
+  using raw_t = float4;
+  static constexpr int kVec = 2;
+  static __device__ __forceinline__ void load_raw(const void* base, int64_t off, raw_t (&r)[2]) {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
+    r[0] = p[0]; r[1] = p[1];
+  }
+  static __device__ __forceinline__ void unpack(const raw_t (&r)[2], float (&v)[8]) { TokenIO<ActF32, 8>::unpack(r, v); }
+  static __device__ __forceinline__ void store(void* base, int64_t off, const float (&v)[8]) {
+    float4* p = reinterpret_cast<float4*>(static_cast<float*>(base) + off);
+    p[0] = make_float4(v[0], v[1], v[2], v[3]); p[1] = make_float4(v[4], v[5], v[6], v[7]);
+  }
+};
+template <>
+struct ActIO8<ActBF16> {
+  using raw_t = uint4;
+  static constexpr int kVec = 1;
+  static __device__ __forceinline__ void load_raw(const void* base, int64_t off, raw_t (&r)[1]) {
+    r[0] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off);
+  }
+  static __device__ __forceinline__ void unpack(const raw_t (&r)[1], float (&v)[8]) { TokenIO<ActBF16, 8>::unpack(r, v); }
+  static __device__ __forceinline__ void store(void* base, int64_t off, const float (&v)[8]) {
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + off) =
+        make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+  }
+};
+
 template <typename ACT, bool GATE, int SPL>
 __global__ __launch_bounds__(64 * kTsWaves) void scan_tokseq_kernel(ScanArgs p) {
   constexpr int QL = kTsN / SPL;           // lanes per channel (an aligned group)
@@ -72,7 +106,7 @@ __global__ __launch_bounds__(64 * kTsWaves) void scan_tokseq_kernel(ScanArgs p) 
   constexpr int DUS = 2 * T + 4;           // row stride (floats) of a channel's (Delta, Delta*u) pairs
   constexpr int BCP = QL / 4;              // B (and C) pieces per lane per block
   static_assert(SPL == 2 || SPL == 4, "4 or 8 lanes per channel");
-  using IO = TokenIO<ACT, 8>;
+  using IO = ActIO8<ACT>;
   using raw_t = typename IO::raw_t;
   // [wave][matrix][token][16 states]; the float4 group of states g of token t sits
   // at group g ^ ((t / 8) % 4), so the lanes writing one token row of different
