@@ -112,8 +112,8 @@ ssm_status ssm_selective_scan_fwd_from_state(
 /*
  * Same operation with an explicit kernel choice, for testing that every
  * implementation agrees: SSM_SCAN_AUTO picks the fastest valid one (measured: the
- * token-sequential kernel for N == 16 from 32768 channels batch * D, in bfloat16
- * only below 65536; else the chunked kernel; else the sequential one);
+ * token-sequential kernel for N == 16 from 32768 channels batch * D; else the
+ * chunked kernel; else the sequential one);
  * SSM_SCAN_SEQUENTIAL runs one thread per (b, d) channel stepping through time
  * (the plain recurrence); SSM_SCAN_CHUNKED runs the chunked wave-scan kernel
  * (returns SSM_ERR_UNSUPPORTED when the shape does not fit it); SSM_SCAN_TOKSEQ

@@ -293,19 +293,16 @@ bool tokseq_supported(const ScanArgs& a) {
   return a.batch * ((ngrp + kTsWaves - 1) / kTsWaves) <= 0x7fffffff;
 }
 
-// Measured on gfx950 (256 CUs), N = 16, 2048 tokens, against the chunked kernel:
-//  * float32: 18 % faster from 32768 channels (2 waves per SIMD at 4 states per
-//    lane; 305 against 372 us at 4 x 8192 channels), even at 16384;
-//  * bfloat16: 3-5 % faster at 32768 channels (289 against 303 us on the 1.4B-shaped
-//    workload), 1 % slower at 65536 where the chunked kernel's two 8-wave groups per
-//    CU have enough waves, 25 % slower at 16384;
-//  * slower everywhere below 16384 channels (too few waves: it has no split of the
-//    sequence).  Two states per lane (twice the waves) measured slower throughout.
-bool tokseq_preferred(const ScanArgs& a, Dt dt) {
-  if (!tokseq_supported(a)) return false;
-  const int64_t ch = a.batch * a.D;
-  if (dt == Dt::F32) return ch >= 32768;
-  return ch >= 32768 && ch < 65536;
+// Measured on gfx950 (256 CUs), N = 16, 2048 tokens, against the chunked kernel.
+// The kernel has no split of the sequence, so it needs channels: at 4 states per
+// lane a SIMD gets batch * D / 16384 waves.
+//  * 32768 channels (2 waves per SIMD): bfloat16 8 % faster (279 against 302 us on
+//    the 1.4B-shaped workload), float32 18 % faster;
+//  * 49152 and 65536 channels: bfloat16 13-15 % and float32 16 % faster;
+//  * 24576 channels (1.5 waves per SIMD, unevenly spread) and 16384: bfloat16
+//    17-22 % slower, float32 even.  Two states per lane measured slower throughout.
+bool tokseq_preferred(const ScanArgs& a, Dt) {
+  return tokseq_supported(a) && a.batch * a.D >= 32768;
 }
 
 hipError_t launch_scan_tokseq(const ScanArgs& a, Dt dt, int states_per_lane, hipStream_t s) {

@@ -270,15 +270,16 @@ def test_ssd_workspace_size(lib):
 
 def test_scan_kernel_choice(lib):
     """The kernel query (host-only) follows the documented choice: the token-sequential
-    kernel for N = 16 from 32768 channels (bfloat16 only below 65536), the chunked
-    kernel otherwise, and the explicit variants as asked."""
+    kernel for N = 16 from 32768 channels, the chunked kernel otherwise, and the
+    explicit variants as asked."""
     k = lib.ssm_selective_scan_fwd_kernel
     F32, BF16 = _lib.SSM_F32, _lib.SSM_BF16
     SEQ, CHK, TOK = _lib.SSM_SCAN_SEQUENTIAL, _lib.SSM_SCAN_CHUNKED, _lib.SSM_SCAN_TOKSEQ
     assert k(2, 2048, 1536, 16, F32, 1, 0, 0) == CHK                # 130M-shaped
     assert k(8, 2048, 4096, 16, BF16, 1, 0, 0) == TOK               # 1.4B-shaped: 32768 channels
     assert k(8, 2048, 4096, 16, F32, 1, 0, 0) == TOK
-    assert k(16, 2048, 4096, 16, BF16, 1, 0, 0) == CHK              # 65536 bfloat16 channels
+    assert k(16, 2048, 4096, 16, BF16, 1, 0, 0) == TOK              # 65536 channels
+    assert k(2, 2048, 16383, 16, BF16, 1, 0, 0) == CHK              # 32766 channels
     assert k(16, 2048, 4096, 16, F32, 0, 0, 0) == TOK
     assert k(4, 2048, 4095, 16, BF16, 1, 0, 0) == CHK               # 16380 channels
     assert k(8, 2048, 4096, 8, BF16, 1, 0, 0) == CHK                # N != 16

@@ -102,7 +102,7 @@ def test_many_channels_sampled(dtype):
     (3, 600, 4100, 16, "f32"),     # 12300 channels: 16-wave groups, the last one ragged
     (2, 264, 16401, 16, "bf16"),   # 32802 channels: the token-sequential kernel, last lane group ragged
     (1, 264, 32771, 16, "f32"),    # 32771 channels: the token-sequential kernel in float32
-    (4, 264, 16400, 16, "bf16"),   # 65600 channels: back to the chunked kernel for bfloat16
+    (2, 264, 16383, 16, "bf16"),   # 32766 channels: still the chunked kernel (8-wave groups)
 ], ids=lambda s: "x".join(map(str, s)))
 def test_workgroup_size_boundaries(shape):
     """Channel counts on both sides of the launch's workgroup-size rules and of the
