@@ -62,16 +62,14 @@ PEAK_MFMA_BF16_TFLOPS = 2500.0
 
 def kernel_of(cfg, kind, variant=0, tokens_per_lane=0):
     """The kernel (or, for the backward, the call) a workload's timed region runs.
-    The forward scan asks the library which kernel it picks for the shape; the full
-    zero-order hold and the fused conv always run the chunked kernel."""
+    The forward scan asks the library which kernel it picks for the shape."""
     if kind != "scan":
         return KERNEL_NAME[kind]
-    if cfg.discretization == "zoh" or cfg.conv_k:
-        return "scan_chunked_kernel"
     import torch
     from selective_state_space_68_amd import selective_scan_fwd_kernel
     dtype = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
-    return selective_scan_fwd_kernel(cfg.batch, cfg.L, cfg.D, cfg.N, dtype, cfg.gate, variant, tokens_per_lane)
+    return selective_scan_fwd_kernel(cfg.batch, cfg.L, cfg.D, cfg.N, dtype, cfg.gate, cfg.discretization,
+                                     cfg.conv_k, variant, tokens_per_lane)
 
 
 def src_hash(kernel):

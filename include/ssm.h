@@ -138,13 +138,16 @@ ssm_status ssm_selective_scan_fwd_variant(
     int variant, int tokens_per_lane);
 
 /*
- * The kernel ssm_selective_scan_fwd_variant runs for a scan of this shape (L > 0)
- * with 16-byte-aligned buffers, `gate` nonzero when z is given:
+ * The kernel a forward scan of this shape (L > 0) with 16-byte-aligned buffers runs:
  * SSM_SCAN_SEQUENTIAL, SSM_SCAN_CHUNKED or SSM_SCAN_TOKSEQ; or a negative
- * ssm_status when such a call would be rejected.  Host-only: touches no device.
+ * ssm_status when such a call would be rejected.  `gate` nonzero when z is given;
+ * `zoh` nonzero for ssm_selective_scan_fwd_zoh, `conv_width` > 0 for
+ * ssm_selective_scan_fwd_conv (those two take variant SSM_SCAN_AUTO only);
+ * otherwise the call is ssm_selective_scan_fwd_variant(variant, tokens_per_lane).
+ * Host-only: touches no device.
  */
-int ssm_selective_scan_fwd_kernel(int64_t batch, int64_t L, int64_t D, int64_t N, ssm_dtype dt, int gate,
-                                  int variant, int tokens_per_lane);
+int ssm_selective_scan_fwd_kernel(int64_t batch, int64_t L, int64_t D, int64_t N, ssm_dtype dt, int gate, int zoh,
+                                  int conv_width, int variant, int tokens_per_lane);
 
 /*
  * One recurrent decode step (the O(1)-state generation mode): advances the

@@ -37,7 +37,7 @@ SIGNATURES = {
                                                  _i64, _i64, _i64, _i64, _int, _vp]),
     "ssm_selective_scan_fwd_variant": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _vp, _vp, _vp,
                                               _i64, _i64, _i64, _i64, _int, _vp, _int, _int]),
-    "ssm_selective_scan_fwd_kernel": (_int, [_i64, _i64, _i64, _i64, _int, _int, _int, _int]),
+    "ssm_selective_scan_fwd_kernel": (_int, [_i64, _i64, _i64, _i64, _int, _int, _int, _int, _int, _int]),
     "ssm_selective_scan_fwd_zoh": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _vp, _vp, _vp,
                                           _i64, _i64, _i64, _i64, _int, _vp]),
     "ssm_state_update_zoh": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _vp,

@@ -98,7 +98,10 @@ struct ActIO8<ActBF16> {
   }
 };
 
-template <typename ACT, bool GATE, int SPL>
+// ZOH: the full zero-order-hold input term (e^{Delta A} - 1)/A * B * u = a w - w with
+// w = u (1/A) B (a = e^{Delta A}): the lanes keep (Delta, u) instead of
+// (Delta, Delta u) in LDS, and 1/A per state.
+template <typename ACT, bool GATE, int SPL, bool ZOH>
 __global__ __launch_bounds__(64 * kTsWaves) void scan_tokseq_kernel(ScanArgs p) {
   constexpr int QL = kTsN / SPL;           // lanes per channel (an aligned group)
   constexpr int CPW = 64 / QL;             // channels per wave
@@ -132,11 +135,12 @@ __global__ __launch_bounds__(64 * kTsWaves) void scan_tokseq_kernel(ScanArgs p) 
   const int64_t row = (b * D + d) * L;
   const float bias = p.bias ? p.bias[d] : 0.0f;
   const float dsk = p.Dskip ? p.Dskip[d] : 0.0f;
-  float a2[SPL], h[SPL];
+  float a2[SPL], ra[SPL], h[SPL];
 #pragma unroll
   for (int j = 0; j < SPL; ++j) {
     const int64_t sidx = d * kTsN + SPL * q + j;
     a2[j] = p.A[sidx] * kLog2e;
+    ra[j] = ZOH ? 1.0f / p.A[sidx] : 0.0f;
     h[j] = p.h0 ? p.h0[(b * D + d) * kTsN + SPL * q + j] : 0.0f;
   }
   const int64_t bc_row = b * kTsN * L;               // B, C rows of this batch row ([N][L])
@@ -190,7 +194,8 @@ __global__ __launch_bounds__(64 * kTsWaves) void scan_tokseq_kernel(ScanArgs p) 
     float4* dst = reinterpret_cast<float4*>(du_w + ch * DUS + 16 * q);
 #pragma unroll
     for (int k = 0; k < 4; ++k)
-      dst[k] = make_float4(dl[2 * k], dl[2 * k] * uv[2 * k], dl[2 * k + 1], dl[2 * k + 1] * uv[2 * k + 1]);
+      dst[k] = ZOH ? make_float4(dl[2 * k], uv[2 * k], dl[2 * k + 1], uv[2 * k + 1])
+                   : make_float4(dl[2 * k], dl[2 * k] * uv[2 * k], dl[2 * k + 1], dl[2 * k + 1] * uv[2 * k + 1]);
 #pragma unroll
     for (int k = 0; k < BCP; ++k) {
       const int v = lane + 64 * k, n = v / QL, pc = v % QL;
@@ -241,7 +246,14 @@ __global__ __launch_bounds__(64 * kTsWaves) void scan_tokseq_kernel(ScanArgs p) 
 #pragma unroll
         for (int j = 0; j < SPL; ++j) {
           const float a = exp2_hw(dd.x * a2[j]);
-          h[j] = __builtin_fmaf(a, h[j], dd.y * bs[j]);
+          float term;
+          if constexpr (ZOH) {
+            const float wz = (dd.y * ra[j]) * bs[j];
+            term = __builtin_fmaf(a, wz, -wz);
+          } else {
+            term = dd.y * bs[j];
+          }
+          h[j] = __builtin_fmaf(a, h[j], term);
           r = __builtin_fmaf(cs[j], h[j], r);
         }
         r += dpp_mov<0xB1, 0xf, false>(0.0f, r);     // quad_perm [1, 0, 3, 2]
@@ -272,12 +284,12 @@ __global__ __launch_bounds__(64 * kTsWaves) void scan_tokseq_kernel(ScanArgs p) 
 
 bool aligned16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; }
 
-template <typename ACT, bool GATE, int SPL>
+template <typename ACT, bool GATE, int SPL, bool ZOH>
 hipError_t launch_spl(const ScanArgs& a, hipStream_t s) {
   constexpr int CPW = 64 * SPL / kTsN;
   const int64_t ngrp = (a.D + CPW - 1) / CPW;
   const int64_t blocks = a.batch * ((ngrp + kTsWaves - 1) / kTsWaves);
-  hipLaunchKernelGGL((scan_tokseq_kernel<ACT, GATE, SPL>), dim3(static_cast<unsigned>(blocks)), dim3(64 * kTsWaves), 0,
+  hipLaunchKernelGGL((scan_tokseq_kernel<ACT, GATE, SPL, ZOH>), dim3(static_cast<unsigned>(blocks)), dim3(64 * kTsWaves), 0,
                      s, a);
   return hipGetLastError();
 }
@@ -285,7 +297,7 @@ hipError_t launch_spl(const ScanArgs& a, hipStream_t s) {
 }  // namespace
 
 bool tokseq_supported(const ScanArgs& a) {
-  if (a.N != kTsN || a.conv_w != nullptr || a.zoh) return false;
+  if (a.N != kTsN || a.conv_w != nullptr) return false;
   if (a.L < 8 || a.L % 8 != 0) return false;
   if (!aligned16(a.u) || !aligned16(a.delta) || !aligned16(a.y) || !aligned16(a.Bm) || !aligned16(a.Cm)) return false;
   if (a.z != nullptr && !aligned16(a.z)) return false;
@@ -308,13 +320,16 @@ bool tokseq_preferred(const ScanArgs& a, Dt) {
 hipError_t launch_scan_tokseq(const ScanArgs& a, Dt dt, int states_per_lane, hipStream_t s) {
   if (!tokseq_supported(a)) return hipErrorInvalidValue;
   const bool gate = a.z != nullptr;
-  const int spl = states_per_lane == 2 ? 2 : 4;
+  // (the full zero-order hold is built for 4 states per lane, the automatic choice)
+  const int spl = (states_per_lane == 2 && !a.zoh) ? 2 : 4;
   if (dt == Dt::F32) {
-    if (spl == 4) return gate ? launch_spl<ActF32, true, 4>(a, s) : launch_spl<ActF32, false, 4>(a, s);
-    return gate ? launch_spl<ActF32, true, 2>(a, s) : launch_spl<ActF32, false, 2>(a, s);
+    if (a.zoh) return gate ? launch_spl<ActF32, true, 4, true>(a, s) : launch_spl<ActF32, false, 4, true>(a, s);
+    if (spl == 4) return gate ? launch_spl<ActF32, true, 4, false>(a, s) : launch_spl<ActF32, false, 4, false>(a, s);
+    return gate ? launch_spl<ActF32, true, 2, false>(a, s) : launch_spl<ActF32, false, 2, false>(a, s);
   }
-  if (spl == 4) return gate ? launch_spl<ActBF16, true, 4>(a, s) : launch_spl<ActBF16, false, 4>(a, s);
-  return gate ? launch_spl<ActBF16, true, 2>(a, s) : launch_spl<ActBF16, false, 2>(a, s);
+  if (a.zoh) return gate ? launch_spl<ActBF16, true, 4, true>(a, s) : launch_spl<ActBF16, false, 4, true>(a, s);
+  if (spl == 4) return gate ? launch_spl<ActBF16, true, 4, false>(a, s) : launch_spl<ActBF16, false, 4, false>(a, s);
+  return gate ? launch_spl<ActBF16, true, 2, false>(a, s) : launch_spl<ActBF16, false, 2, false>(a, s);
 }
 
 }  // namespace ssm

@@ -236,8 +236,8 @@ ssm_status ssm_selective_scan_fwd_variant(const void* u, const void* delta, cons
                   D, N, dt, stream, variant, tokens_per_lane, 0);
 }
 
-int ssm_selective_scan_fwd_kernel(int64_t batch, int64_t L, int64_t D, int64_t N, ssm_dtype dt, int gate,
-                                  int variant, int tokens_per_lane) {
+int ssm_selective_scan_fwd_kernel(int64_t batch, int64_t L, int64_t D, int64_t N, ssm_dtype dt, int gate, int zoh,
+                                  int conv_width, int variant, int tokens_per_lane) {
   if (dt != SSM_F32 && dt != SSM_BF16) return -SSM_ERR_UNSUPPORTED;
   if (batch <= 0 || L <= 0 || D <= 0 || N < 1) return -SSM_ERR_INVALID_ARG;
   if (N > SSM_MAX_N) return -SSM_ERR_UNSUPPORTED;
@@ -245,12 +245,15 @@ int ssm_selective_scan_fwd_kernel(int64_t batch, int64_t L, int64_t D, int64_t N
       variant != SSM_SCAN_TOKSEQ)
     return -SSM_ERR_UNSUPPORTED;
   if (!kernel_option_ok(variant, tokens_per_lane)) return -SSM_ERR_UNSUPPORTED;
+  if (conv_width < 0 || conv_width > SSM_MAX_CONV_WIDTH || (zoh && conv_width)) return -SSM_ERR_UNSUPPORTED;
+  if ((zoh || conv_width) && variant != SSM_SCAN_AUTO) return -SSM_ERR_UNSUPPORTED;   // (those entry points choose)
   // stand-in pointers: 256-byte aligned, never dereferenced
   void* const any = reinterpret_cast<void*>(uintptr_t(256));
   ssm::ScanArgs a;
   a.u = any; a.delta = any; a.A = static_cast<const float*>(any); a.Bm = any; a.Cm = any; a.Dskip = nullptr;
   a.z = gate ? any : nullptr; a.bias = nullptr; a.h0 = nullptr; a.y = any; a.final_state = nullptr;
-  a.batch = batch; a.L = L; a.D = D; a.N = static_cast<int>(N); a.softplus = 1; a.zoh = 0;
+  a.batch = batch; a.L = L; a.D = D; a.N = static_cast<int>(N); a.softplus = 1; a.zoh = zoh ? 1 : 0;
+  if (conv_width) { a.conv_w = static_cast<const float*>(any); a.conv_k = conv_width; }
   return choose_scan_kernel(a, dt == SSM_BF16 ? ssm::Dt::BF16 : ssm::Dt::F32, variant, tokens_per_lane);
 }
 

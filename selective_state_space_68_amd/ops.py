@@ -99,12 +99,15 @@ SCAN_KERNELS = {_lib.SSM_SCAN_SEQUENTIAL: "scan_sequential_kernel", _lib.SSM_SCA
                 _lib.SSM_SCAN_TOKSEQ: "scan_tokseq_kernel"}
 
 
-def selective_scan_fwd_kernel(batch, L, D, N, dtype=torch.float32, gate=True, variant=0, tokens_per_lane=0) -> str:
-    """Name of the kernel selective_scan_fwd runs for this shape (16-byte-aligned
-    tensors, L > 0).  Raises SsmError when such a call would be rejected."""
+def selective_scan_fwd_kernel(batch, L, D, N, dtype=torch.float32, gate=True, discretization="simplified",
+                              conv_width=0, variant=0, tokens_per_lane=0) -> str:
+    """Name of the kernel selective_scan_fwd (or, with conv_width > 0,
+    selective_scan_fwd_conv) runs for this shape (16-byte-aligned tensors, L > 0).
+    Raises SsmError when such a call would be rejected."""
     lib = _lib.load_library()
     dt = _lib.SSM_BF16 if dtype == torch.bfloat16 else _lib.SSM_F32
-    k = lib.ssm_selective_scan_fwd_kernel(int(batch), int(L), int(D), int(N), dt, 1 if gate else 0, int(variant),
+    k = lib.ssm_selective_scan_fwd_kernel(int(batch), int(L), int(D), int(N), dt, 1 if gate else 0,
+                                          1 if discretization == "zoh" else 0, int(conv_width), int(variant),
                                           int(tokens_per_lane))
     if k < 0:
         _lib.check(-k)

@@ -275,23 +275,30 @@ def test_scan_kernel_choice(lib):
     k = lib.ssm_selective_scan_fwd_kernel
     F32, BF16 = _lib.SSM_F32, _lib.SSM_BF16
     SEQ, CHK, TOK = _lib.SSM_SCAN_SEQUENTIAL, _lib.SSM_SCAN_CHUNKED, _lib.SSM_SCAN_TOKSEQ
-    assert k(2, 2048, 1536, 16, F32, 1, 0, 0) == CHK                # 130M-shaped
-    assert k(8, 2048, 4096, 16, BF16, 1, 0, 0) == TOK               # 1.4B-shaped: 32768 channels
-    assert k(8, 2048, 4096, 16, F32, 1, 0, 0) == TOK
-    assert k(16, 2048, 4096, 16, BF16, 1, 0, 0) == TOK              # 65536 channels
-    assert k(2, 2048, 16383, 16, BF16, 1, 0, 0) == CHK              # 32766 channels
-    assert k(16, 2048, 4096, 16, F32, 0, 0, 0) == TOK
-    assert k(4, 2048, 4095, 16, BF16, 1, 0, 0) == CHK               # 16380 channels
-    assert k(8, 2048, 4096, 8, BF16, 1, 0, 0) == CHK                # N != 16
-    assert k(8, 2044, 4096, 16, BF16, 1, 0, 0) == CHK               # L % 8 != 0
-    assert k(8, 2048, 4096, 16, BF16, 1, 0, 16) == CHK              # a chunked option pins the chunked kernel
-    assert k(1, 64, 16, 4, F32, 0, SEQ, 0) == SEQ
-    assert k(1, 64, 16, 16, F32, 0, TOK, 2) == TOK                  # asked for: any supported size
-    assert k(1, 100, 16, 16, F32, 0, TOK, 0) == -_lib.SSM_ERR_UNSUPPORTED
-    assert k(1, 64, 16, 16, F32, 0, TOK, 8) == -_lib.SSM_ERR_UNSUPPORTED   # states per lane: 2 or 4
-    assert k(1, 64, 16, 65, F32, 0, 0, 0) == -_lib.SSM_ERR_UNSUPPORTED
-    assert k(1, 64, 16, 16, F32, 0, 7, 0) == -_lib.SSM_ERR_UNSUPPORTED
-    assert k(0, 64, 16, 16, F32, 0, 0, 0) == -_lib.SSM_ERR_INVALID_ARG
+    assert k(2, 2048, 1536, 16, F32, 1, 0, 0, 0, 0) == CHK                # 130M-shaped
+    assert k(8, 2048, 4096, 16, BF16, 1, 0, 0, 0, 0) == TOK               # 1.4B-shaped: 32768 channels
+    assert k(8, 2048, 4096, 16, F32, 1, 0, 0, 0, 0) == TOK
+    assert k(16, 2048, 4096, 16, BF16, 1, 0, 0, 0, 0) == TOK              # 65536 channels
+    assert k(2, 2048, 16383, 16, BF16, 1, 0, 0, 0, 0) == CHK              # 32766 channels
+    assert k(16, 2048, 4096, 16, F32, 0, 0, 0, 0, 0) == TOK
+    assert k(4, 2048, 4095, 16, BF16, 1, 0, 0, 0, 0) == CHK               # 16380 channels
+    assert k(8, 2048, 4096, 8, BF16, 1, 0, 0, 0, 0) == CHK                # N != 16
+    assert k(8, 2044, 4096, 16, BF16, 1, 0, 0, 0, 0) == CHK               # L % 8 != 0
+    assert k(8, 2048, 4096, 16, BF16, 1, 0, 0, 0, 16) == CHK              # a chunked option pins the chunked kernel
+    assert k(1, 64, 16, 4, F32, 0, 0, 0, SEQ, 0) == SEQ
+    assert k(1, 64, 16, 16, F32, 0, 0, 0, TOK, 2) == TOK                  # asked for: any supported size
+    assert k(1, 100, 16, 16, F32, 0, 0, 0, TOK, 0) == -_lib.SSM_ERR_UNSUPPORTED
+    assert k(1, 64, 16, 16, F32, 0, 0, 0, TOK, 8) == -_lib.SSM_ERR_UNSUPPORTED   # states per lane: 2 or 4
+    assert k(1, 64, 16, 65, F32, 0, 0, 0, 0, 0) == -_lib.SSM_ERR_UNSUPPORTED
+    assert k(1, 64, 16, 16, F32, 0, 0, 0, 7, 0) == -_lib.SSM_ERR_UNSUPPORTED
+    assert k(0, 64, 16, 16, F32, 0, 0, 0, 0, 0) == -_lib.SSM_ERR_INVALID_ARG
+    # the full zero-order hold: token-sequential at many channels, else chunked
+    assert k(8, 2048, 4096, 16, BF16, 1, 1, 0, 0, 0) == TOK
+    assert k(2, 2048, 1536, 16, F32, 1, 1, 0, 0, 0) == CHK
+    assert k(8, 2048, 4096, 16, BF16, 1, 1, 0, CHK, 0) == -_lib.SSM_ERR_UNSUPPORTED   # the zoh entry chooses
+    # the fused conv runs the chunked kernel
+    assert k(8, 2048, 4096, 16, BF16, 1, 0, 4, 0, 0) == CHK
+    assert k(8, 2048, 4096, 16, BF16, 1, 0, 5, 0, 0) == -_lib.SSM_ERR_UNSUPPORTED
 
 
 def test_state_update_empty_is_noop(lib):
