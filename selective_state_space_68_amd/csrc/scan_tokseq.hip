@@ -101,7 +101,12 @@ struct ActIO8<ActBF16> {
 // ZOH: the full zero-order-hold input term (e^{Delta A} - 1)/A * B * u = a w - w with
 // w = u (1/A) B (a = e^{Delta A}): the lanes keep (Delta, u) instead of
 // (Delta, Delta u) in LDS, and 1/A per state.
-template <typename ACT, bool GATE, int SPL, bool ZOH>
+//
+// CONV: the scan input is u = SiLU(causal conv1d(x)) with the taps of p.conv_w,
+// computed in the per-token work: a lane's piece needs the 3 inputs before it, from
+// the previous lane of its group (quad_perm [3, 0, 1, 2]) or, for the block's first
+// piece, from the previous block's last piece, carried (zero before the sequence).
+template <typename ACT, bool GATE, int SPL, bool ZOH, bool CONV>
 __global__ __launch_bounds__(64 * kTsWaves) void scan_tokseq_kernel(ScanArgs p) {
   constexpr int QL = kTsN / SPL;           // lanes per channel (an aligned group)
   constexpr int CPW = 64 / QL;             // channels per wave
@@ -143,6 +148,14 @@ __global__ __launch_bounds__(64 * kTsWaves) void scan_tokseq_kernel(ScanArgs p) 
     ra[j] = ZOH ? 1.0f / p.A[sidx] : 0.0f;
     h[j] = p.h0 ? p.h0[(b * D + d) * kTsN + SPL * q + j] : 0.0f;
   }
+  static_assert(!CONV || SPL == 4, "the fused conv is built for 4 states per lane");
+  // conv taps aligned to the window x[t-3 .. t] (cw4[4-K+k] = w[d, k], the rest zero)
+  float cw4[4] = {0.0f, 0.0f, 0.0f, 0.0f}, cbias = 0.0f, carry[3] = {0.0f, 0.0f, 0.0f};
+  if constexpr (CONV) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) cw4[k] = (k >= 4 - p.conv_k) ? p.conv_w[d * p.conv_k + k - (4 - p.conv_k)] : 0.0f;
+    cbias = p.conv_b ? p.conv_b[d] : 0.0f;
+  }
   const int64_t bc_row = b * kTsN * L;               // B, C rows of this batch row ([N][L])
   float* du_w = s_du[w];
   float* bc_w = reinterpret_cast<float*>(s_bc[w]);
@@ -178,6 +191,27 @@ __global__ __launch_bounds__(64 * kTsWaves) void scan_tokseq_kernel(ScanArgs p) 
     float uv[8], dl[8], ysk[8], gt[8] = {};
     IO::unpack(u_raw, uv);
     IO::unpack(d_raw, dl);
+    if constexpr (CONV) {
+      // uv holds x: u = SiLU(conv(x)), accumulated oldest tap first
+      float xx[11];
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        const float prev = dpp_mov<0x93, 0xf, false>(0.0f, uv[5 + k]);   // quad_perm [3, 0, 1, 2]
+        const float last = dpp_mov<0xFF, 0xf, false>(0.0f, uv[5 + k]);   // quad_perm [3, 3, 3, 3]
+        xx[k] = q == 0 ? carry[k] : prev;
+        carry[k] = last;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) xx[3 + j] = uv[j];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float sc = cbias;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) sc = __builtin_fmaf(cw4[k], xx[j + k], sc);
+        uv[j] = sc * __builtin_amdgcn_rcpf(1.0f + exp2_hw(-sc * kLog2e));
+      }
+      if (p.u_out && store_ok && pvalid) IO::store(p.u_out, row + t0 + 8 * q, uv);
+    }
     if constexpr (GATE) {
       float zv[8];
       IO::unpack(z_raw, zv);
@@ -284,12 +318,13 @@ __global__ __launch_bounds__(64 * kTsWaves) void scan_tokseq_kernel(ScanArgs p) 
 
 bool aligned16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; }
 
-template <typename ACT, bool GATE, int SPL, bool ZOH>
+template <typename ACT, bool GATE, int SPL, bool ZOH, bool CONV = false>
 hipError_t launch_spl(const ScanArgs& a, hipStream_t s) {
   constexpr int CPW = 64 * SPL / kTsN;
   const int64_t ngrp = (a.D + CPW - 1) / CPW;
   const int64_t blocks = a.batch * ((ngrp + kTsWaves - 1) / kTsWaves);
-  hipLaunchKernelGGL((scan_tokseq_kernel<ACT, GATE, SPL, ZOH>), dim3(static_cast<unsigned>(blocks)), dim3(64 * kTsWaves), 0,
+  hipLaunchKernelGGL((scan_tokseq_kernel<ACT, GATE, SPL, ZOH, CONV>), dim3(static_cast<unsigned>(blocks)),
+                     dim3(64 * kTsWaves), 0,
                      s, a);
   return hipGetLastError();
 }
@@ -297,7 +332,8 @@ hipError_t launch_spl(const ScanArgs& a, hipStream_t s) {
 }  // namespace
 
 bool tokseq_supported(const ScanArgs& a) {
-  if (a.N != kTsN || a.conv_w != nullptr) return false;
+  if (a.N != kTsN || (a.conv_w != nullptr && (a.zoh || a.conv_k < 1 || a.conv_k > 4))) return false;
+  if (a.u_out != nullptr && !aligned16(a.u_out)) return false;
   if (a.L < 8 || a.L % 8 != 0) return false;
   if (!aligned16(a.u) || !aligned16(a.delta) || !aligned16(a.y) || !aligned16(a.Bm) || !aligned16(a.Cm)) return false;
   if (a.z != nullptr && !aligned16(a.z)) return false;
@@ -320,8 +356,14 @@ bool tokseq_preferred(const ScanArgs& a, Dt) {
 hipError_t launch_scan_tokseq(const ScanArgs& a, Dt dt, int states_per_lane, hipStream_t s) {
   if (!tokseq_supported(a)) return hipErrorInvalidValue;
   const bool gate = a.z != nullptr;
-  // (the full zero-order hold is built for 4 states per lane, the automatic choice)
-  const int spl = (states_per_lane == 2 && !a.zoh) ? 2 : 4;
+  // (the full zero-order hold and the fused conv are built for 4 states per lane,
+  // the automatic choice)
+  const int spl = (states_per_lane == 2 && !a.zoh && a.conv_w == nullptr) ? 2 : 4;
+  if (a.conv_w != nullptr) {
+    if (dt == Dt::F32)
+      return gate ? launch_spl<ActF32, true, 4, false, true>(a, s) : launch_spl<ActF32, false, 4, false, true>(a, s);
+    return gate ? launch_spl<ActBF16, true, 4, false, true>(a, s) : launch_spl<ActBF16, false, 4, false, true>(a, s);
+  }
   if (dt == Dt::F32) {
     if (a.zoh) return gate ? launch_spl<ActF32, true, 4, true>(a, s) : launch_spl<ActF32, false, 4, true>(a, s);
     if (spl == 4) return gate ? launch_spl<ActF32, true, 4, false>(a, s) : launch_spl<ActF32, false, 4, false>(a, s);

@@ -187,7 +187,8 @@ int choose_scan_kernel(const ssm::ScanArgs& a, ssm::Dt d, int variant, int token
   const bool chunked = (variant == SSM_SCAN_AUTO || variant == SSM_SCAN_CHUNKED) &&
                        ssm::chunked_supported(a, d, tokens_per_lane);
   if (variant == SSM_SCAN_CHUNKED && !chunked) return -SSM_ERR_UNSUPPORTED;
-  if (a.zoh && !chunked) return -SSM_ERR_UNSUPPORTED;   // only the chunked kernel has the full hold
+  // the sequential kernel has neither the full hold nor the fused conv
+  if ((a.zoh || a.conv_w != nullptr) && !chunked) return -SSM_ERR_UNSUPPORTED;
   return chunked ? SSM_SCAN_CHUNKED : SSM_SCAN_SEQUENTIAL;
 }
 
@@ -325,7 +326,9 @@ ssm_status ssm_selective_scan_fwd_conv(const void* x, const float* conv_w, const
   a.batch = batch; a.L = L; a.D = D; a.N = static_cast<int>(N); a.softplus = delta_softplus;
   a.conv_w = conv_w; a.conv_b = conv_b; a.conv_k = static_cast<int>(conv_width); a.u_out = u_out;
   const ssm::Dt d = dt == SSM_BF16 ? ssm::Dt::BF16 : ssm::Dt::F32;
-  if (!ssm::chunked_supported(a, d, tokens_per_lane)) return SSM_ERR_UNSUPPORTED;
+  const int kernel = choose_scan_kernel(a, d, SSM_SCAN_AUTO, tokens_per_lane);
+  if (kernel < 0) return static_cast<ssm_status>(-kernel);
+  if (kernel == SSM_SCAN_TOKSEQ) return from_hip(ssm::launch_scan_tokseq(a, d, 0, s));
   return from_hip(ssm::launch_scan_chunked(a, d, tokens_per_lane, s));
 }
 

@@ -296,8 +296,10 @@ def test_scan_kernel_choice(lib):
     assert k(8, 2048, 4096, 16, BF16, 1, 1, 0, 0, 0) == TOK
     assert k(2, 2048, 1536, 16, F32, 1, 1, 0, 0, 0) == CHK
     assert k(8, 2048, 4096, 16, BF16, 1, 1, 0, CHK, 0) == -_lib.SSM_ERR_UNSUPPORTED   # the zoh entry chooses
-    # the fused conv runs the chunked kernel
-    assert k(8, 2048, 4096, 16, BF16, 1, 0, 4, 0, 0) == CHK
+    # the fused conv: as the plain scan
+    assert k(8, 2048, 4096, 16, BF16, 1, 0, 4, 0, 0) == TOK
+    assert k(2, 2048, 1536, 16, F32, 1, 0, 4, 0, 0) == CHK
+    assert k(8, 2048, 4096, 16, BF16, 1, 0, 4, 0, 8) == CHK
     assert k(8, 2048, 4096, 16, BF16, 1, 0, 5, 0, 0) == -_lib.SSM_ERR_UNSUPPORTED
 
 

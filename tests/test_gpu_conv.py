@@ -91,3 +91,43 @@ def test_scan_with_fused_conv(shape):
                                             t["bias"])
         torch.cuda.synchronize()
         assert torch.equal(us, u) and torch.equal(y1, y2) and torch.equal(f1, f2)
+
+
+@pytest.mark.parametrize("shape", [(1, 264, 32771, "f32", True, 4), (2, 264, 16401, "bf16", True, 3)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_fused_conv_many_channels_token_sequential(shape):
+    """From 32768 channels the fused conv runs in the token-sequential kernel: sampled
+    channels and every batch row's last channels against the oracle, u_out against the
+    oracle's convolution, and (float32) the fused call equal to the standalone conv
+    followed by the scan, bit for bit."""
+    import torch
+    from selective_state_space_68_amd import (causal_conv1d, selective_scan_fwd, selective_scan_fwd_conv,
+                                              selective_scan_fwd_kernel)
+    from gpu_util import sample_channels
+    batch, L, D, dtype, gate, K = shape
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    assert selective_scan_fwd_kernel(batch, L, D, 16, tdt, gate, conv_width=K) == "scan_tokseq_kernel"
+    inp = synth.make_scan_inputs(batch, L, D, 16, dtype, gate=gate, d_skip="normal", seed=D, a_kind="lognormal")
+    w, cb = _conv_params(D, K, seed=7)
+    t = upload_scan(inp)
+    tw, tcb = dev(w), dev(cb)
+    y, fs, u = selective_scan_fwd_conv(t["u"], tw, tcb, t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"],
+                                       t["bias"], return_u=True)
+    torch.cuda.synchronize()
+    yh, fh, uh = host(y), host(fs), host(u)
+    chans = sorted(set(sample_channels(batch, D, 10, seed=8)) | {(b, D - 1 - j) for b in range(batch) for j in range(3)})
+    for b in sorted({b for b, _ in chans}):
+        ds = [d for bb, d in chans if bb == b]
+        u_ref = oracle.causal_conv1d(inp.u[b:b + 1][:, ds], w[ds], cb[ds], apply_silu=True)
+        ry, rf = oracle.selective_scan(u_ref, inp.delta[b:b + 1][:, ds], inp.A[ds], inp.B[b:b + 1], inp.C[b:b + 1],
+                                       inp.Dskip[ds], None if inp.z is None else inp.z[b:b + 1][:, ds],
+                                       inp.delta_bias[ds])
+        ey, ef, eu = row_rel_err(yh[b][ds], ry[0]), row_rel_err(fh[b][ds], rf[0]), row_rel_err(uh[b][ds], u_ref[0])
+        print(f"fused conv tokseq {shape} row {b}: y_err={ey:.2e} state_err={ef:.2e} u_err={eu:.2e}", flush=True)
+        assert ey <= TOL[dtype] and ef <= TOL[dtype]
+        assert eu <= (2e-6 if dtype == "f32" else 8e-3)
+    if dtype == "f32":
+        us = causal_conv1d(t["u"], tw, tcb)
+        y2, f2 = selective_scan_fwd(us, t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["bias"])
+        torch.cuda.synchronize()
+        assert torch.equal(us, u) and torch.equal(y, y2) and torch.equal(fs, f2)
