@@ -115,7 +115,8 @@ size_t bwd_ws_floats(int64_t batch, int64_t L, int64_t D, int N) {
 
 // ---- cross-lane helpers -------------------------------------------------------
 
-// Reverse (suffix) scan across the 64 lanes of (a, b) pairs: on return lane i's b
+// Two reverse (suffix) scans across the 64 lanes of (a, b) pairs, interleaved (no
+// wait states between the DPP steps): on return lane i's b
 // is mu_i = b_i + a_i mu_{i+1} with mu_64 = carry, i.e. the composition of lanes
 // 63 .. i applied to the carry.  Within each row of 16 lanes, Kogge-Stone steps
 // with row_shl 1, 2, 4, 8 (in-place DPP as in the forward scan; a lane whose
@@ -123,35 +124,6 @@ size_t bwd_ws_floats(int64_t batch, int64_t L, int64_t D, int N) {
 // identity).  Then the three row boundaries are resolved from lanes 48, 32, 16
 // read as scalars: row r's lanes apply their row suffix to mu of the first lane
 // of row r + 1.  Pure VALU, no memory access.
-__device__ __forceinline__ void wave_rscan_pairs(float& a, float& b, float carry) {
-  asm volatile(
-      "s_nop 1\n\t"
-      "v_fmac_f32_dpp %0, %0, %1 row_shl:1 row_mask:0xf bank_mask:0xf\n\t"
-      "v_mul_f32_dpp %1, %1, %1 row_shl:1 row_mask:0xf bank_mask:0xf\n\t"
-      "s_nop 0\n\t"
-      "v_fmac_f32_dpp %0, %0, %1 row_shl:2 row_mask:0xf bank_mask:0xf\n\t"
-      "v_mul_f32_dpp %1, %1, %1 row_shl:2 row_mask:0xf bank_mask:0xf\n\t"
-      "s_nop 0\n\t"
-      "v_fmac_f32_dpp %0, %0, %1 row_shl:4 row_mask:0xf bank_mask:0xf\n\t"
-      "v_mul_f32_dpp %1, %1, %1 row_shl:4 row_mask:0xf bank_mask:0xf\n\t"
-      "s_nop 0\n\t"
-      "v_fmac_f32_dpp %0, %0, %1 row_shl:8 row_mask:0xf bank_mask:0xf\n\t"
-      "v_mul_f32_dpp %1, %1, %1 row_shl:8 row_mask:0xf bank_mask:0xf\n\t"
-      "s_nop 1"
-      : "+v"(b), "+v"(a));
-  auto rl = [](float v, int l) { return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l)); };
-  const float m2 = __builtin_fmaf(rl(a, 48), carry, rl(b, 48));
-  const float m1 = __builtin_fmaf(rl(a, 32), m2, rl(b, 32));
-  float m0 = __builtin_fmaf(rl(a, 16), m1, rl(b, 16));
-  float mm1 = m1, mm2 = m2;
-  // (computed for all lanes before the selection, which then stays branch-free)
-  asm volatile("" : "+v"(m0), "+v"(mm1), "+v"(mm2));
-  const int row = (threadIdx.x & 63) >> 4;
-  const float m = row == 3 ? carry : (row == 2 ? mm2 : (row == 1 ? mm1 : m0));
-  b = __builtin_fmaf(a, m, b);
-}
-
-// Two independent reverse scans, interleaved (no wait states between the DPP steps).
 __device__ __forceinline__ void wave_rscan_pairs2(float& a0, float& b0, float carry0, float& a1, float& b1,
                                                   float carry1) {
   asm volatile(

@@ -32,11 +32,11 @@
 //     computes on the current one, and at the end of the step writes it, as
 //     float32 and permuted into the order the lanes read it, to the other of two
 //     LDS buffers; one barrier per step publishes it;
-//   * a wave loads its next chunk's u and delta into registers and this chunk's z
-//     into LDS during the current chunk, and stores the previous chunk's y at its
-//     first step, one kind of traffic per step: every barrier waits for the wave's
-//     outstanding memory operations, so a chunk's HBM traffic is spread over its
-//     steps instead of arriving as one burst per chunk.
+//   * a wave loads its next chunk's u and delta and this chunk's z into registers
+//     during the current chunk, and stores the previous chunk's y at its first
+//     step, one kind of traffic per step, so a chunk's HBM traffic is spread over
+//     its steps instead of arriving as one burst per chunk.  The barriers order
+//     LDS only; a load is waited for where its value is first used.
 // No MFMA: the readout is a per-token dot product over n, not a shared-operand
 // contraction.  The kernel is bound by HBM bandwidth and by the VALU and
 // transcendental rate (one exp per element).
@@ -50,14 +50,6 @@ namespace ssm {
 namespace {
 
 constexpr int kNBGeneric = 4;        // states per step (per staged B/C tile), any N
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Direct global->LDS copy: lane l moves 16 bytes from gsrc (per lane) to
-// lds_base + 16*l (lds_base must be wave-uniform).
-__device__ __forceinline__ void dma16(const void* gsrc, void* lds_base) {
-  __builtin_amdgcn_global_load_lds(gsrc, (lds_void*)(lds_base), 16, 0, 0);
-}
 
 // ---- the scan ----------------------------------------------------------------
 // kNB states per step.  NBLK > 0: N == kNB * NBLK, fixed at compile time; the steps of a chunk are
