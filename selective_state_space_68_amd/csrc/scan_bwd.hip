@@ -423,6 +423,154 @@ __global__ __launch_bounds__(64 * kW) void bwd_summary_kernel(BwdArgs p, BwdLayo
   }
 }
 
+// ---- 1b. chunk summaries, token-sequential (N = 16, many channels) ----------------
+// The same F, X and P as bwd_summary_kernel, from one forward walk over the chunk:
+// a lane owns 4 states of one channel (a wave 16 channels), as in the forward
+// token-sequential scan.  X, the adjoint a chunk sends left from a zero start,
+// nests as x = a_t (g_t C_t + x) from the chunk's end; unrolled it is
+// X = sum_t (prod_{s <= t} a_s) g_t C_t over the chunk, which the forward walk
+// accumulates with the running decay product (re-anchored at every 32-token block
+// to exp2(A * sum of the Deltas before it), so its rounding spans 32 products),
+// sharing each token's exp with the state fold.  About 8 issue slots per element
+// against the two folds and two wave scans of bwd_summary_kernel.  The waves are
+// independent (own LDS slice, no barrier).
+constexpr int kSumWaves = 4;
+constexpr int64_t kSumTokseqMinWaves = 4096;
+
+// Eight consecutive activations of one channel (cached: in bfloat16 a block's 8
+// tokens of a channel are half of a cache line whose other half the next block reads).
+template <typename ACT>
+__device__ __forceinline__ void load8_cached(const void* base, int64_t off, float (&v)[8]) {
+  if constexpr (ACT::kBytes == 4) {
+    const float4* q = reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
+    const float4 x = q[0], y = q[1];
+    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w; v[4] = y.x; v[5] = y.y; v[6] = y.z; v[7] = y.w;
+  } else {
+    const uint4 r = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off);
+    v[0] = bf16_lo(r.x); v[1] = bf16_hi(r.x); v[2] = bf16_lo(r.y); v[3] = bf16_hi(r.y);
+    v[4] = bf16_lo(r.z); v[5] = bf16_hi(r.z); v[6] = bf16_lo(r.w); v[7] = bf16_hi(r.w);
+  }
+}
+
+template <typename ACT, bool GATE>
+__global__ __launch_bounds__(64 * kSumWaves) void bwd_summary_tokseq_kernel(BwdArgs p, BwdLayout g) {
+  constexpr int NS = 16, QL = 4, CPW = 16, T = 32, CH = 512;
+  __shared__ float4 s_bc[kSumWaves][2][T][NS / 4];   // B, C [token][state group], groups XOR-swizzled by piece
+  __shared__ float4 s_tok[kSumWaves][CPW][T + 1];    // (Delta, Delta*u, g, -) per channel and token
+  const int lane = threadIdx.x & 63;
+  const int w = uniform_int(threadIdx.x >> 6);
+  const int64_t L = p.L, D = p.D;
+  const int64_t nbc = p.batch * g.nchunks;
+  // (workgroups of one (batch row, chunk) pair are nbc apart: one XCD when nbc % 8 == 0)
+  const int64_t bc = blockIdx.x % nbc;
+  const int64_t b = bc % p.batch, c = bc / p.batch;
+  const int64_t ngrp = (D + CPW - 1) / CPW;
+  const int64_t grp = static_cast<int64_t>(blockIdx.x / nbc) * kSumWaves + w;
+  const int64_t gcl = grp < ngrp ? grp : ngrp - 1;
+  const int ch = lane / QL, q = lane % QL;
+  const int64_t d_own = gcl * CPW + ch;
+  const bool store_ok = grp < ngrp && d_own < D;
+  const int64_t d = d_own < D ? d_own : D - 1;
+  const int64_t row = (b * D + d) * L;
+  const float bias = p.bias ? p.bias[d] : 0.0f;
+  float a2[4], h[4], X[4], Dc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    a2[j] = p.A[d * NS + 4 * q + j] * kLog2e;
+    h[j] = 0.0f;
+    X[j] = 0.0f;
+  }
+  float cum = 0.0f;                                   // sum of Delta over the chunk so far (the channel's)
+  const int64_t bc_row = b * NS * L;
+  float* bc_w = reinterpret_cast<float*>(s_bc[w]);
+  float4* tok_w = s_tok[w][ch];
+
+  float ru[8], rd[8], ry[8], rz[8], rb[8], rc[8];
+  auto fetch = [&](int64_t t0) __attribute__((always_inline)) {
+    int64_t tp = t0 + 8 * q;
+    tp = tp + 8 <= L ? tp : L - 8;
+    load8_cached<ACT>(p.u, row + tp, ru);
+    load8_cached<ACT>(p.delta, row + tp, rd);
+    load8_cached<ACT>(p.dy, row + tp, ry);
+    if constexpr (GATE) load8_cached<ACT>(p.z, row + tp, rz);
+    // B and C piece of this lane: state lane / 4, tokens 8 (lane % 4) ..
+    int64_t t = t0 + 8 * (lane % QL);
+    t = t + 8 <= L ? t : L - 8;
+    load8_cached<ACT>(p.Bm, bc_row + (lane / QL) * L + t, rb);
+    load8_cached<ACT>(p.Cm, bc_row + (lane / QL) * L + t, rc);
+  };
+
+  const int64_t tc0 = c * CH;
+  fetch(tc0);
+  for (int blk = 0; blk < CH / T; ++blk) {
+    const int64_t t0 = tc0 + blk * T;
+    const bool pvalid = t0 + 8 * q < L;              // L % 8 == 0: a piece is all in or all out
+    // ---- per-token work of this lane's piece; the block's B and C
+    float sp = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float raw = rd[k] + bias;
+      float dl = p.softplus ? softplus_f(raw) : raw;
+      float gk = ry[k];
+      if constexpr (GATE) gk *= silu_f(rz[k]);
+      dl = pvalid ? dl : 0.0f;
+      gk = pvalid ? gk : 0.0f;
+      sp += dl;
+      tok_w[8 * q + k] = make_float4(dl, dl * ru[k], gk, 0.0f);
+    }
+    {
+      const int n = lane / QL, pc = lane % QL;
+      const int col = 4 * ((n >> 2) ^ pc) + (n & 3);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        bc_w[(0 * T + 8 * pc + e) * NS + col] = rb[e];
+        bc_w[(1 * T + 8 * pc + e) * NS + col] = rc[e];
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    fetch(t0 + T < tc0 + CH ? t0 + T : t0);          // next block (the last one reloads itself, unused)
+
+    // ---- the forward walk: F (the state), X (decay-weighted g C) over the block
+#pragma unroll
+    for (int j = 0; j < 4; ++j) Dc[j] = exp2_hw(a2[j] * cum);
+#pragma unroll
+    for (int tb = 0; tb < T / 8; ++tb) {
+      const int gsw = q ^ tb;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int t = 8 * tb + k;
+        const float4 tv = tok_w[t];
+        const float4 bb = reinterpret_cast<const float4*>(bc_w + (0 * T + t) * NS)[gsw];
+        const float4 cc = reinterpret_cast<const float4*>(bc_w + (1 * T + t) * NS)[gsw];
+        const float bs[4] = {bb.x, bb.y, bb.z, bb.w}, cs[4] = {cc.x, cc.y, cc.z, cc.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float a = exp2_hw(tv.x * a2[j]);
+          h[j] = __builtin_fmaf(a, h[j], tv.y * bs[j]);
+          Dc[j] *= a;
+          X[j] = __builtin_fmaf(Dc[j], tv.z * cs[j], X[j]);
+        }
+      }
+    }
+    // the channel's sum of Delta over the block (its 4 pieces)
+    sp += dpp_mov<0xB1, 0xf, false>(0.0f, sp);       // quad_perm [1, 0, 3, 2]
+    sp += dpp_mov<0x4E, 0xf, false>(0.0f, sp);       // quad_perm [2, 3, 0, 1]
+    cum += sp;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+  if (store_ok) {
+    const int64_t off = ((b * g.nchunks + c) * D + d) * NS + 4 * q;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      g.F[off + j] = h[j];
+      g.X[off + j] = X[j];
+      g.P[off + j] = exp2_hw(a2[j] * cum);
+    }
+  }
+}
+
 // ---- 2. sequential combine over chunks --------------------------------------------
 __global__ void bwd_combine_kernel(BwdArgs p, BwdLayout g) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -746,14 +894,31 @@ __global__ void bwd_bc_out_kernel(BwdArgs p, BwdLayout g) {
 
 bool aligned16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; }
 
+// The token-sequential summary: N = 16 (512-token chunks), the vector path, and
+// enough (batch row, chunk, 16-channel group) waves to fill the chip (measured).
+bool bwd_summary_tokseq_ok(const BwdArgs& a, const BwdLayout& g, bool vec) {
+  if (a.N != 16 || g.kpl != 8 || !vec) return false;
+  return a.batch * g.nchunks * ((a.D + 15) / 16) >= kSumTokseqMinWaves;
+}
+
 template <typename ACT, int KPL, int kW, int NT>
 hipError_t launch_bwd_typed(const BwdArgs& a, const BwdLayout& g, hipStream_t s) {
   const bool vec = (a.L % 8 == 0) && aligned16(a.u) && aligned16(a.delta) && aligned16(a.dy) &&
                    (a.z == nullptr || aligned16(a.z)) && aligned16(a.du) && aligned16(a.ddelta) &&
                    (a.dz == nullptr || aligned16(a.dz)) && aligned16(a.Bm) && aligned16(a.Cm);
   const int64_t blocks = a.batch * g.nchunks * g.nslices;
-  hipLaunchKernelGGL((bwd_summary_kernel<ACT, KPL, kW, NT>), dim3(static_cast<unsigned>(blocks)), dim3(64 * kW), 0, s,
-                     a, g, vec ? 1 : 0);
+  if (bwd_summary_tokseq_ok(a, g, vec)) {
+    const int64_t sblocks = a.batch * g.nchunks * ((a.D + 16 * kSumWaves - 1) / (16 * kSumWaves));
+    if (a.z)
+      hipLaunchKernelGGL((bwd_summary_tokseq_kernel<ACT, true>), dim3(static_cast<unsigned>(sblocks)),
+                         dim3(64 * kSumWaves), 0, s, a, g);
+    else
+      hipLaunchKernelGGL((bwd_summary_tokseq_kernel<ACT, false>), dim3(static_cast<unsigned>(sblocks)),
+                         dim3(64 * kSumWaves), 0, s, a, g);
+  } else {
+    hipLaunchKernelGGL((bwd_summary_kernel<ACT, KPL, kW, NT>), dim3(static_cast<unsigned>(blocks)), dim3(64 * kW), 0,
+                       s, a, g, vec ? 1 : 0);
+  }
   const int64_t nc = a.batch * a.D * a.N;
   hipLaunchKernelGGL(bwd_combine_kernel, dim3(static_cast<unsigned>((nc + 255) / 256)), dim3(256), 0, s, a, g);
   hipLaunchKernelGGL((bwd_main_kernel<ACT, KPL, kW, NT>), dim3(static_cast<unsigned>(blocks)), dim3(64 * kW), 0,

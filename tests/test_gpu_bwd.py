@@ -155,3 +155,50 @@ def test_bwd_repeatable_and_workspace_reuse():
         assert np.array_equal(outs[0][k], outs[1][k]), k
     ref = _run_oracle(inp, dyv, hz, dfin)
     _compare(outs[1], ref, "bf16", "bwd reused workspace")
+
+
+def _run_oracle_sliced(inp, dyv, hz, dfin, step=512):
+    """The oracle's adjoint over slices of channels.  Every per-channel gradient
+    depends only on its own channel; dB and dC are sums over channels, so the
+    slices' partial sums add up to the whole.  Keeps the oracle's stored states
+    to one slice at a time."""
+    D = inp.u.shape[1]
+    out = None
+    for d0 in range(0, D, step):
+        s = slice(d0, min(D, d0 + step))
+        cut = lambda x: None if x is None else x[:, s]
+        vec = lambda x: None if x is None else x[s]
+        r = oracle.selective_scan_bwd(inp.u[:, s], inp.delta[:, s], inp.A[s], inp.B, inp.C, dyv[:, s],
+                                      vec(inp.Dskip), cut(inp.z), vec(inp.delta_bias), inp.delta_softplus,
+                                      cut(hz), cut(dfin))
+        if out is None:
+            out = {k: (None if v is None else [v]) for k, v in r.items()}
+        else:
+            for k, v in r.items():
+                if v is not None:
+                    out[k].append(v)
+    cat_axis = {"du": 1, "ddelta": 1, "dz": 1, "dh0": 1, "dA": 0, "dD": 0, "ddelta_bias": 0}
+    res = {}
+    for k, v in out.items():
+        if v is None:
+            res[k] = None
+        elif k in ("dB", "dC"):
+            res[k] = np.sum(v, axis=0)
+        else:
+            res[k] = np.concatenate(v, axis=cat_axis[k])
+    return res
+
+
+@pytest.mark.parametrize("batch,L,D,dtype,kw", [
+    (2, 4104, 3640, "f32", dict(h0=True, dfinal=True)),
+    (8, 1032, 2728, "bf16", dict()),
+])
+def test_bwd_many_channel_chunks(batch, L, D, dtype, kw):
+    """Shapes with at least 4096 (chunk, 16-channel group) pairs, where the
+    chunk summaries come from the token-sequential summary kernel: the last
+    512-token chunk holds 8 tokens, the last 16-channel group is half idle and
+    the last workgroup's 64 channels are partly past the end."""
+    inp, dyv, dyup, hz, dfin = _case(batch, L, D, 16, dtype, seed=D, **kw)
+    got = _run_gpu(inp, dyup, hz, dfin)
+    ref = _run_oracle_sliced(inp, dyv, hz, dfin)
+    _compare(got, ref, dtype, f"bwd many chunks {dtype} b={batch} L={L} D={D} {kw}")
