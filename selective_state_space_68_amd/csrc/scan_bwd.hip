@@ -572,6 +572,24 @@ __global__ __launch_bounds__(64 * kSumWaves) void bwd_summary_tokseq_kernel(BwdA
 }
 
 // ---- 2. sequential combine over chunks --------------------------------------------
+constexpr int kAhead = 8;   // loads issued ahead in the sequential combine and sums
+
+// sum_{k < count} src[k * stride], added in k order (so bitwise the plain loop's
+// result), with the loads issued kAhead at a time (indices past the end clamped to
+// the last, their values unused).
+__device__ __forceinline__ float ordered_sum(const float* src, int64_t stride, int64_t count) {
+  float s = 0.0f;
+  for (int64_t k0 = 0; k0 < count; k0 += kAhead) {
+    float v[kAhead];
+#pragma unroll
+    for (int j = 0; j < kAhead; ++j) v[j] = src[(k0 + j < count ? k0 + j : count - 1) * stride];
+#pragma unroll
+    for (int j = 0; j < kAhead; ++j)
+      if (k0 + j < count) s += v[j];
+  }
+  return s;
+}
+
 __global__ void bwd_combine_kernel(BwdArgs p, BwdLayout g) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   const int N = p.N;
@@ -580,19 +598,43 @@ __global__ void bwd_combine_kernel(BwdArgs p, BwdLayout g) {
   const int64_t n = i % N, d = (i / N) % D, b = i / (N * D);
   const int64_t stride = D * N;
   const int64_t base = b * g.nchunks * stride + d * N + n;
+  const int64_t nch = g.nchunks;
+  // The chunks' values are loaded kAhead at a time before any of them is replaced
+  // (indices past the end are clamped to the last chunk and their values unused),
+  // so each group costs one memory round trip instead of one per chunk.
   float h = p.h0 ? p.h0[i] : 0.0f;
-  for (int64_t c = 0; c < g.nchunks; ++c) {
-    const int64_t o = base + c * stride;
-    const float f = g.F[o];
-    g.F[o] = h;                                      // state entering chunk c
-    h = __builtin_fmaf(g.P[o], h, f);
+  for (int64_t c0 = 0; c0 < nch; c0 += kAhead) {
+    float f[kAhead], dec[kAhead];
+#pragma unroll
+    for (int j = 0; j < kAhead; ++j) {
+      const int64_t o = base + (c0 + j < nch ? c0 + j : nch - 1) * stride;
+      f[j] = g.F[o];
+      dec[j] = g.P[o];
+    }
+#pragma unroll
+    for (int j = 0; j < kAhead; ++j) {
+      if (c0 + j < nch) {
+        g.F[base + (c0 + j) * stride] = h;           // state entering chunk c0 + j
+        h = __builtin_fmaf(dec[j], h, f[j]);
+      }
+    }
   }
   float mu = p.dfinal ? p.dfinal[i] : 0.0f;
-  for (int64_t c = g.nchunks - 1; c >= 0; --c) {
-    const int64_t o = base + c * stride;
-    const float x = g.X[o];
-    g.X[o] = mu;                                     // adjoint entering chunk c from the right
-    mu = __builtin_fmaf(g.P[o], mu, x);
+  for (int64_t c0 = nch - 1; c0 >= 0; c0 -= kAhead) {
+    float x[kAhead], dec[kAhead];
+#pragma unroll
+    for (int j = 0; j < kAhead; ++j) {
+      const int64_t o = base + (c0 - j >= 0 ? c0 - j : 0) * stride;
+      x[j] = g.X[o];
+      dec[j] = g.P[o];
+    }
+#pragma unroll
+    for (int j = 0; j < kAhead; ++j) {
+      if (c0 - j >= 0) {
+        g.X[base + (c0 - j) * stride] = mu;          // adjoint entering chunk c0 - j from the right
+        mu = __builtin_fmaf(dec[j], mu, x[j]);
+      }
+    }
   }
   if (p.dh0) p.dh0[i] = mu;
 }
@@ -863,19 +905,13 @@ __global__ void bwd_param_sums_kernel(BwdArgs p, BwdLayout g) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   const int64_t D = p.D, DN = D * p.N, parts = p.batch * g.nchunks;
   if (i < DN) {
-    float s = 0.0f;
-    for (int64_t k = 0; k < parts; ++k) s += g.P[k * DN + i];
-    p.dA[i] = s;
+    p.dA[i] = ordered_sum(g.P + i, DN, parts);
   } else if (i < DN + D) {
     const int64_t d = i - DN;
-    float s = 0.0f;
-    for (int64_t k = 0; k < parts; ++k) s += g.dDp[k * D + d];
-    if (p.dD) p.dD[d] = s;
+    if (p.dD) p.dD[d] = ordered_sum(g.dDp + d, D, parts);
   } else if (i < DN + 2 * D) {
     const int64_t d = i - DN - D;
-    float s = 0.0f;
-    for (int64_t k = 0; k < parts; ++k) s += g.dbp[k * D + d];
-    if (p.dbias) p.dbias[d] = s;
+    if (p.dbias) p.dbias[d] = ordered_sum(g.dbp + d, D, parts);
   }
 }
 
@@ -885,8 +921,7 @@ __global__ void bwd_bc_out_kernel(BwdArgs p, BwdLayout g) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   const int64_t L = p.L, NL = p.N * L, per = p.batch * 2 * NL;
   if (i >= per) return;
-  float s = 0.0f;
-  for (int64_t k = 0; k < g.nslices; ++k) s += g.part[k * per + i];
+  const float s = ordered_sum(g.part + i, per, g.nslices);
   const int64_t b = i / (2 * NL), rem = i % (2 * NL);
   const int m = static_cast<int>(rem / NL);
   store_act<ACT>(m ? p.dC : p.dB, b * NL + rem % NL, s);
