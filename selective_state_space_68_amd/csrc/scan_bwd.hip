@@ -432,10 +432,17 @@ __global__ __launch_bounds__(64 * kW) void bwd_summary_kernel(BwdArgs p, BwdLayo
 // accumulates with the running decay product (re-anchored at every 32-token block
 // to exp2(A * sum of the Deltas before it), so its rounding spans 32 products),
 // sharing each token's exp with the state fold.  About 8 issue slots per element
-// against the two folds and two wave scans of bwd_summary_kernel.  The waves are
-// independent (own LDS slice, no barrier).
+// against the two folds and two wave scans of bwd_summary_kernel.
+//   SUB = 1: the workgroup's 4 waves take 4 channel groups of one chunk and are
+//            independent (own LDS slice, no barrier).
+//   SUB = 4: for fewer channels, the 4 waves take the 4 quarter-chunks (128 tokens)
+//            of one channel group, each from a zero start, and wave 0 joins them in
+//            order: P = P1 P2 P3 P4, F folds the quarters' F left to right with their
+//            decays, and X = X1 + P1 X2 + P1 P2 X3 + P1 P2 P3 X4 (a quarter past L
+//            has Delta = g = 0: P = 1, F = X = 0).
 constexpr int kSumWaves = 4;
-constexpr int64_t kSumTokseqMinWaves = 4096;
+constexpr int64_t kSumTokseqMinWaves = 4096;      // one wave per (chunk, channel group) from here
+constexpr int64_t kSumSplitMinWaves = 1024;       // quarter-chunk waves from here (measured)
 
 // Eight consecutive activations of one channel (cached: in bfloat16 a block's 8
 // tokens of a channel are half of a cache line whose other half the next block reads).
@@ -452,9 +459,10 @@ __device__ __forceinline__ void load8_cached(const void* base, int64_t off, floa
   }
 }
 
-template <typename ACT, bool GATE>
+template <typename ACT, bool GATE, int SUB>
 __global__ __launch_bounds__(64 * kSumWaves) void bwd_summary_tokseq_kernel(BwdArgs p, BwdLayout g) {
-  constexpr int NS = 16, QL = 4, CPW = 16, T = 32, CH = 512;
+  static_assert(SUB == 1 || SUB == kSumWaves, "one channel group per wave, or one per workgroup");
+  constexpr int NS = 16, QL = 4, CPW = 16, T = 32, CH = 512, SCH = CH / SUB;
   __shared__ float4 s_bc[kSumWaves][2][T][NS / 4];   // B, C [token][state group], groups XOR-swizzled by piece
   __shared__ float4 s_tok[kSumWaves][CPW][T + 1];    // (Delta, Delta*u, g, -) per channel and token
   const int lane = threadIdx.x & 63;
@@ -465,7 +473,9 @@ __global__ __launch_bounds__(64 * kSumWaves) void bwd_summary_tokseq_kernel(BwdA
   const int64_t bc = blockIdx.x % nbc;
   const int64_t b = bc % p.batch, c = bc / p.batch;
   const int64_t ngrp = (D + CPW - 1) / CPW;
-  const int64_t grp = static_cast<int64_t>(blockIdx.x / nbc) * kSumWaves + w;
+  const int64_t grp = SUB == 1 ? static_cast<int64_t>(blockIdx.x / nbc) * kSumWaves + w
+                               : static_cast<int64_t>(blockIdx.x / nbc);
+  const int sub = SUB == 1 ? 0 : w;                  // this wave's part of the chunk
   const int64_t gcl = grp < ngrp ? grp : ngrp - 1;
   const int ch = lane / QL, q = lane % QL;
   const int64_t d_own = gcl * CPW + ch;
@@ -480,7 +490,7 @@ __global__ __launch_bounds__(64 * kSumWaves) void bwd_summary_tokseq_kernel(BwdA
     h[j] = 0.0f;
     X[j] = 0.0f;
   }
-  float cum = 0.0f;                                   // sum of Delta over the chunk so far (the channel's)
+  float cum = 0.0f;                                   // sum of Delta over the wave's part so far (the channel's)
   const int64_t bc_row = b * NS * L;
   float* bc_w = reinterpret_cast<float*>(s_bc[w]);
   float4* tok_w = s_tok[w][ch];
@@ -500,9 +510,9 @@ __global__ __launch_bounds__(64 * kSumWaves) void bwd_summary_tokseq_kernel(BwdA
     load8_cached<ACT>(p.Cm, bc_row + (lane / QL) * L + t, rc);
   };
 
-  const int64_t tc0 = c * CH;
+  const int64_t tc0 = c * CH + sub * SCH;
   fetch(tc0);
-  for (int blk = 0; blk < CH / T; ++blk) {
+  for (int blk = 0; blk < SCH / T; ++blk) {
     const int64_t t0 = tc0 + blk * T;
     const bool pvalid = t0 + 8 * q < L;              // L % 8 == 0: a piece is all in or all out
     // ---- per-token work of this lane's piece; the block's B and C
@@ -529,7 +539,7 @@ __global__ __launch_bounds__(64 * kSumWaves) void bwd_summary_tokseq_kernel(BwdA
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    fetch(t0 + T < tc0 + CH ? t0 + T : t0);          // next block (the last one reloads itself, unused)
+    fetch(t0 + T < tc0 + SCH ? t0 + T : t0);         // next block (the last one reloads itself, unused)
 
     // ---- the forward walk: F (the state), X (decay-weighted g C) over the block
 #pragma unroll
@@ -560,13 +570,48 @@ __global__ __launch_bounds__(64 * kSumWaves) void bwd_summary_tokseq_kernel(BwdA
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
-  if (store_ok) {
-    const int64_t off = ((b * g.nchunks + c) * D + d) * NS + 4 * q;
+  const int64_t off = ((b * g.nchunks + c) * D + d) * NS + 4 * q;
+  if constexpr (SUB == 1) {
+    if (store_ok) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      g.F[off + j] = h[j];
-      g.X[off + j] = X[j];
-      g.P[off + j] = exp2_hw(a2[j] * cum);
+      for (int j = 0; j < 4; ++j) {
+        g.F[off + j] = h[j];
+        g.X[off + j] = X[j];
+        g.P[off + j] = exp2_hw(a2[j] * cum);
+      }
+    }
+  } else {
+    // each wave's (F, X, sum of Delta) per lane into its own LDS slice (its token
+    // values are no longer needed), then wave 0 joins the parts in token order
+    float4* part_w = &s_tok[w][0][0];
+    part_w[3 * lane + 0] = make_float4(h[0], h[1], h[2], h[3]);
+    part_w[3 * lane + 1] = make_float4(X[0], X[1], X[2], X[3]);
+    part_w[3 * lane + 2] = make_float4(cum, 0.0f, 0.0f, 0.0f);
+    __syncthreads();
+    if (w == 0 && store_ok) {
+      float F[4] = {0.0f, 0.0f, 0.0f, 0.0f}, Xs[4] = {0.0f, 0.0f, 0.0f, 0.0f}, Dp[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+      float ctot = 0.0f;
+#pragma unroll
+      for (int k = 0; k < SUB; ++k) {
+        const float4* part_k = &s_tok[k][0][0];
+        const float4 hv = part_k[3 * lane + 0], xv = part_k[3 * lane + 1];
+        const float ck = part_k[3 * lane + 2].x;
+        const float hs[4] = {hv.x, hv.y, hv.z, hv.w}, xs[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float Pk = exp2_hw(a2[j] * ck);
+          F[j] = __builtin_fmaf(Pk, F[j], hs[j]);
+          Xs[j] = __builtin_fmaf(Dp[j], xs[j], Xs[j]);
+          Dp[j] *= Pk;
+        }
+        ctot += ck;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        g.F[off + j] = F[j];
+        g.X[off + j] = Xs[j];
+        g.P[off + j] = exp2_hw(a2[j] * ctot);
+      }
     }
   }
 }
@@ -929,11 +974,15 @@ __global__ void bwd_bc_out_kernel(BwdArgs p, BwdLayout g) {
 
 bool aligned16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; }
 
-// The token-sequential summary: N = 16 (512-token chunks), the vector path, and
-// enough (batch row, chunk, 16-channel group) waves to fill the chip (measured).
-bool bwd_summary_tokseq_ok(const BwdArgs& a, const BwdLayout& g, bool vec) {
-  if (a.N != 16 || g.kpl != 8 || !vec) return false;
-  return a.batch * g.nchunks * ((a.D + 15) / 16) >= kSumTokseqMinWaves;
+// The token-sequential summary: N = 16 (512-token chunks) and the vector path.
+// Returns the parts per chunk (1 or 4) that give enough waves to fill the chip, or 0
+// for the chunked summary (measured thresholds).
+int bwd_summary_tokseq_parts(const BwdArgs& a, const BwdLayout& g, bool vec) {
+  if (a.N != 16 || g.kpl != 8 || !vec) return 0;
+  const int64_t waves = a.batch * g.nchunks * ((a.D + 15) / 16);
+  if (waves >= kSumTokseqMinWaves) return 1;
+  if (waves * kSumWaves >= kSumSplitMinWaves) return kSumWaves;
+  return 0;
 }
 
 template <typename ACT, int KPL, int kW, int NT>
@@ -942,13 +991,22 @@ hipError_t launch_bwd_typed(const BwdArgs& a, const BwdLayout& g, hipStream_t s)
                    (a.z == nullptr || aligned16(a.z)) && aligned16(a.du) && aligned16(a.ddelta) &&
                    (a.dz == nullptr || aligned16(a.dz)) && aligned16(a.Bm) && aligned16(a.Cm);
   const int64_t blocks = a.batch * g.nchunks * g.nslices;
-  if (bwd_summary_tokseq_ok(a, g, vec)) {
+  const int parts = bwd_summary_tokseq_parts(a, g, vec);
+  if (parts == 1) {
     const int64_t sblocks = a.batch * g.nchunks * ((a.D + 16 * kSumWaves - 1) / (16 * kSumWaves));
     if (a.z)
-      hipLaunchKernelGGL((bwd_summary_tokseq_kernel<ACT, true>), dim3(static_cast<unsigned>(sblocks)),
+      hipLaunchKernelGGL((bwd_summary_tokseq_kernel<ACT, true, 1>), dim3(static_cast<unsigned>(sblocks)),
                          dim3(64 * kSumWaves), 0, s, a, g);
     else
-      hipLaunchKernelGGL((bwd_summary_tokseq_kernel<ACT, false>), dim3(static_cast<unsigned>(sblocks)),
+      hipLaunchKernelGGL((bwd_summary_tokseq_kernel<ACT, false, 1>), dim3(static_cast<unsigned>(sblocks)),
+                         dim3(64 * kSumWaves), 0, s, a, g);
+  } else if (parts == kSumWaves) {
+    const int64_t sblocks = a.batch * g.nchunks * ((a.D + 15) / 16);
+    if (a.z)
+      hipLaunchKernelGGL((bwd_summary_tokseq_kernel<ACT, true, kSumWaves>), dim3(static_cast<unsigned>(sblocks)),
+                         dim3(64 * kSumWaves), 0, s, a, g);
+    else
+      hipLaunchKernelGGL((bwd_summary_tokseq_kernel<ACT, false, kSumWaves>), dim3(static_cast<unsigned>(sblocks)),
                          dim3(64 * kSumWaves), 0, s, a, g);
   } else {
     hipLaunchKernelGGL((bwd_summary_kernel<ACT, KPL, kW, NT>), dim3(static_cast<unsigned>(blocks)), dim3(64 * kW), 0,

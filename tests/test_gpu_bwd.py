@@ -192,12 +192,17 @@ def _run_oracle_sliced(inp, dyv, hz, dfin, step=512):
 @pytest.mark.parametrize("batch,L,D,dtype,kw", [
     (2, 4104, 3640, "f32", dict(h0=True, dfinal=True)),
     (8, 1032, 2728, "bf16", dict()),
+    (2, 1032, 1000, "f32", dict(h0=True, dfinal=True)),
+    (3, 1544, 700, "bf16", dict(gate=False)),
 ])
 def test_bwd_many_channel_chunks(batch, L, D, dtype, kw):
-    """Shapes with at least 4096 (chunk, 16-channel group) pairs, where the
-    chunk summaries come from the token-sequential summary kernel: the last
-    512-token chunk holds 8 tokens, the last 16-channel group is half idle and
-    the last workgroup's 64 channels are partly past the end."""
+    """Shapes where the chunk summaries come from the token-sequential summary
+    kernel.  The first two have at least 4096 (chunk, 16-channel group) pairs (one
+    wave each); the last two have from 256 to 4095, where four waves take the four
+    128-token quarters of a chunk and are joined.  In all of them the last 512-token
+    chunk holds 8 tokens (so three of its quarters are past the end), and the last
+    16-channel group is partly idle; in the first two, so is the last workgroup's
+    64 channels."""
     inp, dyv, dyup, hz, dfin = _case(batch, L, D, 16, dtype, seed=D, **kw)
     got = _run_gpu(inp, dyup, hz, dfin)
     ref = _run_oracle_sliced(inp, dyv, hz, dfin)
