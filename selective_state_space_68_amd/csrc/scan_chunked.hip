@@ -139,6 +139,16 @@ __global__ __launch_bounds__(64 * kW) void scan_chunked_kernel(ScanArgs p, int n
     if (VEC && nv == KPL) {
       IO::unpack(u_raw, uv);
       IO::unpack(d_raw, dl);
+    } else if (CONV && VEC && KPL == 8) {
+      // The vector path has L % 8 == 0, so at 8 tokens per lane a lane's tokens
+      // are all in the row or all past it: this lane is past the end.  (With the
+      // fused conv, element loads here, merged with the vector path, made the
+      // compiler keep the prefetched vectors in scratch memory.)
+#pragma unroll
+      for (int j = 0; j < KPL; ++j) {
+        uv[j] = 0.0f;
+        dl[j] = 0.0f;
+      }
     } else {
 #pragma unroll
       for (int j = 0; j < KPL; ++j) {
@@ -150,18 +160,23 @@ __global__ __launch_bounds__(64 * kW) void scan_chunked_kernel(ScanArgs p, int n
     if constexpr (CONV) {
       // uv holds x: u = SiLU(conv(x)).  The 3 inputs before this lane's first
       // token are the previous lane's last three (lane 0: the previous chunk's).
-      float xx[KPL + 3];
-#pragma unroll
-      for (int k = 0; k < 3; ++k) xx[k] = wave_shift_up(uv[KPL - 3 + k], cvc[k]);
-#pragma unroll
-      for (int j = 0; j < KPL; ++j) xx[3 + j] = uv[j];
+      // A sliding window of three scalars (an indexed window array was left in
+      // scratch memory by the compiler); taps applied oldest first.
+      float xm3 = wave_shift_up(uv[KPL - 3], cvc[0]);
+      float xm2 = wave_shift_up(uv[KPL - 2], cvc[1]);
+      float xm1 = wave_shift_up(uv[KPL - 1], cvc[2]);
 #pragma unroll
       for (int k = 0; k < 3; ++k) cvc[k] = wave_lane63(uv[KPL - 3 + k]);
 #pragma unroll
       for (int j = 0; j < KPL; ++j) {
-        float sc = cbias;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) sc = __builtin_fmaf(cw4[k], xx[j + k], sc);
+        const float x0 = uv[j];
+        float sc = __builtin_fmaf(cw4[0], xm3, cbias);
+        sc = __builtin_fmaf(cw4[1], xm2, sc);
+        sc = __builtin_fmaf(cw4[2], xm1, sc);
+        sc = __builtin_fmaf(cw4[3], x0, sc);
+        xm3 = xm2;
+        xm2 = xm1;
+        xm1 = x0;
         uv[j] = sc * __builtin_amdgcn_rcpf(1.0f + exp2_hw(-sc * kLog2e));
       }
       if (p.u_out && valid) {
@@ -200,6 +215,9 @@ __global__ __launch_bounds__(64 * kW) void scan_chunked_kernel(ScanArgs p, int n
       float zv[KPL];
       if (VEC && nv == KPL) {
         IO::unpack(z_raw, zv);
+      } else if (CONV && VEC && KPL == 8) {         // past the end (as in the prologue)
+#pragma unroll
+        for (int j = 0; j < KPL; ++j) zv[j] = 0.0f;
       } else {
 #pragma unroll
         for (int j = 0; j < KPL; ++j) zv[j] = j < nv ? load_act<ACT>(p.z, row + tl + j) : 0.0f;
