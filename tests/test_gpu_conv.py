@@ -60,6 +60,10 @@ FUSED_SHAPES = [
     (1, 700, 5, 16, "bf16", True, 3),
     (2, 2048, 24, 16, "bf16", True, 4),
     (1, 4100, 3, 8, "f32", True, 2),
+    # L % 8 == 0 with an 8-token last chunk: the vector kernels (N = 16) with
+    # lanes past the end, which the fused conv zeroes instead of loading
+    (2, 1032, 40, 16, "f32", True, 4),
+    (1, 1544, 30, 16, "bf16", True, 3),
 ]
 
 
