@@ -620,14 +620,15 @@ __global__ __launch_bounds__(64 * kSumWaves) void bwd_summary_tokseq_kernel(BwdA
 constexpr int kAhead = 8;   // loads issued ahead in the sequential combine and sums
 
 // sum_{k < count} src[k * stride], added in k order (so bitwise the plain loop's
-// result), with the loads issued kAhead at a time (indices past the end clamped to
-// the last, their values unused).
+// result), with the loads issued kAhead at a time (each behind a uniform branch,
+// so the group has no wait between its loads).
 __device__ __forceinline__ float ordered_sum(const float* src, int64_t stride, int64_t count) {
   float s = 0.0f;
   for (int64_t k0 = 0; k0 < count; k0 += kAhead) {
     float v[kAhead];
 #pragma unroll
-    for (int j = 0; j < kAhead; ++j) v[j] = src[(k0 + j < count ? k0 + j : count - 1) * stride];
+    for (int j = 0; j < kAhead; ++j)
+      if (k0 + j < count) v[j] = src[(k0 + j) * stride];
 #pragma unroll
     for (int j = 0; j < kAhead; ++j)
       if (k0 + j < count) s += v[j];
@@ -644,17 +645,18 @@ __global__ void bwd_combine_kernel(BwdArgs p, BwdLayout g) {
   const int64_t stride = D * N;
   const int64_t base = b * g.nchunks * stride + d * N + n;
   const int64_t nch = g.nchunks;
-  // The chunks' values are loaded kAhead at a time before any of them is replaced
-  // (indices past the end are clamped to the last chunk and their values unused),
+  // The chunks' values are loaded kAhead at a time before any of them is replaced,
   // so each group costs one memory round trip instead of one per chunk.
   float h = p.h0 ? p.h0[i] : 0.0f;
   for (int64_t c0 = 0; c0 < nch; c0 += kAhead) {
     float f[kAhead], dec[kAhead];
 #pragma unroll
     for (int j = 0; j < kAhead; ++j) {
-      const int64_t o = base + (c0 + j < nch ? c0 + j : nch - 1) * stride;
-      f[j] = g.F[o];
-      dec[j] = g.P[o];
+      if (c0 + j < nch) {
+        const int64_t o = base + (c0 + j) * stride;
+        f[j] = g.F[o];
+        dec[j] = g.P[o];
+      }
     }
 #pragma unroll
     for (int j = 0; j < kAhead; ++j) {
@@ -669,9 +671,11 @@ __global__ void bwd_combine_kernel(BwdArgs p, BwdLayout g) {
     float x[kAhead], dec[kAhead];
 #pragma unroll
     for (int j = 0; j < kAhead; ++j) {
-      const int64_t o = base + (c0 - j >= 0 ? c0 - j : 0) * stride;
-      x[j] = g.X[o];
-      dec[j] = g.P[o];
+      if (c0 - j >= 0) {
+        const int64_t o = base + (c0 - j) * stride;
+        x[j] = g.X[o];
+        dec[j] = g.P[o];
+      }
     }
 #pragma unroll
     for (int j = 0; j < kAhead; ++j) {
