@@ -224,7 +224,9 @@ __global__ __launch_bounds__(256) void ssd_scan_kernel(SsdArgs p) {
     cr.dt = bf16_at(reinterpret_cast<const uint16_t*>(dtg + t0 * dtrow_b + (dt_off < dcap ? dt_off : dcap)));
   };
 
-  fetch(c_begin);
+  // (a segment always has a chunk; the clamp keeps the first fetch inside the
+  // sequence regardless: a chunk starting at or past L would wrap the row limit)
+  fetch(c_begin < nchunks ? c_begin : nchunks - 1);
   for (int64_t c = c_begin; c < c_end; ++c) {
     const int64_t t0 = c * kQ;
     // ---- 1. Delta and the cumulative decay exponent (every wave, lane = token); the
@@ -455,13 +457,18 @@ __global__ void ssd_combine_kernel(SsdArgs p, int64_t PN) {
 bool ssd_supported(int64_t H, int64_t P, int64_t N) { return H <= 65536 && P == kP && (N == 64 || N == 128); }
 
 // Segments per sequence: enough workgroups for about three per CU (the kernel is
-// latency-bound at one wave per SIMD), at least 4 chunks per segment.
+// latency-bound at one wave per SIMD), at least 4 chunks per segment.  The count is
+// then derived back from the segment length, so that no segment is empty: with
+// ceil(chunks / s) chunks per segment, s segments can leave the last ones without
+// a chunk (130 chunks in 32 segments of 5 use only 26).
 int ssd_segments(int64_t batch, int64_t L, int64_t H) {
   const int64_t nch = (L + kQ - 1) / kQ;
   int64_t s = (768 + batch * H - 1) / (batch * H);
   const int64_t smax = nch / 4 > 1 ? nch / 4 : 1;
   s = s < 1 ? 1 : (s > smax ? smax : s);
-  return static_cast<int>(s > 64 ? 64 : s);
+  s = s > 64 ? 64 : s;
+  const int64_t per = (nch + s - 1) / s;
+  return static_cast<int>((nch + per - 1) / per);
 }
 
 size_t ssd_workspace_bytes(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N) {

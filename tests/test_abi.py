@@ -268,6 +268,27 @@ def test_ssd_workspace_size(lib):
     assert _ssd(lib, batch=0) == _lib.SSM_OK
 
 
+@pytest.mark.parametrize("batch,L,H,segments", [
+    (4, 2048, 80, 3),       # the 2.7B-shaped workload: 32 chunks in 3 segments of 11
+    (1, 8192, 24, 32),      # 128 chunks in 32 segments of 4
+    (1, 8320, 24, 26),      # 130 chunks: 26 segments of 5 (32 of 5 would leave 6 empty)
+    (1, 2085, 2, 7),        # 33 chunks: 7 segments of 5 (8 of 5 would leave the last empty)
+])
+def test_ssd_segments_never_empty(lib, batch, L, H, segments):
+    # The workspace holds one P x N state and one decay per (batch, head, segment),
+    # plus 256 bytes, so its size gives the segment count.  Every segment must hold
+    # a chunk: a segment starting at or past L would have nothing to load.
+    P = N = 64
+    size = lib.ssm_ssd_scan_workspace_size(batch, L, H, P, N, 1)
+    per_segment = batch * H * (P * N + 1) * 4
+    assert (size - 256) % per_segment == 0
+    nseg = (size - 256) // per_segment
+    assert nseg == segments
+    nch = (L + 63) // 64
+    per = (nch + nseg - 1) // nseg
+    assert (nseg - 1) * per < nch                                   # the last segment starts inside L
+
+
 def test_scan_kernel_choice(lib):
     """The kernel query (host-only) follows the documented choice: the token-sequential
     kernel for N = 16 from 32768 channels, the chunked kernel otherwise, and the

@@ -139,3 +139,28 @@ def test_ssd_segments_match_single_pass_and_oracle():
     torch.cuda.synchronize()
     _check(host(y_seg), host(st), ry, rf, "segments, in place")
     _check(host(y_one), host(f_one), ry, rf, "one segment")
+
+
+@pytest.mark.parametrize("L", [8192, 8320], ids=["32x4chunks", "26x5chunks"])
+def test_ssd_many_segments(L):
+    """One batch row of 24 heads over 8192 or 8320 tokens: 32 segments of 4 chunks,
+    and 130 chunks as 26 segments of 5 (a count that leaves no segment empty).  Both
+    match the oracle on three heads, and the segmented run matches the one-segment
+    run (no workspace) on every head."""
+    import torch
+    from selective_state_space_68_amd import ssd_scan_fwd
+    H = 24
+    inp = synth.make_ssd_inputs(1, L, H, 64, 64, "bf16", seed=L, with_h0=True)
+    t = {k: dev(inp.dev[k]) for k in ("x", "dt", "B", "C")}
+    A, Dk, bias = dev(inp.A), dev(inp.D), dev(inp.dt_bias)
+    y_seg, f_seg = ssd_scan_fwd(t["x"], t["dt"], A, t["B"], t["C"], Dk, bias, True, initial_state=dev(inp.h0))
+    y_one, f_one = ssd_scan_fwd(t["x"], t["dt"], A, t["B"], t["C"], Dk, bias, True, initial_state=dev(inp.h0),
+                                workspace=None)
+    torch.cuda.synchronize()
+    ys, fs, yo, fo = host(y_seg), host(f_seg), host(y_one), host(f_one)
+    assert np.isfinite(ys).all() and np.isfinite(fs).all()
+    _check(ys, fs, yo.astype(np.float64), fo.astype(np.float64), f"L={L} segmented vs one segment")
+    heads = [0, 11, H - 1]
+    ry, rf = oracle.ssd_scan(inp.x[:, :, heads], inp.dt[:, :, heads], inp.A[heads], inp.B, inp.C, inp.D[heads],
+                             inp.dt_bias[heads], h0=inp.h0[:, heads])
+    _check(ys[:, :, heads], fs[:, heads], ry, rf, f"L={L} heads={heads}")
