@@ -454,16 +454,23 @@ __global__ void ssd_combine_kernel(SsdArgs p, int64_t PN) {
 
 // (H is bounded so that a chunk's 64 token rows of x span less than 4 GB: the loads
 // use 32-bit offsets from the chunk's first token)
+constexpr int64_t kSsdCUs = 256;                 // compute units of the MI355X
+
 bool ssd_supported(int64_t H, int64_t P, int64_t N) { return H <= 65536 && P == kP && (N == 64 || N == 128); }
 
-// Segments per sequence: enough workgroups for about three per CU (the kernel is
-// latency-bound at one wave per SIMD), at least 4 chunks per segment.  The count is
-// then derived back from the segment length, so that no segment is empty: with
-// ceil(chunks / s) chunks per segment, s segments can leave the last ones without
-// a chunk (130 chunks in 32 segments of 5 use only 26).
-int ssd_segments(int64_t batch, int64_t L, int64_t H) {
+// Segments per sequence: as many as keep the main pass's workgroups within one
+// wave of what the chip holds at once (N = 64: 2 per CU; N = 128: 1), at least 4
+// chunks per segment.  Measured over segment counts on seven shapes, that count was
+// the fastest in every one: a second, partial wave of workgroups, and the pre-pass
+// and combine that segments need, cost more than the parallelism gains (at
+// 4 x 2048 x 80 heads, one segment: 105.5 us against 112.6 with three).  The count
+// is then derived back from the segment length, so that no segment is empty: with
+// ceil(chunks / s) chunks per segment, s segments can leave the last ones without a
+// chunk (130 chunks in 21 segments of 7 use only 19).
+int ssd_segments(int64_t batch, int64_t L, int64_t H, int64_t N) {
   const int64_t nch = (L + kQ - 1) / kQ;
-  int64_t s = (768 + batch * H - 1) / (batch * H);
+  const int64_t resident = (N <= 64 ? 2 : 1) * kSsdCUs;
+  int64_t s = resident / (batch * H);
   const int64_t smax = nch / 4 > 1 ? nch / 4 : 1;
   s = s < 1 ? 1 : (s > smax ? smax : s);
   s = s > 64 ? 64 : s;
@@ -472,7 +479,7 @@ int ssd_segments(int64_t batch, int64_t L, int64_t H) {
 }
 
 size_t ssd_workspace_bytes(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N) {
-  const int s = ssd_segments(batch, L, H);
+  const int s = ssd_segments(batch, L, H, N);
   if (s <= 1) return 0;
   return static_cast<size_t>(batch * H * s) * (P * N + 1) * sizeof(float) + 256;
 }
@@ -480,7 +487,7 @@ size_t ssd_workspace_bytes(int64_t batch, int64_t L, int64_t H, int64_t P, int64
 template <int NS>
 hipError_t launch_ssd_n(SsdArgs a, void* ws, size_t ws_bytes, hipStream_t s) {
   const int64_t nch = (a.L + kQ - 1) / kQ;
-  int nseg = ssd_segments(a.batch, a.L, a.H);
+  int nseg = ssd_segments(a.batch, a.L, a.H, NS);
   if (!ws || ws_bytes < ssd_workspace_bytes(a.batch, a.L, a.H, kP, NS)) nseg = 1;
   a.nseg = nseg;
   a.seg_chunks = (nch + nseg - 1) / nseg;

@@ -261,28 +261,36 @@ def test_ssd_argument_errors(lib, kw, status):
 
 def test_ssd_workspace_size(lib):
     ws = lib.ssm_ssd_scan_workspace_size
-    assert ws(4, 2048, 80, 64, 64, 1) > 0                          # 320 (batch, head) pairs: segments help
+    assert ws(2, 4096, 64, 64, 64, 1) > 0                          # 128 (batch, head) pairs: segments help
+    assert ws(4, 2048, 80, 64, 64, 1) == 0                         # 320 pairs fill the chip: one segment
     assert ws(1, 64, 2, 64, 64, 1) == 0                            # a single chunk: nothing to split
     assert ws(4, 2048, 80, 64, 64, 0) == 0 and ws(4, 2048, 80, 32, 64, 1) == 0
     assert _ssd(lib) == _lib.SSM_ERR_HIP                            # valid arguments reach the device probe
     assert _ssd(lib, batch=0) == _lib.SSM_OK
 
 
-@pytest.mark.parametrize("batch,L,H,segments", [
-    (4, 2048, 80, 3),       # the 2.7B-shaped workload: 32 chunks in 3 segments of 11
-    (1, 8192, 24, 32),      # 128 chunks in 32 segments of 4
-    (1, 8320, 24, 26),      # 130 chunks: 26 segments of 5 (32 of 5 would leave 6 empty)
-    (1, 2085, 2, 7),        # 33 chunks: 7 segments of 5 (8 of 5 would leave the last empty)
+@pytest.mark.parametrize("batch,L,H,N,segments", [
+    (4, 2048, 80, 64, 1),     # the 2.7B-shaped workload: 320 workgroups already fill the chip
+    (2, 4096, 64, 64, 4),     # 128 (batch, head) pairs: 4 segments of 16 chunks, 512 workgroups
+    (1, 8192, 24, 64, 19),    # 128 chunks: 21 segments would be of 7, and 19 of 7 cover them
+    (1, 8320, 24, 64, 19),    # 130 chunks: 19 segments of 7 (21 of 7 would leave 2 empty)
+    (1, 2085, 2, 64, 7),      # 33 chunks: 7 segments of 5 (8 of 5 would leave the last empty)
+    (1, 16384, 16, 64, 32),   # 256 chunks in 32 segments of 8
+    (1, 8192, 8, 128, 32),    # N = 128 holds one workgroup per CU: 32 segments of 4
 ])
-def test_ssd_segments_never_empty(lib, batch, L, H, segments):
+def test_ssd_segments_never_empty(lib, batch, L, H, N, segments):
     # The workspace holds one P x N state and one decay per (batch, head, segment),
-    # plus 256 bytes, so its size gives the segment count.  Every segment must hold
-    # a chunk: a segment starting at or past L would have nothing to load.
-    P = N = 64
+    # plus 256 bytes, so its size gives the segment count (no workspace: one
+    # segment).  Every segment must hold a chunk: a segment starting at or past L
+    # would have nothing to load.
+    P = 64
     size = lib.ssm_ssd_scan_workspace_size(batch, L, H, P, N, 1)
     per_segment = batch * H * (P * N + 1) * 4
-    assert (size - 256) % per_segment == 0
-    nseg = (size - 256) // per_segment
+    if size == 0:
+        nseg = 1
+    else:
+        assert (size - 256) % per_segment == 0
+        nseg = (size - 256) // per_segment
     assert nseg == segments
     nch = (L + 63) // 64
     per = (nch + nseg - 1) // nseg
