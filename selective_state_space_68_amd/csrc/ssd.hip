@@ -460,17 +460,21 @@ bool ssd_supported(int64_t H, int64_t P, int64_t N) { return H <= 65536 && P == 
 
 // Segments per sequence: as many as keep the main pass's workgroups within one
 // wave of what the chip holds at once (N = 64: 2 per CU; N = 128: 1), at least 4
-// chunks per segment.  Measured over segment counts on seven shapes, that count was
-// the fastest in every one: a second, partial wave of workgroups, and the pre-pass
-// and combine that segments need, cost more than the parallelism gains (at
-// 4 x 2048 x 80 heads, one segment: 105.5 us against 112.6 with three).  The count
-// is then derived back from the segment length, so that no segment is empty: with
-// ceil(chunks / s) chunks per segment, s segments can leave the last ones without a
-// chunk (130 chunks in 21 segments of 7 use only 19).
+// chunks per segment.  Measured over segment counts on ten shapes, that count was
+// the fastest wherever the (batch, head) pairs fit in one wave: a second, partial
+// wave of workgroups, and the pre-pass and combine that segments need, cost more
+// than the parallelism gains (at 4 x 2048 x 80 heads, N = 64, one segment: 105.5 us
+// against 112.6 with three).  Past one wave, N = 64 measured fastest unsegmented;
+// N = 128 (4 x 2048 x 80 heads) with about 768 workgroups, 3 segments: 191 us
+// against 212 unsegmented.  The count is then derived back from the segment
+// length, so that no segment is empty: with ceil(chunks / s) chunks per segment,
+// s segments can leave the last ones without a chunk (130 chunks in 21 segments of
+// 7 use only 19).
 int ssd_segments(int64_t batch, int64_t L, int64_t H, int64_t N) {
   const int64_t nch = (L + kQ - 1) / kQ;
   const int64_t resident = (N <= 64 ? 2 : 1) * kSsdCUs;
-  int64_t s = resident / (batch * H);
+  const int64_t pairs = batch * H;
+  int64_t s = pairs <= resident ? resident / pairs : (N <= 64 ? 1 : (768 + pairs - 1) / pairs);
   const int64_t smax = nch / 4 > 1 ? nch / 4 : 1;
   s = s < 1 ? 1 : (s > smax ? smax : s);
   s = s > 64 ? 64 : s;

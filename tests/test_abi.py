@@ -277,6 +277,8 @@ def test_ssd_workspace_size(lib):
     (1, 2085, 2, 64, 7),      # 33 chunks: 7 segments of 5 (8 of 5 would leave the last empty)
     (1, 16384, 16, 64, 32),   # 256 chunks in 32 segments of 8
     (1, 8192, 8, 128, 32),    # N = 128 holds one workgroup per CU: 32 segments of 4
+    (4, 2048, 80, 128, 3),    # N = 128 past one wave (320 pairs): about 768 workgroups, 3 segments
+    (8, 2048, 80, 64, 1),     # N = 64 past one wave (640 pairs): one segment
 ])
 def test_ssd_segments_never_empty(lib, batch, L, H, N, segments):
     # The workspace holds one P x N state and one decay per (batch, head, segment),
