@@ -23,7 +23,9 @@
 // over chunks:
 //   1. summary: per (b, chunk, d, n), the chunk's forward aggregate F (its end
 //      state from a zero start) and reverse aggregate X (the adjoint it sends to
-//      the previous chunk from a zero start), and its decay P = exp(A sum Delta);
+//      the previous chunk from a zero start), and its decay P = exp(A sum Delta)
+//      (at N = 16 with enough channels, from one token-sequential forward walk:
+//      bwd_summary_tokseq_kernel);
 //   2. combine: per (b, d, n), a sequential pass over the chunks turns F into the
 //      state entering each chunk and X into the adjoint entering each chunk;
 //   3. main: per (b, chunk, d), recompute the states inside the chunk from its
@@ -34,16 +36,16 @@
 //      delta bias; dB and dC from float32 to the activation dtype.
 //
 // A workgroup of kW waves owns one (batch row, chunk) pair and a slice of
-// kW * rounds channels: it stages the chunk's B and C once in LDS (float32,
-// permuted so that each lane's tokens are contiguous), and each wave runs one
-// channel per round.  dB and dC are sums over channels.  The main kernel's waves
-// step through the states in pairs together: each wave writes its channel's dB
-// and dC terms for the pair to its own LDS slot, and after a barrier every thread
-// adds the kW slots' values of the entries it owns, in wave order, into its
-// registers (N = 16) or into the workgroup's region of the workspace (other N).
-// Each workgroup writes its slice's partial sums once; the finalize kernel adds
-// the slices in slice order.  Every output is formed in a fixed order, so the
-// results are bitwise reproducible.  (LDS float atomics, the obvious alternative,
+// kW * rounds channels (about one workgroup per CU): it stages the chunk's B and C
+// once in LDS (float32, permuted so that each lane's tokens are contiguous), and
+// each wave runs one channel per round.  dB and dC are sums over channels.  The
+// main kernel's waves step through the states in pairs together: each wave writes
+// its channel's dB and dC terms for the pair to its own LDS slot, and after a
+// barrier every thread adds the kW slots' values of the entries it owns, in wave
+// order, to the workgroup's region of the workspace (its slice's partial for this
+// batch row and chunk, read and rewritten once per round); the finalize kernel
+// adds the slices in slice order.  Every output is formed in a fixed order, so
+// the results are bitwise reproducible.  (LDS float atomics, the obvious alternative,
 // measured 7x slower on gfx950 than this whole kernel.)
 #include <utility>
 

@@ -14,18 +14,18 @@
 // on MFMA; only the P x N state crosses chunks, in registers.
 //
 // Work decomposition: one workgroup of 4 waves per (batch row, head, segment) walks
-// its segment of the sequence chunk by chunk.  With one segment per sequence there
-// are too few waves to hide latency (one per SIMD at the model shapes), so the
-// sequence is cut into segments: a pre-pass computes each segment's end state from
-// zero, a small kernel chains them into each segment's entering state (the operator
-// of the forward recurrence on whole segments), and the main pass runs every
-// segment from its entering state.  Within a workgroup, wave w owns head channels p in [16w, 16w+16) of the
+// its segment of the sequence chunk by chunk.  When the (batch row, head) pairs are
+// too few to fill one resident wave of workgroups, the sequence is cut into
+// segments: a pre-pass computes each segment's end state from zero, a small kernel
+// chains them into each segment's entering state (the operator of the forward
+// recurrence on whole segments), and the main pass runs every segment from its
+// entering state.  Within a workgroup, wave w owns head channels p in [16w, 16w+16) of the
 // products with x, H and y, and rows j in [16w, 16w+16) of C B^T.  The chunk's x, B
 // and C go through LDS as bfloat16 (x and B also transposed, so every MFMA operand
 // is a contiguous 16-byte LDS read), and the next chunk's inputs are loaded into
 // registers while the current one computes.  Inputs are bfloat16; the products
-// accumulate in float32 and the state stays float32 (it is rounded to bfloat16
-// only as the operand of the carried-state product).
+// accumulate in float32 and the state stays float32 (it is split into two bfloat16
+// terms, hi + lo, only as the operand of the carried-state product).
 //
 // MFMA lane layout (gfx950, checked on the device): for v_mfma_f32_16x16x32_bf16,
 // lane l holds A[m = l%16][k = 8(l/16) .. +7], B[k = 8(l/16) .. +7][n = l%16] and
