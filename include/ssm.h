@@ -58,12 +58,15 @@ typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
 #define SSM_MAX_CONV_WIDTH 4
 
 /*
- * Selective scan, forward (prefill / training forward).
+ * Selective scan, forward (prefill / training forward): the interview-prep page's
+ * "Selective scan pseudo-code" (inputs u, Delta, A, B, C; B_t and C_t of shape
+ * (L, N) per sequence) with the D skip term, the SiLU(z) gate and the biased
+ * softplus of Delta described above.
  *
  *   u, delta, z  : [batch][D][L] act   (each channel's time series is contiguous)
  *   A            : [D][N] float32      (the diagonal state matrix, one row per channel)
- *   Bm, Cm       : [batch][N][L] act   (each state's time series is contiguous;
- *                                       shared by all D channels of a batch row)
+ *   Bm, Cm       : [batch][L][N] act   (the pages' order: a token's N values are
+ *                                       contiguous; shared by all D channels of a row)
  *   Dskip        : [D] float32 or NULL (NULL means 0)
  *   z            : NULL means no gate
  *   delta_bias   : [D] float32 or NULL (NULL means 0); added before the softplus
@@ -72,13 +75,19 @@ typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
  *   final_state  : out [batch][D][N] float32, h[b, L-1, d, :], or NULL
  *   batch, L, D  : >= 0 (a zero size is a no-op; with L == 0 the final state is 0)
  *   N            : 1..64
+ *   workspace    : device scratch owned by the caller, 16-byte aligned, of
+ *                  workspace_bytes >= ssm_selective_scan_workspace_size(...) bytes;
+ *                  may be NULL when that size is 0.  Its contents on entry do not
+ *                  matter and on return are unspecified; calls sharing one
+ *                  workspace must not overlap in time.
  *
- * The pages write B and C as (batch, L, N); the library stores every time series
- * contiguous along L (u, delta, z, y per channel; B, C per state), so that each
- * is read as coalesced vectors along L.  The values are the same.
+ * The pages write u, Delta and z as (batch, L, D); the library stores them
+ * channel-major, [batch][D][L], so that each channel's series is read as coalesced
+ * vectors along L.  The values are the same.
  *
  * Errors: SSM_ERR_INVALID_ARG for a NULL required pointer, a negative size, a
- * misaligned pointer, or y / final_state overlapping any input or each other;
+ * misaligned pointer, y / final_state overlapping any input or each other, or a
+ * workspace that is too small, misaligned or overlaps another argument;
  * SSM_ERR_UNSUPPORTED for N outside [1, 64] or a bad dtype; SSM_ERR_HIP when no
  * device is usable or the launch fails.
  */
@@ -86,7 +95,18 @@ ssm_status ssm_selective_scan_fwd(
     const void *u, const void *delta, const float *A, const void *Bm, const void *Cm,
     const float *Dskip, const void *z, const float *delta_bias, int delta_softplus,
     void *y, float *final_state,
-    int64_t batch, int64_t L, int64_t D, int64_t N, ssm_dtype dt, void *stream);
+    int64_t batch, int64_t L, int64_t D, int64_t N, ssm_dtype dt,
+    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Bytes of workspace a forward scan (ssm_selective_scan_fwd, _from_state, _variant)
+ * of this shape needs; 0 when it needs none (then workspace may be NULL).  Every
+ * kernel of this version walks a channel's whole sequence in one wave and keeps its
+ * carry in registers, so the size is 0 for every shape; callers that pass the
+ * queried size keep working when a shape starts to use one.  Returns 0 for invalid
+ * sizes or dtypes (the scan call reports those).  Host-only: touches no device.
+ */
+size_t ssm_selective_scan_workspace_size(int64_t batch, int64_t L, int64_t D, int64_t N, ssm_dtype dt);
 
 /*
  * The same scan started from a given state instead of zero: h[b, -1, d, :] =
@@ -107,7 +127,8 @@ ssm_status ssm_selective_scan_fwd_from_state(
     const void *u, const void *delta, const float *A, const void *Bm, const void *Cm,
     const float *Dskip, const void *z, const float *delta_bias, int delta_softplus,
     const float *initial_state, void *y, float *final_state,
-    int64_t batch, int64_t L, int64_t D, int64_t N, ssm_dtype dt, void *stream);
+    int64_t batch, int64_t L, int64_t D, int64_t N, ssm_dtype dt,
+    void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Same operation with an explicit kernel choice, for testing that every
@@ -134,7 +155,8 @@ ssm_status ssm_selective_scan_fwd_variant(
     const void *u, const void *delta, const float *A, const void *Bm, const void *Cm,
     const float *Dskip, const void *z, const float *delta_bias, int delta_softplus,
     const float *initial_state, void *y, float *final_state,
-    int64_t batch, int64_t L, int64_t D, int64_t N, ssm_dtype dt, void *stream,
+    int64_t batch, int64_t L, int64_t D, int64_t N, ssm_dtype dt,
+    void *workspace, size_t workspace_bytes, void *stream,
     int variant, int tokens_per_lane);
 
 /*
@@ -152,7 +174,11 @@ int ssm_selective_scan_fwd_kernel(int64_t batch, int64_t L, int64_t D, int64_t N
 /*
  * One recurrent decode step (the O(1)-state generation mode): advances the
  * state of `batch` sequences by one token with the same arithmetic as one step
- * of the scan, started from state_in instead of zero.
+ * of the scan, started from state_in instead of zero.  This is the recurrent
+ * mode of the slide deck's introduction and "Where SSMs win" section (one state
+ * update of fixed size per generated token, no cache that grows with the
+ * sequence) and of the lecture notes' §5 "Inference": h_t = exp(Delta A) h_{t-1}
+ * + Delta B_t u_t, y_t = C_t h_t (+ D u_t, gated as above).
  *
  *   state_in     : [batch][D][N] float32
  *   state_out    : [batch][D][N] float32; may equal state_in (in place) but must
@@ -182,10 +208,10 @@ ssm_status ssm_state_update(
  * readout, the skip term and the gate are unchanged.
  *
  * Arguments, layouts, outputs and errors as in ssm_selective_scan_fwd_from_state
- * and ssm_state_update.  Every A[d, n] must be nonzero (the models use A < 0): the
- * term is formed as (exp(Delta A) - 1) * (1/A), and an A of zero gives a NaN for
- * that state instead of the limit Delta * B * u.  The scan runs the chunked kernel
- * at its default 8 tokens per lane.
+ * (without a workspace) and ssm_state_update.  A state with A[d, n] == 0 takes the
+ * term's limit Delta * B * u (the simplified term: with no decay the state
+ * integrates its input).  The scan runs the chunked kernel at 8 tokens per lane or,
+ * from 32768 channels with N == 16, the token-sequential kernel.
  */
 ssm_status ssm_selective_scan_fwd_zoh(
     const void *u, const void *delta, const float *A, const void *Bm, const void *Cm,
@@ -259,7 +285,7 @@ ssm_status ssm_selective_scan_fwd_conv(
  * Outputs (each overwritten, never accumulated into):
  *   du, ddelta    : [batch][D][L] act; ddelta is w.r.t. the raw delta (before bias and softplus)
  *   dA            : [D][N] float32
- *   dB, dC        : [batch][N][L] act (the library's B/C layout)
+ *   dB, dC        : [batch][L][N] act (the layout of B and C)
  *   dD            : [D] float32 or NULL (not computed); the gradient at Dskip (0 if Dskip is NULL)
  *   dz            : [batch][D][L] act or NULL; must be NULL when z is NULL
  *   ddelta_bias   : [D] float32 or NULL; the gradient at delta_bias (0 if NULL)

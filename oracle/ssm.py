@@ -34,8 +34,8 @@ constant, the (Delta A)^-1 (exp(Delta A) - I) Delta B of the slide deck's S4
 section and the lecture notes' §3 "Discretisation" for a diagonal A.
 
 Memory order: u, delta, z are [batch][D][L] (as in the library); B, C are
-[batch][L][N] (the pages' order; the library stores them [batch][N][L]); A is
-[D][N]; Dskip and bias are [D].
+[batch][L][N] (the pages' order, as in the library); A is [D][N]; Dskip and bias
+are [D].
 """
 from __future__ import annotations
 

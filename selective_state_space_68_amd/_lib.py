@@ -28,15 +28,17 @@ SSM_SCAN_TOKSEQ = 3
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
 _int = ctypes.c_int
+_sz = ctypes.c_size_t
 
-# name -> (restype, argtypes); mirrors include/ssm.h
+# name -> (restype, argtypes); mirrors include/ssm.h and include/ssm_calib.h
 SIGNATURES = {
     "ssm_selective_scan_fwd": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _vp, _vp,
-                                      _i64, _i64, _i64, _i64, _int, _vp]),
+                                      _i64, _i64, _i64, _i64, _int, _vp, _sz, _vp]),
+    "ssm_selective_scan_workspace_size": (_sz, [_i64, _i64, _i64, _i64, _int]),
     "ssm_selective_scan_fwd_from_state": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _vp, _vp, _vp,
-                                                 _i64, _i64, _i64, _i64, _int, _vp]),
+                                                 _i64, _i64, _i64, _i64, _int, _vp, _sz, _vp]),
     "ssm_selective_scan_fwd_variant": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _vp, _vp, _vp,
-                                              _i64, _i64, _i64, _i64, _int, _vp, _int, _int]),
+                                              _i64, _i64, _i64, _i64, _int, _vp, _sz, _vp, _int, _int]),
     "ssm_selective_scan_fwd_kernel": (_int, [_i64, _i64, _i64, _i64, _int, _int, _int, _int, _int, _int]),
     "ssm_selective_scan_fwd_zoh": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _vp, _vp, _vp,
                                           _i64, _i64, _i64, _i64, _int, _vp]),
@@ -47,14 +49,17 @@ SIGNATURES = {
                                            _vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _vp, _int]),
     "ssm_state_update": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _vp,
                                 _i64, _i64, _i64, _int, _vp]),
-    "ssm_selective_scan_bwd_workspace_size": (ctypes.c_size_t, [_i64, _i64, _i64, _i64, _int]),
+    "ssm_selective_scan_bwd_workspace_size": (_sz, [_i64, _i64, _i64, _i64, _int]),
     "ssm_selective_scan_bwd": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _vp, _vp, _vp,
                                       _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                                      _i64, _i64, _i64, _i64, _int, _vp, ctypes.c_size_t, _vp]),
-    "ssm_ssd_scan_workspace_size": (ctypes.c_size_t, [_i64, _i64, _i64, _i64, _i64, _int]),
+                                      _i64, _i64, _i64, _i64, _int, _vp, _sz, _vp]),
+    "ssm_ssd_scan_workspace_size": (_sz, [_i64, _i64, _i64, _i64, _i64, _int]),
     "ssm_ssd_scan_fwd": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _vp, _vp, _vp,
-                                _i64, _i64, _i64, _i64, _i64, _int, _vp, ctypes.c_size_t, _vp]),
+                                _i64, _i64, _i64, _i64, _i64, _int, _vp, _sz, _vp]),
     "ssm_status_string": (ctypes.c_char_p, [_int]),
+    "ssm_calib_copy": (_int, [_vp, _vp, _sz, _vp]),
+    "ssm_calib_alu": (_int, [_int, _vp, _i64, _int, _vp]),
+    "ssm_calib_alu_ops": (_i64, [_i64, _int]),
     "ssm_version": (_int, []),
 }
 

@@ -110,6 +110,22 @@ __device__ __forceinline__ float softplus_f(float x) {
   return fmaxf(x, 0.0f) + __builtin_fmaf(__builtin_amdgcn_logf(w), kLn2, err);
 }
 
+// Full zero-order hold: the factor (e^x - 1)/A = Delta * (e^x - 1)/x of the input
+// term, x = Delta * A, from y = x * log2(e) (the exp2 argument), a = 2^y, ra = 1/A and
+// Delta.  Away from x = 0 it is (a - 1)/A.  Near 0 that difference loses relative
+// accuracy to the rounding of a (about 1e-7 / |x|), so for |x| < 0.0624 (|y| < 0.09)
+// it is Delta * (1 + x/2 + x^2/6 + x^3/24), whose truncation is below 1.3e-7 there;
+// at A == 0 that is Delta itself, the term's limit.  (The unselected side may be a
+// NaN at A == 0; the select does not propagate it.)
+__device__ __forceinline__ float zoh_factor(float y, float a, float ra, float delta) {
+  constexpr float c1 = 0.34657359f;     // ln2 / 2      (powers of x = y ln2)
+  constexpr float c2 = 0.08007550f;     // ln2^2 / 6
+  constexpr float c3 = 0.013876027f;    // ln2^3 / 24
+  const float p = __builtin_fmaf(y, __builtin_fmaf(y, __builtin_fmaf(y, c3, c2), c1), 1.0f);
+  const float far = __builtin_fmaf(a, ra, -ra);
+  return fabsf(y) < 0.09f ? delta * p : far;
+}
+
 // SiLU(z) = z / (1 + e^-z); e^-z = inf for very negative z gives -0.
 __device__ __forceinline__ float silu_f(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + exp2_hw(-z * kLog2e));
@@ -205,5 +221,21 @@ __device__ __forceinline__ float wave_lane63(float v) {
 }
 
 __device__ __forceinline__ int uniform_int(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Sum over the 64 lanes (wave-uniform result): row reductions with row_shr
+// (bound_ctrl zero fills), then the row broadcasts 15 and 31 into lane 63.
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_mov<0x111, 0xf, true>(0.0f, v);
+  v += dpp_mov<0x112, 0xf, true>(0.0f, v);
+  v += dpp_mov<0x114, 0xf, true>(0.0f, v);
+  v += dpp_mov<0x118, 0xf, true>(0.0f, v);
+  v += dpp_mov<0x142, 0xa, false>(0.0f, v);
+  v += dpp_mov<0x143, 0xc, false>(0.0f, v);
+  return wave_lane63(v);
+}
+
+__device__ __forceinline__ float lane_value(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
 
 }  // namespace ssm

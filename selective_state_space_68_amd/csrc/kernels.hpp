@@ -12,8 +12,8 @@ struct ScanArgs {
   const void* u;         // [batch][D][L] act
   const void* delta;     // [batch][D][L] act (raw)
   const float* A;        // [D][N]
-  const void* Bm;        // [batch][N][L] act
-  const void* Cm;        // [batch][N][L] act
+  const void* Bm;        // [batch][L][N] act
+  const void* Cm;        // [batch][L][N] act
   const float* Dskip;    // [D] or null
   const void* z;         // [batch][D][L] act or null
   const float* bias;     // [D] or null
@@ -64,8 +64,8 @@ struct BwdArgs {
   const void* u;          // [batch][D][L] act
   const void* delta;      // [batch][D][L] act (raw)
   const float* A;         // [D][N]
-  const void* Bm;         // [batch][N][L] act
-  const void* Cm;         // [batch][N][L] act
+  const void* Bm;         // [batch][L][N] act
+  const void* Cm;         // [batch][L][N] act
   const float* Dskip;     // [D] or null
   const void* z;          // [batch][D][L] act or null
   const float* bias;      // [D] or null
@@ -75,8 +75,8 @@ struct BwdArgs {
   void* du;               // [batch][D][L] act
   void* ddelta;           // [batch][D][L] act (w.r.t. the raw delta)
   float* dA;              // [D][N]
-  void* dB;               // [batch][N][L] act
-  void* dC;               // [batch][N][L] act
+  void* dB;               // [batch][L][N] act
+  void* dC;               // [batch][L][N] act
   float* dD;              // [D] or null
   void* dz;               // [batch][D][L] act or null (null whenever z is null)
   float* dbias;           // [D] or null

@@ -173,22 +173,6 @@ __device__ __forceinline__ float wave_shift_down(float v, float last) {
   return dpp_mov<0x130, 0xf, false>(last, v);
 }
 
-// Sum over the 64 lanes (wave-uniform result): row reductions with row_shr
-// (bound_ctrl zero fills), then the row broadcasts 15 and 31 into lane 63.
-__device__ __forceinline__ float wave_sum(float v) {
-  v += dpp_mov<0x111, 0xf, true>(0.0f, v);
-  v += dpp_mov<0x112, 0xf, true>(0.0f, v);
-  v += dpp_mov<0x114, 0xf, true>(0.0f, v);
-  v += dpp_mov<0x118, 0xf, true>(0.0f, v);
-  v += dpp_mov<0x142, 0xa, false>(0.0f, v);
-  v += dpp_mov<0x143, 0xc, false>(0.0f, v);
-  return wave_lane63(v);
-}
-
-__device__ __forceinline__ float lane_value(float v, int l) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
-}
-
 // ---- memory helpers -------------------------------------------------------------
 
 // Four consecutive activations from element offset i (vector: 16- or 8-byte
@@ -232,29 +216,38 @@ __device__ __forceinline__ void store_tokens(void* dst, int64_t row, int64_t t, 
 // block m*NP + n for matrix m and state n (states N..NP-1, and tokens past L, are
 // zero).  Float4 f of a block (tokens 4f .. 4f+3 of the chunk) goes to slot
 // (f % (KPL/4)) * 64 + f / (KPL/4), so lane i finds its KPL tokens as KPL/4
-// float4 at q * 64 + i.
+// float4 at q * 64 + i.  B and C are [batch][L][N]: a thread loads 4 consecutive
+// states of one token (one 16- or 8-byte vector when N % 4 == 0) and scatters them
+// into their blocks; consecutive threads take consecutive tokens.
 template <typename ACT, int KPL>
 __device__ __forceinline__ void load_tile(float4* tile, const BwdArgs& p, int64_t b, int64_t t0, int NP, bool vec) {
   constexpr int CH = 64 * KPL, F4 = CH / 4, Q = KPL / 4;
   const int N = p.N;
   const int64_t L = p.L;
-  const int total = 2 * NP * F4;
+  const int G = (NP + 3) / 4;                        // groups of 4 states per token
+  const int total = 2 * G * CH;
+  const bool v4 = vec && (N % 4 == 0);
+  float* tf = reinterpret_cast<float*>(tile);
   for (int e = threadIdx.x; e < total; e += blockDim.x) {
-    const int mn = e / F4, f = e % F4;
-    const int m = mn / NP, n = mn % NP;
+    const int tk = e % CH, mg = e / CH;
+    const int m = mg / G, n0 = 4 * (mg % G);
     const void* src = m ? p.Cm : p.Bm;
-    const int64_t off = (b * N + n) * L;
-    const int64_t t = t0 + 4 * f;
+    const int64_t t = t0 + tk;
     float x[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (n < N) {
-      if (vec && t + 4 <= L) {
-        load4<ACT>(src, off + t, x);
+    if (t < L) {
+      const int64_t off = (b * L + t) * N + n0;
+      if (v4) {
+        load4<ACT>(src, off, x);
       } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) x[r] = t + r < L ? load_act<ACT>(src, off + t + r) : 0.0f;
+        for (int r = 0; r < 4; ++r) x[r] = n0 + r < N ? load_act<ACT>(src, off + r) : 0.0f;
       }
     }
-    tile[mn * F4 + (f % Q) * 64 + f / Q] = make_float4(x[0], x[1], x[2], x[3]);
+    const int f = tk >> 2;
+    const int slot = ((f % Q) * 64 + f / Q) * 4 + (tk & 3);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (n0 + r < NP) tf[(m * NP + n0 + r) * (4 * F4) + slot] = x[r];
   }
 }
 
@@ -508,7 +501,7 @@ __global__ __launch_bounds__(64 * kSumWaves) void bwd_summary_tokseq_kernel(BwdA
     X[j] = 0.0f;
   }
   float cum = 0.0f;                                   // sum of Delta over the wave's part so far (the channel's)
-  const int64_t bc_row = b * NS * L;
+  const int64_t bc_row = b * L * NS;
   float* bc_w = reinterpret_cast<float*>(s_bc[w]);
   float4* tok_w = s_tok[w][ch];
 
@@ -520,11 +513,11 @@ __global__ __launch_bounds__(64 * kSumWaves) void bwd_summary_tokseq_kernel(BwdA
     load8_cached<ACT>(p.delta, row + tp, rd);
     load8_cached<ACT>(p.dy, row + tp, ry);
     if constexpr (GATE) load8_cached<ACT>(p.z, row + tp, rz);
-    // B and C piece of this lane: state lane / 4, tokens 8 (lane % 4) ..
-    int64_t t = t0 + 8 * (lane % QL);
-    t = t + 8 <= L ? t : L - 8;
-    load8_cached<ACT>(p.Bm, bc_row + (lane / QL) * L + t, rb);
-    load8_cached<ACT>(p.Cm, bc_row + (lane / QL) * L + t, rc);
+    // B and C piece of this lane ([L][N]): token lane / 2 of the block, states 8 (lane % 2) ..
+    int64_t t = t0 + lane / 2;
+    t = t < L ? t : L - 1;
+    load8_cached<ACT>(p.Bm, bc_row + t * NS + 8 * (lane % 2), rb);
+    load8_cached<ACT>(p.Cm, bc_row + t * NS + 8 * (lane % 2), rc);
   };
 
   const int64_t tc0 = c * CH + sub * SCH;
@@ -546,12 +539,15 @@ __global__ __launch_bounds__(64 * kSumWaves) void bwd_summary_tokseq_kernel(BwdA
       tok_w[8 * q + k] = make_float4(dl, dl * ru[k], gk, 0.0f);
     }
     {
-      const int n = lane / QL, pc = lane % QL;
-      const int col = 4 * ((n >> 2) ^ pc) + (n & 3);
+      // token t, state groups 2h and 2h + 1, each at its swizzled slot (group g of
+      // token t sits at g ^ (t / 8))
+      const int t = lane / 2, h2 = 2 * (lane % 2), sw = (t / 8) & 3;
+      float4* brow = reinterpret_cast<float4*>(bc_w + (0 * T + t) * NS);
+      float4* crow = reinterpret_cast<float4*>(bc_w + (1 * T + t) * NS);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        bc_w[(0 * T + 8 * pc + e) * NS + col] = rb[e];
-        bc_w[(1 * T + 8 * pc + e) * NS + col] = rc[e];
+      for (int g4 = 0; g4 < 2; ++g4) {
+        brow[(h2 + g4) ^ sw] = make_float4(rb[4 * g4], rb[4 * g4 + 1], rb[4 * g4 + 2], rb[4 * g4 + 3]);
+        crow[(h2 + g4) ^ sw] = make_float4(rc[4 * g4], rc[4 * g4 + 1], rc[4 * g4 + 2], rc[4 * g4 + 3]);
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -981,7 +977,8 @@ __global__ void bwd_param_sums_kernel(BwdArgs p, BwdLayout g) {
   }
 }
 
-// dB, dC = the sum over channel slices (in slice order) of the per-slice partials.
+// dB, dC = the sum over channel slices (in slice order) of the per-slice partials
+// ([slice][batch][matrix][N][L]), stored in the B/C layout [batch][L][N].
 template <typename ACT>
 __global__ void bwd_bc_out_kernel(BwdArgs p, BwdLayout g) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -990,7 +987,8 @@ __global__ void bwd_bc_out_kernel(BwdArgs p, BwdLayout g) {
   const float s = ordered_sum(g.part + i, per, g.nslices);
   const int64_t b = i / (2 * NL), rem = i % (2 * NL);
   const int m = static_cast<int>(rem / NL);
-  store_act<ACT>(m ? p.dC : p.dB, b * NL + rem % NL, s);
+  const int64_t n = (rem % NL) / L, t = rem % L;
+  store_act<ACT>(m ? p.dC : p.dB, (b * L + t) * p.N + n, s);
 }
 
 bool aligned16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; }

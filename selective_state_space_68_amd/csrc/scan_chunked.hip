@@ -25,10 +25,11 @@
 //     the carry for the next chunk is lane 63's end state.
 //
 // Data movement (kW waves = kW channels of one batch row per workgroup):
-//   * B and C are shared by all channels of a row and stored [batch][N][L], so a
-//     state's values over a chunk are one contiguous run.  Each step of the
+//   * B and C are shared by all channels of a row and stored [batch][L][N] (the
+//     pages' order), so a token's states are one contiguous run.  Each step of the
 //     kernel covers kNB states of one chunk: the workgroup loads the next step's
-//     B/C tile into registers (coalesced 16- or 8-byte vectors along L) while it
+//     B/C tile into registers (one 16-byte vector of kNB states per token and
+//     matrix; the L2 serves the other steps' states of the same lines) while it
 //     computes on the current one, and at the end of the step writes it, as
 //     float32 and permuted into the order the lanes read it, to the other of two
 //     LDS buffers; one barrier per step publishes it;
@@ -59,8 +60,8 @@ constexpr int kNBGeneric = 4;        // states per step (per staged B/C tile), a
 // load before its value is needed.  NBLK = 0: any N, steps in a runtime loop.
 //
 // ZOH: the full zero-order-hold input term (e^{Delta A} - 1)/A * B * u instead of
-// Delta * B * u: with w = u * B / A it is a*w - w, one FMA and one multiply more per
-// element than the simplified term (1/A is per state, computed once per channel).
+// Delta * B * u: u * B times zoh_factor (about six VALU operations more per element
+// than the simplified term; 1/A is per state, computed once per channel).
 template <typename ACT, bool GATE, int KPL, bool VEC, int NBLK, int kNB, int kW, bool CONV, bool ZOH>
 __global__ __launch_bounds__(64 * kW) void scan_chunked_kernel(ScanArgs p, int n_dblk) {
   constexpr int kThreads = 64 * kW;
@@ -71,7 +72,11 @@ __global__ __launch_bounds__(64 * kW) void scan_chunked_kernel(ScanArgs p, int n
   using raw_t = typename IO::raw_t;
   constexpr int CH = 64 * KPL;
   constexpr int BLK4 = CH / 4;                       // float4 per (state, matrix) block
-  constexpr int TILE4 = kNB * 2 * BLK4;              // float4 per step tile
+  // ROWS (float32, N == 16, vector path, 8 tokens per lane): B and C are staged a
+  // whole chunk at a time, all 16 states of a token together (each B/C line is
+  // fetched once per chunk); otherwise one step's kNB states at a time.
+  constexpr bool ROWS = ACT::kBytes == 4 && VEC && NBLK > 0 && kNB * NBLK == 16 && KPL == 8;
+  constexpr int TILE4 = (ROWS ? 16 : kNB) * 2 * BLK4;  // float4 per LDS buffer
   __shared__ float4 s_tile[2][TILE4];
 
   const int lane = threadIdx.x & 63;
@@ -95,7 +100,8 @@ __global__ __launch_bounds__(64 * kW) void scan_chunked_kernel(ScanArgs p, int n
   // A[d, n] * log2(e) in lane n (read once, so the state loop never issues a
   // vector load of A).
   const float a2_v = lane < N ? p.A[d * N + lane] * kLog2e : 0.0f;
-  // 1/A[d, n] in lane n (full zero-order hold only)
+  // 1/A[d, n] in lane n (full zero-order hold only; inf at A == 0, never selected
+  // there by zoh_factor)
   const float ra_v = (ZOH && lane < N) ? 1.0f / p.A[d * N + lane] : 0.0f;
   // carry of state n lives in lane n; it starts as the initial state (zero if none)
   float carry_v = (lane < N && p.h0) ? p.h0[(b * p.D + d) * N + lane] : 0.0f;
@@ -236,13 +242,12 @@ __global__ __launch_bounds__(64 * kW) void scan_chunked_kernel(ScanArgs p, int n
     }
   };
 
-  // Input term of token j for a state with B value bj and 1/A = ra.
-  auto input_term = [&](float avj, float duj, float bj, float ra) __attribute__((always_inline)) -> float {
+  // Input term of token j for a state with B value bj, decay avj = 2^yj and 1/A = ra.
+  auto input_term = [&](float avj, float yj, int j, float bj, float ra) __attribute__((always_inline)) -> float {
     if constexpr (ZOH) {
-      const float w = (duj * ra) * bj;
-      return __builtin_fmaf(avj, w, -w);
+      return (du[j] * bj) * zoh_factor(yj, avj, ra, dl[j]);
     } else {
-      return duj * bj;
+      return du[j] * bj;
     }
   };
 
@@ -260,8 +265,9 @@ __global__ __launch_bounds__(64 * kW) void scan_chunked_kernel(ScanArgs p, int n
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int j = 4 * q + r;
-        av[j] = exp2_hw(dl[j] * a2);
-        bv[j] = input_term(av[j], du[j], bs[r], ra);
+        const float yj = dl[j] * a2;
+        av[j] = exp2_hw(yj);
+        bv[j] = input_term(av[j], yj, j, bs[r], ra);
         h = __builtin_fmaf(av[j], h, bv[j]);
       }
     }
@@ -301,10 +307,11 @@ __global__ __launch_bounds__(64 * kW) void scan_chunked_kernel(ScanArgs p, int n
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int j = 4 * q + r;
-        av0[j] = exp2_hw(dl[j] * a20);
-        av1[j] = exp2_hw(dl[j] * a21);
-        bv0[j] = input_term(av0[j], du[j], bs0[r], ra0);
-        bv1[j] = input_term(av1[j], du[j], bs1[r], ra1);
+        const float y0 = dl[j] * a20, y1 = dl[j] * a21;
+        av0[j] = exp2_hw(y0);
+        av1[j] = exp2_hw(y1);
+        bv0[j] = input_term(av0[j], y0, j, bs0[r], ra0);
+        bv1[j] = input_term(av1[j], y1, j, bs1[r], ra1);
         h0 = __builtin_fmaf(av0[j], h0, bv0[j]);
         h1 = __builtin_fmaf(av1[j], h1, bv1[j]);
       }
@@ -343,75 +350,116 @@ __global__ __launch_bounds__(64 * kW) void scan_chunked_kernel(ScanArgs p, int n
     carry_v = (lane == n) ? cnew : carry_v;
   };
 
-  // Tile of step k = (chunk c = k / nblk, states n0 = (k % nblk) * kNB ...): for
-  // each of its nn = min(kNB, N - n0) states, B's then C's CH values of the
-  // chunk, which are contiguous in memory.  Float4 f of a block (2 * state +
-  // matrix) holds tokens 4f .. 4f+3; in LDS it goes to the slot lane f / (KPL/4)
-  // reads as its vector f % (KPL/4), so the state loop's LDS reads are
-  // contiguous.  Threads move one 16-byte vector (kTok tokens) each per element:
-  // element e of the tile covers float4 (e % BLKR) * kOut ... of block e / BLKR.
-  // A block is a multiple of 64 elements, so a wave's block (state, matrix) is
-  // wave-uniform and only the token offset is per lane.
+  // Tile of step k = (chunk c = k / nblk, states n0 = (k % nblk) * kNB ...): B and C
+  // are [batch][L][N], so one token's nn = min(kNB, N - n0) states of the step are
+  // contiguous in memory.  A tile element is (matrix m, token tk of the chunk): one
+  // 16-byte vector (4 float32 or 8 bfloat16 states) when N == 16 on the vector path,
+  // else element loads.  Element e = m * CH + tk; a wave's 64 elements share m.
+  // In LDS the tile is float32 blocks (2 * state + matrix) of the chunk's CH tokens:
+  // float4 f of a block holds tokens 4f .. 4f+3 and sits at the slot lane f / (KPL/4)
+  // reads as its vector f % (KPL/4), so the state loop's LDS reads are contiguous.
+  // store_tile scatters each element's states into their blocks.
   //
   // Pipeline: tile j is loaded into register set j % 2 during step j - 2 and
   // written (as float32, permuted) to LDS buffer j % 2 at the end of step j - 1,
   // so each load has a whole step to arrive before its value is needed.
-  using TIO = TileIO<ACT>;
-  using traw_t = typename TIO::raw_t;
-  constexpr int BLKR = BLK4 / TIO::kOut;                     // 16-byte elements per block
-  constexpr int TILER = kNB * 2 * BLKR;                      // elements per tile
+  //
+  // ROWS: tile j is instead piece s of chunk cc, j = cc * NBLK + s + 1 - NBLK: the
+  // PIECE = CH / NBLK tokens from s * PIECE, all 16 states, element e = m * CH +
+  // g * PIECE + tq holding states 4g .. 4g+3 of token tq of the piece (a wave's
+  // elements share m and g, and its loads hit the L1 lines the other groups' waves
+  // fetch).  Piece s of chunk cc is written to LDS buffer cc % 2 at the end of step
+  // (cc - 1) * NBLK + s: after chunk cc - 2 has finished with that buffer, and the
+  // whole chunk is in place by the barrier that ends chunk cc - 1.
+  using SR = StateRun<ACT, kNB>;
+  using traw_t = typename SR::raw_t;
+  constexpr int TILER = 2 * CH;                              // elements per tile
   constexpr int TPT = (TILER + kThreads - 1) / kThreads;     // elements per thread
   static_assert(TPT <= 3, "tile share per thread held in three registers");
-  static_assert(BLKR % 64 == 0, "a tile block spans whole waves");
+  static_assert(CH % 64 == 0, "a wave's tile elements share one matrix");
+  // vector loads of a token's states: N == 16 (compile-time) on the aligned path
+  constexpr bool BCVEC = VEC && NBLK > 0 && kNB * NBLK == 16;
   traw_t tr[2][TPT];
-  int tile_nr[2] = {0, 0};                                   // elements in each staged tile
-  const int64_t bc_row = b * N * L;                          // this batch row of B and C
+  int tile_nn[2] = {0, 0};                                   // states in each staged tile
+  int tile_pc[2] = {0, 0};                                   // ROWS: piece | chunk parity << 8
+  const int64_t bc_row = b * L * N;                          // this batch row of B and C
+  constexpr int PIECE = ROWS ? CH / NBLK : CH;
+  static_assert(!ROWS || PIECE % 64 == 0, "a wave's piece elements share one state group");
+  auto load_rows = [&](int64_t j, int set) __attribute__((always_inline)) {
+    int64_t cc = (j - 1 + NBLK) / NBLK;
+    const int sp = static_cast<int>((j - 1 + NBLK) % NBLK);
+    cc = cc < nchunks ? cc : nchunks - 1;                   // past the last chunk: never stored
+    tile_pc[set] = sp | static_cast<int>((cc & 1) << 8);
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) {
+      int eb = w * 64 + i * kThreads;
+      eb = eb < TILER ? eb : TILER - 64;
+      const void* src = (eb / CH) ? p.Cm : p.Bm;
+      const int g = (eb % CH) / PIECE;
+      int64_t t = cc * CH + sp * PIECE + (eb % PIECE) + lane;
+      t = t < L ? t : L - 1;                                 // padding tokens: identity steps (Delta = 0)
+      tr[set][i] = SR::load_vec(src, bc_row + t * N + 4 * g);
+    }
+  };
+  auto store_rows = [&](int set) __attribute__((always_inline)) {
+    float* dst = reinterpret_cast<float*>(s_tile[tile_pc[set] >> 8]);
+    const int sp = tile_pc[set] & 0xff;
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) {
+      const int eb = w * 64 + i * kThreads;
+      if (eb < TILER) {
+        const int m = eb / CH, g = (eb % CH) / PIECE, tk = sp * PIECE + eb % PIECE + lane, f = tk >> 2;
+        const int slot = ((f % (KPL / 4)) * 64 + f / (KPL / 4)) * 4 + (tk & 3);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dst[(2 * (4 * g + j) + m) * (4 * BLK4) + slot] = SR::get(tr[set][i], j);
+      }
+    }
+  };
   auto load_tile = [&](int64_t k, int set) __attribute__((always_inline)) {
+    if constexpr (ROWS) {
+      load_rows(k, set);
+      return;
+    }
     const int64_t c = k / nblk;
     const int n0 = static_cast<int>(k % nblk) * kNB;
-    const int nr = ((N - n0 < kNB) ? (N - n0) : kNB) * 2 * BLKR;
-    tile_nr[set] = nr;
+    const int nn = NBLK > 0 ? kNB : ((N - n0 < kNB) ? (N - n0) : kNB);
+    tile_nn[set] = nn;
     const int64_t tok0 = c * CH;
 #pragma unroll
     for (int i = 0; i < TPT; ++i) {
       // this wave's first element, clamped into the tile (the surplus is never stored)
       int eb = w * 64 + i * kThreads;
-      eb = eb < nr ? eb : nr - 64;
-      const int blkk = eb / BLKR;
-      const void* src = (blkk & 1) ? p.Cm : p.Bm;
-      const int64_t srow = bc_row + static_cast<int64_t>(n0 + (blkk >> 1)) * L;
-      const int64_t t = tok0 + TIO::kTok * (eb % BLKR + lane);
-      if constexpr (VEC) {
-        // Unconditional load, clamped into the row: a lane past L reloads the
-        // row's last tokens.  Those padding tokens have Delta = 0, so they are
-        // identity steps whatever finite B and C they see, and their y is never
-        // stored.
-        tr[set][i] = TIO::load(src, srow + (t < L ? t : L - TIO::kTok));
+      eb = eb < TILER ? eb : TILER - 64;
+      const void* src = (eb / CH) ? p.Cm : p.Bm;
+      // Unconditional load, clamped into the row: a token past L reloads the row's
+      // last token.  Those padding tokens have Delta = 0, so they are identity steps
+      // whatever finite B and C they see, and their y is never stored.
+      int64_t t = tok0 + (eb % CH) + lane;
+      t = t < L ? t : L - 1;
+      const int64_t off = bc_row + t * N + n0;
+      if constexpr (BCVEC) {
+        tr[set][i] = SR::load_vec(src, off);
       } else {
-        float x[TIO::kTok];
-#pragma unroll
-        for (int r = 0; r < TIO::kTok; ++r) x[r] = t + r < L ? load_act<ACT>(src, srow + t + r) : 0.0f;
-        if constexpr (ACT::kBytes == 4) {
-          tr[set][i] = make_float4(x[0], x[1], x[2], x[3]);
-        } else {
-          tr[set][i] = make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
-                                  pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7]));
-        }
+        tr[set][i] = SR::load_elems(src, off, nn);
       }
     }
   };
   auto store_tile = [&](int set) __attribute__((always_inline)) {
-    float4* dst = s_tile[set];
+    if constexpr (ROWS) {
+      store_rows(set);
+      return;
+    }
+    float* dst = reinterpret_cast<float*>(s_tile[set]);
+    const int nn = tile_nn[set];
 #pragma unroll
     for (int i = 0; i < TPT; ++i) {
       const int eb = w * 64 + i * kThreads;
-      if (eb < tile_nr[set]) {
-        const int blkk = eb / BLKR;
+      if (eb < TILER) {
+        const int m = eb / CH, tk = eb % CH + lane, f = tk >> 2;
+        const int slot = ((f % (KPL / 4)) * 64 + f / (KPL / 4)) * 4 + (tk & 3);
 #pragma unroll
-        for (int j = 0; j < TIO::kOut; ++j) {
-          const int f = (eb % BLKR + lane) * TIO::kOut + j;
-          dst[blkk * BLK4 + (f % (KPL / 4)) * 64 + f / (KPL / 4)] = TIO::out(tr[set][i], j);
-        }
+        for (int j = 0; j < kNB; ++j)
+          if (NBLK > 0 || j < nn) dst[(2 * j + m) * (4 * BLK4) + slot] = SR::get(tr[set][i], j);
       }
     }
   };
@@ -480,16 +528,31 @@ __global__ __launch_bounds__(64 * kW) void scan_chunked_kernel(ScanArgs p, int n
     // (a wave past the last channel skips the state loop; keeping the loop in
     // its own block also keeps the compiler from scheduling it into the
     // surrounding per-token code, which costs registers)
-    if (valid) states(s_tile[par], nb);
+    if (valid) {
+      if constexpr (ROWS)
+        states(s_tile[c & 1] + nb * kNB * 2 * BLK4, nb);
+      else
+        states(s_tile[par], nb);
+    }
     if (!tail1) store_tile(par ^ 1);
     barrier_lds();
   };
 
   prefetch_act(p.u, 0, u_raw);
   prefetch_act(p.delta, 0, d_raw);
-  load_tile(0, 0);
-  if (nsteps > 1) load_tile(1, 1);
-  store_tile(0);
+  if constexpr (ROWS) {
+    // the whole first chunk (tiles 1 - NBLK .. 0), then the next chunk's first piece
+#pragma unroll
+    for (int j = 1 - NBLK; j <= 0; ++j) {
+      load_tile(j, 0);
+      store_tile(0);
+    }
+    load_tile(1, 1);
+  } else {
+    load_tile(0, 0);
+    if (nsteps > 1) load_tile(1, 1);
+    store_tile(0);
+  }
   barrier_lds();
   if constexpr (NBLK > 0) {
     static_assert(NBLK % 2 == 0, "steps are unrolled in pairs");
@@ -503,7 +566,8 @@ __global__ __launch_bounds__(64 * kW) void scan_chunked_kernel(ScanArgs p, int n
     static_for<NBLK>([&](auto nbc) __attribute__((always_inline)) {
       constexpr int nb = decltype(nbc)::value;
       const int64_t k = c * NBLK + nb;
-      step(k, c, nb, nb & 1, true, k + 2 >= nsteps, k + 1 >= nsteps);
+      // (ROWS: the last chunk's steps would stage the chunk after it, which is none)
+      step(k, c, nb, nb & 1, true, ROWS || k + 2 >= nsteps, ROWS || k + 1 >= nsteps);
     });
   } else {
     for (int64_t k = 0; k < nsteps; k += 2) {
@@ -524,11 +588,13 @@ __global__ __launch_bounds__(64 * kW) void scan_chunked_kernel(ScanArgs p, int n
 
 bool aligned16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; }
 
-// Vector path: 16-byte vectors of u, delta, z, y along L, and of B and C (L % 8
-// == 0 keeps every row start 16-byte aligned in both dtypes).
+// Vector path: 16-byte vectors of u, delta, z, y (and the fused conv's u_out) along
+// L (L % 8 == 0 keeps every row start 16-byte aligned in both dtypes), and of a
+// token's states of B and C (N == 16 keeps every token's row 16-byte aligned).
 bool vec_path(const ScanArgs& a, int kpl) {
   return (a.L % 8 == 0) && a.L >= kpl && aligned16(a.u) && aligned16(a.delta) && aligned16(a.y) &&
-         (a.z == nullptr || aligned16(a.z)) && aligned16(a.Bm) && aligned16(a.Cm);
+         (a.z == nullptr || aligned16(a.z)) && (a.u_out == nullptr || aligned16(a.u_out)) && aligned16(a.Bm) &&
+         aligned16(a.Cm);
 }
 
 template <typename ACT, bool GATE, int KPL, int W, bool CONV, bool ZOH>

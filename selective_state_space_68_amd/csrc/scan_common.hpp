@@ -1,7 +1,7 @@
 // Pieces shared by the scan kernels (forward and backward): vector I/O of per-lane
-// runs of KPL consecutive tokens of one channel (TokenIO) and of the 16-byte B/C
-// tile elements (TileIO), with non-temporal accesses for data read or written
-// once; a compile-time loop; an LDS-only workgroup barrier.
+// runs of KPL consecutive tokens of one channel (TokenIO, non-temporal: read or
+// written once) and of runs of consecutive states of one token of B or C
+// (StateRun); a compile-time loop; an LDS-only workgroup barrier.
 #pragma once
 
 #include <utility>
@@ -90,33 +90,63 @@ struct TokenIO<ActBF16, KPL> {
   }
 };
 
-// One B/C tile element: the largest vector load of consecutive tokens of one
-// state (16 bytes): 4 float32 or 8 bfloat16 tokens, converted to kOut float4.
-template <typename ACT>
-struct TileIO;
+// kNB consecutive states of one token of B or C (stored [batch][L][N], so a token's
+// states are contiguous): one 16-byte load when N == 16 and the matrix is 16-byte
+// aligned (4 float32 or 8 bfloat16 states), else element loads of the first `nn`
+// states (the rest read as 0).  get(r, j) is state j as float32.
+template <typename ACT, int kNB>
+struct StateRun;
 
 template <>
-struct TileIO<ActF32> {
-  static constexpr int kTok = 4;
-  static constexpr int kOut = 1;
+struct StateRun<ActF32, 4> {
   using raw_t = float4;
-  static __device__ __forceinline__ raw_t load(const void* base, int64_t off) {
+  static __device__ __forceinline__ raw_t load_vec(const void* base, int64_t off) {
     return *reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
   }
-  static __device__ __forceinline__ float4 out(const raw_t& r, int) { return r; }
+  static __device__ __forceinline__ raw_t load_elems(const void* base, int64_t off, int nn) {
+    const float* q = static_cast<const float*>(base) + off;
+    return make_float4(q[0], nn > 1 ? q[1] : 0.0f, nn > 2 ? q[2] : 0.0f, nn > 3 ? q[3] : 0.0f);
+  }
+  static __device__ __forceinline__ float get(const raw_t& r, int j) {
+    return j == 0 ? r.x : (j == 1 ? r.y : (j == 2 ? r.z : r.w));
+  }
 };
 
 template <>
-struct TileIO<ActBF16> {
-  static constexpr int kTok = 8;
-  static constexpr int kOut = 2;
+struct StateRun<ActBF16, 8> {
   using raw_t = uint4;
-  static __device__ __forceinline__ raw_t load(const void* base, int64_t off) {
+  static __device__ __forceinline__ raw_t load_vec(const void* base, int64_t off) {
     return *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off);
   }
-  static __device__ __forceinline__ float4 out(const raw_t& r, int j) {
-    const unsigned a = j == 0 ? r.x : r.z, b = j == 0 ? r.y : r.w;
-    return make_float4(bf16_lo(a), bf16_hi(a), bf16_lo(b), bf16_hi(b));
+  static __device__ __forceinline__ raw_t load_elems(const void* base, int64_t off, int nn) {
+    const uint16_t* q = static_cast<const uint16_t*>(base) + off;
+    uint32_t v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = j < nn ? q[j] : 0u;
+    return make_uint4(v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16));
+  }
+  static __device__ __forceinline__ float get(const raw_t& r, int j) {
+    const uint32_t w = (j >> 1) == 0 ? r.x : ((j >> 1) == 1 ? r.y : ((j >> 1) == 2 ? r.z : r.w));
+    return (j & 1) ? bf16_hi(w) : bf16_lo(w);
+  }
+};
+
+template <>
+struct StateRun<ActBF16, 4> {
+  using raw_t = uint2;
+  static __device__ __forceinline__ raw_t load_vec(const void* base, int64_t off) {
+    return *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + off);
+  }
+  static __device__ __forceinline__ raw_t load_elems(const void* base, int64_t off, int nn) {
+    const uint16_t* q = static_cast<const uint16_t*>(base) + off;
+    uint32_t v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = j < nn ? q[j] : 0u;
+    return make_uint2(v[0] | (v[1] << 16), v[2] | (v[3] << 16));
+  }
+  static __device__ __forceinline__ float get(const raw_t& r, int j) {
+    const uint32_t w = (j >> 1) == 0 ? r.x : r.y;
+    return (j & 1) ? bf16_hi(w) : bf16_lo(w);
   }
 };
 

@@ -16,8 +16,9 @@
 //     (token, channel): each lane does it for one 8-token piece of its channel in
 //     a block of 8 * 16 / SPL tokens and leaves (Delta, Delta * u) in LDS, and the
 //     readout of its piece's tokens ends up in the same lane for the output;
-//   * B and C of the block are staged in LDS as float32 [token][state], so a lane
-//     reads its SPL states of one token as one vector.
+//   * B and C ([batch][L][N], so a block's B is one contiguous run of T * 16
+//     values) are staged in LDS as float32 [token][state], so a lane reads its
+//     SPL states of one token as one vector.
 //
 // Every wave uses its own LDS slice and never waits for another: a workgroup is
 // kTsWaves independent waves.  Loads of the next block are issued when the current
@@ -34,8 +35,8 @@ namespace {
 constexpr int kTsWaves = 4;          // independent waves per workgroup
 constexpr int kTsN = 16;             // states per channel the kernel is built for
 
-// Eight consecutive B or C values of one state (a 16- or 32-byte load, cached:
-// every channel group of the batch row reads the same tile).
+// Eight consecutive B or C values: states 8h .. 8h+7 of one token (a 16- or 32-byte
+// load, cached: every channel group of the batch row reads the same tile).
 template <typename ACT>
 struct Piece8;
 template <>
@@ -98,9 +99,9 @@ struct ActIO8<ActBF16> {
   }
 };
 
-// ZOH: the full zero-order-hold input term (e^{Delta A} - 1)/A * B * u = a w - w with
-// w = u (1/A) B (a = e^{Delta A}): the lanes keep (Delta, u) instead of
-// (Delta, Delta u) in LDS, and 1/A per state.
+// ZOH: the full zero-order-hold input term (e^{Delta A} - 1)/A * B * u = u B times
+// zoh_factor: the lanes keep (Delta, u) instead of (Delta, Delta u) in LDS, and 1/A
+// per state.
 //
 // CONV: the scan input is u = SiLU(causal conv1d(x)) with the taps of p.conv_w,
 // computed in the per-token work: a lane's piece needs the 3 inputs before it, from
@@ -145,7 +146,7 @@ __global__ __launch_bounds__(64 * kTsWaves) void scan_tokseq_kernel(ScanArgs p) 
   for (int j = 0; j < SPL; ++j) {
     const int64_t sidx = d * kTsN + SPL * q + j;
     a2[j] = p.A[sidx] * kLog2e;
-    ra[j] = ZOH ? 1.0f / p.A[sidx] : 0.0f;
+    ra[j] = ZOH ? 1.0f / p.A[sidx] : 0.0f;   // (inf at A == 0, never selected there by zoh_factor)
     h[j] = p.h0 ? p.h0[(b * D + d) * kTsN + SPL * q + j] : 0.0f;
   }
   static_assert(!CONV || SPL == 4, "the fused conv is built for 4 states per lane");
@@ -156,14 +157,15 @@ __global__ __launch_bounds__(64 * kTsWaves) void scan_tokseq_kernel(ScanArgs p) 
     for (int k = 0; k < 4; ++k) cw4[k] = (k >= 4 - p.conv_k) ? p.conv_w[d * p.conv_k + k - (4 - p.conv_k)] : 0.0f;
     cbias = p.conv_b ? p.conv_b[d] : 0.0f;
   }
-  const int64_t bc_row = b * kTsN * L;               // B, C rows of this batch row ([N][L])
+  const int64_t bc_row = b * L * kTsN;               // B, C of this batch row ([L][N])
   float* du_w = s_du[w];
   float* bc_w = reinterpret_cast<float*>(s_bc[w]);
 
   // Block inputs in registers: this lane's piece (tokens 8q .. 8q+7 of the block) of
-  // u, delta and z, and its BCP pieces of B and C (piece v = lane + 64k: state
-  // v / QL, tokens 8 (v % QL) ..).  Pieces past L (L % 8 == 0: a piece is all in or
-  // all out) reload the row's last piece; their Delta is set to 0.
+  // u, delta and z, and its BCP pieces of B and C (piece v = lane + 64k: token v / 2
+  // of the block, states 8 (v % 2) ..).  Pieces past L (L % 8 == 0: an activation
+  // piece is all in or all out) reload the row's last piece or token; their Delta
+  // is set to 0.
   raw_t u_raw[IO::kVec], d_raw[IO::kVec], z_raw[IO::kVec];
   Piece8<ACT> bp[BCP], cp[BCP];
   auto fetch = [&](int64_t t0) __attribute__((always_inline)) {
@@ -174,11 +176,11 @@ __global__ __launch_bounds__(64 * kTsWaves) void scan_tokseq_kernel(ScanArgs p) 
     if constexpr (GATE) IO::load_raw(p.z, row + tp, z_raw);
 #pragma unroll
     for (int k = 0; k < BCP; ++k) {
-      const int v = lane + 64 * k, n = v / QL, pc = v % QL;
-      int64_t t = t0 + 8 * pc;
-      t = t + 8 <= L ? t : L - 8;
-      bp[k].load(p.Bm, bc_row + n * L + t);
-      cp[k].load(p.Cm, bc_row + n * L + t);
+      const int v = lane + 64 * k;
+      int64_t t = t0 + v / 2;
+      t = t < L ? t : L - 1;
+      bp[k].load(p.Bm, bc_row + t * kTsN + 8 * (v % 2));
+      cp[k].load(p.Cm, bc_row + t * kTsN + 8 * (v % 2));
     }
   };
 
@@ -232,13 +234,16 @@ __global__ __launch_bounds__(64 * kTsWaves) void scan_tokseq_kernel(ScanArgs p) 
                    : make_float4(dl[2 * k], dl[2 * k] * uv[2 * k], dl[2 * k + 1], dl[2 * k + 1] * uv[2 * k + 1]);
 #pragma unroll
     for (int k = 0; k < BCP; ++k) {
-      const int v = lane + 64 * k, n = v / QL, pc = v % QL;
-      const int col = 4 * ((n >> 2) ^ (pc & 3)) + (n & 3);
+      // token t of the block, state groups 2h and 2h + 1, each at its swizzled slot
+      const int v = lane + 64 * k, t = v / 2, h2 = 2 * (v % 2), sw = (t / 8) & 3;
+      float4* brow = reinterpret_cast<float4*>(bc_w + (0 * T + t) * kTsN);
+      float4* crow = reinterpret_cast<float4*>(bc_w + (1 * T + t) * kTsN);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int t = 8 * pc + e;
-        bc_w[(0 * T + t) * kTsN + col] = bp[k].get(e);
-        bc_w[(1 * T + t) * kTsN + col] = cp[k].get(e);
+      for (int g = 0; g < 2; ++g) {
+        brow[(h2 + g) ^ sw] = make_float4(bp[k].get(4 * g), bp[k].get(4 * g + 1), bp[k].get(4 * g + 2),
+                                          bp[k].get(4 * g + 3));
+        crow[(h2 + g) ^ sw] = make_float4(cp[k].get(4 * g), cp[k].get(4 * g + 1), cp[k].get(4 * g + 2),
+                                          cp[k].get(4 * g + 3));
       }
     }
     // the wave's own LDS writes before its reads (one wave's LDS operations are
@@ -279,11 +284,11 @@ __global__ __launch_bounds__(64 * kTsWaves) void scan_tokseq_kernel(ScanArgs p) 
         float r = 0.0f;
 #pragma unroll
         for (int j = 0; j < SPL; ++j) {
-          const float a = exp2_hw(dd.x * a2[j]);
+          const float yj = dd.x * a2[j];
+          const float a = exp2_hw(yj);
           float term;
           if constexpr (ZOH) {
-            const float wz = (dd.y * ra[j]) * bs[j];
-            term = __builtin_fmaf(a, wz, -wz);
+            term = (dd.y * bs[j]) * zoh_factor(yj, a, ra[j], dd.x);
           } else {
             term = dd.y * bs[j];
           }

@@ -11,7 +11,7 @@
 
 namespace {
 
-constexpr int kVersion = 20600;  // 2.6.0: + token-sequential scan kernel (SSM_SCAN_TOKSEQ)
+constexpr int kVersion = 30000;  // 3.0.0: B and C in [batch][L][N]; forward scan workspace arguments
 
 struct Span {
   uintptr_t lo = 0, hi = 0;  // [lo, hi); empty when lo == hi
@@ -192,13 +192,41 @@ int choose_scan_kernel(const ssm::ScanArgs& a, ssm::Dt d, int variant, int token
   return chunked ? SSM_SCAN_CHUNKED : SSM_SCAN_SEQUENTIAL;
 }
 
+// The caller's workspace for a forward scan: NULL with a zero size, or a 16-byte
+// aligned buffer of at least `need` bytes that overlaps no other argument.
+ssm_status check_scan_workspace(const void* workspace, size_t workspace_bytes, size_t need, const void* u,
+                                const void* delta, const float* A, const void* Bm, const void* Cm, const float* Dskip,
+                                const void* z, const float* delta_bias, const float* initial_state, const void* y,
+                                const float* final_state, const ScanSizes& sz) {
+  if (workspace_bytes && !workspace) return SSM_ERR_INVALID_ARG;
+  if (workspace_bytes < need || !aligned(workspace, 16)) return SSM_ERR_INVALID_ARG;
+  const Span ws = span(workspace, workspace_bytes);
+  const Span all[] = {span(u, sz.act_bytes),           span(delta, sz.act_bytes),     span(z, sz.act_bytes),
+                      span(A, sz.a_bytes),             span(Bm, sz.bc_bytes),         span(Cm, sz.bc_bytes),
+                      span(Dskip, sz.vec_bytes),       span(delta_bias, sz.vec_bytes),
+                      span(initial_state, sz.state_bytes), span(y, sz.act_bytes),
+                      span(final_state, sz.state_bytes)};
+  for (const Span& o : all)
+    if (overlaps(ws, o)) return SSM_ERR_INVALID_ARG;
+  return SSM_OK;
+}
+
+// Workspace bytes a forward scan of this shape uses: none.  The kernels need no
+// device memory beyond their arguments; a wave walks all of L for its channel, so
+// no carry crosses workgroups through memory.
+size_t scan_workspace_need(int64_t, int64_t, int64_t, int64_t, ssm_dtype) { return 0; }
+
 ssm_status scan_fwd(const void* u, const void* delta, const float* A, const void* Bm, const void* Cm,
                     const float* Dskip, const void* z, const float* delta_bias, int delta_softplus,
                     const float* initial_state, void* y, float* final_state, int64_t batch, int64_t L, int64_t D,
-                    int64_t N, ssm_dtype dt, void* stream, int variant, int tokens_per_lane, int zoh) {
+                    int64_t N, ssm_dtype dt, void* workspace, size_t workspace_bytes, void* stream, int variant,
+                    int tokens_per_lane, int zoh) {
   ScanSizes sz;
   ssm_status st = check_scan(u, delta, A, Bm, Cm, Dskip, z, delta_bias, delta_softplus, initial_state, y,
                              final_state, batch, L, D, N, dt, &sz);
+  if (st != SSM_OK) return st;
+  st = check_scan_workspace(workspace, workspace_bytes, scan_workspace_need(batch, L, D, N, dt), u, delta, A, Bm, Cm,
+                            Dskip, z, delta_bias, initial_state, y, final_state, sz);
   if (st != SSM_OK) return st;
   if (variant != SSM_SCAN_AUTO && variant != SSM_SCAN_SEQUENTIAL && variant != SSM_SCAN_CHUNKED &&
       variant != SSM_SCAN_TOKSEQ)
@@ -227,14 +255,21 @@ ssm_status scan_fwd(const void* u, const void* delta, const float* A, const void
 
 extern "C" {
 
+size_t ssm_selective_scan_workspace_size(int64_t batch, int64_t L, int64_t D, int64_t N, ssm_dtype dt) {
+  if (dt != SSM_F32 && dt != SSM_BF16) return 0;
+  if (batch <= 0 || L <= 0 || D <= 0 || N < 1 || N > SSM_MAX_N) return 0;
+  return scan_workspace_need(batch, L, D, N, dt);
+}
+
 ssm_status ssm_selective_scan_fwd_variant(const void* u, const void* delta, const float* A, const void* Bm,
                                           const void* Cm, const float* Dskip, const void* z,
                                           const float* delta_bias, int delta_softplus,
                                           const float* initial_state, void* y, float* final_state,
                                           int64_t batch, int64_t L, int64_t D, int64_t N, ssm_dtype dt,
-                                          void* stream, int variant, int tokens_per_lane) {
+                                          void* workspace, size_t workspace_bytes, void* stream, int variant,
+                                          int tokens_per_lane) {
   return scan_fwd(u, delta, A, Bm, Cm, Dskip, z, delta_bias, delta_softplus, initial_state, y, final_state, batch, L,
-                  D, N, dt, stream, variant, tokens_per_lane, 0);
+                  D, N, dt, workspace, workspace_bytes, stream, variant, tokens_per_lane, 0);
 }
 
 int ssm_selective_scan_fwd_kernel(int64_t batch, int64_t L, int64_t D, int64_t N, ssm_dtype dt, int gate, int zoh,
@@ -263,15 +298,16 @@ ssm_status ssm_selective_scan_fwd_zoh(const void* u, const void* delta, const fl
                                       int delta_softplus, const float* initial_state, void* y, float* final_state,
                                       int64_t batch, int64_t L, int64_t D, int64_t N, ssm_dtype dt, void* stream) {
   return scan_fwd(u, delta, A, Bm, Cm, Dskip, z, delta_bias, delta_softplus, initial_state, y, final_state, batch, L,
-                  D, N, dt, stream, SSM_SCAN_AUTO, 0, 1);
+                  D, N, dt, nullptr, 0, stream, SSM_SCAN_AUTO, 0, 1);
 }
 
 ssm_status ssm_selective_scan_fwd(const void* u, const void* delta, const float* A, const void* Bm,
                                   const void* Cm, const float* Dskip, const void* z, const float* delta_bias,
                                   int delta_softplus, void* y, float* final_state, int64_t batch, int64_t L,
-                                  int64_t D, int64_t N, ssm_dtype dt, void* stream) {
-  return ssm_selective_scan_fwd_variant(u, delta, A, Bm, Cm, Dskip, z, delta_bias, delta_softplus, nullptr, y,
-                                        final_state, batch, L, D, N, dt, stream, SSM_SCAN_AUTO, 0);
+                                  int64_t D, int64_t N, ssm_dtype dt, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  return scan_fwd(u, delta, A, Bm, Cm, Dskip, z, delta_bias, delta_softplus, nullptr, y, final_state, batch, L, D, N,
+                  dt, workspace, workspace_bytes, stream, SSM_SCAN_AUTO, 0, 0);
 }
 
 ssm_status ssm_selective_scan_fwd_from_state(const void* u, const void* delta, const float* A, const void* Bm,
@@ -279,10 +315,9 @@ ssm_status ssm_selective_scan_fwd_from_state(const void* u, const void* delta, c
                                              const float* delta_bias, int delta_softplus,
                                              const float* initial_state, void* y, float* final_state,
                                              int64_t batch, int64_t L, int64_t D, int64_t N, ssm_dtype dt,
-                                             void* stream) {
-  return ssm_selective_scan_fwd_variant(u, delta, A, Bm, Cm, Dskip, z, delta_bias, delta_softplus,
-                                        initial_state, y, final_state, batch, L, D, N, dt, stream,
-                                        SSM_SCAN_AUTO, 0);
+                                             void* workspace, size_t workspace_bytes, void* stream) {
+  return scan_fwd(u, delta, A, Bm, Cm, Dskip, z, delta_bias, delta_softplus, initial_state, y, final_state, batch, L,
+                  D, N, dt, workspace, workspace_bytes, stream, SSM_SCAN_AUTO, 0, 0);
 }
 
 ssm_status ssm_selective_scan_fwd_conv(const void* x, const float* conv_w, const float* conv_b, int64_t conv_width,

@@ -41,12 +41,10 @@ __device__ __forceinline__ void store_state4(float* p, float4 h) {
 // one channel's state; CPT channels per lane group, so a lane keeps CPT
 // independent 16-byte state loads in flight (wave instruction k of a wave covers
 // 64 / LPC consecutive channels, 1 KB of contiguous state).
-// Full zero-order-hold input terms (e^{Delta A} - 1)/A * B * u of four states, from
-// their decays a = e^{Delta A}.
-__device__ __forceinline__ float4 zoh_terms(float u, float4 b, float4 A, float ax, float ay, float az, float aw) {
-  const float wx = (u / A.x) * b.x, wy = (u / A.y) * b.y, wz = (u / A.z) * b.z, ww = (u / A.w) * b.w;
-  return make_float4(__builtin_fmaf(ax, wx, -wx), __builtin_fmaf(ay, wy, -wy), __builtin_fmaf(az, wz, -wz),
-                     __builtin_fmaf(aw, ww, -ww));
+// Full zero-order-hold input term (e^{Delta A} - 1)/A * B * u of one state from its
+// exp2 argument y = Delta A log2(e) and decay a = 2^y (zoh_factor; Delta * B * u at A == 0).
+__device__ __forceinline__ float zoh_term(float u, float dl, float b, float A, float y, float a) {
+  return (u * b) * zoh_factor(y, a, 1.0f / A, dl);
 }
 
 template <typename ACT, bool GATE, int LPC, int CPT>
@@ -90,10 +88,13 @@ __global__ __launch_bounds__(256) void state_update_vec_kernel(StepArgs p) {
     float dlk = dl[k];
     if (p.softplus) dlk = softplus_f(dlk);
     const float du = dlk * u[k];
-    const float ax = exp2_hw(dlk * (a4[k].x * kLog2e)), ay = exp2_hw(dlk * (a4[k].y * kLog2e));
-    const float az = exp2_hw(dlk * (a4[k].z * kLog2e)), aw = exp2_hw(dlk * (a4[k].w * kLog2e));
+    const float yx = dlk * (a4[k].x * kLog2e), yy = dlk * (a4[k].y * kLog2e);
+    const float yz = dlk * (a4[k].z * kLog2e), yw = dlk * (a4[k].w * kLog2e);
+    const float ax = exp2_hw(yx), ay = exp2_hw(yy), az = exp2_hw(yz), aw = exp2_hw(yw);
     float4 in = make_float4(du * b4[k].x, du * b4[k].y, du * b4[k].z, du * b4[k].w);
-    if (p.zoh) in = zoh_terms(u[k], b4[k], a4[k], ax, ay, az, aw);
+    if (p.zoh)
+      in = make_float4(zoh_term(u[k], dlk, b4[k].x, a4[k].x, yx, ax), zoh_term(u[k], dlk, b4[k].y, a4[k].y, yy, ay),
+                       zoh_term(u[k], dlk, b4[k].z, a4[k].z, yz, az), zoh_term(u[k], dlk, b4[k].w, a4[k].w, yw, aw));
     float4 h;
     h.x = __builtin_fmaf(ax, h0[k].x, in.x);
     h.y = __builtin_fmaf(ay, h0[k].y, in.y);
@@ -132,13 +133,11 @@ __global__ __launch_bounds__(256) void state_update_generic_kernel(StepArgs p) {
   float y = 0.0f;
   for (int n = 0; n < N; ++n) {
     const float An = p.A[d * N + n];
-    const float a = exp2_hw(dl * (An * kLog2e));
+    const float yn = dl * (An * kLog2e);
+    const float a = exp2_hw(yn);
     const float bn = load_act<ACT>(p.Bm, s * N + n);
     float in = du * bn;
-    if (p.zoh) {
-      const float w = (u / An) * bn;                 // (e^{Delta A} - 1)/A * B * u
-      in = __builtin_fmaf(a, w, -w);
-    }
+    if (p.zoh) in = zoh_term(u, dl, bn, An, yn, a);  // (e^{Delta A} - 1)/A * B * u
     const float h = __builtin_fmaf(a, p.state_in[ch * N + n], in);
     p.state_out[ch * N + n] = h;
     y = __builtin_fmaf(load_act<ACT>(p.Cm, s * N + n), h, y);

@@ -3,7 +3,11 @@
 Torch is used for device memory and streams only; the arithmetic happens in
 libssm.so.  Activations (u, delta, z, B, C and the outputs y) are float32 or
 bfloat16 CUDA/HIP tensors of one dtype; A, D, delta_bias and states are float32.
-Layouts: u, delta, z [batch, D, L]; B, C [batch, N, L]; A [D, N]; D, bias [D].
+Layouts: u, delta, z [batch, D, L]; B, C [batch, L, N]; A [D, N]; D, bias [D].
+
+Every wrapper checks the shape of every tensor it is given, outputs included,
+before it takes a single pointer: the library sees only pointers and sizes, so a
+tensor smaller than its shape says would otherwise be read or written past its end.
 """
 from __future__ import annotations
 
@@ -20,6 +24,16 @@ def _dt(t: torch.Tensor) -> int:
     if t.dtype == torch.bfloat16:
         return _lib.SSM_BF16
     raise TypeError(f"activations must be float32 or bfloat16, got {t.dtype}")
+
+
+def _shape(t, name: str, shape) -> None:
+    """Raise ValueError unless `t` (a tensor, or None for an absent optional) has `shape`."""
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if tuple(t.shape) != tuple(int(s) for s in shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
 
 
 def _ptr(t: Optional[torch.Tensor], name: str, dtype=None, device=None):
@@ -44,37 +58,69 @@ def _stream(stream) -> int:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _workspace(workspace, need: int, dev):
+    """(pointer, bytes) of a caller's workspace tensor, or of one allocated here."""
+    if workspace is None:
+        if need == 0:
+            return None, 0
+        workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
+    if not isinstance(workspace, torch.Tensor) or not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    nbytes = workspace.numel() * workspace.element_size()
+    if nbytes < need:
+        raise ValueError(f"workspace holds {nbytes} bytes, {need} needed")
+    return workspace.data_ptr(), nbytes
+
+
+def _scan_shapes(u, delta, A, B, C, D, z, delta_bias, initial_state, y, final_state):
+    """Shapes of a forward scan's tensors; returns (batch, D, L, N)."""
+    if not isinstance(u, torch.Tensor) or not isinstance(A, torch.Tensor) or u.dim() != 3 or A.dim() != 2:
+        raise ValueError("expected u [batch, D, L] and A [D, N]")
+    batch, Dc, L = u.shape
+    N = A.shape[1]
+    _shape(delta, "delta", (batch, Dc, L))
+    _shape(A, "A", (Dc, N))
+    _shape(B, "B", (batch, L, N))
+    _shape(C, "C", (batch, L, N))
+    _shape(z, "z", (batch, Dc, L))
+    _shape(D, "D", (Dc,))
+    _shape(delta_bias, "delta_bias", (Dc,))
+    _shape(initial_state, "initial_state", (batch, Dc, N))
+    _shape(y, "y", (batch, Dc, L))
+    _shape(final_state, "final_state", (batch, Dc, N))
+    return batch, Dc, L, N
+
+
+def selective_scan_workspace_size(batch, L, D, N, dtype=torch.float32) -> int:
+    """Bytes of device workspace the forward scan needs for this shape (0: none)."""
+    lib = _lib.load_library()
+    dt = _lib.SSM_BF16 if dtype == torch.bfloat16 else _lib.SSM_F32
+    return int(lib.ssm_selective_scan_workspace_size(int(batch), int(L), int(D), int(N), dt))
+
+
 def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True, *,
                        initial_state=None, y=None, final_state=None, return_final_state=True, variant=0,
-                       tokens_per_lane=0, discretization="simplified",
+                       tokens_per_lane=0, discretization="simplified", workspace=None,
                        stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Selective scan forward.  Returns (y [batch, D, L], final_state [batch, D, N] or None).
 
     `initial_state` [batch, D, N] float32 starts the scan from a given state (zero
     when None); `final_state` may be the same tensor (updated in place).
     `discretization`: "simplified" (input term Delta*B*u) or "zoh" (the full
-    zero-order hold, (exp(Delta*A) - 1)/A * B * u; every A must be nonzero).
+    zero-order hold, (exp(Delta*A) - 1)/A * B * u, Delta*B*u where A == 0).
+    `workspace`: a device tensor of at least selective_scan_workspace_size(...)
+    bytes, or None (allocated here when the size is nonzero).
     """
     if discretization not in ("simplified", "zoh"):
         raise ValueError(f"unknown discretization {discretization!r}")
     lib = _lib.load_library()
-    if u.dim() != 3 or B.dim() != 3 or A.dim() != 2:
-        raise ValueError("expected u [batch, D, L], B/C [batch, N, L], A [D, N]")
-    batch, Dc, L = u.shape
-    N = A.shape[1]
+    batch, Dc, L, N = _scan_shapes(u, delta, A, B, C, D, z, delta_bias, initial_state, y, final_state)
     act = u.dtype
     dev = u.device
-    if tuple(delta.shape) != (batch, Dc, L) or tuple(A.shape) != (Dc, N):
-        raise ValueError("delta / A shape mismatch")
-    if tuple(B.shape) != (batch, N, L) or tuple(C.shape) != (batch, N, L):
-        raise ValueError("B / C must be [batch, N, L]")
-    if z is not None and tuple(z.shape) != (batch, Dc, L):
-        raise ValueError("z must be [batch, D, L]")
-    for name, v in (("D", D), ("delta_bias", delta_bias)):
-        if v is not None and tuple(v.shape) != (Dc,):
-            raise ValueError(f"{name} must be [D]")
-    if initial_state is not None and tuple(initial_state.shape) != (batch, Dc, N):
-        raise ValueError("initial_state must be [batch, D, N]")
+    if discretization == "zoh" and (variant or tokens_per_lane or workspace is not None):
+        raise ValueError("the zoh scan runs the default kernel (variant=0, tokens_per_lane=0, no workspace)")
+    if discretization != "zoh":
+        ws_ptr, ws_bytes = _workspace(workspace, selective_scan_workspace_size(batch, L, Dc, N, act), dev)
     if y is None:
         y = torch.empty((batch, Dc, L), dtype=act, device=dev)
     if final_state is None and return_final_state:
@@ -84,13 +130,12 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta
             _ptr(z, "z", act, dev), _ptr(delta_bias, "delta_bias", torch.float32, dev),
             1 if delta_softplus else 0, _ptr(initial_state, "initial_state", torch.float32, dev),
             _ptr(y, "y", act, dev), _ptr(final_state, "final_state", torch.float32, dev),
-            batch, L, Dc, N, _dt(u), _stream(stream))
+            batch, L, Dc, N, _dt(u))
     if discretization == "zoh":
-        if variant or tokens_per_lane:
-            raise ValueError("the zoh scan runs the default kernel (variant=0, tokens_per_lane=0)")
-        st = lib.ssm_selective_scan_fwd_zoh(*args)
+        st = lib.ssm_selective_scan_fwd_zoh(*args, _stream(stream))
     else:
-        st = lib.ssm_selective_scan_fwd_variant(*args, int(variant), int(tokens_per_lane))
+        st = lib.ssm_selective_scan_fwd_variant(*args, ws_ptr, ws_bytes, _stream(stream), int(variant),
+                                                int(tokens_per_lane))
     _lib.check(st)
     return y, final_state
 
@@ -127,36 +172,21 @@ def selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, d
     """Backward pass of selective_scan_fwd (same inputs) for the output gradient dy
     [batch, D, L] and optionally the final-state gradient dfinal_state [batch, D, N].
 
-    Returns a dict with du, ddelta (w.r.t. the raw delta), dA, dB, dC and, where
-    computed, dD, dz, ddelta_bias and dinitial_state (None otherwise).  dD,
-    ddelta_bias and dinitial_state are computed when the matching input is given,
-    unless the want_* flag says otherwise; dz whenever z is given.  `workspace` is a
-    device tensor of at least selective_scan_bwd_workspace_size(...) bytes, or None
-    to allocate one.  `out` may hold preallocated output tensors under the same keys
-    (missing keys are allocated).
+    Returns a dict with du, ddelta (w.r.t. the raw delta), dA, dB, dC ([batch, L, N],
+    the layout of B and C) and, where computed, dD, dz, ddelta_bias and
+    dinitial_state (None otherwise).  dD, ddelta_bias and dinitial_state are computed
+    when the matching input is given, unless the want_* flag says otherwise; dz
+    whenever z is given.  `workspace` is a device tensor of at least
+    selective_scan_bwd_workspace_size(...) bytes, or None to allocate one.  `out`
+    may hold preallocated output tensors under the same keys (missing keys are
+    allocated).
     """
     lib = _lib.load_library()
-    if u.dim() != 3 or B.dim() != 3 or A.dim() != 2:
-        raise ValueError("expected u [batch, D, L], B/C [batch, N, L], A [D, N]")
-    batch, Dc, L = u.shape
-    N = A.shape[1]
+    batch, Dc, L, N = _scan_shapes(u, delta, A, B, C, D, z, delta_bias, initial_state, None, None)
+    _shape(dy, "dy", (batch, Dc, L))
+    _shape(dfinal_state, "dfinal_state", (batch, Dc, N))
     act = u.dtype
     dev = u.device
-    for name, v in (("delta", delta), ("dy", dy)):
-        if tuple(v.shape) != (batch, Dc, L):
-            raise ValueError(f"{name} must be [batch, D, L]")
-    if tuple(A.shape) != (Dc, N):
-        raise ValueError("A must be [D, N]")
-    if tuple(B.shape) != (batch, N, L) or tuple(C.shape) != (batch, N, L):
-        raise ValueError("B / C must be [batch, N, L]")
-    if z is not None and tuple(z.shape) != (batch, Dc, L):
-        raise ValueError("z must be [batch, D, L]")
-    for name, v in (("D", D), ("delta_bias", delta_bias)):
-        if v is not None and tuple(v.shape) != (Dc,):
-            raise ValueError(f"{name} must be [D]")
-    for name, v in (("initial_state", initial_state), ("dfinal_state", dfinal_state)):
-        if v is not None and tuple(v.shape) != (batch, Dc, N):
-            raise ValueError(f"{name} must be [batch, D, N]")
     want_dD = D is not None if want_dD is None else want_dD
     want_db = delta_bias is not None if want_ddelta_bias is None else want_ddelta_bias
     want_dh0 = initial_state is not None if want_dinitial_state is None else want_dinitial_state
@@ -165,8 +195,8 @@ def selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, d
         "du": ((batch, Dc, L), act, True),
         "ddelta": ((batch, Dc, L), act, True),
         "dA": ((Dc, N), f32, True),
-        "dB": ((batch, N, L), act, True),
-        "dC": ((batch, N, L), act, True),
+        "dB": ((batch, L, N), act, True),
+        "dC": ((batch, L, N), act, True),
         "dD": ((Dc,), f32, want_dD),
         "dz": ((batch, Dc, L), act, z is not None),
         "ddelta_bias": ((Dc,), f32, want_db),
@@ -177,17 +207,16 @@ def selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, d
     for k, (shape, dt_, computed) in spec.items():
         t = given.get(k)
         if t is not None and computed:
-            if tuple(t.shape) != shape or t.dtype != dt_:
-                raise ValueError(f"out[{k!r}] must be {dt_} of shape {shape}")
+            _shape(t, f"out[{k!r}]", shape)
+            if t.dtype != dt_:
+                raise TypeError(f"out[{k!r}] must be {dt_}")
             out[k] = t
         else:
             out[k] = torch.empty(shape, dtype=dt_, device=dev) if computed else None
     need = int(lib.ssm_selective_scan_bwd_workspace_size(batch, L, Dc, N, _dt(u)))
     if workspace is None:
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
-    if not workspace.is_cuda or not workspace.is_contiguous():
-        raise ValueError("workspace must be a contiguous GPU tensor")
-    ws_bytes = workspace.numel() * workspace.element_size()
+    ws_ptr, ws_bytes = _workspace(workspace, need, dev)
     st = lib.ssm_selective_scan_bwd(
         _ptr(u, "u", act, dev), _ptr(delta, "delta", act, dev), _ptr(A, "A", f32, dev),
         _ptr(B, "B", act, dev), _ptr(C, "C", act, dev), _ptr(D, "D", f32, dev),
@@ -197,7 +226,7 @@ def selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, d
         _ptr(out["du"], "du"), _ptr(out["ddelta"], "ddelta"), _ptr(out["dA"], "dA"), _ptr(out["dB"], "dB"),
         _ptr(out["dC"], "dC"), _ptr(out["dD"], "dD"), _ptr(out["dz"], "dz"),
         _ptr(out["ddelta_bias"], "ddelta_bias"), _ptr(out["dinitial_state"], "dinitial_state"),
-        batch, L, Dc, N, _dt(u), workspace.data_ptr(), ws_bytes, _stream(stream))
+        batch, L, Dc, N, _dt(u), ws_ptr, ws_bytes, _stream(stream))
     _lib.check(st)
     return out
 
@@ -216,30 +245,33 @@ def ssd_scan_fwd(x, dt, A, B, C, D=None, dt_bias=None, dt_softplus=True, *, init
     least ssd_scan_workspace_size(...) bytes, None (one segment per sequence), or
     "auto" (allocated here)."""
     lib = _lib.load_library()
-    if x.dim() != 4 or B.dim() != 3:
+    if not isinstance(x, torch.Tensor) or not isinstance(B, torch.Tensor) or x.dim() != 4 or B.dim() != 3:
         raise ValueError("expected x [batch, L, H, P] and B/C [batch, L, N]")
     batch, L, H, P = x.shape
     N = B.shape[2]
+    _shape(dt, "dt", (batch, L, H))
+    _shape(A, "A", (H,))
+    _shape(B, "B", (batch, L, N))
+    _shape(C, "C", (batch, L, N))
+    _shape(D, "D", (H,))
+    _shape(dt_bias, "dt_bias", (H,))
+    _shape(initial_state, "initial_state", (batch, H, P, N))
+    _shape(y, "y", (batch, L, H, P))
+    _shape(final_state, "final_state", (batch, H, P, N))
     act, dev = x.dtype, x.device
-    if tuple(dt.shape) != (batch, L, H) or tuple(A.shape) != (H,):
-        raise ValueError("dt must be [batch, L, H] and A [H]")
-    if tuple(B.shape) != (batch, L, N) or tuple(C.shape) != (batch, L, N):
-        raise ValueError("B / C must be [batch, L, N]")
-    for name, v in (("D", D), ("dt_bias", dt_bias)):
-        if v is not None and tuple(v.shape) != (H,):
-            raise ValueError(f"{name} must be [H]")
-    if initial_state is not None and tuple(initial_state.shape) != (batch, H, P, N):
-        raise ValueError("initial_state must be [batch, H, P, N]")
     if y is None:
         y = torch.empty((batch, L, H, P), dtype=act, device=dev)
     if final_state is None and return_final_state:
         final_state = torch.empty((batch, H, P, N), dtype=torch.float32, device=dev)
     f32 = torch.float32
     if isinstance(workspace, str):
-        need = ssd_scan_workspace_size(batch, L, H, P, N)
-        workspace = torch.empty((need,), dtype=torch.uint8, device=dev) if need else None
-    ws_ptr = workspace.data_ptr() if workspace is not None else None
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        if workspace != "auto":
+            raise ValueError(f"unknown workspace option {workspace!r}")
+        ws_ptr, ws_bytes = _workspace(None, ssd_scan_workspace_size(batch, L, H, P, N), dev)
+    elif workspace is None:
+        ws_ptr, ws_bytes = None, 0
+    else:
+        ws_ptr, ws_bytes = _workspace(workspace, 0, dev)
     st = lib.ssm_ssd_scan_fwd(
         _ptr(x, "x", act, dev), _ptr(dt, "dt", act, dev), _ptr(A, "A", f32, dev), _ptr(B, "B", act, dev),
         _ptr(C, "C", act, dev), _ptr(D, "D", f32, dev), _ptr(dt_bias, "dt_bias", f32, dev),
@@ -254,11 +286,12 @@ def causal_conv1d(x, weight, bias=None, silu=True, *, out=None, stream=None) -> 
     """Causal depthwise conv1d along L (+ SiLU).  x [batch, D, L]; weight [D, K] float32
     (K <= 4, weight[:, K-1] weighs the current token); bias [D] or None."""
     lib = _lib.load_library()
-    if x.dim() != 3 or weight.dim() != 2 or weight.shape[0] != x.shape[1]:
+    if not isinstance(x, torch.Tensor) or not isinstance(weight, torch.Tensor) or x.dim() != 3 \
+            or weight.dim() != 2 or weight.shape[0] != x.shape[1]:
         raise ValueError("expected x [batch, D, L] and weight [D, K]")
     batch, Dc, L = x.shape
-    if bias is not None and tuple(bias.shape) != (Dc,):
-        raise ValueError("bias must be [D]")
+    _shape(bias, "bias", (Dc,))
+    _shape(out, "out", (batch, Dc, L))
     dev = x.device
     if out is None:
         out = torch.empty_like(x)
@@ -279,21 +312,13 @@ def selective_scan_fwd_conv(x, conv_weight, conv_bias, delta, A, B, C, D=None, z
     Returns (y, final_state, u) where u is the convolution output when `return_u`
     (or `u_out` is given), else None."""
     lib = _lib.load_library()
-    if x.dim() != 3 or B.dim() != 3 or A.dim() != 2 or conv_weight.dim() != 2:
-        raise ValueError("expected x [batch, D, L], B/C [batch, N, L], A [D, N], conv_weight [D, K]")
-    batch, Dc, L = x.shape
-    N = A.shape[1]
+    batch, Dc, L, N = _scan_shapes(x, delta, A, B, C, D, z, delta_bias, initial_state, y, final_state)
+    if not isinstance(conv_weight, torch.Tensor) or conv_weight.dim() != 2 or conv_weight.shape[0] != Dc:
+        raise ValueError("conv_weight must be [D, K]")
+    _shape(conv_bias, "conv_bias", (Dc,))
+    _shape(u_out, "u_out", (batch, Dc, L))
     act = x.dtype
     dev = x.device
-    if tuple(delta.shape) != (batch, Dc, L) or tuple(A.shape) != (Dc, N) or conv_weight.shape[0] != Dc:
-        raise ValueError("delta / A / conv_weight shape mismatch")
-    if tuple(B.shape) != (batch, N, L) or tuple(C.shape) != (batch, N, L):
-        raise ValueError("B / C must be [batch, N, L]")
-    if z is not None and tuple(z.shape) != (batch, Dc, L):
-        raise ValueError("z must be [batch, D, L]")
-    for name, v in (("D", D), ("delta_bias", delta_bias), ("conv_bias", conv_bias)):
-        if v is not None and tuple(v.shape) != (Dc,):
-            raise ValueError(f"{name} must be [D]")
     if y is None:
         y = torch.empty((batch, Dc, L), dtype=act, device=dev)
     if final_state is None and return_final_state:
@@ -317,12 +342,25 @@ def selective_scan_fwd_conv(x, conv_weight, conv_bias, delta, A, B, C, D=None, z
 def state_update(state, u_t, delta_t, A, B_t, C_t, D=None, z_t=None, delta_bias=None,
                  delta_softplus=True, *, out_state=None, y=None, discretization="simplified",
                  stream=None) -> torch.Tensor:
-    """One decode step.  Updates `out_state` (default: `state`, in place); returns y_t [S, D].
-    `discretization` as in selective_scan_fwd."""
+    """One decode step.  state [S, D, N] float32; u_t, delta_t, z_t [S, D]; A [D, N];
+    B_t, C_t [S, N]; D, delta_bias [D].  Updates `out_state` (default: `state`, in
+    place); returns y_t [S, D].  `discretization` as in selective_scan_fwd."""
     if discretization not in ("simplified", "zoh"):
         raise ValueError(f"unknown discretization {discretization!r}")
     lib = _lib.load_library()
+    if not isinstance(state, torch.Tensor) or state.dim() != 3:
+        raise ValueError("expected state [S, D, N]")
     S, Dc, N = state.shape
+    _shape(u_t, "u_t", (S, Dc))
+    _shape(delta_t, "delta_t", (S, Dc))
+    _shape(z_t, "z_t", (S, Dc))
+    _shape(A, "A", (Dc, N))
+    _shape(B_t, "B_t", (S, N))
+    _shape(C_t, "C_t", (S, N))
+    _shape(D, "D", (Dc,))
+    _shape(delta_bias, "delta_bias", (Dc,))
+    _shape(out_state, "out_state", (S, Dc, N))
+    _shape(y, "y", (S, Dc))
     act = u_t.dtype
     dev = state.device
     if out_state is None:

@@ -2,10 +2,8 @@
 
 Layouts (row-major):
   u, delta (raw, before bias/softplus), z : [batch][D][L]
-  B, C                                    : [batch][L][N] as float arrays (the pages'
-                                            order, which the oracle takes) and
-                                            [batch][N][L] as upload arrays (the
-                                            library's memory order)
+  B, C                                    : [batch][L][N] (the pages' order, which
+                                            both the oracle and the library take)
   A                                       : [D][N]   (float32 always)
   Dskip, delta_bias                       : [D]      (float32 always)
 Decode step tensors:
@@ -55,13 +53,6 @@ def f32_from_bf16_bits(bits: np.ndarray) -> np.ndarray:
     """bfloat16 bit patterns -> float32 (exact)."""
     bits = np.ascontiguousarray(bits, dtype=np.uint16)
     return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
-
-
-def _device_order(name: str, up: np.ndarray) -> np.ndarray:
-    """B and C go to the device as [batch][N][L]; everything else as drawn."""
-    if name in ("B", "C"):
-        return np.ascontiguousarray(up.transpose(0, 2, 1))
-    return up
 
 
 def _act(x32: np.ndarray, dtype: str):
@@ -114,7 +105,7 @@ class ScanInputs:
             if not np.array_equal(vals, v.astype(np.float32), equal_nan=True):
                 raise ValueError(f"{name} holds values not representable in {self.dtype}")
             setattr(self, name, vals)
-            self.dev[name] = _device_order(name, up)
+            self.dev[name] = up
 
 
 def make_scan_inputs(batch: int, L: int, D: int, N: int, dtype: str = "f32",
@@ -160,7 +151,7 @@ def make_scan_inputs(batch: int, L: int, D: int, N: int, dtype: str = "f32",
             continue
         vals, up = _act(v, dtype)
         setattr(inp, name, vals)
-        inp.dev[name] = _device_order(name, up)
+        inp.dev[name] = up
         del v
     return inp
 

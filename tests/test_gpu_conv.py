@@ -100,14 +100,13 @@ def test_scan_with_fused_conv(shape):
 @pytest.mark.parametrize("shape", [(1, 264, 32771, "f32", True, 4), (2, 264, 16401, "bf16", True, 3)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_fused_conv_many_channels_token_sequential(shape):
-    """From 32768 channels the fused conv runs in the token-sequential kernel: sampled
-    channels and every batch row's last channels against the oracle, u_out against the
-    oracle's convolution, and (float32) the fused call equal to the standalone conv
-    followed by the scan, bit for bit."""
+    """From 32768 channels the fused conv runs in the token-sequential kernel: every
+    channel against the oracle, u_out against the oracle's convolution, and (float32)
+    the fused call equal to the standalone conv followed by the scan, bit for bit."""
     import torch
     from selective_state_space_68_amd import (causal_conv1d, selective_scan_fwd, selective_scan_fwd_conv,
                                               selective_scan_fwd_kernel)
-    from gpu_util import sample_channels
+    import oracle_pool
     batch, L, D, dtype, gate, K = shape
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     assert selective_scan_fwd_kernel(batch, L, D, 16, tdt, gate, conv_width=K) == "scan_tokseq_kernel"
@@ -119,19 +118,39 @@ def test_fused_conv_many_channels_token_sequential(shape):
                                        t["bias"], return_u=True)
     torch.cuda.synchronize()
     yh, fh, uh = host(y), host(fs), host(u)
-    chans = sorted(set(sample_channels(batch, D, 10, seed=8)) | {(b, D - 1 - j) for b in range(batch) for j in range(3)})
-    for b in sorted({b for b, _ in chans}):
-        ds = [d for bb, d in chans if bb == b]
-        u_ref = oracle.causal_conv1d(inp.u[b:b + 1][:, ds], w[ds], cb[ds], apply_silu=True)
-        ry, rf = oracle.selective_scan(u_ref, inp.delta[b:b + 1][:, ds], inp.A[ds], inp.B[b:b + 1], inp.C[b:b + 1],
-                                       inp.Dskip[ds], None if inp.z is None else inp.z[b:b + 1][:, ds],
-                                       inp.delta_bias[ds])
-        ey, ef, eu = row_rel_err(yh[b][ds], ry[0]), row_rel_err(fh[b][ds], rf[0]), row_rel_err(uh[b][ds], u_ref[0])
-        print(f"fused conv tokseq {shape} row {b}: y_err={ey:.2e} state_err={ef:.2e} u_err={eu:.2e}", flush=True)
-        assert ey <= TOL[dtype] and ef <= TOL[dtype]
-        assert eu <= (2e-6 if dtype == "f32" else 8e-3)
+    ey, ef, _, eu = oracle_pool.scan_errors(inp, yh, fh, conv=(w, cb), u_gpu=uh, label=f"fused conv tokseq {shape}")
+    assert ey <= TOL[dtype] and ef <= TOL[dtype], (ey, ef)
+    assert eu <= (2e-6 if dtype == "f32" else 8e-3), eu
     if dtype == "f32":
         us = causal_conv1d(t["u"], tw, tcb)
         y2, f2 = selective_scan_fwd(us, t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["bias"])
         torch.cuda.synchronize()
         assert torch.equal(us, u) and torch.equal(y, y2) and torch.equal(fs, f2)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_fused_conv_u_out_one_element_off_alignment(dtype):
+    """u_out a contiguous view one element past a 16-byte boundary: the scan must not
+    store it with 16-byte vectors (it takes the element path); u, y and the state
+    against the oracle, and the element just before the view untouched."""
+    import torch
+    from selective_state_space_68_amd import selective_scan_fwd_conv
+    batch, L, D, N, K = 2, 1032, 12, 16, 4
+    inp = synth.make_scan_inputs(batch, L, D, N, dtype, gate=True, d_skip="normal", seed=31, a_kind="lognormal")
+    w, cb = _conv_params(D, K, seed=3)
+    u_ref = oracle.causal_conv1d(inp.u, w, cb, apply_silu=True)
+    ry, rf = oracle.selective_scan(u_ref, inp.delta, inp.A, inp.B, inp.C, inp.Dskip, inp.z, inp.delta_bias)
+    t = upload_scan(inp)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    buf = torch.full((batch * D * L + 1,), 7.0, dtype=tdt, device="cuda")
+    u_out = buf[1:].view(batch, D, L)
+    assert u_out.data_ptr() % 16 != 0 and u_out.is_contiguous()
+    y, fs, u = selective_scan_fwd_conv(t["u"], dev(w), dev(cb), t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"],
+                                       t["bias"], u_out=u_out)
+    torch.cuda.synchronize()
+    assert u.data_ptr() == u_out.data_ptr()
+    eu, ey, ef = row_rel_err(host(u), u_ref), row_rel_err(host(y), ry), row_rel_err(host(fs), rf)
+    print(f"unaligned u_out {dtype}: u_err={eu:.2e} y_err={ey:.2e} state_err={ef:.2e}", flush=True)
+    assert eu <= (2e-6 if dtype == "f32" else 8e-3)
+    assert ey <= TOL[dtype] and ef <= TOL[dtype]
+    assert float(buf[0]) == 7.0

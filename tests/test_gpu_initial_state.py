@@ -72,7 +72,8 @@ def test_scan_in_pieces_matches_one_scan(dtype):
     state = torch.zeros((batch, D, N), dtype=torch.float32, device="cuda")
     ys = []
     for a, b in ((0, 1000), (1000, 1001), (1001, 2200), (2200, 3000)):
-        piece = {k: t[k][:, :, a:b].contiguous() for k in ("u", "delta", "z", "B", "C")}
+        piece = {k: t[k][:, :, a:b].contiguous() for k in ("u", "delta", "z")}
+        piece |= {k: t[k][:, a:b].contiguous() for k in ("B", "C")}      # [batch][L][N]
         y, _ = selective_scan_fwd(piece["u"], piece["delta"], t["A"], piece["B"], piece["C"], t["D"],
                                   piece["z"], t["bias"], initial_state=state, final_state=state)
         ys.append(host(y))
@@ -94,7 +95,7 @@ def test_zero_length_returns_the_initial_state():
     th0 = dev(h0)
     A = dev(np.full((3, 4), -1.0, dtype=np.float32))
     e = torch.empty((2, 3, 0), device="cuda")
-    ebc = torch.empty((2, 4, 0), device="cuda")
+    ebc = torch.empty((2, 0, 4), device="cuda")              # B, C [batch][L][N]
     _, fs = selective_scan_fwd(e, e.clone(), A, ebc, ebc.clone(), initial_state=th0)
     torch.cuda.synchronize()
     assert np.array_equal(host(fs), h0.astype(np.float64))

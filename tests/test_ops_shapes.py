@@ -1,0 +1,119 @@
+"""The Python binding checks every tensor's shape, outputs included, before it hands
+a single pointer to the library (which sees only pointers and sizes).  CPU tensors
+suffice: a wrong shape must raise before the GPU check is reached."""
+import pytest
+import torch
+
+import selective_state_space_68_amd as ssm
+
+F32 = torch.float32
+
+
+def _scan_inputs(batch=2, L=16, D=3, N=4):
+    t = lambda *s: torch.zeros(s, dtype=F32)
+    return dict(u=t(batch, D, L), delta=t(batch, D, L), A=t(D, N), B=t(batch, L, N), C=t(batch, L, N),
+                D=t(D), z=t(batch, D, L), delta_bias=t(D))
+
+
+SCAN_BAD = [
+    ("delta", (2, 3, 15)), ("A", (3, 5)), ("B", (2, 4, 16)), ("C", (2, 16, 5)), ("z", (2, 3, 17)),
+    ("D", (4,)), ("delta_bias", (2,)),
+]
+
+
+@pytest.mark.parametrize("name,shape", SCAN_BAD)
+def test_scan_rejects_wrong_input_shapes(name, shape):
+    a = _scan_inputs()
+    a[name] = torch.zeros(shape, dtype=F32)
+    with pytest.raises(ValueError, match="must have shape"):
+        ssm.selective_scan_fwd(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["delta_bias"])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(y=torch.zeros(2, 3, 15)), dict(final_state=torch.zeros(2, 3, 5)), dict(initial_state=torch.zeros(1, 3, 4)),
+])
+def test_scan_rejects_wrong_output_and_state_shapes(kw):
+    a = _scan_inputs()
+    with pytest.raises(ValueError, match="must have shape"):
+        ssm.selective_scan_fwd(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["delta_bias"], **kw)
+
+
+def test_scan_right_shapes_reach_the_device_check():
+    a = _scan_inputs()
+    with pytest.raises(ValueError, match="must live on the GPU"):
+        ssm.selective_scan_fwd(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["delta_bias"],
+                               y=torch.zeros(2, 3, 16), final_state=torch.zeros(2, 3, 4))
+
+
+def test_scan_rejects_a_workspace_that_is_not_a_device_tensor():
+    a = _scan_inputs()
+    with pytest.raises(ValueError, match="workspace"):
+        ssm.selective_scan_fwd(a["u"], a["delta"], a["A"], a["B"], a["C"], workspace=object())
+
+
+@pytest.mark.parametrize("name,shape", SCAN_BAD + [("dy", (2, 3, 15)), ("dfinal_state", (2, 3, 5))])
+def test_bwd_rejects_wrong_shapes(name, shape):
+    a = _scan_inputs()
+    a["dy"] = torch.zeros(2, 3, 16)
+    a["dfinal_state"] = torch.zeros(2, 3, 4)
+    a[name] = torch.zeros(shape, dtype=F32)
+    with pytest.raises(ValueError, match="must have shape"):
+        ssm.selective_scan_bwd(a["u"], a["delta"], a["A"], a["B"], a["C"], a["dy"], a["D"], a["z"],
+                               a["delta_bias"], dfinal_state=a["dfinal_state"])
+
+
+def test_bwd_rejects_wrong_output_shapes():
+    a = _scan_inputs()
+    dy = torch.zeros(2, 3, 16)
+    for key, shape in (("dB", (2, 4, 16)), ("du", (2, 3, 15)), ("dA", (4, 3))):
+        with pytest.raises(ValueError, match="must have shape"):
+            ssm.selective_scan_bwd(a["u"], a["delta"], a["A"], a["B"], a["C"], dy, out={key: torch.zeros(shape)})
+
+
+def test_conv_and_fused_conv_shapes():
+    a = _scan_inputs()
+    w = torch.zeros(3, 4)
+    with pytest.raises(ValueError, match="must have shape"):
+        ssm.causal_conv1d(a["u"], w, torch.zeros(2))
+    with pytest.raises(ValueError, match="must have shape"):
+        ssm.causal_conv1d(a["u"], w, out=torch.zeros(2, 3, 8))
+    with pytest.raises(ValueError, match="must have shape"):
+        ssm.selective_scan_fwd_conv(a["u"], w, None, a["delta"], a["A"], a["B"], a["C"],
+                                    u_out=torch.zeros(2, 3, 15))
+    with pytest.raises(ValueError, match="must have shape"):
+        ssm.selective_scan_fwd_conv(a["u"], w, torch.zeros(5), a["delta"], a["A"], a["B"], a["C"])
+    with pytest.raises(ValueError, match="must have shape"):
+        ssm.selective_scan_fwd_conv(a["u"], w, None, a["delta"], a["A"], a["B"].transpose(1, 2), a["C"])
+
+
+STEP_BAD = [
+    ("u_t", (4, 7)), ("delta_t", (3, 8)), ("z_t", (4,)), ("A", (8, 15)), ("B_t", (16,)), ("C_t", (4, 8)),
+    ("D", (7,)), ("delta_bias", (9,)), ("out_state", (4, 8, 8)), ("y", (4, 9)),
+]
+
+
+@pytest.mark.parametrize("name,shape", STEP_BAD)
+def test_state_update_rejects_wrong_shapes(name, shape):
+    S, D, N = 4, 8, 16
+    a = dict(state=torch.zeros(S, D, N), u_t=torch.zeros(S, D), delta_t=torch.zeros(S, D), A=torch.zeros(D, N),
+             B_t=torch.zeros(S, N), C_t=torch.zeros(S, N), D=torch.zeros(D), z_t=torch.zeros(S, D),
+             delta_bias=torch.zeros(D), out_state=None, y=None)
+    a[name] = torch.zeros(shape)
+    with pytest.raises(ValueError, match="must have shape"):
+        ssm.state_update(a["state"], a["u_t"], a["delta_t"], a["A"], a["B_t"], a["C_t"], a["D"], a["z_t"],
+                         a["delta_bias"], out_state=a["out_state"], y=a["y"])
+
+
+@pytest.mark.parametrize("name,shape", [
+    ("dt", (1, 64, 3)), ("A", (3,)), ("B", (1, 64, 32)), ("C", (1, 63, 64)), ("D", (1,)), ("dt_bias", (4,)),
+    ("initial_state", (1, 2, 64, 32)), ("y", (1, 64, 2, 32)), ("final_state", (2, 2, 64, 64)),
+])
+def test_ssd_rejects_wrong_shapes(name, shape):
+    b, L, H, P, N = 1, 64, 2, 64, 64
+    a = dict(x=torch.zeros(b, L, H, P), dt=torch.zeros(b, L, H), A=torch.zeros(H), B=torch.zeros(b, L, N),
+             C=torch.zeros(b, L, N), D=torch.zeros(H), dt_bias=torch.zeros(H), initial_state=None, y=None,
+             final_state=None)
+    a[name] = torch.zeros(shape)
+    with pytest.raises(ValueError, match="must have shape"):
+        ssm.ssd_scan_fwd(a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["dt_bias"],
+                         initial_state=a["initial_state"], y=a["y"], final_state=a["final_state"])

@@ -337,8 +337,6 @@ def test_generator_is_deterministic_and_bf16_exact():
     for name in ("u", "delta", "B", "C", "z"):
         assert np.array_equal(a.dev[name], b.dev[name])
         vals = synth.f32_from_bf16_bits(a.dev[name])
-        if name in ("B", "C"):                      # uploaded as [batch][N][L]
-            vals = vals.transpose(0, 2, 1)
         assert np.array_equal(vals, getattr(a, name))
     c = synth.make_scan_inputs(2, 64, 8, 4, "bf16", seed=4)
     assert not np.array_equal(a.dev["u"], c.dev["u"])
