@@ -49,7 +49,8 @@ typedef enum {
   SSM_OK = 0,
   SSM_ERR_INVALID_ARG = 1,  /* null required pointer, negative size, misalignment, aliasing */
   SSM_ERR_UNSUPPORTED = 2,  /* N outside [1, 64], unknown dtype or variant */
-  SSM_ERR_HIP = 3           /* no usable device, launch failure, or missing gfx950 code */
+  SSM_ERR_HIP = 3,          /* no usable device, launch failure, or missing gfx950 code */
+  SSM_ERR_TOO_LARGE = 4     /* the call needs more scratch than the allocation-free entry point holds */
 } ssm_status;
 
 typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
@@ -358,6 +359,30 @@ ssm_status ssm_ssd_scan_fwd(
     const float *initial_state, void *y, float *final_state,
     int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, ssm_dtype dtype,
     void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * The SSD scan for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same operation,
+ * arguments (without the workspace), layouts, errors and results as ssm_ssd_scan_fwd
+ * given a workspace of ssm_ssd_scan_workspace_size(...) bytes: the segment states
+ * live in a library-owned
+ * device array of SSM_SSD_NOALLOC_SCRATCH_BYTES per GPU (allocated when the library's
+ * code is loaded on that GPU, held until the process ends), so the call allocates
+ * nothing.  A shape whose workspace size exceeds that array returns SSM_ERR_TOO_LARGE
+ * (no supported shape does: the segment rule keeps it under ~51 MB).  The first call
+ * on a device looks up the array's address there (thread-safe).  Calls on one GPU
+ * share the array: two calls that overlap in time on the same GPU (on different
+ * streams, or captured into graphs that run concurrently) race on it and give wrong
+ * results; calls in one stream order are safe.  Nothing in the array needs clearing:
+ * each call writes every entry it reads.
+ */
+#define SSM_SSD_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+ssm_status ssm_ssd_scan_fwd_noalloc(
+    const void *x, const void *dt, const float *A, const void *Bm, const void *Cm,
+    const float *Dskip, const float *dt_bias, int dt_softplus,
+    const float *initial_state, void *y, float *final_state,
+    int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, ssm_dtype dtype, void *stream);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char *ssm_status_string(ssm_status s);

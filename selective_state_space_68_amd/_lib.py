@@ -16,6 +16,7 @@ SSM_OK = 0
 SSM_ERR_INVALID_ARG = 1
 SSM_ERR_UNSUPPORTED = 2
 SSM_ERR_HIP = 3
+SSM_ERR_TOO_LARGE = 4
 
 SSM_F32 = 0
 SSM_BF16 = 1
@@ -56,6 +57,8 @@ SIGNATURES = {
     "ssm_ssd_scan_workspace_size": (_sz, [_i64, _i64, _i64, _i64, _i64, _int]),
     "ssm_ssd_scan_fwd": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _vp, _vp, _vp,
                                 _i64, _i64, _i64, _i64, _i64, _int, _vp, _sz, _vp]),
+    "ssm_ssd_scan_fwd_noalloc": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _vp, _vp, _vp,
+                                        _i64, _i64, _i64, _i64, _i64, _int, _vp]),
     "ssm_status_string": (ctypes.c_char_p, [_int]),
     "ssm_calib_copy": (_int, [_vp, _vp, _sz, _vp]),
     "ssm_calib_alu": (_int, [_int, _vp, _i64, _int, _vp]),

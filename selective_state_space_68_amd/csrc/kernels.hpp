@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/ssm.h"
+
 namespace ssm {
 
 enum class Dt : int { F32 = 0, BF16 = 1 };
@@ -29,7 +31,6 @@ struct ScanArgs {
   int N;
   int softplus;
   int zoh = 0;           // 1: full zero-order hold, input term (exp(Delta A) - 1)/A * B * u
-                         //    (chunked kernel only)
 };
 
 struct ConvArgs {
@@ -113,6 +114,13 @@ struct SsdArgs {
 bool ssd_supported(int64_t H, int64_t P, int64_t N);
 size_t ssd_workspace_bytes(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N);
 hipError_t launch_ssd_scan(const SsdArgs& a, void* ws, size_t ws_bytes, hipStream_t s);
+// The C-ABI SSD call split in two (ssm_api.cpp): argument validation (everything the
+// header documents, before any device call; fills *a) and the run on `stream`.
+ssm_status ssd_check(const void* x, const void* dt, const float* A, const void* Bm, const void* Cm, const float* Dskip,
+                     const float* dt_bias, int dt_softplus, const float* initial_state, const void* y,
+                     const float* final_state, int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N,
+                     ssm_dtype dtype, const void* workspace, size_t workspace_bytes, SsdArgs* a);
+ssm_status ssd_run(const SsdArgs& a, void* workspace, size_t workspace_bytes, void* stream);
 
 // One thread per (b, d) channel, sequential over time.  Any N in [1, 64].
 hipError_t launch_scan_sequential(const ScanArgs& a, Dt dt, hipStream_t s);

@@ -11,7 +11,7 @@
 
 namespace {
 
-constexpr int kVersion = 30000;  // 3.0.0: B and C in [batch][L][N]; forward scan workspace arguments
+constexpr int kVersion = 30100;  // 3.1.0: + allocation-free SSD entry point (ssm_ssd_scan_fwd_noalloc)
 
 struct Span {
   uintptr_t lo = 0, hi = 0;  // [lo, hi); empty when lo == hi
@@ -96,23 +96,16 @@ ssm_status check_scan(const void* u, const void* delta, const float* A, const vo
 
 }  // namespace
 
-extern "C" {
+namespace ssm {
 
-size_t ssm_ssd_scan_workspace_size(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, ssm_dtype dtype) {
-  if (dtype != SSM_BF16 || !ssm::ssd_supported(H, P, N) || batch <= 0 || L <= 0 || H <= 0) return 0;
-  uint64_t t;
-  if (!mul_ok(batch, H, &t) || !mul_ok(t, L, &t) || t > (uint64_t(1) << 50)) return 0;
-  return ssm::ssd_workspace_bytes(batch, L, H, P, N);
-}
-
-ssm_status ssm_ssd_scan_fwd(const void* x, const void* dt, const float* A, const void* Bm, const void* Cm,
-                            const float* Dskip, const float* dt_bias, int dt_softplus, const float* initial_state,
-                            void* y, float* final_state, int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N,
-                            ssm_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
+ssm_status ssd_check(const void* x, const void* dt, const float* A, const void* Bm, const void* Cm, const float* Dskip,
+                     const float* dt_bias, int dt_softplus, const float* initial_state, const void* y,
+                     const float* final_state, int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N,
+                     ssm_dtype dtype, const void* workspace, size_t workspace_bytes, SsdArgs* a) {
   if (dtype != SSM_F32 && dtype != SSM_BF16) return SSM_ERR_UNSUPPORTED;
   if (batch < 0 || L < 0 || H < 0 || P < 0 || N < 0) return SSM_ERR_INVALID_ARG;
   if (dt_softplus != 0 && dt_softplus != 1) return SSM_ERR_INVALID_ARG;
-  if (dtype != SSM_BF16 || !ssm::ssd_supported(H, P, N)) return SSM_ERR_UNSUPPORTED;
+  if (dtype != SSM_BF16 || !ssd_supported(H, P, N)) return SSM_ERR_UNSUPPORTED;
   uint64_t blh, xe, xbytes, dtbytes, bl, bcbytes, bh, st, stbytes;
   if (!mul_ok(batch, L, &blh) || !mul_ok(blh, H, &blh) || !mul_ok(blh, P, &xe) || !mul_ok(xe, 2, &xbytes) ||
       !mul_ok(batch, L, &bl) || !mul_ok(bl, H, &dtbytes) || !mul_ok(dtbytes, 2, &dtbytes) ||
@@ -141,17 +134,45 @@ ssm_status ssm_ssd_scan_fwd(const void* x, const void* dt, const float* A, const
   for (const Span& s : in)
     if (overlaps(wsp, s)) return SSM_ERR_INVALID_ARG;
   if (overlaps(wsp, ys) || overlaps(wsp, fs) || overlaps(wsp, hs)) return SSM_ERR_INVALID_ARG;
-  if (batch == 0 || H == 0) return SSM_OK;
+  a->x = x; a->dt = dt; a->A = A; a->Bm = Bm; a->Cm = Cm; a->Dskip = Dskip; a->dt_bias = dt_bias;
+  a->h0 = initial_state; a->y = const_cast<void*>(y); a->final_state = const_cast<float*>(final_state);
+  a->batch = batch; a->L = L; a->H = H; a->P = static_cast<int>(P); a->N = static_cast<int>(N);
+  a->softplus = dt_softplus;
+  return SSM_OK;
+}
+
+ssm_status ssd_run(const SsdArgs& a, void* workspace, size_t workspace_bytes, void* stream) {
+  if (a.batch == 0 || a.H == 0) return SSM_OK;
   const ssm_status ds = probe_device();
   if (ds != SSM_OK) return ds;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (L == 0)
-    return final_state ? from_hip(ssm::launch_copy_state(final_state, initial_state, batch * H * P * N, s)) : SSM_OK;
+  if (a.L == 0)
+    return a.final_state
+               ? from_hip(launch_copy_state(a.final_state, a.h0, a.batch * a.H * a.P * a.N, s))
+               : SSM_OK;
+  return from_hip(launch_ssd_scan(a, workspace, workspace_bytes, s));
+}
+
+}  // namespace ssm
+
+extern "C" {
+
+size_t ssm_ssd_scan_workspace_size(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, ssm_dtype dtype) {
+  if (dtype != SSM_BF16 || !ssm::ssd_supported(H, P, N) || batch <= 0 || L <= 0 || H <= 0) return 0;
+  uint64_t t;
+  if (!mul_ok(batch, H, &t) || !mul_ok(t, L, &t) || t > (uint64_t(1) << 50)) return 0;
+  return ssm::ssd_workspace_bytes(batch, L, H, P, N);
+}
+
+ssm_status ssm_ssd_scan_fwd(const void* x, const void* dt, const float* A, const void* Bm, const void* Cm,
+                            const float* Dskip, const float* dt_bias, int dt_softplus, const float* initial_state,
+                            void* y, float* final_state, int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N,
+                            ssm_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
   ssm::SsdArgs a;
-  a.x = x; a.dt = dt; a.A = A; a.Bm = Bm; a.Cm = Cm; a.Dskip = Dskip; a.dt_bias = dt_bias; a.h0 = initial_state;
-  a.y = y; a.final_state = final_state;
-  a.batch = batch; a.L = L; a.H = H; a.P = static_cast<int>(P); a.N = static_cast<int>(N); a.softplus = dt_softplus;
-  return from_hip(ssm::launch_ssd_scan(a, workspace, workspace_bytes, s));
+  const ssm_status st = ssm::ssd_check(x, dt, A, Bm, Cm, Dskip, dt_bias, dt_softplus, initial_state, y, final_state,
+                                       batch, L, H, P, N, dtype, workspace, workspace_bytes, &a);
+  if (st != SSM_OK) return st;
+  return ssm::ssd_run(a, workspace, workspace_bytes, stream);
 }
 
 const char* ssm_status_string(ssm_status s) {
@@ -160,6 +181,8 @@ const char* ssm_status_string(ssm_status s) {
     case SSM_ERR_INVALID_ARG: return "SSM_ERR_INVALID_ARG: invalid argument (null pointer, negative size, misalignment or aliasing)";
     case SSM_ERR_UNSUPPORTED: return "SSM_ERR_UNSUPPORTED: unsupported configuration (N outside [1, 64], dtype or variant)";
     case SSM_ERR_HIP: return "SSM_ERR_HIP: HIP runtime error (no usable device, or launch failed)";
+    case SSM_ERR_TOO_LARGE:
+      return "SSM_ERR_TOO_LARGE: the call needs more scratch than the allocation-free entry point holds";
   }
   return "SSM: unknown status";
 }

@@ -41,8 +41,8 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.ssm_version() == 30000
-    for s in range(4):
+    assert lib.ssm_version() == 30100
+    for s in range(5):
         assert lib.ssm_status_string(s).decode().startswith(("SSM_OK", "SSM_ERR"))
     assert b"unknown" in lib.ssm_status_string(99)
 
