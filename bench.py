@@ -59,6 +59,9 @@ MALL_BYTES = 256 << 20
 CALIB_BYTES = 1 << 30
 DEFAULT_WORKLOAD = "long131k_bf16"
 GRADED = ("tiny_f32", "mamba130m_f32", "mamba1p4b_bf16", "long131k_bf16", "decode_bf16")
+# bfloat16 workloads whose A rows (-(n+1)) let the library's arithmetic-progression
+# decay path run; bench.py times them both ways and reports that path separately
+AP_WORKLOADS = ("mamba1p4b_bf16", "long131k_bf16")
 MIN_WARM_S = 0.1
 STAT_REPS = 50
 _CSRC = "selective_state_space_68_amd/csrc/"
@@ -94,7 +97,7 @@ def src_hash(kernel):
 
 def traffic_from_profiles(workload, kernel):
     """HBM bytes per launch from the committed rocprofv3 counter summaries
-    (profile_counters.py writes them), or None when the kernel source changed since
+    (profile_summary.py writes them), or None when the kernel source changed since
     the counters were taken."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
@@ -474,7 +477,10 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(synth.CONFIGS))
-    ap.add_argument("--variant", type=int, default=0)
+    ap.add_argument("--variant", type=int, default=0, help="ssm_scan_variant (--ap adds SSM_SCAN_AP)")
+    ap.add_argument("--ap", action="store_true",
+                    help="let the scan take its arithmetic-progression decay path where A allows it "
+                         "(default: the general path, one exp per element)")
     ap.add_argument("--kpl", type=int, default=0)
     ap.add_argument("--sets", type=int, default=0, help="input copies to rotate (0 = enough to exceed 600 MB)")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
@@ -492,6 +498,8 @@ def main():
     import torch
     import selective_state_space_68_amd as lib_ops
     lib = lib_ops.load_library()
+    if args.ap:
+        args.variant |= lib_ops.SSM_SCAN_AP
     torch.cuda.set_device(0)
     props = torch.cuda.get_device_properties(0)
 
@@ -527,6 +535,20 @@ def main():
             others[name] = summary(name, mo)
             torch.cuda.empty_cache()
 
+    # The arithmetic-progression decay path: the same calls with SSM_SCAN_AP
+    ap_path = {}
+    if not args.no_others and not args.ap and args.workload in GRADED:
+        general = dict(others, **{args.workload: summary(args.workload, m)})
+        oargs = argparse.Namespace(**vars(args))
+        oargs.variant, oargs.kpl, oargs.sets = lib_ops.SSM_SCAN_AP, 0, 0
+        for name in AP_WORKLOADS:
+            mo = run_workload(name, oargs, torch, lib_ops, warm=0)
+            mo["inp"] = None
+            s = summary(name, mo)
+            s["speedup_vs_general"] = general[name]["us_per_call"] / s["us_per_call"]
+            ap_path[name] = s
+            torch.cuda.empty_cache()
+
     kernel = m["kernel"]
     traffic = traffic_from_profiles(args.workload, kernel)
     hbm = {"achieved": hbm_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": hbm_gbs / PEAK_HBM_GBS,
@@ -551,6 +573,8 @@ def main():
         config = {"workload": args.workload, "batch": cfg.batch, "L": cfg.L, "D": cfg.D, "N": cfg.N,
                   "act_dtype": cfg.dtype, "gate": cfg.gate, "conv_width": cfg.conv_k,
                   "discretization": cfg.discretization, "variant": args.variant,
+                  "decay_path": "arithmetic progression (SSM_SCAN_AP)" if args.ap else
+                  "general (one exp per element)",
                   "tokens_per_lane": args.kpl or "auto"}
     elif kind == "ssd":
         config = {"workload": args.workload, "batch": cfg.batch, "L": cfg.L, "H": cfg.H, "P": cfg.P, "N": cfg.N,
@@ -579,6 +603,7 @@ def main():
                    "iterations": m["iterations"], "steps_per_iteration": K, "warmup_steps": m["warm_steps"],
                    "warmup_s": m["warm_s"], "min_warmup_s": MIN_WARM_S},
         "workloads": others,
+        "ap_path": ap_path,
         "calibration": calib,
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "hbm_gib": props.total_memory / 2 ** 30},

@@ -149,7 +149,20 @@ typedef enum {
   SSM_SCAN_AUTO = 0,
   SSM_SCAN_SEQUENTIAL = 1,
   SSM_SCAN_CHUNKED = 2,
-  SSM_SCAN_TOKSEQ = 3
+  SSM_SCAN_TOKSEQ = 3,
+  /* Flag, OR-ed into any of the above: allow the arithmetic-progression decay path.
+   * With it, the bfloat16 scan kernels with N == 16 and the simplified input term
+   * (the chunked kernel in its 12-wave vector-load form, the token-sequential kernel
+   * at 4 states per lane) check each channel's A row and, where it is an exact
+   * non-increasing arithmetic progression, A[d, n] == A[d, 0] + n * b in float32 with
+   * b = A[d, 1] - A[d, 0] <= 0 (the S4D-real -(n+1) and the HiPPO-derived -(2n+1)
+   * rows of the interview-prep page's "Discretization and initialization details"),
+   * form exp(Delta A[d, n]) as exp(Delta A[d, n0]) * exp(Delta b)^(n - n0) with
+   * n - n0 < 8: multiplies in place of most exponentials, within a few float32
+   * roundings of the direct values.  Other rows, other kernels, float32 and the full
+   * zero-order hold compute every exp(Delta A) directly (the general path), as every
+   * call without the flag does. */
+  SSM_SCAN_AP = 16
 } ssm_scan_variant;
 
 ssm_status ssm_selective_scan_fwd_variant(

@@ -25,6 +25,7 @@ SSM_SCAN_AUTO = 0
 SSM_SCAN_SEQUENTIAL = 1
 SSM_SCAN_CHUNKED = 2
 SSM_SCAN_TOKSEQ = 3
+SSM_SCAN_AP = 16
 
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64

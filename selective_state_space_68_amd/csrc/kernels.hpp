@@ -31,6 +31,8 @@ struct ScanArgs {
   int N;
   int softplus;
   int zoh = 0;           // 1: full zero-order hold, input term (exp(Delta A) - 1)/A * B * u
+  int ap = 0;            // 1: the arithmetic-progression decay path where a kernel has it
+                         //    (SSM_SCAN_AP)
 };
 
 struct ConvArgs {

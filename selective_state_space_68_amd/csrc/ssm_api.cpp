@@ -251,6 +251,8 @@ ssm_status scan_fwd(const void* u, const void* delta, const float* A, const void
   st = check_scan_workspace(workspace, workspace_bytes, scan_workspace_need(batch, L, D, N, dt), u, delta, A, Bm, Cm,
                             Dskip, z, delta_bias, initial_state, y, final_state, sz);
   if (st != SSM_OK) return st;
+  const int ap = (variant & SSM_SCAN_AP) ? 1 : 0;
+  variant &= ~SSM_SCAN_AP;
   if (variant != SSM_SCAN_AUTO && variant != SSM_SCAN_SEQUENTIAL && variant != SSM_SCAN_CHUNKED &&
       variant != SSM_SCAN_TOKSEQ)
     return SSM_ERR_UNSUPPORTED;
@@ -260,6 +262,7 @@ ssm_status scan_fwd(const void* u, const void* delta, const float* A, const void
   a.u = u; a.delta = delta; a.A = A; a.Bm = Bm; a.Cm = Cm; a.Dskip = Dskip; a.z = z;
   a.bias = delta_bias; a.h0 = initial_state; a.y = y; a.final_state = final_state;
   a.batch = batch; a.L = L; a.D = D; a.N = static_cast<int>(N); a.softplus = delta_softplus; a.zoh = zoh;
+  a.ap = ap;
   const ssm::Dt d = dt == SSM_BF16 ? ssm::Dt::BF16 : ssm::Dt::F32;
   const int kernel = L > 0 ? choose_scan_kernel(a, d, variant, tokens_per_lane) : SSM_SCAN_SEQUENTIAL;
   if (kernel < 0) return static_cast<ssm_status>(-kernel);
@@ -300,6 +303,7 @@ int ssm_selective_scan_fwd_kernel(int64_t batch, int64_t L, int64_t D, int64_t N
   if (dt != SSM_F32 && dt != SSM_BF16) return -SSM_ERR_UNSUPPORTED;
   if (batch <= 0 || L <= 0 || D <= 0 || N < 1) return -SSM_ERR_INVALID_ARG;
   if (N > SSM_MAX_N) return -SSM_ERR_UNSUPPORTED;
+  variant &= ~SSM_SCAN_AP;                           // (the decay path does not change the kernel)
   if (variant != SSM_SCAN_AUTO && variant != SSM_SCAN_SEQUENTIAL && variant != SSM_SCAN_CHUNKED &&
       variant != SSM_SCAN_TOKSEQ)
     return -SSM_ERR_UNSUPPORTED;

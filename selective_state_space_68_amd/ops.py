@@ -117,7 +117,7 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta
     batch, Dc, L, N = _scan_shapes(u, delta, A, B, C, D, z, delta_bias, initial_state, y, final_state)
     act = u.dtype
     dev = u.device
-    if discretization == "zoh" and (variant or tokens_per_lane or workspace is not None):
+    if discretization == "zoh" and ((variant & ~_lib.SSM_SCAN_AP) or tokens_per_lane or workspace is not None):
         raise ValueError("the zoh scan runs the default kernel (variant=0, tokens_per_lane=0, no workspace)")
     if discretization != "zoh":
         ws_ptr, ws_bytes = _workspace(workspace, selective_scan_workspace_size(batch, L, Dc, N, act), dev)

@@ -14,8 +14,9 @@ Decode step tensors:
 Distributions (the workloads' recipe): u, B, C, z ~ N(0, 1); raw delta ~ N(0, 0.5^2)
 (0.5 is read as the standard deviation); the delta bias per channel is the inverse
 softplus, log(expm1(dt)), of dt drawn log-uniformly in [1e-3, 1e-1]; A[d, n] = -(n+1)
-("S4D-real") unless ``a_kind="lognormal"`` (A = -exp(N(0,1)), an input that is not an
-arithmetic progression along n); the skip vector is N(0,1) or all ones.
+("S4D-real") unless ``a_kind="hippo"`` (A[d, n] = -(2n+1)) or ``a_kind="lognormal"``
+(A = -exp(N(0,1)), an input that is not an arithmetic progression along n); the skip
+vector is N(0,1) or all ones.
 
 Activations are drawn in float32 and, for bf16 workloads, rounded to bfloat16 by
 round-to-nearest-even on the bit pattern.  Every float array returned here holds
@@ -128,6 +129,8 @@ def make_scan_inputs(batch: int, L: int, D: int, N: int, dtype: str = "f32",
 
     if a_kind == "s4d":
         A = np.broadcast_to(-(np.arange(N, dtype=np.float32) + 1.0), (D, N)).copy()
+    elif a_kind == "hippo":
+        A = np.broadcast_to(-(2.0 * np.arange(N, dtype=np.float32) + 1.0), (D, N)).copy()
     elif a_kind == "lognormal":
         A = (-np.exp(rng["A"].standard_normal((D, N)))).astype(np.float32)
     else:

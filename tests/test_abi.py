@@ -368,6 +368,12 @@ def test_scan_kernel_choice(lib):
     assert k(1, 64, 16, 16, F32, 0, 0, 0, TOK, 8) == -_lib.SSM_ERR_UNSUPPORTED   # states per lane: 2 or 4
     assert k(1, 64, 16, 65, F32, 0, 0, 0, 0, 0) == -_lib.SSM_ERR_UNSUPPORTED
     assert k(1, 64, 16, 16, F32, 0, 0, 0, 7, 0) == -_lib.SSM_ERR_UNSUPPORTED
+    # the arithmetic-progression flag does not change the kernel
+    AP = _lib.SSM_SCAN_AP
+    assert k(8, 2048, 4096, 16, BF16, 1, 0, 0, AP, 0) == TOK
+    assert k(1, 131072, 2560, 16, BF16, 1, 0, 0, AP, 0) == CHK
+    assert k(1, 64, 16, 16, F32, 0, 0, 0, TOK | AP, 2) == TOK
+    assert k(1, 64, 16, 16, F32, 0, 0, 0, 7 | AP, 0) == -_lib.SSM_ERR_UNSUPPORTED
     assert k(0, 64, 16, 16, F32, 0, 0, 0, 0, 0) == -_lib.SSM_ERR_INVALID_ARG
     # the full zero-order hold: token-sequential at many channels, else chunked
     assert k(8, 2048, 4096, 16, BF16, 1, 1, 0, 0, 0) == TOK
