@@ -254,10 +254,11 @@ __device__ __forceinline__ void load_tile(float4* tile, const BwdArgs& p, int64_
 // One channel's per-token inputs for its KPL tokens of the chunk.  The vector path
 // (8 tokens per lane, L % 8 == 0, 16-byte aligned rows) loads them as raw 16-byte
 // vectors ahead of use: fetch() issues the loads, get() unpacks them.  In float32
-// only u and delta are fetched ahead; dy and z are loaded in get().  The four
-// float32 vectors held across a round made the main kernel spill 18 registers;
-// with two it spills 10 and the 130M-shaped backward is 6 % faster (198.7 -> 186.6
-// us; fetching only u measured the same as u and delta).  A lane whose
+// only u and delta are fetched ahead; dy and z are loaded in get().  (Before the
+// main kernel's LDS accumulator freed about 40 registers, the four float32 vectors
+// held across a round made it spill 18 registers and two spilled 10, 6 % faster on
+// the 130M-shaped backward; with the accumulator, four measured the same as two.)
+// A lane whose
 // tokens start at or past L loads the row's last tokens instead (the start is
 // clamped) and its values are masked by the caller.
 template <typename ACT, int KPL>
@@ -703,11 +704,18 @@ __global__ void bwd_combine_kernel(BwdArgs p, BwdLayout g) {
 
 // ---- 3. the gradients -----------------------------------------------------------------
 // NT: the most states the instantiation holds in LDS (even).  The workgroup's dB/dC
-// sums over its channels accumulate in its own region of the workspace (its
-// slice's partial for this batch row and chunk): each thread owns the same
-// entries in every round, loads a pair's entries before computing the pair and
-// writes them back after adding the waves' terms, so no two threads touch one
-// entry and the loads have a pair's compute time to arrive from L2.
+// sums over its channels (its slice's partial for this batch row and chunk) are
+// formed in a fixed order: per pair, every wave writes its channel's terms to its
+// own LDS slot, and after a barrier each thread adds the waves' values of the
+// entries it owns (the same entries in every round, so no two threads touch one).
+//   ACC (when it fits in LDS: N <= 16 at 8 tokens per lane): the running sums stay
+//     in an LDS accumulator across all rounds and are written to the workspace once,
+//     at the end.  The slots then hold one matrix at a time (dC after the forward
+//     replay, dB after the reverse replay), two more barriers per pair, so that tile
+//     (64 KB), slots (32 KB) and accumulator (64 KB) fit in the CU's 160 KB.
+//   otherwise: the running sums live in the workspace region; a thread loads a
+//     pair's entries before computing the pair and writes them back after adding
+//     the waves' terms, so the loads have a pair's compute time to arrive from L2.
 template <typename ACT, int KPL, int kW, int NT>
 __global__ __launch_bounds__(64 * kW) void bwd_main_kernel(BwdArgs p, BwdLayout g, int vec_flag) {
   constexpr int CH = 64 * KPL, F4 = CH / 4, Q = KPL / 4;
@@ -716,8 +724,15 @@ __global__ __launch_bounds__(64 * kW) void bwd_main_kernel(BwdArgs p, BwdLayout 
   static_assert(NT % 2 == 0, "states are processed in pairs");
   static_assert(RED4 % kThreads == 0, "every thread owns whole float4 entries");
   constexpr int RPT = RED4 / kThreads;               // entries per thread per pair
+  constexpr int kTileBytes = 2 * NT * F4 * 16, kAccBytes = (NT / 2) * RED4 * 16;
+  constexpr bool ACC = kTileBytes + kAccBytes + kW * 2 * F4 * 16 <= 160 * 1024;
+  constexpr int SLOT4 = ACC ? 2 * F4 : RED4;         // float4 per wave slot: one matrix (ACC) or both
+  constexpr int H2 = 4 * F4;                         // ACC: float2 per (pair, matrix): 2 states x chunk
+  static_assert(!ACC || H2 % kThreads == 0, "every thread owns whole float2 entries");
+  constexpr int RPT2 = H2 / kThreads;                // ACC: float2 entries per thread per (pair, matrix)
   __shared__ float4 s_tile[2 * NT * F4];
-  __shared__ float4 s_red[kW * RED4];               // per wave: its channel's terms for the current pair
+  __shared__ float4 s_red[kW * SLOT4];              // per wave: its channel's terms for the current pair
+  __shared__ float2 s_acc[ACC ? (NT / 2) * 2 * H2 : 2];   // ACC: [pair][matrix][state in pair][chunk] sums
   const bool vec = vec_flag != 0;
   const int lane = threadIdx.x & 63;
   const bool lane0 = lane == 0;
@@ -749,6 +764,31 @@ __global__ __launch_bounds__(64 * kW) void bwd_main_kernel(BwdArgs p, BwdLayout 
     const int64_t d = slice * dg + r * kW + w;
     return d < D ? d : D - 1;
   };
+  // ACC: accumulator entry e of (pair pp, matrix m) is float2 e of the two states'
+  // blocks of the chunk (state in pair e / (2 F4), then the permuted slot layout)
+  auto acc_sum = [&](int pp, int m) __attribute__((always_inline)) {
+    const float2* red2 = reinterpret_cast<const float2*>(s_red);
+    float2* acc2 = s_acc + (pp * 2 + m) * H2;
+#pragma unroll
+    for (int k = 0; k < RPT2; ++k) {
+      const int e = threadIdx.x + k * kThreads;
+      float2 sum = red2[e];
+#pragma unroll
+      for (int ww = 1; ww < kW; ++ww) {
+        const float2 v = red2[ww * H2 + e];
+        sum.x += v.x;
+        sum.y += v.y;
+      }
+      float2 a = acc2[e];
+      a.x += sum.x;
+      a.y += sum.y;
+      acc2[e] = a;
+    }
+  };
+  if constexpr (ACC) {
+    for (int e = threadIdx.x; e < (NT / 2) * 2 * H2; e += kThreads) s_acc[e] = make_float2(0.0f, 0.0f);
+  }
+
   TokenLoader<ACT, KPL> ld;
   if (vec) ld.fetch(p, (b * D + chan(0)) * L, tl);
   for (int r = 0; r < g.rounds; ++r) {
@@ -791,25 +831,30 @@ __global__ __launch_bounds__(64 * kW) void bwd_main_kernel(BwdArgs p, BwdLayout 
       const float4* sB1 = s_tile + n1 * F4;
       const float4* sC0 = s_tile + (NP + n0) * F4;
       const float4* sC1 = s_tile + (NP + n1) * F4;
-      float4* slot = s_red + w * RED4;                 // this wave's dB/dC terms for the pair
+      float4* slot = s_red + w * SLOT4;                // this wave's dB/dC terms for the pair
       // B and C are read from LDS again in each phase instead of being held in
       // registers across the pair (the compiler barrier keeps it from reusing them).
       auto reload = []() __attribute__((always_inline)) { asm volatile("" ::: "memory"); };
-      barrier_lds();                                 // the previous pair's sums have read the slots
+      if constexpr (!ACC) barrier_lds();             // the previous pair's sums have read the slots
       // this thread's accumulated entries of the pair (none yet in the first round)
-      float4 prev[RPT];
-      float* dst[RPT];
-      bool whole[RPT];
+      float4 prev[ACC ? 1 : RPT];
+      float* dst[ACC ? 1 : RPT];
+      bool whole[ACC ? 1 : RPT];
+      if constexpr (!ACC) {
 #pragma unroll
-      for (int k = 0; k < RPT; ++k) {
-        int n, m;
-        int64_t t;
-        entry(pp, threadIdx.x + k * kThreads, n, m, t);
-        dst[k] = n < N ? part + (m * N + n) * L + t : nullptr;
-        whole[k] = n < N && t + 4 <= L && L % 4 == 0;
-        prev[k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        if (r > 0 && whole[k]) prev[k] = *reinterpret_cast<const float4*>(dst[k]);
+        for (int k = 0; k < RPT; ++k) {
+          int n, m;
+          int64_t t;
+          entry(pp, threadIdx.x + k * kThreads, n, m, t);
+          dst[k] = n < N ? part + (m * N + n) * L + t : nullptr;
+          whole[k] = n < N && t + 4 <= L && L % 4 == 0;
+          prev[k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+          if (r > 0 && whole[k]) prev[k] = *reinterpret_cast<const float4*>(dst[k]);
+        }
       }
+      // slot blocks: ACC, one matrix at a time: 0 = state n0, 1 = state n1;
+      // otherwise 2 * (state in pair) + matrix
+      constexpr int kC0 = ACC ? 0 : 1, kC1 = ACC ? 1 : 3, kB0 = 0, kB1 = ACC ? 1 : 2;
 
       // forward recomputation: fold, scan, replay (h_j kept per token)
       float av0[KPL], av1[KPL], hv0[KPL], hv1[KPL];
@@ -831,6 +876,9 @@ __global__ __launch_bounds__(64 * kW) void bwd_main_kernel(BwdArgs p, BwdLayout 
       float R0 = P0, R1 = P1;
       wave_scan_pairs2(P0, h0, P1, h1);
       const float hin0 = wave_shift_up(h0, hs0), hin1 = wave_shift_up(h1, hs1);
+      // ACC: the previous pair's dB sums have read the slots (placed after the fold
+      // and scan, which do not touch them, so the waves' skew is absorbed there)
+      if constexpr (ACC) barrier_lds();
       reload();
       {
         float hh0 = hin0, hh1 = hin1;
@@ -853,9 +901,13 @@ __global__ __launch_bounds__(64 * kW) void bwd_main_kernel(BwdArgs p, BwdLayout 
             t0[k] = ts.g[j] * hh0;                     // dC terms
             t1[k] = ts.g[j] * hh1;
           }
-          slot[1 * F4 + q * 64 + lane] = make_float4(t0[0], t0[1], t0[2], t0[3]);
-          slot[3 * F4 + q * 64 + lane] = make_float4(t1[0], t1[1], t1[2], t1[3]);
+          slot[kC0 * F4 + q * 64 + lane] = make_float4(t0[0], t0[1], t0[2], t0[3]);
+          slot[kC1 * F4 + q * 64 + lane] = make_float4(t1[0], t1[1], t1[2], t1[3]);
         }
+      }
+      if constexpr (ACC) {
+        barrier_lds();                               // every wave's dC terms are in its slot
+        acc_sum(pp, 1);
       }
       // adjoint: reverse fold, reverse scan, reverse replay
       reload();
@@ -874,6 +926,7 @@ __global__ __launch_bounds__(64 * kW) void bwd_main_kernel(BwdArgs p, BwdLayout 
       wave_rscan_pairs2(R0, x0, me0, R1, x1, me1);
       float mu0 = wave_shift_down(x0, me0), mu1 = wave_shift_down(x1, me1);
       float dal0 = 0.0f, dal1 = 0.0f;
+      if constexpr (ACC) barrier_lds();              // every thread has added the dC terms
       reload();
 #pragma unroll
       for (int q = Q - 1; q >= 0; --q) {
@@ -900,33 +953,37 @@ __global__ __launch_bounds__(64 * kW) void bwd_main_kernel(BwdArgs p, BwdLayout 
           dal0 = __builtin_fmaf(e0, ts.dl[j], dal0);
           dal1 = __builtin_fmaf(e1, ts.dl[j], dal1);
         }
-        slot[0 * F4 + q * 64 + lane] = make_float4(t0[0], t0[1], t0[2], t0[3]);
-        slot[2 * F4 + q * 64 + lane] = make_float4(t1[0], t1[1], t1[2], t1[3]);
+        slot[kB0 * F4 + q * 64 + lane] = make_float4(t0[0], t0[1], t0[2], t0[3]);
+        slot[kB1 * F4 + q * 64 + lane] = make_float4(t1[0], t1[1], t1[2], t1[3]);
       }
       const float dan0 = wave_sum(dal0), dan1 = wave_sum(dal1);
       dA_v = lane == n0 ? dan0 : (lane == n1 ? dan1 : dA_v);
 
       barrier_lds();                                 // every wave's terms are in its slot
-      // the fixed-order sum over the waves' slots of the entries this thread owns
+      if constexpr (ACC) {
+        acc_sum(pp, 0);
+      } else {
+        // the fixed-order sum over the waves' slots of the entries this thread owns
 #pragma unroll
-      for (int k = 0; k < RPT; ++k) {
-        const int x = threadIdx.x + k * kThreads;
-        float4 sum = s_red[x];
+        for (int k = 0; k < RPT; ++k) {
+          const int x = threadIdx.x + k * kThreads;
+          float4 sum = s_red[x];
 #pragma unroll
-        for (int ww = 1; ww < kW; ++ww) {
-          const float4 v = s_red[ww * RED4 + x];
-          sum.x += v.x; sum.y += v.y; sum.z += v.z; sum.w += v.w;
-        }
-        if (whole[k]) {
-          sum.x += prev[k].x; sum.y += prev[k].y; sum.z += prev[k].z; sum.w += prev[k].w;
-          *reinterpret_cast<float4*>(dst[k]) = sum;
-        } else if (dst[k]) {
-          int n, m;
-          int64_t t;
-          entry(pp, x, n, m, t);
-          const float sv[4] = {sum.x, sum.y, sum.z, sum.w};
-          for (int rr = 0; rr < 4; ++rr)
-            if (t + rr < L) dst[k][rr] = (r > 0 ? dst[k][rr] : 0.0f) + sv[rr];
+          for (int ww = 1; ww < kW; ++ww) {
+            const float4 v = s_red[ww * RED4 + x];
+            sum.x += v.x; sum.y += v.y; sum.z += v.z; sum.w += v.w;
+          }
+          if (whole[k]) {
+            sum.x += prev[k].x; sum.y += prev[k].y; sum.z += prev[k].z; sum.w += prev[k].w;
+            *reinterpret_cast<float4*>(dst[k]) = sum;
+          } else if (dst[k]) {
+            int n, m;
+            int64_t t;
+            entry(pp, x, n, m, t);
+            const float sv[4] = {sum.x, sum.y, sum.z, sum.w};
+            for (int rr = 0; rr < 4; ++rr)
+              if (t + rr < L) dst[k][rr] = (r > 0 ? dst[k][rr] : 0.0f) + sv[rr];
+          }
         }
       }
     };
@@ -957,6 +1014,31 @@ __global__ __launch_bounds__(64 * kW) void bwd_main_kernel(BwdArgs p, BwdLayout 
       if (lane0) {
         g.dDp[(b * g.nchunks + c) * D + d] = dDs;
         g.dbp[(b * g.nchunks + c) * D + d] = dbs;
+      }
+    }
+  }
+  if constexpr (ACC) {
+    // the workgroup's sums, written once: float2 e of (pair pp, matrix m) holds
+    // tokens t, t + 1 of state 2 pp + e / (2 F4) (the slot layout of the terms)
+    for (int pp = 0; pp < NP / 2; ++pp) {
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+#pragma unroll
+        for (int k = 0; k < RPT2; ++k) {
+          const int e = threadIdx.x + k * kThreads;
+          const int n = 2 * pp + e / (2 * F4);
+          const int f2 = e % (2 * F4), sl = f2 >> 1;
+          const int64_t t = t0 + static_cast<int64_t>(sl % 64) * KPL + 4 * (sl / 64) + 2 * (f2 & 1);
+          if (n >= N || t >= L) continue;
+          float* dp = part + (m * N + n) * L + t;
+          const float2 v = s_acc[(pp * 2 + m) * H2 + e];
+          if (t + 2 <= L && L % 2 == 0) {
+            *reinterpret_cast<float2*>(dp) = v;
+          } else {
+            dp[0] = v.x;
+            if (t + 1 < L) dp[1] = v.y;
+          }
+        }
       }
     }
   }
