@@ -123,7 +123,7 @@ def test_named_entry_point_through_ctypes(name):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_many_channels_sampled(dtype):
+def test_many_channels_full(dtype):
     """Many channels (batch * D = 16400: 8-wave workgroups for bfloat16, 16-wave for
     float32), with D not a multiple of 16 so that the last workgroup of each row has
     idle waves."""
