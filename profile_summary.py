@@ -6,7 +6,8 @@
 
     # two counter runs (FETCH_SIZE, then WRITE_SIZE) -> profiles/traffic.json entry + text
     python3 profile_summary.py traffic --fetch-dir <dir> --write-dir <dir> --workload <workload> \\
-        --kernel <substring of the kernel's name> --out profiles/<name>.txt --command "<command lines>"
+        --kernel <substring of the kernel's name> --out profiles/<name>.txt --command "<command lines>" \\
+        [--kernels-per-call K]      # a call that launches K kernels matching the substring (the backward: 5)
 
 The counters are scaled by what they read for the calibration copy bench.py runs
 (ssm_calib_copy: 1 GiB read and 1 GiB written per dispatch), so HBM bytes per launch
@@ -76,6 +77,14 @@ def _counter_rows(d):
     return rows
 
 
+def _short_name(name):
+    for key in ("bwd_summary_tokseq_kernel", "bwd_summary_kernel", "bwd_combine_kernel", "bwd_main_kernel",
+                "bwd_param_sums_kernel", "bwd_bc_out_kernel"):
+        if key in name:
+            return key
+    return _short(name.split("(")[0])
+
+
 def _per_dispatch(rows, counter, match):
     """Per-dispatch totals of `counter` for kernels whose name contains `match`."""
     tot = {}
@@ -100,9 +109,14 @@ def traffic(args):
         cal_kib = sorted(cal.values())[len(cal) // 2]                # median calibration dispatch
         scale = CALIB_BYTES / (cal_kib * 1024.0)
         vals = list(ker.values())
-        out[counter] = {"kib_per_dispatch": sum(vals) / len(vals), "dispatches": len(vals),
+        calls = len(vals) / args.kernels_per_call
+        per_kernel = {}
+        for (_, name), v in ker.items():
+            per_kernel.setdefault(_short_name(name), []).append(v)
+        out[counter] = {"kib_per_dispatch": sum(vals) / calls, "dispatches": len(vals),
                         "calib_kib_per_dispatch": cal_kib, "scale": scale,
-                        "kernels": sorted({k[1] for k in ker})}
+                        "kernels": sorted({k[1] for k in ker}),
+                        "per_kernel_kib": {k: sum(v) / len(v) for k, v in per_kernel.items()}}
     fetch_b = out["FETCH_SIZE"]["kib_per_dispatch"] * 1024 * out["FETCH_SIZE"]["scale"]
     write_b = out["WRITE_SIZE"]["kib_per_dispatch"] * 1024 * out["WRITE_SIZE"]["scale"]
     import synth
@@ -121,14 +135,20 @@ def traffic(args):
         f.write("\n")
     lines = [f"# rocprofv3 HBM counters: {args.workload}", "", "Commands (MI355X, one GPU):"]
     lines += [f"    {c}" for c in args.command.split(" ;; ")]
-    lines += ["", "| counter | KiB per dispatch | dispatches | calibration copy KiB per dispatch (1 GiB moved) | "
-              "scale | bytes per launch |", "|---|---|---|---|---|---|"]
+    lines += ["", "| counter | KiB per call | dispatches | calibration copy KiB per dispatch (1 GiB moved) | "
+              "scale | bytes per call |", "|---|---|---|---|---|---|"]
     for counter, b in (("FETCH_SIZE", fetch_b), ("WRITE_SIZE", write_b)):
         o = out[counter]
         lines.append(f"| {counter} | {o['kib_per_dispatch']:.0f} | {o['dispatches']} | {o['calib_kib_per_dispatch']:.0f} | "
                      f"{o['scale']:.4f} | {b / 1e6:.2f} MB |")
-    lines += ["", f"HBM traffic per launch: {(fetch_b + write_b) / 1e6:.2f} MB against {alg / 1e6:.2f} MB "
-                  f"algorithmic ({(fetch_b + write_b) / alg:.3f}x).", f"Kernel: {', '.join(entry['kernels'])}"]
+    if args.kernels_per_call > 1:
+        lines += ["", "| kernel | read MB (scaled) | written MB (scaled) |", "|---|---|---|"]
+        for k in out["FETCH_SIZE"]["per_kernel_kib"]:
+            rd = out["FETCH_SIZE"]["per_kernel_kib"][k] * 1024 * out["FETCH_SIZE"]["scale"] / 1e6
+            wr = out["WRITE_SIZE"]["per_kernel_kib"].get(k, 0.0) * 1024 * out["WRITE_SIZE"]["scale"] / 1e6
+            lines.append(f"| {k} | {rd:.2f} | {wr:.2f} |")
+    lines += ["", f"HBM traffic per call: {(fetch_b + write_b) / 1e6:.2f} MB against {alg / 1e6:.2f} MB "
+                  f"algorithmic ({(fetch_b + write_b) / alg:.3f}x).", f"Kernels: {', '.join(entry['kernels'])}"]
     with open(args.out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -152,6 +172,7 @@ def main():
                                                         "kernel bench.py reports for the workload)")
     c.add_argument("--out", required=True)
     c.add_argument("--command", required=True)
+    c.add_argument("--kernels-per-call", type=int, default=1)
     a = ap.parse_args()
     trace(a) if a.cmd == "trace" else traffic(a)
 
