@@ -142,8 +142,8 @@ ssm_status ssm_selective_scan_fwd_from_state(
  * runs the token-sequential kernel, whose lanes own states and walk the tokens in
  * order (N == 16, L % 8 == 0, 16-byte aligned activations, B and C; else
  * SSM_ERR_UNSUPPORTED).  `tokens_per_lane` (0 = default) selects the chunked
- * kernel's tokens per lane (8 or 16), and for SSM_SCAN_TOKSEQ the states per lane
- * (4 or 2).  Other arguments as in ssm_selective_scan_fwd_from_state.
+ * kernel's tokens per lane (8, 12 or 16; 12 is built without the full ZOH and the
+ * fused conv), and for SSM_SCAN_TOKSEQ the states per lane (4 or 2).  Other arguments as in ssm_selective_scan_fwd_from_state.
  */
 typedef enum {
   SSM_SCAN_AUTO = 0,

@@ -72,8 +72,8 @@ template <typename ACT, bool GATE, int KPL, bool VEC, int NBLK, int kNB, int kW,
 __global__ __launch_bounds__(64 * kW) void scan_chunked_kernel(ScanArgs p, int n_dblk) {
   constexpr int kThreads = 64 * kW;
   static_assert(KPL >= 3, "the fused conv takes its 3 earlier tokens from the previous lane");
-  // states processed two at a time where the registers allow it (8 tokens per lane)
-  constexpr bool PAIR = KPL <= 8;
+  // states processed two at a time where the registers allow it (8 or 12 tokens per lane)
+  constexpr bool PAIR = KPL <= 12;
   // The arithmetic-progression build exists for bfloat16 12-wave N == 16 vector-load
   // kernels only: its running powers take about 40 more registers, which the
   // one-workgroup-per-CU 12-wave launch has to spare; in the 8- and 16-wave groups,
@@ -678,7 +678,7 @@ hipError_t launch_w(const ScanArgs& a, hipStream_t s) {
   // N == 16, bfloat16, 8 tokens per lane: 8 states per step (two steps per
   // chunk, half the barriers; measured 2 % faster).  float32 measured no faster
   // that way, and at 16 tokens per lane the larger tile's registers would spill.
-  constexpr int N16_STEPS = (ACT::kBytes == 2 && KPL <= 8) ? 2 : 4;
+  constexpr int N16_STEPS = (ACT::kBytes == 2 && KPL <= 12) ? 2 : 4;
   if constexpr (ACT::kBytes == 2 && W == 12 && KPL == 8 && !CONV && !ZOH) {
     if (vec && n16 && a.ap) {
       hipLaunchKernelGGL((scan_chunked_kernel<ACT, GATE, KPL, true, N16_STEPS, 16 / N16_STEPS, W, CONV, ZOH, true>),
@@ -734,30 +734,41 @@ hipError_t launch_gate(const ScanArgs& a, int kpl, hipStream_t s) {
   const bool conv = a.conv_w != nullptr;
   if (a.zoh) return launch_kpl<ACT, GATE, 8, false, true>(a, s);   // (8 tokens per lane, no conv: see chunked_supported)
   if (kpl == 8) return conv ? launch_kpl<ACT, GATE, 8, true, false>(a, s) : launch_kpl<ACT, GATE, 8, false, false>(a, s);
+  if (kpl == 12) return launch_kpl<ACT, GATE, 12, false, false>(a, s);   // (no conv: see chunked_supported)
   return conv ? launch_kpl<ACT, GATE, 16, true, false>(a, s) : launch_kpl<ACT, GATE, 16, false, false>(a, s);
 }
 
 // Default tokens per lane, from measurement on gfx950: 8, where the registers
 // leave room to run two states at once, beats 16 (half the wave-scan overhead
-// per element, one state at a time) for both activation types.
-int resolve_kpl(int tokens_per_lane, Dt) {
-  return tokens_per_lane != 0 ? tokens_per_lane : 8;
+// per element, one state at a time) for both activation types.  12 still runs
+// two states at once in the 12-wave launch (bfloat16, N == 16, 168 registers) and
+// spends a third less on the wave scan per element: 2.7 % faster on a 131072-token
+// sequence (1869 against 1920 us).  Its 768-token chunks pad a short sequence
+// (2048 tokens: 12.5 % padding), so it is the default from 32768 tokens, and not
+// with the arithmetic-progression path, whose build is for 8.
+int resolve_kpl(const ScanArgs& a, int tokens_per_lane, Dt dt) {
+  if (tokens_per_lane != 0) return tokens_per_lane;
+  const bool twelve = dt == Dt::BF16 && a.N == 16 && !a.zoh && a.conv_w == nullptr && !a.ap && a.L >= 32768 &&
+                      a.batch * a.D <= 12 * 256 && vec_path(a, 12);
+  return twelve ? 12 : 8;
 }
 
 }  // namespace
 
 bool chunked_supported(const ScanArgs& a, Dt, int tokens_per_lane) {
-  if (!(tokens_per_lane == 0 || tokens_per_lane == 8 || tokens_per_lane == 16)) return false;
+  if (!(tokens_per_lane == 0 || tokens_per_lane == 8 || tokens_per_lane == 12 || tokens_per_lane == 16)) return false;
   if (a.N < 1 || a.N > 64) return false;
   // the full zero-order hold is built for the default 8 tokens per lane without the fused conv
-  if (a.zoh && (a.conv_w != nullptr || tokens_per_lane == 16)) return false;
+  if (a.zoh && (a.conv_w != nullptr || tokens_per_lane == 16 || tokens_per_lane == 12)) return false;
+  // 12 tokens per lane is built without the fused conv
+  if (a.conv_w != nullptr && tokens_per_lane == 12) return false;
   const int64_t n_dblk = (a.D + 8 - 1) / 8;                  // the most workgroups any launch uses (8 waves each)
   return a.batch * n_dblk <= 0x7fffffff;
 }
 
 hipError_t launch_scan_chunked(const ScanArgs& a, Dt dt, int tokens_per_lane, hipStream_t s) {
   if (!chunked_supported(a, dt, tokens_per_lane)) return hipErrorInvalidValue;
-  const int kpl = resolve_kpl(tokens_per_lane, dt);
+  const int kpl = resolve_kpl(a, tokens_per_lane, dt);
   const bool gate = a.z != nullptr;
   if (dt == Dt::F32)
     return gate ? launch_gate<ActF32, true>(a, kpl, s) : launch_gate<ActF32, false>(a, kpl, s);

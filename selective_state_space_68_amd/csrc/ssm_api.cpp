@@ -197,7 +197,7 @@ namespace {
 // per lane of the token-sequential kernel (2 or 4); 0 = default.
 bool kernel_option_ok(int variant, int tokens_per_lane) {
   if (variant == SSM_SCAN_TOKSEQ) return tokens_per_lane == 0 || tokens_per_lane == 2 || tokens_per_lane == 4;
-  return tokens_per_lane == 0 || tokens_per_lane == 8 || tokens_per_lane == 16;
+  return tokens_per_lane == 0 || tokens_per_lane == 8 || tokens_per_lane == 12 || tokens_per_lane == 16;
 }
 
 // The kernel a scan with these arguments runs (L > 0): SSM_SCAN_SEQUENTIAL,

@@ -100,7 +100,7 @@ def _step(lib, **kw):
     (dict(dt=7), _lib.SSM_ERR_UNSUPPORTED),
     (dict(softplus=2), _lib.SSM_ERR_INVALID_ARG),
     (dict(variant=9), _lib.SSM_ERR_UNSUPPORTED),
-    (dict(kpl=12), _lib.SSM_ERR_UNSUPPORTED),
+    (dict(kpl=10), _lib.SSM_ERR_UNSUPPORTED),
     (dict(u=F + 2), _lib.SSM_ERR_INVALID_ARG),                       # misaligned f32
     (dict(dt=1, u=F + 1), _lib.SSM_ERR_INVALID_ARG),                 # misaligned bf16
     (dict(y=F), _lib.SSM_ERR_INVALID_ARG),                           # y aliases u
@@ -366,6 +366,10 @@ def test_scan_kernel_choice(lib):
     assert k(1, 64, 16, 16, F32, 0, 0, 0, TOK, 2) == TOK                  # asked for: any supported size
     assert k(1, 100, 16, 16, F32, 0, 0, 0, TOK, 0) == -_lib.SSM_ERR_UNSUPPORTED
     assert k(1, 64, 16, 16, F32, 0, 0, 0, TOK, 8) == -_lib.SSM_ERR_UNSUPPORTED   # states per lane: 2 or 4
+    assert k(1, 64, 16, 16, BF16, 1, 0, 0, CHK, 12) == CHK                # 12 tokens per lane
+    assert k(1, 64, 16, 16, BF16, 1, 0, 4, 0, 12) == -_lib.SSM_ERR_UNSUPPORTED   # not with the fused conv
+    assert k(1, 64, 16, 16, BF16, 1, 1, 0, 0, 12) == -_lib.SSM_ERR_UNSUPPORTED   # nor the full ZOH
+    assert k(1, 64, 16, 16, BF16, 1, 0, 0, CHK, 10) == -_lib.SSM_ERR_UNSUPPORTED
     assert k(1, 64, 16, 65, F32, 0, 0, 0, 0, 0) == -_lib.SSM_ERR_UNSUPPORTED
     assert k(1, 64, 16, 16, F32, 0, 0, 0, 7, 0) == -_lib.SSM_ERR_UNSUPPORTED
     # the arithmetic-progression flag does not change the kernel

@@ -50,7 +50,7 @@ def test_initial_state_all_variants(shape):
     ry, rf = _oracle(inp, h0.astype(np.float64))
     t = upload_scan(inp)
     th0 = dev(h0)
-    for variant, kpl in ((0, 0), (1, 0), (2, 8), (2, 16)):
+    for variant, kpl in ((0, 0), (1, 0), (2, 8), (2, 12), (2, 16)):
         y, fs = selective_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["bias"],
                                    inp.delta_softplus, initial_state=th0, variant=variant, tokens_per_lane=kpl)
         ey, ef = row_rel_err(host(y), ry), row_rel_err(host(fs), rf)

@@ -46,7 +46,7 @@ def test_tiny_f32_all_variants():
     inp = synth.make_config_inputs(cfg)
     ry, rf = oracle_scan(inp)
     t = upload_scan(inp)
-    for variant, kpl in ((0, 0), (1, 0), (2, 8), (2, 16)):
+    for variant, kpl in ((0, 0), (1, 0), (2, 8), (2, 12), (2, 16)):
         y, fs = run_scan(inp, t, variant=variant, tokens_per_lane=kpl)
         _check(host(y), host(fs), ry, rf, cfg.dtype, f"tiny v{variant}/{kpl}")
 
@@ -215,7 +215,7 @@ def test_edge_shapes_all_variants(shape):
         inp.refresh()
     ry, rf = oracle_scan(inp)
     t = upload_scan(inp)
-    for variant, kpl in ((0, 0), (1, 0), (2, 8), (2, 16)):
+    for variant, kpl in ((0, 0), (1, 0), (2, 8), (2, 12), (2, 16)):
         y, fs = run_scan(inp, t, variant=variant, tokens_per_lane=kpl)
         _check(host(y), host(fs), ry, rf, dtype, f"{shape} v{variant}/{kpl}")
 
