@@ -600,10 +600,23 @@ __global__ __launch_bounds__(64 * kW) void scan_chunked_kernel(ScanArgs p, int n
     // its own block also keeps the compiler from scheduling it into the
     // surrounding per-token code, which costs registers)
     if (valid) {
-      if constexpr (ROWS)
+      if constexpr (ROWS) {
         states(s_tile[c & 1] + nb * kNB * 2 * BLK4, nb);
-      else
+      } else if constexpr (2 * TILE4 * 16 > 65536) {
+        // Buffers past the 64 KB reach of an LDS read's immediate offset (48 KB
+        // each at 12 tokens per lane): the buffer's offset goes through a scalar
+        // register the compiler cannot see into, so each step forms one base
+        // address and every read of the tile is an immediate offset from it.  With
+        // the constant folded in, every read of the second buffer's upper blocks
+        // needed an address instruction of its own (32 VALU per step).  Where the
+        // tiles fit in 64 KB the constant is better (measured 1.3 % slower
+        // opaque).
+        int toff = par * TILE4;
+        asm volatile("" : "+s"(toff));
+        states(&s_tile[0][0] + toff, nb);
+      } else {
         states(s_tile[par], nb);
+      }
     }
     if (!tail1) store_tile(par ^ 1);
     barrier_lds();
