@@ -226,7 +226,8 @@ __global__ __launch_bounds__(64 * kW) void scan_chunked_kernel(ScanArgs p, int n
     }
     if (p.softplus) {
 #pragma unroll
-      for (int j = 0; j < KPL; ++j) dl[j] = softplus_f(dl[j] + bias);
+      for (int j = 0; j < KPL; ++j)
+        dl[j] = ACT::kBytes == 2 ? softplus_bf16act(dl[j] + bias) : softplus_f(dl[j] + bias);
     } else {
 #pragma unroll
       for (int j = 0; j < KPL; ++j) dl[j] = dl[j] + bias;
