@@ -70,14 +70,19 @@ KERNEL_SRC = {"scan_chunked_kernel": _CSRC + "scan_chunked.hip", "scan_tokseq_ke
               "state_update_vec_kernel": _CSRC + "state_update.hip", "ssd_scan_kernel": _CSRC + "ssd.hip"}
 KERNEL_NAME = {"decode": "state_update_vec_kernel",
                "bwd": "scan backward call (bwd_summary, bwd_combine, bwd_main, bwd_param_sums, bwd_bc_out kernels)",
+               "bwd_saved": "scan backward call with saved chunk states (bwd_main chunk walk, bwd_param_sums, "
+                            "bwd_bc_out kernels)",
                "ssd": "ssd_scan_kernel"}
 KERNEL_SRC[KERNEL_NAME["bwd"]] = _CSRC + "scan_bwd.hip"
+KERNEL_SRC[KERNEL_NAME["bwd_saved"]] = _CSRC + "scan_bwd.hip"
 PEAK_MFMA_BF16_TFLOPS = 2500.0
 
 
 def kernel_of(cfg, kind, variant=0, tokens_per_lane=0):
     """The kernel (or, for the backward, the call) a workload's timed region runs.
     The forward scan asks the library which kernel it picks for the shape."""
+    if kind == "bwd" and cfg.saved:
+        return KERNEL_NAME["bwd_saved"]
     if kind != "scan":
         return KERNEL_NAME[kind]
     import torch
@@ -293,18 +298,24 @@ def prepare(name, args, torch, lib_ops):
         dyv, dyup, _ = synth.make_scan_cotangents(cfg.batch, cfg.L, cfg.D, cfg.N, cfg.dtype, seed=cfg.seed)
         inp.dy = dyv
         act = bufs[0]["u"].dtype
-        ws = torch.empty((lib_ops.selective_scan_bwd_workspace_size(cfg.batch, cfg.L, cfg.D, cfg.N, act),),
+        ws = torch.empty((lib_ops.selective_scan_bwd_workspace_size(cfg.batch, cfg.L, cfg.D, cfg.N, act,
+                                                                    saved=cfg.saved),),
                          dtype=torch.uint8, device="cuda")
         grads = None
         for t in bufs:
             t["dy"] = dev(torch, dyup)
+            t["cs"] = None
+            if cfg.saved:   # the forward pass that saves the chunk states runs once, before the timing
+                _, _, t["cs"] = lib_ops.selective_scan_fwd_save(t["u"], t["delta"], A, t["B"], t["C"], Dk, t["z"],
+                                                                bias, True, y=t["y"], final_state=t["fs"])
             del t["y"], t["fs"]
+        torch.cuda.synchronize()
 
         def step(i):
             nonlocal grads
             t = bufs[i % sets]
             grads = lib_ops.selective_scan_bwd(t["u"], t["delta"], A, t["B"], t["C"], t["dy"], Dk, t["z"], bias,
-                                               True, workspace=ws, out=grads)
+                                               True, workspace=ws, out=grads, chunk_states=t["cs"])
             t["g"] = grads
         return cfg, inp, kind, nbytes, cfg.elements, sets, step, bufs
 

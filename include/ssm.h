@@ -331,6 +331,60 @@ ssm_status ssm_selective_scan_bwd(
     void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Training pair with saved chunk states: a forward scan that also stores the state
+ * entering every SSM_SAVE_CHUNK-token chunk, and a backward pass that reads those
+ * states instead of recomputing them.  The recomputation trade of the slide deck on
+ * Mamba's fused kernel (keep the inputs, rebuild the states) is kept inside each
+ * chunk; across chunks the backward pass starts from the stored states, so it no
+ * longer needs a pass over the whole sequence to find them.  The stored states are
+ * batch * D * ceil(L / 512) * N floats: at N = 16 a sixteenth of the size of u in
+ * bfloat16 (8 MB for batch 8, D 4096, L 2048).
+ *
+ * ssm_selective_scan_fwd_save: as ssm_selective_scan_fwd_from_state (same inputs,
+ * outputs and errors), plus
+ *   chunk_states : out [batch][D][ceil(L / SSM_SAVE_CHUNK)][N] float32, 16-byte
+ *                  aligned, owned by the caller; entry c is the state entering
+ *                  token c * SSM_SAVE_CHUNK (entry 0: initial_state, or zeros).
+ *                  NULL is invalid for a nonempty call; it must not overlap any
+ *                  other buffer.
+ * N above 16 is SSM_ERR_UNSUPPORTED.  y and final_state are the ones
+ * ssm_selective_scan_fwd_from_state gives (the same kernels' arithmetic; the
+ * chunked kernel runs at 8 tokens per lane).
+ *
+ * ssm_selective_scan_bwd_saved: as ssm_selective_scan_bwd (same inputs, outputs,
+ * determinism and errors), plus
+ *   chunk_states : [batch][D][ceil(L / SSM_SAVE_CHUNK)][N] float32, what
+ *                  ssm_selective_scan_fwd_save wrote for these same inputs (the
+ *                  call cannot check this; other contents give wrong gradients).
+ *                  NULL is invalid for a nonempty call.
+ * Workspace: ssm_selective_scan_bwd_saved_workspace_size(...) bytes.  With
+ * N <= 16 and batch * D >= 16384 (enough channels to fill the device without
+ * splitting the sequence) the pass walks each channel's chunks from the last to
+ * the first, one read of every input; other shapes ignore chunk_states and run the
+ * ssm_selective_scan_bwd decomposition.  The gradients match ssm_selective_scan_bwd's
+ * to float32 rounding (the states are summed in a different order), not bitwise.
+ */
+#define SSM_SAVE_CHUNK 512
+
+ssm_status ssm_selective_scan_fwd_save(
+    const void *u, const void *delta, const float *A, const void *Bm, const void *Cm,
+    const float *Dskip, const void *z, const float *delta_bias, int delta_softplus,
+    const float *initial_state, void *y, float *final_state, float *chunk_states,
+    int64_t batch, int64_t L, int64_t D, int64_t N, ssm_dtype dt,
+    void *workspace, size_t workspace_bytes, void *stream);
+
+size_t ssm_selective_scan_bwd_saved_workspace_size(int64_t batch, int64_t L, int64_t D, int64_t N, ssm_dtype dt);
+
+ssm_status ssm_selective_scan_bwd_saved(
+    const void *u, const void *delta, const float *A, const void *Bm, const void *Cm,
+    const float *Dskip, const void *z, const float *delta_bias, int delta_softplus,
+    const float *initial_state, const void *dy, const float *dfinal_state, const float *chunk_states,
+    void *du, void *ddelta, float *dA, void *dB, void *dC, float *dD, void *dz,
+    float *ddelta_bias, float *dinitial_state,
+    int64_t batch, int64_t L, int64_t D, int64_t N, ssm_dtype dt,
+    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Mamba-2 SSD scan: a scalar decay per head (the slide deck's "Mamba-2" table; the
  * interview-prep page's "Mamba-2 and State Space Duality").  For batch b, time t,
  * head h, head channel p and state n:

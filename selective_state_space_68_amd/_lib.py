@@ -55,6 +55,12 @@ SIGNATURES = {
     "ssm_selective_scan_bwd": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _vp, _vp, _vp,
                                       _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                       _i64, _i64, _i64, _i64, _int, _vp, _sz, _vp]),
+    "ssm_selective_scan_fwd_save": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _vp, _vp, _vp, _vp,
+                                           _i64, _i64, _i64, _i64, _int, _vp, _sz, _vp]),
+    "ssm_selective_scan_bwd_saved_workspace_size": (_sz, [_i64, _i64, _i64, _i64, _int]),
+    "ssm_selective_scan_bwd_saved": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _vp, _vp, _vp, _vp,
+                                            _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                            _i64, _i64, _i64, _i64, _int, _vp, _sz, _vp]),
     "ssm_ssd_scan_workspace_size": (_sz, [_i64, _i64, _i64, _i64, _i64, _int]),
     "ssm_ssd_scan_fwd": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _vp, _vp, _vp,
                                 _i64, _i64, _i64, _i64, _i64, _int, _vp, _sz, _vp]),

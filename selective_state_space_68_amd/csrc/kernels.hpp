@@ -33,7 +33,16 @@ struct ScanArgs {
   int zoh = 0;           // 1: full zero-order hold, input term (exp(Delta A) - 1)/A * B * u
   int ap = 0;            // 1: the arithmetic-progression decay path where a kernel has it
                          //    (SSM_SCAN_AP)
+  // [batch][D][ceil(L / kSaveChunk)][N] float32, or null: the state entering each
+  // kSaveChunk-token chunk (entry 0 is the initial state), for the backward pass
+  // (N <= 16; written by the chunked kernel at 8 tokens per lane, the
+  // token-sequential kernel and the sequential kernel)
+  float* chunk_states = nullptr;
 };
+
+// Tokens per chunk of the saved forward states: the backward pass's chunk at
+// N <= 16 (64 lanes x 8 tokens).
+constexpr int kSaveChunk = SSM_SAVE_CHUNK;
 
 struct ConvArgs {
   const void* x;       // [batch][D][L] act
@@ -84,6 +93,9 @@ struct BwdArgs {
   void* dz;               // [batch][D][L] act or null (null whenever z is null)
   float* dbias;           // [D] or null
   float* dh0;             // [batch][D][N] or null
+  // [batch][D][ceil(L / kSaveChunk)][N] or null: the forward pass's saved states
+  // entering every kSaveChunk-token chunk (entry 0: the initial state)
+  const float* chunk_states = nullptr;
   int64_t batch, L, D;
   int N;
   int softplus;
@@ -130,6 +142,9 @@ hipError_t launch_scan_sequential(const ScanArgs& a, Dt dt, hipStream_t s);
 // Chunked wave-scan kernel.  Returns hipErrorInvalidValue when the shape does not
 // fit (callers check chunked_supported first).
 bool chunked_supported(const ScanArgs& a, Dt dt, int tokens_per_lane);
+// Whether the chunked kernel has a build that saves the chunk states for this shape
+// (N == 16 on the vector path); other shapes save through the sequential kernel.
+bool chunked_save_supported(const ScanArgs& a);
 hipError_t launch_scan_chunked(const ScanArgs& a, Dt dt, int tokens_per_lane, hipStream_t s);
 
 // Token-sequential kernel for many channels: N == 16, L % 8 == 0, 16-byte aligned
@@ -143,8 +158,9 @@ hipError_t launch_scan_tokseq(const ScanArgs& a, Dt dt, int states_per_lane, hip
 // final_state = initial state, or zeros when src is null (the L == 0 scan).
 hipError_t launch_copy_state(float* dst, const float* src, int64_t n, hipStream_t s);
 
-// Backward pass (batch, L, D > 0): float32 workspace of scan_bwd_workspace_bytes.
-size_t scan_bwd_workspace_bytes(int64_t batch, int64_t L, int64_t D, int N);
+// Backward pass (batch, L, D > 0): float32 workspace of scan_bwd_workspace_bytes
+// (saved: the forward pass's chunk states come with the call, BwdArgs::chunk_states).
+size_t scan_bwd_workspace_bytes(int64_t batch, int64_t L, int64_t D, int N, bool saved);
 bool scan_bwd_grid_ok(int64_t batch, int64_t L, int64_t D, int N);
 hipError_t launch_scan_bwd(const BwdArgs& a, Dt dt, void* workspace, hipStream_t s);
 

@@ -35,6 +35,13 @@
 //   4. finalize: fixed-order sums of the per-(b, chunk) partials of dA, dD and the
 //      delta bias; dB and dC from float32 to the activation dtype.
 //
+// With the forward pass's saved chunk states (the state entering every 512-token
+// chunk, written by the forward kernels' SAVE builds) and enough channels to fill
+// the chip without splitting the sequence, steps 1 and 2 go: the main kernel's SEQ
+// build walks each workgroup's chunks from the last to the first, takes the
+// entering state from the saved states and the entering adjoint from the chunk it
+// processed before, and so reads every input once.
+//
 // A workgroup of kW waves owns one (batch row, chunk) pair and a slice of
 // kW * rounds channels (about one workgroup per CU): it stages the chunk's B and C
 // once in LDS (float32, permuted so that each lane's tokens are contiguous), and
@@ -112,6 +119,47 @@ BwdLayout bwd_layout(int64_t batch, int64_t L, int64_t D, int N, float* ws) {
   }
   return g;
 }
+
+// The chunk walk (bwd_main_kernel's SEQ build, from saved forward states): a
+// workgroup per (batch row, slice of 8 * rounds channels), with the rounds chosen
+// for about 256 workgroups.  Workspace: the carried adjoints (batch * D * N), the
+// per-chunk dA partials, the per-slice dB/dC partials and the per-chunk dD and bias
+// partials.
+BwdLayout bwd_layout_seq(int64_t batch, int64_t L, int64_t D, int N, float* ws) {
+  BwdLayout g{};
+  g.kpl = 8;
+  g.waves = kWFast;
+  const int64_t CH = 64 * g.kpl, W = g.waves;
+  g.nchunks = (L + CH - 1) / CH;
+  constexpr int64_t kTargetGroups = 256;
+  int64_t r = (batch * D + W * kTargetGroups - 1) / (W * kTargetGroups);
+  const int64_t rmax = (D + W - 1) / W;
+  r = r < 1 ? 1 : (r > rmax ? rmax : r);
+  g.rounds = static_cast<int>(r);
+  g.nslices = (D + W * r - 1) / (W * r);
+  const int64_t cs = align64(batch * D * N), pp = align64(batch * g.nchunks * D * N);
+  const int64_t pt = align64(g.nslices * batch * 2 * N * L), pd = align64(batch * g.nchunks * D);
+  if (ws) {
+    g.F = nullptr;
+    g.X = ws;
+    g.P = g.X + cs;
+    g.part = g.P + pp;
+    g.dDp = g.part + pt;
+    g.dbp = g.dDp + pd;
+  }
+  return g;
+}
+
+size_t bwd_seq_ws_floats(int64_t batch, int64_t L, int64_t D, int N) {
+  const BwdLayout g = bwd_layout_seq(batch, L, D, N, nullptr);
+  return static_cast<size_t>(align64(batch * D * N) + align64(batch * g.nchunks * D * N) +
+                             align64(g.nslices * batch * 2 * N * L) + 2 * align64(batch * g.nchunks * D));
+}
+
+// The chunk walk replaces the summary where the channels alone give every CU at
+// least 8 rounds of work (from 16384 channels); with fewer, the chunk-parallel
+// decomposition keeps the chip full.
+bool bwd_seq_suits(int64_t batch, int64_t D, int N) { return bwd_fast(N) && batch * D >= 16384; }
 
 size_t bwd_ws_floats(int64_t batch, int64_t L, int64_t D, int N) {
   const BwdLayout g = bwd_layout(batch, L, D, N, nullptr);
@@ -716,7 +764,14 @@ __global__ void bwd_combine_kernel(BwdArgs p, BwdLayout g) {
 //   otherwise: the running sums live in the workspace region; a thread loads a
 //     pair's entries before computing the pair and writes them back after adding
 //     the waves' terms, so the loads have a pair's compute time to arrive from L2.
-template <typename ACT, int KPL, int kW, int NT>
+//
+// SEQ (with the forward pass's saved chunk states, p.chunk_states): a workgroup owns
+// one batch row and a channel slice and walks the chunks from the last to the
+// first.  The state entering each chunk comes from the saved states and the
+// adjoint entering it from the right is the one the workgroup's previous chunk sent
+// left (kept per channel in the workspace, g.X, by the lane that reads it next), so
+// no summary or combine pass is needed and every input is read once.
+template <typename ACT, int KPL, int kW, int NT, bool SEQ = false>
 __global__ __launch_bounds__(64 * kW) void bwd_main_kernel(BwdArgs p, BwdLayout g, int vec_flag) {
   constexpr int CH = 64 * KPL, F4 = CH / 4, Q = KPL / 4;
   constexpr int kThreads = 64 * kW;
@@ -737,13 +792,15 @@ __global__ __launch_bounds__(64 * kW) void bwd_main_kernel(BwdArgs p, BwdLayout 
   const int lane = threadIdx.x & 63;
   const bool lane0 = lane == 0;
   const int w = uniform_int(threadIdx.x >> 6);
-  const int64_t nbc = p.batch * g.nchunks;
+  static_assert(!SEQ || ACC, "the chunk walk keeps its sums in the LDS accumulator");
+  const int64_t nbc = SEQ ? p.batch : p.batch * g.nchunks;
   const int64_t bc = blockIdx.x % nbc, slice = blockIdx.x / nbc;
-  const int64_t b = bc % p.batch, c = bc / p.batch;
+  const int64_t b = bc % p.batch;
+  int64_t c = SEQ ? g.nchunks - 1 : bc / p.batch;   // SEQ: from the last chunk to the first
   const int N = p.N;
   const int NP = (N + 1) & ~1;
   const int64_t L = p.L, D = p.D;
-  const int64_t t0 = c * CH;
+  int64_t t0 = c * CH;
   load_tile<ACT, KPL>(s_tile, p, b, t0, NP, vec);
 
   // Entry x (< RED4) of a pair: block x / F4 = 2 * (state within the pair) +
@@ -758,7 +815,7 @@ __global__ __launch_bounds__(64 * kW) void bwd_main_kernel(BwdArgs p, BwdLayout 
   };
   __syncthreads();
 
-  const int64_t tl = t0 + static_cast<int64_t>(lane) * KPL;
+  int64_t tl = t0 + static_cast<int64_t>(lane) * KPL;
   const int64_t dg = static_cast<int64_t>(kW) * g.rounds;
   auto chan = [&](int r) __attribute__((always_inline)) -> int64_t {
     const int64_t d = slice * dg + r * kW + w;
@@ -785,12 +842,23 @@ __global__ __launch_bounds__(64 * kW) void bwd_main_kernel(BwdArgs p, BwdLayout 
       acc2[e] = a;
     }
   };
+  TokenLoader<ACT, KPL> ld;
+  if (vec) ld.fetch(p, (b * D + chan(0)) * L, tl);
+  for (int64_t ci = 0; ci < (SEQ ? g.nchunks : 1); ++ci) {
+  if constexpr (SEQ) {
+    if (ci > 0) {
+      // every wave is past the previous chunk's last tile read (its last pair's
+      // final barrier), so the next tile can be staged
+      c = g.nchunks - 1 - ci;
+      t0 = c * CH;
+      tl = t0 + static_cast<int64_t>(lane) * KPL;
+      load_tile<ACT, KPL>(s_tile, p, b, t0, NP, vec);
+      __syncthreads();
+    }
+  }
   if constexpr (ACC) {
     for (int e = threadIdx.x; e < (NT / 2) * 2 * H2; e += kThreads) s_acc[e] = make_float2(0.0f, 0.0f);
   }
-
-  TokenLoader<ACT, KPL> ld;
-  if (vec) ld.fetch(p, (b * D + chan(0)) * L, tl);
   for (int r = 0; r < g.rounds; ++r) {
     // A wave past the last channel runs the last channel with zero g and Delta*u:
     // it takes part in the barriers and adds only zeros.
@@ -805,11 +873,28 @@ __global__ __launch_bounds__(64 * kW) void bwd_main_kernel(BwdArgs p, BwdLayout 
       ld.get(p, row, tl, vec, ts.u, ts.dl, dy, z);
       ts.set(p, tl, valid, p.bias ? p.bias[d] : 0.0f, dy, z);
     }
-    if (vec && r + 1 < g.rounds) ld.fetch(p, (b * D + chan(r + 1)) * L, tl);   // next round's inputs
+    if (vec && r + 1 < g.rounds) {
+      ld.fetch(p, (b * D + chan(r + 1)) * L, tl);   // next round's inputs
+    } else if (SEQ && vec && c > 0) {
+      ld.fetch(p, (b * D + chan(0)) * L, (c - 1) * CH + static_cast<int64_t>(lane) * KPL);   // next chunk's
+    }
     const float A_v = lane < N ? p.A[d * N + lane] : 0.0f;
     const float a2_v = A_v * kLog2e;
-    const float hs_v = lane < N ? g.F[soff + lane] : 0.0f;
-    const float mu_v = lane < N ? g.X[soff + lane] : 0.0f;
+    float hs_v = 0.0f, mu_v = 0.0f;
+    if constexpr (SEQ) {
+      // the saved state entering chunk c; the adjoint entering it from the right:
+      // the final state's cotangent for the last chunk, else what chunk c + 1 sent
+      // (a wave past the last channel takes zeros: it reads nothing another wave writes)
+      const int64_t cidx = (b * D + d) * N + lane;
+      if (lane < N && valid) {
+        hs_v = p.chunk_states[((b * D + d) * g.nchunks + c) * N + lane];
+        mu_v = c == g.nchunks - 1 ? (p.dfinal ? p.dfinal[cidx] : 0.0f) : g.X[cidx];
+      }
+    } else {
+      hs_v = lane < N ? g.F[soff + lane] : 0.0f;
+      mu_v = lane < N ? g.X[soff + lane] : 0.0f;
+    }
+    float mu_out_v = 0.0f;                            // SEQ: lane n, the adjoint this chunk sends left
     float s1[KPL], s2[KPL], yt[KPL];
 #pragma unroll
     for (int j = 0; j < KPL; ++j) {
@@ -956,6 +1041,12 @@ __global__ __launch_bounds__(64 * kW) void bwd_main_kernel(BwdArgs p, BwdLayout 
         slot[kB0 * F4 + q * 64 + lane] = make_float4(t0[0], t0[1], t0[2], t0[3]);
         slot[kB1 * F4 + q * 64 + lane] = make_float4(t1[0], t1[1], t1[2], t1[3]);
       }
+      if constexpr (SEQ) {
+        // lane 0's adjoint after its first token is what this chunk sends to the one before
+        const float o0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mu0), 0));
+        const float o1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mu1), 0));
+        mu_out_v = lane == n0 ? o0 : (lane == n1 ? o1 : mu_out_v);
+      }
       const float dan0 = wave_sum(dal0), dan1 = wave_sum(dal1);
       dA_v = lane == n0 ? dan0 : (lane == n1 ? dan1 : dA_v);
 
@@ -1015,6 +1106,16 @@ __global__ __launch_bounds__(64 * kW) void bwd_main_kernel(BwdArgs p, BwdLayout 
         g.dDp[(b * g.nchunks + c) * D + d] = dDs;
         g.dbp[(b * g.nchunks + c) * D + d] = dbs;
       }
+      if constexpr (SEQ) {
+        // the adjoint sent to chunk c - 1 (read back by this lane for it), or past
+        // the first token the gradient of the initial state
+        if (lane < N) {
+          if (c > 0)
+            g.X[(b * D + d) * N + lane] = mu_out_v;
+          else if (p.dh0)
+            p.dh0[(b * D + d) * N + lane] = mu_out_v;
+        }
+      }
     }
   }
   if constexpr (ACC) {
@@ -1042,6 +1143,7 @@ __global__ __launch_bounds__(64 * kW) void bwd_main_kernel(BwdArgs p, BwdLayout 
       }
     }
   }
+  }  // chunks (SEQ: from the last to the first)
 }
 
 // ---- 4. fixed-order sums and dtype conversion ---------------------------------------
@@ -1126,6 +1228,22 @@ hipError_t launch_bwd_typed(const BwdArgs& a, const BwdLayout& g, hipStream_t s)
 }
 
 template <typename ACT>
+hipError_t launch_bwd_seq(const BwdArgs& a, const BwdLayout& g, hipStream_t s) {
+  const bool vec = (a.L % 8 == 0) && aligned16(a.u) && aligned16(a.delta) && aligned16(a.dy) &&
+                   (a.z == nullptr || aligned16(a.z)) && aligned16(a.du) && aligned16(a.ddelta) &&
+                   (a.dz == nullptr || aligned16(a.dz)) && aligned16(a.Bm) && aligned16(a.Cm);
+  const int64_t blocks = a.batch * g.nslices;
+  hipLaunchKernelGGL((bwd_main_kernel<ACT, 8, kWFast, kNMaxFast, true>), dim3(static_cast<unsigned>(blocks)),
+                     dim3(64 * kWFast), 0, s, a, g, vec ? 1 : 0);
+  const int64_t np = a.D * a.N + 2 * a.D;
+  hipLaunchKernelGGL(bwd_param_sums_kernel, dim3(static_cast<unsigned>((np + 255) / 256)), dim3(256), 0, s, a, g);
+  const int64_t nbc = a.batch * 2 * a.N * a.L;
+  hipLaunchKernelGGL((bwd_bc_out_kernel<ACT>), dim3(static_cast<unsigned>((nbc + 255) / 256)), dim3(256), 0, s, a,
+                     g);
+  return hipGetLastError();
+}
+
+template <typename ACT>
 hipError_t launch_bwd_act(const BwdArgs& a, const BwdLayout& g, hipStream_t s) {
   if (bwd_fast(a.N)) return launch_bwd_typed<ACT, 8, kWFast, kNMaxFast>(a, g, s);
   return launch_bwd_typed<ACT, 4, kWGen, kNMaxGen>(a, g, s);
@@ -1133,8 +1251,9 @@ hipError_t launch_bwd_act(const BwdArgs& a, const BwdLayout& g, hipStream_t s) {
 
 }  // namespace
 
-size_t scan_bwd_workspace_bytes(int64_t batch, int64_t L, int64_t D, int N) {
+size_t scan_bwd_workspace_bytes(int64_t batch, int64_t L, int64_t D, int N, bool saved) {
   if (batch <= 0 || L <= 0 || D <= 0) return 0;
+  if (saved && bwd_seq_suits(batch, D, N)) return bwd_seq_ws_floats(batch, L, D, N) * sizeof(float);
   return bwd_ws_floats(batch, L, D, N) * sizeof(float);
 }
 
@@ -1146,6 +1265,11 @@ bool scan_bwd_grid_ok(int64_t batch, int64_t L, int64_t D, int N) {
 }
 
 hipError_t launch_scan_bwd(const BwdArgs& a, Dt dt, void* ws, hipStream_t s) {
+  if (a.chunk_states && bwd_seq_suits(a.batch, a.D, a.N)) {
+    const BwdLayout g = bwd_layout_seq(a.batch, a.L, a.D, a.N, static_cast<float*>(ws));
+    if (dt == Dt::F32) return launch_bwd_seq<ActF32>(a, g, s);
+    return launch_bwd_seq<ActBF16>(a, g, s);
+  }
   const BwdLayout g = bwd_layout(a.batch, a.L, a.D, a.N, static_cast<float*>(ws));
   if (dt == Dt::F32) return launch_bwd_act<ActF32>(a, g, s);
   return launch_bwd_act<ActBF16>(a, g, s);

@@ -68,7 +68,12 @@ constexpr int kNBGeneric = 4;        // states per step (per staged B/C tile), a
 // caller allows it (SSM_SCAN_AP); rows that are not such progressions still take
 // the general path in it.  A separate build so that the default one keeps its
 // registers and schedule.
-template <typename ACT, bool GATE, int KPL, bool VEC, int NBLK, int kNB, int kW, bool CONV, bool ZOH, bool AP = false>
+//
+// SAVE: the build that also writes the saved chunk states (p.chunk_states), for the
+// backward pass; 8 tokens per lane, so a chunk is one 512-token saved entry.  A
+// separate build, so that the default ones keep their registers.
+template <typename ACT, bool GATE, int KPL, bool VEC, int NBLK, int kNB, int kW, bool CONV, bool ZOH, bool AP = false,
+          bool SAVE = false>
 __global__ __launch_bounds__(64 * kW) void scan_chunked_kernel(ScanArgs p, int n_dblk) {
   constexpr int kThreads = 64 * kW;
   static_assert(KPL >= 3, "the fused conv takes its 3 earlier tokens from the previous lane");
@@ -137,6 +142,14 @@ __global__ __launch_bounds__(64 * kW) void scan_chunked_kernel(ScanArgs p, int n
 
   const int nblk = NBLK > 0 ? NBLK : (N + kNB - 1) / kNB;
   const int64_t nchunks = (L + CH - 1) / CH;
+  // Saved chunk states (8 tokens per lane: a chunk is one 512-token saved entry):
+  // entry c is the state entering chunk c; entry 0 is the initial state.
+  static_assert(!SAVE || (CH == kSaveChunk && !AP), "the saving build has 512-token chunks");
+  float* cst = nullptr;
+  if constexpr (SAVE) {
+    if (valid) cst = p.chunk_states + (b * p.D + d) * nchunks * N;
+    if (cst && lane < N) cst[lane] = carry_v;
+  }
   const int64_t nsteps = nchunks * nblk;
 
   float dl[KPL], du[KPL], yv[KPL];
@@ -639,6 +652,19 @@ __global__ __launch_bounds__(64 * kW) void scan_chunked_kernel(ScanArgs p, int n
     store_tile(0);
   }
   barrier_lds();
+  // the state entering chunk c (after the steps of chunk c - 1) to the saved entry c
+  auto save_chunk = [&](int64_t c) __attribute__((always_inline)) {
+    if constexpr (SAVE) {
+      if (cst) {
+        float v = carry_v;
+        if constexpr (NBLK > 0) {
+#pragma unroll
+          for (int n = 0; n < NS; ++n) v = lane == n ? cs[n] : v;
+        }
+        if (lane < N) cst[c * N + lane] = v;
+      }
+    }
+  };
   if constexpr (NBLK > 0) {
     static_assert(NBLK % 2 == 0, "steps are unrolled in pairs");
     for (int64_t c = 0; c + 1 < nchunks; ++c) {
@@ -646,6 +672,7 @@ __global__ __launch_bounds__(64 * kW) void scan_chunked_kernel(ScanArgs p, int n
         constexpr int nb = decltype(nbc)::value;
         step(c * NBLK + nb, c, nb, nb & 1, false, false, false);
       });
+      save_chunk(c + 1);
     }
     const int64_t c = nchunks - 1;
     static_for<NBLK>([&](auto nbc) __attribute__((always_inline)) {
@@ -658,8 +685,15 @@ __global__ __launch_bounds__(64 * kW) void scan_chunked_kernel(ScanArgs p, int n
     for (int64_t k = 0; k < nsteps; k += 2) {
       const int64_t c0 = k / nblk, c1 = (k + 1) / nblk;
       step(k, c0, static_cast<int>(k % nblk), 0, c0 + 1 >= nchunks, k + 2 >= nsteps, k + 1 >= nsteps);
-      if (k + 1 < nsteps)
+      if constexpr (SAVE) {
+        if ((k + 1) % nblk == 0 && c0 + 1 < nchunks) save_chunk(c0 + 1);
+      }
+      if (k + 1 < nsteps) {
         step(k + 1, c1, static_cast<int>((k + 1) % nblk), 1, c1 + 1 >= nchunks, k + 3 >= nsteps, k + 2 >= nsteps);
+        if constexpr (SAVE) {
+          if ((k + 2) % nblk == 0 && c1 + 1 < nchunks) save_chunk(c1 + 1);
+        }
+      }
     }
   }
   if constexpr (NBLK > 0) {
@@ -693,6 +727,15 @@ hipError_t launch_w(const ScanArgs& a, hipStream_t s) {
   // chunk, half the barriers; measured 2 % faster).  float32 measured no faster
   // that way, and at 16 tokens per lane the larger tile's registers would spill.
   constexpr int N16_STEPS = (ACT::kBytes == 2 && KPL <= 12) ? 2 : 4;
+  if constexpr (KPL == 8 && !CONV && !ZOH) {
+    if (a.chunk_states) {   // (the host sends only N == 16 vector-path shapes here)
+      if (!(vec && n16)) return hipErrorInvalidValue;
+      hipLaunchKernelGGL(
+          (scan_chunked_kernel<ACT, GATE, KPL, true, N16_STEPS, 16 / N16_STEPS, W, CONV, ZOH, false, true>), grid,
+          block, 0, s, a, n_dblk);
+      return hipGetLastError();
+    }
+  }
   if constexpr (ACT::kBytes == 2 && W == 12 && KPL == 8 && !CONV && !ZOH) {
     if (vec && n16 && a.ap) {
       hipLaunchKernelGGL((scan_chunked_kernel<ACT, GATE, KPL, true, N16_STEPS, 16 / N16_STEPS, W, CONV, ZOH, true>),
@@ -768,6 +811,10 @@ int resolve_kpl(const ScanArgs& a, int tokens_per_lane, Dt dt) {
 }
 
 }  // namespace
+
+bool chunked_save_supported(const ScanArgs& a) {
+  return a.N == 16 && a.zoh == 0 && a.conv_w == nullptr && vec_path(a, 8);
+}
 
 bool chunked_supported(const ScanArgs& a, Dt, int tokens_per_lane) {
   if (!(tokens_per_lane == 0 || tokens_per_lane == 8 || tokens_per_lane == 12 || tokens_per_lane == 16)) return false;

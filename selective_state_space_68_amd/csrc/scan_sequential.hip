@@ -30,6 +30,14 @@ __global__ __launch_bounds__(64) void scan_sequential_kernel(ScanArgs p) {
   const float dsk = p.Dskip ? p.Dskip[d] : 0.0f;
   const int64_t row = ch * p.L;                // u / delta / z / y offset of this channel
   const int64_t bc_row = b * p.L * N;          // B / C offset of this batch row ([L][N] within it)
+  // saved chunk states: entry c is the state entering 512-token chunk c
+  const int64_t nck = (p.L + kSaveChunk - 1) / kSaveChunk;
+  float* cst = p.chunk_states ? p.chunk_states + ch * nck * N : nullptr;
+  if (cst) {
+#pragma unroll
+    for (int n = 0; n < NB; ++n)
+      if (n < N) cst[n] = h[n];
+  }
 
   for (int64_t t = 0; t < p.L; ++t) {
     const float u = load_act<ACT>(p.u, row + t);
@@ -49,6 +57,12 @@ __global__ __launch_bounds__(64) void scan_sequential_kernel(ScanArgs p) {
     y = __builtin_fmaf(dsk, u, y);
     if (GATE) y *= silu_f(load_act<ACT>(p.z, row + t));
     store_act<ACT>(p.y, row + t, y);
+    if (cst && (t + 1) % kSaveChunk == 0 && t + 1 < p.L) {
+      float* o = cst + ((t + 1) / kSaveChunk) * N;
+#pragma unroll
+      for (int n = 0; n < NB; ++n)
+        if (n < N) o[n] = h[n];
+    }
   }
   if (p.final_state) {
 #pragma unroll

@@ -113,7 +113,11 @@ struct ActIO8<ActBF16> {
 // AP: the build with the arithmetic-progression decay path, used when the caller
 // allows it (SSM_SCAN_AP); a separate build so that the default one keeps its
 // registers and schedule.
-template <typename ACT, bool GATE, int SPL, bool ZOH, bool CONV, bool AP = false>
+//
+// SAVE: the build that also writes the saved chunk states (p.chunk_states) every
+// 512 tokens, for the backward pass; a separate build, so that the default ones keep
+// their registers.
+template <typename ACT, bool GATE, int SPL, bool ZOH, bool CONV, bool AP = false, bool SAVE = false>
 __global__ __launch_bounds__(64 * kTsWaves) void scan_tokseq_kernel(ScanArgs p) {
   constexpr int QL = kTsN / SPL;           // lanes per channel (an aligned group)
   constexpr int CPW = 64 / QL;             // channels per wave
@@ -210,6 +214,16 @@ __global__ __launch_bounds__(64 * kTsWaves) void scan_tokseq_kernel(ScanArgs p) 
   };
 
   const int64_t nblk = (L + T - 1) / T;
+  // saved chunk states: entry c is the state entering 512-token chunk c (T divides 512)
+  static_assert(kSaveChunk % T == 0, "a block never straddles a saved chunk");
+  float* cst = nullptr;
+  if constexpr (SAVE) {
+    if (store_ok) cst = p.chunk_states + (b * D + d) * ((L + kSaveChunk - 1) / kSaveChunk) * kTsN;
+  }
+  if (SAVE && cst) {
+#pragma unroll
+    for (int j = 0; j < SPL; ++j) cst[SPL * q + j] = h[j];
+  }
   fetch(0);
   for (int64_t blk = 0; blk < nblk; ++blk) {
     const int64_t t0 = blk * T;
@@ -354,6 +368,11 @@ __global__ __launch_bounds__(64 * kTsWaves) void scan_tokseq_kernel(ScanArgs p) 
       }
       IO::store(p.y, row + t0 + 8 * q, yv);
     }
+    // the state after this block, when it ends a saved 512-token chunk
+    if (SAVE && cst && (t0 + T) % kSaveChunk == 0 && t0 + T < L) {
+#pragma unroll
+      for (int j = 0; j < SPL; ++j) cst[((t0 + T) / kSaveChunk) * kTsN + SPL * q + j] = h[j];
+    }
     // reads of this block's LDS before the next block's writes
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -366,12 +385,12 @@ __global__ __launch_bounds__(64 * kTsWaves) void scan_tokseq_kernel(ScanArgs p) 
 
 bool aligned16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; }
 
-template <typename ACT, bool GATE, int SPL, bool ZOH, bool CONV = false, bool AP = false>
+template <typename ACT, bool GATE, int SPL, bool ZOH, bool CONV = false, bool AP = false, bool SAVE = false>
 hipError_t launch_spl(const ScanArgs& a, hipStream_t s) {
   constexpr int CPW = 64 * SPL / kTsN;
   const int64_t ngrp = (a.D + CPW - 1) / CPW;
   const int64_t blocks = a.batch * ((ngrp + kTsWaves - 1) / kTsWaves);
-  hipLaunchKernelGGL((scan_tokseq_kernel<ACT, GATE, SPL, ZOH, CONV, AP>), dim3(static_cast<unsigned>(blocks)),
+  hipLaunchKernelGGL((scan_tokseq_kernel<ACT, GATE, SPL, ZOH, CONV, AP, SAVE>), dim3(static_cast<unsigned>(blocks)),
                      dim3(64 * kTsWaves), 0,
                      s, a);
   return hipGetLastError();
@@ -407,6 +426,14 @@ hipError_t launch_scan_tokseq(const ScanArgs& a, Dt dt, int states_per_lane, hip
   // (the full zero-order hold and the fused conv are built for 4 states per lane,
   // the automatic choice)
   const int spl = (states_per_lane == 2 && !a.zoh && a.conv_w == nullptr) ? 2 : 4;
+  if (a.chunk_states) {   // saving the chunk states (simplified input term, no conv: checked by the host)
+    if (a.zoh || a.conv_w != nullptr) return hipErrorInvalidValue;
+    if (dt == Dt::F32)
+      return gate ? launch_spl<ActF32, true, 4, false, false, false, true>(a, s)
+                  : launch_spl<ActF32, false, 4, false, false, false, true>(a, s);
+    return gate ? launch_spl<ActBF16, true, 4, false, false, false, true>(a, s)
+                : launch_spl<ActBF16, false, 4, false, false, false, true>(a, s);
+  }
   if (a.conv_w != nullptr) {
     if (dt == Dt::F32)
       return gate ? launch_spl<ActF32, true, 4, false, true>(a, s) : launch_spl<ActF32, false, 4, false, true>(a, s);

@@ -34,6 +34,13 @@ bool mul_ok(uint64_t a, uint64_t b, uint64_t* out) { return !__builtin_mul_overf
 
 bool aligned(const void* p, uintptr_t a) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// Bytes of the saved chunk states: [batch][D][ceil(L / 512)][N] float32 (sizes already
+// checked by check_scan, so the product does not overflow).
+uint64_t chunk_states_bytes(int64_t batch, int64_t L, int64_t D, int64_t N) {
+  const uint64_t nck = (static_cast<uint64_t>(L) + ssm::kSaveChunk - 1) / ssm::kSaveChunk;
+  return static_cast<uint64_t>(batch) * static_cast<uint64_t>(D) * nck * static_cast<uint64_t>(N) * sizeof(float);
+}
+
 // 1 = a device is usable, 0 = none; probed once per process.
 std::atomic<int> g_device_state{-1};
 
@@ -243,7 +250,7 @@ ssm_status scan_fwd(const void* u, const void* delta, const float* A, const void
                     const float* Dskip, const void* z, const float* delta_bias, int delta_softplus,
                     const float* initial_state, void* y, float* final_state, int64_t batch, int64_t L, int64_t D,
                     int64_t N, ssm_dtype dt, void* workspace, size_t workspace_bytes, void* stream, int variant,
-                    int tokens_per_lane, int zoh) {
+                    int tokens_per_lane, int zoh, float* chunk_states = nullptr) {
   ScanSizes sz;
   ssm_status st = check_scan(u, delta, A, Bm, Cm, Dskip, z, delta_bias, delta_softplus, initial_state, y,
                              final_state, batch, L, D, N, dt, &sz);
@@ -251,6 +258,19 @@ ssm_status scan_fwd(const void* u, const void* delta, const float* A, const void
   st = check_scan_workspace(workspace, workspace_bytes, scan_workspace_need(batch, L, D, N, dt), u, delta, A, Bm, Cm,
                             Dskip, z, delta_bias, initial_state, y, final_state, sz);
   if (st != SSM_OK) return st;
+  if (chunk_states) {
+    if (N > 16) return SSM_ERR_UNSUPPORTED;
+    if (!aligned(chunk_states, 16)) return SSM_ERR_INVALID_ARG;
+    const uint64_t cs_bytes = chunk_states_bytes(batch, L, D, N);
+    const Span cs = span(chunk_states, cs_bytes);
+    const Span all[] = {span(u, sz.act_bytes),           span(delta, sz.act_bytes),     span(z, sz.act_bytes),
+                        span(A, sz.a_bytes),             span(Bm, sz.bc_bytes),         span(Cm, sz.bc_bytes),
+                        span(Dskip, sz.vec_bytes),       span(delta_bias, sz.vec_bytes),
+                        span(initial_state, sz.state_bytes), span(y, sz.act_bytes),
+                        span(final_state, sz.state_bytes), span(workspace, workspace_bytes)};
+    for (const Span& o : all)
+      if (overlaps(cs, o)) return SSM_ERR_INVALID_ARG;
+  }
   const int ap = (variant & SSM_SCAN_AP) ? 1 : 0;
   variant &= ~SSM_SCAN_AP;
   if (variant != SSM_SCAN_AUTO && variant != SSM_SCAN_SEQUENTIAL && variant != SSM_SCAN_CHUNKED &&
@@ -263,16 +283,22 @@ ssm_status scan_fwd(const void* u, const void* delta, const float* A, const void
   a.bias = delta_bias; a.h0 = initial_state; a.y = y; a.final_state = final_state;
   a.batch = batch; a.L = L; a.D = D; a.N = static_cast<int>(N); a.softplus = delta_softplus; a.zoh = zoh;
   a.ap = ap;
+  a.chunk_states = chunk_states;
   const ssm::Dt d = dt == SSM_BF16 ? ssm::Dt::BF16 : ssm::Dt::F32;
   const int kernel = L > 0 ? choose_scan_kernel(a, d, variant, tokens_per_lane) : SSM_SCAN_SEQUENTIAL;
+  // the saved states are 512-token chunks: the chunked kernel runs at 8 tokens per lane
+  if (chunk_states) tokens_per_lane = 8;
   if (kernel < 0) return static_cast<ssm_status>(-kernel);
-  const bool tokseq = L > 0 && kernel == SSM_SCAN_TOKSEQ, chunked = L > 0 && kernel == SSM_SCAN_CHUNKED;
+  const bool tokseq = L > 0 && kernel == SSM_SCAN_TOKSEQ;
+  // saving the chunk states: the chunked kernel's saving build covers N == 16 on the
+  // vector path; other shapes save through the sequential kernel
+  const bool chunked = L > 0 && kernel == SSM_SCAN_CHUNKED && (!chunk_states || ssm::chunked_save_supported(a));
   st = probe_device();
   if (st != SSM_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (L == 0)  // the final state is the initial state
     return final_state ? from_hip(ssm::launch_copy_state(final_state, initial_state, batch * D * N, s)) : SSM_OK;
-  if (tokseq) return from_hip(ssm::launch_scan_tokseq(a, d, tokens_per_lane, s));
+  if (tokseq) return from_hip(ssm::launch_scan_tokseq(a, d, chunk_states ? 0 : tokens_per_lane, s));
   if (chunked) return from_hip(ssm::launch_scan_chunked(a, d, tokens_per_lane, s));
   return from_hip(ssm::launch_scan_sequential(a, d, s));
 }
@@ -345,6 +371,16 @@ ssm_status ssm_selective_scan_fwd_from_state(const void* u, const void* delta, c
                                              void* workspace, size_t workspace_bytes, void* stream) {
   return scan_fwd(u, delta, A, Bm, Cm, Dskip, z, delta_bias, delta_softplus, initial_state, y, final_state, batch, L,
                   D, N, dt, workspace, workspace_bytes, stream, SSM_SCAN_AUTO, 0, 0);
+}
+
+ssm_status ssm_selective_scan_fwd_save(const void* u, const void* delta, const float* A, const void* Bm,
+                                       const void* Cm, const float* Dskip, const void* z, const float* delta_bias,
+                                       int delta_softplus, const float* initial_state, void* y, float* final_state,
+                                       float* chunk_states, int64_t batch, int64_t L, int64_t D, int64_t N,
+                                       ssm_dtype dt, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!chunk_states && batch > 0 && L > 0 && D > 0) return SSM_ERR_INVALID_ARG;
+  return scan_fwd(u, delta, A, Bm, Cm, Dskip, z, delta_bias, delta_softplus, initial_state, y, final_state, batch, L,
+                  D, N, dt, workspace, workspace_bytes, stream, SSM_SCAN_AUTO, 0, 0, chunk_states);
 }
 
 ssm_status ssm_selective_scan_fwd_conv(const void* x, const float* conv_w, const float* conv_b, int64_t conv_width,
@@ -422,20 +458,27 @@ ssm_status ssm_causal_conv1d_fwd(const void* x, const float* conv_w, const float
                                             static_cast<hipStream_t>(stream)));
 }
 
-size_t ssm_selective_scan_bwd_workspace_size(int64_t batch, int64_t L, int64_t D, int64_t N, ssm_dtype dt) {
+}  // extern "C"
+
+namespace {
+
+size_t bwd_workspace(int64_t batch, int64_t L, int64_t D, int64_t N, ssm_dtype dt, bool saved) {
   if (dt != SSM_F32 && dt != SSM_BF16) return 0;
   if (batch <= 0 || L <= 0 || D <= 0 || N < 1 || N > SSM_MAX_N) return 0;
   uint64_t t;
   if (!mul_ok(batch, D, &t) || !mul_ok(t, L, &t) || t > (uint64_t(1) << 58)) return 0;
-  return ssm::scan_bwd_workspace_bytes(batch, L, D, static_cast<int>(N));
+  return ssm::scan_bwd_workspace_bytes(batch, L, D, static_cast<int>(N), saved);
 }
 
-ssm_status ssm_selective_scan_bwd(const void* u, const void* delta, const float* A, const void* Bm, const void* Cm,
-                                  const float* Dskip, const void* z, const float* delta_bias, int delta_softplus,
-                                  const float* initial_state, const void* dy, const float* dfinal_state, void* du,
-                                  void* ddelta, float* dA, void* dB, void* dC, float* dD, void* dz,
-                                  float* ddelta_bias, float* dinitial_state, int64_t batch, int64_t L, int64_t D,
-                                  int64_t N, ssm_dtype dt, void* workspace, size_t workspace_bytes, void* stream) {
+// chunk_states: null for the plain backward pass, else the forward pass's saved
+// chunk states (used where the shape suits the chunk walk, ignored otherwise).
+ssm_status scan_bwd(const void* u, const void* delta, const float* A, const void* Bm, const void* Cm,
+                    const float* Dskip, const void* z, const float* delta_bias, int delta_softplus,
+                    const float* initial_state, const void* dy, const float* dfinal_state, const float* chunk_states,
+                    void* du, void* ddelta, float* dA, void* dB, void* dC, float* dD, void* dz, float* ddelta_bias,
+                    float* dinitial_state, int64_t batch, int64_t L, int64_t D, int64_t N, ssm_dtype dt,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  const bool saved = chunk_states != nullptr;
   ScanSizes sz;
   // the forward checks cover the inputs (du stands in for y: required, act-sized)
   ssm_status st = check_scan(u, delta, A, Bm, Cm, Dskip, z, delta_bias, delta_softplus, initial_state, du,
@@ -448,13 +491,14 @@ ssm_status ssm_selective_scan_bwd(const void* u, const void* delta, const float*
   if (dz && !z) return SSM_ERR_INVALID_ARG;  // no gate: there is no z to differentiate
   if (!aligned(dy, e) || !aligned(ddelta, e) || !aligned(dB, e) || !aligned(dC, e) || !aligned(dz, e) ||
       !aligned(dA, 4) || !aligned(dD, 4) || !aligned(ddelta_bias, 4) || !aligned(dinitial_state, 4) ||
-      !aligned(dfinal_state, 4) || !aligned(workspace, 16))
+      !aligned(dfinal_state, 4) || !aligned(chunk_states, 4) || !aligned(workspace, 16))
     return SSM_ERR_INVALID_ARG;
+  const uint64_t cs_bytes = saved ? chunk_states_bytes(batch, L, D, N) : 0;
   const Span ins[] = {span(u, sz.act_bytes),         span(delta, sz.act_bytes),      span(z, sz.act_bytes),
                       span(A, sz.a_bytes),           span(Bm, sz.bc_bytes),          span(Cm, sz.bc_bytes),
                       span(Dskip, sz.vec_bytes),     span(delta_bias, sz.vec_bytes), span(initial_state, sz.state_bytes),
-                      span(dy, sz.act_bytes),        span(dfinal_state, sz.state_bytes)};
-  const size_t need = ssm_selective_scan_bwd_workspace_size(batch, L, D, N, dt);
+                      span(dy, sz.act_bytes),        span(dfinal_state, sz.state_bytes), span(chunk_states, cs_bytes)};
+  const size_t need = bwd_workspace(batch, L, D, N, dt, saved);
   const Span outs[] = {span(du, sz.act_bytes),          span(ddelta, sz.act_bytes),   span(dA, sz.a_bytes),
                        span(dB, sz.bc_bytes),           span(dC, sz.bc_bytes),        span(dD, sz.vec_bytes),
                        span(dz, sz.act_bytes),          span(ddelta_bias, sz.vec_bytes),
@@ -483,11 +527,47 @@ ssm_status ssm_selective_scan_bwd(const void* u, const void* delta, const float*
   }
   ssm::BwdArgs a;
   a.u = u; a.delta = delta; a.A = A; a.Bm = Bm; a.Cm = Cm; a.Dskip = Dskip; a.z = z; a.bias = delta_bias;
-  a.h0 = initial_state; a.dy = dy; a.dfinal = dfinal_state;
+  a.h0 = initial_state; a.dy = dy; a.dfinal = dfinal_state; a.chunk_states = chunk_states;
   a.du = du; a.ddelta = ddelta; a.dA = dA; a.dB = dB; a.dC = dC; a.dD = dD; a.dz = dz; a.dbias = ddelta_bias;
   a.dh0 = dinitial_state;
   a.batch = batch; a.L = L; a.D = D; a.N = static_cast<int>(N); a.softplus = delta_softplus;
   return from_hip(ssm::launch_scan_bwd(a, dt == SSM_BF16 ? ssm::Dt::BF16 : ssm::Dt::F32, workspace, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ssm_selective_scan_bwd_workspace_size(int64_t batch, int64_t L, int64_t D, int64_t N, ssm_dtype dt) {
+  return bwd_workspace(batch, L, D, N, dt, false);
+}
+
+size_t ssm_selective_scan_bwd_saved_workspace_size(int64_t batch, int64_t L, int64_t D, int64_t N, ssm_dtype dt) {
+  return bwd_workspace(batch, L, D, N, dt, true);
+}
+
+ssm_status ssm_selective_scan_bwd(const void* u, const void* delta, const float* A, const void* Bm, const void* Cm,
+                                  const float* Dskip, const void* z, const float* delta_bias, int delta_softplus,
+                                  const float* initial_state, const void* dy, const float* dfinal_state, void* du,
+                                  void* ddelta, float* dA, void* dB, void* dC, float* dD, void* dz,
+                                  float* ddelta_bias, float* dinitial_state, int64_t batch, int64_t L, int64_t D,
+                                  int64_t N, ssm_dtype dt, void* workspace, size_t workspace_bytes, void* stream) {
+  return scan_bwd(u, delta, A, Bm, Cm, Dskip, z, delta_bias, delta_softplus, initial_state, dy, dfinal_state, nullptr,
+                  du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dinitial_state, batch, L, D, N, dt, workspace,
+                  workspace_bytes, stream);
+}
+
+ssm_status ssm_selective_scan_bwd_saved(const void* u, const void* delta, const float* A, const void* Bm,
+                                        const void* Cm, const float* Dskip, const void* z, const float* delta_bias,
+                                        int delta_softplus, const float* initial_state, const void* dy,
+                                        const float* dfinal_state, const float* chunk_states, void* du, void* ddelta,
+                                        float* dA, void* dB, void* dC, float* dD, void* dz, float* ddelta_bias,
+                                        float* dinitial_state, int64_t batch, int64_t L, int64_t D, int64_t N,
+                                        ssm_dtype dt, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!chunk_states && batch > 0 && L > 0 && D > 0 && N > 0) return SSM_ERR_INVALID_ARG;
+  return scan_bwd(u, delta, A, Bm, Cm, Dskip, z, delta_bias, delta_softplus, initial_state, dy, dfinal_state,
+                  chunk_states, du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dinitial_state,
+                  batch, L, D, N, dt, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -140,6 +140,41 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta
     return y, final_state
 
 
+SAVE_CHUNK = 512   # tokens per saved chunk state (SSM_SAVE_CHUNK)
+
+
+def selective_scan_fwd_save(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True, *,
+                            initial_state=None, y=None, final_state=None, chunk_states=None,
+                            return_final_state=True, workspace=None, stream=None):
+    """selective_scan_fwd that also stores the state entering every SAVE_CHUNK-token
+    chunk, for selective_scan_bwd(..., chunk_states=...).  Returns (y, final_state or
+    None, chunk_states [batch, D, ceil(L / SAVE_CHUNK), N] float32); entry 0 is the
+    initial state (zeros when None).  N <= 16."""
+    lib = _lib.load_library()
+    batch, Dc, L, N = _scan_shapes(u, delta, A, B, C, D, z, delta_bias, initial_state, y, final_state)
+    act = u.dtype
+    dev = u.device
+    nck = (L + SAVE_CHUNK - 1) // SAVE_CHUNK
+    ws_ptr, ws_bytes = _workspace(workspace, selective_scan_workspace_size(batch, L, Dc, N, act), dev)
+    if y is None:
+        y = torch.empty((batch, Dc, L), dtype=act, device=dev)
+    if final_state is None and return_final_state:
+        final_state = torch.empty((batch, Dc, N), dtype=torch.float32, device=dev)
+    if chunk_states is None:
+        chunk_states = torch.empty((batch, Dc, nck, N), dtype=torch.float32, device=dev)
+    _shape(chunk_states, "chunk_states", (batch, Dc, nck, N))
+    st = lib.ssm_selective_scan_fwd_save(
+        _ptr(u, "u", act, dev), _ptr(delta, "delta", act, dev), _ptr(A, "A", torch.float32, dev),
+        _ptr(B, "B", act, dev), _ptr(C, "C", act, dev), _ptr(D, "D", torch.float32, dev),
+        _ptr(z, "z", act, dev), _ptr(delta_bias, "delta_bias", torch.float32, dev), 1 if delta_softplus else 0,
+        _ptr(initial_state, "initial_state", torch.float32, dev), _ptr(y, "y", act, dev),
+        _ptr(final_state, "final_state", torch.float32, dev),
+        _ptr(chunk_states, "chunk_states", torch.float32, dev),
+        batch, L, Dc, N, _dt(u), ws_ptr, ws_bytes, _stream(stream))
+    _lib.check(st)
+    return y, final_state, chunk_states
+
+
 SCAN_KERNELS = {_lib.SSM_SCAN_SEQUENTIAL: "scan_sequential_kernel", _lib.SSM_SCAN_CHUNKED: "scan_chunked_kernel",
                 _lib.SSM_SCAN_TOKSEQ: "scan_tokseq_kernel"}
 
@@ -159,16 +194,19 @@ def selective_scan_fwd_kernel(batch, L, D, N, dtype=torch.float32, gate=True, di
     return SCAN_KERNELS[k]
 
 
-def selective_scan_bwd_workspace_size(batch, L, D, N, dtype=torch.float32) -> int:
-    """Bytes of device workspace selective_scan_bwd needs for this shape."""
+def selective_scan_bwd_workspace_size(batch, L, D, N, dtype=torch.float32, saved=False) -> int:
+    """Bytes of device workspace selective_scan_bwd needs for this shape (saved: with
+    chunk_states from selective_scan_fwd_save)."""
     lib = _lib.load_library()
     dt = _lib.SSM_BF16 if dtype == torch.bfloat16 else _lib.SSM_F32
-    return int(lib.ssm_selective_scan_bwd_workspace_size(int(batch), int(L), int(D), int(N), dt))
+    fn = lib.ssm_selective_scan_bwd_saved_workspace_size if saved else lib.ssm_selective_scan_bwd_workspace_size
+    return int(fn(int(batch), int(L), int(D), int(N), dt))
 
 
 def selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, delta_softplus=True, *,
-                       initial_state=None, dfinal_state=None, want_dD=None, want_ddelta_bias=None,
-                       want_dinitial_state=None, workspace=None, out=None, stream=None) -> dict:
+                       initial_state=None, dfinal_state=None, chunk_states=None, want_dD=None,
+                       want_ddelta_bias=None, want_dinitial_state=None, workspace=None, out=None,
+                       stream=None) -> dict:
     """Backward pass of selective_scan_fwd (same inputs) for the output gradient dy
     [batch, D, L] and optionally the final-state gradient dfinal_state [batch, D, N].
 
@@ -179,7 +217,10 @@ def selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, d
     whenever z is given.  `workspace` is a device tensor of at least
     selective_scan_bwd_workspace_size(...) bytes, or None to allocate one.  `out`
     may hold preallocated output tensors under the same keys (missing keys are
-    allocated).
+    allocated).  `chunk_states`: what selective_scan_fwd_save returned for these
+    inputs; the pass then starts each chunk from the saved state
+    (ssm_selective_scan_bwd_saved) and the workspace is
+    selective_scan_bwd_workspace_size(..., saved=True) bytes.
     """
     lib = _lib.load_library()
     batch, Dc, L, N = _scan_shapes(u, delta, A, B, C, D, z, delta_bias, initial_state, None, None)
@@ -213,16 +254,24 @@ def selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, d
             out[k] = t
         else:
             out[k] = torch.empty(shape, dtype=dt_, device=dev) if computed else None
-    need = int(lib.ssm_selective_scan_bwd_workspace_size(batch, L, Dc, N, _dt(u)))
+    saved = chunk_states is not None
+    if saved:
+        _shape(chunk_states, "chunk_states", (batch, Dc, (L + SAVE_CHUNK - 1) // SAVE_CHUNK, N))
+    need = selective_scan_bwd_workspace_size(batch, L, Dc, N, act, saved)
     if workspace is None:
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
     ws_ptr, ws_bytes = _workspace(workspace, need, dev)
-    st = lib.ssm_selective_scan_bwd(
-        _ptr(u, "u", act, dev), _ptr(delta, "delta", act, dev), _ptr(A, "A", f32, dev),
-        _ptr(B, "B", act, dev), _ptr(C, "C", act, dev), _ptr(D, "D", f32, dev),
-        _ptr(z, "z", act, dev), _ptr(delta_bias, "delta_bias", f32, dev), 1 if delta_softplus else 0,
-        _ptr(initial_state, "initial_state", f32, dev), _ptr(dy, "dy", act, dev),
-        _ptr(dfinal_state, "dfinal_state", f32, dev),
+    ins = (_ptr(u, "u", act, dev), _ptr(delta, "delta", act, dev), _ptr(A, "A", f32, dev),
+           _ptr(B, "B", act, dev), _ptr(C, "C", act, dev), _ptr(D, "D", f32, dev),
+           _ptr(z, "z", act, dev), _ptr(delta_bias, "delta_bias", f32, dev), 1 if delta_softplus else 0,
+           _ptr(initial_state, "initial_state", f32, dev), _ptr(dy, "dy", act, dev),
+           _ptr(dfinal_state, "dfinal_state", f32, dev))
+    if saved:
+        fn, ins = lib.ssm_selective_scan_bwd_saved, ins + (_ptr(chunk_states, "chunk_states", f32, dev),)
+    else:
+        fn = lib.ssm_selective_scan_bwd
+    st = fn(
+        *ins,
         _ptr(out["du"], "du"), _ptr(out["ddelta"], "ddelta"), _ptr(out["dA"], "dA"), _ptr(out["dB"], "dB"),
         _ptr(out["dC"], "dC"), _ptr(out["dD"], "dD"), _ptr(out["dz"], "dz"),
         _ptr(out["ddelta_bias"], "ddelta_bias"), _ptr(out["dinitial_state"], "dinitial_state"),

@@ -22,6 +22,7 @@ class ScanConfig:
     conv_k: int = 0     # > 0: the input is x and u = SiLU(causal conv1d of width conv_k) is fused in
     backward: bool = False  # the workload is the backward pass (gradients for dy) instead of the forward
     discretization: str = "simplified"   # or "zoh": the full zero-order-hold input term
+    saved: bool = False  # backward: the forward pass's saved 512-token chunk states are read
 
     @property
     def elements(self) -> int:
@@ -34,7 +35,8 @@ class ScanConfig:
         if self.backward:
             # reads u, delta, dy (+ z), B, C, A, D, bias; writes du, ddelta (+ dz), dB, dC, dA, dD, dbias
             n_act = 5 + (2 if self.gate else 0)
-            return (per_tok * n_act
+            saved = 4 * self.batch * self.D * (-(-self.L // 512)) * self.N if self.saved else 0
+            return (per_tok * n_act + saved
                     + 4 * self.batch * self.L * self.N * e    # B, C read; dB, dC written
                     + 8 * self.D * self.N                     # A read, dA written
                     + 16 * self.D)                            # D skip, bias read; their gradients written
@@ -130,6 +132,9 @@ CONFIGS = {
                                     backward=True),
     "bwd_mamba1p4b_bf16": ScanConfig("bwd_mamba1p4b_bf16", 8, 2048, 4096, 16, "bf16", gate=True, d_skip="ones",
                                      backward=True),
+    # ... with the forward pass's saved chunk states (the training pair)
+    "bwd_saved_mamba1p4b_bf16": ScanConfig("bwd_saved_mamba1p4b_bf16", 8, 2048, 4096, 16, "bf16", gate=True,
+                                           d_skip="ones", backward=True, saved=True),
     "bwd_long131k_bf16": ScanConfig("bwd_long131k_bf16", 1, 131072, 2560, 16, "bf16", gate=True, d_skip="ones",
                                     backward=True),
 }

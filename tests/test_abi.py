@@ -266,6 +266,80 @@ def test_bwd_argument_errors(lib, kw, status):
     assert _bwd(lib, **kw) == status
 
 
+def _bwd_saved(lib, **kw):
+    """ssm_selective_scan_bwd_saved: the _bwd arguments plus the saved chunk states."""
+    slots = ["u", "delta", "A", "B", "C", "Dskip", "z", "bias", "h0", "dy", "dfinal",
+             "du", "ddelta", "dA", "dB", "dC", "dD", "dz", "dbias", "dh0", "ws"]
+    a = {k: F + i * 64 * MB for i, k in enumerate(slots)}
+    a.update(Dskip=None, z=None, bias=None, h0=None, dfinal=None, dD=None, dz=None, dbias=None, dh0=None,
+             softplus=1, batch=1, L=64, D=16, N=4, dt=0, ws_bytes=None, cs=F + 22 * 64 * MB)
+    a.update(kw)
+    if a["ws_bytes"] is None:
+        a["ws_bytes"] = lib.ssm_selective_scan_bwd_saved_workspace_size(a["batch"], a["L"], a["D"], a["N"],
+                                                                        a["dt"])
+    return lib.ssm_selective_scan_bwd_saved(a["u"], a["delta"], a["A"], a["B"], a["C"], a["Dskip"], a["z"],
+                                            a["bias"], a["softplus"], a["h0"], a["dy"], a["dfinal"], a["cs"],
+                                            a["du"], a["ddelta"], a["dA"], a["dB"], a["dC"], a["dD"], a["dz"],
+                                            a["dbias"], a["dh0"], a["batch"], a["L"], a["D"], a["N"], a["dt"],
+                                            a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(u=None), _lib.SSM_ERR_INVALID_ARG),
+    (dict(dy=None), _lib.SSM_ERR_INVALID_ARG),
+    (dict(ws=None), _lib.SSM_ERR_INVALID_ARG),
+    (dict(ws_bytes=64), _lib.SSM_ERR_INVALID_ARG),
+    (dict(du=F), _lib.SSM_ERR_INVALID_ARG),
+    (dict(cs=None), _lib.SSM_ERR_INVALID_ARG),                      # the saved states are required
+    (dict(cs=F + 22 * 64 * MB + 2), _lib.SSM_ERR_INVALID_ARG),      # misaligned saved states
+    (dict(cs=F + 11 * 64 * MB), _lib.SSM_ERR_INVALID_ARG),          # saved states alias an output (du)
+    (dict(cs=F + 20 * 64 * MB), _lib.SSM_ERR_INVALID_ARG),          # ... or the workspace
+    (dict(N=65), _lib.SSM_ERR_UNSUPPORTED),
+    (dict(L=-1), _lib.SSM_ERR_INVALID_ARG),
+])
+def test_bwd_saved_argument_errors(lib, kw, status):
+    assert _bwd_saved(lib, **kw) == status
+
+
+def test_bwd_saved_workspace_size(lib):
+    plain = lib.ssm_selective_scan_bwd_workspace_size
+    saved = lib.ssm_selective_scan_bwd_saved_workspace_size
+    # shapes that run the plain decomposition: the same size
+    for shape in ((2, 2048, 1536, 16), (1, 1000, 7, 5), (8, 2048, 4096, 24)):
+        assert saved(*shape, 1) == plain(*shape, 1)
+    # the chunk walk (N <= 16 and batch * D >= 16384): at least the carried adjoints
+    # (batch*D*N floats), the dA partials (batch*chunks*D*N) and one float32 dB, dC
+    # copy (batch*2*N*L); no per-chunk entering states (batch*chunks*D*N)
+    for batch, L, D, N in ((8, 2048, 4096, 16), (1, 1100, 16384, 16), (4, 2056, 4100, 5)):
+        nc = -(-L // 512)
+        assert saved(batch, L, D, N, 1) >= 4 * (batch * D * N + batch * nc * D * N + batch * 2 * N * L)
+        assert saved(batch, L, D, N, 1) == saved(batch, L, D, N, 0)
+    assert saved(0, 64, 16, 4, 0) == 0 and saved(1, 64, 16, 65, 0) == 0
+
+
+def _scan_save(lib, **kw):
+    a = _scan_args(**kw)
+    a.setdefault("cs", F + 8 * 64 * MB)
+    a.update({k: v for k, v in kw.items() if k == "cs"})
+    return lib.ssm_selective_scan_fwd_save(a["u"], a["delta"], a["A"], a["B"], a["C"], a["Dskip"], a["z"],
+                                           a["bias"], a["softplus"], a["h0"], a["y"], a["final"], a["cs"],
+                                           a["batch"], a["L"], a["D"], a["N"], a["dt"], a["ws"], a["ws_bytes"],
+                                           None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(u=None), _lib.SSM_ERR_INVALID_ARG),
+    (dict(y=F), _lib.SSM_ERR_INVALID_ARG),
+    (dict(cs=None), _lib.SSM_ERR_INVALID_ARG),
+    (dict(cs=F + 8 * 64 * MB + 8), _lib.SSM_ERR_INVALID_ARG),      # saved states not 16-byte aligned
+    (dict(cs=F + 5 * 64 * MB), _lib.SSM_ERR_INVALID_ARG),          # saved states alias y
+    (dict(cs=F + 4 * 64 * MB + 64), _lib.SSM_ERR_INVALID_ARG),     # ... overlap C
+    (dict(N=17), _lib.SSM_ERR_UNSUPPORTED),                        # saving covers up to 16 states
+])
+def test_scan_save_argument_errors(lib, kw, status):
+    assert _scan_save(lib, **kw) == status
+
+
 def test_bwd_empty_channels_is_noop(lib):
     assert _bwd(lib, D=0, u=None, delta=None, dy=None, du=None, ddelta=None, dA=None, ws=None) == _lib.SSM_OK
 
@@ -429,6 +503,10 @@ def test_valid_call_without_device_reports_hip_error(lib):
     assert _bwd(lib, z=F + 6 * 64 * MB, dz=F + 17 * 64 * MB, h0=F + 8 * 64 * MB, dh0=F + 19 * 64 * MB,
                 dfinal=F + 10 * 64 * MB, Dskip=F + 5 * 64 * MB, dD=F + 16 * 64 * MB) == _lib.SSM_ERR_HIP
     assert _bwd(lib, L=0) == _lib.SSM_ERR_HIP               # sums over no tokens still write zeros
+    assert _bwd_saved(lib) == _lib.SSM_ERR_HIP
+    assert _bwd_saved(lib, batch=1, L=1100, D=16384, N=16, dt=1) == _lib.SSM_ERR_HIP    # a chunk-walk shape
+    assert _scan_save(lib) == _lib.SSM_ERR_HIP
+    assert _scan_save(lib, N=16, L=1024) == _lib.SSM_ERR_HIP
     with pytest.raises(_lib.SsmError) as ei:
         _lib.check(_lib.SSM_ERR_HIP)
     assert ei.value.status == _lib.SSM_ERR_HIP

@@ -207,3 +207,145 @@ def test_bwd_many_channel_chunks(batch, L, D, dtype, kw):
     got = _run_gpu(inp, dyup, hz, dfin)
     ref = _run_oracle_sliced(inp, dyv, hz, dfin)
     _compare(got, ref, dtype, f"bwd many chunks {dtype} b={batch} L={L} D={D} {kw}")
+
+
+# ---- the training pair with saved chunk states ---------------------------------------
+
+SAVE = 512
+
+
+def _oracle_chunk_states(inp, hz):
+    """The state entering every 512-token chunk: the oracle's scan over each chunk,
+    started from the state the previous chunk ended in (entry 0: the initial state)."""
+    batch, D, L = inp.u.shape
+    N = inp.A.shape[1]
+    h = np.zeros((batch, D, N)) if hz is None else np.asarray(hz, np.float64)
+    out = []
+    for t0 in range(0, L, SAVE):
+        out.append(h)
+        s = slice(t0, min(L, t0 + SAVE))
+        _, h = oracle.selective_scan(inp.u[:, :, s], inp.delta[:, :, s], inp.A, inp.B[:, s], inp.C[:, s],
+                                     inp.Dskip, None if inp.z is None else inp.z[:, :, s], inp.delta_bias,
+                                     inp.delta_softplus, h0=h)
+    return np.stack(out, axis=2), h                          # [batch][D][chunks][N], final state
+
+
+def _run_gpu_saved(inp, dyup, hz, dfin, want_dh0=None):
+    import torch
+    from selective_state_space_68_amd import selective_scan_bwd, selective_scan_fwd_save
+    t = {k: dev(inp.upload_array(k)) for k in ("u", "delta", "B", "C", "z")}
+    y, fs, cs = selective_scan_fwd_save(t["u"], t["delta"], dev(inp.A), t["B"], t["C"], dev(inp.Dskip), t["z"],
+                                        dev(inp.delta_bias), inp.delta_softplus, initial_state=dev(hz))
+    g = selective_scan_bwd(t["u"], t["delta"], dev(inp.A), t["B"], t["C"], dev(dyup), dev(inp.Dskip), t["z"],
+                           dev(inp.delta_bias), inp.delta_softplus, initial_state=dev(hz),
+                           dfinal_state=dev(dfin), chunk_states=cs, want_dinitial_state=want_dh0)
+    torch.cuda.synchronize()
+    return host(y), host(fs), host(cs), {k: host(v) for k, v in g.items()}
+
+
+SAVE_FWD_CASES = [
+    # batch, L, D, N, dtype, kwargs; the forward kernel that saves
+    (2, 1536, 24, 16, "bf16", dict(h0=True)),                  # chunked, 3 whole chunks
+    (1, 2056, 40, 16, "f32", dict()),                          # chunked; last chunk 8 tokens
+    (2, 1100, 13, 16, "bf16", dict(h0=True)),                  # L % 8: the sequential kernel
+    (1, 1300, 9, 5, "f32", dict(h0=True, gate=False)),         # N != 16: the sequential kernel
+    (2, 1032, 16400, 16, "bf16", dict(h0=True)),               # 32800 channels: the token-sequential kernel
+    (1, 512, 7, 16, "f32", dict()),                            # one whole chunk: entry 0 only
+    (1, 40, 3, 16, "f32", dict(h0=True)),                      # shorter than a chunk
+]
+
+
+@pytest.mark.parametrize("batch,L,D,N,dtype,kw", SAVE_FWD_CASES)
+def test_fwd_save_chunk_states_match_oracle(batch, L, D, N, dtype, kw):
+    import torch
+    from selective_state_space_68_amd import selective_scan_fwd_save, selective_scan_fwd_kernel
+    inp = synth.make_scan_inputs(batch, L, D, N, dtype, gate=kw.get("gate", True), seed=L + D)
+    hz = synth.make_scan_initial_state(batch, D, N, seed=L) if kw.get("h0") else None
+    t = {k: dev(inp.upload_array(k)) for k in ("u", "delta", "B", "C", "z")}
+    y, fs, cs = selective_scan_fwd_save(t["u"], t["delta"], dev(inp.A), t["B"], t["C"], dev(inp.Dskip), t["z"],
+                                        dev(inp.delta_bias), True, initial_state=dev(hz))
+    torch.cuda.synchronize()
+    kern = selective_scan_fwd_kernel(batch, L, D, N, torch.bfloat16 if dtype == "bf16" else torch.float32,
+                                     gate=inp.z is not None)
+    ref_cs, ref_fs = _oracle_chunk_states(inp, hz)
+    ry, _ = oracle.selective_scan(inp.u, inp.delta, inp.A, inp.B, inp.C, inp.Dskip, inp.z, inp.delta_bias, True,
+                                  h0=hz)
+    assert cs.shape == (batch, D, -(-L // SAVE), N)
+    e_cs = row_rel_err(host(cs), ref_cs)
+    e_fs = row_rel_err(host(fs), ref_fs)
+    e_y = row_rel_err(host(y), ry)
+    print(f"fwd_save {kern} b={batch} L={L} D={D} N={N} {dtype}: cs {e_cs:.2e} fs {e_fs:.2e} y {e_y:.2e}",
+          flush=True)
+    tol = TOL[dtype]
+    assert e_cs <= tol and e_fs <= tol and e_y <= tol
+    # entry 0 is the initial state itself (zeros without one)
+    want0 = np.zeros((batch, D, N)) if hz is None else np.asarray(hz, np.float64)
+    assert np.array_equal(host(cs)[:, :, 0], want0)
+
+
+SAVED_BWD_CASES = [
+    # batch, L, D, dtype, kwargs (N = 16); batch * D >= 16384 walks the chunks
+    (1, 1100, 16384, "bf16", dict(h0=True, dfinal=True)),     # non-vector path (L % 8), ragged last chunk
+    (2, 1536, 8192, "f32", dict(gate=False)),                 # vector path, 3 whole chunks
+    (4, 2056, 4100, "bf16", dict(dfinal=True)),               # last chunk 8 tokens; last slice partly idle
+    (2, 1032, 16400, "bf16", dict(h0=True)),                  # forward states from the token-sequential kernel
+    (2, 1100, 13, "f32", dict(h0=True, dfinal=True)),         # few channels: the chunk-parallel decomposition
+]
+
+
+@pytest.mark.parametrize("batch,L,D,dtype,kw", SAVED_BWD_CASES)
+def test_bwd_saved_matches_oracle(batch, L, D, dtype, kw):
+    inp, dyv, dyup, hz, dfin = _case(batch, L, D, 16, dtype, seed=D + 1, **kw)
+    _, _, _, got = _run_gpu_saved(inp, dyup, hz, dfin)
+    ref = _run_oracle_sliced(inp, dyv, hz, dfin)
+    _compare(got, ref, dtype, f"bwd saved {dtype} b={batch} L={L} D={D} {kw}")
+
+
+def test_bwd_saved_fewer_states():
+    # N = 5 (an odd count: a zero padding state) on the chunk walk, from the
+    # sequential kernel's saved states
+    inp, dyv, dyup, hz, dfin = _case(1, 1000, 16400, 5, "f32", seed=5, h0=True, dfinal=True)
+    _, _, _, got = _run_gpu_saved(inp, dyup, hz, dfin)
+    ref = _run_oracle_sliced(inp, dyv, hz, dfin)
+    _compare(got, ref, "f32", "bwd saved N=5")
+
+
+def test_bwd_saved_dinitial_state_without_initial_state():
+    inp, dyv, dyup, _, dfin = _case(1, 1024, 16384, 16, "bf16", seed=3, dfinal=True)
+    _, _, _, got = _run_gpu_saved(inp, dyup, None, dfin, want_dh0=True)
+    ref = _run_oracle_sliced(inp, dyv, np.zeros((1, 16384, 16)), dfin)
+    _compare(got, ref, "bf16", "bwd saved dh0 at zero state")
+
+
+def test_bwd_saved_repeatable_and_workspace_reuse():
+    # bitwise reproducible on the chunk walk too; a dirty, reused workspace changes nothing
+    import torch
+    from selective_state_space_68_amd import (selective_scan_bwd, selective_scan_bwd_workspace_size,
+                                              selective_scan_fwd_save)
+    batch, L, D = 2, 1024, 8192
+    inp, dyv, dyup, hz, dfin = _case(batch, L, D, 16, "bf16", seed=11, h0=True, dfinal=True)
+    t = {k: dev(inp.upload_array(k)) for k in ("u", "delta", "B", "C", "z")}
+    _, _, cs = selective_scan_fwd_save(t["u"], t["delta"], dev(inp.A), t["B"], t["C"], dev(inp.Dskip), t["z"],
+                                       dev(inp.delta_bias), True, initial_state=dev(hz))
+    n = selective_scan_bwd_workspace_size(batch, L, D, 16, torch.bfloat16, saved=True)
+    ws = torch.full((n,), 0x7f, dtype=torch.uint8, device="cuda")
+    outs = []
+    for _ in range(2):
+        g = selective_scan_bwd(t["u"], t["delta"], dev(inp.A), t["B"], t["C"], dev(dyup), dev(inp.Dskip), t["z"],
+                               dev(inp.delta_bias), True, initial_state=dev(hz), dfinal_state=dev(dfin),
+                               chunk_states=cs, workspace=ws)
+        torch.cuda.synchronize()
+        outs.append({k: host(v) for k, v in g.items()})
+    for k in ("du", "ddelta", "dz", "dA", "dB", "dC", "dD", "ddelta_bias", "dinitial_state"):
+        assert np.array_equal(outs[0][k], outs[1][k]), k
+    ref = _run_oracle_sliced(inp, dyv, hz, dfin)
+    _compare(outs[1], ref, "bf16", "bwd saved reused workspace")
+
+
+def test_bwd_saved_small_shape_is_the_plain_pass():
+    # below 16384 channels the saved states are not read: the plain pass, bit for bit
+    inp, dyv, dyup, hz, dfin = _case(2, 1100, 40, 16, "bf16", seed=2, h0=True, dfinal=True)
+    _, _, _, got = _run_gpu_saved(inp, dyup, hz, dfin)
+    plain = _run_gpu(inp, dyup, hz, dfin)
+    for k in ("du", "ddelta", "dz", "dA", "dB", "dC", "dD", "ddelta_bias", "dinitial_state"):
+        assert np.array_equal(got[k], plain[k]), k
