@@ -52,6 +52,7 @@ namespace ssm {
 namespace {
 
 constexpr int kNBGeneric = 4;        // states per step (per staged B/C tile), any N
+constexpr int64_t kSplitMaxChannels = 10 * 256;   // the split build: one 10-channel workgroup per CU
 
 // ---- the scan ----------------------------------------------------------------
 // kNB states per step.  NBLK > 0: N == kNB * NBLK, fixed at compile time; the steps of a chunk are
@@ -72,8 +73,19 @@ constexpr int kNBGeneric = 4;        // states per step (per staged B/C tile), a
 // SAVE: the build that also writes the saved chunk states (p.chunk_states), for the
 // backward pass; 8 tokens per lane, so a chunk is one 512-token saved entry.  A
 // separate build, so that the default ones keep their registers.
+//
+// SPLIT: a workgroup of kW waves owns kW - 2 channels.  Waves 0 .. kW-5 run one
+// channel each; the last four run two channels, two waves per channel, each wave
+// taking half of every step's states (the first wave states n0 .. n0+3 of the
+// step, the second n0+4 .. n0+7).  The states of a channel are independent until
+// the readout sums over them, so the second wave adds its partial readout to the
+// first one's through LDS once per chunk, and the first wave applies the gate and
+// stores y.  With one workgroup per CU and waves dealt to the four SIMDs in turn,
+// every SIMD holds two whole channels and one half: at 10 channels per CU (2560
+// channels on 256 CUs) that is 2.5 channels' work per SIMD where 12-channel groups
+// put 3 on some SIMDs and leave CUs idle.
 template <typename ACT, bool GATE, int KPL, bool VEC, int NBLK, int kNB, int kW, bool CONV, bool ZOH, bool AP = false,
-          bool SAVE = false>
+          bool SAVE = false, bool SPLIT = false>
 __global__ __launch_bounds__(64 * kW) void scan_chunked_kernel(ScanArgs p, int n_dblk) {
   constexpr int kThreads = 64 * kW;
   static_assert(KPL >= 3, "the fused conv takes its 3 earlier tokens from the previous lane");
@@ -86,6 +98,8 @@ __global__ __launch_bounds__(64 * kW) void scan_chunked_kernel(ScanArgs p, int n
   constexpr bool kAP = AP;
   static_assert(!AP || (ACT::kBytes == 2 && kW == 12 && VEC && NBLK > 0 && PAIR && !ZOH && !CONV),
                 "no arithmetic-progression build for this configuration");
+  static_assert(!SPLIT || (kW == 12 && KPL == 12 && VEC && NBLK > 0 && kNB == 8 && PAIR && !AP && !SAVE && !ZOH && !CONV),
+                "no split build for this configuration");
   using IO = TokenIO<ACT, KPL>;
   using raw_t = typename IO::raw_t;
   constexpr int CH = 64 * KPL;
@@ -96,6 +110,8 @@ __global__ __launch_bounds__(64 * kW) void scan_chunked_kernel(ScanArgs p, int n
   constexpr bool ROWS = ACT::kBytes == 4 && VEC && NBLK > 0 && kNB * NBLK == 16 && KPL == 8;
   constexpr int TILE4 = (ROWS ? 16 : kNB) * 2 * BLK4;  // float4 per LDS buffer
   __shared__ float4 s_tile[2][TILE4];
+  // SPLIT: the second wave's partial readout of the last chunk, per split channel
+  __shared__ float4 s_y[SPLIT ? 2 * 16 * KPL : 1];
 
   const int lane = threadIdx.x & 63;
   const bool lane0 = lane == 0;
@@ -105,7 +121,11 @@ __global__ __launch_bounds__(64 * kW) void scan_chunked_kernel(ScanArgs p, int n
   // XCD's L2 holds only that row's B and C.
   const int blk = blockIdx.x;
   const int64_t b = blk % p.batch;
-  const int64_t d_own = static_cast<int64_t>(blk / p.batch) * kW + w;
+  constexpr int kChan = SPLIT ? kW - 2 : kW;          // channels per workgroup
+  constexpr int kWhole = SPLIT ? kW - 4 : kW;         // waves that run a whole channel
+  const bool split = SPLIT && w >= kWhole;            // wave-uniform
+  const int half = split ? ((w - kWhole) & 1) : 0;    // 1: the second half of each step's states
+  const int64_t d_own = static_cast<int64_t>(blk / p.batch) * kChan + (split ? kWhole + (w - kWhole) / 2 : w);
   const bool valid = d_own < p.D;                    // wave-uniform
   // A wave past the last channel runs the same code on the last channel (so no
   // branch depends on it) and stores nothing.
@@ -114,7 +134,8 @@ __global__ __launch_bounds__(64 * kW) void scan_chunked_kernel(ScanArgs p, int n
   const int64_t L = p.L;
   const int64_t row = (b * p.D + d) * L;
   const float bias = p.bias ? p.bias[d] : 0.0f;
-  const float dsk = p.Dskip ? p.Dskip[d] : 0.0f;
+  // (SPLIT: the skip term is added once, by the first wave of a channel)
+  const float dsk = (p.Dskip && !(SPLIT && half)) ? p.Dskip[d] : 0.0f;
   // A[d, n] * log2(e) in lane n (read once, so the state loop never issues a
   // vector load of A).
   const float a2_v = lane < N ? p.A[d * N + lane] * kLog2e : 0.0f;
@@ -259,6 +280,20 @@ __global__ __launch_bounds__(64 * kW) void scan_chunked_kernel(ScanArgs p, int n
   };
 
   auto epilogue = [&](int64_t c) __attribute__((always_inline)) {
+    if constexpr (SPLIT) {
+      if (half) return;                              // its partial readout went to LDS
+      if (split) {                                   // add the second wave's partial
+        const float4* src = s_y + ((w - kWhole) / 2) * 16 * KPL;
+#pragma unroll
+        for (int q = 0; q < KPL / 4; ++q) {
+          const float4 v = src[q * 64 + lane];
+          yv[4 * q] += v.x;
+          yv[4 * q + 1] += v.y;
+          yv[4 * q + 2] += v.z;
+          yv[4 * q + 3] += v.w;
+        }
+      }
+    }
     const int64_t tl = c * CH + static_cast<int64_t>(lane) * KPL;
     if (GATE) {
       float zv[KPL];
@@ -544,12 +579,17 @@ __global__ __launch_bounds__(64 * kW) void scan_chunked_kernel(ScanArgs p, int n
   // by compile-time n once the steps are unrolled.
   constexpr int NS = NBLK > 0 ? kNB * NBLK : 1;
   float a2s[NS], cs[NS], ras[NS];
+  // SPLIT: slot n (n % 8 < 4) of the second wave of a channel holds state n + 4.
+  auto slot_state = [&](int n) __attribute__((always_inline)) -> int {
+    return (SPLIT && (n % 8) < 4) ? n + 4 * half : n;
+  };
   if constexpr (NBLK > 0) {
 #pragma unroll
     for (int n = 0; n < NS; ++n) {
-      a2s[n] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, a2_v), n));
-      ras[n] = ZOH ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ra_v), n)) : 0.0f;
-      cs[n] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, carry_v), n));
+      const int sn = slot_state(n);
+      a2s[n] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, a2_v), sn));
+      ras[n] = ZOH ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ra_v), sn)) : 0.0f;
+      cs[n] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, carry_v), sn));
     }
   }
 
@@ -564,6 +604,12 @@ __global__ __launch_bounds__(64 * kW) void scan_chunked_kernel(ScanArgs p, int n
         auto pairs = [&](auto apm) __attribute__((always_inline)) {
 #pragma unroll
           for (int nl = 0; nl < nn; nl += 2) {
+            // SPLIT: a split wave runs the step's first two pairs only, on the tile
+            // `cur` offset by 4 half states, with its states' scalars in slots
+            // n0 .. n0 + 3 (the second wave loaded them there)
+            if constexpr (SPLIT) {
+              if (nl >= nn / 2 && split) break;
+            }
             const int n = n0 + nl;
             scan_two(apm, t + nl * 2 * BLK4, t + (nl * 2 + 1) * BLK4, a2s[n], ras[n], cs[n],
                      t + (nl * 2 + 2) * BLK4, t + (nl * 2 + 3) * BLK4, a2s[n + 1], ras[n + 1], cs[n + 1], cs[n],
@@ -625,11 +671,21 @@ __global__ __launch_bounds__(64 * kW) void scan_chunked_kernel(ScanArgs p, int n
         // needed an address instruction of its own (32 VALU per step).  Where the
         // tiles fit in 64 KB the constant is better (measured 1.3 % slower
         // opaque).
-        int toff = par * TILE4;
+        int toff = par * TILE4 + (SPLIT ? half * kNB * BLK4 : 0);   // (SPLIT: the second wave's states)
         asm volatile("" : "+s"(toff));
         states(&s_tile[0][0] + toff, nb);
       } else {
         states(s_tile[par], nb);
+      }
+    }
+    if constexpr (SPLIT) {
+      // the second wave's partial readout of this chunk, for the first wave's
+      // epilogue after the barrier (which reads it before the next chunk's last step)
+      if (half && nb == nblk - 1) {
+        float4* dst = s_y + ((w - kWhole) / 2) * 16 * KPL;
+#pragma unroll
+        for (int q = 0; q < KPL / 4; ++q)
+          dst[q * 64 + lane] = make_float4(yv[4 * q], yv[4 * q + 1], yv[4 * q + 2], yv[4 * q + 3]);
       }
     }
     if (!tail1) store_tile(par ^ 1);
@@ -697,12 +753,18 @@ __global__ __launch_bounds__(64 * kW) void scan_chunked_kernel(ScanArgs p, int n
     }
   }
   if constexpr (NBLK > 0) {
-    // carries back into lane n for the final-state store
+    // carries back into lane n for the final-state store (SPLIT: a split wave's
+    // slots n % 8 < 4, holding states slot_state(n))
 #pragma unroll
-    for (int n = 0; n < NS; ++n) carry_v = lane == n ? cs[n] : carry_v;
+    for (int n = 0; n < NS; ++n) {
+      if (SPLIT && split && (n % 8) >= 4) continue;
+      carry_v = lane == slot_state(n) ? cs[n] : carry_v;
+    }
   }
   epilogue(nchunks - 1);
-  if (valid && p.final_state && lane < N) p.final_state[(b * p.D + d) * N + lane] = carry_v;
+  // (SPLIT: each wave of a channel stores the states it ran, n % 8 < 4 the first)
+  const bool own = !split || (((lane >> 2) & 1) == half);
+  if (valid && p.final_state && lane < N && own) p.final_state[(b * p.D + d) * N + lane] = carry_v;
 }
 
 bool aligned16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; }
@@ -733,6 +795,17 @@ hipError_t launch_w(const ScanArgs& a, hipStream_t s) {
       hipLaunchKernelGGL(
           (scan_chunked_kernel<ACT, GATE, KPL, true, N16_STEPS, 16 / N16_STEPS, W, CONV, ZOH, false, true>), grid,
           block, 0, s, a, n_dblk);
+      return hipGetLastError();
+    }
+  }
+  if constexpr (ACT::kBytes == 2 && W == 12 && KPL == 12 && !CONV && !ZOH) {
+    // Up to 10 channels per CU: 10-channel workgroups with the last two channels
+    // split over two waves each (SPLIT), one workgroup per CU.
+    if (vec && n16 && !a.ap && !a.chunk_states && a.batch * a.D <= kSplitMaxChannels) {
+      const int n_split = static_cast<int>((a.D + W - 3) / (W - 2));
+      hipLaunchKernelGGL(
+          (scan_chunked_kernel<ACT, GATE, KPL, true, N16_STEPS, 16 / N16_STEPS, W, CONV, ZOH, false, false, true>),
+          dim3(static_cast<unsigned>(a.batch * n_split)), block, 0, s, a, n_split);
       return hipGetLastError();
     }
   }

@@ -202,6 +202,39 @@ EDGE = [
 ]
 
 
+SPLIT_SHAPES = [
+    # batch, L, D, gate, h0: bfloat16, N = 16, 12 tokens per lane, 10-channel workgroups
+    # whose last two channels run on two waves each (half of every step's states)
+    (1, 1536, 9, True, False),        # one workgroup: 8 whole channels, one split, one idle pair
+    (2, 2304, 23, False, True),       # 3 workgroups per row; the last holds 3 channels
+    (1, 2304, 20, True, True),        # 2 full workgroups
+    (3, 1000, 10, True, False),       # a ragged last chunk (232 of 768 tokens)
+    (1, 32768, 30, True, False),      # the automatic choice (12 tokens per lane from 32768 tokens)
+]
+
+
+@pytest.mark.parametrize("shape", SPLIT_SHAPES, ids=lambda s: "x".join(map(str, s[:3])))
+def test_split_channel_workgroups(shape):
+    """The chunked kernel's 12-tokens-per-lane build for up to 2560 channels: every
+    output, the final state of each half of the split channels' states included,
+    against the oracle, from a zero and from a given initial state."""
+    from selective_state_space_68_amd import selective_scan_fwd
+    import torch
+    batch, L, D, gate, h0 = shape
+    inp = synth.make_scan_inputs(batch, L, D, 16, "bf16", gate=gate, d_skip="normal", seed=L + D,
+                                 a_kind="lognormal")
+    hz = synth.make_scan_initial_state(batch, D, 16, seed=D) if h0 else None
+    t = upload_scan(inp)
+    kpl = 0 if L >= 32768 else 12
+    y, fs = selective_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["bias"], True,
+                               initial_state=dev(hz), variant=0 if kpl == 0 else 2, tokens_per_lane=kpl)
+    torch.cuda.synchronize()
+    import oracle
+    ry, rf = oracle.selective_scan(inp.u, inp.delta, inp.A, inp.B, inp.C, inp.Dskip, inp.z, inp.delta_bias, True,
+                                   h0=hz)
+    _check(host(y), host(fs), ry, rf, "bf16", f"split {shape}")
+
+
 @pytest.mark.parametrize("shape", EDGE, ids=lambda s: "x".join(map(str, s[:4])) + f"-{s[4]}")
 def test_edge_shapes_all_variants(shape):
     batch, L, D, N, dtype, gate, dsk, bias, sp = shape
