@@ -372,17 +372,20 @@ struct TokenState {
       }
     } else {
 #pragma unroll
-      for (int j = 0; j < KPL; ++j) g[j] = dy[j];
+      for (int j = 0; j < KPL; ++j) {
+        g[j] = dy[j];
+        if constexpr (FULL) dzf[j] = 0.0f;
+      }
     }
     sdl = 0.0f;
+    // Branch-free in the softplus flag (selects, with sg = 1 without it): a branch per
+    // token here left values in scratch memory in the main kernel.
+    const bool sp = p.softplus != 0;
 #pragma unroll
     for (int j = 0; j < KPL; ++j) {
       const float raw = dl[j] + bias;
-      float d = raw;
-      if (p.softplus) {
-        d = softplus_f(raw);
-        if constexpr (FULL) sg[j] = __builtin_amdgcn_rcpf(1.0f + exp2_hw(-raw * kLog2e));
-      }
+      float d = sp ? softplus_f(raw) : raw;
+      if constexpr (FULL) sg[j] = sp ? __builtin_amdgcn_rcpf(1.0f + exp2_hw(-raw * kLog2e)) : 1.0f;
       const bool ok = live && t + j < L;
       d = ok ? d : 0.0f;
       g[j] = ok ? g[j] : 0.0f;
@@ -941,7 +944,8 @@ __global__ __launch_bounds__(64 * kW) void bwd_main_kernel(BwdArgs p, BwdLayout 
       // otherwise 2 * (state in pair) + matrix
       constexpr int kC0 = ACC ? 0 : 1, kC1 = ACC ? 1 : 3, kB0 = 0, kB1 = ACC ? 1 : 2;
 
-      // forward recomputation: fold, scan, replay (h_j kept per token)
+      // forward recomputation: fold, scan, replay (h_j kept per token; the input
+      // terms Delta u B from the fold are kept for the replay, which reads only C)
       float av0[KPL], av1[KPL], hv0[KPL], hv1[KPL];
       float h0 = lane0 ? hs0 : 0.0f, h1 = lane0 ? hs1 : 0.0f;
 #pragma unroll
@@ -953,8 +957,10 @@ __global__ __launch_bounds__(64 * kW) void bwd_main_kernel(BwdArgs p, BwdLayout 
           const int j = 4 * q + k;
           av0[j] = exp2_hw(ts.dl[j] * a20);
           av1[j] = exp2_hw(ts.dl[j] * a21);
-          h0 = __builtin_fmaf(av0[j], h0, ts.du[j] * b0[k]);
-          h1 = __builtin_fmaf(av1[j], h1, ts.du[j] * b1[k]);
+          hv0[j] = ts.du[j] * b0[k];
+          hv1[j] = ts.du[j] * b1[k];
+          h0 = __builtin_fmaf(av0[j], h0, hv0[j]);
+          h1 = __builtin_fmaf(av1[j], h1, hv1[j]);
         }
       }
       float P0 = exp2_hw(a20 * ts.sdl), P1 = exp2_hw(a21 * ts.sdl);
@@ -969,16 +975,14 @@ __global__ __launch_bounds__(64 * kW) void bwd_main_kernel(BwdArgs p, BwdLayout 
         float hh0 = hin0, hh1 = hin1;
 #pragma unroll
         for (int q = 0; q < Q; ++q) {
-          const float4 x0 = sB0[q * 64 + lane], x1 = sB1[q * 64 + lane];
           const float4 y0 = sC0[q * 64 + lane], y1 = sC1[q * 64 + lane];
-          const float b0[4] = {x0.x, x0.y, x0.z, x0.w}, b1[4] = {x1.x, x1.y, x1.z, x1.w};
           const float c0[4] = {y0.x, y0.y, y0.z, y0.w}, c1[4] = {y1.x, y1.y, y1.z, y1.w};
           float t0[4], t1[4];
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
             const int j = 4 * q + k;
-            hh0 = __builtin_fmaf(av0[j], hh0, ts.du[j] * b0[k]);
-            hh1 = __builtin_fmaf(av1[j], hh1, ts.du[j] * b1[k]);
+            hh0 = __builtin_fmaf(av0[j], hh0, hv0[j]);   // hv: the input term, then the state
+            hh1 = __builtin_fmaf(av1[j], hh1, hv1[j]);
             hv0[j] = hh0;
             hv1[j] = hh1;
             yt[j] = __builtin_fmaf(c0[k], hh0, yt[j]);
@@ -1086,8 +1090,7 @@ __global__ __launch_bounds__(64 * kW) void bwd_main_kernel(BwdArgs p, BwdLayout 
 #pragma unroll
     for (int j = 0; j < KPL; ++j) {
       o_du[j] = __builtin_fmaf(dsk, ts.g[j], ts.dl[j] * s1[j]);
-      float dd = __builtin_fmaf(ts.u[j], s1[j], s2[j]);
-      if (p.softplus) dd *= ts.sg[j];
+      const float dd = __builtin_fmaf(ts.u[j], s1[j], s2[j]) * ts.sg[j];   // (sg = 1 without the softplus)
       o_dd[j] = dd;
       dDl = __builtin_fmaf(ts.g[j], ts.u[j], dDl);
       dbl += tl + j < L ? dd : 0.0f;
