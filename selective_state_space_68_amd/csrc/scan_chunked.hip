@@ -83,7 +83,9 @@ constexpr int64_t kSplitMaxChannels = 10 * 256;   // the split build: one 10-cha
 // stores y.  With one workgroup per CU and waves dealt to the four SIMDs in turn,
 // every SIMD holds two whole channels and one half: at 10 channels per CU (2560
 // channels on 256 CUs) that is 2.5 channels' work per SIMD where 12-channel groups
-// put 3 on some SIMDs and leave CUs idle.
+// put 3 on some SIMDs and leave CUs idle.  (A split channel's readout is summed as
+// two halves, so its y can differ from a whole channel's in the last bit: results
+// are deterministic, but a channel's rounding depends on its slot in the group.)
 template <typename ACT, bool GATE, int KPL, bool VEC, int NBLK, int kNB, int kW, bool CONV, bool ZOH, bool AP = false,
           bool SAVE = false, bool SPLIT = false>
 __global__ __launch_bounds__(64 * kW) void scan_chunked_kernel(ScanArgs p, int n_dblk) {
@@ -98,7 +100,8 @@ __global__ __launch_bounds__(64 * kW) void scan_chunked_kernel(ScanArgs p, int n
   constexpr bool kAP = AP;
   static_assert(!AP || (ACT::kBytes == 2 && kW == 12 && VEC && NBLK > 0 && PAIR && !ZOH && !CONV),
                 "no arithmetic-progression build for this configuration");
-  static_assert(!SPLIT || (kW == 12 && KPL == 12 && VEC && NBLK > 0 && kNB == 8 && PAIR && !AP && !SAVE && !ZOH && !CONV),
+  static_assert(!SPLIT || (kW == 12 && (KPL == 12 || KPL == 8) && VEC && NBLK > 0 && kNB == 8 && PAIR && !SAVE &&
+                          !ZOH && !CONV),
                 "no split build for this configuration");
   using IO = TokenIO<ACT, KPL>;
   using raw_t = typename IO::raw_t;
@@ -675,7 +678,7 @@ __global__ __launch_bounds__(64 * kW) void scan_chunked_kernel(ScanArgs p, int n
         asm volatile("" : "+s"(toff));
         states(&s_tile[0][0] + toff, nb);
       } else {
-        states(s_tile[par], nb);
+        states(s_tile[par] + (SPLIT ? half * kNB * BLK4 : 0), nb);   // (SPLIT: the second wave's states)
       }
     }
     if constexpr (SPLIT) {
@@ -798,14 +801,21 @@ hipError_t launch_w(const ScanArgs& a, hipStream_t s) {
       return hipGetLastError();
     }
   }
-  if constexpr (ACT::kBytes == 2 && W == 12 && KPL == 12 && !CONV && !ZOH) {
+  if constexpr (ACT::kBytes == 2 && W == 12 && (KPL == 8 || KPL == 12) && !CONV && !ZOH) {
     // Up to 10 channels per CU: 10-channel workgroups with the last two channels
-    // split over two waves each (SPLIT), one workgroup per CU.
-    if (vec && n16 && !a.ap && !a.chunk_states && a.batch * a.D <= kSplitMaxChannels) {
+    // split over two waves each (SPLIT), one workgroup per CU; at 8 tokens per lane
+    // also in the arithmetic-progression build.
+    if (vec && n16 && a.batch * a.D <= kSplitMaxChannels) {
       const int n_split = static_cast<int>((a.D + W - 3) / (W - 2));
-      hipLaunchKernelGGL(
-          (scan_chunked_kernel<ACT, GATE, KPL, true, N16_STEPS, 16 / N16_STEPS, W, CONV, ZOH, false, false, true>),
-          dim3(static_cast<unsigned>(a.batch * n_split)), block, 0, s, a, n_split);
+      const dim3 sgrid(static_cast<unsigned>(a.batch * n_split));
+      if (KPL == 8 && a.ap)
+        hipLaunchKernelGGL(
+            (scan_chunked_kernel<ACT, GATE, KPL, true, N16_STEPS, 16 / N16_STEPS, W, CONV, ZOH, KPL == 8, false, true>),
+            sgrid, block, 0, s, a, n_split);
+      else
+        hipLaunchKernelGGL(
+            (scan_chunked_kernel<ACT, GATE, KPL, true, N16_STEPS, 16 / N16_STEPS, W, CONV, ZOH, false, false, true>),
+            sgrid, block, 0, s, a, n_split);
       return hipGetLastError();
     }
   }
@@ -875,7 +885,8 @@ hipError_t launch_gate(const ScanArgs& a, int kpl, hipStream_t s) {
 // spends a third less on the wave scan per element: 2.7 % faster on a 131072-token
 // sequence (1869 against 1920 us).  Its 768-token chunks pad a short sequence
 // (2048 tokens: 12.5 % padding), so it is the default from 32768 tokens, and not
-// with the arithmetic-progression path, whose build is for 8.
+// with the arithmetic-progression path, whose build is for 8 (in the split form,
+// 131072 x 2560: 1466 us against the general path's 1565 us at 12).
 int resolve_kpl(const ScanArgs& a, int tokens_per_lane, Dt dt) {
   if (tokens_per_lane != 0) return tokens_per_lane;
   const bool twelve = dt == Dt::BF16 && a.N == 16 && !a.zoh && a.conv_w == nullptr && !a.ap && a.L >= 32768 &&
