@@ -109,6 +109,47 @@ def selective_scan(u, delta, A, B, C, Dskip=None, z=None, delta_bias=None,
     return y, h
 
 
+def selective_scan_magnitude(u, delta, A, B, C, Dskip=None, z=None, delta_bias=None,
+                             delta_softplus=True, h0=None, discretization="simplified"):
+    """Return (m [batch][D][L], m_final [batch][D][N]): the size of the summands of each
+    output of selective_scan, in float64.
+
+    The state recurrence is run on absolute values, H_t = exp(Delta*A) H_{t-1} + |bbar*u|
+    (the decay is positive), from H_{-1} = |h0|, and each output's readout is sized the same
+    way: m = (sum_n |C| H + |D u|) |SiLU(z)|.  Every term a floating-point evaluation of y adds
+    up is bounded by m, so an evaluation in precision eps is off by a small multiple of eps*m.
+    This is the scale for comparing outputs that cancel to near zero, where a relative error
+    is undefined; the pages fix no error metric, so the scale is a reading (the test's own).
+    The operations follow selective_scan's step by step, so with nonnegative inputs
+    m == y and m_final == final exactly.
+    """
+    u = np.asarray(u, dtype=np.float64)
+    Bt, Dc, L = u.shape
+    A = np.asarray(A, dtype=np.float64)
+    N = A.shape[1]
+    Bm = np.asarray(B, dtype=np.float64)
+    Cm = np.abs(np.asarray(C, dtype=np.float64))
+    delta = np.asarray(delta, dtype=np.float64)
+    bias = None if delta_bias is None else np.asarray(delta_bias, dtype=np.float64)[None, :]
+    Dv = None if Dskip is None else np.asarray(Dskip, dtype=np.float64)[None, :]
+
+    H = np.zeros((Bt, Dc, N)) if h0 is None else np.abs(np.array(h0, dtype=np.float64))
+    m = np.empty((Bt, Dc, L))
+    for t in range(L):
+        dt = _step_delta(delta[:, :, t], bias, delta_softplus)
+        abar = np.exp(dt[:, :, None] * A[None, :, :])
+        scale = _input_scale(dt, A[None, :, :], discretization)
+        inp = np.abs(scale * u[:, :, t, None] * Bm[:, t, None, :])
+        H = abar * H + inp
+        mt = np.einsum("bdn,bn->bd", H, Cm[:, t, :])
+        if Dv is not None:
+            mt = mt + np.abs(Dv * u[:, :, t])
+        m[:, :, t] = mt
+    if z is not None:
+        m = m * np.abs(silu(z))
+    return m, H
+
+
 def state_update(state, u_t, delta_t, A, B_t, C_t, Dskip=None, z_t=None,
                  delta_bias=None, delta_softplus=True, discretization="simplified"):
     """One recurrent decode step: returns (y_t [S][D], new_state [S][D][N]) in float64.

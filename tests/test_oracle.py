@@ -364,3 +364,69 @@ def test_decode_steps_regenerate_independently():
     s2 = synth.make_decode_step(4, 8, 4, step=7)
     s3 = synth.make_decode_step(4, 8, 4, step=8)
     assert np.array_equal(s1.dev["u"], s2.dev["u"]) and not np.array_equal(s1.dev["u"], s3.dev["u"])
+
+
+# ---------------------------------------------------------------- readout magnitude
+
+def _brute_magnitude(u, delta, A, B, C, Dskip=None, z=None, bias=None, softplus=True, h0=None):
+    """The unrolled closed form of brute_force with every summand in absolute value."""
+    u = np.asarray(u, np.float64)
+    Bt, Dc, L = u.shape
+    N = A.shape[1]
+    m = np.zeros((Bt, Dc, L))
+    for b in range(Bt):
+        for d in range(Dc):
+            raw = np.asarray(delta[b, d], np.float64) + (0.0 if bias is None else float(bias[d]))
+            dl = _softplus_lib(raw) if softplus else raw
+            S = np.cumsum(dl)
+            for t in range(L):
+                H = np.zeros(N)
+                if h0 is not None:
+                    H += np.exp(A[d].astype(np.float64) * S[t]) * np.abs(h0[b, d])
+                for s in range(t + 1):
+                    H += np.exp(A[d].astype(np.float64) * (S[t] - S[s])) * np.abs(
+                        dl[s] * B[b, s].astype(np.float64) * u[b, d, s])
+                mt = float(np.dot(np.abs(C[b, t].astype(np.float64)), H))
+                if Dskip is not None:
+                    mt += abs(float(Dskip[d]) * u[b, d, t])
+                if z is not None:
+                    mt *= abs(float(_silu_lib(z[b, d, t])))
+                m[b, d, t] = mt
+    return m
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_magnitude_matches_unrolled_closed_form(seed):
+    inp = synth.make_scan_inputs(2, 23, 3, 5, "f32", gate=True, d_skip="normal", seed=60 + seed,
+                                 a_kind="lognormal")
+    h0 = synth.make_scan_initial_state(2, 3, 5, seed=seed)
+    m, _ = oracle.selective_scan_magnitude(inp.u, inp.delta, inp.A, inp.B, inp.C, inp.Dskip, inp.z,
+                                           inp.delta_bias, True, h0=h0)
+    ref = _brute_magnitude(inp.u, inp.delta, inp.A, inp.B, inp.C, inp.Dskip, inp.z, inp.delta_bias, True, h0)
+    assert np.max(np.abs(m - ref) / ref) < 1e-12
+
+
+def test_magnitude_equals_output_for_nonnegative_inputs():
+    # every summand nonnegative: the sizes add up to the output itself, bit for bit
+    inp = synth.make_scan_inputs(2, 40, 4, 6, "f32", gate=True, d_skip="normal", seed=71)
+    u, B, C = np.abs(inp.u), np.abs(inp.B), np.abs(inp.C)
+    Dk, z = np.abs(inp.Dskip), np.abs(inp.z)
+    h0 = np.abs(synth.make_scan_initial_state(2, 4, 6, seed=7))
+    y, hf = oracle.selective_scan(u, inp.delta, inp.A, B, C, Dk, z, inp.delta_bias, True, h0=h0)
+    m, mf = oracle.selective_scan_magnitude(u, inp.delta, inp.A, B, C, Dk, z, inp.delta_bias, True, h0=h0)
+    assert np.array_equal(m, y) and np.array_equal(mf, hf)
+
+
+def test_magnitude_bounds_output_and_ignores_signs():
+    inp = synth.make_scan_inputs(2, 60, 5, 16, "f32", gate=True, d_skip="normal", seed=73, a_kind="lognormal")
+    h0 = synth.make_scan_initial_state(2, 5, 16, seed=3)
+    args = (inp.delta, inp.A)
+    y, hf = oracle.selective_scan(inp.u, *args, inp.B, inp.C, inp.Dskip, inp.z, inp.delta_bias, True, h0=h0)
+    m, mf = oracle.selective_scan_magnitude(inp.u, *args, inp.B, inp.C, inp.Dskip, inp.z, inp.delta_bias, True,
+                                            h0=h0)
+    assert np.all(m >= np.abs(y) * (1 - 1e-12)) and np.all(mf >= np.abs(hf) * (1 - 1e-12))
+    assert np.mean(m > 2 * np.abs(y)) > 0.1            # cancellation: the size exceeds the value
+    # flipping the signs of u, C, D and h0 changes y but not the sizes
+    m2, mf2 = oracle.selective_scan_magnitude(-inp.u, *args, inp.B, -inp.C, -inp.Dskip, inp.z, inp.delta_bias,
+                                              True, h0=-h0)
+    assert np.allclose(m2, m, rtol=1e-13, atol=0) and np.allclose(mf2, mf, rtol=1e-13, atol=0)
