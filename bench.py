@@ -72,9 +72,11 @@ KERNEL_NAME = {"decode": "state_update_vec_kernel",
                "bwd": "scan backward call (bwd_summary, bwd_combine, bwd_main, bwd_param_sums, bwd_bc_out kernels)",
                "bwd_saved": "scan backward call with saved chunk states (bwd_main chunk walk, bwd_param_sums, "
                             "bwd_bc_out kernels)",
+               "train": "training pair: the forward scan saving chunk states, then the backward from them",
                "ssd": "ssd_scan_kernel"}
 KERNEL_SRC[KERNEL_NAME["bwd"]] = _CSRC + "scan_bwd.hip"
 KERNEL_SRC[KERNEL_NAME["bwd_saved"]] = _CSRC + "scan_bwd.hip"
+KERNEL_SRC[KERNEL_NAME["train"]] = _CSRC + "scan_bwd.hip"
 PEAK_MFMA_BF16_TFLOPS = 2500.0
 
 
@@ -82,7 +84,7 @@ def kernel_of(cfg, kind, variant=0, tokens_per_lane=0):
     """The kernel (or, for the backward, the call) a workload's timed region runs.
     The forward scan asks the library which kernel it picks for the shape."""
     if kind == "bwd" and cfg.saved:
-        return KERNEL_NAME["bwd_saved"]
+        return KERNEL_NAME["train" if cfg.train else "bwd_saved"]
     if kind != "scan":
         return KERNEL_NAME[kind]
     import torch
@@ -305,15 +307,19 @@ def prepare(name, args, torch, lib_ops):
         for t in bufs:
             t["dy"] = dev(torch, dyup)
             t["cs"] = None
-            if cfg.saved:   # the forward pass that saves the chunk states runs once, before the timing
+            if cfg.saved:   # the forward pass that saves the chunk states (in the step too, when training)
                 _, _, t["cs"] = lib_ops.selective_scan_fwd_save(t["u"], t["delta"], A, t["B"], t["C"], Dk, t["z"],
                                                                 bias, True, y=t["y"], final_state=t["fs"])
-            del t["y"], t["fs"]
+            if not cfg.train:
+                del t["y"], t["fs"]
         torch.cuda.synchronize()
 
         def step(i):
             nonlocal grads
             t = bufs[i % sets]
+            if cfg.train:
+                lib_ops.selective_scan_fwd_save(t["u"], t["delta"], A, t["B"], t["C"], Dk, t["z"], bias, True,
+                                                y=t["y"], final_state=t["fs"], chunk_states=t["cs"])
             grads = lib_ops.selective_scan_bwd(t["u"], t["delta"], A, t["B"], t["C"], t["dy"], Dk, t["z"], bias,
                                                True, workspace=ws, out=grads, chunk_states=t["cs"])
             t["g"] = grads
@@ -402,7 +408,8 @@ def steps_for(nbytes):
 
 
 def alu_roofline(kind, cfg, elements, launch_s):
-    spe = (BWD_ALU_SLOTS_PER_ELEMENT if kind == "bwd" else
+    spe = (BWD_ALU_SLOTS_PER_ELEMENT + (ALU_SLOTS_PER_ELEMENT if getattr(cfg, "train", False) else 0)
+           if kind == "bwd" else
            ZOH_ALU_SLOTS_PER_ELEMENT if cfg.discretization == "zoh" else ALU_SLOTS_PER_ELEMENT)
     slots = spe * elements
     alu = slots / launch_s / 1e12

@@ -23,6 +23,7 @@ class ScanConfig:
     backward: bool = False  # the workload is the backward pass (gradients for dy) instead of the forward
     discretization: str = "simplified"   # or "zoh": the full zero-order-hold input term
     saved: bool = False  # backward: the forward pass's saved 512-token chunk states are read
+    train: bool = False  # with saved: the step is the forward pass that saves them, then the backward
 
     @property
     def elements(self) -> int:
@@ -36,7 +37,15 @@ class ScanConfig:
             # reads u, delta, dy (+ z), B, C, A, D, bias; writes du, ddelta (+ dz), dB, dC, dA, dD, dbias
             n_act = 5 + (2 if self.gate else 0)
             saved = 4 * self.batch * self.D * (-(-self.L // 512)) * self.N if self.saved else 0
-            return (per_tok * n_act + saved
+            if self.train:
+                # plus the forward pass: u, delta (+ z) read again, y and the final
+                # state written, the saved states written once more
+                n_act += 3 + (1 if self.gate else 0)
+                saved *= 2
+                per_tok_extra = 2 * self.batch * self.L * self.N * e + 4 * self.batch * self.D * self.N
+            else:
+                per_tok_extra = 0
+            return (per_tok * n_act + saved + per_tok_extra
                     + 4 * self.batch * self.L * self.N * e    # B, C read; dB, dC written
                     + 8 * self.D * self.N                     # A read, dA written
                     + 16 * self.D)                            # D skip, bias read; their gradients written
@@ -135,6 +144,9 @@ CONFIGS = {
     # ... with the forward pass's saved chunk states (the training pair)
     "bwd_saved_mamba1p4b_bf16": ScanConfig("bwd_saved_mamba1p4b_bf16", 8, 2048, 4096, 16, "bf16", gate=True,
                                            d_skip="ones", backward=True, saved=True),
+    # the training pair: the forward pass saving chunk states, then the backward from them
+    "train_mamba1p4b_bf16": ScanConfig("train_mamba1p4b_bf16", 8, 2048, 4096, 16, "bf16", gate=True, d_skip="ones",
+                                       backward=True, saved=True, train=True),
     "bwd_long131k_bf16": ScanConfig("bwd_long131k_bf16", 1, 131072, 2560, 16, "bf16", gate=True, d_skip="ones",
                                     backward=True),
 }
