@@ -117,3 +117,18 @@ def test_ssd_rejects_wrong_shapes(name, shape):
     with pytest.raises(ValueError, match="must have shape"):
         ssm.ssd_scan_fwd(a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["dt_bias"],
                          initial_state=a["initial_state"], y=a["y"], final_state=a["final_state"])
+
+
+def test_saved_chunk_states_shapes():
+    # [batch][D][ceil(L / 512)][N] for both calls of the training pair
+    a = _scan_inputs(L=1100)
+    bad = torch.zeros(2, 3, 2, 4)                       # 1100 tokens need 3 saved chunks
+    with pytest.raises(ValueError, match="must have shape"):
+        ssm.selective_scan_fwd_save(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["delta_bias"],
+                                    chunk_states=bad)
+    with pytest.raises(ValueError, match="must have shape"):
+        ssm.selective_scan_bwd(a["u"], a["delta"], a["A"], a["B"], a["C"], torch.zeros(2, 3, 1100), a["D"], a["z"],
+                               a["delta_bias"], chunk_states=bad)
+    with pytest.raises(ValueError, match="must live on the GPU"):
+        ssm.selective_scan_fwd_save(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["delta_bias"],
+                                    chunk_states=torch.zeros(2, 3, 3, 4))
