@@ -378,7 +378,7 @@ ssm_status ssm_selective_scan_fwd_save(const void* u, const void* delta, const f
                                        int delta_softplus, const float* initial_state, void* y, float* final_state,
                                        float* chunk_states, int64_t batch, int64_t L, int64_t D, int64_t N,
                                        ssm_dtype dt, void* workspace, size_t workspace_bytes, void* stream) {
-  if (!chunk_states && batch > 0 && L > 0 && D > 0) return SSM_ERR_INVALID_ARG;
+  if (!chunk_states && batch > 0 && L > 0 && D > 0 && N > 0) return SSM_ERR_INVALID_ARG;
   return scan_fwd(u, delta, A, Bm, Cm, Dskip, z, delta_bias, delta_softplus, initial_state, y, final_state, batch, L,
                   D, N, dt, workspace, workspace_bytes, stream, SSM_SCAN_AUTO, 0, 0, chunk_states);
 }

@@ -335,6 +335,7 @@ def _scan_save(lib, **kw):
     (dict(cs=F + 5 * 64 * MB), _lib.SSM_ERR_INVALID_ARG),          # saved states alias y
     (dict(cs=F + 4 * 64 * MB + 64), _lib.SSM_ERR_INVALID_ARG),     # ... overlap C
     (dict(N=17), _lib.SSM_ERR_UNSUPPORTED),                        # saving covers up to 16 states
+    (dict(N=0, cs=None), _lib.SSM_ERR_UNSUPPORTED),                # the state count is reported first
 ])
 def test_scan_save_argument_errors(lib, kw, status):
     assert _scan_save(lib, **kw) == status
