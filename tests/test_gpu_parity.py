@@ -182,6 +182,52 @@ def test_decode_workload_512_steps():
     assert ey <= TOL[cfg.dtype] and ef <= TOL[cfg.dtype], (ey, ef)
 
 
+DECODE_SHAPES = [
+    # S, D, N, dtype, gate, in_place, d_skip, bias: every vector-path N (1 to 16 lanes per
+    # channel), channel blocks with idle lanes (D not a multiple of 64 / (N / 4)), one
+    # sequence, and a sequence count past one round of waves (each wave then visits
+    # several sequences of its channel block), plus the scalar kernel (N = 5)
+    (3, 37, 4, "f32", True, True, "normal", True),
+    (5, 100, 8, "bf16", False, False, "none", True),
+    (2, 70, 16, "f32", True, False, "normal", False),
+    (4, 9, 32, "bf16", True, True, "ones", True),
+    (3, 5, 64, "f32", True, True, "normal", True),
+    (1, 5120, 16, "bf16", True, True, "ones", True),
+    (3000, 48, 16, "bf16", True, True, "normal", True),
+    (4, 33, 5, "f32", True, False, "normal", True),
+]
+
+
+@pytest.mark.parametrize("shape", DECODE_SHAPES)
+def test_decode_shapes(shape):
+    """Three decode steps on shapes that exercise the decode kernel's channel blocks and
+    its walk over sequences, every output and state against the oracle's steps."""
+    import oracle
+    import torch
+    from selective_state_space_68_amd import state_update
+    S, D, N, dtype, gate, in_place, d_skip, use_bias = shape
+    A, Dsk, bias = synth.make_decode_params(S, D, N, d_skip=d_skip, seed=3)
+    bias = bias if use_bias else None
+    st = synth.make_decode_state(S, D, N, seed=3)
+    state = dev(st)
+    ref = st.astype(np.float64)
+    for k in range(3):
+        x = synth.make_decode_step(S, D, N, k, dtype, gate, seed=3)
+        out = state if in_place else torch.full_like(state, float("nan"))
+        before = None if in_place else host(state)
+        y = state_update(state, dev(x.dev["u"]), dev(x.dev["delta"]), dev(A), dev(x.dev["B"]), dev(x.dev["C"]),
+                         dev(Dsk) if Dsk is not None else None, dev(x.dev["z"]) if gate else None,
+                         dev(bias) if bias is not None else None, True, out_state=out)
+        ry, ref = oracle.state_update(ref, x.u, x.delta, A, x.B, x.C, Dsk, x.z if gate else None, bias, True)
+        torch.cuda.synchronize()
+        ey, es = row_rel_err(host(y), ry, axis=None), row_rel_err(host(out), ref)
+        print(f"decode {shape} step {k}: y_err={ey:.2e} state_err={es:.2e}", flush=True)
+        assert ey <= TOL[dtype] and es <= TOL[dtype], (k, ey, es)
+        if not in_place:
+            assert np.array_equal(host(state), before), "state_in written"
+            state = out
+
+
 # ------------------------------------------------------------------ edge shapes
 
 EDGE = [
