@@ -110,16 +110,17 @@ __device__ __forceinline__ float softplus_f(float x) {
   return fmaxf(x, 0.0f) + __builtin_fmaf(__builtin_amdgcn_logf(w), kLn2, err);
 }
 
-// softplus for bfloat16 activations: log(1 + e^x) from the hardware exp2 and log2,
-// without the compensation above.  Rounding 1 + e^x costs about 6e-8 absolute, so
-// the relative error is about 6e-8 / e^x where x < 0 (1e-3 at x = -10, where Delta
-// is 4.5e-5; Delta's own error then stays below 1e-7 absolute), and a few 1e-8 for
-// x >= 0; beyond x = 15 the result is x (the remainder e^-x < 3.1e-7 is below half
-// an ulp of x).  Four VALU operations and two transcendentals per token fewer than
-// the compensated form, within the bfloat16 bar by orders of magnitude.
+// softplus for bfloat16 activations: max(x, 0) + log(1 + e^-|x|) from the hardware
+// exp2 and log2, without the compensation above.  Rounding 1 + e^-|x| costs about
+// 6e-8 absolute, so the relative error is about 6e-8 / e^x where x < 0 (1e-3 at
+// x = -10, where Delta is 4.5e-5; Delta's own error then stays below 1e-7 absolute)
+// and a few 1e-8 for x >= 0, with no overflow for large x.  Four VALU operations
+// (max, the scaled argument, 1 + e, the final FMA) and two transcendentals: three
+// VALU operations and two transcendentals per token fewer than the compensated
+// form, within the bfloat16 bar by orders of magnitude.
 __device__ __forceinline__ float softplus_bf16act(float x) {
-  const float l = __builtin_amdgcn_logf(1.0f + exp2_hw(x * kLog2e)) * kLn2;
-  return x > 15.0f ? x : l;
+  const float l = __builtin_amdgcn_logf(1.0f + exp2_hw(-fabsf(x) * kLog2e));
+  return __builtin_fmaf(l, kLn2, fmaxf(x, 0.0f));
 }
 
 // Full zero-order hold: the factor (e^x - 1)/A = Delta * (e^x - 1)/x of the input
