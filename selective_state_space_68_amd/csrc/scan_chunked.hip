@@ -692,7 +692,12 @@ __global__ __launch_bounds__(64 * kW) void scan_chunked_kernel(ScanArgs p, int n
       }
     }
     if (!tail1) store_tile(par ^ 1);
-    barrier_lds();
+    // ROWS: the steps of chunk c all read buffer c % 2, and the pieces of chunk c + 1
+    // go to the other buffer, which chunk c - 1 finished reading before the barrier
+    // that ended it.  So only the chunk's last step needs the barrier: it publishes
+    // chunk c + 1 and frees buffer c % 2 for the pieces of chunk c + 2.  Otherwise each
+    // step's tile is its own buffer, written during the step before: a barrier per step.
+    if (!ROWS || nb == nblk - 1) barrier_lds();
   };
 
   prefetch_act(p.u, 0, u_raw);
