@@ -117,7 +117,7 @@ struct ActIO8<ActBF16> {
 // SAVE: the build that also writes the saved chunk states (p.chunk_states) every
 // 512 tokens, for the backward pass; a separate build, so that the default ones keep
 // their registers.
-template <typename ACT, bool GATE, int SPL, bool ZOH, bool CONV, bool AP = false, bool SAVE = false>
+template <typename ACT, bool GATE, int SPL, bool ZOH, bool CONV, bool AP = false, bool SAVE = false, bool PF2 = false>
 __global__ __launch_bounds__(64 * kTsWaves) void scan_tokseq_kernel(ScanArgs p) {
   constexpr int QL = kTsN / SPL;           // lanes per channel (an aligned group)
   constexpr int CPW = 64 / QL;             // channels per wave
@@ -195,21 +195,27 @@ __global__ __launch_bounds__(64 * kTsWaves) void scan_tokseq_kernel(ScanArgs p) 
   // of the block, states 8 (v % 2) ..).  Pieces past L (L % 8 == 0: an activation
   // piece is all in or all out) reload the row's last piece or token; their Delta
   // is set to 0.
-  raw_t u_raw[IO::kVec], d_raw[IO::kVec], z_raw[IO::kVec];
-  Piece8<ACT> bp[BCP], cp[BCP];
-  auto fetch = [&](int64_t t0) __attribute__((always_inline)) {
+  // PF2: two sets, alternating by block, so block k's loads are issued while block
+  // k - 2 computes, two blocks ahead of their use instead of one.  The second set
+  // takes about 24 more registers, so the host picks this build only where the launch
+  // has at most 2 waves per SIMD and the registers cost no occupancy.
+  struct BlockRegs {
+    raw_t u[IO::kVec], d[IO::kVec], z[IO::kVec];
+    Piece8<ACT> bp[BCP], cp[BCP];
+  };
+  auto fetch = [&](int64_t t0, BlockRegs& rg) __attribute__((always_inline)) {
     int64_t tp = t0 + 8 * q;
     tp = tp + 8 <= L ? tp : L - 8;
-    IO::load_raw(p.u, row + tp, u_raw);
-    IO::load_raw(p.delta, row + tp, d_raw);
-    if constexpr (GATE) IO::load_raw(p.z, row + tp, z_raw);
+    IO::load_raw(p.u, row + tp, rg.u);
+    IO::load_raw(p.delta, row + tp, rg.d);
+    if constexpr (GATE) IO::load_raw(p.z, row + tp, rg.z);
 #pragma unroll
     for (int k = 0; k < BCP; ++k) {
       const int v = lane + 64 * k;
       int64_t t = t0 + v / 2;
       t = t < L ? t : L - 1;
-      bp[k].load(p.Bm, bc_row + t * kTsN + 8 * (v % 2));
-      cp[k].load(p.Cm, bc_row + t * kTsN + 8 * (v % 2));
+      rg.bp[k].load(p.Bm, bc_row + t * kTsN + 8 * (v % 2));
+      rg.cp[k].load(p.Cm, bc_row + t * kTsN + 8 * (v % 2));
     }
   };
 
@@ -224,14 +230,15 @@ __global__ __launch_bounds__(64 * kTsWaves) void scan_tokseq_kernel(ScanArgs p) 
 #pragma unroll
     for (int j = 0; j < SPL; ++j) cst[SPL * q + j] = h[j];
   }
-  fetch(0);
-  for (int64_t blk = 0; blk < nblk; ++blk) {
+  constexpr int kAhead = PF2 ? 2 : 1;                 // blocks between a set's load and its use
+  BlockRegs rg0, rg1;
+  auto block = [&](int64_t blk, BlockRegs& rg) __attribute__((always_inline)) {
     const int64_t t0 = blk * T;
     const bool pvalid = t0 + 8 * q < L;
     // ---- per-token work of this lane's piece; (Delta, Delta*u) and the B/C tile to LDS
     float uv[8], dl[8], ysk[8], gt[8] = {};
-    IO::unpack(u_raw, uv);
-    IO::unpack(d_raw, dl);
+    IO::unpack(rg.u, uv);
+    IO::unpack(rg.d, dl);
     if constexpr (CONV) {
       // uv holds x: u = SiLU(conv(x)), accumulated oldest tap first
       float xx[11];
@@ -255,7 +262,7 @@ __global__ __launch_bounds__(64 * kTsWaves) void scan_tokseq_kernel(ScanArgs p) 
     }
     if constexpr (GATE) {
       float zv[8];
-      IO::unpack(z_raw, zv);
+      IO::unpack(rg.z, zv);
 #pragma unroll
       for (int k = 0; k < 8; ++k) gt[k] = silu_f(zv[k]);
     }
@@ -279,17 +286,17 @@ __global__ __launch_bounds__(64 * kTsWaves) void scan_tokseq_kernel(ScanArgs p) 
       float4* crow = reinterpret_cast<float4*>(bc_w + (1 * T + t) * kTsN);
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
-        brow[(h2 + g) ^ sw] = make_float4(bp[k].get(4 * g), bp[k].get(4 * g + 1), bp[k].get(4 * g + 2),
-                                          bp[k].get(4 * g + 3));
-        crow[(h2 + g) ^ sw] = make_float4(cp[k].get(4 * g), cp[k].get(4 * g + 1), cp[k].get(4 * g + 2),
-                                          cp[k].get(4 * g + 3));
+        brow[(h2 + g) ^ sw] = make_float4(rg.bp[k].get(4 * g), rg.bp[k].get(4 * g + 1), rg.bp[k].get(4 * g + 2),
+                                          rg.bp[k].get(4 * g + 3));
+        crow[(h2 + g) ^ sw] = make_float4(rg.cp[k].get(4 * g), rg.cp[k].get(4 * g + 1), rg.cp[k].get(4 * g + 2),
+                                          rg.cp[k].get(4 * g + 3));
       }
     }
     // the wave's own LDS writes before its reads (one wave's LDS operations are
     // performed in order; this keeps the compiler from moving reads above writes)
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    fetch(t0 + T < L ? t0 + T : t0);                 // next block (the last one reloads itself, unused)
+    fetch(t0 + kAhead * T < L ? t0 + kAhead * T : t0, rg);   // block blk + kAhead into this set (past the end: this block, unused)
 
     // ---- the recurrence, token by token; lane q keeps the readout of tokens 8q .. 8q+7
     float rsel[8];
@@ -376,6 +383,16 @@ __global__ __launch_bounds__(64 * kTsWaves) void scan_tokseq_kernel(ScanArgs p) 
     // reads of this block's LDS before the next block's writes
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  fetch(0, rg0);
+  if constexpr (PF2) {
+    fetch(T < L ? T : 0, rg1);                       // (one block only: block 0 again, unused)
+    for (int64_t blk = 0; blk < nblk; blk += 2) {
+      block(blk, rg0);
+      if (blk + 1 < nblk) block(blk + 1, rg1);
+    }
+  } else {
+    for (int64_t blk = 0; blk < nblk; ++blk) block(blk, rg0);
   }
   if (store_ok && p.final_state) {
 #pragma unroll
@@ -390,9 +407,16 @@ hipError_t launch_spl(const ScanArgs& a, hipStream_t s) {
   constexpr int CPW = 64 * SPL / kTsN;
   const int64_t ngrp = (a.D + CPW - 1) / CPW;
   const int64_t blocks = a.batch * ((ngrp + kTsWaves - 1) / kTsWaves);
-  hipLaunchKernelGGL((scan_tokseq_kernel<ACT, GATE, SPL, ZOH, CONV, AP, SAVE>), dim3(static_cast<unsigned>(blocks)),
-                     dim3(64 * kTsWaves), 0,
-                     s, a);
+  // Two block loads in flight per wave (PF2) where the launch has at most 2 waves per
+  // SIMD (1024 SIMDs), so its extra registers cost no occupancy.  Measured at the
+  // 1.4B shape (2 waves per SIMD), same box: fused conv 317.5 -> 307.8 us, ZOH 456.2
+  // -> 452.9 us, the plain scan 282.8 -> 282.3 us.
+  if (blocks * kTsWaves <= 2 * 1024)
+    hipLaunchKernelGGL((scan_tokseq_kernel<ACT, GATE, SPL, ZOH, CONV, AP, SAVE, true>),
+                       dim3(static_cast<unsigned>(blocks)), dim3(64 * kTsWaves), 0, s, a);
+  else
+    hipLaunchKernelGGL((scan_tokseq_kernel<ACT, GATE, SPL, ZOH, CONV, AP, SAVE, false>),
+                       dim3(static_cast<unsigned>(blocks)), dim3(64 * kTsWaves), 0, s, a);
   return hipGetLastError();
 }
 
