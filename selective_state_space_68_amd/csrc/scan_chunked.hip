@@ -34,10 +34,9 @@
 //     float32 and permuted into the order the lanes read it, to the other of two
 //     LDS buffers; one barrier per step publishes it;
 //   * a wave loads its next chunk's u and delta and this chunk's z into registers
-//     during the current chunk, and stores the previous chunk's y at its first
-//     step, one kind of traffic per step, so a chunk's HBM traffic is spread over
-//     its steps instead of arriving as one burst per chunk.  The barriers order
-//     LDS only; a load is waited for where its value is first used.
+//     during the current chunk, each as early as its registers are free, and stores
+//     the previous chunk's y at its first step.  The barriers order LDS only; a load
+//     is waited for where its value is first used.
 // No MFMA: the readout is a per-token dot product over n, not a shared-operand
 // contraction.  The kernel is bound by HBM bandwidth and by the VALU and
 // transcendental rate (one exp per element).
@@ -570,14 +569,18 @@ __global__ __launch_bounds__(64 * kW) void scan_chunked_kernel(ScanArgs p, int n
     }
   };
 
-  // HBM traffic is spread over a chunk's steps: at step 0 the previous chunk's y is
-  // stored and this chunk's z loaded (its registers were just read by the previous
-  // chunk's epilogue, and it is used by this chunk's, so it has the whole chunk to
-  // arrive), the next chunk's u is loaded at step 1 and its delta at step 2.  (z
-  // loaded at the chunk's last step, one step before its use, measured 1.3 % slower
-  // on the 131072-token bfloat16 workload and the same on the float32 130M one.)
-  const int st_u = nblk > 1 ? 1 : 0;
-  const int st_d = nblk > 2 ? 2 : st_u;
+  // A chunk's HBM traffic: at step 0 the previous chunk's y is stored and this chunk's
+  // z loaded (its registers were just read by the previous chunk's epilogue, and it is
+  // used by this chunk's, so it has the whole chunk to arrive).  The next chunk's u and
+  // delta: with two steps per chunk (bfloat16, N = 16) at step 0 as well, right after
+  // the prologue has read this chunk's, two steps before their use; with more steps
+  // per chunk spread over steps 1 and 2.  Measured on the 131072-token bfloat16
+  // workload (two steps): z at step 0 instead of the last step 1560 -> 1539 us, then
+  // u and delta at step 0 instead of step 1 1534 -> 1517 us.  On the float32 130M
+  // workload (four steps) z at step 0 measured the same, and u and delta at step 0
+  // 5 % slower than at steps 1 and 2.
+  const int st_u = nblk > 2 ? 1 : 0;
+  const int st_d = nblk > 2 ? 2 : 0;
   const int st_z = 0;
 
   // Per-state wave-uniform values when the state count is fixed at compile time
